@@ -1,0 +1,124 @@
+"""CPU oracle for the KDA gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and this package imports nothing from
+the product path: the two share no code.
+
+Two independent fp64 implementations live here:
+
+* ``recurrent_fwd`` / ``recurrent_step`` -- the definition, token by token, in
+  plain C (``kda_oracle.c``) with OpenMP over independent sequences.  It is the
+  update rule of "Hybrid Linear Attention Architecture: Making LLM Training and
+  Inference More Efficient" §3.3 (KDA equation) with the read-after-write
+  output of "Demystifying Hybrid LLM Architectures: Linear Attention,
+  Residuals, and Latent MoE" §2.3.
+* ``oracle.chunked`` -- the chunkwise-parallel form of the same pages' §IV /
+  §2.4, in NumPy fp64, which exposes the per-chunk intermediates (cumulative
+  log-gates, W, U, the residual U - W S, the chunk-entry states).
+
+Pins (tests that tie both to something other than themselves) are in
+``tests/test_oracle_pins.py`` and ``tests/test_chunked_model.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP).  Returns the .so path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                           i64, i64, i64, i64, i64, ctypes.c_int]
+            lib.kda_oracle_fwd.restype = ctypes.c_int
+            lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                            i64, i64, i64, i64, ctypes.c_int]
+            lib.kda_oracle_step.restype = ctypes.c_int
+            lib.kda_oracle_max_threads.argtypes = []
+            lib.kda_oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast to a C-contiguous float64 array (exact for bf16/fp32 values)."""
+    if hasattr(x, "detach"):            # a torch tensor: copy to host, upcast
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_load().kda_oracle_max_threads())
+
+
+def recurrent_fwd(q, k, v, g, beta, S0=None, nthreads: int = 0):
+    """Token-by-token fp64 forward.
+
+    q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
+    S0: [B, H, dk, dv] or None (zeros).  Returns (o [B,T,H,dv], S_T [B,H,dk,dv]).
+    """
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, T, H, dk) and g.shape == (B, T, H, dk)
+    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    S0a = None if S0 is None else _f64(S0)
+    if S0a is not None:
+        assert S0a.shape == (B, H, dk, dv)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    ST = np.zeros((B, H, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(S0a), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                                int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_fwd failed ({rc})")
+    return o, ST
+
+
+def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0):
+    """One decode token for N sequences.  S [N,H,dk,dv] fp64 is returned
+    updated (a new array; the input is not modified).  Returns (o, S_new)."""
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    Sn = _f64(S).copy()
+    assert Sn.shape == (N, H, dk, dv)
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = _load().kda_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(Sn), _ptr(o), N, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_step failed ({rc})")
+    return o, Sn

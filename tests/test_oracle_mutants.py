@@ -1,0 +1,125 @@
+"""The pins must catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one mistake in a private copy of the C oracle's source
+(dropped term, wrong order, wrong sign, read before write, ...), builds it
+into a temporary library, and checks that the pin suite rejects it while the
+unmodified source passes.  Nothing here touches the real oracle library.
+"""
+import ctypes
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kda_oracle.c")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "decay_first_example.json")
+
+# (name, original text, replacement) -- each a single plausible slip.
+MUTANTS = [
+    ("erase_before_decay",
+     "    /* 1. per-channel forget gate",
+     "    /* (mutant) decay moved after the update */ if (0) {} /* 1."),
+    ("decay_sign",
+     "const double a = exp(g[c]);",
+     "const double a = exp(-g[c]);"),
+    ("no_erase",
+     "S[c * dv + j] += beta * k[c] * (v[j] - r[j]);",
+     "S[c * dv + j] += beta * k[c] * (v[j]);"),
+    ("erase_sign",
+     "S[c * dv + j] += beta * k[c] * (v[j] - r[j]);",
+     "S[c * dv + j] += beta * k[c] * (v[j] + r[j]);"),
+    ("no_beta",
+     "S[c * dv + j] += beta * k[c] * (v[j] - r[j]);",
+     "S[c * dv + j] += k[c] * (v[j] - r[j]);"),
+    ("read_with_k",
+     "o[j] += q[c] * S[c * dv + j];",
+     "o[j] += k[c] * S[c * dv + j];"),
+    ("retrieve_with_q",
+     "r[j] += k[c] * S[c * dv + j];",
+     "r[j] += q[c] * S[c * dv + j];"),
+]
+
+
+def _apply(src, name, old, new):
+    if name == "erase_before_decay":
+        # move the decay loop after erase/write (and before the read)
+        start = src.index("    /* 1. per-channel forget gate")
+        end = src.index("    /* 2. retrieve")
+        decay = src[start:end]
+        src = src[:start] + src[end:]
+        pos = src.index("    /* 4. read after write")
+        return src[:pos] + decay + src[pos:]
+    assert old in src, name
+    return src.replace(old, new)
+
+
+def _build(tmp_path, src, tag):
+    c = tmp_path / f"o_{tag}.c"
+    so = tmp_path / f"o_{tag}.so"
+    c.write_text(src)
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-std=c99", str(c), "-o", str(so), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.kda_oracle_fwd.argtypes = [dp] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int]
+    return lib
+
+
+def _fwd(lib, q, k, v, g, beta, S0):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, g, beta)]
+    S0a = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    o = np.zeros((B, T, H, dv)); ST = np.zeros((B, H, dk, dv))
+    p = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = lib.kda_oracle_fwd(*[p(a) for a in arrs], p(S0a), p(o), p(ST), B, T, H, dk, dv, 1)
+    assert rc == 0
+    return o, ST
+
+
+def _pins_fail(lib):
+    """Return the names of the pins this build fails."""
+    rng = np.random.default_rng(7)
+    fails = []
+    # P5 hand-worked example
+    ex = json.load(open(GOLDEN))
+    i = ex["inputs"]
+    o, ST = _fwd(lib, np.array(i["q"])[None, None, None], np.array(i["k"])[None, None, None],
+                 np.array(i["v"])[None, None, None], np.array(i["g"])[None, None, None],
+                 np.array([[[i["beta"]]]]), np.array(i["S0"])[None, None])
+    if np.max(np.abs(ST[0, 0] - np.array(ex["expected"]["S1"]))) > 1e-12 or abs(o[0, 0, 0, 0] - 0.25) > 1e-12:
+        fails.append("worked_example")
+    # P1 single-token closed form
+    dk, dv = 5, 3
+    q = rng.standard_normal((1, 1, 1, dk)); k = rng.standard_normal((1, 1, 1, dk)); k /= np.linalg.norm(k)
+    v = rng.standard_normal((1, 1, 1, dv)); g = -np.abs(rng.standard_normal((1, 1, 1, dk)))
+    beta = np.array([[[0.6]]]); S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST = _fwd(lib, q, k, v, g, beta, S0)
+    kk = k[0, 0, 0]
+    S1 = (np.eye(dk) - 0.6 * np.outer(kk, kk)) @ np.diag(np.exp(g[0, 0, 0])) @ S0[0, 0] + 0.6 * np.outer(kk, v[0, 0, 0])
+    if np.max(np.abs(ST[0, 0] - S1)) > 1e-12 or np.max(np.abs(o[0, 0, 0] - S1.T @ q[0, 0, 0])) > 1e-12:
+        fails.append("single_token")
+    # P4 orthonormal recall
+    T = 4
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Qm[:, :T].T
+    V = rng.standard_normal((T, dv))
+    o, ST = _fwd(lib, K[None, :, None], K[None, :, None], V[None, :, None],
+                 np.zeros((1, T, 1, dk)), np.ones((1, T, 1)), S0)
+    if np.max(np.abs(K @ ST[0, 0] - V)) > 1e-12:
+        fails.append("recall")
+    return fails
+
+
+def test_unmodified_source_passes(tmp_path):
+    lib = _build(tmp_path, open(SRC).read(), "ok")
+    assert _pins_fail(lib) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = _apply(open(SRC).read(), name, old, new)
+    lib = _build(tmp_path, src, name)
+    assert _pins_fail(lib), f"mutant {name} passed every pin"
