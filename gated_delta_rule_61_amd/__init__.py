@@ -1,0 +1,205 @@
+"""MI355X (gfx950) KDA: chunkwise gated delta rule with a per-channel forget
+gate, and its one-token decode step.
+
+Thin ctypes binding over the C ABI of ``libkda.so`` (declared in
+``include/kda.h``): tensors in, device pointers and the current HIP stream
+out.  PyTorch only allocates device memory and provides the stream; every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: without the built library (``python -m gated_delta_rule_61_amd._build``
+or ``__graft_entry__.build()``) every call raises.
+
+Layouts (row-major, contiguous):
+  q, k, g [B, T, H, d_k]; v, o [B, T, H, d_v]; beta [B, T, H];
+  S0, S_T [B, H, d_k, d_v] float32.  q, k, v, g, beta share one dtype
+  (torch.bfloat16 or torch.float32); o has that dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+ROOT = os.path.dirname(_PKG)
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+KDA_F32, KDA_BF16 = 0, 1
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "kda_chunk_fwd": ([_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_staged": ([_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_workspace_size": ([_i] * 6, _sz),
+    "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
+    "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
+    "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
+    "kda_stage_ut": ([_vp] * 6 + [_i] * 6 + [_vp], _i),
+    "kda_stage_state": ([_vp] * 8 + [_i] * 6 + [_vp], _i),
+    "kda_stage_output": ([_vp] * 6 + [_i] * 6 + [_vp], _i),
+    "kda_status_string": ([_i], ctypes.c_char_p),
+    "kda_last_hip_error": ([], _i),
+    "kda_version": ([], _i),
+}
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise KDAError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_delta_rule_61_amd._build` (hipcc, gfx950)")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().kda_status_string(status).decode()
+        raise KDAError(f"KDA call failed with status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise KDAError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    return _DT[t.dtype]
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        raise KDAError(f"{name} is required")
+    if not t.is_cuda:
+        raise KDAError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise KDAError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise KDAError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise KDAError(f"{name} must be contiguous")
+
+
+def _prefill_shapes(q, k, v, g, beta):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, (B, T, H, dk), dt, "q")
+    _need(k, (B, T, H, dk), dt, "k")
+    _need(g, (B, T, H, dk), dt, "g")
+    _need(v, (B, T, H, dv), dt, "v")
+    _need(beta, (B, T, H), dt, "beta")
+    return B, T, H, dk, dv, dt
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
+              workspace=None, stream=None, want_state=True):
+    """Prefill: returns (o, S_T).  With staged=True the four-kernel schedule
+    runs instead of the fused kernel (same result up to rounding)."""
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta)
+    dev = q.device
+    if S0 is not None:
+        _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    L = lib()
+    code = _dtype(q)
+    fn = L.kda_chunk_fwd_staged if staged else L.kda_chunk_fwd
+    wsz = (L.kda_chunk_fwd_staged_workspace_size if staged else L.kda_chunk_fwd_workspace_size)(
+        B, T, H, dk, dv, code)
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+              B, T, H, dk, dv, code, _ptr(workspace) if wsz else None, wsz, _stream(stream)))
+    return o, S_T
+
+
+def recurrent_step(q, k, v, g, beta, S, *, o=None, stream=None):
+    """One decode token for N sequences; S [N,H,d_k,d_v] fp32 is updated in
+    place.  Returns o [N,H,d_v]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, (N, H, dk), dt, "q")
+    _need(k, (N, H, dk), dt, "k")
+    _need(g, (N, H, dk), dt, "g")
+    _need(v, (N, H, dv), dt, "v")
+    _need(beta, (N, H), dt, "beta")
+    _need(S, (N, H, dk, dv), torch.float32, "S")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check(lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                                    N, H, dk, dv, _dtype(q), _stream(stream)))
+    return o
+
+
+# ---- the staged schedule's steps, one call each ---------------------------
+
+def stage_cumsum(g, *, stream=None):
+    B, T, H, dk = g.shape
+    b = torch.empty((B, T, H, dk), dtype=torch.float32, device=g.device)
+    _check(lib().kda_stage_cumsum(_ptr(g), _ptr(b), B, T, H, dk, _dtype(g), _stream(stream)))
+    return b
+
+
+def stage_ut(k, v, beta, b, *, stream=None):
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    W = torch.empty((B, T, H, dk), dtype=torch.float32, device=k.device)
+    U = torch.empty((B, T, H, dv), dtype=torch.float32, device=k.device)
+    _check(lib().kda_stage_ut(_ptr(k), _ptr(v), _ptr(beta), _ptr(b), _ptr(W), _ptr(U),
+                              B, T, H, dk, dv, _dtype(k), _stream(stream)))
+    return W, U
+
+
+def stage_state(k, b, W, U, S0=None, *, stream=None):
+    B, T, H, dk = k.shape
+    dv = U.shape[-1]
+    N = (T + 63) // 64
+    dev = k.device
+    Delta = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S_chunks = torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(lib().kda_stage_state(_ptr(k), _ptr(b), _ptr(W), _ptr(U), _ptr(S0), _ptr(Delta),
+                                 _ptr(S_chunks), _ptr(S_T), B, T, H, dk, dv, _dtype(k), _stream(stream)))
+    return Delta, S_chunks, S_T
+
+
+def stage_output(q, k, b, Delta, S_chunks, *, stream=None):
+    B, T, H, dk = q.shape
+    dv = Delta.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _check(lib().kda_stage_output(_ptr(q), _ptr(k), _ptr(b), _ptr(Delta), _ptr(S_chunks), _ptr(o),
+                                  B, T, H, dk, dv, _dtype(q), _stream(stream)))
+    return o
+
+
+__all__ = ["chunk_fwd", "recurrent_step", "stage_cumsum", "stage_ut", "stage_state",
+           "stage_output", "lib", "KDAError", "LIB_PATH", "HEADER"]

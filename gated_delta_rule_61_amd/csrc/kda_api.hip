@@ -1,0 +1,230 @@
+// kda_api.hip -- the C ABI (include/kda.h): argument validation, workspace
+// layout and launch order.  No allocation, no synchronisation; all work goes
+// on the caller's stream.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  g_last_hip = (int)e;
+  return KDA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+// head sizes the chunked kernels are built for
+int check_chunk_dims(int B, int T, int H, int dk, int dv, int dt) {
+  if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
+  if (dt == KDA_BF16 && !((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return KDA_ERR_SHAPE;
+  if (dt == KDA_F32 && !(dk == 64 && dv == 64)) return KDA_ERR_SHAPE;
+  // 32-bit byte offsets inside one chunk of one tensor, 64-bit elsewhere
+  if ((int64_t)H * dk * 64 * 4 > INT32_MAX || (int64_t)H * dv * 64 * 4 > INT32_MAX) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+int check_step_dims(int N, int H, int dk, int dv, int dt) {
+  if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  if (N < 0 || H < 0) return KDA_ERR_SHAPE;
+  if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct StagedWs {
+  size_t b, W, U, Delta, S, total;
+};
+
+StagedWs staged_layout(int B, int T, int H, int dk, int dv) {
+  const size_t tok = (size_t)B * (size_t)T * (size_t)H;
+  const size_t nch = ((size_t)T + 63) / 64;
+  StagedWs w;
+  size_t off = 0;
+  w.b = off; off += round256(tok * dk * 4);
+  w.W = off; off += round256(tok * dk * 4);
+  w.U = off; off += round256(tok * dv * 4);
+  w.Delta = off; off += round256(tok * dv * 4);
+  w.S = off; off += round256((size_t)B * H * nch * dk * dv * 4);
+  w.total = off;
+  return w;
+}
+
+int env_nsplit() {
+  const char* e = getenv("KDA_FUSED_NSPLIT");
+  if (!e) return 0;
+  const int v = atoi(e);
+  return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
+}
+
+#define KDA_REQUIRE(cond, code) \
+  do {                          \
+    if (!(cond)) return (code); \
+  } while (0)
+
+// q, k, v, g, o are read/written as 16-byte vectors; beta only needs the
+// alignment of its element type.
+int check_tokens(const void* q, const void* k, const void* v, const void* g, const void* beta, const void* o,
+                 int dtype) {
+  KDA_REQUIRE(q && k && v && g && beta && o, KDA_ERR_NULL);
+  const uintptr_t esz = dtype == KDA_BF16 ? 2u : 4u;
+  KDA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g) && aligned16(o) &&
+              (reinterpret_cast<uintptr_t>(beta) % esz) == 0, KDA_ERR_ALIGN);
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 10000; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "unsupported or negative size (supported: d_k = d_v in {64,128} for bf16, 64 for fp32)";
+    case KDA_ERR_DTYPE: return "unsupported dtype";
+    case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return hipGetErrorString((hipError_t)g_last_hip);
+    case KDA_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int kda_last_hip_error(void) { return g_last_hip; }
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
+  (void)B; (void)T; (void)H; (void)d_k; (void)d_v; (void)dtype;
+  return 0;
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16, env_nsplit()};
+  return hip_status(kda::launch_fused(a, (hipStream_t)stream));
+}
+
+size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
+  if (check_chunk_dims(B, T, H, d_k, d_v, dtype)) return 0;
+  return staged_layout(B, T, H, d_k, d_v).total;
+}
+
+int kda_chunk_fwd_staged(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
+                         int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  const StagedWs w = staged_layout(B, T, H, d_k, d_v);
+  KDA_REQUIRE(workspace != nullptr && workspace_bytes >= w.total, KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+  char* ws = static_cast<char*>(workspace);
+  kda::StageArgs a{q, k, v, g, beta, S0, o, S_T,
+                   reinterpret_cast<float*>(ws + w.b), reinterpret_cast<float*>(ws + w.W),
+                   reinterpret_cast<float*>(ws + w.U), reinterpret_cast<float*>(ws + w.Delta),
+                   reinterpret_cast<float*>(ws + w.S), B, T, H, d_k, d_v, dtype == KDA_BF16};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kda::launch_stage_cumsum(a, s);
+  if (e == hipSuccess) e = kda::launch_stage_ut(a, s);
+  if (e == hipSuccess) e = kda::launch_stage_state(a, s);
+  if (e == hipSuccess) e = kda::launch_stage_output(a, s);
+  return hip_status(e);
+}
+
+int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k, int dtype, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_k, dtype);
+  if (st) return st;
+  if ((int64_t)B * H * T == 0) return KDA_OK;
+  KDA_REQUIRE(g && b, KDA_ERR_NULL);
+  KDA_REQUIRE(aligned16(g) && aligned16(b), KDA_ERR_ALIGN);
+  kda::StageArgs a{};
+  a.g = g; a.b = b; a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_k; a.bf16 = dtype == KDA_BF16;
+  return hip_status(kda::launch_stage_cumsum(a, (hipStream_t)stream));
+}
+
+int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b, float* W, float* U, int B,
+                 int T, int H, int d_k, int d_v, int dtype, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H * T == 0) return KDA_OK;
+  KDA_REQUIRE(k && v && beta && b && W && U, KDA_ERR_NULL);
+  KDA_REQUIRE(aligned16(k) && aligned16(v) && aligned16(b) && aligned16(W) && aligned16(U), KDA_ERR_ALIGN);
+  kda::StageArgs a{};
+  a.k = k; a.v = v; a.beta = beta; a.b = const_cast<float*>(b); a.W = W; a.U = U;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
+  return hip_status(kda::launch_stage_ut(a, (hipStream_t)stream));
+}
+
+int kda_stage_state(const void* k, const float* b, const float* W, const float* U, const float* S0, float* Delta,
+                    float* S_chunks, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    KDA_REQUIRE(k && b && W && U && Delta && S_chunks, KDA_ERR_NULL);
+    KDA_REQUIRE(aligned16(k) && aligned16(b) && aligned16(W) && aligned16(U) && aligned16(Delta) &&
+                aligned16(S_chunks), KDA_ERR_ALIGN);
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  kda::StageArgs a{};
+  a.k = k; a.b = const_cast<float*>(b); a.W = const_cast<float*>(W); a.U = const_cast<float*>(U);
+  a.S0 = S0; a.Delta = Delta; a.S_chunks = S_chunks; a.S_T = S_T;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
+  return hip_status(kda::launch_stage_state(a, (hipStream_t)stream));
+}
+
+int kda_stage_output(const void* q, const void* k, const float* b, const float* Delta, const float* S_chunks,
+                     void* o, int B, int T, int H, int d_k, int d_v, int dtype, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H * T == 0) return KDA_OK;
+  KDA_REQUIRE(q && k && b && Delta && S_chunks && o, KDA_ERR_NULL);
+  KDA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(b) && aligned16(Delta) && aligned16(S_chunks) &&
+              aligned16(o), KDA_ERR_ALIGN);
+  kda::StageArgs a{};
+  a.q = q; a.k = k; a.b = const_cast<float*>(b); a.Delta = const_cast<float*>(Delta);
+  a.S_chunks = const_cast<float*>(S_chunks); a.o = o;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
+  return hip_status(kda::launch_stage_output(a, (hipStream_t)stream));
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* S,
+                       void* o, int N, int H, int d_k, int d_v, int dtype, void* stream) {
+  int st = check_step_dims(N, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)N * H == 0) return KDA_OK;
+  st = check_tokens(q, k, v, g, beta, o, dtype);
+  if (st) return st;
+  KDA_REQUIRE(S != nullptr, KDA_ERR_NULL);
+  KDA_REQUIRE(aligned16(S), KDA_ERR_ALIGN);
+  kda::DecodeArgs a{q, k, v, g, beta, S, o, N, H, d_k, d_v, dtype == KDA_BF16};
+  return hip_status(kda::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA library: the chunkwise-parallel
+ * gated delta rule with a per-channel forget gate, and its one-token decode
+ * step.
+ *
+ * The operation (pages cited by title):
+ *   "Hybrid Linear Attention Architecture: Making LLM Training and Inference
+ *    More Efficient" §3.3 (the KDA update) and §IV (the chunkwise form);
+ *   "Demystifying Hybrid LLM Architectures: Linear Attention, Residuals, and
+ *    Latent MoE" §2.3 (read-out after the update) and §2.4 (chunked and
+ *    recurrent forms are the same function).
+ * For every sequence (b, h) and token t, with the state S a d_k x d_v fp32
+ * matrix (row = key channel):
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ * g = log(alpha) is the per-channel log forget gate (g <= 0 expected).  No
+ * scaling or normalisation of q or k happens inside; callers pass them as
+ * they want them used.
+ *
+ * Common conventions
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no per-call state.
+ *   - Layouts are row-major and contiguous:
+ *       q, k, g [B, T, H, d_k]   v, o [B, T, H, d_v]   beta [B, T, H]
+ *       S0, S_T [B, H, d_k, d_v] (fp32 always)
+ *     Decode uses the same with (B, T) replaced by N sequences of one token.
+ *   - q, k, v, g, beta and o share one element type `dtype` (KDA_F32 or
+ *     KDA_BF16); the recurrent state and the arithmetic are fp32
+ *     (bf16 operands of matrix products are rounded to nearest even).
+ *   - Every tensor pointer must be 16-byte aligned (beta: aligned to its
+ *     element size).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *     calls return after enqueueing, without synchronising.
+ *   - Supported head sizes: d_k = d_v in {64, 128}, except the chunked
+ *     path with KDA_F32 inputs, which supports d_k = d_v = 64 (its fp32
+ *     operand tiles for 128 do not fit in one CU's LDS).
+ *   - Numerical domain of the chunked path: every channel's log-gate summed
+ *     over any 64 consecutive tokens of a chunk must stay above -80 (decay
+ *     over one chunk >= e^-80); beyond it results may be Inf/NaN.  The decode
+ *     step has no such limit.  NaN/Inf inputs propagate; nothing is checked
+ *     on the device.
+ *
+ * Return values: KDA_OK (0) or a negative kda_status.  No C++ exception
+ * crosses this interface.  On KDA_ERR_HIP the HIP error of the failing call
+ * is kept per thread; kda_status_string(KDA_ERR_HIP) names it.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,       /* a required pointer is NULL                    */
+  KDA_ERR_SHAPE = -2,      /* negative size, or unsupported d_k / d_v        */
+  KDA_ERR_DTYPE = -3,      /* dtype not a kda_dtype, or not supported here   */
+  KDA_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned               */
+  KDA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required        */
+  KDA_ERR_HIP = -6,        /* a HIP launch / runtime call failed             */
+  KDA_ERR_ARG = -7         /* any other invalid argument (e.g. bad option)   */
+} kda_status;
+
+/*
+ * kda_chunk_fwd -- prefill: the whole sequence in chunks of 64 tokens.
+ * ("...Making LLM Training and Inference More Efficient" §IV: recursion
+ * between chunks, parallel work inside a chunk.)
+ *   q,k,v,g,beta  inputs (see layouts above), dtype `dtype`
+ *   S0            initial state [B,H,d_k,d_v] fp32, or NULL for zeros
+ *   o             output [B,T,H,d_v], dtype `dtype`
+ *   S_T           final state [B,H,d_k,d_v] fp32, or NULL to skip writing it.
+ *                 S_T may alias S0 exactly (streaming continuation); no other
+ *                 aliasing between arguments is allowed.
+ *   B, T, H       batch, tokens per sequence (any T >= 0; a partial last
+ *                 chunk is handled; T = 0 copies S0 to S_T), heads
+ *   workspace     scratch of kda_chunk_fwd_workspace_size() bytes, or NULL
+ *                 when that size is 0 (it is 0 for this schedule)
+ * Results do not depend on the chunk length up to rounding, and T calls of
+ * kda_recurrent_step give the same result up to rounding.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S0, void* o, float* S_T,
+                  int B, int T, int H, int d_k, int d_v, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kda_chunk_fwd needs for these sizes (0 = none). */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
+
+/*
+ * kda_recurrent_step -- one decode token for N independent sequences
+ * ("...Linear Attention, Residuals, and Latent MoE" §2.1 / §2.3: constant
+ * per-step cost, retrieve -> erase/write -> read).
+ *   q,k,g [N,H,d_k], v [N,H,d_v], beta [N,H]  (dtype `dtype`)
+ *   S     [N,H,d_k,d_v] fp32, read and overwritten IN PLACE with S_t
+ *   o     [N,H,d_v] output (dtype `dtype`), o = S_t^T q
+ */
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float* S, void* o,
+                       int N, int H, int d_k, int d_v, int dtype, void* stream);
+
+/*
+ * Staged schedule: the same forward as kda_chunk_fwd, run as four separate
+ * kernels with intermediates in a caller-provided workspace (the chunked
+ * method's steps one by one).  Slower than kda_chunk_fwd; it exists so each
+ * step can be checked on its own.  Arguments as kda_chunk_fwd.
+ */
+int kda_chunk_fwd_staged(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* S0, void* o, float* S_T,
+                         int B, int T, int H, int d_k, int d_v, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
+
+/*
+ * The four steps of the staged schedule, callable one at a time.  With
+ * C = 64 and N = ceil(T / 64) chunks, positions r inside a chunk, and
+ * b_r = sum_{m<=r} g_m (cumulative log-gate within the chunk):
+ *
+ *  kda_stage_cumsum: b [B,T,H,d_k] fp32 <- in-chunk inclusive cumsum of g
+ *    ("accumulating gate products in log-space", ...More Efficient §IV).
+ *  kda_stage_ut: per chunk, A = (I + StrictTril(Diag(beta) Kg Kd^T))^-1 with
+ *    Kg = exp(b)*k, Kd = exp(-b)*k, solved by blocked forward substitution;
+ *    W = A Diag(beta) Kg [B,T,H,d_k] fp32 and U = A Diag(beta) V [B,T,H,d_v]
+ *    fp32 (the U, W of the chunk equations in §IV).
+ *  kda_stage_state: sequential over chunks; Delta = U - W S_[n] [B,T,H,d_v]
+ *    fp32, the chunk-entry states S_[n] [B,H,N,d_k,d_v] fp32, and
+ *    S_[n+1] = Diag(exp b_C) S_[n] + (exp(b_C - b) * K)^T Delta; S_T as above.
+ *  kda_stage_output: O = (exp(b)*Q) S_[n] + Tril((exp(b)*Q)(exp(-b)*K)^T) Delta
+ *    (Tril keeps the diagonal), written to o in `dtype`.
+ * All pointers are device pointers; intermediates are fp32 and 16-B aligned.
+ */
+int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k,
+                     int dtype, void* stream);
+int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b,
+                 float* W, float* U, int B, int T, int H, int d_k, int d_v,
+                 int dtype, void* stream);
+int kda_stage_state(const void* k, const float* b, const float* W, const float* U,
+                    const float* S0, float* Delta, float* S_chunks, float* S_T,
+                    int B, int T, int H, int d_k, int d_v, int dtype, void* stream);
+int kda_stage_output(const void* q, const void* k, const float* b, const float* Delta,
+                     const float* S_chunks, void* o, int B, int T, int H, int d_k,
+                     int d_v, int dtype, void* stream);
+
+/* Human-readable text for a status (static storage; never NULL). */
+const char* kda_status_string(int status);
+
+/* The HIP error code of the last KDA_ERR_HIP on this thread (0 if none). */
+int kda_last_hip_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,85 @@
+"""Shared parity helpers for the GPU tests: tolerances and oracle calls.
+
+Tolerances (stated as numbers, applied per call):
+  fp32 inputs : max |err| <= 1e-4 * RMS(o_ref) on o and on S_T
+  bf16 inputs : per-head relative L2 <= 5e-3 on o and on S_T, and
+                max |err| <= 3e-2 * RMS(ref) (o against RMS(o_ref),
+                S_T against RMS(S_T_ref))
+The oracle always receives exact fp64 copies of the values the GPU received.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+FP32_MAX = 1e-4
+BF16_REL_L2 = 5e-3
+BF16_MAX = 3e-2
+
+
+def to64(t):
+    if t is None:
+        return None
+    return t.detach().to("cpu").double().numpy()
+
+
+def rms(x):
+    return float(np.sqrt(np.mean(np.square(x)))) if x.size else 0.0
+
+
+def check_prefill(o_gpu, S_gpu, o_ref, S_ref, dtype, what=""):
+    """o_*: [B,T,H,dv]; S_*: [B,H,dk,dv] (numpy fp64)."""
+    stats = {}
+    if dtype == torch.float32:
+        scale = rms(o_ref)
+        e_o = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+        e_s = float(np.max(np.abs(S_gpu - S_ref))) if S_ref.size else 0.0
+        stats.update(max_err_o=e_o, max_err_S=e_s, rms_o=scale)
+        assert e_o <= FP32_MAX * scale + 1e-30, f"{what}: o max err {e_o:.3e} > 1e-4*RMS {scale:.3e}"
+        assert e_s <= FP32_MAX * max(scale, 1e-30), f"{what}: S_T max err {e_s:.3e} > 1e-4*RMS(o) {scale:.3e}"
+        return stats
+    B, T, H, dv = o_ref.shape
+    worst_o = 0.0
+    for b in range(B):
+        for h in range(H):
+            ref = o_ref[b, :, h]
+            n = np.linalg.norm(ref)
+            if n > 0:
+                worst_o = max(worst_o, float(np.linalg.norm(o_gpu[b, :, h] - ref) / n))
+    worst_s = 0.0
+    for b in range(B):
+        for h in range(H):
+            ref = S_ref[b, h]
+            n = np.linalg.norm(ref)
+            if n > 0:
+                worst_s = max(worst_s, float(np.linalg.norm(S_gpu[b, h] - ref) / n))
+    e_o = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+    e_s = float(np.max(np.abs(S_gpu - S_ref))) if S_ref.size else 0.0
+    stats.update(rel_l2_o=worst_o, rel_l2_S=worst_s, max_err_o=e_o, max_err_S=e_s,
+                 rms_o=rms(o_ref), rms_S=rms(S_ref))
+    assert worst_o <= BF16_REL_L2, f"{what}: per-head rel L2 of o {worst_o:.3e} > 5e-3"
+    assert worst_s <= BF16_REL_L2, f"{what}: per-head rel L2 of S_T {worst_s:.3e} > 5e-3"
+    assert e_o <= BF16_MAX * rms(o_ref), f"{what}: o max err {e_o:.3e} > 3e-2*RMS {rms(o_ref):.3e}"
+    assert e_s <= BF16_MAX * rms(S_ref), f"{what}: S_T max err {e_s:.3e} > 3e-2*RMS {rms(S_ref):.3e}"
+    return stats
+
+
+def oracle_prefill(inp, heads=None, nthreads=0):
+    """Oracle on all heads, or on a list of (b, h) pairs (returned stacked as
+    B' = len(heads) sequences of one head each)."""
+    q, k, v, g, beta, S0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "S0"))
+    if heads is None:
+        return oracle.recurrent_fwd(to64(q), to64(k), to64(v), to64(g), to64(beta), to64(S0), nthreads)
+    sel = lambda t: np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
+    selb = lambda t: np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
+    S0s = None if S0 is None else np.stack([to64(S0[b, h]) for b, h in heads])[:, None]
+    return oracle.recurrent_fwd(sel(q), sel(k), sel(v), sel(g), selb(beta), S0s, nthreads)
+
+
+def pick(o, S, heads):
+    """GPU results of the (b, h) pairs, shaped like oracle_prefill(heads=...)."""
+    o_s = np.stack([to64(o[b, :, h]) for b, h in heads])[:, :, None]
+    S_s = np.stack([to64(S[b, h]) for b, h in heads])[:, None]
+    return o_s, S_s

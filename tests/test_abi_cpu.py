@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every symbol include/kda.h declares,
+and host-side validation rejects bad arguments before any launch.  CPU only:
+no call here reaches a kernel (every one returns from argument checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import gated_delta_rule_61_amd as kda
+    if not os.path.exists(kda.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return kda.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size", "kda_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared():
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.kda_version() == 10000
+    for code in range(0, -8, -1):
+        assert L.kda_status_string(code)
+    assert L.kda_status_string(0) == b"ok"
+
+
+NULL = None
+
+
+def _fwd(L, **kw):
+    a = dict(q=16, k=16, v=16, g=16, beta=16, S0=None, o=16, ST=None, B=1, T=64, H=1, dk=128, dv=128, dt=1)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kda_chunk_fwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["S0"]), p(a["o"]),
+                           p(a["ST"]), a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], None, 0, None)
+
+
+def test_prefill_validation(L):
+    # fake aligned addresses: validation must fail before any launch
+    assert _fwd(L, q=None) == -1
+    assert _fwd(L, dk=96, dv=96) == -2
+    assert _fwd(L, dk=128, dv=64) == -2
+    assert _fwd(L, dt=0, dk=128, dv=128) == -2           # fp32 supports d=64 only
+    assert _fwd(L, dt=7) == -3
+    assert _fwd(L, B=-1) == -2
+    assert _fwd(L, q=18) == -4                          # misaligned
+    assert _fwd(L, beta=17) == -4                       # beta only needs 2-byte alignment
+    assert _fwd(L, B=0) == 0                            # nothing to do: no launch
+    assert _fwd(L, H=0) == 0
+    assert L.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 1) == 0
+
+
+def test_staged_workspace(L):
+    n = L.kda_chunk_fwd_staged_workspace_size(1, 100, 2, 64, 64, 0)
+    tok = 100 * 2
+    assert n >= tok * 64 * 4 * 4 + 2 * 2 * 64 * 64 * 4
+    p = ctypes.c_void_p(16)
+    st = L.kda_chunk_fwd_staged(p, p, p, p, p, None, p, None, 1, 100, 2, 64, 64, 0, None, 0, None)
+    assert st == -5
+    st = L.kda_chunk_fwd_staged(p, p, p, p, p, None, p, None, 1, 100, 2, 64, 64, 0, p, n - 1, None)
+    assert st == -5
+
+
+def test_decode_validation(L):
+    p = ctypes.c_void_p(16)
+    assert L.kda_recurrent_step(p, p, p, p, p, None, p, 4, 2, 128, 128, 1, None) == -1
+    assert L.kda_recurrent_step(p, p, p, p, p, p, p, 4, 2, 100, 100, 1, None) == -2
+    assert L.kda_recurrent_step(p, p, p, p, p, p, p, 4, 2, 128, 128, 5, None) == -3
+    assert L.kda_recurrent_step(p, p, p, p, p, ctypes.c_void_p(20), p, 4, 2, 128, 128, 1, None) == -4
+    assert L.kda_recurrent_step(p, p, p, p, p, p, p, 0, 2, 128, 128, 1, None) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import gated_delta_rule_61_amd as kda
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(kda.KDAError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1), None)

@@ -1,0 +1,96 @@
+"""GPU parity of the one-token decode step against the fp64 oracle, through
+the C ABI.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import BF16_MAX, BF16_REL_L2, FP32_MAX, rms, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_61_amd as kda
+    kda.lib()
+    return kda
+
+
+def _check_step(o_g, o_r, dtype, what):
+    if dtype == torch.float32:
+        assert np.max(np.abs(o_g - o_r)) <= FP32_MAX * rms(o_r), what
+        return
+    N, H, _ = o_r.shape
+    for n in range(N):
+        for h in range(H):
+            den = np.linalg.norm(o_r[n, h])
+            if den > 0:
+                assert np.linalg.norm(o_g[n, h] - o_r[n, h]) / den <= BF16_REL_L2, what
+    assert np.max(np.abs(o_g - o_r)) <= BF16_MAX * rms(o_r), what
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_steps_small(kda, dtype, d):
+    cfg = W.Decode("small", 5, 3, d, d, 12, dtype, 0.05)
+    S = W.decode_state(cfg, device="cuda")
+    tok = W.decode_tokens(cfg, device="cuda")
+    S_ref = to64(S)
+    for t in range(cfg.steps):
+        args = [tok[n][t].contiguous() for n in ("q", "k", "v", "g", "beta")]
+        o = kda.recurrent_step(*args, S)
+        torch.cuda.synchronize()
+        o_r, S_ref = oracle.recurrent_step(*[to64(a) for a in args], S_ref)
+        _check_step(to64(o), o_r, dtype, f"step {t}")
+    err = np.max(np.abs(to64(S) - S_ref))
+    assert err <= 1e-5 * rms(S_ref), err
+
+
+def test_decode_workload_256x32_sampled(kda):
+    """The decode workload at full size (256 sequences x 32 heads, 64 steps);
+    every step's o and the final state of sampled heads against the oracle."""
+    cfg = W.DECODE_256x32
+    S = W.decode_state(cfg, device="cuda")
+    tok = W.decode_tokens(cfg, device="cuda")
+    picks = [(0, 0), (17, 5), (255, 31), (128, 16), (77, 3), (200, 30)]
+    S_ref = np.stack([to64(S[n, h]) for n, h in picks])[:, None]
+    for t in range(cfg.steps):
+        args = [tok[n][t] for n in ("q", "k", "v", "g", "beta")]
+        o = kda.recurrent_step(*args, S)
+        sel = [np.stack([to64(a[n, h]) for n, h in picks])[:, None] for a in args]
+        o_r, S_ref = oracle.recurrent_step(*sel, S_ref)
+        torch.cuda.synchronize()
+        o_g = np.stack([to64(o[n, h]) for n, h in picks])[:, None]
+        _check_step(o_g, o_r, torch.bfloat16, f"step {t}")
+    S_g = np.stack([to64(S[n, h]) for n, h in picks])[:, None]
+    for i in range(len(picks)):
+        assert np.linalg.norm(S_g[i] - S_ref[i]) / np.linalg.norm(S_ref[i]) <= BF16_REL_L2
+    assert torch.isfinite(S).all()
+
+
+def test_decode_matches_prefill(kda):
+    """T decode steps and one prefill over the same tokens agree (both vs the
+    oracle, and with each other within the bf16 bounds)."""
+    cfg = W.PREFILL_BF16_H16_T4K
+    inp = W.prefill_inputs(cfg, device="cuda", seed=8, B=2, T=70, H=3)
+    o_p, S_p = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(70):
+        outs.append(kda.recurrent_step(*(inp[n][:, t].contiguous() for n in ("q", "k", "v", "g", "beta")), S))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, 1)
+    rel = (o_d.float() - o_p.float()).norm() / o_p.float().norm()
+    assert rel < 5e-3
+    assert ((S - S_p).norm() / S_p.norm()) < 5e-3
+
+
+def test_zero_sequences_is_noop(kda):
+    z = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((0, 4, 128, 128), dtype=torch.float32, device="cuda")
+    o = kda.recurrent_step(z, z, z, z, torch.empty((0, 4), dtype=torch.bfloat16, device="cuda"), S)
+    assert o.shape == (0, 4, 128)
