@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill over the B=8, H=32, T=8192, d=128 bf16
+workload (kda_chunk_fwd, S0 = 0, o bf16 + S_T fp32) followed by 64 decode
+tokens for 256 sequences x 32 heads (kda_recurrent_step, fp32 state updated
+in place).  Inputs are synthetic (seeded, see workloads/) and resident in HBM
+before timing starts.  Prints ONE JSON line:
+  value         prefill tokens/s (B*T tokens per prefill call)
+  decode        decode tokens/s (256 sequences x 64 tokens per step) + roofline
+  roofline      the fused prefill kernel against the HBM bound
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same work
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, TFLOP/s
+
+# Algorithmic work per token and head (d_k = d_v = 128, chunk 64, bf16 I/O):
+#   bytes: q, k, v, g (4 x 256) + beta (2) + o (256) = 1282
+#   flops: 6 d^2 + (C+1) 4d + (C-1) d + C^2/3 + d^2/C  (triangles counted once)
+D = 128
+C = 64
+PREFILL_BYTES_PER_TOKHEAD = 4 * D * 2 + 2 + D * 2
+PREFILL_FLOPS_PER_TOKHEAD = 6 * D * D + (C + 1) * 4 * D + (C - 1) * D + C * C / 3 + D * D / C
+STATE_BYTES = D * D * 4
+DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKHEAD   # state read + write + token I/O
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (used for profiler runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_61_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(W, oracle, torch):
+    """The fp64 oracle on the prefill workload's inputs (all 8 x 32 sequences
+    of 8192 tokens), timed on the host cores."""
+    cfg = W.PREFILL_BF16_B8_H32_T8K
+    inp = W.prefill_inputs(cfg, device="cuda")
+    f64 = lambda t: None if t is None else t.detach().cpu().double().numpy()
+    args = [f64(inp[n]) for n in ("q", "k", "v", "g", "beta", "S0")]
+    del inp
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.recurrent_fwd(*args, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tokens = cfg.B * cfg.T
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole prefill workload (B={cfg.B}, H={cfg.H}, T={cfg.T}, d=128) once, "
+                      f"fp64 token recurrence, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calibrate_copy:
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        y = torch.empty_like(x)
+        x.fill_(1.0)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
+        return
+    import gated_delta_rule_61_amd as kda
+    import workloads as W
+
+    if not os.path.exists(kda.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    pcfg = W.PREFILL_BF16_B8_H32_T8K
+    dcfg = W.DECODE_256x32
+    inp = W.prefill_inputs(pcfg, device="cuda")
+    o = torch.empty_like(inp["v"])
+    S_T = torch.empty(pcfg.B, pcfg.H, D, D, dtype=torch.float32, device="cuda")
+    S = W.decode_state(dcfg, device="cuda")
+    tok = W.decode_tokens(dcfg, device="cuda")
+    steps_tok = [[tok[n][t] for n in ("q", "k", "v", "g", "beta")] for t in range(dcfg.steps)]
+    od = torch.empty(dcfg.N, dcfg.H, D, dtype=torch.bfloat16, device="cuda")
+
+    def prefill():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T)
+
+    def decode():
+        for t in range(dcfg.steps):
+            kda.recurrent_step(*steps_tok[t], S, o=od)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        decode()
+        e2.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    pre_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    dec_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    BTH = pcfg.B * pcfg.T * pcfg.H
+    pre_bytes = BTH * PREFILL_BYTES_PER_TOKHEAD + pcfg.B * pcfg.H * STATE_BYTES   # + S_T write
+    pre_flops = BTH * PREFILL_FLOPS_PER_TOKHEAD
+    pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
+    digest = source_digest()
+    step_heads = dcfg.N * dcfg.H
+    dec_step_ms = dec_avg / dcfg.steps
+    dec_gbs = step_heads * DECODE_BYTES_PER_HEAD / (dec_step_ms * 1e-3) / 1e9
+
+    def traffic(kernel):
+        t = measured_traffic(kernel, digest)
+        return None if t is None else float(t)
+
+    line = {
+        "metric": "KDA prefill tokens/s and decode tokens/s, % of MFMA/HBM roofline",
+        "value": pcfg.B * pcfg.T / (pre_avg * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
+                "g=-softplus(N(-3,1)))",
+        "config": {"workload": "kda_chunk_fwd B8 H32 T8192 d128 bf16 (S0=0) + "
+                               "kda_recurrent_step 256x32 d128 x64 tokens",
+                   "prefill_ms": pre_avg, "decode_ms_per_token_step": dec_step_ms},
+        "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic("fused_fwd_kernel"),
+                     "kernel": "fused_fwd_kernel<bf16,128,128,1>",
+                     "mfma_frac_algorithmic": pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "decode": {"value": dcfg.N * dcfg.steps / (dec_avg * 1e-3), "unit": "tokens/s",
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic("decode_kernel"),
+                                "kernel": "decode_kernel<bf16,128,128>"}},
+    }
+    del inp, o, S, tok, steps_tok
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline(W, oracle, torch)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

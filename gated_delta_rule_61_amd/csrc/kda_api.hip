@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_launch.hpp"
 
 namespace {

@@ -20,6 +20,9 @@ namespace kda {
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 
@@ -27,10 +30,12 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(f16 x) { return static_cast<float>(x); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return static_cast<f16>(x); }
 
 // Per-type operand fragments and MFMA wrappers.
 template <typename T> struct Mma;
@@ -38,10 +43,10 @@ template <typename T> struct Mma;
 template <> struct Mma<bf16> {
   typedef bf16x4 F16;   // operand fragment of a 16-index slab
   typedef bf16x8 F32;   // operand fragment of a 32-index slab
-  static __device__ __forceinline__ F16 f16(floatx4 a) {
+  static __device__ __forceinline__ F16 frag16(floatx4 a) {
     F16 r; r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3]; return r;
   }
-  static __device__ __forceinline__ F32 f32(floatx4 a, floatx4 b) {
+  static __device__ __forceinline__ F32 frag32(floatx4 a, floatx4 b) {
     F32 r;
     r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3];
     r[4] = (bf16)b[0]; r[5] = (bf16)b[1]; r[6] = (bf16)b[2]; r[7] = (bf16)b[3];
@@ -62,11 +67,37 @@ template <> struct Mma<bf16> {
   }
 };
 
+template <> struct Mma<f16> {
+  typedef f16x4 F16;
+  typedef f16x8 F32;
+  static __device__ __forceinline__ F16 frag16(floatx4 a) {
+    F16 r; r[0] = (_Float16)a[0]; r[1] = (_Float16)a[1]; r[2] = (_Float16)a[2]; r[3] = (_Float16)a[3]; return r;
+  }
+  static __device__ __forceinline__ F32 frag32(floatx4 a, floatx4 b) {
+    F32 r;
+    r[0] = (_Float16)a[0]; r[1] = (_Float16)a[1]; r[2] = (_Float16)a[2]; r[3] = (_Float16)a[3];
+    r[4] = (_Float16)b[0]; r[5] = (_Float16)b[1]; r[6] = (_Float16)b[2]; r[7] = (_Float16)b[3];
+    return r;
+  }
+  static __device__ __forceinline__ F32 lds32(const _Float16* p) {
+    F16 lo = *reinterpret_cast<const F16*>(p);
+    F16 hi = *reinterpret_cast<const F16*>(p + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  static __device__ __forceinline__ F16 lds16(const _Float16* p) { return *reinterpret_cast<const F16*>(p); }
+  static __device__ __forceinline__ floatx4 mma32(F32 a, F32 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 mma16(F16 a, F16 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+
 template <> struct Mma<float> {
   typedef floatx4 F16;
   typedef floatx8 F32;
-  static __device__ __forceinline__ F16 f16(floatx4 a) { return a; }
-  static __device__ __forceinline__ F32 f32(floatx4 a, floatx4 b) {
+  static __device__ __forceinline__ F16 frag16(floatx4 a) { return a; }
+  static __device__ __forceinline__ F32 frag32(floatx4 a, floatx4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   static __device__ __forceinline__ F32 lds32(const float* p) {
@@ -107,5 +138,17 @@ __device__ __forceinline__ Vec16 ldg16(const void* p) {
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// Matrix-operand types of the chunked forward, per input type T.
+//   TL: products whose operands carry gate factors of the whole chunk or the
+//       recurrent state (Kg Kd^T, Qg Kd^T, Qg S, W S) -- bf16 for bf16 inputs,
+//       whose 8-bit exponent covers factors up to e^+-80 and any state size.
+//   TF: products of bounded operands (forward substitution with L and the
+//       diagonal-block inverses, Tril(Qg Kd^T) Delta, Kb^T Delta) -- fp16 for
+//       bf16 inputs: 3 more mantissa bits at the same MFMA rate.
+// fp32 inputs keep every operand in fp32.
+template <typename T> struct Operands;
+template <> struct Operands<bf16> { typedef bf16 TL; typedef f16 TF; };
+template <> struct Operands<float> { typedef float TL; typedef float TF; };
 
 }  // namespace kda

@@ -76,8 +76,10 @@ struct Layout {
 template <typename T, int DK, int DVW>
 struct Smem {
   typedef Layout<T, DK, DVW> Lay;
-  T* Kt; T* Kh; T* Wn; T* Qt; T* KbT; T* V;
-  float* G; T* Ln; T* P; float* Ld; T* Db;
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  TL* Kt; TL* Kh; TL* Wn; TL* Qt; TF* KbT; T* V;
+  float* G; TF* Ln; TF* P; float* Ld; TF* Db;
   float* tot; float* beta; float* gam; float* bC;
   // `opaque` is an offset the compiler cannot see through (zero at run time):
   // rebuilding the view with it every chunk keeps LDS address arithmetic
@@ -92,17 +94,17 @@ struct Smem {
     set(base0 + opq);
   }
   __device__ __forceinline__ void set(unsigned char* base) {
-    Kt = reinterpret_cast<T*>(base + Lay::O_KT);
-    Kh = reinterpret_cast<T*>(base + Lay::O_KH);
+    Kt = reinterpret_cast<TL*>(base + Lay::O_KT);
+    Kh = reinterpret_cast<TL*>(base + Lay::O_KH);
     Wn = Kh;
-    Qt = reinterpret_cast<T*>(base + Lay::O_QT);
-    KbT = reinterpret_cast<T*>(base + Lay::O_KBT);
+    Qt = reinterpret_cast<TL*>(base + Lay::O_QT);
+    KbT = reinterpret_cast<TF*>(base + Lay::O_KBT);
     V = reinterpret_cast<T*>(base + Lay::O_V);
     G = reinterpret_cast<float*>(base + Lay::O_G);
-    Ln = reinterpret_cast<T*>(base + Lay::O_LN);
-    P = reinterpret_cast<T*>(base + Lay::O_P);
+    Ln = reinterpret_cast<TF*>(base + Lay::O_LN);
+    P = reinterpret_cast<TF*>(base + Lay::O_P);
     Ld = reinterpret_cast<float*>(base + Lay::O_LD);
-    Db = reinterpret_cast<T*>(base + Lay::O_DB);
+    Db = reinterpret_cast<TF*>(base + Lay::O_DB);
     tot = reinterpret_cast<float*>(base + Lay::O_TOT);
     beta = reinterpret_cast<float*>(base + Lay::O_BETA);
     gam = reinterpret_cast<float*>(base + Lay::O_GAM);
@@ -271,16 +273,18 @@ __device__ __forceinline__ void apply_gates(Smem<T, DK, DVW>& sm, const Vec16* k
       float kf[RV::VN], qf[RV::VN];
       vec_to_f32<T>(kq[i], kf);
       if (DO_QT) vec_to_f32<T>(qq[i], qf);
-      T kt[RV::VN], kh[RV::VN], qt[RV::VN];
+      typedef typename Operands<T>::TL TL;
+      typedef typename Operands<T>::TF TF;
+      TL kt[RV::VN], kh[RV::VN], qt[RV::VN];
 #pragma unroll
       for (int e = 0; e < RV::VN; ++e) {
         const float b = sm.G[row * Lay::LDG + c0 + e];
         const float ep = fast_exp(b);
         const float em = fast_exp(-b);
-        kt[e] = from_f32<T>(kf[e] * ep);
-        kh[e] = from_f32<T>(kf[e] * em);
-        if (DO_QT) qt[e] = from_f32<T>(qf[e] * ep);
-        if (DO_KB) sm.KbT[(c0 + e) * Lay::LDC + row] = from_f32<T>(kf[e] * fast_exp(sm.bC[c0 + e] - b));
+        kt[e] = from_f32<TL>(kf[e] * ep);
+        kh[e] = from_f32<TL>(kf[e] * em);
+        if (DO_QT) qt[e] = from_f32<TL>(qf[e] * ep);
+        if (DO_KB) sm.KbT[(c0 + e) * Lay::LDC + row] = from_f32<TF>(kf[e] * fast_exp(sm.bC[c0 + e] - b));
       }
       if (DO_KT) *reinterpret_cast<Vec16*>(&sm.Kt[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kt);
       if (DO_KH) *reinterpret_cast<Vec16*>(&sm.Kh[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kh);
@@ -316,7 +320,9 @@ __device__ __forceinline__ void blk_ij(int t, int& I, int& J) {
 // in T) and/or P = Tril(Qt Kh^T) (T), distributed over the wavefronts.
 template <typename T, int DK, int DVW, bool DO_L, bool DO_P>
 __device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, int wave, int lane) {
-  typedef Mma<T> M;
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TL> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
   constexpr int NL = DO_L ? 10 : 0;
@@ -327,7 +333,7 @@ __device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, int wave, int lan
     blk_ij(isL ? tile : tile - NL, I, J);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     if (I >= J) {
-      const T* A = isL ? sm.Kt : sm.Qt;
+      const TL* A = isL ? sm.Kt : sm.Qt;
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const typename M::F32 af = M::lds32(A + (16 * I + l16) * Lay::LDK + 32 * ks + 4 * g4);
@@ -346,12 +352,12 @@ __device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, int wave, int lan
           if (il <= l16) val = 0.f;
           sm.Ld[(I * 16 + il) * Lay::LDL + l16] = val;
         } else {
-          sm.Ln[i * Lay::LDC + jc] = from_f32<T>(-val);
+          sm.Ln[i * Lay::LDC + jc] = from_f32<TF>(-val);
         }
       } else {
         if (I == J && il < l16) val = 0.f;
         if (I < J) val = 0.f;
-        sm.P[i * Lay::LDC + jc] = from_f32<T>(val);
+        sm.P[i * Lay::LDC + jc] = from_f32<TF>(val);
       }
     }
   }
@@ -382,17 +388,17 @@ __device__ __forceinline__ void diag_inverse(Smem<T, DK, DVW>& sm, int lane) {
     if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sm.Db[(blk * 16 + r) * Lay::LDD + c] = from_f32<T>(x[r]);
+  for (int r = 0; r < 16; ++r) sm.Db[(blk * 16 + r) * Lay::LDD + c] = from_f32<typename Operands<T>::TF>(x[r]);
 }
 
 // Blocked forward substitution for one 16-column tile:
 //   X_I = D_I (beta * Src_I - sum_{M<I} L_IM X_M),  I = 0..3,
 // Src rows from LDS (ld = row stride, col0 = first column).  X stays in
 // registers (C layout, fp32).
-template <typename T, int DK, int DVW>
-__device__ __forceinline__ void fwd_subst_tile(Smem<T, DK, DVW>& sm, const T* src, int ld, int col0,
+template <typename T, int DK, int DVW, typename TS>
+__device__ __forceinline__ void fwd_subst_tile(Smem<T, DK, DVW>& sm, const TS* src, int ld, int col0,
                                                floatx4 (&X)[4], int lane) {
-  typedef Mma<T> M;
+  typedef Mma<typename Operands<T>::TF> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -407,10 +413,10 @@ __device__ __forceinline__ void fwd_subst_tile(Smem<T, DK, DVW>& sm, const T* sr
 #pragma unroll
     for (int Mb = 0; Mb < I; ++Mb) {
       const typename M::F16 af = M::lds16(sm.Ln + (16 * I + l16) * Lay::LDC + 16 * Mb + 4 * g4);
-      acc = M::mma16(af, M::f16(X[Mb]), acc);
+      acc = M::mma16(af, M::frag16(X[Mb]), acc);
     }
     const typename M::F16 df = M::lds16(sm.Db + (16 * I + l16) * Lay::LDD + 4 * g4);
-    X[I] = M::mma16(df, M::f16(acc), zero);
+    X[I] = M::mma16(df, M::frag16(acc), zero);
   }
 }
 
@@ -423,14 +429,14 @@ __device__ __forceinline__ void store_negw(Smem<T, DK, DVW>& sm, const floatx4 (
   for (int I = 0; I < 4; ++I)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      sm.Wn[(16 * I + 4 * g4 + j) * Lay::LDK + col0 + l16] = from_f32<T>(-X[I][j]);
+      sm.Wn[(16 * I + 4 * g4 + j) * Lay::LDK + col0 + l16] = from_f32<typename Operands<T>::TL>(-X[I][j]);
 }
 
 // State as reduction operand: fragments of 32 state rows (key channels).
-template <typename T, int DK>
-__device__ __forceinline__ void state_frags(const floatx4 (&S)[DK / 16], typename Mma<T>::F32 (&Sf)[DK / 32]) {
+template <typename TO, int DK>
+__device__ __forceinline__ void state_frags(const floatx4 (&S)[DK / 16], typename Mma<TO>::F32 (&Sf)[DK / 32]) {
 #pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) Sf[ks] = Mma<T>::f32(S[2 * ks], S[2 * ks + 1]);
+  for (int ks = 0; ks < DK / 32; ++ks) Sf[ks] = Mma<TO>::frag32(S[2 * ks], S[2 * ks + 1]);
 }
 
 // acc[I] (+)= A[rows 16I..] @ S  for the four 16-token row blocks, A in LDS [C][LDK].
@@ -448,9 +454,10 @@ __device__ __forceinline__ void rows_times_state(const T* A, int lda, const type
 
 // O[I] += P[rows 16I..] @ Delta  (P lower triangular: slab 1 only for I >= 2)
 template <typename T, int DK, int DVW>
-__device__ __forceinline__ void intra_output(Smem<T, DK, DVW>& sm, const typename Mma<T>::F32 (&Df)[2],
+__device__ __forceinline__ void intra_output(Smem<T, DK, DVW>& sm,
+                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[2],
                                              floatx4 (&O)[4], int lane) {
-  typedef Mma<T> M;
+  typedef Mma<typename Operands<T>::TF> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
@@ -462,9 +469,10 @@ __device__ __forceinline__ void intra_output(Smem<T, DK, DVW>& sm, const typenam
 
 // S <- Diag(gam) S + KbT @ Delta
 template <typename T, int DK, int DVW>
-__device__ __forceinline__ void state_update(Smem<T, DK, DVW>& sm, const typename Mma<T>::F32 (&Df)[2],
+__device__ __forceinline__ void state_update(Smem<T, DK, DVW>& sm,
+                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[2],
                                              floatx4 (&S)[DK / 16], int lane) {
-  typedef Mma<T> M;
+  typedef Mma<typename Operands<T>::TF> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
@@ -565,7 +573,10 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<T, DK, DV, DVW>& rg, const
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV, int NSPLIT>
 __global__ __launch_bounds__(NT) void fused_fwd_kernel(PrefillArgs a) {
-  typedef Mma<T> M;
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TL> ML;
+  typedef Mma<TF> MF;
   constexpr int DVW = DV / NSPLIT;
   constexpr int OWN = DVW / 16;
   typedef Layout<T, DK, DVW> Lay;
@@ -635,17 +646,17 @@ __global__ __launch_bounds__(NT) void fused_fwd_kernel(PrefillArgs a) {
     KDA_FRESH_LANE();
 
     if (owner) {
-      typename M::F32 Sf[DK / 32];
-      state_frags<T, DK>(S, Sf);
+      typename ML::F32 Sf[DK / 32];
+      state_frags<TL, DK>(S, Sf);
       // read-out of the chunk-entry state, O = Qt S, and Delta = U - W S
       floatx4 O[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) O[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      rows_times_state<T, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
-      rows_times_state<T, DK>(sm.Wn, Lay::LDK, Sf, Ux, lane);
-      typename M::F32 Df[2];
-      Df[0] = M::f32(Ux[0], Ux[1]);
-      Df[1] = M::f32(Ux[2], Ux[3]);
+      rows_times_state<TL, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
+      rows_times_state<TL, DK>(sm.Wn, Lay::LDK, Sf, Ux, lane);
+      typename MF::F32 Df[2];
+      Df[0] = MF::frag32(Ux[0], Ux[1]);
+      Df[1] = MF::frag32(Ux[2], Ux[3]);
       intra_output<T, DK, DVW>(sm, Df, O, lane);
       {
         const __amdgpu_buffer_rsrc_t ro =
@@ -755,7 +766,10 @@ __global__ __launch_bounds__(NT) void stage_ut_kernel(StageArgs a) {
 // Sequential state pass.  grid (B*H*NSPLIT) with the fused kernel's mapping.
 template <typename T, int DK, int DV, int NSPLIT>
 __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
-  typedef Mma<T> M;
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TL> ML;
+  typedef Mma<TF> MF;
   constexpr int DVW = DV / NSPLIT;
   constexpr int OWN = DVW / 16;
   typedef Layout<T, DK, DVW> Lay;
@@ -785,7 +799,7 @@ __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
     for (int idx = tid; idx < C * DK; idx += NT) {
       const int row = idx / DK, c = idx % DK;
       const float w = row < nv ? a.W[(ti.row0 + (int64_t)row * ti.rstride) * DK + c] : 0.f;
-      sm.Wn[row * Lay::LDK + c] = from_f32<T>(-w);
+      sm.Wn[row * Lay::LDK + c] = from_f32<TL>(-w);
     }
     __syncthreads();
     apply_gates<T, DK, DVW, false, false, false, true>(sm, kr, kr, tid);
@@ -797,17 +811,17 @@ __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
       for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + wcol + l16] = S[rt][j];
-      typename M::F32 Sf[DK / 32];
-      state_frags<T, DK>(S, Sf);
+      typename ML::F32 Sf[DK / 32];
+      state_frags<TL, DK>(S, Sf);
       floatx4 Dx[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) Dx[I] = load_tile_rows_f32<T>(a.U, DV, ti, I, wcol + l16, nv, lane);
-      rows_times_state<T, DK>(sm.Wn, Lay::LDK, Sf, Dx, lane);
+      rows_times_state<TL, DK>(sm.Wn, Lay::LDK, Sf, Dx, lane);
 #pragma unroll
       for (int I = 0; I < 4; ++I) store_tile_rows<float>(a.Delta, DV, ti, I, wcol + l16, Dx[I], nv, lane);
-      typename M::F32 Df[2];
-      Df[0] = M::f32(Dx[0], Dx[1]);
-      Df[1] = M::f32(Dx[2], Dx[3]);
+      typename MF::F32 Df[2];
+      Df[0] = MF::frag32(Dx[0], Dx[1]);
+      Df[1] = MF::frag32(Dx[2], Dx[3]);
       state_update<T, DK, DVW>(sm, Df, S, lane);
     }
   }
@@ -817,7 +831,10 @@ __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
 // O = Qt S_[n] + Tril(Qt Kh^T) Delta.  grid (chunks, B*H)
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
-  typedef Mma<T> M;
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TL> ML;
+  typedef Mma<TF> MF;
   typedef Layout<T, DK, DV> Lay;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Smem<T, DK, DV> sm(smem_raw);
@@ -847,18 +864,18 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[rt][j] = Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + col];
-    typename M::F32 Sf[DK / 32];
-    state_frags<T, DK>(S, Sf);
+    typename ML::F32 Sf[DK / 32];
+    state_frags<TL, DK>(S, Sf);
     floatx4 O[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) O[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-    rows_times_state<T, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
+    rows_times_state<TL, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
     floatx4 Dx[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) Dx[I] = load_tile_rows_f32<T>(a.Delta, DV, ti, I, col, nv, lane);
-    typename M::F32 Df[2];
-    Df[0] = M::f32(Dx[0], Dx[1]);
-    Df[1] = M::f32(Dx[2], Dx[3]);
+    typename MF::F32 Df[2];
+    Df[0] = MF::frag32(Dx[0], Dx[1]);
+    Df[1] = MF::frag32(Dx[2], Dx[3]);
     intra_output<T, DK, DV>(sm, Df, O, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) store_tile_rows<T>(reinterpret_cast<T*>(a.o), DV, ti, I, col, O[I], nv, lane);

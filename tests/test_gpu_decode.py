@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import BF16_MAX, BF16_REL_L2, FP32_MAX, rms, to64
+from tests.parity import BF16_MAX, BF16_REL_L2, BF16_U, FP32_MAX, rms, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,8 @@ def _check_step(o_g, o_r, dtype, what):
             den = np.linalg.norm(o_r[n, h])
             if den > 0:
                 assert np.linalg.norm(o_g[n, h] - o_r[n, h]) / den <= BF16_REL_L2, what
-    assert np.max(np.abs(o_g - o_r)) <= BF16_MAX * rms(o_r), what
+    # error beyond the bf16 output's own rounding (see tests/parity.py)
+    assert np.max(np.abs(o_g - o_r) - BF16_U * np.abs(o_r)) <= BF16_MAX * rms(o_r), what
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
