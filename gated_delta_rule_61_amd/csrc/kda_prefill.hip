@@ -36,11 +36,19 @@ namespace kda {
 constexpr int C = 64;        // chunk length
 constexpr int NW = 8;        // wavefronts per workgroup
 constexpr int NT = NW * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // LDS layout.  Rows of bf16/fp32 operand arrays are padded by 16 bytes so that
 // the 16 rows an MFMA fragment read touches fall in different banks.
 // ---------------------------------------------------------------------------
+// State columns per owner wavefront: 32 (two 16-wide MFMA tiles sharing
+// every A operand read) when the workgroup has at least 32 columns.
+template <int DVW> struct StateTiles {
+  static constexpr int NTILE = DVW >= 32 ? 2 : 1;
+  static constexpr int OWN = DVW / (16 * NTILE);        // owner wavefronts
+};
+
 template <typename T, int DK, int DVW>
 struct Layout {
   static constexpr int PE = 16 / (int)sizeof(T);
@@ -56,7 +64,7 @@ struct Layout {
   static constexpr int O_KH = O_KT + SZ_CK;            // later reused for -W
   static constexpr int O_QT = O_KH + SZ_CK;
   static constexpr int O_KBT = O_QT + SZ_CK;
-  static constexpr int O_V = O_KBT + DK * LDC * (int)sizeof(T);
+  static constexpr int O_V = O_KBT + DK * C * (int)sizeof(T);      // Kb^T: unpadded, swizzled
   static constexpr int O_G = O_V + C * LDV * (int)sizeof(T);
   static constexpr int SZ_GATE = C * LDG * 4;
   static constexpr int SZ_LP = 2 * C * LDC * (int)sizeof(T) + 4 * 16 * LDL * 4 + 4 * 16 * LDD * (int)sizeof(T);
@@ -70,7 +78,10 @@ struct Layout {
   static constexpr int O_BETA = O_TOT + NSEG * DK * 4;
   static constexpr int O_GAM = O_BETA + C * 4;
   static constexpr int O_BC = O_GAM + DK * 4;
-  static constexpr int BYTES = O_BC + DK * 4;
+  // per owner wavefront: its 64 x (16*NTILE) output block, rows padded by 8 bytes
+  static constexpr int LDS_O = 16 * StateTiles<DVW>::NTILE + 8 / (int)sizeof(T);
+  static constexpr int O_STG = O_BC + DK * 4;
+  static constexpr int BYTES = O_STG + StateTiles<DVW>::OWN * C * LDS_O * (int)sizeof(T);
 };
 
 template <typename T, int DK, int DVW>
@@ -81,6 +92,7 @@ struct Smem {
   TL* Kt; TL* Kh; TL* Wn; TL* Qt; TF* KbT; T* V;
   float* G; TF* Ln; TF* P; float* Ld; TF* Db;
   float* tot; float* beta; float* gam; float* bC;
+  T* stg;
   // `opaque` is an offset the compiler cannot see through (zero at run time):
   // rebuilding the view with it every chunk keeps LDS address arithmetic
   // inside the chunk loop instead of pinning one register per address.
@@ -109,8 +121,16 @@ struct Smem {
     beta = reinterpret_cast<float*>(base + Lay::O_BETA);
     gam = reinterpret_cast<float*>(base + Lay::O_GAM);
     bC = reinterpret_cast<float*>(base + Lay::O_BC);
+    stg = reinterpret_cast<T*>(base + Lay::O_STG);
   }
 };
+
+// Kb^T is stored [d_k][C] without padding; token t of channel c sits at column
+// t ^ kb_swz(c).  The XOR moves whole 4-token groups, so MFMA operand reads
+// (4 consecutive tokens) stay contiguous, while the transposed 2-byte writes of
+// one wavefront (16 channels x 4 tokens) and the operand reads (16 channels x
+// 2 token groups) each land in distinct LDS banks.
+__device__ __forceinline__ int kb_swz(int c) { return 4 * ((3 * (c >> 3) + 2 * (c & 7)) & 15); }
 
 // ---------------------------------------------------------------------------
 // Global -> register staging of one chunk of one head.
@@ -203,17 +223,67 @@ struct ChunkRegs {
   Vec16 k[RowVecs<T, DK>::PER];
   Vec16 g[RowVecs<T, DK>::PER];
   Vec16 v[RowVecs<T, DVW>::PER];
-  float beta;
+  uint32_t beta_bits;   // raw bits: converting at load time would wait for the whole prefetch
 };
+
+template <typename T> __device__ __forceinline__ float bits_to_f32(uint32_t u);
+template <> __device__ __forceinline__ float bits_to_f32<bf16>(uint32_t u) { return __uint_as_float(u << 16); }
+template <> __device__ __forceinline__ float bits_to_f32<float>(uint32_t u) { return __uint_as_float(u); }
 
 // ---------------------------------------------------------------------------
 // Device blocks of the chunk computation.
 // ---------------------------------------------------------------------------
 
 // g (registers) -> G (fp32 LDS); beta -> LDS.
+// Column order of the fp32 gate rows in LDS.  With d_k = 128 and 8 channels
+// per thread, channel c = 8a + 4b + r is stored at 64b + 4a + r: the first
+// halves of all 16 channel groups of a row are contiguous, then the second
+// halves, so each 16-byte access of the 16 lanes of a row hits 64 distinct
+// banks.  Other shapes keep the natural order.
+template <int DK, int VN> struct GateCols {
+  static constexpr bool PERM = (DK == 128 && VN == 8);
+  static __device__ __forceinline__ int pos(int c) {
+    return PERM ? (((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3)) : c;
+  }
+  static __device__ __forceinline__ int chan(int j) {   // inverse of pos
+    return PERM ? (((j & 63) >> 2) * 8 + (j >> 6) * 4 + (j & 3)) : j;
+  }
+};
+
+// The 8 (or 4) gates of one thread's vector: two (one) 16-byte LDS accesses.
+template <int DK, int VN>
+__device__ __forceinline__ void gate_store(float* row, int c0, const float* f) {
+  if constexpr (GateCols<DK, VN>::PERM) {
+    const int a = c0 >> 3;
+    *reinterpret_cast<floatx4*>(row + 4 * a) = floatx4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<floatx4*>(row + 64 + 4 * a) = floatx4{f[4], f[5], f[6], f[7]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < VN; ++e) row[c0 + e] = f[e];
+  }
+}
+template <int DK, int VN>
+__device__ __forceinline__ void gate_load(const float* row, int c0, float* f) {
+  if constexpr (GateCols<DK, VN>::PERM) {
+    const int a = c0 >> 3;
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(row + 4 * a);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(row + 64 + 4 * a);
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < VN; ++e) f[e] = row[c0 + e];
+  }
+}
+
+// 2^x by the hardware instruction (results below the fp32 normal range
+// flush towards zero, which is below every tolerance here).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// g (registers) -> G (fp32 LDS, multiplied by `scale`); beta -> LDS.
 template <typename T, int DK, int DVW>
 __device__ __forceinline__ void stage_gates(Smem<T, DK, DVW>& sm, const Vec16* g,
-                                            float beta, int tid) {
+                                            float beta, int tid, float scale) {
   typedef RowVecs<T, DK> RV;
   typedef Layout<T, DK, DVW> Lay;
 #pragma unroll
@@ -224,7 +294,8 @@ __device__ __forceinline__ void stage_gates(Smem<T, DK, DVW>& sm, const Vec16* g
       float f[RV::VN];
       vec_to_f32<T>(g[i], f);
 #pragma unroll
-      for (int e = 0; e < RV::VN; ++e) sm.G[row * Lay::LDG + c0 + e] = f[e];
+      for (int e = 0; e < RV::VN; ++e) f[e] *= scale;
+      gate_store<DK, RV::VN>(&sm.G[row * Lay::LDG], c0, f);
     }
   }
   if (tid < C) sm.beta[tid] = beta;
@@ -253,9 +324,11 @@ __device__ __forceinline__ void chunk_cumsum(Smem<T, DK, DVW>& sm, int tid) {
 #pragma unroll
   for (int r = 0; r < RPS; ++r) sm.G[(seg * RPS + r) * Lay::LDG + c] += off;
   if (seg == NSEG - 1) {
+    // this thread scanned physical column c; record its channel's totals
+    const int ch = GateCols<DK, VecTraits<T>::N>::chan(c);
     const float bl = run + off;
-    sm.bC[c] = bl;
-    sm.gam[c] = fast_exp(bl);
+    sm.bC[ch] = bl;
+    sm.gam[ch] = hw_exp2(bl);
   }
 }
 
@@ -276,15 +349,20 @@ __device__ __forceinline__ void apply_gates(Smem<T, DK, DVW>& sm, const Vec16* k
       typedef typename Operands<T>::TL TL;
       typedef typename Operands<T>::TF TF;
       TL kt[RV::VN], kh[RV::VN], qt[RV::VN];
+      float bv[RV::VN];
+      gate_load<DK, RV::VN>(&sm.G[row * Lay::LDG], c0, bv);
 #pragma unroll
       for (int e = 0; e < RV::VN; ++e) {
-        const float b = sm.G[row * Lay::LDG + c0 + e];
-        const float ep = fast_exp(b);
-        const float em = fast_exp(-b);
+        // G holds log2-scaled cumulative gates: exp(b) = exp2(G)
+        const float ep = hw_exp2(bv[e]);
+        const float em = hw_exp2(-bv[e]);
         kt[e] = from_f32<TL>(kf[e] * ep);
         kh[e] = from_f32<TL>(kf[e] * em);
         if (DO_QT) qt[e] = from_f32<TL>(qf[e] * ep);
-        if (DO_KB) sm.KbT[(c0 + e) * Lay::LDC + row] = from_f32<TF>(kf[e] * fast_exp(sm.bC[c0 + e] - b));
+        if (DO_KB) {
+          const int c = c0 + e;
+          sm.KbT[c * C + (row ^ kb_swz(c))] = from_f32<TF>(kf[e] * (sm.gam[c] * em));
+        }
       }
       if (DO_KT) *reinterpret_cast<Vec16*>(&sm.Kt[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kt);
       if (DO_KH) *reinterpret_cast<Vec16*>(&sm.Kh[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kh);
@@ -307,70 +385,72 @@ __device__ __forceinline__ void stage_values(Smem<T, DK, DVW>& sm, const Vec16* 
   }
 }
 
-// Lower-triangular 16x16 block list of a 64x64 matrix; for P the blocks (0,1)
-// and (2,3) are included (as zeros) because 32-wide reduction slabs read them.
-__device__ __forceinline__ void blk_ij(int t, int& I, int& J) {
-  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3) (0,1) (2,3),
-  // packed 4 bits per entry (no indexed private arrays)
-  I = (int)((0x203333222110ull >> (4 * t)) & 15u);
-  J = (int)((0x313210210100ull >> (4 * t)) & 15u);
-}
-
-// L = StrictTril(Diag(beta) Kt Kh^T) (fp32 diagonal blocks, -L off-diagonal
-// in T) and/or P = Tril(Qt Kh^T) (T), distributed over the wavefronts.
-template <typename T, int DK, int DVW, bool DO_L, bool DO_P>
-__device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, int wave, int lane) {
+// Tiles (I, J) of L = StrictTril(Diag(beta) Kt Kh^T) or of P = Tril(Qt Kh^T),
+// NTL at a time so that their operand reads and MFMAs overlap.  L's diagonal
+// blocks go to Ld (fp32) for the inverse, its off-diagonal blocks to Ln as -L;
+// P goes to P (both in the TF type).  P's blocks (0,1) and (2,3) above the
+// diagonal are written as zeros because 32-wide reduction slabs read them.
+template <typename T, int DK, int DVW, int NTL>
+__device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, const bool (&isL)[NTL], const int (&I)[NTL],
+                                         const int (&J)[NTL], int lane) {
   typedef typename Operands<T>::TL TL;
   typedef typename Operands<T>::TF TF;
   typedef Mma<TL> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
-  constexpr int NL = DO_L ? 10 : 0;
-  constexpr int NP = DO_P ? 12 : 0;
-  for (int tile = wave; tile < NL + NP; tile += NW) {
-    const bool isL = tile < NL;
-    int I, J;
-    blk_ij(isL ? tile : tile - NL, I, J);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (I >= J) {
-      const TL* A = isL ? sm.Kt : sm.Qt;
+  floatx4 acc[NTL];
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const typename M::F32 af = M::lds32(A + (16 * I + l16) * Lay::LDK + 32 * ks + 4 * g4);
-        const typename M::F32 bf = M::lds32(sm.Kh + (16 * J + l16) * Lay::LDK + 32 * ks + 4 * g4);
-        acc = M::mma32(af, bf, acc);
+  for (int t = 0; t < NTL; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      if (I[t] >= J[t]) {
+        const TL* A = isL[t] ? sm.Kt : sm.Qt;
+        const typename M::F32 af = M::lds32(A + (16 * I[t] + l16) * Lay::LDK + 32 * ks + 4 * g4);
+        const typename M::F32 bf = M::lds32(sm.Kh + (16 * J[t] + l16) * Lay::LDK + 32 * ks + 4 * g4);
+        acc[t] = M::mma32(af, bf, acc[t]);
       }
     }
+  }
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int il = 4 * g4 + j;             // row inside the block
-      const int i = 16 * I + il, jc = 16 * J + l16;
-      float val = acc[j];
-      if (isL) {
+      const int i = 16 * I[t] + il, jc = 16 * J[t] + l16;
+      float val = acc[t][j];
+      if (isL[t]) {
         val *= sm.beta[i];
-        if (I == J) {
+        if (I[t] == J[t]) {
           if (il <= l16) val = 0.f;
-          sm.Ld[(I * 16 + il) * Lay::LDL + l16] = val;
+          sm.Ld[(I[t] * 16 + il) * Lay::LDL + l16] = val;
         } else {
           sm.Ln[i * Lay::LDC + jc] = from_f32<TF>(-val);
         }
       } else {
-        if (I == J && il < l16) val = 0.f;
-        if (I < J) val = 0.f;
+        if ((I[t] == J[t] && il < l16) || I[t] < J[t]) val = 0.f;
         sm.P[i * Lay::LDC + jc] = from_f32<TF>(val);
       }
     }
   }
 }
 
-// (I + L_ii)^-1 for the four diagonal 16x16 blocks, by forward substitution:
-// lane = 16 * block + column; column c of the inverse solves (I + L_ii) x = e_c.
-// Rows of L_ii are read as 16-byte vectors; a scheduling fence every four
-// rows bounds how many of them are held in registers at once.
 template <typename T, int DK, int DVW>
-__device__ __forceinline__ void diag_inverse(Smem<T, DK, DVW>& sm, int lane) {
+__device__ __forceinline__ void lp_tile(Smem<T, DK, DVW>& sm, bool isL, int I, int J, int lane) {
+  const bool l[1] = {isL};
+  const int i[1] = {I}, j[1] = {J};
+  lp_tiles<T, DK, DVW, 1>(sm, l, i, j, lane);
+}
+
+// (I + L_bb)^-1 of one diagonal 16x16 block by forward substitution: lane c
+// (mod 16) solves (I + L_bb) x = e_c for column c of the inverse.  Rows of
+// L_bb are read as 16-byte vectors; a scheduling fence every four rows bounds
+// how many are held in registers at once.
+template <typename T, int DK, int DVW>
+__device__ __forceinline__ void diag_inverse_block(Smem<T, DK, DVW>& sm, int blk, int lane) {
   typedef Layout<T, DK, DVW> Lay;
-  const int blk = lane >> 4, c = lane & 15;
+  const int c = lane & 15;
   const float* Lb = sm.Ld + blk * 16 * Lay::LDL;
   float x[16];
 #pragma unroll
@@ -381,43 +461,94 @@ __device__ __forceinline__ void diag_inverse(Smem<T, DK, DVW>& sm, int lane) {
       const floatx4 v = *reinterpret_cast<const floatx4*>(Lb + r * Lay::LDL + 4 * m4);
       row[4 * m4 + 0] = v[0]; row[4 * m4 + 1] = v[1]; row[4 * m4 + 2] = v[2]; row[4 * m4 + 3] = v[3];
     }
-    float s = (r == c) ? 1.f : 0.f;
+    float sacc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-    for (int m = 0; m < r; ++m) s -= row[m] * x[m];
-    x[r] = s;
+    for (int m = 0; m < r; ++m) sacc -= row[m] * x[m];
+    x[r] = sacc;
     if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
+  if (lane < 16) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sm.Db[(blk * 16 + r) * Lay::LDD + c] = from_f32<typename Operands<T>::TF>(x[r]);
+    for (int r = 0; r < 16; ++r) sm.Db[(blk * 16 + r) * Lay::LDD + c] = from_f32<typename Operands<T>::TF>(x[r]);
+  }
 }
 
-// Blocked forward substitution for one 16-column tile:
+// The intra-chunk matrices of one chunk, without a barrier between the L
+// diagonal blocks and their inverses: wavefronts 0-3 each compute one diagonal
+// block of L and invert it; the other wavefronts compute the off-diagonal L
+// blocks and the P blocks meanwhile.  With DO_L false all wavefronts share P.
+template <typename T, int DK, int DVW, bool DO_L, bool DO_P>
+__device__ __forceinline__ void intra_chunk_matrices(Smem<T, DK, DVW>& sm, int wave, int lane) {
+  // off-diagonal L blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) and P blocks
+  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3) (0,1) (2,3)
+  constexpr int NL = DO_L ? 6 : 0;
+  constexpr int NP = DO_P ? 12 : 0;
+  constexpr int FIRST = DO_L ? 4 : 0;
+  if (DO_L && wave < 4) {
+    lp_tile<T, DK, DVW>(sm, true, wave, wave, lane);
+    diag_inverse_block<T, DK, DVW>(sm, wave, lane);   // same wavefront: LDS order suffices
+    return;
+  }
+  // tile t < NL: off-diagonal L, else P; handled two at a time
+  constexpr int STEP = NW - FIRST;
+  auto decode = [](int t, bool& isL, int& I, int& J) {
+    isL = t < NL;
+    const int u = isL ? t : t - NL;
+    I = isL ? (int)((0x333221ull >> (4 * u)) & 15u) : (int)((0x203333222110ull >> (4 * u)) & 15u);
+    J = isL ? (int)((0x210100ull >> (4 * u)) & 15u) : (int)((0x313210210100ull >> (4 * u)) & 15u);
+  };
+  for (int t = wave - FIRST; t < NL + NP; t += 2 * STEP) {
+    if (t + STEP < NL + NP) {
+      bool l[2]; int I[2], J[2];
+      decode(t, l[0], I[0], J[0]);
+      decode(t + STEP, l[1], I[1], J[1]);
+      lp_tiles<T, DK, DVW, 2>(sm, l, I, J, lane);
+    } else {
+      bool l[1]; int I[1], J[1];
+      decode(t, l[0], I[0], J[0]);
+      lp_tiles<T, DK, DVW, 1>(sm, l, I, J, lane);
+    }
+  }
+}
+
+// Blocked forward substitution for NT 16-column tiles at once:
 //   X_I = D_I (beta * Src_I - sum_{M<I} L_IM X_M),  I = 0..3,
-// Src rows from LDS (ld = row stride, col0 = first column).  X stays in
-// registers (C layout, fp32).
-template <typename T, int DK, int DVW, typename TS>
-__device__ __forceinline__ void fwd_subst_tile(Smem<T, DK, DVW>& sm, const TS* src, int ld, int col0,
-                                               floatx4 (&X)[4], int lane) {
+// Src rows from LDS (ld = row stride, col[t] = first column of tile t).  The
+// tiles' dependency chains are independent, so their MFMAs interleave.  X stays
+// in registers (C layout, fp32).
+template <typename T, int DK, int DVW, typename TS, int NTL>
+__device__ __forceinline__ void fwd_subst_tiles(Smem<T, DK, DVW>& sm, const TS* src, int ld, const int (&col)[NTL],
+                                                floatx4 (&X)[NTL][4], int lane) {
   typedef Mma<typename Operands<T>::TF> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
-    floatx4 acc;
+    floatx4 acc[NTL];
+    const floatx4 bt = *reinterpret_cast<const floatx4*>(&sm.beta[16 * I + 4 * g4]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * I + 4 * g4 + j;
-      acc[j] = sm.beta[row] * to_f32(src[row * ld + col0 + l16]);
-    }
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[t][j] = bt[j] * to_f32(src[(16 * I + 4 * g4 + j) * ld + col[t] + l16]);
 #pragma unroll
     for (int Mb = 0; Mb < I; ++Mb) {
       const typename M::F16 af = M::lds16(sm.Ln + (16 * I + l16) * Lay::LDC + 16 * Mb + 4 * g4);
-      acc = M::mma16(af, M::frag16(X[Mb]), acc);
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) acc[t] = M::mma16(af, M::frag16(X[t][Mb]), acc[t]);
     }
     const typename M::F16 df = M::lds16(sm.Db + (16 * I + l16) * Lay::LDD + 4 * g4);
-    X[I] = M::mma16(df, M::frag16(acc), zero);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) X[t][I] = M::mma16(df, M::frag16(acc[t]), zero);
   }
+}
+
+// One tile (the staged kernels).
+template <typename T, int DK, int DVW, typename TS>
+__device__ __forceinline__ void fwd_subst_tile(Smem<T, DK, DVW>& sm, const TS* src, int ld, int col0,
+                                               floatx4 (&X)[4], int lane) {
+  const int col[1] = {col0};
+  fwd_subst_tiles<T, DK, DVW, TS, 1>(sm, src, ld, col, *reinterpret_cast<floatx4(*)[1][4]>(&X), lane);
 }
 
 // Store -W of a 16-column tile into Wn (row-major [C][DK]).
@@ -432,55 +563,117 @@ __device__ __forceinline__ void store_negw(Smem<T, DK, DVW>& sm, const floatx4 (
       sm.Wn[(16 * I + 4 * g4 + j) * Lay::LDK + col0 + l16] = from_f32<typename Operands<T>::TL>(-X[I][j]);
 }
 
-// State as reduction operand: fragments of 32 state rows (key channels).
-template <typename TO, int DK>
-__device__ __forceinline__ void state_frags(const floatx4 (&S)[DK / 16], typename Mma<TO>::F32 (&Sf)[DK / 32]) {
-#pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) Sf[ks] = Mma<TO>::frag32(S[2 * ks], S[2 * ks + 1]);
-}
+// ---- products against the state, for NTILE 16-column tiles per wavefront.
+// S[nt][rt]: rows 16rt.. of the state (key channels), C layout.
 
-// acc[I] (+)= A[rows 16I..] @ S  for the four 16-token row blocks, A in LDS [C][LDK].
-template <typename T, int DK>
-__device__ __forceinline__ void rows_times_state(const T* A, int lda, const typename Mma<T>::F32 (&Sf)[DK / 32],
-                                                 floatx4 (&acc)[4], int lane) {
-  typedef Mma<T> M;
+// Dx[nt][I] += A1[rows 16I..] @ S[nt]   and, if A2, O[nt][I] += A2[rows 16I..] @ S[nt]
+// (A1 = -W gives Delta = U - W S; A2 = Qt gives the read-out of the chunk-entry
+// state).  Each A fragment is read once and used for every tile.
+template <typename TL, int DK, int NTILE, bool WITH_O>
+__device__ __forceinline__ void rows_times_state(const TL* A1, const TL* A2, int lda,
+                                                 const floatx4 (&S)[NTILE][DK / 16],
+                                                 floatx4 (&Dx)[NTILE][4], floatx4 (&O)[NTILE][4], int lane) {
+  typedef Mma<TL> M;
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    typename M::F32 sf[NTILE];
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-      acc[I] = M::mma32(M::lds32(A + (16 * I + l16) * lda + 32 * ks + 4 * g4), Sf[ks], acc[I]);
+    for (int nt = 0; nt < NTILE; ++nt) sf[nt] = M::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const typename M::F32 a1 = M::lds32(A1 + (16 * I + l16) * lda + 32 * ks + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) Dx[nt][I] = M::mma32(a1, sf[nt], Dx[nt][I]);
+      if (WITH_O) {
+        const typename M::F32 a2 = M::lds32(A2 + (16 * I + l16) * lda + 32 * ks + 4 * g4);
+#pragma unroll
+        for (int nt = 0; nt < NTILE; ++nt) O[nt][I] = M::mma32(a2, sf[nt], O[nt][I]);
+      }
+    }
+  }
 }
 
-// O[I] += P[rows 16I..] @ Delta  (P lower triangular: slab 1 only for I >= 2)
-template <typename T, int DK, int DVW>
+// O[nt][I] += P[rows 16I..] @ Delta[nt]  (P lower triangular: slab 1 only for I >= 2)
+template <typename T, int DK, int DVW, int NTILE>
 __device__ __forceinline__ void intra_output(Smem<T, DK, DVW>& sm,
-                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[2],
-                                             floatx4 (&O)[4], int lane) {
+                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[NTILE][2],
+                                             floatx4 (&O)[NTILE][4], int lane) {
   typedef Mma<typename Operands<T>::TF> M;
   typedef Layout<T, DK, DVW> Lay;
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
-    O[I] = M::mma32(M::lds32(sm.P + (16 * I + l16) * Lay::LDC + 4 * g4), Df[0], O[I]);
-    if (I >= 2) O[I] = M::mma32(M::lds32(sm.P + (16 * I + l16) * Lay::LDC + 32 + 4 * g4), Df[1], O[I]);
+    const typename M::F32 a0 = M::lds32(sm.P + (16 * I + l16) * Lay::LDC + 4 * g4);
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt) O[nt][I] = M::mma32(a0, Df[nt][0], O[nt][I]);
+    if (I >= 2) {
+      const typename M::F32 a1 = M::lds32(sm.P + (16 * I + l16) * Lay::LDC + 32 + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) O[nt][I] = M::mma32(a1, Df[nt][1], O[nt][I]);
+    }
   }
 }
 
-// S <- Diag(gam) S + KbT @ Delta
-template <typename T, int DK, int DVW>
+// S <- Diag(gam) S + Kb^T @ Delta, Kb^T read through its swizzle.
+template <typename T, int DK, int DVW, int NTILE>
 __device__ __forceinline__ void state_update(Smem<T, DK, DVW>& sm,
-                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[2],
-                                             floatx4 (&S)[DK / 16], int lane) {
-  typedef Mma<typename Operands<T>::TF> M;
-  typedef Layout<T, DK, DVW> Lay;
+                                             const typename Mma<typename Operands<T>::TF>::F32 (&Df)[NTILE][2],
+                                             floatx4 (&S)[NTILE][DK / 16], int lane) {
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TF> M;
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int rt = 0; rt < DK / 16; ++rt) {
+    const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[16 * rt + 4 * g4]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S[rt][j] *= sm.gam[16 * rt + 4 * g4 + j];
-    S[rt] = M::mma32(M::lds32(sm.KbT + (16 * rt + l16) * Lay::LDC + 4 * g4), Df[0], S[rt]);
-    S[rt] = M::mma32(M::lds32(sm.KbT + (16 * rt + l16) * Lay::LDC + 32 + 4 * g4), Df[1], S[rt]);
+    for (int nt = 0; nt < NTILE; ++nt) S[nt][rt] *= gm;
+    const int c = 16 * rt + l16;
+    const int sw = kb_swz(c);
+    const TF* row = sm.KbT + c * C;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t0 = 32 * h + 4 * g4;      // tokens t0..t0+3 and t0+16..t0+19
+      const typename M::F16 lo = M::lds16(row + (t0 ^ sw));
+      const typename M::F16 hi = M::lds16(row + ((t0 + 16) ^ sw));
+      const typename M::F32 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) S[nt][rt] = M::mma32(a, Df[nt][h], S[nt][rt]);
+    }
+  }
+}
+
+// Write an owner wavefront's 64 x (16*NTILE) output block to o: C layout ->
+// its private LDS staging rows -> 16-byte buffer stores (rows past the end of
+// the sequence fall outside the buffer range and are dropped).
+template <typename T, int DK, int DVW, int NTILE>
+__device__ __forceinline__ void store_output(Smem<T, DK, DVW>& sm, const floatx4 (&O)[NTILE][4], int owner_idx,
+                                             __amdgpu_buffer_rsrc_t ro, int row_elems, int col, int lane) {
+  typedef Layout<T, DK, DVW> Lay;
+  constexpr int W = 16 * NTILE;
+  constexpr int LD = Lay::LDS_O;
+  T* st = sm.stg + owner_idx * C * LD;
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[(16 * I + 4 * g4 + j) * LD + 16 * nt + l16] = from_f32<T>(O[nt][I][j]);
+  // 8-byte reads (rows are 8-byte aligned), paired into 16-byte stores
+  constexpr int E8 = 8 / (int)sizeof(T);          // elements per 8 bytes
+  constexpr int VPR = W / (2 * E8);              // 16-byte vectors per row
+  constexpr int PER = C * VPR / kWave;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = lane + kWave * i;
+    const int row = idx / VPR, cv = idx % VPR;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x2 a = *reinterpret_cast<const u32x2*>(st + row * LD + cv * 2 * E8);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(st + row * LD + cv * 2 * E8 + E8);
+    const u32x4 v = {a[0], a[1], b[0], b[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((row * row_elems + col + cv * 2 * E8) * (int)sizeof(T)), 0, 0);
   }
 }
 
@@ -509,24 +702,30 @@ __device__ __forceinline__ floatx4 load_tile_rows_f32(const float* base, int D, 
   return r;
 }
 
-// state tile io: S[(head*DK + row) * DV + col]
-template <int DK, int DV>
-__device__ __forceinline__ void load_state(floatx4 (&S)[DK / 16], const float* S0, int64_t head, int col, int lane) {
+// state tile io: S[(head*DK + row) * DV + col], tile nt at columns col + 16 nt
+template <int DK, int DV, int NTILE>
+__device__ __forceinline__ void load_state(floatx4 (&S)[NTILE][DK / 16], const float* S0, int64_t head, int col,
+                                           int lane) {
   const int g4 = lane >> 4;
 #pragma unroll
-  for (int rt = 0; rt < DK / 16; ++rt)
+  for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S[rt][j] = S0 ? S0[(head * DK + 16 * rt + 4 * g4 + j) * DV + col] : 0.f;
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S[nt][rt][j] = S0 ? S0[(head * DK + 16 * rt + 4 * g4 + j) * DV + col + 16 * nt] : 0.f;
 }
 
-template <int DK, int DV>
-__device__ __forceinline__ void store_state(const floatx4 (&S)[DK / 16], float* out, int64_t head, int col, int lane) {
+template <int DK, int DV, int NTILE>
+__device__ __forceinline__ void store_state(const floatx4 (&S)[NTILE][DK / 16], float* out, int64_t head, int col,
+                                            int lane) {
   const int g4 = lane >> 4;
 #pragma unroll
-  for (int rt = 0; rt < DK / 16; ++rt)
+  for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[(head * DK + 16 * rt + 4 * g4 + j) * DV + col] = S[rt][j];
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[(head * DK + 16 * rt + 4 * g4 + j) * DV + col + 16 * nt] = S[nt][rt][j];
 }
 
 // Workgroup -> (head, split): the NSPLIT workgroups of one head get block ids
@@ -554,7 +753,134 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<T, DK, DV, DVW>& rg, const
   buf_load_rows<T, DVW>(rg.v, make_rsrc(reinterpret_cast<const T*>(a.v) + tok0 * DV + col0,
                                         chunk_bytes(nv, a.H * DV, DVW, es)), a.H * DV, tid);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<const T*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, es));
-  rg.beta = buf_load_scalar<T>(rb, tid < C ? (uint32_t)(tid * a.H * es) : 0x80000000u);
+  const uint32_t boff = tid < C ? (uint32_t)(tid * a.H * es) : 0x80000000u;
+  if constexpr (sizeof(T) == 2)
+    rg.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, boff, 0, 0);
+  else
+    rg.beta_bits = __builtin_amdgcn_raw_buffer_load_b32(rb, boff, 0, 0);
+}
+
+
+// ---------------------------------------------------------------------------
+// Fused forward.
+// ---------------------------------------------------------------------------
+// One 16x16 tile with compile-time block indices (straight-line code, so the
+// operand reads and MFMAs of consecutive tiles overlap).  IS_L: L tile (I > J
+// to Ln as -L, I == J to Ld in fp32); else P tile (I < J written as zeros).
+template <typename T, int DK, int DVW, bool IS_L, int I, int J>
+__device__ __forceinline__ void lp_tile_ct(Smem<T, DK, DVW>& sm, int lane) {
+  typedef typename Operands<T>::TL TL;
+  typedef typename Operands<T>::TF TF;
+  typedef Mma<TL> M;
+  typedef Layout<T, DK, DVW> Lay;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (I >= J) {
+    const TL* A = IS_L ? sm.Kt : sm.Qt;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const typename M::F32 af = M::lds32(A + (16 * I + l16) * Lay::LDK + 32 * ks + 4 * g4);
+      const typename M::F32 bf = M::lds32(sm.Kh + (16 * J + l16) * Lay::LDK + 32 * ks + 4 * g4);
+      acc = M::mma32(af, bf, acc);
+    }
+  }
+  if constexpr (IS_L) {
+    const floatx4 bt = *reinterpret_cast<const floatx4*>(&sm.beta[16 * I + 4 * g4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int il = 4 * g4 + j;
+      float val = acc[j] * bt[j];
+      if constexpr (I == J) {
+        sm.Ld[(I * 16 + il) * Lay::LDL + l16] = (il > l16) ? val : 0.f;
+      } else {
+        sm.Ln[(16 * I + il) * Lay::LDC + 16 * J + l16] = from_f32<TF>(-val);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int il = 4 * g4 + j;
+      float val = acc[j];
+      if constexpr (I == J) val = (il >= l16) ? val : 0.f;
+      if constexpr (I < J) val = 0.f;
+      sm.P[(16 * I + il) * Lay::LDC + 16 * J + l16] = from_f32<TF>(val);
+    }
+  }
+}
+
+// The off-diagonal L blocks and the P blocks, split over four "tile"
+// wavefronts (tw = 0..3) with the same MFMA count each.
+template <typename T, int DK, int DVW>
+__device__ __forceinline__ void lp_tile_schedule(Smem<T, DK, DVW>& sm, int tw, int lane) {
+  switch (tw) {
+    case 0:
+      lp_tile_ct<T, DK, DVW, true, 1, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, true, 2, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 0, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 1, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 0, 1>(sm, lane);
+      break;
+    case 1:
+      lp_tile_ct<T, DK, DVW, true, 2, 1>(sm, lane);
+      lp_tile_ct<T, DK, DVW, true, 3, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 1, 1>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 2, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 2, 3>(sm, lane);
+      break;
+    case 2:
+      lp_tile_ct<T, DK, DVW, true, 3, 1>(sm, lane);
+      lp_tile_ct<T, DK, DVW, true, 3, 2>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 2, 1>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 2, 2>(sm, lane);
+      break;
+    default:
+      lp_tile_ct<T, DK, DVW, false, 3, 0>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 3, 1>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 3, 2>(sm, lane);
+      lp_tile_ct<T, DK, DVW, false, 3, 3>(sm, lane);
+      break;
+  }
+}
+
+// Diagonal block b of L and its inverse (I + L_bb)^-1 by forward
+// substitution, lane c (mod 16) solving for column c.  The whole block is read
+// into registers first, so the substitution chain waits on LDS only once.
+template <typename T, int DK, int DVW, int B>
+__device__ __forceinline__ void diag_block_inverse_ct(Smem<T, DK, DVW>& sm, int lane) {
+  typedef Layout<T, DK, DVW> Lay;
+  lp_tile_ct<T, DK, DVW, true, B, B>(sm, lane);      // same wavefront: LDS order suffices
+  const int c = lane & 15;
+  const float* Lb = sm.Ld + B * 16 * Lay::LDL;
+  float Lr[16][16];
+#pragma unroll
+  for (int r = 1; r < 16; ++r)
+#pragma unroll
+    for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(Lb + r * Lay::LDL + 4 * m4);
+      Lr[r][4 * m4 + 0] = v[0]; Lr[r][4 * m4 + 1] = v[1]; Lr[r][4 * m4 + 2] = v[2]; Lr[r][4 * m4 + 3] = v[3];
+    }
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float sacc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < r; ++m) sacc -= Lr[r][m] * x[m];
+    x[r] = sacc;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.Db[(B * 16 + r) * Lay::LDD + c] = from_f32<typename Operands<T>::TF>(x[r]);
+  }
+}
+
+template <typename T, int DK, int DVW>
+__device__ __forceinline__ void diag_block_inverse(Smem<T, DK, DVW>& sm, int b, int lane) {
+  switch (b) {
+    case 0: diag_block_inverse_ct<T, DK, DVW, 0>(sm, lane); break;
+    case 1: diag_block_inverse_ct<T, DK, DVW, 1>(sm, lane); break;
+    case 2: diag_block_inverse_ct<T, DK, DVW, 2>(sm, lane); break;
+    default: diag_block_inverse_ct<T, DK, DVW, 3>(sm, lane); break;
+  }
 }
 
 // Re-derive the thread / lane ids from an opaque copy: per-lane index
@@ -568,19 +894,52 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<T, DK, DV, DVW>& rg, const
     lane = t_ & 63;                                \
   } while (0)
 
+// The gate phase of one chunk, shared by both wavefront roles: log2-scaled
+// in-chunk cumulative sum, the gated operands, and the next chunk's loads.
+// Three barriers; leaves the LDS view rebased after the last one.
+template <typename T, int DK, int DV, int DVW>
+__device__ __forceinline__ void gate_phase(Smem<T, DK, DVW>& sm, unsigned char* smem_raw, ChunkRegs<T, DK, DV, DVW>& rg,
+                                           const PrefillArgs& a, int bb, int h, int n, int nchunks, int col0,
+                                           int& tid, int& lane) {
+  sm.sync_rebase(smem_raw);              // previous chunk is done with LDS
+  KDA_FRESH_LANE();
+  stage_gates<T, DK, DVW>(sm, rg.g, bits_to_f32<T>(rg.beta_bits), tid, kLog2e);
+  __syncthreads();
+  chunk_cumsum<T, DK, DVW>(sm, tid);
+  sm.sync_rebase(smem_raw);
+  KDA_FRESH_LANE();
+  apply_gates<T, DK, DVW, true, true, true, true>(sm, rg.k, rg.q, tid);
+  stage_values<T, DK, DVW>(sm, rg.v, tid);
+  // Next chunk's loads overlap this chunk's math.  Issued unconditionally:
+  // past the last chunk the buffer range is empty and they return zeros.  (A
+  // branch here would make the loaded registers merge with the old ones and
+  // force a wait for the loads right away.)
+  fetch_chunk<T, DK, DV, DVW>(rg, a, bb, h, n + 1, col0, tid);
+  sm.sync_rebase(smem_raw);
+  KDA_FRESH_LANE();
+}
+
 // ---------------------------------------------------------------------------
-// Fused forward.
+// Fused forward.  The workgroup's wavefronts take two roles, each running its
+// own copy of the chunk loop with the same barrier sequence (seven per chunk):
+//   owners (waves 0..OWN-1): hold 16*NTILE state columns in registers; take
+//     tile-schedule slots of L / P and read the entry state (O = Qt S), solve
+//     their U tiles, then Delta, O += P Delta, the output and the S update.
+//   workers (the rest): waves OWN..OWN+3 each invert one diagonal block of L,
+//     the others take the remaining tile-schedule slots; all solve W tiles.
+// Separate loops keep the state registers and the workers' temporaries apart,
+// so the prefetched next chunk never has to leave its registers early.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV, int NSPLIT>
 __global__ __launch_bounds__(NT) void fused_fwd_kernel(PrefillArgs a) {
   typedef typename Operands<T>::TL TL;
   typedef typename Operands<T>::TF TF;
-  typedef Mma<TL> ML;
   typedef Mma<TF> MF;
   constexpr int DVW = DV / NSPLIT;
-  constexpr int OWN = DVW / 16;
+  constexpr int NTILE = StateTiles<DVW>::NTILE;
+  constexpr int OWN = StateTiles<DVW>::OWN;
   typedef Layout<T, DK, DVW> Lay;
-  static_assert(OWN >= 1 && OWN <= NW, "column split");
+  static_assert(OWN >= 1 && OWN <= 4, "column split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
 
   int tid = threadIdx.x, lane = tid & 63;
@@ -590,87 +949,91 @@ __global__ __launch_bounds__(NT) void fused_fwd_kernel(PrefillArgs a) {
   if (head >= a.B * a.H) return;
   const int bb = head / a.H, h = head % a.H;
   const int col0 = split * DVW;
-  const bool owner = wave < OWN;
-  const int wcol = col0 + 16 * wave;
-
-
-  floatx4 S[DK / 16];
-  if (owner) load_state<DK, DV>(S, a.S0, head, wcol + (lane & 15), lane);
-
   const int nchunks = (a.T + C - 1) / C;
   ChunkRegs<T, DK, DV, DVW> rg;
   if (nchunks > 0) fetch_chunk<T, DK, DV, DVW>(rg, a, bb, h, 0, col0, tid);
   Smem<T, DK, DVW> sm(smem_raw);
 
-  for (int n = 0; n < nchunks; ++n) {
-    const int t0 = n * C;
-    const int nv = min(C, a.T - t0);
-    TokIdx ti;
-    ti.row0 = ((int64_t)bb * a.T + t0) * a.H + h;
-    ti.rstride = a.H;
+  if (wave < OWN) {
+    // ------------------------------------------------------------ owners
+    const int wcol = col0 + 16 * NTILE * wave;   // first state column
+    floatx4 S[NTILE][DK / 16];
+    load_state<DK, DV, NTILE>(S, a.S0, head, wcol + (lane & 15), lane);
+    for (int n = 0; n < nchunks; ++n) {
+      const int t0 = n * C;
+      const int nv = min(C, a.T - t0);
+      gate_phase<T, DK, DV, DVW>(sm, smem_raw, rg, a, bb, h, n, nchunks, col0, tid, lane);
 
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();              // previous chunk is done with LDS
-    stage_gates<T, DK, DVW>(sm, rg.g, rg.beta, tid);
-    __syncthreads();
-    chunk_cumsum<T, DK, DVW>(sm, tid);
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();
-    apply_gates<T, DK, DVW, true, true, true, true>(sm, rg.k, rg.q, tid);
-    stage_values<T, DK, DVW>(sm, rg.v, tid);
-    if (n + 1 < nchunks) fetch_chunk<T, DK, DV, DVW>(rg, a, bb, h, n + 1, col0, tid);  // overlaps this chunk's math
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();
+      // this owner's share of the L / P blocks, and the read-out of the
+      // chunk-entry state O = Qt S (needs only the gated queries)
+      lp_tile_schedule<T, DK, DVW>(sm, wave, lane);
+      floatx4 O[NTILE][4];
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+      rows_times_state<TL, DK, NTILE, false>(sm.Qt, sm.Qt, Lay::LDK, S, O, O, lane);
+      sm.sync_rebase(smem_raw);
+      KDA_FRESH_LANE();
 
-    // L and P products
-    lp_tiles<T, DK, DVW, true, true>(sm, wave, lane);
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();
-    if (wave == 0) diag_inverse<T, DK, DVW>(sm, lane);
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();
+      // this owner's U tiles, kept in registers
+      floatx4 Ux[NTILE][4];
+      int ucol[NTILE];
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) ucol[nt] = 16 * (NTILE * wave + nt);
+      fwd_subst_tiles<T, DK, DVW, T, NTILE>(sm, sm.V, Lay::LDV, ucol, Ux, lane);
+      sm.sync_rebase(smem_raw);
+      KDA_FRESH_LANE();
 
-    // forward substitution: U tile of each owner in its registers, W to LDS
-    floatx4 Ux[4];
-    for (int t = wave; t < OWN + DK / 16; t += NW) {
-      if (t < OWN) {
-        fwd_subst_tile<T, DK, DVW>(sm, sm.V, Lay::LDV, 16 * t, Ux, lane);
-      } else {
-        floatx4 Wx[4];
-        const int wc = 16 * (t - OWN);
-        fwd_subst_tile<T, DK, DVW>(sm, sm.Kt, Lay::LDK, wc, Wx, lane);
-        store_negw<T, DK, DVW>(sm, Wx, wc, lane);
+      // Delta = U - W S (Ux holds U), the intra-chunk term O += P Delta, and
+      // the state update
+      rows_times_state<TL, DK, NTILE, false>(sm.Wn, sm.Wn, Lay::LDK, S, Ux, Ux, lane);
+      typename MF::F32 Df[NTILE][2];
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) {
+        Df[nt][0] = MF::frag32(Ux[nt][0], Ux[nt][1]);
+        Df[nt][1] = MF::frag32(Ux[nt][2], Ux[nt][3]);
       }
+      intra_output<T, DK, DVW, NTILE>(sm, Df, O, lane);
+      const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc(reinterpret_cast<T*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, (int)sizeof(T)));
+      store_output<T, DK, DVW, NTILE>(sm, O, wave, ro, a.H * DV, wcol, lane);
+      state_update<T, DK, DVW, NTILE>(sm, Df, S, lane);
     }
-    sm.sync_rebase(smem_raw);
-    KDA_FRESH_LANE();
+    if (a.S_T) store_state<DK, DV, NTILE>(S, a.S_T, head, wcol + (lane & 15), lane);
+  } else {
+    // ------------------------------------------------------------ workers
+    constexpr int NNO = NW - OWN;
+    for (int n = 0; n < nchunks; ++n) {
+      gate_phase<T, DK, DV, DVW>(sm, smem_raw, rg, a, bb, h, n, nchunks, col0, tid, lane);
 
-    if (owner) {
-      typename ML::F32 Sf[DK / 32];
-      state_frags<TL, DK>(S, Sf);
-      // read-out of the chunk-entry state, O = Qt S, and Delta = U - W S
-      floatx4 O[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) O[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      rows_times_state<TL, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
-      rows_times_state<TL, DK>(sm.Wn, Lay::LDK, Sf, Ux, lane);
-      typename MF::F32 Df[2];
-      Df[0] = MF::frag32(Ux[0], Ux[1]);
-      Df[1] = MF::frag32(Ux[2], Ux[3]);
-      intra_output<T, DK, DVW>(sm, Df, O, lane);
-      {
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(reinterpret_cast<T*>(a.o) + ti.row0 * DV, chunk_bytes(nv, a.H * DV, DV, (int)sizeof(T)));
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            buf_store_scalar<T>(ro, (uint32_t)(((16 * I + 4 * (lane >> 4) + j) * a.H * DV + wcol + (lane & 15)) * (int)sizeof(T)), O[I][j]);
+      // waves OWN..OWN+3 invert the diagonal blocks of L; the rest take the
+      // tile schedule slots the owners leave
+      if (wave < OWN + 4) diag_block_inverse<T, DK, DVW>(sm, wave - OWN, lane);
+      else lp_tile_schedule<T, DK, DVW>(sm, wave - 4, lane);
+      sm.sync_rebase(smem_raw);
+      KDA_FRESH_LANE();
+
+      // W tiles i = wave - OWN + k (NW - OWN), two at a time, to LDS as -W
+      for (int i = wave - OWN; i < DK / 16; i += 2 * NNO) {
+        if (i + NNO < DK / 16) {
+          const int wc[2] = {16 * i, 16 * (i + NNO)};
+          floatx4 Wx[2][4];
+          fwd_subst_tiles<T, DK, DVW, TL, 2>(sm, sm.Kt, Lay::LDK, wc, Wx, lane);
+          store_negw<T, DK, DVW>(sm, Wx[0], wc[0], lane);
+          store_negw<T, DK, DVW>(sm, Wx[1], wc[1], lane);
+        } else {
+          floatx4 Wx[4];
+          fwd_subst_tile<T, DK, DVW>(sm, sm.Kt, Lay::LDK, 16 * i, Wx, lane);
+          store_negw<T, DK, DVW>(sm, Wx, 16 * i, lane);
+        }
       }
-      state_update<T, DK, DVW>(sm, Df, S, lane);
+      sm.sync_rebase(smem_raw);
+      KDA_FRESH_LANE();
+      // (the owners' Delta / output / state update runs here)
     }
   }
-  if (owner && a.S_T) store_state<DK, DV>(S, a.S_T, head, wcol + (lane & 15), lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -692,13 +1055,14 @@ __global__ __launch_bounds__(NT) void stage_cumsum_kernel(StageArgs a) {
   ti.rstride = a.H;
   Vec16 gr[RowVecs<T, DK>::PER];
   load_rows<T, DK>(gr, reinterpret_cast<const T*>(a.g), DK, 0, ti, nv, tid);
-  stage_gates<T, DK, 16>(sm, gr, 0.f, tid);
+  stage_gates<T, DK, 16>(sm, gr, 0.f, tid, 1.0f);   // natural-log units: b is an output
   __syncthreads();
   chunk_cumsum<T, DK, 16>(sm, tid);
   __syncthreads();
   for (int idx = tid; idx < C * DK; idx += NT) {
     const int row = idx / DK, c = idx % DK;
-    if (row < nv) a.b[(ti.row0 + (int64_t)row * ti.rstride) * DK + c] = sm.G[row * Lay::LDG + c];
+    if (row < nv)
+      a.b[(ti.row0 + (int64_t)row * ti.rstride) * DK + c] = sm.G[row * Lay::LDG + GateCols<DK, VecTraits<T>::N>::pos(c)];
   }
 }
 
@@ -710,12 +1074,13 @@ __device__ __forceinline__ void load_b(Smem<T, DK, DVW>& sm, const float* b, con
     const int row = idx / DK, c = idx % DK;
     // rows past the end repeat the last valid row (zero gate beyond T)
     const int rr = row < nv ? row : nv - 1;
-    sm.G[row * Lay::LDG + c] = b[(ti.row0 + (int64_t)rr * ti.rstride) * DK + c];
+    sm.G[row * Lay::LDG + GateCols<DK, VecTraits<T>::N>::pos(c)] =
+        kLog2e * b[(ti.row0 + (int64_t)rr * ti.rstride) * DK + c];
   }
   if (tid < DK) {
-    const float bl = b[(ti.row0 + (int64_t)(nv - 1) * ti.rstride) * DK + tid];
+    const float bl = kLog2e * b[(ti.row0 + (int64_t)(nv - 1) * ti.rstride) * DK + tid];
     sm.bC[tid] = bl;
-    sm.gam[tid] = fast_exp(bl);
+    sm.gam[tid] = hw_exp2(bl);
   }
 }
 
@@ -743,9 +1108,7 @@ __global__ __launch_bounds__(NT) void stage_ut_kernel(StageArgs a) {
   apply_gates<T, DK, DV, true, true, false, false>(sm, kr, kr, tid);
   stage_values<T, DK, DV>(sm, vr, tid);
   __syncthreads();
-  lp_tiles<T, DK, DV, true, false>(sm, wave, lane);
-  __syncthreads();
-  if (wave == 0) diag_inverse<T, DK, DV>(sm, lane);
+  intra_chunk_matrices<T, DK, DV, true, false>(sm, wave, lane);
   __syncthreads();
   const int l16 = lane & 15;
   for (int t = wave; t < DK / 16 + DV / 16; t += NW) {
@@ -785,8 +1148,8 @@ __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
   const int l16 = lane & 15;
   const int nchunks = (a.T + C - 1) / C;
 
-  floatx4 S[DK / 16];
-  if (owner) load_state<DK, DV>(S, a.S0, head, wcol + l16, lane);
+  floatx4 S[1][DK / 16];
+  if (owner) load_state<DK, DV, 1>(S, a.S0, head, wcol + l16, lane);
   for (int n = 0; n < nchunks; ++n) {
     const int t0 = n * C, nv = min(C, a.T - t0);
     TokIdx ti;
@@ -810,22 +1173,20 @@ __global__ __launch_bounds__(NT) void stage_state_kernel(StageArgs a) {
 #pragma unroll
       for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + wcol + l16] = S[rt][j];
-      typename ML::F32 Sf[DK / 32];
-      state_frags<TL, DK>(S, Sf);
-      floatx4 Dx[4];
+        for (int j = 0; j < 4; ++j) Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + wcol + l16] = S[0][rt][j];
+      floatx4 Dx[1][4], unused[1][4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) Dx[I] = load_tile_rows_f32<T>(a.U, DV, ti, I, wcol + l16, nv, lane);
-      rows_times_state<TL, DK>(sm.Wn, Lay::LDK, Sf, Dx, lane);
+      for (int I = 0; I < 4; ++I) Dx[0][I] = load_tile_rows_f32<T>(a.U, DV, ti, I, wcol + l16, nv, lane);
+      rows_times_state<TL, DK, 1, false>(sm.Wn, sm.Wn, Lay::LDK, S, Dx, unused, lane);
 #pragma unroll
-      for (int I = 0; I < 4; ++I) store_tile_rows<float>(a.Delta, DV, ti, I, wcol + l16, Dx[I], nv, lane);
-      typename MF::F32 Df[2];
-      Df[0] = MF::frag32(Dx[0], Dx[1]);
-      Df[1] = MF::frag32(Dx[2], Dx[3]);
-      state_update<T, DK, DVW>(sm, Df, S, lane);
+      for (int I = 0; I < 4; ++I) store_tile_rows<float>(a.Delta, DV, ti, I, wcol + l16, Dx[0][I], nv, lane);
+      typename MF::F32 Df[1][2];
+      Df[0][0] = MF::frag32(Dx[0][0], Dx[0][1]);
+      Df[0][1] = MF::frag32(Dx[0][2], Dx[0][3]);
+      state_update<T, DK, DVW, 1>(sm, Df, S, lane);
     }
   }
-  if (owner && a.S_T) store_state<DK, DV>(S, a.S_T, head, wcol + l16, lane);
+  if (owner && a.S_T) store_state<DK, DV, 1>(S, a.S_T, head, wcol + l16, lane);
 }
 
 // O = Qt S_[n] + Tril(Qt Kh^T) Delta.  grid (chunks, B*H)
@@ -854,31 +1215,29 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
   __syncthreads();
   apply_gates<T, DK, DV, false, true, true, false>(sm, kr, qr, tid);
   __syncthreads();
-  lp_tiles<T, DK, DV, false, true>(sm, wave, lane);
+  intra_chunk_matrices<T, DK, DV, false, true>(sm, wave, lane);
   __syncthreads();
   for (int ct = wave; ct < DV / 16; ct += NW) {
     const int col = 16 * ct + l16;
-    floatx4 S[DK / 16];
+    floatx4 S[1][DK / 16];
     const float* Sc = a.S_chunks + ((int64_t)head * nchunks + n) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[rt][j] = Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + col];
-    typename ML::F32 Sf[DK / 32];
-    state_frags<TL, DK>(S, Sf);
-    floatx4 O[4];
+      for (int j = 0; j < 4; ++j) S[0][rt][j] = Sc[(int64_t)(16 * rt + 4 * (lane >> 4) + j) * DV + col];
+    floatx4 O[1][4], unused[1][4];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) O[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-    rows_times_state<TL, DK>(sm.Qt, Lay::LDK, Sf, O, lane);
+    for (int I = 0; I < 4; ++I) O[0][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+    rows_times_state<TL, DK, 1, false>(sm.Qt, sm.Qt, Lay::LDK, S, O, unused, lane);
     floatx4 Dx[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) Dx[I] = load_tile_rows_f32<T>(a.Delta, DV, ti, I, col, nv, lane);
-    typename MF::F32 Df[2];
-    Df[0] = MF::frag32(Dx[0], Dx[1]);
-    Df[1] = MF::frag32(Dx[2], Dx[3]);
-    intra_output<T, DK, DV>(sm, Df, O, lane);
+    typename MF::F32 Df[1][2];
+    Df[0][0] = MF::frag32(Dx[0], Dx[1]);
+    Df[0][1] = MF::frag32(Dx[2], Dx[3]);
+    intra_output<T, DK, DV, 1>(sm, Df, O, lane);
 #pragma unroll
-    for (int I = 0; I < 4; ++I) store_tile_rows<T>(reinterpret_cast<T*>(a.o), DV, ti, I, col, O[I], nv, lane);
+    for (int I = 0; I < 4; ++I) store_tile_rows<T>(reinterpret_cast<T*>(a.o), DV, ti, I, col, O[0][I], nv, lane);
   }
 }
 
