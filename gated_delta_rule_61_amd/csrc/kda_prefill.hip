@@ -64,7 +64,7 @@ struct Layout {
   static constexpr int O_KH = O_KT + SZ_CK;            // later reused for -W
   static constexpr int O_QT = O_KH + SZ_CK;
   static constexpr int O_KBT = O_QT + SZ_CK;
-  static constexpr int O_V = O_KBT + DK * C * (int)sizeof(T);      // Kb^T: unpadded, swizzled
+  static constexpr int O_V = O_KBT + DK * LDC * (int)sizeof(T);    // Kb^T, swizzled
   static constexpr int O_G = O_V + C * LDV * (int)sizeof(T);
   static constexpr int SZ_GATE = C * LDG * 4;
   static constexpr int SZ_LP = 2 * C * LDC * (int)sizeof(T) + 4 * 16 * LDL * 4 + 4 * 16 * LDD * (int)sizeof(T);
@@ -125,12 +125,14 @@ struct Smem {
   }
 };
 
-// Kb^T is stored [d_k][C] without padding; token t of channel c sits at column
-// t ^ kb_swz(c).  The XOR moves whole 4-token groups, so MFMA operand reads
-// (4 consecutive tokens) stay contiguous, while the transposed 2-byte writes of
-// one wavefront (16 channels x 4 tokens) and the operand reads (16 channels x
-// 2 token groups) each land in distinct LDS banks.
-__device__ __forceinline__ int kb_swz(int c) { return 4 * ((3 * (c >> 3) + 2 * (c & 7)) & 15); }
+// Kb^T is stored [d_k][C + pad] (row stride LDC); token t of channel c sits at
+// column t ^ kb_swz(c).  The XOR moves whole 4-token groups, so MFMA operand
+// reads (4 consecutive tokens) stay contiguous, while the transposed 2-byte
+// writes of one wavefront (16 channel groups x 4 tokens) and the operand reads
+// (16 channels x 2 token groups) each land in distinct LDS banks.  It depends
+// on c only through c / 8, so a thread writing 8 consecutive channels computes
+// it once.
+__device__ __forceinline__ int kb_swz(int c) { return 4 * ((c >> 3) & 15); }
 
 // ---------------------------------------------------------------------------
 // Global -> register staging of one chunk of one head.
@@ -310,19 +312,21 @@ __device__ __forceinline__ void chunk_cumsum(Smem<T, DK, DVW>& sm, int tid) {
   constexpr int NSEG = Lay::NSEG;
   constexpr int RPS = C / NSEG;
   const int c = tid % DK, seg = tid / DK;
+  float v[RPS];
+#pragma unroll
+  for (int r = 0; r < RPS; ++r) v[r] = sm.G[(seg * RPS + r) * Lay::LDG + c];
   float run = 0.f;
 #pragma unroll
   for (int r = 0; r < RPS; ++r) {
-    float* p = &sm.G[(seg * RPS + r) * Lay::LDG + c];
-    run += *p;
-    *p = run;
+    run += v[r];
+    v[r] = run;
   }
   sm.tot[seg * DK + c] = run;
   __syncthreads();
   float off = 0.f;
   for (int s = 0; s < seg; ++s) off += sm.tot[s * DK + c];
 #pragma unroll
-  for (int r = 0; r < RPS; ++r) sm.G[(seg * RPS + r) * Lay::LDG + c] += off;
+  for (int r = 0; r < RPS; ++r) sm.G[(seg * RPS + r) * Lay::LDG + c] = v[r] + off;
   if (seg == NSEG - 1) {
     // this thread scanned physical column c; record its channel's totals
     const int ch = GateCols<DK, VecTraits<T>::N>::chan(c);
@@ -359,10 +363,7 @@ __device__ __forceinline__ void apply_gates(Smem<T, DK, DVW>& sm, const Vec16* k
         kt[e] = from_f32<TL>(kf[e] * ep);
         kh[e] = from_f32<TL>(kf[e] * em);
         if (DO_QT) qt[e] = from_f32<TL>(qf[e] * ep);
-        if (DO_KB) {
-          const int c = c0 + e;
-          sm.KbT[c * C + (row ^ kb_swz(c))] = from_f32<TF>(kf[e] * (sm.gam[c] * em));
-        }
+        if (DO_KB) sm.KbT[(c0 + e) * Lay::LDC + (row ^ kb_swz(c0))] = from_f32<TF>(kf[e] * (sm.gam[c0 + e] * em));
       }
       if (DO_KT) *reinterpret_cast<Vec16*>(&sm.Kt[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kt);
       if (DO_KH) *reinterpret_cast<Vec16*>(&sm.Kh[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kh);
@@ -630,7 +631,7 @@ __device__ __forceinline__ void state_update(Smem<T, DK, DVW>& sm,
     for (int nt = 0; nt < NTILE; ++nt) S[nt][rt] *= gm;
     const int c = 16 * rt + l16;
     const int sw = kb_swz(c);
-    const TF* row = sm.KbT + c * C;
+    const TF* row = sm.KbT + c * Layout<T, DK, DVW>::LDC;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t0 = 32 * h + 4 * g4;      // tokens t0..t0+3 and t0+16..t0+19
@@ -859,6 +860,9 @@ __device__ __forceinline__ void diag_block_inverse_ct(Smem<T, DK, DVW>& sm, int 
       const floatx4 v = *reinterpret_cast<const floatx4*>(Lb + r * Lay::LDL + 4 * m4);
       Lr[r][4 * m4 + 0] = v[0]; Lr[r][4 * m4 + 1] = v[1]; Lr[r][4 * m4 + 2] = v[2]; Lr[r][4 * m4 + 3] = v[3];
     }
+  // keep every read above this point: one wait for all of them instead of one
+  // per row group
+  __builtin_amdgcn_sched_barrier(0);
   float x[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
