@@ -66,6 +66,13 @@ int env_nsplit() {
   return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
 }
 
+// KDA_FUSED_PIPELINE=0 selects the non-pipelined fused schedule everywhere
+// (kept for comparison and for checking one schedule against the other).
+int env_pipeline() {
+  const char* e = getenv("KDA_FUSED_PIPELINE");
+  return (e && e[0] == '0') ? 0 : 1;
+}
+
 #define KDA_REQUIRE(cond, code) \
   do {                          \
     if (!(cond)) return (code); \
@@ -121,7 +128,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
     if (st) return st;
   }
   KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
-  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16, env_nsplit()};
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16, env_nsplit(), env_pipeline()};
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 

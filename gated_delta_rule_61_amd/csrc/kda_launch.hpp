@@ -12,6 +12,7 @@ struct PrefillArgs {
   int B, T, H, dk, dv;
   int bf16;       // 1: bf16 inputs/outputs, 0: fp32
   int nsplit;     // column split of the state across workgroups (0 = auto)
+  int pipeline;   // 1: software-pipelined schedule where it applies (bf16, d = 128, no split)
 };
 
 struct StageArgs {

@@ -1246,6 +1246,738 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined forward for bf16 inputs with d_k = d_v = 128.
+//
+// Only the readout O = Qt S + P Delta and the update of S depend on the state;
+// everything else of a chunk (gates, gated operands, L, (I+L)^-1, W, U, P) does
+// not.  The workgroup therefore runs two chunks at once: while the four owner
+// wavefronts (state columns 32o..32o+31 in registers) finish chunk n, the four
+// worker wavefronts prepare chunk n+1.  One "slot" has four phases separated
+// by workgroup barriers:
+//   1   owners: Delta = U - W S, O += P Delta, store O, S update      (chunk n)
+//       workers: in-chunk cumsum of the gates, Kt Kh Qt Kt^T          (n+1)
+//   2a  owners: P tiles;  worker 0: diagonal L blocks and their inverses;
+//       workers 1-3: off-diagonal L blocks;  all workers: Kb^T, V^T    (n+1)
+//   2b  owners: O = Qt S (entry state of n+1);  worker 0: the off-diagonal
+//       blocks of A' = (I+L)^-1 Diag(beta)                             (n+1)
+//   3   workers: W = A' Kt;  owners: U = A' V                          (n+1)
+// The inverse is formed explicitly (blocked, 16x16 diagonal blocks solved by
+// substitution in fp32, couplings on MFMA), so that W and U are plain
+// products.  Worker wavefront w owns gate channels 32w..32w+31 of every token:
+// its lanes hold 4 consecutive tokens x 8 channels, the in-chunk prefix sum
+// runs in registers (DPP row shifts across the 16 token groups), and the
+// transposed operands are written 4 tokens at a time.
+// ---------------------------------------------------------------------------
+namespace pipe {
+
+constexpr int DK = 128, DV = 128;
+constexpr int LDK = DK + 8;      // bf16 [C][DK] rows
+constexpr int LDT = C + 8;       // fp16 [D][C] rows (transposed operands), [C][C] rows
+constexpr int LDB = 24;          // fp16 16x16 solver blocks
+constexpr int LDL = 20;          // fp32 16x16 diagonal blocks of L (transposed)
+constexpr int SZ_RM = C * LDK * 2;
+constexpr int SZ_TR = DK * LDT * 2;
+constexpr int SZ_CC = C * LDT * 2;
+constexpr int O_KT = 0;
+constexpr int O_KH = O_KT + SZ_RM;
+constexpr int O_QT = O_KH + SZ_RM;
+constexpr int O_WN = O_QT + SZ_RM;       // -W; scratch of the solver wavefront in phase 2
+constexpr int O_KTT = O_WN + SZ_RM;
+constexpr int O_KBT = O_KTT + SZ_TR;
+constexpr int O_VT = O_KBT + SZ_TR;      // V^T; owners' output staging in phase 1
+constexpr int O_P = O_VT + SZ_TR;
+constexpr int O_A = O_P + SZ_CC;
+constexpr int O_BETA = O_A + SZ_CC;
+constexpr int O_GAM = O_BETA + C * 4;    // two chunk parities
+constexpr int BYTES = O_GAM + 2 * DK * 4;
+// solver scratch inside the -W region
+constexpr int S_LDT = 0;                           // fp32 [4][16][LDL]: L_II^T
+constexpr int S_LN = S_LDT + 4 * 16 * LDL * 4;     // fp16 [6][16][LDB]: -L_IJ, I > J
+constexpr int S_D = S_LN + 6 * 16 * LDB * 2;       // fp16 [4][16][LDB]: D_I = (I + L_II)^-1
+constexpr int S_DT = S_D + 4 * 16 * LDB * 2;       // fp16 [4][16][LDB]: D_I^T
+constexpr int S_END = S_DT + 4 * 16 * LDB * 2;
+constexpr int LDS_O = 36;                          // output staging rows (bf16)
+static_assert(S_END <= SZ_RM, "solver scratch");
+static_assert(4 * C * LDS_O * 2 <= SZ_TR, "output staging");
+static_assert(BYTES <= 160 * 1024, "LDS");
+
+struct Ptr {
+  bf16 *Kt, *Kh, *Qt, *Wn;
+  f16 *KtT, *KbT, *VT, *P, *A;
+  float *beta, *gam;
+  float* LdT; f16 *Ln, *D, *Dt;
+  bf16* stg;
+  __device__ __forceinline__ void set(unsigned char* b) {
+    Kt = reinterpret_cast<bf16*>(b + O_KT);
+    Kh = reinterpret_cast<bf16*>(b + O_KH);
+    Qt = reinterpret_cast<bf16*>(b + O_QT);
+    Wn = reinterpret_cast<bf16*>(b + O_WN);
+    KtT = reinterpret_cast<f16*>(b + O_KTT);
+    KbT = reinterpret_cast<f16*>(b + O_KBT);
+    VT = reinterpret_cast<f16*>(b + O_VT);
+    P = reinterpret_cast<f16*>(b + O_P);
+    A = reinterpret_cast<f16*>(b + O_A);
+    beta = reinterpret_cast<float*>(b + O_BETA);
+    gam = reinterpret_cast<float*>(b + O_GAM);
+    LdT = reinterpret_cast<float*>(b + O_WN + S_LDT);
+    Ln = reinterpret_cast<f16*>(b + O_WN + S_LN);
+    D = reinterpret_cast<f16*>(b + O_WN + S_D);
+    Dt = reinterpret_cast<f16*>(b + O_WN + S_DT);
+    stg = reinterpret_cast<bf16*>(b + O_VT);
+  }
+  // barrier, then rebuild the pointers from an offset the compiler cannot see
+  // through, so that each phase computes its own LDS addresses
+  __device__ __forceinline__ void sync(unsigned char* b) {
+    __syncthreads();
+    uint32_t opq = 0;
+    asm volatile("" : "+s"(opq));
+    set(b + opq);
+  }
+};
+
+typedef Mma<bf16> MB;
+typedef Mma<f16> MH;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Reduction-index order in LDS.  A product with one operand from registers in
+// C layout (the state S, or Delta) reads, for lane group g, the indices
+// {4g..4g+3, 16+4g..16+4g+3} of each 32-index slab.  The arrays read against
+// such operands (Kt Kh Qt -W along the key channels, Kb^T and P along the
+// tokens) store index k of a slab at position slot32(k), which makes that set
+// the 16 contiguous bytes at 8g: one ds_read_b128 per fragment instead of two
+// 8-byte reads.  Products of two such arrays read both the same way and pair
+// the same indices.
+__device__ __forceinline__ int slot32(int k) {
+  return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
+}
+
+// Keeps a batch of LDS reads ahead of the products that use them (otherwise
+// the scheduler sinks each read next to its product to save registers, and
+// every product then waits for a full LDS round trip).
+#define KDA_READS_FIRST() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ void unpack8(const Vec16& v, float* f) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { f[2 * k] = bf_lo(v.w[k]); f[2 * k + 1] = bf_hi(v.w[k]); }
+}
+// x + (value of the lane K places lower in the same 16-lane row, 0 if none)
+template <int K>
+__device__ __forceinline__ float add_row_shr(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + K, 0xF, 0xF, true));
+}
+// lane 15 of the caller's 16-lane row (ds_swizzle bit mode: and 0x10, or 0x0f)
+__device__ __forceinline__ float row_last(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F0));
+}
+
+// Chunk inputs of one worker wavefront: rows 4m..4m+3 (m = lane % 16) and
+// channels / value columns 32w + 8(lane / 16) .. +8.
+struct WRegs {
+  Vec16 q[4], k[4], g[4], v[4];
+  uint32_t beta_bits;
+};
+
+__device__ __forceinline__ uint32_t wlane_off(int H, int w, int lane) {
+  return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * (lane >> 4)) * 2);
+}
+
+__device__ __forceinline__ void fetch_qkg(WRegs& r, const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
+  const int t0 = n * C, nv = min(C, a.T - t0);
+  const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+  const uint32_t bytes = chunk_bytes(nv, a.H * DK, DK, 2);
+  const uint32_t vo = wlane_off(a.H, w, lane);
+  const int rs = a.H * DK * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok0 * DK, bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok0 * DK, bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0 * DK, bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rg, vo, i * rs, 0);
+    r.g[i].w[0] = x[0]; r.g[i].w[1] = x[1]; r.g[i].w[2] = x[2]; r.g[i].w[3] = x[3];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, i * rs, 0);
+    r.k[i].w[0] = x[0]; r.k[i].w[1] = x[1]; r.k[i].w[2] = x[2]; r.k[i].w[3] = x[3];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, vo, i * rs, 0);
+    r.q[i].w[0] = x[0]; r.q[i].w[1] = x[1]; r.q[i].w[2] = x[2]; r.q[i].w[3] = x[3];
+  }
+  const __amdgpu_buffer_rsrc_t rb =
+      make_rsrc(reinterpret_cast<const bf16*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, 2));
+  r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(lane * a.H * 2), 0, 0);
+}
+
+__device__ __forceinline__ void fetch_v(WRegs& r, const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
+  const int t0 = n * C, nv = min(C, a.T - t0);
+  const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
+  const uint32_t vo = wlane_off(a.H, w, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, i * a.H * DV * 2, 0);
+    r.v[i].w[0] = x[0]; r.v[i].w[1] = x[1]; r.v[i].w[2] = x[2]; r.v[i].w[3] = x[3];
+  }
+}
+
+// Phase 1 of a worker: log2-scaled in-chunk prefix sums of its gate channels,
+// then Kt = 2^b k, Kh = 2^-b k, Qt = 2^b q (row-major bf16), Kt^T (fp16), the
+// chunk decay gam = 2^b_C of its channels, and Kb = gam 2^-b k kept in
+// registers (kb[e] = tokens 4m..4m+3 of channel e) for phase 2a.
+__device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w, int lane, int par,
+                                             f16x4 (&kb)[8]) {
+  const int j = lane >> 4, m = lane & 15;
+  const int c0 = 32 * w + 8 * j;
+  float b[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unpack8(r.g[i], b[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[i][e] *= kLog2e;
+  }
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[i][e] += b[i - 1][e];
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float tot = b[3][e];
+    float s = add_row_shr<1>(tot);
+    s = add_row_shr<2>(s);
+    s = add_row_shr<4>(s);
+    s = add_row_shr<8>(s);
+    const float ex = s - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i][e] += ex;
+    gm[e] = exp2_hw(row_last(s));
+  }
+  if (m == 0) {
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gm[0], gm[1], gm[2], gm[3]};
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gm[4], gm[5], gm[6], gm[7]};
+  }
+  f16x4 kt_t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float kf[8], qf[8];
+    unpack8(r.k[i], kf);
+    unpack8(r.q[i], qf);
+    bf16x8 kt, kh, qt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ep = exp2_hw(b[i][e]);
+      const float em = exp2_hw(-b[i][e]);
+      const float a = kf[e] * ep, d = kf[e] * em;
+      kt[e] = (bf16)a;
+      kh[e] = (bf16)d;
+      qt[e] = (bf16)(qf[e] * ep);
+      kt_t[e][i] = (f16)a;
+      kb[e][i] = (f16)(d * gm[e]);
+    }
+    // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
+    const int r0 = (4 * m + i) * LDK + slot32(c0), r1 = (4 * m + i) * LDK + slot32(c0 + 4);
+    *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(p.Kh + r1) = __builtin_shufflevector(kh, kh, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x4*>(p.Qt + r0) = __builtin_shufflevector(qt, qt, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(p.Qt + r1) = __builtin_shufflevector(qt, qt, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
+}
+
+// Phase 2a of a worker: Kb^T and V^T from registers.
+__device__ __forceinline__ void worker_transposed(const Ptr& p, const WRegs& r, const f16x4 (&kb)[8], int w,
+                                                  int lane) {
+  const int j = lane >> 4, m = lane & 15;
+  const int c0 = 32 * w + 8 * j;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KbT + (c0 + e) * LDT + slot32(4 * m)) = kb[e];
+  f16x4 vt[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float vf[8];
+    unpack8(r.v[i], vf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[e][i] = (f16)vf[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.VT + (c0 + e) * LDT + 4 * m) = vt[e];
+}
+
+// Products whose two operands both come from LDS use 16-byte fragments: lane
+// group g supplies indices 8g..8g+7 of each 32-index slab (one ds_read_b128
+// per fragment).  Every fragment of a group of tiles is read before the first
+// product, so the reads overlap each other instead of each waiting in turn.
+//
+// Transposed tiles: A and B fragments have the same lane layout (lane (g, i)
+// holds the slab indices of row / column i), so passing them to the MFMA in
+// swapped order yields the transposed product (A B)^T in C layout, where a
+// lane holds four consecutive columns of one row.  Tiles that are stored to a
+// row-major array are computed this way and written 8 bytes per lane: 2-byte
+// LDS writes cost several times more than wide ones.
+__device__ __forceinline__ MB::F32 ldc_b(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ MH::F32 ldc_h(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// NTL 16x16 tiles X_t = A[rows 16 I_t ..] Kh[rows 16 J_t ..]^T of row-major
+// bf16 [C][DK] arrays (C layout).
+// (A_t = Qt where useQ[t], else Kt)
+template <int NTL, bool SWAP>
+__device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], const int (&I)[NTL],
+                                         const int (&J)[NTL], floatx4 (&acc)[NTL], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const bf16* Kh = p.Kh;
+  MB::F32 af[NTL][DK / 32], bf[NTL][DK / 32];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t)
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + (16 * I[t] + l16) * LDK + 32 * ks + 8 * g4);
+      bf[t][ks] = ldc_b(Kh + (16 * J[t] + l16) * LDK + 32 * ks + 8 * g4);
+    }
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+      acc[t] = SWAP ? MB::mma32(bf[t][ks], af[t][ks], acc[t]) : MB::mma32(af[t][ks], bf[t][ks], acc[t]);
+}
+
+__device__ __forceinline__ int ln_block(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// Owners in phase 2a: blocks (I_t, J_t) of P = Tril(Qt Kh^T) (isP[t]) and
+// off-diagonal blocks of L = Diag(beta) Kt Kh^T, stored as -L, all fp16.
+template <int NTL>
+__device__ __forceinline__ void owner_tiles(const Ptr& p, const bool (&isP)[NTL], const int (&I)[NTL],
+                                            const int (&J)[NTL], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  floatx4 acc[NTL];
+  kh_tiles<NTL, true>(p, isP, I, J, acc, lane);     // lane: row l16, columns 4g..4g+3
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    f16x4 v;
+    if (isP[t]) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)((I[t] > J[t] || l16 >= 4 * g4 + jj) ? acc[t][jj] : 0.f);
+      *reinterpret_cast<f16x4*>(p.P + (16 * I[t] + l16) * LDT + slot32(16 * J[t] + 4 * g4)) = v;
+    } else {
+      const float bt = -p.beta[16 * I[t] + l16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(acc[t][jj] * bt);
+      *reinterpret_cast<f16x4*>(p.Ln + ln_block(I[t], J[t]) * 16 * LDB + l16 * LDB + 4 * g4) = v;
+    }
+  }
+}
+
+// Worker I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32
+// (lane c = l16 computes column c of D_I by forward substitution and row c by
+// the transposed system; the four 16-lane groups repeat the same work and the
+// first one writes).  Writes D_I, D_I^T and block (I, I) of A' = D_I Diag(beta).
+__device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  {
+    const bool kq[1] = {false};
+    const int II[1] = {I};
+    floatx4 acc[1];
+    kh_tiles<1, false>(p, kq, II, II, acc, lane);
+    const floatx4 bt = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4 * g4);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[0][jj] = (4 * g4 + jj > l16) ? acc[0][jj] * bt[jj] : 0.f;
+    // L_II^T row l16 = column l16 of L_II (same wavefront reads it back: LDS order suffices)
+    *reinterpret_cast<floatx4*>(p.LdT + (I * 16 + l16) * LDL + 4 * g4) = acc[0];
+  }
+  const int c = l16;
+  const float* Lt = p.LdT + I * 16 * LDL;
+  // columns mm of L_II, entries 4 q4 .. 4 q4 + 3 (only q4 >= (mm + 1) / 4 used)
+  floatx4 col[15][4];
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4) col[mm][q4] = *reinterpret_cast<const floatx4*>(Lt + mm * LDL + 4 * q4);
+  // x = column c of D_I: forward substitution, column by column of L
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int mm = 0; mm < 15; ++mm) {
+    if (mm == 4) {
+      // second half of the columns, read while the first half is used
+#pragma unroll
+      for (int m2 = 8; m2 < 15; ++m2)
+#pragma unroll
+        for (int q4 = (m2 + 1) / 4; q4 < 4; ++q4)
+          col[m2][q4] = *reinterpret_cast<const floatx4*>(Lt + m2 * LDL + 4 * q4);
+    }
+#pragma unroll
+    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (4 * q4 + u > mm) x[4 * q4 + u] -= col[mm][q4][u] * x[mm];
+  }
+  // d = row c of D_I: D_I (I + L_II) = I, solved from the last entry down;
+  // entry r takes L[m][r] (m > r), i.e. row r of L^T -- the same registers
+  float d[16];
+#pragma unroll
+  for (int r = 15; r >= 0; --r) {
+    float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 15; m > r; --m) acc -= col[r][m >> 2][m & 3] * d[m];   // d[r + 1] last
+    d[r] = acc;
+  }
+  f16x8 lo, hi, dlo, dhi, alo, ahi;
+  const floatx4 b0 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I);
+  const floatx4 b1 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4);
+  const floatx4 b2 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 8);
+  const floatx4 b3 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 12);
+  const float bb[16] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3],
+                        b2[0], b2[1], b2[2], b2[3], b3[0], b3[1], b3[2], b3[3]};
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    lo[r] = (f16)x[r]; hi[r] = (f16)x[8 + r];
+    dlo[r] = (f16)d[r]; dhi[r] = (f16)d[8 + r];
+    alo[r] = (f16)(d[r] * bb[r]); ahi[r] = (f16)(d[8 + r] * bb[8 + r]);
+  }
+  if (lane < 16) {
+    *reinterpret_cast<f16x8*>(p.Dt + (I * 16 + c) * LDB) = lo;
+    *reinterpret_cast<f16x8*>(p.Dt + (I * 16 + c) * LDB + 8) = hi;
+    *reinterpret_cast<f16x8*>(p.D + (I * 16 + c) * LDB) = dlo;
+    *reinterpret_cast<f16x8*>(p.D + (I * 16 + c) * LDB + 8) = dhi;
+    // row 16I + c of A', columns 16I .. 16I + 15
+    *reinterpret_cast<f16x8*>(p.A + (16 * I + c) * LDT + 16 * I) = alo;
+    *reinterpret_cast<f16x8*>(p.A + (16 * I + c) * LDT + 16 * I + 8) = ahi;
+  }
+}
+
+// Worker 0 in phase 2b: off-diagonal blocks of A = (I + L)^-1,
+//   A_IJ = D_I sum_{J <= K < I} (-L_IK) A_KJ   (A_KK = D_K),
+// level by level, intermediate blocks kept in registers; A'_IJ = A_IJ Diag(beta_J).
+__device__ __forceinline__ void solver_offdiag(const Ptr& p, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  auto Lf = [&](int I, int J) { return MH::lds16(p.Ln + ln_block(I, J) * 16 * LDB + l16 * LDB + 4 * g4); };
+  auto Df = [&](int I) { return MH::lds16(p.D + (I * 16 + l16) * LDB + 4 * g4); };
+  auto DTf = [&](int J) { return MH::lds16(p.Dt + (J * 16 + l16) * LDB + 4 * g4); };
+  // A'_IJ from its transposed product: lane holds row l16, columns 4g..4g+3
+  auto store_t = [&](int I, int J, const floatx4& vt) {
+    const floatx4 bj = *reinterpret_cast<const floatx4*>(p.beta + 16 * J + 4 * g4);
+    f16x4 v;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(vt[jj] * bj[jj]);
+    *reinterpret_cast<f16x4*>(p.A + (16 * I + l16) * LDT + 16 * J + 4 * g4) = v;
+  };
+  const MH::F16 d1 = Df(1), d2 = Df(2), d3 = Df(3);
+  // level 1
+  floatx4 y10 = MH::mma16(Lf(1, 0), DTf(0), z);
+  floatx4 y21 = MH::mma16(Lf(2, 1), DTf(1), z);
+  floatx4 y32 = MH::mma16(Lf(3, 2), DTf(2), z);
+  floatx4 y20 = MH::mma16(Lf(2, 0), DTf(0), z);
+  floatx4 y31 = MH::mma16(Lf(3, 1), DTf(1), z);
+  floatx4 y30 = MH::mma16(Lf(3, 0), DTf(0), z);
+  const MH::F16 y10f = MH::frag16(y10), y21f = MH::frag16(y21), y32f = MH::frag16(y32);
+  const floatx4 a10 = MH::mma16(d1, y10f, z);
+  const floatx4 a21 = MH::mma16(d2, y21f, z);
+  store_t(1, 0, MH::mma16(y10f, d1, z));
+  store_t(2, 1, MH::mma16(y21f, d2, z));
+  store_t(3, 2, MH::mma16(y32f, d3, z));
+  // level 2
+  const MH::F16 a10f = MH::frag16(a10);
+  y20 = MH::mma16(Lf(2, 1), a10f, y20);
+  y31 = MH::mma16(Lf(3, 2), MH::frag16(a21), y31);
+  y30 = MH::mma16(Lf(3, 1), a10f, y30);
+  const MH::F16 y20f = MH::frag16(y20), y31f = MH::frag16(y31);
+  const floatx4 a20 = MH::mma16(d2, y20f, z);
+  store_t(2, 0, MH::mma16(y20f, d2, z));
+  store_t(3, 1, MH::mma16(y31f, d3, z));
+  // level 3
+  y30 = MH::mma16(Lf(3, 2), MH::frag16(a20), y30);
+  store_t(3, 0, MH::mma16(MH::frag16(y30), d3, z));
+}
+
+// Phase 3, workers: W^T tile rows 32w.. of W = A' Kt (fp16 products from Kt^T
+// and A'), stored as -W into the row-major bf16 array.  A' is lower
+// triangular, so token blocks 0 and 1 need only the first 32-token slab.
+__device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  MH::F32 ka[2][2], ab[4][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) ka[ct][sl] = ldc_h(p.KtT + (32 * w + 16 * ct + l16) * LDT + 32 * sl + 8 * g4);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int sl = 0; sl < (tb >= 2 ? 2 : 1); ++sl) ab[tb][sl] = ldc_h(p.A + (16 * tb + l16) * LDT + 32 * sl + 8 * g4);
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      floatx4 acc = MH::mma32(ka[ct][0], ab[tb][0], floatx4{0.f, 0.f, 0.f, 0.f});
+      if (tb >= 2) acc = MH::mma32(ka[ct][1], ab[tb][1], acc);
+      bf16x4 o;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
+      *reinterpret_cast<bf16x4*>(p.Wn + (16 * tb + l16) * LDK + slot32(32 * w + 16 * ct + 4 * g4)) = o;
+    }
+}
+
+// Phase 3, owners: U = A' V for columns col0 .. col0 + 31 (C layout).
+__device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[2][4], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  MH::F32 vb[2][2], aa[4][2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) vb[nt][sl] = ldc_h(p.VT + (col0 + 16 * nt + l16) * LDT + 32 * sl + 8 * g4);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int sl = 0; sl < (tb >= 2 ? 2 : 1); ++sl) aa[tb][sl] = ldc_h(p.A + (16 * tb + l16) * LDT + 32 * sl + 8 * g4);
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      U[nt][tb] = MH::mma32(aa[tb][0], vb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+      if (tb >= 2) U[nt][tb] = MH::mma32(aa[tb][1], vb[nt][1], U[nt][tb]);
+    }
+}
+
+// Dx[nt][I] += A[rows 16I..] @ S[nt] (A row-major bf16 in LDS, S in registers),
+// every A fragment read before the products.  With SWAP the tiles are held
+// transposed (lane: token l16, state columns 4g..4g+3).
+template <bool SWAP>
+__device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 (&S)[2][DK / 16],
+                                                   floatx4 (&Dx)[2][4], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  MB::F32 af[DK / 32][4];
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) af[ks][I] = ldc_b(A + (16 * I + l16) * LDK + 32 * ks + 8 * g4);
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    MB::F32 sf[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        Dx[nt][I] = SWAP ? MB::mma32(sf[nt], af[ks][I], Dx[nt][I]) : MB::mma32(af[ks][I], sf[nt], Dx[nt][I]);
+  }
+}
+
+// Phase 1, owners: O += P Delta, S <- Diag(gam) S + Kb^T Delta.
+__device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[2][2], floatx4 (&O)[2][4], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  MH::F32 pa[4][2];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int sl = 0; sl < (I >= 2 ? 2 : 1); ++sl) pa[I][sl] = ldc_h(p.P + (16 * I + l16) * LDT + 32 * sl + 8 * g4);
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      O[nt][I] = MH::mma32(Df[nt][0], pa[I][0], O[nt][I]);
+      if (I >= 2) O[nt][I] = MH::mma32(Df[nt][1], pa[I][1], O[nt][I]);
+    }
+}
+
+__device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[2][2], floatx4 (&S)[2][DK / 16],
+                                            int par, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  MH::F32 ka[DK / 16][2];
+#pragma unroll
+  for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ka[rt][h] = ldc_h(p.KbT + (16 * rt + l16) * LDT + 32 * h + 8 * g4);
+  KDA_READS_FIRST();
+#pragma unroll
+  for (int rt = 0; rt < DK / 16; ++rt) {
+    const floatx4 gm = *reinterpret_cast<const floatx4*>(p.gam + par * DK + 16 * rt + 4 * g4);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      S[nt][rt] *= gm;
+      S[nt][rt] = MH::mma32(ka[rt][0], Df[nt][0], S[nt][rt]);
+      S[nt][rt] = MH::mma32(ka[rt][1], Df[nt][1], S[nt][rt]);
+    }
+  }
+}
+
+__device__ __forceinline__ void owner_store(const Ptr& p, const floatx4 (&O)[2][4], int o, __amdgpu_buffer_rsrc_t ro,
+                                            int row_elems, int col, int lane) {
+  bf16* st = p.stg + o * C * LDS_O;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  // O is held transposed: lane has token 16I + l16, columns 16nt + 4g .. + 3
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      bf16x4 v;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = (bf16)O[nt][I][jj];
+      *reinterpret_cast<bf16x4*>(st + (16 * I + l16) * LDS_O + 16 * nt + 4 * g4) = v;
+    }
+  // 64 rows x 64 bytes: four 16-byte vectors per row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = lane + 64 * i;
+    const int row = idx >> 2, cv = idx & 3;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 x = *reinterpret_cast<const u32x2*>(st + row * LDS_O + 8 * cv);
+    const u32x2 y = *reinterpret_cast<const u32x2*>(st + row * LDS_O + 8 * cv + 4);
+    const u32x4 v = {x[0], x[1], y[0], y[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((row * row_elems + col + 8 * cv) * 2), 0, 0);
+  }
+}
+
+}  // namespace pipe
+
+__global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
+  using namespace pipe;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int head, split;
+  block_to_head<1>(blockIdx.x, head, split);
+  if (head >= a.B * a.H) return;
+  const int bb = head / a.H, h = head % a.H;
+  const int nchunks = (a.T + C - 1) / C;
+  Ptr p;
+  p.set(smem_raw);
+  // blocks (0,1) and (2,3) of P and A' above the diagonal are read by the
+  // 32-token reduction slabs and never written otherwise (in P they are spread
+  // over rows 0-15 and 32-47 by the slab order: clear those rows whole, the
+  // written blocks are rewritten every chunk)
+  for (int idx = tid; idx < 2 * 16 * 16; idx += NT) {
+    const int blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+    const int row = 32 * blk + r, col = 32 * blk + 16 + c;
+    p.A[row * LDT + col] = (f16)0.f;
+  }
+  for (int idx = tid; idx < 2 * 16 * 64; idx += NT) {
+    const int blk = idx >> 10, r = (idx >> 6) & 15, c = idx & 63;
+    p.P[(32 * blk + r) * LDT + c] = (f16)0.f;
+  }
+
+  if (wave < 4) {
+    // ---------------------------------------------------------------- owners
+    const int o = wave;
+    const int col0 = 32 * o;
+    floatx4 S[2][DK / 16];
+    load_state<DK, DV, 2>(S, a.S0, head, col0 + (lane & 15), lane);
+    floatx4 O[2][4], U[2][4];
+    for (int n = -1; n < nchunks; ++n) {
+      const bool nxt = n + 1 < nchunks;
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 1: finish chunk n
+      if (n >= 0) {
+        rows_times_state_b<false>(p.Wn, S, U, lane);
+        MH::F32 Df[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          Df[nt][0] = MH::frag32(U[nt][0], U[nt][1]);
+          Df[nt][1] = MH::frag32(U[nt][2], U[nt][3]);
+        }
+        owner_intra(p, Df, O, lane);
+        const int t0 = n * C, nv = min(C, a.T - t0);
+        const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
+        owner_store(p, O, o, ro, a.H * DV, col0, lane);
+        owner_state(p, Df, S, n & 1, lane);
+      }
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 2a: P and off-diagonal L blocks of chunk n+1
+      if (nxt) {
+        // the ten blocks of P and the six off-diagonal blocks of L, four each
+        switch (o) {
+          case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
+                    owner_tiles<4>(p, q, I, J, lane); break; }
+          case 1: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {1, 1, 3, 3}, J[4] = {0, 1, 1, 2};
+                    owner_tiles<4>(p, q, I, J, lane); break; }
+          case 2: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 2, 2, 3}, J[4] = {0, 1, 0, 1};
+                    owner_tiles<4>(p, q, I, J, lane); break; }
+          default: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 3, 2, 3}, J[4] = {2, 2, 1, 0};
+                     owner_tiles<4>(p, q, I, J, lane); break; }
+        }
+      }
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 2b: entry-state readout of chunk n+1
+      if (nxt) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+        rows_times_state_b<true>(p.Qt, S, O, lane);
+      }
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 3: U of chunk n+1
+      if (nxt) owner_u(p, col0, U, lane);
+    }
+    if (a.S_T) store_state<DK, DV, 2>(S, a.S_T, head, col0 + (lane & 15), lane);
+  } else {
+    // --------------------------------------------------------------- workers
+    const int w = wave - 4;
+    WRegs r;
+    if (nchunks > 0) {
+      fetch_qkg(r, a, bb, h, 0, w, lane);
+      fetch_v(r, a, bb, h, 0, w, lane);
+    }
+    for (int n = -1; n < nchunks; ++n) {
+      const bool nxt = n + 1 < nchunks;
+      f16x4 kb[8];
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 1: gates of chunk n+1, then the next loads
+      if (nxt) {
+        if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
+        worker_gates(p, r, w, lane, (n + 1) & 1, kb);
+      }
+      // Loads for chunk n+2, issued unconditionally: past the end the buffer
+      // range is empty and they return zeros.  (Under a branch the loaded
+      // registers would merge with the old ones and the merge would wait for
+      // the loads right here.)
+      fetch_qkg(r, a, bb, h, n + 2, w, lane);
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 2a: Kb^T, V^T; diagonal block w of L and its inverse
+      if (nxt) {
+        worker_transposed(p, r, kb, w, lane);
+        solver_block(p, w, lane);
+      }
+      // after the role switch: loads issued before it were seen to leave one
+      // wavefront's copy of the loaded registers wrong
+      fetch_v(r, a, bb, h, n + 2, w, lane);
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 2b: the rest of A'
+      if (nxt && w == 0) solver_offdiag(p, lane);
+      p.sync(smem_raw);
+      KDA_FRESH_LANE();
+      // phase 3: W
+      if (nxt) worker_w(p, w, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <typename K>
@@ -1287,10 +2019,22 @@ static hipError_t launch_fused_d(const PrefillArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
+  const int bytes = pipe::BYTES;
+  hipError_t e = set_smem(fused_pipe_kernel, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(a.B * a.H, 1)), dim3(NT), bytes, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
   if (a.bf16) {
-    if (a.dk == 128 && a.dv == 128) return launch_fused_d<bf16, 128, 128>(a, s);
+    if (a.dk == 128 && a.dv == 128) {
+      const int ns = a.nsplit > 0 ? a.nsplit : fused_default_nsplit(a.B * a.H, 128);
+      if (ns == 1 && a.pipeline) return launch_pipe(a, s);
+      return launch_fused_d<bf16, 128, 128>(a, s);
+    }
     if (a.dk == 64 && a.dv == 64) return launch_fused_d<bf16, 64, 64>(a, s);
   } else {
     if (a.dk == 64 && a.dv == 64) return launch_fused_d<float, 64, 64>(a, s);
