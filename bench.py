@@ -188,8 +188,8 @@ def main():
                                "kda_recurrent_step 256x32 d128 x64 tokens",
                    "prefill_ms": pre_avg, "decode_ms_per_token_step": dec_step_ms},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic("fused_fwd_kernel"),
-                     "kernel": "fused_fwd_kernel<bf16,128,128,1>",
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic("fused_pipe_kernel"),
+                     "kernel": "fused_pipe_kernel (bf16, d_k = d_v = 128)",
                      "mfma_frac_algorithmic": pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "decode": {"value": dcfg.N * dcfg.steps / (dec_avg * 1e-3), "unit": "tokens/s",
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -80,7 +80,8 @@ struct Layout {
   static constexpr int O_BC = O_GAM + DK * 4;
   // per owner wavefront: its 64 x (16*NTILE) output block, rows padded by 8 bytes
   static constexpr int LDS_O = 16 * StateTiles<DVW>::NTILE + 8 / (int)sizeof(T);
-  static constexpr int O_STG = O_BC + DK * 4;
+  static constexpr int O_QK = O_BC + DK * 4;                          // q_t . k_t per row
+  static constexpr int O_STG = O_QK + C * 4;
   static constexpr int BYTES = O_STG + StateTiles<DVW>::OWN * C * LDS_O * (int)sizeof(T);
 };
 
@@ -91,7 +92,7 @@ struct Smem {
   typedef typename Operands<T>::TF TF;
   TL* Kt; TL* Kh; TL* Wn; TL* Qt; TF* KbT; T* V;
   float* G; TF* Ln; TF* P; float* Ld; TF* Db;
-  float* tot; float* beta; float* gam; float* bC;
+  float* tot; float* beta; float* gam; float* bC; float* qk;
   T* stg;
   // `opaque` is an offset the compiler cannot see through (zero at run time):
   // rebuilding the view with it every chunk keeps LDS address arithmetic
@@ -121,6 +122,7 @@ struct Smem {
     beta = reinterpret_cast<float*>(base + Lay::O_BETA);
     gam = reinterpret_cast<float*>(base + Lay::O_GAM);
     bC = reinterpret_cast<float*>(base + Lay::O_BC);
+    qk = reinterpret_cast<float*>(base + Lay::O_QK);
     stg = reinterpret_cast<T*>(base + Lay::O_STG);
   }
 };
@@ -369,6 +371,21 @@ __device__ __forceinline__ void apply_gates(Smem<T, DK, DVW>& sm, const Vec16* k
       if (DO_KH) *reinterpret_cast<Vec16*>(&sm.Kh[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(kh);
       if (DO_QT) *reinterpret_cast<Vec16*>(&sm.Qt[row * Lay::LDK + c0]) = *reinterpret_cast<Vec16*>(qt);
     }
+    if (DO_QT) {
+      // the diagonal of P is q_t . k_t (the gates cancel): summed in fp32 from
+      // the inputs over the VPR threads that hold one row
+      float d = 0.f;
+      if (idx < RV::TOTAL) {
+        float kf[RV::VN], qf[RV::VN];
+        vec_to_f32<T>(kq[i], kf);
+        vec_to_f32<T>(qq[i], qf);
+#pragma unroll
+        for (int e = 0; e < RV::VN; ++e) d += qf[e] * kf[e];
+      }
+#pragma unroll
+      for (int off = RV::VPR / 2; off > 0; off >>= 1) d += __shfl_xor(d, off);
+      if (idx < RV::TOTAL && idx % RV::VPR == 0) sm.qk[idx / RV::VPR] = d;
+    }
   }
 }
 
@@ -431,6 +448,7 @@ __device__ __forceinline__ void lp_tiles(Smem<T, DK, DVW>& sm, const bool (&isL)
         }
       } else {
         if ((I[t] == J[t] && il < l16) || I[t] < J[t]) val = 0.f;
+        if (I[t] == J[t] && il == l16) val = sm.qk[i];
         sm.P[i * Lay::LDC + jc] = from_f32<TF>(val);
       }
     }
@@ -802,7 +820,7 @@ __device__ __forceinline__ void lp_tile_ct(Smem<T, DK, DVW>& sm, int lane) {
     for (int j = 0; j < 4; ++j) {
       const int il = 4 * g4 + j;
       float val = acc[j];
-      if constexpr (I == J) val = (il >= l16) ? val : 0.f;
+      if constexpr (I == J) val = (il > l16) ? val : (il == l16 ? sm.qk[16 * I + il] : 0.f);
       if constexpr (I < J) val = 0.f;
       sm.P[(16 * I + il) * Lay::LDC + 16 * J + l16] = from_f32<TF>(val);
     }
@@ -1289,7 +1307,8 @@ constexpr int O_P = O_VT + SZ_TR;
 constexpr int O_A = O_P + SZ_CC;
 constexpr int O_BETA = O_A + SZ_CC;
 constexpr int O_GAM = O_BETA + C * 4;    // two chunk parities
-constexpr int BYTES = O_GAM + 2 * DK * 4;
+constexpr int O_QK = O_GAM + 2 * DK * 4;  // q_t . k_t partial sums, per worker
+constexpr int BYTES = O_QK + 4 * C * 4;
 // solver scratch inside the -W region
 constexpr int S_LDT = 0;                           // fp32 [4][16][LDL]: L_II^T
 constexpr int S_LN = S_LDT + 4 * 16 * LDL * 4;     // fp16 [6][16][LDB]: -L_IJ, I > J
@@ -1304,7 +1323,7 @@ static_assert(BYTES <= 160 * 1024, "LDS");
 struct Ptr {
   bf16 *Kt, *Kh, *Qt, *Wn;
   f16 *KtT, *KbT, *VT, *P, *A;
-  float *beta, *gam;
+  float *beta, *gam, *qk;
   float* LdT; f16 *Ln, *D, *Dt;
   bf16* stg;
   __device__ __forceinline__ void set(unsigned char* b) {
@@ -1319,6 +1338,7 @@ struct Ptr {
     A = reinterpret_cast<f16*>(b + O_A);
     beta = reinterpret_cast<float*>(b + O_BETA);
     gam = reinterpret_cast<float*>(b + O_GAM);
+    qk = reinterpret_cast<float*>(b + O_QK);
     LdT = reinterpret_cast<float*>(b + O_WN + S_LDT);
     Ln = reinterpret_cast<f16*>(b + O_WN + S_LN);
     D = reinterpret_cast<f16*>(b + O_WN + S_D);
@@ -1463,11 +1483,15 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gm[4], gm[5], gm[6], gm[7]};
   }
   f16x4 kt_t[8];
+  float qk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float kf[8], qf[8];
     unpack8(r.k[i], kf);
     unpack8(r.q[i], qf);
+    qk[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qk[i] += qf[e] * kf[e];
     bf16x8 kt, kh, qt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1491,6 +1515,14 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
+  // the diagonal of P is q_t . k_t (the gates cancel): summed here in fp32 from
+  // the inputs instead of from the separately rounded gated operands
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qk[i] += __shfl_xor(qk[i], 16);
+    qk[i] += __shfl_xor(qk[i], 32);
+  }
+  if (j == 0) *reinterpret_cast<floatx4*>(p.qk + w * C + 4 * m) = floatx4{qk[0], qk[1], qk[2], qk[3]};
 }
 
 // Phase 2a of a worker: Kb^T and V^T from registers.
@@ -1566,8 +1598,17 @@ __device__ __forceinline__ void owner_tiles(const Ptr& p, const bool (&isP)[NTL]
   for (int t = 0; t < NTL; ++t) {
     f16x4 v;
     if (isP[t]) {
+      float dg = 0.f;
+      if (I[t] == J[t]) {
+        const int row = 16 * I[t] + l16;
+        dg = (p.qk[row] + p.qk[C + row]) + (p.qk[2 * C + row] + p.qk[3 * C + row]);
+      }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)((I[t] > J[t] || l16 >= 4 * g4 + jj) ? acc[t][jj] : 0.f);
+      for (int jj = 0; jj < 4; ++jj) {
+        float x = (I[t] > J[t] || l16 >= 4 * g4 + jj) ? acc[t][jj] : 0.f;
+        if (I[t] == J[t] && l16 == 4 * g4 + jj) x = dg;
+        v[jj] = (f16)x;
+      }
       *reinterpret_cast<f16x4*>(p.P + (16 * I[t] + l16) * LDT + slot32(16 * J[t] + 4 * g4)) = v;
     } else {
       const float bt = -p.beta[16 * I[t] + l16];

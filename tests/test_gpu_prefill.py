@@ -75,6 +75,38 @@ def test_column_split_variants(kda, nsplit, monkeypatch):
     check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"nsplit={nsplit}")
 
 
+PIPE_SHAPES = [(1, 1, 2), (1, 63, 2), (1, 64, 1), (1, 65, 2), (2, 130, 3), (1, 517, 2), (3, 192, 1)]
+
+
+@pytest.mark.parametrize("B,T,H", PIPE_SHAPES, ids=[f"B{b}T{t}H{h}" for b, t, h in PIPE_SHAPES])
+@pytest.mark.parametrize("pipeline", ["1", "0"], ids=["pipelined", "serial"])
+def test_bf16_d128_schedules(kda, B, T, H, pipeline, monkeypatch):
+    """Both whole-sequence schedules for bf16, d = 128 without a column split
+    (the software-pipelined one and the serial one), on single-chunk, exact,
+    ragged and multi-chunk lengths."""
+    monkeypatch.setenv("KDA_FUSED_NSPLIT", "1")
+    monkeypatch.setenv("KDA_FUSED_PIPELINE", pipeline)
+    inp = _case(W.PREFILL_BF16_H16_T4K, B, T, H, seed=300 + T + 7 * H, s0=True)
+    print(f"case bf16 d128 B{B} T{T} H{H} pipeline={pipeline}", flush=True)
+    o, S = _run(kda, inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"B{B}T{T}H{H} pipeline={pipeline}")
+
+
+@pytest.mark.parametrize("pipeline", ["1", "0"], ids=["pipelined", "serial"])
+def test_single_token_seeds(kda, pipeline, monkeypatch):
+    """Single-token prefill over many seeds: the output is q^T S_1 with S_1 one
+    rank-one update of S0, so the current-token term q_t . k_t carries much of
+    it and is summed exactly (it is the gate-free diagonal of P)."""
+    monkeypatch.setenv("KDA_FUSED_NSPLIT", "1")
+    monkeypatch.setenv("KDA_FUSED_PIPELINE", pipeline)
+    for seed in range(8):
+        inp = _case(W.PREFILL_BF16_H16_T4K, 1, 1, 4, seed=4000 + seed, s0=True)
+        o, S = _run(kda, inp)
+        o_ref, S_ref = oracle_prefill(inp)
+        check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"T1 seed {4000 + seed} pipeline={pipeline}")
+
+
 def test_workload_fp32_B1_H2_T256(kda):
     """The fp32 workload at its full size (S0 = 0)."""
     inp = W.prefill_inputs(W.PREFILL_FP32_SMALL, device="cuda")
