@@ -1394,9 +1394,10 @@ __device__ __forceinline__ float row_last(float x) {
 }
 
 // Chunk inputs of one worker wavefront: rows 4m..4m+3 (m = lane % 16) and
-// channels / value columns 32w + 8(lane / 16) .. +8.
+// channels 32w + 8(lane / 16) .. +8.  (Owner o loads the value columns
+// 32o.. of v in the same lane layout.)
 struct WRegs {
-  Vec16 q[4], k[4], g[4], v[4];
+  Vec16 q[4], k[4], g[4];
   uint32_t beta_bits;
 };
 
@@ -1433,7 +1434,7 @@ __device__ __forceinline__ void fetch_qkg(WRegs& r, const PrefillArgs& a, int bb
   r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(lane * a.H * 2), 0, 0);
 }
 
-__device__ __forceinline__ void fetch_v(WRegs& r, const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
+__device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
   const int t0 = n * C, nv = min(C, a.T - t0);
   const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
   const __amdgpu_buffer_rsrc_t rv =
@@ -1442,7 +1443,7 @@ __device__ __forceinline__ void fetch_v(WRegs& r, const PrefillArgs& a, int bb, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, i * a.H * DV * 2, 0);
-    r.v[i].w[0] = x[0]; r.v[i].w[1] = x[1]; r.v[i].w[2] = x[2]; r.v[i].w[3] = x[3];
+    v[i].w[0] = x[0]; v[i].w[1] = x[1]; v[i].w[2] = x[2]; v[i].w[3] = x[3];
   }
 }
 
@@ -1525,18 +1526,24 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w
   if (j == 0) *reinterpret_cast<floatx4*>(p.qk + w * C + 4 * m) = floatx4{qk[0], qk[1], qk[2], qk[3]};
 }
 
-// Phase 2a of a worker: Kb^T and V^T from registers.
-__device__ __forceinline__ void worker_transposed(const Ptr& p, const WRegs& r, const f16x4 (&kb)[8], int w,
-                                                  int lane) {
+// Phase 2a of a worker: Kb^T from registers.
+__device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], int w, int lane) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KbT + (c0 + e) * LDT + slot32(4 * m)) = kb[e];
+}
+
+// Phase 2a of owner o: V^T rows 32o .. 32o + 31 (its own value columns) from
+// registers, 4 tokens per 8-byte store.
+__device__ __forceinline__ void owner_vt(const Ptr& p, const Vec16 (&v)[4], int o, int lane) {
+  const int j = lane >> 4, m = lane & 15;
+  const int c0 = 32 * o + 8 * j;
   f16x4 vt[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float vf[8];
-    unpack8(r.v[i], vf);
+    unpack8(v[i], vf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) vt[e][i] = (f16)vf[e];
   }
@@ -1586,10 +1593,10 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
 
 __device__ __forceinline__ int ln_block(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// Owners in phase 2a: blocks (I_t, J_t) of P = Tril(Qt Kh^T) (isP[t]) and
+// Workers in phase 2a: blocks (I_t, J_t) of P = Tril(Qt Kh^T) (isP[t]) and
 // off-diagonal blocks of L = Diag(beta) Kt Kh^T, stored as -L, all fp16.
 template <int NTL>
-__device__ __forceinline__ void owner_tiles(const Ptr& p, const bool (&isP)[NTL], const int (&I)[NTL],
+__device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[NTL], const int (&I)[NTL],
                                             const int (&J)[NTL], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   floatx4 acc[NTL];
@@ -1619,7 +1626,7 @@ __device__ __forceinline__ void owner_tiles(const Ptr& p, const bool (&isP)[NTL]
   }
 }
 
-// Worker I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32
+// Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32
 // (lane c = l16 computes column c of D_I by forward substitution and row c by
 // the transposed system; the four 16-lane groups repeat the same work and the
 // first one writes).  Writes D_I, D_I^T and block (I, I) of A' = D_I Diag(beta).
@@ -1638,40 +1645,34 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   }
   const int c = l16;
   const float* Lt = p.LdT + I * 16 * LDL;
-  // columns mm of L_II, entries 4 q4 .. 4 q4 + 3 (only q4 >= (mm + 1) / 4 used)
-  floatx4 col[15][4];
-#pragma unroll
-  for (int mm = 0; mm < 8; ++mm)
-#pragma unroll
-    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4) col[mm][q4] = *reinterpret_cast<const floatx4*>(Lt + mm * LDL + 4 * q4);
   // x = column c of D_I: forward substitution, column by column of L
+  // (row mm of L^T holds column mm of L; entries 4q4..4q4+3, q4 >= (mm+1)/4)
   float x[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
   for (int mm = 0; mm < 15; ++mm) {
-    if (mm == 4) {
-      // second half of the columns, read while the first half is used
 #pragma unroll
-      for (int m2 = 8; m2 < 15; ++m2)
-#pragma unroll
-        for (int q4 = (m2 + 1) / 4; q4 < 4; ++q4)
-          col[m2][q4] = *reinterpret_cast<const floatx4*>(Lt + m2 * LDL + 4 * q4);
-    }
-#pragma unroll
-    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4)
+    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4) {
+      const floatx4 col = *reinterpret_cast<const floatx4*>(Lt + mm * LDL + 4 * q4);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (4 * q4 + u > mm) x[4 * q4 + u] -= col[mm][q4][u] * x[mm];
+        if (4 * q4 + u > mm) x[4 * q4 + u] -= col[u] * x[mm];
+    }
   }
   // d = row c of D_I: D_I (I + L_II) = I, solved from the last entry down;
-  // entry r takes L[m][r] (m > r), i.e. row r of L^T -- the same registers
+  // entry r takes L[m][r] (m > r), i.e. row r of L^T
   float d[16];
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
     float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-    for (int m = 15; m > r; --m) acc -= col[r][m >> 2][m & 3] * d[m];   // d[r + 1] last
+    for (int q4 = 3; q4 >= (r + 1) / 4; --q4) {
+      const floatx4 row = *reinterpret_cast<const floatx4*>(Lt + r * LDL + 4 * q4);
+#pragma unroll
+      for (int u = 3; u >= 0; --u)
+        if (4 * q4 + u > r) acc -= row[u] * d[4 * q4 + u];   // d[r + 1] last
+    }
     d[r] = acc;
   }
   f16x8 lo, hi, dlo, dhi, alo, ahi;
@@ -1698,7 +1699,7 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   }
 }
 
-// Worker 0 in phase 2b: off-diagonal blocks of A = (I + L)^-1,
+// Owner 0 in phase 2b: off-diagonal blocks of A = (I + L)^-1,
 //   A_IJ = D_I sum_{J <= K < I} (-L_IK) A_KJ   (A_KK = D_K),
 // level by level, intermediate blocks kept in registers; A'_IJ = A_IJ Diag(beta_J).
 __device__ __forceinline__ void solver_offdiag(const Ptr& p, int lane) {
@@ -1800,22 +1801,28 @@ template <bool SWAP>
 __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 (&S)[2][DK / 16],
                                                    floatx4 (&Dx)[2][4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  MB::F32 af[DK / 32][4];
+  // two halves of the reduction, each half's fragments read ahead of its
+  // products (the second half's reads overlap the first half's MFMAs)
 #pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks)
+  for (int hf = 0; hf < 2; ++hf) {
+    MB::F32 af[2][4];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) af[ks][I] = ldc_b(A + (16 * I + l16) * LDK + 32 * ks + 8 * g4);
-  KDA_READS_FIRST();
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) {
-    MB::F32 sf[2];
+      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + (16 * I + l16) * LDK + 32 * (2 * hf + k2) + 8 * g4);
+    KDA_READS_FIRST();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ks = 2 * hf + k2;
+      MB::F32 sf[2];
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+      for (int nt = 0; nt < 2; ++nt) sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        Dx[nt][I] = SWAP ? MB::mma32(sf[nt], af[ks][I], Dx[nt][I]) : MB::mma32(af[ks][I], sf[nt], Dx[nt][I]);
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          Dx[nt][I] = SWAP ? MB::mma32(sf[nt], af[k2][I], Dx[nt][I]) : MB::mma32(af[k2][I], sf[nt], Dx[nt][I]);
+    }
   }
 }
 
@@ -1840,20 +1847,25 @@ __device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[2]
 __device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[2][2], floatx4 (&S)[2][DK / 16],
                                             int par, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  MH::F32 ka[DK / 16][2];
 #pragma unroll
-  for (int rt = 0; rt < DK / 16; ++rt)
+  for (int hf = 0; hf < 2; ++hf) {
+    MH::F32 ka[DK / 32][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ka[rt][h] = ldc_h(p.KbT + (16 * rt + l16) * LDT + 32 * h + 8 * g4);
-  KDA_READS_FIRST();
+    for (int r2 = 0; r2 < DK / 32; ++r2)
 #pragma unroll
-  for (int rt = 0; rt < DK / 16; ++rt) {
-    const floatx4 gm = *reinterpret_cast<const floatx4*>(p.gam + par * DK + 16 * rt + 4 * g4);
+      for (int h = 0; h < 2; ++h)
+        ka[r2][h] = ldc_h(p.KbT + (16 * (hf * DK / 32 + r2) + l16) * LDT + 32 * h + 8 * g4);
+    KDA_READS_FIRST();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      S[nt][rt] *= gm;
-      S[nt][rt] = MH::mma32(ka[rt][0], Df[nt][0], S[nt][rt]);
-      S[nt][rt] = MH::mma32(ka[rt][1], Df[nt][1], S[nt][rt]);
+    for (int r2 = 0; r2 < DK / 32; ++r2) {
+      const int rt = hf * DK / 32 + r2;
+      const floatx4 gm = *reinterpret_cast<const floatx4*>(p.gam + par * DK + 16 * rt + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        S[nt][rt] *= gm;
+        S[nt][rt] = MH::mma32(ka[r2][0], Df[nt][0], S[nt][rt]);
+        S[nt][rt] = MH::mma32(ka[r2][1], Df[nt][1], S[nt][rt]);
+      }
     }
   }
 }
@@ -1920,6 +1932,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     floatx4 S[2][DK / 16];
     load_state<DK, DV, 2>(S, a.S0, head, col0 + (lane & 15), lane);
     floatx4 O[2][4], U[2][4];
+    Vec16 vr[4];
+    if (nchunks > 0) fetch_v(vr, a, bb, h, 0, o, lane);
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       p.sync(smem_raw);
@@ -1943,33 +1957,33 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2a: P and off-diagonal L blocks of chunk n+1
+      // phase 2a: V^T; diagonal block o of L and its inverse (chunk n+1)
       if (nxt) {
-        // the ten blocks of P and the six off-diagonal blocks of L, four each
-        switch (o) {
-          case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
-                    owner_tiles<4>(p, q, I, J, lane); break; }
-          case 1: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {1, 1, 3, 3}, J[4] = {0, 1, 1, 2};
-                    owner_tiles<4>(p, q, I, J, lane); break; }
-          case 2: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 2, 2, 3}, J[4] = {0, 1, 0, 1};
-                    owner_tiles<4>(p, q, I, J, lane); break; }
-          default: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 3, 2, 3}, J[4] = {2, 2, 1, 0};
-                     owner_tiles<4>(p, q, I, J, lane); break; }
-        }
+        owner_vt(p, vr, o, lane);
+        solver_block(p, o, lane);
       }
+      // values of chunk n+2: unconditional (zeros past the end), and after the
+      // role switch -- loads issued just before such a switch were seen to
+      // leave one wavefront's copy of the loaded registers wrong
+      fetch_v(vr, a, bb, h, n + 2, o, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: entry-state readout of chunk n+1
-      if (nxt) {
+      // phase 2b: the rest of A' (owner 0), entry-state readout of chunk n+1
+      if (nxt && o == 0) solver_offdiag(p, lane);
+      // O and U are (re)defined on every path, so their previous values are
+      // not kept alive through the other phases
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-        rows_times_state_b<true>(p.Qt, S, O, lane);
-      }
+        for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (nxt) rows_times_state_b<true>(p.Qt, S, O, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: U of chunk n+1
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) U[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (nxt) owner_u(p, col0, U, lane);
     }
     if (a.S_T) store_state<DK, DV, 2>(S, a.S_T, head, col0 + (lane & 15), lane);
@@ -1977,10 +1991,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
     WRegs r;
-    if (nchunks > 0) {
-      fetch_qkg(r, a, bb, h, 0, w, lane);
-      fetch_v(r, a, bb, h, 0, w, lane);
-    }
+    if (nchunks > 0) fetch_qkg(r, a, bb, h, 0, w, lane);
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8];
@@ -1991,25 +2002,29 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
         worker_gates(p, r, w, lane, (n + 1) & 1, kb);
       }
-      // Loads for chunk n+2, issued unconditionally: past the end the buffer
-      // range is empty and they return zeros.  (Under a branch the loaded
-      // registers would merge with the old ones and the merge would wait for
-      // the loads right here.)
-      fetch_qkg(r, a, bb, h, n + 2, w, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2a: Kb^T, V^T; diagonal block w of L and its inverse
+      // phase 2a: Kb^T; P blocks and the off-diagonal blocks of L, four each
       if (nxt) {
-        worker_transposed(p, r, kb, w, lane);
-        solver_block(p, w, lane);
+        worker_kbt(p, kb, w, lane);
+        switch (w) {
+          case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
+                    lp_block_tiles<4>(p, q, I, J, lane); break; }
+          case 1: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {1, 1, 3, 3}, J[4] = {0, 1, 1, 2};
+                    lp_block_tiles<4>(p, q, I, J, lane); break; }
+          case 2: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 2, 2, 3}, J[4] = {0, 1, 0, 1};
+                    lp_block_tiles<4>(p, q, I, J, lane); break; }
+          default: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 3, 2, 3}, J[4] = {2, 2, 1, 0};
+                     lp_block_tiles<4>(p, q, I, J, lane); break; }
+        }
       }
-      // after the role switch: loads issued before it were seen to leave one
-      // wavefront's copy of the loaded registers wrong
-      fetch_v(r, a, bb, h, n + 2, w, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: the rest of A'
-      if (nxt && w == 0) solver_offdiag(p, lane);
+      // phase 2b: loads for chunk n+2 (the workers have nothing else here),
+      // issued unconditionally -- past the end the buffer range is empty and
+      // they return zeros; under a branch the loaded registers would merge with
+      // the old ones and the merge would wait for the loads
+      fetch_qkg(r, a, bb, h, n + 2, w, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
