@@ -1405,6 +1405,31 @@ __device__ __forceinline__ uint32_t wlane_off(int H, int w, int lane) {
   return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * (lane >> 4)) * 2);
 }
 
+// Buffer resources and offsets of one chunk's q, k, g, beta for a worker.
+struct QkgSrc {
+  __amdgpu_buffer_rsrc_t q, k, g, b;
+  uint32_t vo, boff;
+  int rs;
+  __device__ __forceinline__ QkgSrc(const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
+    const int t0 = n * C, nv = min(C, a.T - t0);
+    const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+    const uint32_t bytes = chunk_bytes(nv, a.H * DK, DK, 2);
+    q = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok0 * DK, bytes);
+    k = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok0 * DK, bytes);
+    g = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0 * DK, bytes);
+    b = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, 2));
+    vo = wlane_off(a.H, w, lane);
+    boff = (uint32_t)(lane * a.H * 2);
+    rs = a.H * DK * 2;
+  }
+};
+__device__ __forceinline__ Vec16 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t vo, int so) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0);
+  Vec16 v;
+  v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
+  return v;
+}
+
 __device__ __forceinline__ void fetch_qkg(WRegs& r, const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
   const int t0 = n * C, nv = min(C, a.T - t0);
   const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
@@ -1451,8 +1476,13 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
 // then Kt = 2^b k, Kh = 2^-b k, Qt = 2^b q (row-major bf16), Kt^T (fp16), the
 // chunk decay gam = 2^b_C of its channels, and Kb = gam 2^-b k kept in
 // registers (kb[e] = tokens 4m..4m+3 of channel e) for phase 2a.
-__device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w, int lane, int par,
-                                             f16x4 (&kb)[8]) {
+//
+// The next-but-one chunk's inputs are loaded into the same registers as each
+// one is consumed (g after the prefix sum starts, k and q row by row), so the
+// loads spread over this phase's arithmetic instead of arriving as one burst;
+// each group is pinned in place by scheduling fences.
+__device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int lane, int par,
+                                             f16x4 (&kb)[8], const QkgSrc& nx) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
   float b[4][8];
@@ -1462,6 +1492,10 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w
 #pragma unroll
     for (int e = 0; e < 8; ++e) b[i][e] *= kLog2e;
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.g[i] = ld16(nx.g, nx.vo, i * nx.rs);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 1; i < 4; ++i)
 #pragma unroll
@@ -1490,6 +1524,10 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, const WRegs& r, int w
     float kf[8], qf[8];
     unpack8(r.k[i], kf);
     unpack8(r.q[i], qf);
+    __builtin_amdgcn_sched_barrier(0);
+    r.k[i] = ld16(nx.k, nx.vo, i * nx.rs);
+    r.q[i] = ld16(nx.q, nx.vo, i * nx.rs);
+    __builtin_amdgcn_sched_barrier(0);
     qk[i] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qk[i] += qf[e] * kf[e];
@@ -1991,16 +2029,21 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
     WRegs r;
-    if (nchunks > 0) fetch_qkg(r, a, bb, h, 0, w, lane);
+    fetch_qkg(r, a, bb, h, 0, w, lane);   // zeros when the sequence is empty
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8];
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 1: gates of chunk n+1, then the next loads
-      if (nxt) {
+      // phase 1: gates of chunk n+1 with the loads of chunk n+2 interleaved.
+      // Runs on every slot (past the last chunk on zeros, into arrays nobody
+      // reads again), so the loads are never under a branch: loaded registers
+      // merging with old ones at a join would make the merge wait for them.
+      {
+        const QkgSrc nx(a, bb, h, n + 2, w, lane);
         if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
-        worker_gates(p, r, w, lane, (n + 1) & 1, kb);
+        r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
+        worker_gates(p, r, w, lane, (n + 1) & 1, kb, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
@@ -2020,11 +2063,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: loads for chunk n+2 (the workers have nothing else here),
-      // issued unconditionally -- past the end the buffer range is empty and
-      // they return zeros; under a branch the loaded registers would merge with
-      // the old ones and the merge would wait for the loads
-      fetch_qkg(r, a, bb, h, n + 2, w, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
