@@ -1308,7 +1308,8 @@ constexpr int O_A = O_P + SZ_CC;
 constexpr int O_BETA = O_A + SZ_CC;
 constexpr int O_GAM = O_BETA + C * 4;    // two chunk parities
 constexpr int O_QK = O_GAM + 2 * DK * 4;  // q_t . k_t partial sums, per worker
-constexpr int BYTES = O_QK + 4 * C * 4;
+constexpr int NQK = 16;                   // q.k partial sums per token (worker lane groups)
+constexpr int BYTES = O_QK + NQK * C * 4;
 // solver scratch inside the -W region
 constexpr int S_LDT = 0;                           // fp32 [4][16][LDL]: L_II^T
 constexpr int S_LN = S_LDT + 4 * 16 * LDL * 4;     // fp16 [6][16][LDB]: -L_IJ, I > J
@@ -1473,16 +1474,17 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
 }
 
 // Phase 1 of a worker: log2-scaled in-chunk prefix sums of its gate channels,
-// then Kt = 2^b k, Kh = 2^-b k, Qt = 2^b q (row-major bf16), Kt^T (fp16), the
-// chunk decay gam = 2^b_C of its channels, and Kb = gam 2^-b k kept in
-// registers (kb[e] = tokens 4m..4m+3 of channel e) for phase 2a.
+// then Kt = 2^b k, Kh = 2^-b k, Qt = 2^b q (row-major bf16), the chunk decay
+// gam = 2^b_C of its channels and the q.k partial sums; Kt and Kb = gam 2^-b k
+// stay in registers as fp16 (kt_t[e], kb[e] = tokens 4m..4m+3 of channel e)
+// and are stored transposed in phase 2a.
 //
 // The next-but-one chunk's inputs are loaded into the same registers as each
 // one is consumed (g after the prefix sum starts, k and q row by row), so the
 // loads spread over this phase's arithmetic instead of arriving as one burst;
 // each group is pinned in place by scheduling fences.
 __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int lane, int par,
-                                             f16x4 (&kb)[8], const QkgSrc& nx) {
+                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
   float b[4][8];
@@ -1517,7 +1519,6 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gm[0], gm[1], gm[2], gm[3]};
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gm[4], gm[5], gm[6], gm[7]};
   }
-  f16x4 kt_t[8];
   float qk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1552,22 +1553,19 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
     *reinterpret_cast<bf16x4*>(p.Qt + r0) = __builtin_shufflevector(qt, qt, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4*>(p.Qt + r1) = __builtin_shufflevector(qt, qt, 4, 5, 6, 7);
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
-  // the diagonal of P is q_t . k_t (the gates cancel): summed here in fp32 from
-  // the inputs instead of from the separately rounded gated operands
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    qk[i] += __shfl_xor(qk[i], 16);
-    qk[i] += __shfl_xor(qk[i], 32);
-  }
-  if (j == 0) *reinterpret_cast<floatx4*>(p.qk + w * C + 4 * m) = floatx4{qk[0], qk[1], qk[2], qk[3]};
+  // the diagonal of P is q_t . k_t (the gates cancel): summed in fp32 from
+  // the inputs instead of from the separately rounded gated operands; each
+  // lane group leaves its 8-channel partial sums, which the P tiles add up
+  *reinterpret_cast<floatx4*>(p.qk + (4 * w + j) * C + 4 * m) = floatx4{qk[0], qk[1], qk[2], qk[3]};
 }
 
-// Phase 2a of a worker: Kb^T from registers.
-__device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], int w, int lane) {
+// Phase 2a of a worker: Kt^T and Kb^T from registers (4 tokens per store).
+__device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], const f16x4 (&kt_t)[8], int w,
+                                           int lane) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KbT + (c0 + e) * LDT + slot32(4 * m)) = kb[e];
 }
@@ -1646,7 +1644,14 @@ __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[N
       float dg = 0.f;
       if (I[t] == J[t]) {
         const int row = 16 * I[t] + l16;
-        dg = (p.qk[row] + p.qk[C + row]) + (p.qk[2 * C + row] + p.qk[3 * C + row]);
+        float sp[NQK];
+#pragma unroll
+        for (int u = 0; u < NQK; ++u) sp[u] = p.qk[u * C + row];
+#pragma unroll
+        for (int st = 1; st < NQK; st *= 2)
+#pragma unroll
+          for (int u = 0; u + st < NQK; u += 2 * st) sp[u] += sp[u + st];
+        dg = sp[0];
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -1683,6 +1688,8 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   }
   const int c = l16;
   const float* Lt = p.LdT + I * 16 * LDL;
+  f16x8 lo, hi;
+  float d[16];
   // x = column c of D_I: forward substitution, column by column of L
   // (row mm of L^T holds column mm of L; entries 4q4..4q4+3, q4 >= (mm+1)/4)
   float x[16];
@@ -1700,7 +1707,6 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   }
   // d = row c of D_I: D_I (I + L_II) = I, solved from the last entry down;
   // entry r takes L[m][r] (m > r), i.e. row r of L^T
-  float d[16];
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
     float acc = (r == c) ? 1.f : 0.f;
@@ -1713,7 +1719,9 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
     }
     d[r] = acc;
   }
-  f16x8 lo, hi, dlo, dhi, alo, ahi;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) { lo[r] = (f16)x[r]; hi[r] = (f16)x[8 + r]; }
+  f16x8 dlo, dhi, alo, ahi;
   const floatx4 b0 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I);
   const floatx4 b1 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4);
   const floatx4 b2 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 8);
@@ -1722,7 +1730,6 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
                         b2[0], b2[1], b2[2], b2[3], b3[0], b3[1], b3[2], b3[3]};
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    lo[r] = (f16)x[r]; hi[r] = (f16)x[8 + r];
     dlo[r] = (f16)d[r]; dhi[r] = (f16)d[8 + r];
     alo[r] = (f16)(d[r] * bb[r]); ahi[r] = (f16)(d[8 + r] * bb[8 + r]);
   }
@@ -1811,11 +1818,12 @@ __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
 }
 
 // Phase 3, owners: U = A' V for columns col0 .. col0 + 31 (C layout).
-__device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[2][4], int lane) {
+template <int NTL>
+__device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[NTL][4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  MH::F32 vb[2][2], aa[4][2];
+  MH::F32 vb[NTL][2], aa[4][2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) vb[nt][sl] = ldc_h(p.VT + (col0 + 16 * nt + l16) * LDT + 32 * sl + 8 * g4);
 #pragma unroll
@@ -1826,7 +1834,7 @@ __device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[2][
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTL; ++nt) {
       U[nt][tb] = MH::mma32(aa[tb][0], vb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
       if (tb >= 2) U[nt][tb] = MH::mma32(aa[tb][1], vb[nt][1], U[nt][tb]);
     }
@@ -1835,9 +1843,9 @@ __device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[2][
 // Dx[nt][I] += A[rows 16I..] @ S[nt] (A row-major bf16 in LDS, S in registers),
 // every A fragment read before the products.  With SWAP the tiles are held
 // transposed (lane: token l16, state columns 4g..4g+3).
-template <bool SWAP>
-__device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 (&S)[2][DK / 16],
-                                                   floatx4 (&Dx)[2][4], int lane) {
+template <bool SWAP, int NTL>
+__device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 (&S)[NTL][DK / 16],
+                                                   floatx4 (&Dx)[NTL][4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   // two halves of the reduction, each half's fragments read ahead of its
   // products (the second half's reads overlap the first half's MFMAs)
@@ -1852,20 +1860,21 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int ks = 2 * hf + k2;
-      MB::F32 sf[2];
+      MB::F32 sf[NTL];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+      for (int nt = 0; nt < NTL; ++nt) sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTL; ++nt)
           Dx[nt][I] = SWAP ? MB::mma32(sf[nt], af[k2][I], Dx[nt][I]) : MB::mma32(af[k2][I], sf[nt], Dx[nt][I]);
     }
   }
 }
 
 // Phase 1, owners: O += P Delta, S <- Diag(gam) S + Kb^T Delta.
-__device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[2][2], floatx4 (&O)[2][4], int lane) {
+template <int NTL>
+__device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[NTL][2], floatx4 (&O)[NTL][4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   MH::F32 pa[4][2];
 #pragma unroll
@@ -1876,13 +1885,14 @@ __device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[2]
 #pragma unroll
   for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTL; ++nt) {
       O[nt][I] = MH::mma32(Df[nt][0], pa[I][0], O[nt][I]);
       if (I >= 2) O[nt][I] = MH::mma32(Df[nt][1], pa[I][1], O[nt][I]);
     }
 }
 
-__device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[2][2], floatx4 (&S)[2][DK / 16],
+template <int NTL>
+__device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[NTL][2], floatx4 (&S)[NTL][DK / 16],
                                             int par, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
@@ -1899,7 +1909,7 @@ __device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[2]
       const int rt = hf * DK / 32 + r2;
       const floatx4 gm = *reinterpret_cast<const floatx4*>(p.gam + par * DK + 16 * rt + 4 * g4);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTL; ++nt) {
         S[nt][rt] *= gm;
         S[nt][rt] = MH::mma32(ka[r2][0], Df[nt][0], S[nt][rt]);
         S[nt][rt] = MH::mma32(ka[r2][1], Df[nt][1], S[nt][rt]);
@@ -2006,8 +2016,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       fetch_v(vr, a, bb, h, n + 2, o, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: the rest of A' (owner 0), entry-state readout of chunk n+1
-      if (nxt && o == 0) solver_offdiag(p, lane);
+      // phase 2b: entry-state readout of chunk n+1
       // O and U are (re)defined on every path, so their previous values are
       // not kept alive through the other phases
 #pragma unroll
@@ -2032,7 +2041,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     fetch_qkg(r, a, bb, h, 0, w, lane);   // zeros when the sequence is empty
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
-      f16x4 kb[8];
+      f16x4 kb[8], kt_t[8];
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 1: gates of chunk n+1 with the loads of chunk n+2 interleaved.
@@ -2043,13 +2052,13 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         const QkgSrc nx(a, bb, h, n + 2, w, lane);
         if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
         r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
-        worker_gates(p, r, w, lane, (n + 1) & 1, kb, nx);
+        worker_gates(p, r, w, lane, (n + 1) & 1, kb, kt_t, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2a: Kb^T; P blocks and the off-diagonal blocks of L, four each
+      // phase 2a: Kt^T, Kb^T; P blocks and the off-diagonal blocks of L, four each
       if (nxt) {
-        worker_kbt(p, kb, w, lane);
+        worker_kbt(p, kb, kt_t, w, lane);
         switch (w) {
           case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
                     lp_block_tiles<4>(p, q, I, J, lane); break; }
@@ -2063,6 +2072,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
+      // phase 2b: worker 0: off-diagonal blocks of A'
+      if (nxt && w == 0) solver_offdiag(p, lane);
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
