@@ -1372,6 +1372,22 @@ __device__ __forceinline__ int slot32(int k) {
   return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
 }
 
+// Bank-conflict-free placement of the row-major bf16 arrays (Kt, Kh, Qt, -W).
+// A worker store covers rows 4m + i (m = 0..15) of one column block: with
+// rows in natural order those fall on 4 bank offsets only (the row pitch is
+// 68 dwords), a 4-way conflict.  Token row t is therefore kept at row prow(t),
+// which rotates each group of four rows by (t / 16) mod 4: the 16 rows of a
+// worker store then fall on 16 distinct bank offsets, and the 16 rows 16I + i
+// of an MFMA fragment read stay on distinct offsets too.
+__device__ __forceinline__ int prow(int t) { return (t & ~3) | ((t + (t >> 4)) & 3); }
+
+// Channel group (8 channels) of lane group j = lane / 16 in the worker and
+// owner input layouts.  Groups 0, 3 share a 32-lane half and groups 1, 2 the
+// other, so that each half of a row-major store lands on both dword pairs of
+// a 16-byte bank slot (group >> 1 differs) and each half of a transposed
+// store on both 32-bank halves (group & 1 differs).
+__device__ __forceinline__ int chgrp(int j) { return (3 * (j & 1)) ^ (j >> 1); }
+
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
 // the scheduler sinks each read next to its product to save registers, and
 // every product then waits for a full LDS round trip).
@@ -1395,7 +1411,7 @@ __device__ __forceinline__ float row_last(float x) {
 }
 
 // Chunk inputs of one worker wavefront: rows 4m..4m+3 (m = lane % 16) and
-// channels 32w + 8(lane / 16) .. +8.  (Owner o loads the value columns
+// channels 32w + 8 chgrp(lane / 16) .. +8.  (Owner o loads the value columns
 // 32o.. of v in the same lane layout.)
 struct WRegs {
   Vec16 q[4], k[4], g[4];
@@ -1403,7 +1419,7 @@ struct WRegs {
 };
 
 __device__ __forceinline__ uint32_t wlane_off(int H, int w, int lane) {
-  return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * (lane >> 4)) * 2);
+  return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * chgrp(lane >> 4)) * 2);
 }
 
 // Buffer resources and offsets of one chunk's q, k, g, beta for a worker.
@@ -1486,7 +1502,7 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
 __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int lane, int par,
                                              f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * j;
+  const int c0 = 32 * w + 8 * chgrp(j);
   float b[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1545,7 +1561,7 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
       kb[e][i] = (f16)(d * gm[e]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
-    const int r0 = (4 * m + i) * LDK + slot32(c0), r1 = (4 * m + i) * LDK + slot32(c0 + 4);
+    const int r0 = prow(4 * m + i) * LDK + slot32(c0), r1 = prow(4 * m + i) * LDK + slot32(c0 + 4);
     *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
     *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
@@ -1563,7 +1579,7 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
 __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], const f16x4 (&kt_t)[8], int w,
                                            int lane) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * j;
+  const int c0 = 32 * w + 8 * chgrp(j);
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
 #pragma unroll
@@ -1574,7 +1590,7 @@ __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], c
 // registers, 4 tokens per 8-byte store.
 __device__ __forceinline__ void owner_vt(const Ptr& p, const Vec16 (&v)[4], int o, int lane) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * o + 8 * j;
+  const int c0 = 32 * o + 8 * chgrp(j);
   f16x4 vt[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1614,8 +1630,8 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + (16 * I[t] + l16) * LDK + 32 * ks + 8 * g4);
-      bf[t][ks] = ldc_b(Kh + (16 * J[t] + l16) * LDK + 32 * ks + 8 * g4);
+      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + prow(16 * I[t] + l16) * LDK + 32 * ks + 8 * g4);
+      bf[t][ks] = ldc_b(Kh + prow(16 * J[t] + l16) * LDK + 32 * ks + 8 * g4);
     }
   KDA_READS_FIRST();
 #pragma unroll
@@ -1669,10 +1685,14 @@ __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[N
   }
 }
 
-// Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32
-// (lane c = l16 computes column c of D_I by forward substitution and row c by
-// the transposed system; the four 16-lane groups repeat the same work and the
-// first one writes).  Writes D_I, D_I^T and block (I, I) of A' = D_I Diag(beta).
+// Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32.
+// Lane c = l16 computes column c of D_I by forward substitution (the four
+// 16-lane groups repeat the same work); lane group g then holds entries
+// 4g..4g+3 of that column, i.e. D_I in MFMA accumulator layout.  The rows of
+// D_I come from a product with the identity (an MFMA whose A operand is read
+// from an accumulator tile multiplies by that tile's transpose), taken on a
+// two-term fp16 split so the transposed values keep fp32 accuracy.  Writes
+// D_I, D_I^T and block (I, I) of A' = D_I Diag(beta), 8 bytes per lane.
 __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   {
@@ -1688,8 +1708,6 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   }
   const int c = l16;
   const float* Lt = p.LdT + I * 16 * LDL;
-  f16x8 lo, hi;
-  float d[16];
   // x = column c of D_I: forward substitution, column by column of L
   // (row mm of L^T holds column mm of L; entries 4q4..4q4+3, q4 >= (mm+1)/4)
   float x[16];
@@ -1705,43 +1723,33 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
         if (4 * q4 + u > mm) x[4 * q4 + u] -= col[u] * x[mm];
     }
   }
-  // d = row c of D_I: D_I (I + L_II) = I, solved from the last entry down;
-  // entry r takes L[m][r] (m > r), i.e. row r of L^T
+  // entries 4g..4g+3 of the column: D_I in accumulator layout
+  floatx4 dc;
 #pragma unroll
-  for (int r = 15; r >= 0; --r) {
-    float acc = (r == c) ? 1.f : 0.f;
+  for (int jj = 0; jj < 4; ++jj)
+    dc[jj] = g4 == 0 ? x[jj] : g4 == 1 ? x[4 + jj] : g4 == 2 ? x[8 + jj] : x[12 + jj];
+  MH::F16 dh, dl, eye;
 #pragma unroll
-    for (int q4 = 3; q4 >= (r + 1) / 4; --q4) {
-      const floatx4 row = *reinterpret_cast<const floatx4*>(Lt + r * LDL + 4 * q4);
-#pragma unroll
-      for (int u = 3; u >= 0; --u)
-        if (4 * q4 + u > r) acc -= row[u] * d[4 * q4 + u];   // d[r + 1] last
-    }
-    d[r] = acc;
+  for (int jj = 0; jj < 4; ++jj) {
+    dh[jj] = (f16)dc[jj];
+    dl[jj] = (f16)(dc[jj] - (float)dh[jj]);
+    eye[jj] = (f16)(4 * g4 + jj == l16 ? 1.f : 0.f);
   }
+  // D_I^T row c = column c of D_I, entries 4g..4g+3
+  *reinterpret_cast<f16x4*>(p.Dt + (I * 16 + c) * LDB + 4 * g4) = dh;
+  // lane (g, c): D_I[c][4g..4g+3]
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  const floatx4 dr = MH::mma16(dh, eye, MH::mma16(dl, eye, z));
+  const floatx4 bt = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4 * g4);
+  f16x4 drow, arow;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) { lo[r] = (f16)x[r]; hi[r] = (f16)x[8 + r]; }
-  f16x8 dlo, dhi, alo, ahi;
-  const floatx4 b0 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I);
-  const floatx4 b1 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4);
-  const floatx4 b2 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 8);
-  const floatx4 b3 = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 12);
-  const float bb[16] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3],
-                        b2[0], b2[1], b2[2], b2[3], b3[0], b3[1], b3[2], b3[3]};
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    dlo[r] = (f16)d[r]; dhi[r] = (f16)d[8 + r];
-    alo[r] = (f16)(d[r] * bb[r]); ahi[r] = (f16)(d[8 + r] * bb[8 + r]);
+  for (int jj = 0; jj < 4; ++jj) {
+    drow[jj] = (f16)dr[jj];
+    arow[jj] = (f16)(dr[jj] * bt[jj]);
   }
-  if (lane < 16) {
-    *reinterpret_cast<f16x8*>(p.Dt + (I * 16 + c) * LDB) = lo;
-    *reinterpret_cast<f16x8*>(p.Dt + (I * 16 + c) * LDB + 8) = hi;
-    *reinterpret_cast<f16x8*>(p.D + (I * 16 + c) * LDB) = dlo;
-    *reinterpret_cast<f16x8*>(p.D + (I * 16 + c) * LDB + 8) = dhi;
-    // row 16I + c of A', columns 16I .. 16I + 15
-    *reinterpret_cast<f16x8*>(p.A + (16 * I + c) * LDT + 16 * I) = alo;
-    *reinterpret_cast<f16x8*>(p.A + (16 * I + c) * LDT + 16 * I + 8) = ahi;
-  }
+  *reinterpret_cast<f16x4*>(p.D + (I * 16 + c) * LDB + 4 * g4) = drow;
+  // row 16I + c of A', columns 16I + 4g .. 16I + 4g + 3
+  *reinterpret_cast<f16x4*>(p.A + (16 * I + c) * LDT + 16 * I + 4 * g4) = arow;
 }
 
 // Owner 0 in phase 2b: off-diagonal blocks of A = (I + L)^-1,
@@ -1813,7 +1821,7 @@ __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
       bf16x4 o;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
-      *reinterpret_cast<bf16x4*>(p.Wn + (16 * tb + l16) * LDK + slot32(32 * w + 16 * ct + 4 * g4)) = o;
+      *reinterpret_cast<bf16x4*>(p.Wn + prow(16 * tb + l16) * LDK + slot32(32 * w + 16 * ct + 4 * g4)) = o;
     }
 }
 
@@ -1855,7 +1863,7 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + (16 * I + l16) * LDK + 32 * (2 * hf + k2) + 8 * g4);
+      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + prow(16 * I + l16) * LDK + 32 * (2 * hf + k2) + 8 * g4);
     KDA_READS_FIRST();
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
