@@ -1990,10 +1990,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, 0, o, lane);
+    // (the owners keep their per-lane addresses in registers for the whole
+    // loop; the workers, short of registers, recompute them in each phase)
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 1: finish chunk n
       if (n >= 0) {
         rows_times_state_b<false>(p.Wn, S, U, lane);
@@ -2012,7 +2013,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         owner_state(p, Df, S, n & 1, lane);
       }
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 2a: V^T; diagonal block o of L and its inverse (chunk n+1)
       if (nxt) {
         owner_vt(p, vr, o, lane);
@@ -2023,7 +2023,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // leave one wavefront's copy of the loaded registers wrong
       fetch_v(vr, a, bb, h, n + 2, o, lane);
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 2b: entry-state readout of chunk n+1
       // O and U are (re)defined on every path, so their previous values are
       // not kept alive through the other phases
@@ -2033,7 +2032,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (nxt) rows_times_state_b<true>(p.Qt, S, O, lane);
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 3: U of chunk n+1
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
