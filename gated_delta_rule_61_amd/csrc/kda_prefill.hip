@@ -1302,7 +1302,7 @@ constexpr int O_QT = O_KH + SZ_RM;
 constexpr int O_WN = O_QT + SZ_RM;       // -W; scratch of the solver wavefront in phase 2
 constexpr int O_KTT = O_WN + SZ_RM;
 constexpr int O_KBT = O_KTT + SZ_TR;
-constexpr int O_VT = O_KBT + SZ_TR;      // V^T; owners' output staging in phase 1
+constexpr int O_VT = O_KBT + SZ_TR;      // V^T
 constexpr int O_P = O_VT + SZ_TR;
 constexpr int O_A = O_P + SZ_CC;
 constexpr int O_BETA = O_A + SZ_CC;
@@ -1316,9 +1316,7 @@ constexpr int S_LN = S_LDT + 4 * 16 * LDL * 4;     // fp16 [6][16][LDB]: -L_IJ, 
 constexpr int S_D = S_LN + 6 * 16 * LDB * 2;       // fp16 [4][16][LDB]: D_I = (I + L_II)^-1
 constexpr int S_DT = S_D + 4 * 16 * LDB * 2;       // fp16 [4][16][LDB]: D_I^T
 constexpr int S_END = S_DT + 4 * 16 * LDB * 2;
-constexpr int LDS_O = 36;                          // output staging rows (bf16)
 static_assert(S_END <= SZ_RM, "solver scratch");
-static_assert(4 * C * LDS_O * 2 <= SZ_TR, "output staging");
 static_assert(BYTES <= 160 * 1024, "LDS");
 
 struct Ptr {
@@ -1326,7 +1324,6 @@ struct Ptr {
   f16 *KtT, *KbT, *VT, *P, *A;
   float *beta, *gam, *qk;
   float* LdT; f16 *Ln, *D, *Dt;
-  bf16* stg;
   __device__ __forceinline__ void set(unsigned char* b) {
     Kt = reinterpret_cast<bf16*>(b + O_KT);
     Kh = reinterpret_cast<bf16*>(b + O_KH);
@@ -1344,7 +1341,6 @@ struct Ptr {
     Ln = reinterpret_cast<f16*>(b + O_WN + S_LN);
     D = reinterpret_cast<f16*>(b + O_WN + S_D);
     Dt = reinterpret_cast<f16*>(b + O_WN + S_DT);
-    stg = reinterpret_cast<bf16*>(b + O_VT);
   }
   // barrier, then rebuild the pointers from an offset the compiler cannot see
   // through, so that each phase computes its own LDS addresses
@@ -1387,6 +1383,35 @@ __device__ __forceinline__ int prow(int t) { return (t & ~3) | ((t + (t >> 4)) &
 // a 16-byte bank slot (group >> 1 differs) and each half of a transposed
 // store on both 32-bank halves (group & 1 differs).
 __device__ __forceinline__ int chgrp(int j) { return (3 * (j & 1)) ^ (j >> 1); }
+
+// Value column, relative to the owner's first, of column i of the owner's
+// state tile nt.  An owner's two 16-column MFMA tiles interleave in groups of
+// four, so that the four output columns a lane holds in each tile (4g..4g+3)
+// are the 8 adjacent columns 8g..8g+7: one 16-byte store per token.
+__device__ __forceinline__ int vcol(int nt, int i) { return 8 * (i >> 2) + 4 * nt + (i & 3); }
+
+// State tiles of an owner (fp32 [d_k][d_v] per head) in that column order.
+__device__ __forceinline__ void load_state_v(floatx4 (&S)[2][DK / 16], const float* S0, int64_t head, int col0,
+                                             int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S[nt][rt][j] = S0 ? S0[(head * DK + 16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] : 0.f;
+}
+__device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], float* out, int64_t head, int col0,
+                                              int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[(head * DK + 16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
+}
 
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
 // the scheduler sinks each read next to its product to save registers, and
@@ -1833,7 +1858,7 @@ __device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[NTL
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) vb[nt][sl] = ldc_h(p.VT + (col0 + 16 * nt + l16) * LDT + 32 * sl + 8 * g4);
+    for (int sl = 0; sl < 2; ++sl) vb[nt][sl] = ldc_h(p.VT + (col0 + vcol(nt, l16)) * LDT + 32 * sl + 8 * g4);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -1926,30 +1951,22 @@ __device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[NT
   }
 }
 
-__device__ __forceinline__ void owner_store(const Ptr& p, const floatx4 (&O)[2][4], int o, __amdgpu_buffer_rsrc_t ro,
-                                            int row_elems, int col, int lane) {
-  bf16* st = p.stg + o * C * LDS_O;
+// Phase 1, owners: the output tile straight to memory.  O is held transposed
+// (lane: token 16I + l16, tile columns 4g..4g+3 of both tiles), which in the
+// owner's column order are the 8 adjacent value columns col0 + 8g .. + 7.
+__device__ __forceinline__ void owner_store(const floatx4 (&O)[2][4], __amdgpu_buffer_rsrc_t ro, int row_elems,
+                                            int col0, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  // O is held transposed: lane has token 16I + l16, columns 16nt + 4g .. + 3
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int I = 0; I < 4; ++I) {
+    bf16x8 v;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      bf16x4 v;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] = (bf16)O[nt][I][jj];
-      *reinterpret_cast<bf16x4*>(st + (16 * I + l16) * LDS_O + 16 * nt + 4 * g4) = v;
+    for (int jj = 0; jj < 4; ++jj) {
+      v[jj] = (bf16)O[0][I][jj];
+      v[4 + jj] = (bf16)O[1][I][jj];
     }
-  // 64 rows x 64 bytes: four 16-byte vectors per row
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = lane + 64 * i;
-    const int row = idx >> 2, cv = idx & 3;
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 x = *reinterpret_cast<const u32x2*>(st + row * LDS_O + 8 * cv);
-    const u32x2 y = *reinterpret_cast<const u32x2*>(st + row * LDS_O + 8 * cv + 4);
-    const u32x4 v = {x[0], x[1], y[0], y[1]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((row * row_elems + col + 8 * cv) * 2), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                           (uint32_t)(((16 * I + l16) * row_elems + col0 + 8 * g4) * 2), 0, 0);
   }
 }
 
@@ -1986,7 +2003,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int o = wave;
     const int col0 = 32 * o;
     floatx4 S[2][DK / 16];
-    load_state<DK, DV, 2>(S, a.S0, head, col0 + (lane & 15), lane);
+    load_state_v(S, a.S0, head, col0, lane);
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, 0, o, lane);
@@ -2009,7 +2026,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
-        owner_store(p, O, o, ro, a.H * DV, col0, lane);
+        owner_store(O, ro, a.H * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
       p.sync(smem_raw);
@@ -2039,7 +2056,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         for (int I = 0; I < 4; ++I) U[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (nxt) owner_u(p, col0, U, lane);
     }
-    if (a.S_T) store_state<DK, DV, 2>(S, a.S_T, head, col0 + (lane & 15), lane);
+    if (a.S_T) store_state_v(S, a.S_T, head, col0, lane);
   } else {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
