@@ -1514,26 +1514,23 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
   }
 }
 
-// Phase 1 of a worker: log2-scaled in-chunk prefix sums of its gate channels,
-// then Kt = 2^b k, Kh = 2^-b k, Qt = 2^b q (row-major bf16), the chunk decay
-// gam = 2^b_C of its channels and the q.k partial sums; Kt and Kb = gam 2^-b k
-// stay in registers as fp16 (kt_t[e], kb[e] = tokens 4m..4m+3 of channel e)
-// and are stored transposed in phase 2a.
-//
-// The next-but-one chunk's inputs are loaded into the same registers as each
-// one is consumed (g after the prefix sum starts, k and q row by row), so the
-// loads spread over this phase's arithmetic instead of arriving as one burst;
-// each group is pinned in place by scheduling fences.
-__device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int lane, int par,
-                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
-  const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * chgrp(j);
+// In-chunk prefix sums of a worker's gate channels, log2-scaled (b[i][e]:
+// token 4m + i, channel e of the lane's eight), and the chunk decay
+// gm[e] = 2^b_C.  Computed one slot ahead of their use, in phase 2b where the
+// workers are otherwise idle.
+struct Gates {
   float b[4][8];
+  float gm[8];
+};
+
+// Prefix sums of the gates in r.g; r.g is then reloaded with the gates of the
+// chunk that nx addresses (the next scan's input).
+__device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc& nx) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    unpack8(r.g[i], b[i]);
+    unpack8(r.g[i], gt.b[i]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[i][e] *= kLog2e;
+    for (int e = 0; e < 8; ++e) gt.b[i][e] *= kLog2e;
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1542,23 +1539,38 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
 #pragma unroll
   for (int i = 1; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[i][e] += b[i - 1][e];
-  float gm[8];
+    for (int e = 0; e < 8; ++e) gt.b[i][e] += gt.b[i - 1][e];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float tot = b[3][e];
+    const float tot = gt.b[3][e];
     float s = add_row_shr<1>(tot);
     s = add_row_shr<2>(s);
     s = add_row_shr<4>(s);
     s = add_row_shr<8>(s);
     const float ex = s - tot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i][e] += ex;
-    gm[e] = exp2_hw(row_last(s));
+    for (int i = 0; i < 4; ++i) gt.b[i][e] += ex;
+    gt.gm[e] = exp2_hw(row_last(s));
   }
+}
+
+// Phase 1 of a worker: from the prefix sums, Kt = 2^b k, Kh = 2^-b k,
+// Qt = 2^b q (row-major bf16), the chunk decay gam of its channels and the
+// q.k partial sums; Kt and Kb = gam 2^-b k stay in registers as fp16
+// (kt_t[e], kb[e] = tokens 4m..4m+3 of channel e) and are stored transposed
+// in phase 2a.
+//
+// The next-but-one chunk's k and q are loaded into the same registers row by
+// row as each row is consumed, so the loads spread over this phase's
+// arithmetic instead of arriving as one burst; each row's loads are pinned in
+// place by scheduling fences.
+__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
+                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
+  const int j = lane >> 4, m = lane & 15;
+  const int c0 = 32 * w + 8 * chgrp(j);
   if (m == 0) {
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gm[0], gm[1], gm[2], gm[3]};
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gm[4], gm[5], gm[6], gm[7]};
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
   }
   float qk[4];
 #pragma unroll
@@ -1576,14 +1588,14 @@ __device__ __forceinline__ void worker_gates(const Ptr& p, WRegs& r, int w, int 
     bf16x8 kt, kh, qt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float ep = exp2_hw(b[i][e]);
-      const float em = exp2_hw(-b[i][e]);
+      const float ep = exp2_hw(gt.b[i][e]);
+      const float em = exp2_hw(-gt.b[i][e]);
       const float a = kf[e] * ep, d = kf[e] * em;
       kt[e] = (bf16)a;
       kh[e] = (bf16)d;
       qt[e] = (bf16)(qf[e] * ep);
       kt_t[e][i] = (f16)a;
-      kb[e][i] = (f16)(d * gm[e]);
+      kb[e][i] = (f16)(d * gt.gm[e]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
     const int r0 = prow(4 * m + i) * LDK + slot32(c0), r1 = prow(4 * m + i) * LDK + slot32(c0 + 4);
@@ -2061,21 +2073,24 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
     WRegs r;
+    Gates gt;
     fetch_qkg(r, a, bb, h, 0, w, lane);   // zeros when the sequence is empty
+    worker_scan(r, gt, QkgSrc(a, bb, h, 1, w, lane));
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 1: gates of chunk n+1 with the loads of chunk n+2 interleaved.
-      // Runs on every slot (past the last chunk on zeros, into arrays nobody
-      // reads again), so the loads are never under a branch: loaded registers
-      // merging with old ones at a join would make the merge wait for them.
+      // phase 1: gated operands of chunk n+1 with the k / q loads of chunk
+      // n+2 interleaved.  Runs on every slot (past the last chunk on zeros,
+      // into arrays nobody reads again), so the loads are never under a
+      // branch: loaded registers merging with old ones at a join would make
+      // the merge wait for them.
       {
         const QkgSrc nx(a, bb, h, n + 2, w, lane);
         if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
         r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
-        worker_gates(p, r, w, lane, (n + 1) & 1, kb, kt_t, nx);
+        worker_apply(p, r, gt, w, lane, (n + 1) & 1, kb, kt_t, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
@@ -2095,8 +2110,10 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: worker 0: off-diagonal blocks of A'
+      // phase 2b: worker 0: off-diagonal blocks of A'; all: gate prefix sums
+      // of chunk n+2 and the gate loads of chunk n+3 (on every slot)
       if (nxt && w == 0) solver_offdiag(p, lane);
+      worker_scan(r, gt, QkgSrc(a, bb, h, n + 3, w, lane));
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
