@@ -1623,8 +1623,8 @@ __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], c
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KbT + (c0 + e) * LDT + slot32(4 * m)) = kb[e];
 }
 
-// Phase 2a of owner o: V^T rows 32o .. 32o + 31 (its own value columns) from
-// registers, 4 tokens per 8-byte store.
+// Phase 1 of owner o (for the next chunk): V^T rows 32o .. 32o + 31 (its own
+// value columns) from registers, 4 tokens per 8-byte store.
 __device__ __forceinline__ void owner_vt(const Ptr& p, const Vec16 (&v)[4], int o, int lane) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * o + 8 * chgrp(j);
@@ -2041,12 +2041,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         owner_store(O, ro, a.H * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
+      // V^T of chunk n+1 (U is formed in phase 3)
+      if (nxt) owner_vt(p, vr, o, lane);
       p.sync(smem_raw);
-      // phase 2a: V^T; diagonal block o of L and its inverse (chunk n+1)
-      if (nxt) {
-        owner_vt(p, vr, o, lane);
-        solver_block(p, o, lane);
-      }
+      // phase 2a: diagonal block o of L and its inverse (chunk n+1)
+      if (nxt) solver_block(p, o, lane);
       // values of chunk n+2: unconditional (zeros past the end), and after the
       // role switch -- loads issued just before such a switch were seen to
       // leave one wavefront's copy of the loaded registers wrong
