@@ -2175,8 +2175,11 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {
-      const int ns = a.nsplit > 0 ? a.nsplit : fused_default_nsplit(a.B * a.H, 128);
-      if (ns == 1 && a.pipeline) return launch_pipe(a, s);
+      // the pipelined kernel without a column split is the faster one at every
+      // measured head count (B1 H16 T4096: 0.33 ms against 0.45 ms for the best
+      // split; B1 H32 T131072: 10.3 ms against 14.0 ms); an explicit split or
+      // a disabled pipeline selects the serial kernel
+      if (a.nsplit <= 1 && a.pipeline) return launch_pipe(a, s);
       return launch_fused_d<bf16, 128, 128>(a, s);
     }
     if (a.dk == 64 && a.dv == 64) return launch_fused_d<bf16, 64, 64>(a, s);
