@@ -73,6 +73,32 @@ int env_pipeline() {
   return (e && e[0] == '0') ? 0 : 1;
 }
 
+// Compute units of the current device (0 when there is none).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// Segments per sequence of the segmented prefill schedule for these sizes
+// (0: one pass).  It applies where the pipelined kernel does; the count comes
+// from the launch cost model, or from KDA_SEGMENTS (0 or 1: off; n >= 3:
+// about n segments of equal length).
+int segment_count(int B, int T, int H, int dk, int dv, int dtype) {
+  if (dtype != KDA_BF16 || dk != 128 || dv != 128 || env_nsplit() > 1 || !env_pipeline()) return 0;
+  if ((int64_t)B * H <= 0 || T <= 0) return 0;
+  const char* e = getenv("KDA_SEGMENTS");
+  if (e) {
+    const int want = atoi(e);
+    if (want < 3) return 0;
+    const int N = (T + 63) / 64;
+    const int L = (N + want - 1) / want, P = (N + L - 1) / L;
+    return P >= 3 ? P : 0;
+  }
+  return kda::prefill_segments(B * H, T, device_cus());
+}
+
 #define KDA_REQUIRE(cond, code) \
   do {                          \
     if (!(cond)) return (code); \
@@ -112,14 +138,13 @@ const char* kda_status_string(int status) {
 int kda_last_hip_error(void) { return g_last_hip; }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
-  (void)B; (void)T; (void)H; (void)d_k; (void)d_v; (void)dtype;
-  return 0;
+  if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
+  return kda::prefill_segment_workspace(B * H, segment_count(B, T, H, d_k, d_v, dtype));
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
   if ((int64_t)B * H == 0) return KDA_OK;
@@ -129,6 +154,14 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
   }
   KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16, env_nsplit(), env_pipeline()};
+  // segmented schedule when the caller passes the workspace it needs
+  const int nseg = segment_count(B, T, H, d_k, d_v, dtype);
+  if (nseg >= 3 && workspace && aligned16(workspace) &&
+      workspace_bytes >= kda::prefill_segment_workspace(B * H, nseg)) {
+    a.nseg = nseg;
+    a.seg_len = kda::prefill_segment_len(T, nseg);
+    a.ws = static_cast<float*>(workspace);
+  }
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 

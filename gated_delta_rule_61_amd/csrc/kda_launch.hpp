@@ -13,6 +13,11 @@ struct PrefillArgs {
   int bf16;       // 1: bf16 inputs/outputs, 0: fp32
   int nsplit;     // column split of the state across workgroups (0 = auto)
   int pipeline;   // 1: software-pipelined schedule where it applies (bf16, d = 128, no split)
+  // Segmented schedule of the pipelined kernel (nseg >= 3 segments of seg_len
+  // chunks per sequence, see launch_pipe); nseg = 0: one pass per sequence.
+  int nseg, seg_len;
+  int pass;       // set by the launcher: 1 = segment maps and segment 0, 3 = segments 1..nseg-1
+  float* ws;      // nseg_workspace_bytes() of fp32 scratch
 };
 
 struct StageArgs {
@@ -37,5 +42,11 @@ hipError_t launch_stage_output(const StageArgs& a, hipStream_t s);
 
 // Default column split of the fused prefill for B*H heads on this device.
 int fused_default_nsplit(int BH, int dv);
+
+// Segments per sequence for the segmented pipelined prefill on a device with
+// `cus` compute units (0: one pass), chunks per segment, and the workspace.
+int prefill_segments(int BH, int T, int cus);
+int prefill_segment_len(int T, int nseg);
+size_t prefill_segment_workspace(int BH, int nseg);
 
 }  // namespace kda

@@ -1390,8 +1390,9 @@ __device__ __forceinline__ int chgrp(int j) { return (3 * (j & 1)) ^ (j >> 1); }
 // are the 8 adjacent columns 8g..8g+7: one 16-byte store per token.
 __device__ __forceinline__ int vcol(int nt, int i) { return 8 * (i >> 2) + 4 * nt + (i & 3); }
 
-// State tiles of an owner (fp32 [d_k][d_v] per head) in that column order.
-__device__ __forceinline__ void load_state_v(floatx4 (&S)[2][DK / 16], const float* S0, int64_t head, int col0,
+// State tiles of an owner in that column order, from / to one head's fp32
+// [d_k][d_v] matrix (S0 NULL: zeros; ident: the identity).
+__device__ __forceinline__ void load_state_v(floatx4 (&S)[2][DK / 16], const float* S0, bool ident, int col0,
                                              int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
@@ -1399,18 +1400,25 @@ __device__ __forceinline__ void load_state_v(floatx4 (&S)[2][DK / 16], const flo
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        S[nt][rt][j] = S0 ? S0[(head * DK + 16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * rt + 4 * g4 + j, col = col0 + vcol(nt, l16);
+        S[nt][rt][j] = S0 ? S0[row * DV + col] : (ident && row == col ? 1.f : 0.f);
+      }
 }
-__device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], float* out, int64_t head, int col0,
-                                              int lane) {
+__device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[(head * DK + 16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
+      for (int j = 0; j < 4; ++j) out[(16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
+}
+
+// Workspace matrix (fp32 [d_k][d_v]) of the segmented schedule: for sequence /
+// head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N.
+__device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int s, int kind) {
+  return ws + ((head * nseg + s) * 3 + kind) * (int64_t)(DK * DV);
 }
 
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
@@ -1989,11 +1997,55 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int head, split;
-  block_to_head<1>(blockIdx.x, head, split);
-  if (head >= a.B * a.H) return;
+  // Work of this workgroup: chunks c0 .. c0 + nchunks - 1 of one sequence and
+  // head, entry state from s0p (NULL: zeros, or the identity if ident), final
+  // state to sTp (NULL: dropped), outputs stored if outp, values used unless
+  // vzero.  One pass: the whole sequence.  Segmented (nseg segments of
+  // seg_len chunks): pass 1 runs segment 0 for real, and for each segment s =
+  // 1 .. nseg-2 the offset N_s (from zero) and the transition M_s (from the
+  // identity, values zero) of S_end = M_s S_start + N_s; pass 3 runs segments
+  // 1 .. nseg-1 from their entry states, which the combine kernel has formed
+  // in between.
+  int head, c0 = 0, nchunks = (a.T + C - 1) / C;
+  const float* s0p = nullptr;
+  float* sTp = nullptr;
+  bool ident = false, outp = true, vzero = false;
+  if (a.pass == 0) {
+    int split;
+    block_to_head<1>(blockIdx.x, head, split);
+    if (head >= a.B * a.H) return;
+    if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
+    if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
+  } else {
+    const int njobs = a.pass == 1 ? 2 * a.nseg - 3 : a.nseg - 1;
+    head = blockIdx.x / njobs;
+    const int job = blockIdx.x % njobs;
+    if (head >= a.B * a.H) return;
+    int sg;
+    if (a.pass == 1) {
+      if (job == 0) {
+        sg = 0;
+        if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
+        sTp = seg_mat(a.ws, head, a.nseg, 1, 0);
+      } else if (job <= a.nseg - 2) {
+        sg = job;
+        outp = false;
+        sTp = seg_mat(a.ws, head, a.nseg, sg, 2);
+      } else {
+        sg = job - (a.nseg - 2);
+        outp = false;
+        ident = vzero = true;
+        sTp = seg_mat(a.ws, head, a.nseg, sg, 1);
+      }
+    } else {
+      sg = job + 1;
+      s0p = seg_mat(a.ws, head, a.nseg, sg, 0);
+      if (sg == a.nseg - 1 && a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
+    }
+    c0 = sg * a.seg_len;
+    nchunks = min(a.seg_len, nchunks - c0);
+  }
   const int bb = head / a.H, h = head % a.H;
-  const int nchunks = (a.T + C - 1) / C;
   Ptr p;
   p.set(smem_raw);
   // blocks (0,1) and (2,3) of P and A' above the diagonal are read by the
@@ -2015,10 +2067,10 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int o = wave;
     const int col0 = 32 * o;
     floatx4 S[2][DK / 16];
-    load_state_v(S, a.S0, head, col0, lane);
+    load_state_v(S, s0p, ident, col0, lane);
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
-    if (nchunks > 0) fetch_v(vr, a, bb, h, 0, o, lane);
+    if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
     // (the owners keep their per-lane addresses in registers for the whole
     // loop; the workers, short of registers, recompute them in each phase)
     for (int n = -1; n < nchunks; ++n) {
@@ -2034,11 +2086,13 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           Df[nt][1] = MH::frag32(U[nt][2], U[nt][3]);
         }
         owner_intra(p, Df, O, lane);
-        const int t0 = n * C, nv = min(C, a.T - t0);
-        const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
-        owner_store(O, ro, a.H * DV, col0, lane);
+        if (outp) {
+          const int t0 = (c0 + n) * C, nv = min(C, a.T - t0);
+          const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+          const __amdgpu_buffer_rsrc_t ro =
+              make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
+          owner_store(O, ro, a.H * DV, col0, lane);
+        }
         owner_state(p, Df, S, n & 1, lane);
       }
       // V^T of chunk n+1 (U is formed in phase 3)
@@ -2049,7 +2103,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // values of chunk n+2: unconditional (zeros past the end), and after the
       // role switch -- loads issued just before such a switch were seen to
       // leave one wavefront's copy of the loaded registers wrong
-      fetch_v(vr, a, bb, h, n + 2, o, lane);
+      fetch_v(vr, a, bb, h, c0 + n + 2, o, lane);
       p.sync(smem_raw);
       // phase 2b: entry-state readout of chunk n+1
       // O and U are (re)defined on every path, so their previous values are
@@ -2065,16 +2119,16 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int I = 0; I < 4; ++I) U[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (nxt) owner_u(p, col0, U, lane);
+      if (nxt && !vzero) owner_u(p, col0, U, lane);
     }
-    if (a.S_T) store_state_v(S, a.S_T, head, col0, lane);
+    if (sTp) store_state_v(S, sTp, col0, lane);
   } else {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
     WRegs r;
     Gates gt;
-    fetch_qkg(r, a, bb, h, 0, w, lane);   // zeros when the sequence is empty
-    worker_scan(r, gt, QkgSrc(a, bb, h, 1, w, lane));
+    fetch_qkg(r, a, bb, h, c0, w, lane);   // zeros when the sequence is empty
+    worker_scan(r, gt, QkgSrc(a, bb, h, c0 + 1, w, lane));
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
@@ -2086,7 +2140,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // branch: loaded registers merging with old ones at a join would make
       // the merge wait for them.
       {
-        const QkgSrc nx(a, bb, h, n + 2, w, lane);
+        const QkgSrc nx(a, bb, h, c0 + n + 2, w, lane);
         if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
         r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
         worker_apply(p, r, gt, w, lane, (n + 1) & 1, kb, kt_t, nx);
@@ -2112,11 +2166,85 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // phase 2b: worker 0: off-diagonal blocks of A'; all: gate prefix sums
       // of chunk n+2 and the gate loads of chunk n+3 (on every slot)
       if (nxt && w == 0) solver_offdiag(p, lane);
-      worker_scan(r, gt, QkgSrc(a, bb, h, n + 3, w, lane));
+      worker_scan(r, gt, QkgSrc(a, bb, h, c0 + n + 3, w, lane));
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
       if (nxt) worker_w(p, w, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segmented schedule, between the two passes: the entry state of each
+// segment, S_{s+1} = M_s S_s + N_s for s = 1 .. nseg-2 (S_1 is segment 0's
+// final state), one 1024-thread workgroup per sequence and head, fp32 MFMA
+// (v_mfma_f32_16x16x4_f32) with S_s and M_s staged in LDS.
+// ---------------------------------------------------------------------------
+namespace segc {
+constexpr int NTC = 1024;
+constexpr int LDS_S = 144;   // fp32 rows of S: B-operand reads (rows 4kb + g, 16 columns) hit 64 banks
+constexpr int LDS_M = 132;   // fp32 rows of M: A-operand reads (16 rows, 4 columns) hit 64 banks
+constexpr int BYTES = (128 * LDS_S + 128 * LDS_M) * 4;
+}  // namespace segc
+
+__global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
+  using namespace segc;
+  constexpr int D = 128;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  float* Sl = reinterpret_cast<float*>(smem_raw);
+  float* Ml = Sl + D * LDS_S;
+  const int head = blockIdx.x;
+  if (head >= a.B * a.H) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  auto mat = [&](int s, int kind) { return a.ws + ((int64_t(head) * a.nseg + s) * 3 + kind) * (D * D); };
+  {
+    const floatx4* src = reinterpret_cast<const floatx4*>(mat(1, 0));
+    for (int i = tid; i < D * D / 4; i += NTC) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      *reinterpret_cast<floatx4*>(Sl + r * LDS_S + 4 * c4) = src[i];
+    }
+  }
+  for (int sg = 1; sg + 1 < a.nseg; ++sg) {
+    {
+      const floatx4* src = reinterpret_cast<const floatx4*>(mat(sg, 1));
+      for (int i = tid; i < D * D / 4; i += NTC) {
+        const int r = i / (D / 4), c4 = i % (D / 4);
+        *reinterpret_cast<floatx4*>(Ml + r * LDS_M + 4 * c4) = src[i];
+      }
+    }
+    __syncthreads();
+    // wave w: output tiles 4w .. 4w+3 of the 8 x 8 tile grid (16 x 16 each)
+    const float* Nm = mat(sg, 2);
+    floatx4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[u][jj] = Nm[(16 * ti + 4 * g4 + jj) * D + 16 * tj + l16];
+    }
+#pragma unroll 4
+    for (int kb = 0; kb < D / 4; ++kb) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
+        const float av = Ml[(16 * ti + l16) * LDS_M + 4 * kb + g4];
+        const float bv = Sl[(4 * kb + g4) * LDS_S + 16 * tj + l16];
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[u], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every read of S_s and M_s is done
+    float* dst = mat(sg + 1, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * ti + 4 * g4 + jj, c = 16 * tj + l16;
+        Sl[r * LDS_S + c] = acc[u][jj];
+        dst[r * D + c] = acc[u][jj];
+      }
     }
   }
 }
@@ -2167,8 +2295,55 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
   const int bytes = pipe::BYTES;
   hipError_t e = set_smem(fused_pipe_kernel, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(a.B * a.H, 1)), dim3(NT), bytes, s, a);
+  const int BH = a.B * a.H;
+  if (a.nseg < 3) {
+    PrefillArgs a0 = a;
+    a0.pass = 0;
+    hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(BH, 1)), dim3(NT), bytes, s, a0);
+    return hipGetLastError();
+  }
+  // segmented: maps of the middle segments (and segment 0 itself), entry
+  // states, then segments 1 .. nseg-1
+  PrefillArgs a1 = a, a3 = a;
+  a1.pass = 1;
+  a3.pass = 3;
+  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (2 * a.nseg - 3)), dim3(NT), bytes, s, a1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_combine_kernel, dim3(BH), dim3(segc::NTC), segc::BYTES, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
   return hipGetLastError();
+}
+
+// Segments per sequence for the segmented schedule, from a cost model in
+// units of one chunk step of one workgroup: one pass takes N steps; nseg
+// segments of L chunks take (rounds of pass 1 + rounds of pass 3) (L + 2)
+// (2: pipeline fill and state traffic per workgroup) plus about half a step
+// per combine, where a round is one workgroup per compute unit.  0 if one
+// pass is cheaper.
+int prefill_segments(int BH, int T, int cus) {
+  const int N = (T + C - 1) / C;
+  if (BH <= 0 || cus <= 0 || N < 12) return 0;
+  double best = N + 2.0;
+  int best_p = 0;
+  for (int P = 3; P <= 64; ++P) {
+    const int L = (N + P - 1) / P, Pe = (N + L - 1) / L;
+    if (Pe != P) continue;   // only counts that split into equal-length segments (bar the last)
+    const int r1 = (BH * (2 * P - 3) + cus - 1) / cus, r3 = (BH * (P - 1) + cus - 1) / cus;
+    const double cost = (r1 + r3) * (L + 2.0) + 0.5 * (P - 2);
+    if (cost < best) { best = cost; best_p = P; }
+  }
+  return best_p;
+}
+
+int prefill_segment_len(int T, int nseg) {
+  const int N = (T + C - 1) / C;
+  return nseg > 0 ? (N + nseg - 1) / nseg : N;
+}
+
+size_t prefill_segment_workspace(int BH, int nseg) {
+  return nseg >= 3 ? (size_t)BH * nseg * 3 * 128 * 128 * sizeof(float) : 0;
 }
 
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {

@@ -79,8 +79,14 @@ typedef enum {
  *                 aliasing between arguments is allowed.
  *   B, T, H       batch, tokens per sequence (any T >= 0; a partial last
  *                 chunk is handled; T = 0 copies S0 to S_T), heads
- *   workspace     scratch of kda_chunk_fwd_workspace_size() bytes, or NULL
- *                 when that size is 0 (it is 0 for this schedule)
+ *   workspace     device scratch of kda_chunk_fwd_workspace_size() bytes
+ *                 (16-byte aligned), or NULL.  A nonzero size means that for
+ *                 these sizes a segmented schedule is faster: each sequence
+ *                 is cut into segments whose state maps S_end = M S_start + N
+ *                 are formed in parallel and chained (the state recursion
+ *                 between chunks is linear in the state, "...More Efficient"
+ *                 §IV).  With NULL or a smaller workspace the one-pass
+ *                 schedule runs; the results agree up to rounding.
  * Results do not depend on the chunk length up to rounding, and T calls of
  * kda_recurrent_step give the same result up to rounding.
  */
@@ -89,7 +95,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   int B, int T, int H, int d_k, int d_v, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kda_chunk_fwd needs for these sizes (0 = none). */
+/* Workspace bytes of the fastest kda_chunk_fwd schedule for these sizes on
+ * the current device (0 = none needed).  Environment: KDA_SEGMENTS = 0 turns
+ * the segmented schedule off, n >= 3 asks for about n segments. */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
 
 /*

@@ -93,6 +93,31 @@ def test_bf16_d128_schedules(kda, B, T, H, pipeline, monkeypatch):
     check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"B{B}T{T}H{H} pipeline={pipeline}")
 
 
+SEG_SHAPES = [(1, 64 * 12, 2, 3, True), (1, 64 * 13 + 17, 2, 4, True), (2, 64 * 20, 1, 5, False),
+              (1, 64 * 9 + 1, 3, 3, True), (1, 64 * 40, 1, 8, True)]
+
+
+@pytest.mark.parametrize("B,T,H,nseg,s0", SEG_SHAPES, ids=[f"B{b}T{t}H{h}-seg{n}{'-S0' if z else ''}" for b, t, h, n, z in SEG_SHAPES])
+def test_segmented_schedule(kda, B, T, H, nseg, s0, monkeypatch):
+    """The segmented schedule (segment state maps S_end = M S_start + N formed
+    in parallel, chained, then every segment run again from its entry state)
+    against the oracle, on exact and ragged lengths, with and without S0; and
+    against the one-pass schedule on the same inputs."""
+    monkeypatch.setenv("KDA_SEGMENTS", str(nseg))
+    inp = _case(W.PREFILL_BF16_H16_T4K, B, T, H, seed=500 + T + nseg, s0=s0)
+    assert kda.lib().kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 1) > 0
+    print(f"case segmented B{B} T{T} H{H} nseg={nseg} s0={s0}", flush=True)
+    o, S = _run(kda, inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"segmented B{B}T{T}H{H}")
+    monkeypatch.setenv("KDA_SEGMENTS", "0")
+    assert kda.lib().kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 1) == 0
+    o1, S1 = _run(kda, inp)
+    rel = (o.float() - o1.float()).norm() / o1.float().norm()
+    assert rel < 5e-3, rel
+    assert ((S - S1).norm() / S1.norm()) < 1e-3
+
+
 @pytest.mark.parametrize("pipeline", ["1", "0"], ids=["pipelined", "serial"])
 def test_single_token_seeds(kda, pipeline, monkeypatch):
     """Single-token prefill over many seeds: the output is q^T S_1 with S_1 one
