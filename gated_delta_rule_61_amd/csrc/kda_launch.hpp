@@ -16,7 +16,7 @@ struct PrefillArgs {
   // Segmented schedule of the pipelined kernel (nseg >= 3 segments of seg_len
   // chunks per sequence, see launch_pipe); nseg = 0: one pass per sequence.
   int nseg, seg_len;
-  int pass;       // set by the launcher: 1 = segment maps and segment 0, 3 = segments 1..nseg-1
+  int pass;       // set by the launcher: 1 = segment 0 and the segment maps, 3 = segments 1..nseg-1
   float* ws;      // nseg_workspace_bytes() of fp32 scratch
 };
 

@@ -1999,13 +1999,14 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Work of this workgroup: chunks c0 .. c0 + nchunks - 1 of one sequence and
   // head, entry state from s0p (NULL: zeros, or the identity if ident), final
-  // state to sTp (NULL: dropped), outputs stored if outp, values used unless
-  // vzero.  One pass: the whole sequence.  Segmented (nseg segments of
-  // seg_len chunks): pass 1 runs segment 0 for real, and for each segment s =
-  // 1 .. nseg-2 the offset N_s (from zero) and the transition M_s (from the
-  // identity, values zero) of S_end = M_s S_start + N_s; pass 3 runs segments
-  // 1 .. nseg-1 from their entry states, which the combine kernel has formed
-  // in between.
+  // state to sTp (NULL: dropped), outputs formed and stored if outp (else only
+  // the state runs: no P, no Qg S), values used unless vzero.
+  // One pass: the whole sequence.  Segmented (nseg segments of seg_len
+  // chunks): pass 1 runs segment 0 (its final state is segment 1's entry
+  // state) and, state only, for each segment s = 1 .. nseg-2 the offset N_s
+  // (from zero) and the transition M_s (from the identity, values zero) of
+  // S_end = M_s S_start + N_s; pass 3 runs segments 1 .. nseg-1 from their
+  // entry states, which the combine kernel has formed in between.
   int head, c0 = 0, nchunks = (a.T + C - 1) / C;
   const float* s0p = nullptr;
   float* sTp = nullptr;
@@ -2085,8 +2086,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           Df[nt][0] = MH::frag32(U[nt][0], U[nt][1]);
           Df[nt][1] = MH::frag32(U[nt][2], U[nt][3]);
         }
-        owner_intra(p, Df, O, lane);
         if (outp) {
+          owner_intra(p, Df, O, lane);
           const int t0 = (c0 + n) * C, nv = min(C, a.T - t0);
           const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
           const __amdgpu_buffer_rsrc_t ro =
@@ -2096,7 +2097,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         owner_state(p, Df, S, n & 1, lane);
       }
       // V^T of chunk n+1 (U is formed in phase 3)
-      if (nxt) owner_vt(p, vr, o, lane);
+      if (nxt && !vzero) owner_vt(p, vr, o, lane);
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
       if (nxt) solver_block(p, o, lane);
@@ -2112,7 +2113,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (nxt) rows_times_state_b<true>(p.Qt, S, O, lane);
+      if (nxt && outp) rows_times_state_b<true>(p.Qt, S, O, lane);
       p.sync(smem_raw);
       // phase 3: U of chunk n+1
 #pragma unroll
@@ -2147,8 +2148,21 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2a: Kt^T, Kb^T; P blocks and the off-diagonal blocks of L, four each
-      if (nxt) {
+      // phase 2a: Kt^T, Kb^T; P blocks and the off-diagonal blocks of L, four
+      // each (state-only runs: the L blocks alone)
+      if (nxt && !outp) {
+        worker_kbt(p, kb, kt_t, w, lane);
+        switch (w) {
+          case 0: { const bool q[2] = {0, 0}; const int I[2] = {1, 2}, J[2] = {0, 1};
+                    lp_block_tiles<2>(p, q, I, J, lane); break; }
+          case 1: { const bool q[2] = {0, 0}; const int I[2] = {2, 3}, J[2] = {0, 2};
+                    lp_block_tiles<2>(p, q, I, J, lane); break; }
+          case 2: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {0};
+                    lp_block_tiles<1>(p, q, I, J, lane); break; }
+          default: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {1};
+                     lp_block_tiles<1>(p, q, I, J, lane); break; }
+        }
+      } else if (nxt) {
         worker_kbt(p, kb, kt_t, w, lane);
         switch (w) {
           case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
@@ -2302,8 +2316,8 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(BH, 1)), dim3(NT), bytes, s, a0);
     return hipGetLastError();
   }
-  // segmented: maps of the middle segments (and segment 0 itself), entry
-  // states, then segments 1 .. nseg-1
+  // segmented: segment 0 and the maps of the middle segments, entry states,
+  // then segments 1 .. nseg-1
   PrefillArgs a1 = a, a3 = a;
   a1.pass = 1;
   a3.pass = 3;
@@ -2318,10 +2332,12 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
 
 // Segments per sequence for the segmented schedule, from a cost model in
 // units of one chunk step of one workgroup: one pass takes N steps; nseg
-// segments of L chunks take (rounds of pass 1 + rounds of pass 3) (L + 2)
-// (2: pipeline fill and state traffic per workgroup) plus about half a step
-// per combine, where a round is one workgroup per compute unit.  0 if one
-// pass is cheaper.
+// segments of L chunks take (1 + 0.7 (rounds of pass 1 - 1) + rounds of
+// pass 3) (L + 2) (pass 1's first round holds the full runs of segment 0,
+// its other rounds only state runs at about 0.7 of a full step; 2: pipeline
+// fill and state traffic per workgroup) plus about half a step per combine,
+// where a round is one workgroup per compute unit.  0 if one pass is
+// cheaper.
 int prefill_segments(int BH, int T, int cus) {
   const int N = (T + C - 1) / C;
   if (BH <= 0 || cus <= 0 || N < 12) return 0;
@@ -2331,7 +2347,7 @@ int prefill_segments(int BH, int T, int cus) {
     const int L = (N + P - 1) / P, Pe = (N + L - 1) / L;
     if (Pe != P) continue;   // only counts that split into equal-length segments (bar the last)
     const int r1 = (BH * (2 * P - 3) + cus - 1) / cus, r3 = (BH * (P - 1) + cus - 1) / cus;
-    const double cost = (r1 + r3) * (L + 2.0) + 0.5 * (P - 2);
+    const double cost = (1.0 + 0.7 * (r1 - 1) + r3) * (L + 2.0) + 0.5 * (P - 2);
     if (cost < best) { best = cost; best_p = P; }
   }
   return best_p;
