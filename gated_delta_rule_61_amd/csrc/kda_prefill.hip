@@ -1797,49 +1797,42 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   *reinterpret_cast<f16x4*>(p.A + (16 * I + c) * LDT + 16 * I + 4 * g4) = arow;
 }
 
-// Owner 0 in phase 2b: off-diagonal blocks of A = (I + L)^-1,
-//   A_IJ = D_I sum_{J <= K < I} (-L_IK) A_KJ   (A_KK = D_K),
-// level by level, intermediate blocks kept in registers; A'_IJ = A_IJ Diag(beta_J).
-__device__ __forceinline__ void solver_offdiag(const Ptr& p, int lane) {
+// Phase 2b, one worker per block column J = 0, 1, 2: the off-diagonal blocks
+// of A = (I + L)^-1 below D_J,
+//   A_IJ = D_I Y_IJ,  Y_IJ = (-L_IJ) D_J + sum_{J < K < I} (-L_IK) A_KJ,
+// top to bottom with the blocks of the column kept in registers (accumulator
+// tiles serve directly as B operands); A'_IJ = A_IJ Diag(beta_J).
+template <int J>
+__device__ __forceinline__ void solver_offdiag_col(const Ptr& p, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  auto Lf = [&](int I, int J) { return MH::lds16(p.Ln + ln_block(I, J) * 16 * LDB + l16 * LDB + 4 * g4); };
+  auto Lf = [&](int I, int K) { return MH::lds16(p.Ln + ln_block(I, K) * 16 * LDB + l16 * LDB + 4 * g4); };
   auto Df = [&](int I) { return MH::lds16(p.D + (I * 16 + l16) * LDB + 4 * g4); };
-  auto DTf = [&](int J) { return MH::lds16(p.Dt + (J * 16 + l16) * LDB + 4 * g4); };
-  // A'_IJ from its transposed product: lane holds row l16, columns 4g..4g+3
-  auto store_t = [&](int I, int J, const floatx4& vt) {
-    const floatx4 bj = *reinterpret_cast<const floatx4*>(p.beta + 16 * J + 4 * g4);
+  MH::F16 lf[4][4], df[4];
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    df[I] = Df(I);
+#pragma unroll
+    for (int K = J; K < I; ++K) lf[I][K] = Lf(I, K);
+  }
+  const MH::F16 dtj = MH::lds16(p.Dt + (J * 16 + l16) * LDB + 4 * g4);
+  const floatx4 bj = *reinterpret_cast<const floatx4*>(p.beta + 16 * J + 4 * g4);
+  KDA_READS_FIRST();
+  MH::F16 af[4];
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    floatx4 y = MH::mma16(lf[I][J], dtj, z);
+#pragma unroll
+    for (int K = J + 1; K < I; ++K) y = MH::mma16(lf[I][K], af[K], y);
+    const MH::F16 yf = MH::frag16(y);
+    if (I < 3) af[I] = MH::frag16(MH::mma16(df[I], yf, z));
+    // A'_IJ from the transposed product: lane holds row l16, columns 4g..4g+3
+    const floatx4 at = MH::mma16(yf, df[I], z);
     f16x4 v;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(vt[jj] * bj[jj]);
+    for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(at[jj] * bj[jj]);
     *reinterpret_cast<f16x4*>(p.A + (16 * I + l16) * LDT + 16 * J + 4 * g4) = v;
-  };
-  const MH::F16 d1 = Df(1), d2 = Df(2), d3 = Df(3);
-  // level 1
-  floatx4 y10 = MH::mma16(Lf(1, 0), DTf(0), z);
-  floatx4 y21 = MH::mma16(Lf(2, 1), DTf(1), z);
-  floatx4 y32 = MH::mma16(Lf(3, 2), DTf(2), z);
-  floatx4 y20 = MH::mma16(Lf(2, 0), DTf(0), z);
-  floatx4 y31 = MH::mma16(Lf(3, 1), DTf(1), z);
-  floatx4 y30 = MH::mma16(Lf(3, 0), DTf(0), z);
-  const MH::F16 y10f = MH::frag16(y10), y21f = MH::frag16(y21), y32f = MH::frag16(y32);
-  const floatx4 a10 = MH::mma16(d1, y10f, z);
-  const floatx4 a21 = MH::mma16(d2, y21f, z);
-  store_t(1, 0, MH::mma16(y10f, d1, z));
-  store_t(2, 1, MH::mma16(y21f, d2, z));
-  store_t(3, 2, MH::mma16(y32f, d3, z));
-  // level 2
-  const MH::F16 a10f = MH::frag16(a10);
-  y20 = MH::mma16(Lf(2, 1), a10f, y20);
-  y31 = MH::mma16(Lf(3, 2), MH::frag16(a21), y31);
-  y30 = MH::mma16(Lf(3, 1), a10f, y30);
-  const MH::F16 y20f = MH::frag16(y20), y31f = MH::frag16(y31);
-  const floatx4 a20 = MH::mma16(d2, y20f, z);
-  store_t(2, 0, MH::mma16(y20f, d2, z));
-  store_t(3, 1, MH::mma16(y31f, d3, z));
-  // level 3
-  y30 = MH::mma16(Lf(3, 2), MH::frag16(a20), y30);
-  store_t(3, 0, MH::mma16(MH::frag16(y30), d3, z));
+  }
 }
 
 // Phase 3, workers: W^T tile rows 32w.. of W = A' Kt (fp16 products from Kt^T
@@ -2177,9 +2170,17 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2b: worker 0: off-diagonal blocks of A'; all: gate prefix sums
-      // of chunk n+2 and the gate loads of chunk n+3 (on every slot)
-      if (nxt && w == 0) solver_offdiag(p, lane);
+      // phase 2b: workers 1-3: the off-diagonal blocks of A' in block columns
+      // 0-2; all: gate prefix sums of chunk n+2 and the gate loads of chunk
+      // n+3 (on every slot)
+      if (nxt) {
+        if (w == 1)
+          solver_offdiag_col<0>(p, lane);
+        else if (w == 2)
+          solver_offdiag_col<1>(p, lane);
+        else if (w == 3)
+          solver_offdiag_col<2>(p, lane);
+      }
       worker_scan(r, gt, QkgSrc(a, bb, h, c0 + n + 3, w, lane));
       p.sync(smem_raw);
       KDA_FRESH_LANE();
