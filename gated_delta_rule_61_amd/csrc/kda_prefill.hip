@@ -1289,8 +1289,8 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
 namespace pipe {
 
 constexpr int DK = 128, DV = 128;
-constexpr int LDK = DK + 8;      // bf16 [C][DK] rows
-constexpr int LDT = C + 8;       // fp16 [D][C] rows (transposed operands), [C][C] rows
+constexpr int LDK = DK + 16;     // bf16 [C][DK] rows (16-byte chunks swizzled, see rmo)
+constexpr int LDT = C + 16;      // fp16 [D][C] rows (transposed operands), [C][C] rows
 constexpr int LDB = 24;          // fp16 16x16 solver blocks
 constexpr int LDL = 20;          // fp32 16x16 diagonal blocks of L (transposed)
 constexpr int SZ_RM = C * LDK * 2;
@@ -1368,21 +1368,16 @@ __device__ __forceinline__ int slot32(int k) {
   return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
 }
 
-// Bank-conflict-free placement of the row-major bf16 arrays (Kt, Kh, Qt, -W).
-// A worker store covers rows 4m + i (m = 0..15) of one column block: with
-// rows in natural order those fall on 4 bank offsets only (the row pitch is
-// 68 dwords), a 4-way conflict.  Token row t is therefore kept at row prow(t),
-// which rotates each group of four rows by (t / 16) mod 4: the 16 rows of a
-// worker store then fall on 16 distinct bank offsets, and the 16 rows 16I + i
-// of an MFMA fragment read stay on distinct offsets too.
-__device__ __forceinline__ int prow(int t) { return (t & ~3) | ((t + (t >> 4)) & 3); }
-
-// Channel group (8 channels) of lane group j = lane / 16 in the worker and
-// owner input layouts.  Groups 0, 3 share a 32-lane half and groups 1, 2 the
-// other, so that each half of a row-major store lands on both dword pairs of
-// a 16-byte bank slot (group >> 1 differs) and each half of a transposed
-// store on both 32-bank halves (group & 1 differs).
-__device__ __forceinline__ int chgrp(int j) { return (3 * (j & 1)) ^ (j >> 1); }
+// Element offset of element e of token row t in the row-major bf16 arrays
+// (Kt, Kh, Qt, -W): rows of 144 elements, and the 16-byte chunks of row t
+// permuted by XOR with (t / 4) mod 8.  With this pitch and swizzle the MFMA
+// fragment reads (16 rows x one chunk per lane group) are free of LDS bank
+// conflicts, and the workers' 8-byte stores of rows 4m + i are at most
+// 2-way (measured with the LDS bank-conflict counter: natural rows of 136
+// elements gave 2-way conflicts on every fragment read and 8-way on the
+// stores).  [D][C] fp16 rows of 80 elements likewise make their fragment
+// reads conflict-free.
+__device__ __forceinline__ int rmo(int t, int e) { return t * LDK + (e ^ ((t << 1) & 56)); }
 
 // Value column, relative to the owner's first, of column i of the owner's
 // state tile nt.  An owner's two 16-column MFMA tiles interleave in groups of
@@ -1444,7 +1439,7 @@ __device__ __forceinline__ float row_last(float x) {
 }
 
 // Chunk inputs of one worker wavefront: rows 4m..4m+3 (m = lane % 16) and
-// channels 32w + 8 chgrp(lane / 16) .. +8.  (Owner o loads the value columns
+// channels 32w + 8(lane / 16) .. +8.  (Owner o loads the value columns
 // 32o.. of v in the same lane layout.)
 struct WRegs {
   Vec16 q[4], k[4], g[4];
@@ -1452,7 +1447,7 @@ struct WRegs {
 };
 
 __device__ __forceinline__ uint32_t wlane_off(int H, int w, int lane) {
-  return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * chgrp(lane >> 4)) * 2);
+  return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * (lane >> 4)) * 2);
 }
 
 // Buffer resources and offsets of one chunk's q, k, g, beta for a worker.
@@ -1575,7 +1570,7 @@ __device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc& n
 __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
                                              f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * chgrp(j);
+  const int c0 = 32 * w + 8 * j;
   if (m == 0) {
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
@@ -1606,7 +1601,7 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
       kb[e][i] = (f16)(d * gt.gm[e]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
-    const int r0 = prow(4 * m + i) * LDK + slot32(c0), r1 = prow(4 * m + i) * LDK + slot32(c0 + 4);
+    const int r0 = rmo(4 * m + i, slot32(c0)), r1 = rmo(4 * m + i, slot32(c0 + 4));
     *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
     *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
@@ -1624,7 +1619,7 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
 __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], const f16x4 (&kt_t)[8], int w,
                                            int lane) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * chgrp(j);
+  const int c0 = 32 * w + 8 * j;
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
 #pragma unroll
@@ -1635,7 +1630,7 @@ __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], c
 // value columns) from registers, 4 tokens per 8-byte store.
 __device__ __forceinline__ void owner_vt(const Ptr& p, const Vec16 (&v)[4], int o, int lane) {
   const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * o + 8 * chgrp(j);
+  const int c0 = 32 * o + 8 * j;
   f16x4 vt[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1675,8 +1670,8 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + prow(16 * I[t] + l16) * LDK + 32 * ks + 8 * g4);
-      bf[t][ks] = ldc_b(Kh + prow(16 * J[t] + l16) * LDK + 32 * ks + 8 * g4);
+      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + rmo(16 * I[t] + l16, 32 * ks + 8 * g4));
+      bf[t][ks] = ldc_b(Kh + rmo(16 * J[t] + l16, 32 * ks + 8 * g4));
     }
   KDA_READS_FIRST();
 #pragma unroll
@@ -1859,7 +1854,7 @@ __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
       bf16x4 o;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
-      *reinterpret_cast<bf16x4*>(p.Wn + prow(16 * tb + l16) * LDK + slot32(32 * w + 16 * ct + 4 * g4)) = o;
+      *reinterpret_cast<bf16x4*>(p.Wn + rmo(16 * tb + l16, slot32(32 * w + 16 * ct + 4 * g4))) = o;
     }
 }
 
@@ -1901,7 +1896,7 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + prow(16 * I + l16) * LDK + 32 * (2 * hf + k2) + 8 * g4);
+      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + rmo(16 * I + l16, 32 * (2 * hf + k2) + 8 * g4));
     KDA_READS_FIRST();
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
