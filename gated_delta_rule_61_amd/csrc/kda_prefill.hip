@@ -1378,6 +1378,17 @@ __device__ __forceinline__ int slot32(int k) {
 // stores).  [D][C] fp16 rows of 80 elements likewise make their fragment
 // reads conflict-free.
 __device__ __forceinline__ int rmo(int t, int e) { return t * LDK + (e ^ ((t << 1) & 56)); }
+// The same offsets split into a per-lane part and a compile-time part, so
+// that each access is one immediate offset from a lane base:
+//  * MFMA fragment of rows 16I + l16, 32-element slab ks, lane group g4:
+//    rmo(16I + l16, 32ks + 8g4) = frag_lane + frag_off(I, ks);
+//  * stores of rows 16I + l16 at element 32s + 8g4 + e (e < 8): likewise with
+//    slab s and + e.
+__device__ __forceinline__ int frag_lane(int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  return l16 * LDK + ((8 * g4) ^ ((2 * l16) & 24));
+}
+__device__ __forceinline__ constexpr int frag_off(int I, int ks) { return 16 * I * LDK + 32 * (ks ^ (I & 1)); }
 
 // Value column, relative to the owner's first, of column i of the owner's
 // state tile nt.  An owner's two 16-column MFMA tiles interleave in groups of
@@ -1575,6 +1586,9 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
     *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
   }
+  // rows 4m + i: rmo(4m + i, e) = 4m LDK + i LDK + (e ^ ((m & 7) << 3)) for i < 4
+  const int wb0 = 4 * m * LDK + (slot32(c0) ^ ((m & 7) << 3));
+  const int wb1 = 4 * m * LDK + (slot32(c0 + 4) ^ ((m & 7) << 3));
   float qk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1601,7 +1615,7 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
       kb[e][i] = (f16)(d * gt.gm[e]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
-    const int r0 = rmo(4 * m + i, slot32(c0)), r1 = rmo(4 * m + i, slot32(c0 + 4));
+    const int r0 = wb0 + i * LDK, r1 = wb1 + i * LDK;
     *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
     *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
@@ -1665,13 +1679,14 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
                                          const int (&J)[NTL], floatx4 (&acc)[NTL], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const bf16* Kh = p.Kh;
+  const int fl = frag_lane(lane);
   MB::F32 af[NTL][DK / 32], bf[NTL][DK / 32];
 #pragma unroll
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + rmo(16 * I[t] + l16, 32 * ks + 8 * g4));
-      bf[t][ks] = ldc_b(Kh + rmo(16 * J[t] + l16, 32 * ks + 8 * g4));
+      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + fl + frag_off(I[t], ks));
+      bf[t][ks] = ldc_b(Kh + fl + frag_off(J[t], ks));
     }
   KDA_READS_FIRST();
 #pragma unroll
@@ -1835,6 +1850,7 @@ __device__ __forceinline__ void solver_offdiag_col(const Ptr& p, int lane) {
 // triangular, so token blocks 0 and 1 need only the first 32-token slab.
 __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
+  const int fl = frag_lane(lane);
   MH::F32 ka[2][2], ab[4][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -1854,7 +1870,8 @@ __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
       bf16x4 o;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
-      *reinterpret_cast<bf16x4*>(p.Wn + rmo(16 * tb + l16, slot32(32 * w + 16 * ct + 4 * g4))) = o;
+      // = rmo(16 tb + l16, slot32(32 w + 16 ct + 4 g4))
+      *reinterpret_cast<bf16x4*>(p.Wn + fl + 16 * tb * LDK + 32 * (w ^ (tb & 1)) + 4 * ct) = o;
     }
 }
 
@@ -1887,7 +1904,7 @@ __device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[NTL
 template <bool SWAP, int NTL>
 __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 (&S)[NTL][DK / 16],
                                                    floatx4 (&Dx)[NTL][4], int lane) {
-  const int g4 = lane >> 4, l16 = lane & 15;
+  const int fl = frag_lane(lane);
   // two halves of the reduction, each half's fragments read ahead of its
   // products (the second half's reads overlap the first half's MFMAs)
 #pragma unroll
@@ -1896,7 +1913,7 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + rmo(16 * I + l16, 32 * (2 * hf + k2) + 8 * g4));
+      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_b(A + fl + frag_off(I, 2 * hf + k2));
     KDA_READS_FIRST();
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
