@@ -1546,10 +1546,8 @@ __device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc& n
 #pragma unroll
     for (int e = 0; e < 8; ++e) gt.b[i][e] *= kLog2e;
   }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.g[i] = ld16(nx.g, nx.vo, i * nx.rs);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 1; i < 4; ++i)
 #pragma unroll
