@@ -61,6 +61,12 @@ def _load():
             lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                             i64, i64, i64, i64, ctypes.c_int]
             lib.kda_oracle_step.restype = ctypes.c_int
+            lib.kda_oracle_fwd_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                              i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+            lib.kda_oracle_fwd_ex.restype = ctypes.c_int
+            lib.kda_oracle_step_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                               i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+            lib.kda_oracle_step_ex.restype = ctypes.c_int
             lib.kda_oracle_max_threads.argtypes = []
             lib.kda_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -84,41 +90,56 @@ def max_threads() -> int:
     return int(_load().kda_oracle_max_threads())
 
 
-def recurrent_fwd(q, k, v, g, beta, S0=None, nthreads: int = 0):
+SCALAR_GATE = 1   # g holds one log-gate per token and head (Gated DeltaNet)
+NO_DELTA = 2      # S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T (no erase; beta unused)
+
+
+def _flags(scalar_gate: bool, delta: bool) -> int:
+    return (SCALAR_GATE if scalar_gate else 0) | (0 if delta else NO_DELTA)
+
+
+def recurrent_fwd(q, k, v, g, beta, S0=None, nthreads: int = 0, scalar_gate: bool = False,
+                  delta: bool = True):
     """Token-by-token fp64 forward.
 
-    q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
+    q, k: [B, T, H, dk]; g: [B, T, H, dk] ([B, T, H] with scalar_gate);
+    v: [B, T, H, dv]; beta: [B, T, H] (may be None without the delta rule);
     S0: [B, H, dk, dv] or None (zeros).  Returns (o [B,T,H,dv], S_T [B,H,dk,dv]).
     """
-    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    q, k, v, g = (_f64(a) for a in (q, k, v, g))
+    beta = None if beta is None else _f64(beta)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    assert k.shape == (B, T, H, dk) and g.shape == (B, T, H, dk)
-    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    assert k.shape == (B, T, H, dk) and g.shape == ((B, T, H) if scalar_gate else (B, T, H, dk))
+    assert v.shape == (B, T, H, dv)
+    assert (beta is None and not delta) or beta.shape == (B, T, H)
     S0a = None if S0 is None else _f64(S0)
     if S0a is not None:
         assert S0a.shape == (B, H, dk, dv)
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     ST = np.zeros((B, H, dk, dv), dtype=np.float64)
-    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(S0a), _ptr(o), _ptr(ST), B, T, H, dk, dv,
-                                int(nthreads))
+    rc = _load().kda_oracle_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(S0a), _ptr(o), _ptr(ST), B, T, H, dk, dv,
+                                   _flags(scalar_gate, delta), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_fwd failed ({rc})")
     return o, ST
 
 
-def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0):
-    """One decode token for N sequences.  S [N,H,dk,dv] fp64 is returned
-    updated (a new array; the input is not modified).  Returns (o, S_new)."""
-    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0, scalar_gate: bool = False, delta: bool = True):
+    """One decode token for N sequences (g [N,H,dk], or [N,H] with
+    scalar_gate).  S [N,H,dk,dv] fp64 is returned updated (a new array; the
+    input is not modified).  Returns (o, S_new)."""
+    q, k, v, g = (_f64(a) for a in (q, k, v, g))
+    beta = None if beta is None else _f64(beta)
     N, H, dk = q.shape
     dv = v.shape[-1]
     Sn = _f64(S).copy()
     assert Sn.shape == (N, H, dk, dv)
     o = np.zeros((N, H, dv), dtype=np.float64)
-    rc = _load().kda_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(Sn), _ptr(o), N, H, dk, dv, int(nthreads))
+    rc = _load().kda_oracle_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(Sn), _ptr(o), N, H, dk, dv, _flags(scalar_gate, delta),
+                                    int(nthreads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_step failed ({rc})")
     return o, Sn

@@ -263,3 +263,72 @@ def test_empty_sequence_returns_initial_state(rng):
     o, ST = oracle.recurrent_fwd(q, k, v, g, beta, S0)
     assert o.shape[1] == 0
     assert np.array_equal(ST, S0)
+
+
+# ------------------------------------------------- variants: scalar gate, no delta
+def test_scalar_gate_mode_is_gated_deltanet(rng):
+    """The scalar-gate mode (one log-gate per token and head) against the
+    scalar-gated rule of [HLA-1] §3.3 written as explicit matrices,
+    S_t = alpha_t (I - beta k k^T) S_{t-1} + beta k v^T (d_k x d_v form)."""
+    T, dk, dv = 6, 4, 3
+    q, k, v, _, beta, S0 = _rand_case(rng, T=T, H=2, dk=dk, dv=dv)
+    a = -np.abs(rng.standard_normal((1, T, 2))) * 0.5
+    o, ST = oracle.recurrent_fwd(q, k, v, a, beta, S0, scalar_gate=True)
+    for h in range(2):
+        S = S0[0, h].copy()
+        for t in range(T):
+            kk = k[0, t, h]
+            S = np.exp(a[0, t, h]) * (np.eye(dk) - beta[0, t, h] * np.outer(kk, kk)) @ S \
+                + beta[0, t, h] * np.outer(kk, v[0, t, h])
+            assert np.max(np.abs(o[0, t, h] - S.T @ q[0, t, h])) < TOL
+        assert np.max(np.abs(ST[0, h] - S)) < TOL
+
+
+def test_no_delta_ungated_is_causal_linear_attention(rng):
+    """Without the delta rule and with alpha = 1 the state is the plain sum of
+    writes, S_t = S_0 + sum_{s<=t} k_s v_s^T ([HLA-1] §3.1), so the read-out is
+    causal linear attention: o_t = S_0^T q_t + sum_{s<=t} (k_s . q_t) v_s."""
+    T, dk, dv = 7, 5, 3
+    q, k, v, _, _, S0 = _rand_case(rng, T=T, H=1, dk=dk, dv=dv)
+    o, ST = oracle.recurrent_fwd(q, k, v, np.zeros((1, T, 1, dk)), None, S0, delta=False)
+    for t in range(T):
+        ref = S0[0, 0].T @ q[0, t, 0] + sum((k[0, s, 0] @ q[0, t, 0]) * v[0, s, 0] for s in range(t + 1))
+        assert np.max(np.abs(o[0, t, 0] - ref)) < TOL
+    assert np.max(np.abs(ST[0, 0] - (S0[0, 0] + np.einsum("sc,sj->cj", k[0, :, 0], v[0, :, 0])))) < TOL
+
+
+def test_no_delta_gated_closed_form(rng):
+    """Per-channel decay without the delta rule (GLA / RWKV-6 form of [HLA-1]
+    §3.3): unrolling the recurrence, channel c of the state is
+    prod_{r<=t} alpha_rc S0[c] + sum_{s<=t} k_sc v_s prod_{s<r<=t} alpha_rc;
+    beta plays no part."""
+    T, dk, dv = 6, 4, 3
+    q, k, v, g, beta, S0 = _rand_case(rng, T=T, H=1, dk=dk, dv=dv)
+    o, ST = oracle.recurrent_fwd(q, k, v, g, beta, S0, delta=False)
+    o2, _ = oracle.recurrent_fwd(q, k, v, g, None, S0, delta=False)
+    assert np.array_equal(o, o2)
+    G = np.cumsum(g[0, :, 0], axis=0)          # G[t, c] = sum_{r<=t} g_rc
+    for t in range(T):
+        S = np.exp(G[t])[:, None] * S0[0, 0]
+        for s in range(t + 1):
+            S = S + np.exp(G[t] - G[s])[:, None] * np.outer(k[0, s, 0], v[0, s, 0])
+        assert np.max(np.abs(o[0, t, 0] - S.T @ q[0, t, 0])) < TOL
+        if t == T - 1:
+            assert np.max(np.abs(ST[0, 0] - S)) < TOL
+
+
+def test_variant_steps_equal_prefill(rng):
+    """T decode steps equal one prefill of T tokens in every variant (the
+    streaming consistency of [HLA-5] §5)."""
+    T, dk, dv = 5, 4, 3
+    q, k, v, g, beta, S0 = _rand_case(rng, T=T, H=2, dk=dk, dv=dv)
+    for scalar_gate in (False, True):
+        gg = g[..., 0] if scalar_gate else g
+        for delta in (True, False):
+            o, ST = oracle.recurrent_fwd(q, k, v, gg, beta, S0, scalar_gate=scalar_gate, delta=delta)
+            S = S0.copy()                      # [N = 1, H, dk, dv]
+            for t in range(T):
+                ot, S = oracle.recurrent_step(q[:, t], k[:, t], v[:, t], gg[:, t], beta[:, t], S,
+                                              scalar_gate=scalar_gate, delta=delta)
+                assert np.max(np.abs(ot - o[:, t])) < TOL
+            assert np.max(np.abs(S - ST)) < TOL
