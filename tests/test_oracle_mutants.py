@@ -23,8 +23,8 @@ MUTANTS = [
      "    /* 1. per-channel forget gate",
      "    /* (mutant) decay moved after the update */ if (0) {} /* 1."),
     ("decay_sign",
-     "const double a = exp(g[c]);",
-     "const double a = exp(-g[c]);"),
+     "? g[0] : g[c]);",
+     "? -g[0] : -g[c]);"),
     ("no_erase",
      "S[c * dv + j] += beta * k[c] * (v[j] - r[j]);",
      "S[c * dv + j] += beta * k[c] * (v[j]);"),
@@ -40,6 +40,15 @@ MUTANTS = [
     ("retrieve_with_q",
      "r[j] += k[c] * S[c * dv + j];",
      "r[j] += q[c] * S[c * dv + j];"),
+    ("scalar_gate_read_per_channel",
+     "(flags & KDA_ORACLE_SCALAR_GATE) ? g[0] : g[c]",
+     "g[c]"),
+    ("no_delta_keeps_beta",
+     "S[c * dv + j] += k[c] * v[j];",
+     "S[c * dv + j] += beta * k[c] * v[j];"),
+    ("no_delta_still_erases",
+     "    if (flags & KDA_ORACLE_NO_DELTA) {",
+     "    if (0) {"),
 ]
 
 
@@ -47,7 +56,7 @@ def _apply(src, name, old, new):
     if name == "erase_before_decay":
         # move the decay loop after erase/write (and before the read)
         start = src.index("    /* 1. per-channel forget gate")
-        end = src.index("    /* 2. retrieve")
+        end = src.index("    if (flags & KDA_ORACLE_NO_DELTA) {")
         decay = src[start:end]
         src = src[:start] + src[end:]
         pos = src.index("    /* 4. read after write")
@@ -64,17 +73,18 @@ def _build(tmp_path, src, tag):
     lib = ctypes.CDLL(str(so))
     dp = ctypes.POINTER(ctypes.c_double)
     lib.kda_oracle_fwd.argtypes = [dp] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int]
+    lib.kda_oracle_fwd_ex.argtypes = [dp] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int]
     return lib
 
 
-def _fwd(lib, q, k, v, g, beta, S0):
+def _fwd(lib, q, k, v, g, beta, S0, flags=0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, g, beta)]
     S0a = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
     o = np.zeros((B, T, H, dv)); ST = np.zeros((B, H, dk, dv))
     p = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-    rc = lib.kda_oracle_fwd(*[p(a) for a in arrs], p(S0a), p(o), p(ST), B, T, H, dk, dv, 1)
+    rc = lib.kda_oracle_fwd_ex(*[p(a) for a in arrs], p(S0a), p(o), p(ST), B, T, H, dk, dv, flags, 1)
     assert rc == 0
     return o, ST
 
@@ -110,6 +120,24 @@ def _pins_fail(lib):
                  np.zeros((1, T, 1, dk)), np.ones((1, T, 1)), S0)
     if np.max(np.abs(K @ ST[0, 0] - V)) > 1e-12:
         fails.append("recall")
+    # scalar gate (flag 1): one gate per token, g laid out [B, T, H]; a
+    # single token against the matrix form with alpha I
+    gs = -np.abs(rng.standard_normal((1, 2, 1)))
+    q2 = rng.standard_normal((1, 2, 1, dk)); k2 = rng.standard_normal((1, 2, 1, dk))
+    v2 = rng.standard_normal((1, 2, 1, dv)); b2 = np.full((1, 2, 1), 0.4)
+    o, ST = _fwd(lib, q2, k2, v2, gs, b2, S0, flags=1)
+    S = S0[0, 0]
+    for t in range(2):
+        kt = k2[0, t, 0]
+        S = (np.eye(dk) - 0.4 * np.outer(kt, kt)) @ (np.exp(gs[0, t, 0]) * S) + 0.4 * np.outer(kt, v2[0, t, 0])
+        if np.max(np.abs(o[0, t, 0] - S.T @ q2[0, t, 0])) > 1e-12:
+            fails.append("scalar_gate")
+            break
+    # no delta (flag 2), ungated: causal linear attention o_t = sum_{s<=t} (q_t.k_s) v_s
+    o, ST = _fwd(lib, q2, k2, v2, np.zeros((1, 2, 1, dk)), b2, None, flags=2)
+    ref = np.tril(q2[0, :, 0] @ k2[0, :, 0].T) @ v2[0, :, 0]
+    if np.max(np.abs(o[0, :, 0] - ref)) > 1e-12:
+        fails.append("no_delta")
     return fails
 
 
