@@ -10,6 +10,8 @@ before timing starts.  Prints ONE JSON line:
   decode        decode tokens/s (256 sequences x 64 tokens per step) + roofline
   roofline      the fused prefill kernel against the HBM bound
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same work
+--variant runs the same step for a variant of the recurrence (scalar gate,
+no delta rule, or both) on the same shapes; the default is KDA itself.
 """
 from __future__ import annotations
 
@@ -37,6 +39,16 @@ PREFILL_FLOPS_PER_TOKHEAD = 6 * D * D + (C + 1) * 4 * D + (C - 1) * D + C * C / 
 STATE_BYTES = D * D * 4
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKHEAD   # state read + write + token I/O
 
+# Variants: (scalar_gate, delta).  A scalar gate reads one bf16 per token and
+# head instead of d_k; without the delta rule beta is not read.
+VARIANTS = {"kda": (False, True), "scalar": (True, True), "nodelta": (False, False),
+            "scalar-nodelta": (True, False)}
+
+
+def tok_bytes(scalar_gate: bool, delta: bool) -> int:
+    """Algorithmic HBM bytes per token and head: q, k, v, g, beta in, o out."""
+    return 3 * D * 2 + (2 if scalar_gate else D * 2) + (2 if delta else 0) + D * 2
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -45,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default="kda",
+                    help="recurrence variant (default: KDA)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -73,17 +87,17 @@ def measured_traffic(kernel: str, digest: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(W, oracle, torch):
+def cpu_baseline(W, oracle, torch, scalar_gate=False, delta=True):
     """The fp64 oracle on the prefill workload's inputs (all 8 x 32 sequences
     of 8192 tokens), timed on the host cores."""
     cfg = W.PREFILL_BF16_B8_H32_T8K
-    inp = W.prefill_inputs(cfg, device="cuda")
+    inp = W.prefill_inputs(cfg, device="cuda", scalar_gate=scalar_gate)
     f64 = lambda t: None if t is None else t.detach().cpu().double().numpy()
     args = [f64(inp[n]) for n in ("q", "k", "v", "g", "beta", "S0")]
     del inp
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    oracle.recurrent_fwd(*args, nthreads=threads)
+    oracle.recurrent_fwd(*args, nthreads=threads, scalar_gate=scalar_gate, delta=delta)
     dt = time.perf_counter() - t0
     tokens = cfg.B * cfg.T
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -116,22 +130,31 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
+    scalar_gate, delta = VARIANTS[args.variant]
+    flags = (1 if scalar_gate else 0) | (0 if delta else 2)
     pcfg = W.PREFILL_BF16_B8_H32_T8K
     dcfg = W.DECODE_256x32
-    inp = W.prefill_inputs(pcfg, device="cuda")
+    inp = W.prefill_inputs(pcfg, device="cuda", scalar_gate=scalar_gate)
     o = torch.empty_like(inp["v"])
     S_T = torch.empty(pcfg.B, pcfg.H, D, D, dtype=torch.float32, device="cuda")
     S = W.decode_state(dcfg, device="cuda")
-    tok = W.decode_tokens(dcfg, device="cuda")
-    steps_tok = [[tok[n][t] for n in ("q", "k", "v", "g", "beta")] for t in range(dcfg.steps)]
+    tok = W.decode_tokens(dcfg, device="cuda", scalar_gate=scalar_gate)
+    if not delta:
+        inp["beta"] = tok["beta"] = None
+    steps_tok = [[None if tok[n] is None else tok[n][t] for n in ("q", "k", "v", "g", "beta")]
+                 for t in range(dcfg.steps)]
     od = torch.empty(dcfg.N, dcfg.H, D, dtype=torch.bfloat16, device="cuda")
+    vkw = dict(scalar_gate=scalar_gate, delta=delta)
+    ws_bytes = kda.lib().kda_chunk_fwd_ex_workspace_size(pcfg.B, pcfg.T, pcfg.H, D, D, 1, flags)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def prefill():
-        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T)
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T,
+                      workspace=ws, **vkw)
 
     def decode():
         for t in range(dcfg.steps):
-            kda.recurrent_step(*steps_tok[t], S, o=od)
+            kda.recurrent_step(*steps_tok[t], S, o=od, **vkw)
 
     for _ in range(args.warmup):
         prefill()
@@ -158,13 +181,17 @@ def main():
     dec_avg = sum(dec_ms) / len(dec_ms)
 
     BTH = pcfg.B * pcfg.T * pcfg.H
-    pre_bytes = BTH * PREFILL_BYTES_PER_TOKHEAD + pcfg.B * pcfg.H * STATE_BYTES   # + S_T write
+    pre_bytes = BTH * tok_bytes(scalar_gate, delta) + pcfg.B * pcfg.H * STATE_BYTES   # + S_T write
     pre_flops = BTH * PREFILL_FLOPS_PER_TOKHEAD
     pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
     digest = source_digest()
     step_heads = dcfg.N * dcfg.H
     dec_step_ms = dec_avg / dcfg.steps
-    dec_gbs = step_heads * DECODE_BYTES_PER_HEAD / (dec_step_ms * 1e-3) / 1e9
+    dec_gbs = step_heads * (2 * STATE_BYTES + tok_bytes(scalar_gate, delta)) / (dec_step_ms * 1e-3) / 1e9
+    pk = "fused_pipe_kernel" if flags == 0 else f"fused_pipe_kernel<{flags}>"
+    dk_name = "decode_kernel" if flags == 0 else f"decode_kernel<{flags}>"
+    vname = {"kda": "", "scalar": " [scalar gate]", "nodelta": " [no delta rule]",
+             "scalar-nodelta": " [scalar gate, no delta rule]"}[args.variant]
 
     def traffic(kernel):
         t = measured_traffic(kernel, digest)
@@ -185,21 +212,22 @@ def main():
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
                 "g=-softplus(N(-3,1)))",
         "config": {"workload": "kda_chunk_fwd B8 H32 T8192 d128 bf16 (S0=0) + "
-                               "kda_recurrent_step 256x32 d128 x64 tokens",
+                               "kda_recurrent_step 256x32 d128 x64 tokens" + vname,
                    "prefill_ms": pre_avg, "decode_ms_per_token_step": dec_step_ms},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic("fused_pipe_kernel"),
-                     "kernel": "fused_pipe_kernel (bf16, d_k = d_v = 128)",
-                     "mfma_frac_algorithmic": pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic(pk),
+                     "kernel": pk + " (bf16, d_k = d_v = 128)",
+                     "mfma_frac_algorithmic": (pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+                                               if flags == 0 else None)},
         "decode": {"value": dcfg.N * dcfg.steps / (dec_avg * 1e-3), "unit": "tokens/s",
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic("decode_kernel"),
-                                "kernel": "decode_kernel<bf16,128,128>"}},
+                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic(dk_name),
+                                "kernel": dk_name + " (bf16, 128 x 128)"}},
     }
     del inp, o, S, tok, steps_tok
     if not args.no_cpu_baseline:
         import oracle
-        line["cpu_baseline"] = cpu_baseline(W, oracle, torch)
+        line["cpu_baseline"] = cpu_baseline(W, oracle, torch, scalar_gate, delta)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

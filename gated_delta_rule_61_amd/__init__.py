@@ -12,6 +12,11 @@ Layouts (row-major, contiguous):
   q, k, g [B, T, H, d_k]; v, o [B, T, H, d_v]; beta [B, T, H];
   S0, S_T [B, H, d_k, d_v] float32.  q, k, v, g, beta share one dtype
   (torch.bfloat16 or torch.float32); o has that dtype.
+
+Variants (keyword arguments of chunk_fwd and recurrent_step): scalar_gate=True
+takes one log-gate per token and head (g [B, T, H]; Gated DeltaNet), and
+delta=False drops the delta rule (S_t = Diag(exp g_t) S_{t-1} + k_t v_t^T;
+beta unused, may be None).
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ ROOT = os.path.dirname(_PKG)
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_SCALAR, KDA_NO_DELTA = 1, 2
 _DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
 _lock = threading.Lock()
@@ -37,6 +43,9 @@ _SIGS = {
     "kda_chunk_fwd": ([_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_staged": ([_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_workspace_size": ([_i] * 6, _sz),
+    "kda_chunk_fwd_ex": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
+    "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -105,23 +114,32 @@ def _need(t, shape, dtype, name):
         raise KDAError(f"{name} must be contiguous")
 
 
-def _prefill_shapes(q, k, v, g, beta):
+def _flags(scalar_gate: bool, delta: bool) -> int:
+    return (KDA_GATE_SCALAR if scalar_gate else 0) | (0 if delta else KDA_NO_DELTA)
+
+
+def _prefill_shapes(q, k, v, g, beta, scalar_gate=False, delta=True):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     _need(q, (B, T, H, dk), dt, "q")
     _need(k, (B, T, H, dk), dt, "k")
-    _need(g, (B, T, H, dk), dt, "g")
+    _need(g, (B, T, H) if scalar_gate else (B, T, H, dk), dt, "g")
     _need(v, (B, T, H, dv), dt, "v")
-    _need(beta, (B, T, H), dt, "beta")
+    if delta or beta is not None:
+        _need(beta, (B, T, H), dt, "beta")
     return B, T, H, dk, dv, dt
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
-              workspace=None, stream=None, want_state=True):
+              workspace=None, stream=None, want_state=True, scalar_gate=False, delta=True):
     """Prefill: returns (o, S_T).  With staged=True the four-kernel schedule
-    runs instead of the fused kernel (same result up to rounding)."""
-    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta)
+    runs instead of the fused kernel (same result up to rounding).  The
+    variants (scalar_gate, delta=False) run on the fused kernel only."""
+    flags = _flags(scalar_gate, delta)
+    if flags and staged:
+        raise KDAError("the staged schedule computes the KDA rule only (no variants)")
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate, delta)
     dev = q.device
     if S0 is not None:
         _need(S0, (B, H, dk, dv), torch.float32, "S0")
@@ -131,32 +149,45 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     L = lib()
     code = _dtype(q)
-    fn = L.kda_chunk_fwd_staged if staged else L.kda_chunk_fwd
-    wsz = (L.kda_chunk_fwd_staged_workspace_size if staged else L.kda_chunk_fwd_workspace_size)(
-        B, T, H, dk, dv, code)
+    if flags:
+        wsz = L.kda_chunk_fwd_ex_workspace_size(B, T, H, dk, dv, code, flags)
+    else:
+        wsz = (L.kda_chunk_fwd_staged_workspace_size if staged else L.kda_chunk_fwd_workspace_size)(
+            B, T, H, dk, dv, code)
     if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
         workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
-              B, T, H, dk, dv, code, _ptr(workspace) if wsz else None, wsz, _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+            B, T, H, dk, dv, code)
+    tail = (_ptr(workspace) if wsz else None, wsz, _stream(stream))
+    if flags:
+        _check(L.kda_chunk_fwd_ex(*args, flags, *tail))
+    else:
+        _check((L.kda_chunk_fwd_staged if staged else L.kda_chunk_fwd)(*args, *tail))
     return o, S_T
 
 
-def recurrent_step(q, k, v, g, beta, S, *, o=None, stream=None):
+def recurrent_step(q, k, v, g, beta, S, *, o=None, stream=None, scalar_gate=False, delta=True):
     """One decode token for N sequences; S [N,H,d_k,d_v] fp32 is updated in
-    place.  Returns o [N,H,d_v]."""
+    place.  Returns o [N,H,d_v].  Variants as for chunk_fwd (g [N,H] with
+    scalar_gate)."""
+    flags = _flags(scalar_gate, delta)
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     _need(q, (N, H, dk), dt, "q")
     _need(k, (N, H, dk), dt, "k")
-    _need(g, (N, H, dk), dt, "g")
+    _need(g, (N, H) if scalar_gate else (N, H, dk), dt, "g")
     _need(v, (N, H, dv), dt, "v")
-    _need(beta, (N, H), dt, "beta")
+    if delta or beta is not None:
+        _need(beta, (N, H), dt, "beta")
     _need(S, (N, H, dk, dv), torch.float32, "S")
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _check(lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
-                                    N, H, dk, dv, _dtype(q), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv, _dtype(q))
+    if flags:
+        _check(lib().kda_recurrent_step_ex(*args, flags, _stream(stream)))
+    else:
+        _check(lib().kda_recurrent_step(*args, _stream(stream)))
     return o
 
 

@@ -85,8 +85,9 @@ int device_cus() {
 // (0: one pass).  It applies where the pipelined kernel does; the count comes
 // from the launch cost model, or from KDA_SEGMENTS (0 or 1: off; n >= 3:
 // about n segments of equal length).
-int segment_count(int B, int T, int H, int dk, int dv, int dtype) {
-  if (dtype != KDA_BF16 || dk != 128 || dv != 128 || env_nsplit() > 1 || !env_pipeline()) return 0;
+int segment_count(int B, int T, int H, int dk, int dv, int dtype, bool variant = false) {
+  if (dtype != KDA_BF16 || dk != 128 || dv != 128) return 0;
+  if (!variant && (env_nsplit() > 1 || !env_pipeline())) return 0;
   if ((int64_t)B * H <= 0 || T <= 0) return 0;
   const char* e = getenv("KDA_SEGMENTS");
   if (e) {
@@ -104,16 +105,24 @@ int segment_count(int B, int T, int H, int dk, int dv, int dtype) {
     if (!(cond)) return (code); \
   } while (0)
 
-// q, k, v, g, o are read/written as 16-byte vectors; beta only needs the
-// alignment of its element type.
+// q, k, v, g, o are read/written as 16-byte vectors; beta, and g with a
+// scalar gate, only need the alignment of their element type.  Without the
+// delta rule beta is not read.
 int check_tokens(const void* q, const void* k, const void* v, const void* g, const void* beta, const void* o,
-                 int dtype) {
-  KDA_REQUIRE(q && k && v && g && beta && o, KDA_ERR_NULL);
+                 int dtype, int flags = 0) {
+  const bool need_beta = (flags & KDA_NO_DELTA) == 0;
+  KDA_REQUIRE(q && k && v && g && o && (beta || !need_beta), KDA_ERR_NULL);
   const uintptr_t esz = dtype == KDA_BF16 ? 2u : 4u;
-  KDA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g) && aligned16(o) &&
-              (reinterpret_cast<uintptr_t>(beta) % esz) == 0, KDA_ERR_ALIGN);
+  const bool g_ok = (flags & KDA_GATE_SCALAR) ? reinterpret_cast<uintptr_t>(g) % esz == 0 : aligned16(g);
+  KDA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && g_ok && aligned16(o) &&
+              (!need_beta || (reinterpret_cast<uintptr_t>(beta) % esz) == 0), KDA_ERR_ALIGN);
   return KDA_OK;
 }
+
+bool valid_flags(int flags) { return (flags & ~(KDA_GATE_SCALAR | KDA_NO_DELTA)) == 0; }
+
+// sizes and dtype for which the prefill variants exist (the pipelined kernel)
+bool variant_dims(int dk, int dv, int dt) { return dt == KDA_BF16 && dk == 128 && dv == 128; }
 
 }  // namespace
 
@@ -142,20 +151,38 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int d
   return kda::prefill_segment_workspace(B * H, segment_count(B, T, H, d_k, d_v, dtype));
 }
 
+size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
+  if (flags == 0) return kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, dtype);
+  if (!valid_flags(flags) || !variant_dims(d_k, d_v, dtype) || check_chunk_dims(B, T, H, d_k, d_v, dtype))
+    return 0;
+  return kda::prefill_segment_workspace(B * H, segment_count(B, T, H, d_k, d_v, dtype, true));
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream) {
+  return kda_chunk_fwd_ex(q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype, 0, workspace,
+                          workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
+                     int flags, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
+  KDA_REQUIRE(valid_flags(flags) && (flags == 0 || variant_dims(d_k, d_v, dtype)), KDA_ERR_ARG);
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
-    st = check_tokens(q, k, v, g, beta, o, dtype);
+    st = check_tokens(q, k, v, g, beta, o, dtype, flags);
     if (st) return st;
   }
   KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
-  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16, env_nsplit(), env_pipeline()};
+  // (the variants run on the pipelined kernel whatever the schedule overrides say)
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16,
+                     flags ? 0 : env_nsplit(), flags ? 1 : env_pipeline()};
+  a.variant = flags;
   // segmented schedule when the caller passes the workspace it needs
-  const int nseg = segment_count(B, T, H, d_k, d_v, dtype);
+  const int nseg = segment_count(B, T, H, d_k, d_v, dtype, flags != 0);
   if (nseg >= 3 && workspace && aligned16(workspace) &&
       workspace_bytes >= kda::prefill_segment_workspace(B * H, nseg)) {
     a.nseg = nseg;
@@ -256,14 +283,21 @@ int kda_stage_output(const void* q, const void* k, const float* b, const float* 
 
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* S,
                        void* o, int N, int H, int d_k, int d_v, int dtype, void* stream) {
+  return kda_recurrent_step_ex(q, k, v, g, beta, S, o, N, H, d_k, d_v, dtype, 0, stream);
+}
+
+int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, float* S,
+                          void* o, int N, int H, int d_k, int d_v, int dtype, int flags, void* stream) {
   int st = check_step_dims(N, H, d_k, d_v, dtype);
   if (st) return st;
+  KDA_REQUIRE(valid_flags(flags), KDA_ERR_ARG);
   if ((int64_t)N * H == 0) return KDA_OK;
-  st = check_tokens(q, k, v, g, beta, o, dtype);
+  st = check_tokens(q, k, v, g, beta, o, dtype, flags);
   if (st) return st;
   KDA_REQUIRE(S != nullptr, KDA_ERR_NULL);
   KDA_REQUIRE(aligned16(S), KDA_ERR_ALIGN);
   kda::DecodeArgs a{q, k, v, g, beta, S, o, N, H, d_k, d_v, dtype == KDA_BF16};
+  a.variant = flags;
   return hip_status(kda::launch_decode(a, (hipStream_t)stream));
 }
 

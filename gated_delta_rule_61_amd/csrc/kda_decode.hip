@@ -18,8 +18,12 @@
 
 namespace kda {
 
-template <typename T, int DK, int DV>
+// Variants (V): a scalar gate reads one g per sequence and head and decays
+// every row by it; without the delta rule delta = v (nothing is retrieved or
+// erased, beta is not read), so only S'^T q is reduced.
+template <typename T, int DK, int DV, int V>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr bool SG = (V & kVarScalarGate) != 0, ND = (V & kVarNoDelta) != 0;
   constexpr int NT = 256;
   constexpr int CG = DV / 4;        // float4 column groups
   constexpr int RG = NT / CG;       // row groups
@@ -44,13 +48,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   const T* qh = reinterpret_cast<const T*>(a.q) + head * DK;
   const T* kh = reinterpret_cast<const T*>(a.k) + head * DK;
-  const T* gh = reinterpret_cast<const T*>(a.g) + head * DK;
+  const T* gh = reinterpret_cast<const T*>(a.g) + head * (SG ? 1 : DK);
   const T* vh = reinterpret_cast<const T*>(a.v) + head * DV;
-  const float beta = to_f32(reinterpret_cast<const T*>(a.beta)[head]);
+  const float beta = ND ? 1.f : to_f32(reinterpret_cast<const T*>(a.beta)[head]);
   if (tid < DK) {
     sk[tid] = to_f32(kh[tid]);
     sq[tid] = to_f32(qh[tid]);
-    sa[tid] = fast_exp(to_f32(gh[tid]));
+    sa[tid] = fast_exp(to_f32(gh[SG ? 0 : tid]));
   }
   if (tid < DV) sv[tid] = to_f32(vh[tid]);
   __syncthreads();
@@ -70,10 +74,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < RPT; ++i) {
     const int row = rg + RG * i;
     s[i] *= sa[row];
-    r += sk[row] * s[i];
+    if constexpr (!ND) r += sk[row] * s[i];
     sqv += sq[row] * s[i];
   }
-  *reinterpret_cast<floatx4*>(&red_r[rg][4 * cg]) = r;
+  if constexpr (!ND) *reinterpret_cast<floatx4*>(&red_r[rg][4 * cg]) = r;
   *reinterpret_cast<floatx4*>(&red_s[rg][4 * cg]) = sqv;
   __syncthreads();
 
@@ -81,8 +85,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (tid < DV) {
     float rr = 0.f, ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < RG; ++j) { rr += red_r[j][tid]; ss += red_s[j][tid]; }
-    const float d = beta * (sv[tid] - rr);
+    for (int j = 0; j < RG; ++j) {
+      if constexpr (!ND) rr += red_r[j][tid];
+      ss += red_s[j][tid];
+    }
+    const float d = ND ? sv[tid] : beta * (sv[tid] - rr);
     sdelta[tid] = d;
     T* oh = reinterpret_cast<T*>(a.o) + head * DV;
     oh[tid] = from_f32<T>(ss + d * skq);
@@ -103,7 +110,16 @@ template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int64_t nh = (int64_t)a.N * a.H;
   if (nh == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)nh), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)nh), block(256);
+  switch (a.variant) {
+    case 0: hipLaunchKernelGGL((decode_kernel<T, DK, DV, 0>), grid, block, 0, s, a); break;
+    case kVarScalarGate: hipLaunchKernelGGL((decode_kernel<T, DK, DV, kVarScalarGate>), grid, block, 0, s, a); break;
+    case kVarNoDelta: hipLaunchKernelGGL((decode_kernel<T, DK, DV, kVarNoDelta>), grid, block, 0, s, a); break;
+    case kVarScalarGate | kVarNoDelta:
+      hipLaunchKernelGGL((decode_kernel<T, DK, DV, kVarScalarGate | kVarNoDelta>), grid, block, 0, s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -6,6 +6,10 @@
 
 namespace kda {
 
+// Variants of the recurrence, bit flags (the values of the C ABI's):
+constexpr int kVarScalarGate = 1;   // g holds one log-gate per token and head ([B,T,H] / [N,H])
+constexpr int kVarNoDelta = 2;      // no erase term: S_t = Diag(exp g_t) S_{t-1} + k_t v_t^T, beta unused
+
 struct PrefillArgs {
   const void* q; const void* k; const void* v; const void* g; const void* beta;
   const float* S0; void* o; float* S_T;
@@ -18,6 +22,7 @@ struct PrefillArgs {
   int nseg, seg_len;
   int pass;       // set by the launcher: 1 = segment 0 and the segment maps, 3 = segments 1..nseg-1
   float* ws;      // nseg_workspace_bytes() of fp32 scratch
+  int variant;    // kVar* flags (nonzero: bf16, d = 128, pipelined kernel only)
 };
 
 struct StageArgs {
@@ -31,6 +36,7 @@ struct DecodeArgs {
   const void* q; const void* k; const void* v; const void* g; const void* beta;
   float* S; void* o;
   int N, H, dk, dv, bf16;
+  int variant;    // kVar* flags
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

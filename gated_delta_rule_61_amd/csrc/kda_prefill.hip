@@ -1454,6 +1454,7 @@ __device__ __forceinline__ float row_last(float x) {
 // 32o.. of v in the same lane layout.)
 struct WRegs {
   Vec16 q[4], k[4], g[4];
+  uint32_t gs[4];      // scalar-gate variant: the gates of tokens 4m..4m+3 (bf16 bits)
   uint32_t beta_bits;
 };
 
@@ -1461,24 +1462,6 @@ __device__ __forceinline__ uint32_t wlane_off(int H, int w, int lane) {
   return (uint32_t)((4 * (lane & 15) * H * DK + 32 * w + 8 * (lane >> 4)) * 2);
 }
 
-// Buffer resources and offsets of one chunk's q, k, g, beta for a worker.
-struct QkgSrc {
-  __amdgpu_buffer_rsrc_t q, k, g, b;
-  uint32_t vo, boff;
-  int rs;
-  __device__ __forceinline__ QkgSrc(const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
-    const int t0 = n * C, nv = min(C, a.T - t0);
-    const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
-    const uint32_t bytes = chunk_bytes(nv, a.H * DK, DK, 2);
-    q = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok0 * DK, bytes);
-    k = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok0 * DK, bytes);
-    g = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0 * DK, bytes);
-    b = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, 2));
-    vo = wlane_off(a.H, w, lane);
-    boff = (uint32_t)(lane * a.H * 2);
-    rs = a.H * DK * 2;
-  }
-};
 __device__ __forceinline__ Vec16 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t vo, int so) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0);
   Vec16 v;
@@ -1486,33 +1469,58 @@ __device__ __forceinline__ Vec16 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t vo, in
   return v;
 }
 
+// Buffer resources and offsets of one chunk's q, k, g, beta for a worker.
+// Scalar gate: g is [B, T, H] and the lane reads the gates of its tokens
+// 4m..4m+3 (go, then gr bytes apart).  No delta rule: beta is not read.
+template <int V>
+struct QkgSrc {
+  __amdgpu_buffer_rsrc_t q, k, g, b;
+  uint32_t vo, boff, go;
+  int rs, gr;
+  __device__ __forceinline__ QkgSrc(const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
+    const int t0 = n * C, nv = min(C, a.T - t0);
+    const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
+    const uint32_t bytes = chunk_bytes(nv, a.H * DK, DK, 2);
+    q = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok0 * DK, bytes);
+    k = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok0 * DK, bytes);
+    vo = wlane_off(a.H, w, lane);
+    rs = a.H * DK * 2;
+    if constexpr ((V & kVarScalarGate) != 0) {
+      g = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0, chunk_bytes(nv, a.H, 1, 2));
+      go = (uint32_t)(4 * (lane & 15) * a.H * 2);
+      gr = a.H * 2;
+    } else {
+      g = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0 * DK, bytes);
+      go = vo;
+      gr = rs;
+    }
+    if constexpr ((V & kVarNoDelta) == 0) {
+      b = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, 2));
+      boff = (uint32_t)(lane * a.H * 2);
+    }
+  }
+  // this chunk's gates (of the variant's layout) into r
+  __device__ __forceinline__ void load_g(WRegs& r) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr ((V & kVarScalarGate) != 0)
+        r.gs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(g, go, i * gr, 0);
+      else
+        r.g[i] = ld16(g, go, i * gr);
+    }
+  }
+};
+
+template <int V>
 __device__ __forceinline__ void fetch_qkg(WRegs& r, const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
-  const int t0 = n * C, nv = min(C, a.T - t0);
-  const int64_t tok0 = ((int64_t)bb * a.T + t0) * a.H + h;
-  const uint32_t bytes = chunk_bytes(nv, a.H * DK, DK, 2);
-  const uint32_t vo = wlane_off(a.H, w, lane);
-  const int rs = a.H * DK * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok0 * DK, bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok0 * DK, bytes);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<const bf16*>(a.g) + tok0 * DK, bytes);
+  const QkgSrc<V> src(a, bb, h, n, w, lane);
+  src.load_g(r);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rg, vo, i * rs, 0);
-    r.g[i].w[0] = x[0]; r.g[i].w[1] = x[1]; r.g[i].w[2] = x[2]; r.g[i].w[3] = x[3];
-  }
+  for (int i = 0; i < 4; ++i) r.k[i] = ld16(src.k, src.vo, i * src.rs);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, i * rs, 0);
-    r.k[i].w[0] = x[0]; r.k[i].w[1] = x[1]; r.k[i].w[2] = x[2]; r.k[i].w[3] = x[3];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, vo, i * rs, 0);
-    r.q[i].w[0] = x[0]; r.q[i].w[1] = x[1]; r.q[i].w[2] = x[2]; r.q[i].w[3] = x[3];
-  }
-  const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(reinterpret_cast<const bf16*>(a.beta) + tok0, chunk_bytes(nv, a.H, 1, 2));
-  r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(lane * a.H * 2), 0, 0);
+  for (int i = 0; i < 4; ++i) r.q[i] = ld16(src.q, src.vo, i * src.rs);
+  if constexpr ((V & kVarNoDelta) == 0)
+    r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src.b, src.boff, 0, 0);
 }
 
 __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int bb, int h, int n, int w, int lane) {
@@ -1538,16 +1546,38 @@ struct Gates {
 };
 
 // Prefix sums of the gates in r.g; r.g is then reloaded with the gates of the
-// chunk that nx addresses (the next scan's input).
-__device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc& nx) {
+// chunk that nx addresses (the next scan's input).  With a scalar gate the
+// one sum per token is formed once and copied to all eight channels.
+template <int V>
+__device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc<V>& nx) {
+  if constexpr ((V & kVarScalarGate) != 0) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = bf_lo(r.gs[i]) * kLog2e;
+    nx.load_g(r);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) x[i] += x[i - 1];
+    const float tot = x[3];
+    float s = add_row_shr<1>(tot);
+    s = add_row_shr<2>(s);
+    s = add_row_shr<4>(s);
+    s = add_row_shr<8>(s);
+    const float ex = s - tot, gm = exp2_hw(row_last(s));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt.b[i][e] = x[i] + ex;
+      gt.gm[e] = gm;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     unpack8(r.g[i], gt.b[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) gt.b[i][e] *= kLog2e;
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.g[i] = ld16(nx.g, nx.vo, i * nx.rs);
+  nx.load_g(r);
 #pragma unroll
   for (int i = 1; i < 4; ++i)
 #pragma unroll
@@ -1576,8 +1606,13 @@ __device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc& n
 // row as each row is consumed, so the loads spread over this phase's
 // arithmetic instead of arriving as one burst; each row's loads are pinned in
 // place by scheduling fences.
+//
+// Without the delta rule Kt (row-major and transposed) has no reader and is
+// not formed.
+template <int V>
 __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
-                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc& nx) {
+                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc<V>& nx) {
+  constexpr bool ND = (V & kVarNoDelta) != 0;
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
   if (m == 0) {
@@ -1603,19 +1638,23 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
     bf16x8 kt, kh, qt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float ep = exp2_hw(gt.b[i][e]);
-      const float em = exp2_hw(-gt.b[i][e]);
+      // (a scalar gate: the same factors for every channel)
+      const int es = (V & kVarScalarGate) ? 0 : e;
+      const float ep = exp2_hw(gt.b[i][es]);
+      const float em = exp2_hw(-gt.b[i][es]);
       const float a = kf[e] * ep, d = kf[e] * em;
       kt[e] = (bf16)a;
       kh[e] = (bf16)d;
       qt[e] = (bf16)(qf[e] * ep);
-      kt_t[e][i] = (f16)a;
-      kb[e][i] = (f16)(d * gt.gm[e]);
+      if constexpr (!ND) kt_t[e][i] = (f16)a;
+      kb[e][i] = (f16)(d * gt.gm[es]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
     const int r0 = wb0 + i * LDK, r1 = wb1 + i * LDK;
-    *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
-    *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
+    if constexpr (!ND) {
+      *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
+      *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
+    }
     *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4*>(p.Kh + r1) = __builtin_shufflevector(kh, kh, 4, 5, 6, 7);
     *reinterpret_cast<bf16x4*>(p.Qt + r0) = __builtin_shufflevector(qt, qt, 0, 1, 2, 3);
@@ -1628,12 +1667,16 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
 }
 
 // Phase 2a of a worker: Kt^T and Kb^T from registers (4 tokens per store).
+// (Kt^T only with the delta rule.)
+template <int V>
 __device__ __forceinline__ void worker_kbt(const Ptr& p, const f16x4 (&kb)[8], const f16x4 (&kt_t)[8], int w,
                                            int lane) {
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
+  if constexpr ((V & kVarNoDelta) == 0) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KtT + (c0 + e) * LDT + 4 * m) = kt_t[e];
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<f16x4*>(p.KbT + (c0 + e) * LDT + slot32(4 * m)) = kb[e];
 }
@@ -1896,6 +1939,20 @@ __device__ __forceinline__ void owner_u(const Ptr& p, int col0, floatx4 (&U)[NTL
     }
 }
 
+// Phase 3, owners, without the delta rule: U = V for columns col0 ..
+// col0 + 31 in the layout of owner_u (the values are the pseudo-values when
+// nothing is erased), read from V^T.
+__device__ __forceinline__ void owner_v_rows(const Ptr& p, int col0, floatx4 (&U)[2][4], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const f16x4 x = *reinterpret_cast<const f16x4*>(p.VT + (col0 + vcol(nt, l16)) * LDT + 16 * tb + 4 * g4);
+      U[nt][tb] = floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+}
+
 // Dx[nt][I] += A[rows 16I..] @ S[nt] (A row-major bf16 in LDS, S in registers),
 // every A fragment read before the products.  With SWAP the tiles are held
 // transposed (lane: token l16, state columns 4g..4g+3).
@@ -1995,8 +2052,13 @@ __device__ __forceinline__ void owner_store(const floatx4 (&O)[2][4], __amdgpu_b
 
 }  // namespace pipe
 
+// V: variant flags (kVarScalarGate, kVarNoDelta).  Without the delta rule
+// A' = I and W = 0: the pseudo-values are the values, so the L blocks, the
+// solver, W and the W S product drop out and only P, Kh, Qt, Kb remain.
+template <int V>
 __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   using namespace pipe;
+  constexpr bool ND = (V & kVarNoDelta) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2082,7 +2144,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       p.sync(smem_raw);
       // phase 1: finish chunk n
       if (n >= 0) {
-        rows_times_state_b<false>(p.Wn, S, U, lane);
+        if constexpr (!ND) rows_times_state_b<false>(p.Wn, S, U, lane);
         MH::F32 Df[2][2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -2103,7 +2165,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       if (nxt && !vzero) owner_vt(p, vr, o, lane);
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
-      if (nxt) solver_block(p, o, lane);
+      if (!ND && nxt) solver_block(p, o, lane);
       // values of chunk n+2: unconditional (zeros past the end), and after the
       // role switch -- loads issued just before such a switch were seen to
       // leave one wavefront's copy of the loaded registers wrong
@@ -2123,7 +2185,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int I = 0; I < 4; ++I) U[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (nxt && !vzero) owner_u(p, col0, U, lane);
+      if (nxt && !vzero) {
+        if constexpr (ND)
+          owner_v_rows(p, col0, U, lane);
+        else
+          owner_u(p, col0, U, lane);
+      }
     }
     if (sTp) store_state_v(S, sTp, col0, lane);
   } else {
@@ -2131,8 +2198,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int w = wave - 4;
     WRegs r;
     Gates gt;
-    fetch_qkg(r, a, bb, h, c0, w, lane);   // zeros when the sequence is empty
-    worker_scan(r, gt, QkgSrc(a, bb, h, c0 + 1, w, lane));
+    fetch_qkg<V>(r, a, bb, h, c0, w, lane);   // zeros when the sequence is empty
+    worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + 1, w, lane));
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
@@ -2144,17 +2211,34 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // branch: loaded registers merging with old ones at a join would make
       // the merge wait for them.
       {
-        const QkgSrc nx(a, bb, h, c0 + n + 2, w, lane);
-        if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
-        r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
-        worker_apply(p, r, gt, w, lane, (n + 1) & 1, kb, kt_t, nx);
+        const QkgSrc<V> nx(a, bb, h, c0 + n + 2, w, lane);
+        if constexpr (!ND) {
+          if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
+          r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
+        }
+        worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, kb, kt_t, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 2a: Kt^T, Kb^T; P blocks and the off-diagonal blocks of L, four
-      // each (state-only runs: the L blocks alone)
-      if (nxt && !outp) {
-        worker_kbt(p, kb, kt_t, w, lane);
+      // each (state-only runs: the L blocks alone; no delta rule: the P blocks
+      // alone)
+      if (ND && nxt && outp) {
+        worker_kbt<V>(p, kb, kt_t, w, lane);
+        switch (w) {
+          case 0: { const bool q[3] = {1, 1, 1}; const int I[3] = {0, 3, 3}, J[3] = {0, 0, 3};
+                    lp_block_tiles<3>(p, q, I, J, lane); break; }
+          case 1: { const bool q[3] = {1, 1, 1}; const int I[3] = {1, 1, 3}, J[3] = {0, 1, 1};
+                    lp_block_tiles<3>(p, q, I, J, lane); break; }
+          case 2: { const bool q[2] = {1, 1}; const int I[2] = {2, 2}, J[2] = {0, 1};
+                    lp_block_tiles<2>(p, q, I, J, lane); break; }
+          default: { const bool q[2] = {1, 1}; const int I[2] = {2, 3}, J[2] = {2, 2};
+                     lp_block_tiles<2>(p, q, I, J, lane); break; }
+        }
+      } else if (ND && nxt) {
+        worker_kbt<V>(p, kb, kt_t, w, lane);
+      } else if (nxt && !outp) {
+        worker_kbt<V>(p, kb, kt_t, w, lane);
         switch (w) {
           case 0: { const bool q[2] = {0, 0}; const int I[2] = {1, 2}, J[2] = {0, 1};
                     lp_block_tiles<2>(p, q, I, J, lane); break; }
@@ -2166,7 +2250,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
                      lp_block_tiles<1>(p, q, I, J, lane); break; }
         }
       } else if (nxt) {
-        worker_kbt(p, kb, kt_t, w, lane);
+        worker_kbt<V>(p, kb, kt_t, w, lane);
         switch (w) {
           case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
                     lp_block_tiles<4>(p, q, I, J, lane); break; }
@@ -2183,7 +2267,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // phase 2b: workers 1-3: the off-diagonal blocks of A' in block columns
       // 0-2; all: gate prefix sums of chunk n+2 and the gate loads of chunk
       // n+3 (on every slot)
-      if (nxt) {
+      if (!ND && nxt) {
         if (w == 1)
           solver_offdiag_col<0>(p, lane);
         else if (w == 2)
@@ -2191,11 +2275,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         else if (w == 3)
           solver_offdiag_col<2>(p, lane);
       }
-      worker_scan(r, gt, QkgSrc(a, bb, h, c0 + n + 3, w, lane));
+      worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
       p.sync(smem_raw);
       KDA_FRESH_LANE();
       // phase 3: W
-      if (nxt) worker_w(p, w, lane);
+      if (!ND && nxt) worker_w(p, w, lane);
     }
   }
 }
@@ -2316,8 +2400,10 @@ static hipError_t launch_fused_d(const PrefillArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
+template <int V>
+static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
   const int bytes = pipe::BYTES;
+  auto fused_pipe_kernel = ::kda::fused_pipe_kernel<V>;
   hipError_t e = set_smem(fused_pipe_kernel, bytes);
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H;
@@ -2339,6 +2425,16 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
   return hipGetLastError();
+}
+
+static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
+  switch (a.variant) {
+    case 0: return launch_pipe_v<0>(a, s);
+    case kVarScalarGate: return launch_pipe_v<kVarScalarGate>(a, s);
+    case kVarNoDelta: return launch_pipe_v<kVarNoDelta>(a, s);
+    case kVarScalarGate | kVarNoDelta: return launch_pipe_v<kVarScalarGate | kVarNoDelta>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Segments per sequence for the segmented schedule, from a cost model in
@@ -2375,6 +2471,8 @@ size_t prefill_segment_workspace(int BH, int nseg) {
 
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
+  // the variants exist in the pipelined kernel only
+  if (a.variant != 0) return (a.bf16 && a.dk == 128 && a.dv == 128) ? launch_pipe(a, s) : hipErrorInvalidValue;
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {
       // the pipelined kernel without a column split is the faster one at every

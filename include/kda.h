@@ -113,6 +113,45 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
                        int N, int H, int d_k, int d_v, int dtype, void* stream);
 
 /*
+ * Variants of the recurrence, the two relatives of KDA on "...Making LLM
+ * Training and Inference More Efficient", as bit flags:
+ *   KDA_GATE_SCALAR  one forget gate per token and head (Gated DeltaNet,
+ *                    §3.2): g is [B,T,H] ([N,H] for a decode step) and
+ *                    Diag(exp g_t) becomes exp(g_t) I.
+ *   KDA_NO_DELTA     no delta rule (the per-channel decay of GLA / RWKV-6,
+ *                    §3.3): S_t = Diag(exp g_t) S_{t-1} + k_t v_t^T,
+ *                    o_t = S_t^T q_t; beta is not read and may be NULL.
+ * Both may be combined (a scalar-gated linear attention).
+ */
+typedef enum { KDA_GATE_SCALAR = 1, KDA_NO_DELTA = 2 } kda_variant;
+
+/*
+ * kda_chunk_fwd_ex -- kda_chunk_fwd for the variants above.  `flags` is an
+ * OR of kda_variant values (0: exactly kda_chunk_fwd).  Arguments, layouts,
+ * aliasing and workspace as for kda_chunk_fwd, except the g layout and the
+ * optional beta that the flags change.  Nonzero flags are supported for
+ * dtype KDA_BF16 with d_k = d_v = 128 (the software-pipelined kernel, one
+ * pass or segmented); other sizes / dtypes return KDA_ERR_ARG, unknown flag
+ * bits KDA_ERR_ARG.
+ */
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* S0, void* o, float* S_T,
+                     int B, int T, int H, int d_k, int d_v, int dtype, int flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_chunk_fwd_ex's fastest schedule (0 = none needed). */
+size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
+
+/*
+ * kda_recurrent_step_ex -- kda_recurrent_step for the variants above (every
+ * dtype and head size kda_recurrent_step supports).  With KDA_GATE_SCALAR
+ * g is [N,H]; with KDA_NO_DELTA beta may be NULL.
+ */
+int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* S, void* o,
+                          int N, int H, int d_k, int d_v, int dtype, int flags, void* stream);
+
+/*
  * Staged schedule: the same forward as kda_chunk_fwd, run as four separate
  * kernels with intermediates in a caller-provided workspace (the chunked
  * method's steps one by one).  Slower than kda_chunk_fwd; it exists so each

@@ -39,10 +39,10 @@
 /* Variants (flags of the _ex entry points):
  *   KDA_ORACLE_SCALAR_GATE: one log-gate per token and head, g [B, T, H]
  *     ([N, H] for a step), applied to every key channel -- the scalar-gated
- *     delta rule (Gated DeltaNet) of [HLA-1] §3.3, alpha_t times the identity.
+ *     delta rule (Gated DeltaNet) of [HLA-1] §3.2, alpha_t times the identity.
  *   KDA_ORACLE_NO_DELTA: no erase step, S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T
- *     -- per-channel decay without the delta rule (GLA / RWKV-6 style,
- *     [HLA-1] §3.3); beta is not used. */
+ *     -- per-channel decay without the delta rule (GLA / RWKV-6,
+ *     [HLA-1] §3.3, first formula); beta is not used. */
 #define KDA_ORACLE_SCALAR_GATE 1
 #define KDA_ORACLE_NO_DELTA 2
 

@@ -77,16 +77,19 @@ def check_prefill(o_gpu, S_gpu, o_ref, S_ref, dtype, what=""):
     return stats
 
 
-def oracle_prefill(inp, heads=None, nthreads=0):
+def oracle_prefill(inp, heads=None, nthreads=0, scalar_gate=False, delta=True):
     """Oracle on all heads, or on a list of (b, h) pairs (returned stacked as
-    B' = len(heads) sequences of one head each)."""
+    B' = len(heads) sequences of one head each).  scalar_gate / delta select
+    the variants (g [B,T,H]; no erase, beta unused)."""
     q, k, v, g, beta, S0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "S0"))
+    if not delta:
+        beta = None
+    kw = dict(scalar_gate=scalar_gate, delta=delta)
     if heads is None:
-        return oracle.recurrent_fwd(to64(q), to64(k), to64(v), to64(g), to64(beta), to64(S0), nthreads)
-    sel = lambda t: np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
-    selb = lambda t: np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
+        return oracle.recurrent_fwd(to64(q), to64(k), to64(v), to64(g), to64(beta), to64(S0), nthreads, **kw)
+    sel = lambda t: None if t is None else np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
     S0s = None if S0 is None else np.stack([to64(S0[b, h]) for b, h in heads])[:, None]
-    return oracle.recurrent_fwd(sel(q), sel(k), sel(v), sel(g), selb(beta), S0s, nthreads)
+    return oracle.recurrent_fwd(sel(q), sel(k), sel(v), sel(g), sel(beta), S0s, nthreads, **kw)
 
 
 def pick(o, S, heads):

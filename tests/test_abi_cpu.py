@@ -96,3 +96,33 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(kda.KDAError):
         kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1), None)
+
+
+def _fwd_ex(L, flags, **kw):
+    a = dict(q=16, k=16, v=16, g=16, beta=16, S0=None, o=16, ST=None, B=1, T=64, H=1, dk=128, dv=128, dt=1)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kda_chunk_fwd_ex(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["S0"]), p(a["o"]),
+                              p(a["ST"]), a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], flags, None, 0, None)
+
+
+def test_variant_validation(L):
+    """kda_chunk_fwd_ex / kda_recurrent_step_ex: unknown flags and sizes the
+    variants do not cover are rejected, beta may be NULL only without the
+    delta rule, and a scalar gate needs only element alignment."""
+    assert _fwd_ex(L, 4) == -7                        # unknown flag bit
+    assert _fwd_ex(L, 1, dk=64, dv=64) == -7          # variants: bf16 d = 128 only
+    assert _fwd_ex(L, 2, dt=0, dk=64, dv=64) == -7
+    assert _fwd_ex(L, 1, beta=None) == -1             # the delta rule needs beta
+    assert _fwd_ex(L, 1, g=18, q=None) == -1
+    assert _fwd_ex(L, 2, beta=None, q=18) == -4       # beta may be NULL, q still checked
+    assert _fwd_ex(L, 3, beta=None, g=18, q=18) == -4
+    assert _fwd_ex(L, 0, dk=96, dv=96) == -2          # flags 0: the plain entry point's checks
+    assert _fwd_ex(L, 3, B=0) == 0
+    assert L.kda_chunk_fwd_ex_workspace_size(1, 4096, 16, 64, 64, 1, 1) == 0
+    assert L.kda_chunk_fwd_ex_workspace_size(1, 4096, 16, 128, 128, 1, 8) == 0
+    p = ctypes.c_void_p(16)
+    assert L.kda_recurrent_step_ex(p, p, p, p, p, p, p, 4, 2, 128, 128, 1, 8, None) == -7
+    assert L.kda_recurrent_step_ex(p, p, p, p, None, p, p, 4, 2, 128, 128, 1, 1, None) == -1
+    assert L.kda_recurrent_step_ex(p, p, p, ctypes.c_void_p(18), p, p, p, 4, 2, 128, 128, 1, 0, None) == -4
+    assert L.kda_recurrent_step_ex(p, p, p, p, p, p, p, 0, 2, 128, 128, 1, 3, None) == 0

@@ -187,7 +187,7 @@ def test_linearity_in_values_and_state(rng):
 
 
 def test_scalar_gate_matches_gated_deltanet(rng):
-    """A channel-constant gate is the scalar-gated rule of [HLA-1] §3.3,
+    """A channel-constant gate is the scalar-gated rule of [HLA-1] §3.2,
     S_t = alpha_t (I - beta k k^T) S_{t-1} + beta v k^T (in d_k x d_v form)."""
     T, dk, dv = 5, 4, 3
     q, k, v, _, beta, S0 = _rand_case(rng, T=T, H=1, dk=dk, dv=dv)
@@ -233,7 +233,8 @@ def test_norm_growth_bound(rng):
 # ---------------------------------------------------------------- P10
 def test_full_overwrite_latest_value_wins(rng):
     """beta = 1 with the same unit key repeated: the latest value replaces the
-    old one (S_t^T k = v_t), [HLA-1] §3.2 ("beta -> 1 means complete overwrite")."""
+    old one (S_t^T k = v_t): [HLA-1] §3.2 and [HLA-4] §2.3 give beta = 1 as a
+    full overwrite."""
     T, dk, dv = 6, 5, 3
     kk = rng.standard_normal(dk)
     kk /= np.linalg.norm(kk)
@@ -268,7 +269,7 @@ def test_empty_sequence_returns_initial_state(rng):
 # ------------------------------------------------- variants: scalar gate, no delta
 def test_scalar_gate_mode_is_gated_deltanet(rng):
     """The scalar-gate mode (one log-gate per token and head) against the
-    scalar-gated rule of [HLA-1] §3.3 written as explicit matrices,
+    scalar-gated rule of [HLA-1] §3.2 written as explicit matrices,
     S_t = alpha_t (I - beta k k^T) S_{t-1} + beta k v^T (d_k x d_v form)."""
     T, dk, dv = 6, 4, 3
     q, k, v, _, beta, S0 = _rand_case(rng, T=T, H=2, dk=dk, dv=dv)

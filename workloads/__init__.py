@@ -11,7 +11,9 @@ Input recipe (per token and head):
   g     = -softplus(N(mu, 1)), mu = -3 (or -5)  shape [B, T, H, d_k]   (log alpha)
   S0    = 0, or N(0, sigma) in fp32             shape [B, H, d_k, d_v]
 then q, k, v, g, beta are cast to the workload's input dtype.  The second
-argument of N(.,.) is a standard deviation.
+argument of N(.,.) is a standard deviation.  For the scalar-gate variant g is
+drawn the same way with one value per token and head (shape [B, T, H]); the
+variant without the delta rule draws beta as usual and does not use it.
 """
 from __future__ import annotations
 
@@ -66,28 +68,29 @@ def _gen(device, seed: int) -> torch.Generator:
     return gen
 
 
-def _tokens(shape_lead, dk, dv, dtype, gate_mu, device, gen):
+def _tokens(shape_lead, dk, dv, dtype, gate_mu, device, gen, scalar_gate=False):
     """Draw q, k, v, g, beta for a leading shape (e.g. (B,T,H) or (N,H))."""
     f32 = dict(dtype=torch.float32, device=device, generator=gen)
     q = torch.randn(*shape_lead, dk, **f32)
     k = torch.randn(*shape_lead, dk, **f32)
     v = torch.randn(*shape_lead, dv, **f32)
     beta = torch.sigmoid(torch.randn(*shape_lead, **f32))
-    g = -F.softplus(torch.randn(*shape_lead, dk, **f32) + gate_mu)
+    g = -F.softplus(torch.randn(*shape_lead, *(() if scalar_gate else (dk,)), **f32) + gate_mu)
     q = q / q.norm(dim=-1, keepdim=True)
     k = k / k.norm(dim=-1, keepdim=True)
     return [x.to(dtype).contiguous() for x in (q, k, v, g, beta)]
 
 
 def prefill_inputs(cfg: Prefill, device="cpu", seed: int | None = None,
-                   B: int | None = None, T: int | None = None, H: int | None = None):
+                   B: int | None = None, T: int | None = None, H: int | None = None,
+                   scalar_gate: bool = False):
     """Return dict(q,k,v,g,beta,S0) for a prefill workload (shapes may be
     overridden to draw a smaller case with the same distributions)."""
     B = cfg.B if B is None else B
     T = cfg.T if T is None else T
     H = cfg.H if H is None else H
     gen = _gen(device, cfg.seed if seed is None else seed)
-    q, k, v, g, beta = _tokens((B, T, H), cfg.dk, cfg.dv, cfg.dtype, cfg.gate_mu, device, gen)
+    q, k, v, g, beta = _tokens((B, T, H), cfg.dk, cfg.dv, cfg.dtype, cfg.gate_mu, device, gen, scalar_gate)
     S0 = None
     if cfg.s0_std is not None:
         S0 = (torch.randn(B, H, cfg.dk, cfg.dv, dtype=torch.float32, device=device,
@@ -103,11 +106,12 @@ def decode_state(cfg: Decode, device="cpu", seed: int | None = None, N: int | No
 
 
 def decode_tokens(cfg: Decode, device="cpu", seed: int | None = None, N: int | None = None,
-                  steps: int | None = None):
+                  steps: int | None = None, scalar_gate: bool = False):
     """Tokens for `steps` decode steps: dict of tensors with a leading step axis
     q,k,g [steps,N,H,dk], v [steps,N,H,dv], beta [steps,N,H]."""
     N = cfg.N if N is None else N
     steps = cfg.steps if steps is None else steps
     gen = _gen(device, cfg.seed if seed is None else seed)
-    q, k, v, g, beta = _tokens((steps, N, cfg.H), cfg.dk, cfg.dv, cfg.dtype, cfg.gate_mu, device, gen)
+    q, k, v, g, beta = _tokens((steps, N, cfg.H), cfg.dk, cfg.dv, cfg.dtype, cfg.gate_mu, device, gen,
+                               scalar_gate)
     return dict(q=q, k=k, v=v, g=g, beta=beta)
