@@ -46,6 +46,7 @@ _SIGS = {
     "kda_chunk_fwd_ex": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
+    "kda_chunk_fwd_varlen": ([_vp] * 9 + [_i] * 7 + [_vp], _i),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -163,6 +164,39 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
         _check(L.kda_chunk_fwd_ex(*args, flags, *tail))
     else:
         _check((L.kda_chunk_fwd_staged if staged else L.kda_chunk_fwd)(*args, *tail))
+    return o, S_T
+
+
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, o=None, S_T=None, stream=None,
+                     want_state=True, scalar_gate=False, delta=True):
+    """Prefill of N packed sequences: q, k, g [T_total, H, d_k] (g [T_total, H]
+    with scalar_gate), v [T_total, H, d_v], beta [T_total, H], cu_seqlens
+    int32 [N + 1] on the device (sequence i = tokens cu[i] .. cu[i+1] - 1),
+    S0 [N, H, d_k, d_v] fp32 or None.  Returns (o [T_total, H, d_v], S_T)."""
+    flags = _flags(scalar_gate, delta)
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise KDAError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _need(q, (Tt, H, dk), dt, "q")
+    _need(k, (Tt, H, dk), dt, "k")
+    _need(g, (Tt, H) if scalar_gate else (Tt, H, dk), dt, "g")
+    _need(v, (Tt, H, dv), dt, "v")
+    if delta or beta is not None:
+        _need(beta, (Tt, H), dt, "beta")
+    if S0 is not None:
+        _need(S0, (N, H, dk, dv), torch.float32, "S0")
+    dev = q.device
+    if o is None:
+        o = torch.zeros((Tt, H, dv), dtype=dt, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                      _ptr(S_T), _ptr(cu_seqlens), N, Tt, H, dk, dv, _dtype(q), flags,
+                                      _stream(stream)))
     return o, S_T
 
 

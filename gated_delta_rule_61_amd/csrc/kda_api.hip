@@ -192,6 +192,26 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, void* o, float* S_T, const int32_t* cu_seqlens, int N, int T_total,
+                         int H, int d_k, int d_v, int dtype, int flags, void* stream) {
+  int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  if ((int64_t)N * H == 0) return KDA_OK;
+  KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
+  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0, KDA_ERR_ALIGN);
+  if (T_total > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype, flags);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, N, T_total, H, d_k, d_v, 1, 0, 1};
+  a.variant = flags;
+  a.cu_seqlens = cu_seqlens;
+  return hip_status(kda::launch_fused(a, (hipStream_t)stream));
+}
+
 size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype)) return 0;
   return staged_layout(B, T, H, d_k, d_v).total;

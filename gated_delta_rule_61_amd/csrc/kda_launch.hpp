@@ -23,6 +23,9 @@ struct PrefillArgs {
   int pass;       // set by the launcher: 1 = segment 0 and the segment maps, 3 = segments 1..nseg-1
   float* ws;      // nseg_workspace_bytes() of fp32 scratch
   int variant;    // kVar* flags (nonzero: bf16, d = 128, pipelined kernel only)
+  // Packed sequences (pipelined kernel, one pass): B sequences, sequence b is
+  // tokens [cu_seqlens[b], cu_seqlens[b+1]) of [T, H, d] tensors; NULL: [B, T, H, d].
+  const int* cu_seqlens;
 };
 
 struct StageArgs {

@@ -2111,7 +2111,25 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     c0 = sg * a.seg_len;
     nchunks = min(a.seg_len, nchunks - c0);
   }
-  const int bb = head / a.H, h = head % a.H;
+  int bb = head / a.H;
+  const int h = head % a.H;
+  if (a.cu_seqlens) {
+    // packed sequences (one pass): sequence bb is tokens [cu[bb], cu[bb+1]) of
+    // the [T, H, d] tensors, clamped to them; from here on it is addressed as a
+    // batch of one sequence
+    const int e0 = min(max(a.cu_seqlens[bb], 0), a.T);
+    const int e1 = min(max(a.cu_seqlens[bb + 1], e0), a.T);
+    const int64_t r0 = (int64_t)e0 * a.H;   // first row of the sequence
+    a.q = reinterpret_cast<const bf16*>(a.q) + r0 * DK;
+    a.k = reinterpret_cast<const bf16*>(a.k) + r0 * DK;
+    a.g = reinterpret_cast<const bf16*>(a.g) + r0 * ((V & kVarScalarGate) ? 1 : DK);
+    a.v = reinterpret_cast<const bf16*>(a.v) + r0 * DV;
+    a.o = reinterpret_cast<bf16*>(a.o) + r0 * DV;
+    if constexpr ((V & kVarNoDelta) == 0) a.beta = reinterpret_cast<const bf16*>(a.beta) + r0;
+    a.T = e1 - e0;
+    bb = 0;
+    nchunks = (a.T + C - 1) / C;
+  }
   Ptr p;
   p.set(smem_raw);
   // blocks (0,1) and (2,3) of P and A' above the diagonal are read by the
@@ -2471,8 +2489,11 @@ size_t prefill_segment_workspace(int BH, int nseg) {
 
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
-  // the variants exist in the pipelined kernel only
-  if (a.variant != 0) return (a.bf16 && a.dk == 128 && a.dv == 128) ? launch_pipe(a, s) : hipErrorInvalidValue;
+  // the variants and packed sequences exist in the pipelined kernel only
+  if (a.variant != 0 || a.cu_seqlens) {
+    if (!(a.bf16 && a.dk == 128 && a.dv == 128) || (a.cu_seqlens && a.nseg >= 3)) return hipErrorInvalidValue;
+    return launch_pipe(a, s);
+  }
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {
       // the pipelined kernel without a column split is the faster one at every

@@ -143,6 +143,34 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
 size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
 
 /*
+ * kda_chunk_fwd_varlen -- prefill of N variable-length sequences packed
+ * along the token axis, each continuing from its own entry state: only the
+ * state is carried between chunks, so streamed input can be taken piece by
+ * piece ("Linear Attention Architecture Deep Dive: From State Updates to
+ * Efficient Chunked Computation" §5 and §7); a decode state, or the S_T of
+ * an earlier call, is such an entry state.
+ *   q,k,g     [T_total,H,d_k]  v, o [T_total,H,d_v]  beta [T_total,H]
+ *             (g [T_total,H] with KDA_GATE_SCALAR; beta may be NULL with
+ *             KDA_NO_DELTA), dtype `dtype`
+ *   cu_seqlens DEVICE int32 [N+1]: sequence i is tokens
+ *             [cu_seqlens[i], cu_seqlens[i+1]); expected 0 = cu_seqlens[0]
+ *             <= ... <= cu_seqlens[N] = T_total.  Not checked on the host;
+ *             the kernel clamps each range into [0, T_total], so bad
+ *             values give wrong results but no out-of-bounds access.
+ *             Tokens outside every range are neither read nor written.
+ *   S0, S_T   [N,H,d_k,d_v] fp32 (NULL / aliasing as in kda_chunk_fwd);
+ *             an empty sequence copies its S0 to S_T.
+ *   flags     kda_variant flags as in kda_chunk_fwd_ex.
+ * Supported: dtype KDA_BF16, d_k = d_v = 128 (else KDA_ERR_ARG).  Each
+ * sequence runs as one chained pass per head (no segmented schedule), so a
+ * single long sequence is better served by kda_chunk_fwd with a workspace.
+ */
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* S0, void* o, float* S_T,
+                         const int32_t* cu_seqlens, int N, int T_total, int H,
+                         int d_k, int d_v, int dtype, int flags, void* stream);
+
+/*
  * kda_recurrent_step_ex -- kda_recurrent_step for the variants above (every
  * dtype and head size kda_recurrent_step supports).  With KDA_GATE_SCALAR
  * g is [N,H]; with KDA_NO_DELTA beta may be NULL.

@@ -126,3 +126,16 @@ def test_variant_validation(L):
     assert L.kda_recurrent_step_ex(p, p, p, p, None, p, p, 4, 2, 128, 128, 1, 1, None) == -1
     assert L.kda_recurrent_step_ex(p, p, p, ctypes.c_void_p(18), p, p, p, 4, 2, 128, 128, 1, 0, None) == -4
     assert L.kda_recurrent_step_ex(p, p, p, p, p, p, p, 0, 2, 128, 128, 1, 3, None) == 0
+
+
+def test_varlen_validation(L):
+    p = ctypes.c_void_p(16)
+    cu = ctypes.c_void_p(64)
+    f = L.kda_chunk_fwd_varlen
+    assert f(p, p, p, p, p, None, p, None, None, 3, 100, 2, 128, 128, 1, 0, None) == -1   # no cu_seqlens
+    assert f(p, p, p, p, p, None, p, None, ctypes.c_void_p(66), 3, 100, 2, 128, 128, 1, 0, None) == -4
+    assert f(p, p, p, p, p, None, p, None, cu, 3, 100, 2, 64, 64, 1, 0, None) == -7        # bf16 d128 only
+    assert f(p, p, p, p, p, None, p, None, cu, 3, 100, 2, 128, 128, 1, 8, None) == -7      # unknown flag
+    assert f(p, p, p, p, None, None, p, None, cu, 3, 100, 2, 128, 128, 1, 0, None) == -1   # beta needed
+    assert f(p, p, p, p, p, None, p, None, cu, -1, 100, 2, 128, 128, 1, 0, None) == -2
+    assert f(p, p, p, p, p, None, p, None, None, 0, 100, 2, 128, 128, 1, 0, None) == 0     # nothing to do
