@@ -12,6 +12,9 @@ before timing starts.  Prints ONE JSON line:
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same work
 --variant runs the same step for a variant of the recurrence (scalar gate,
 no delta rule, or both) on the same shapes; the default is KDA itself.
+--packed runs the prefill on the same 65 536 tokens x 32 heads cut into
+variable-length sequences (geometric lengths, mean 1024, seeded) through
+kda_varlen_schedule + kda_chunk_fwd_varlen.
 """
 from __future__ import annotations
 
@@ -59,6 +62,8 @@ def parse():
                     help="skip the CPU oracle leg (used for profiler runs)")
     ap.add_argument("--variant", choices=sorted(VARIANTS), default="kda",
                     help="recurrence variant (default: KDA)")
+    ap.add_argument("--packed", action="store_true",
+                    help="prefill over variable-length packed sequences of the same tokens")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -152,6 +157,27 @@ def main():
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T,
                       workspace=ws, **vkw)
 
+    n_states = pcfg.B * pcfg.H
+    if args.packed:
+        lengths = W.packed_lengths(pcfg.B * pcfg.T, 1024.0, seed=11)
+        cu_host = [0]
+        for n in lengths:
+            cu_host.append(cu_host[-1] + n)
+        cu = torch.tensor(cu_host, dtype=torch.int32, device="cuda")
+        flat = lambda t: None if t is None else t.reshape(pcfg.B * pcfg.T, pcfg.H, *t.shape[3:])
+        pk = {n: flat(inp[n]) for n in ("q", "k", "v", "g", "beta")}
+        o_flat = o.view(pcfg.B * pcfg.T, pcfg.H, D)
+        S_T = torch.empty(len(lengths), pcfg.H, D, D, dtype=torch.float32, device="cuda")
+        n_states = len(lengths) * pcfg.H
+
+        order = torch.empty(len(lengths), dtype=torch.int32, device="cuda")
+
+        def prefill():
+            # the longest-first order is recomputed every step (it is timed)
+            kda.varlen_schedule(cu, pcfg.B * pcfg.T, out=order)
+            kda.chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu, None, seq_order=order,
+                                 o=o_flat, S_T=S_T, **vkw)
+
     def decode():
         for t in range(dcfg.steps):
             kda.recurrent_step(*steps_tok[t], S, o=od, **vkw)
@@ -181,14 +207,14 @@ def main():
     dec_avg = sum(dec_ms) / len(dec_ms)
 
     BTH = pcfg.B * pcfg.T * pcfg.H
-    pre_bytes = BTH * tok_bytes(scalar_gate, delta) + pcfg.B * pcfg.H * STATE_BYTES   # + S_T write
+    pre_bytes = BTH * tok_bytes(scalar_gate, delta) + n_states * STATE_BYTES   # + S_T write
     pre_flops = BTH * PREFILL_FLOPS_PER_TOKHEAD
     pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
     digest = source_digest()
     step_heads = dcfg.N * dcfg.H
     dec_step_ms = dec_avg / dcfg.steps
     dec_gbs = step_heads * (2 * STATE_BYTES + tok_bytes(scalar_gate, delta)) / (dec_step_ms * 1e-3) / 1e9
-    pk = "fused_pipe_kernel" if flags == 0 else f"fused_pipe_kernel<{flags}>"
+    pkn = "fused_pipe_kernel" if flags == 0 else f"fused_pipe_kernel<{flags}>"
     dk_name = "decode_kernel" if flags == 0 else f"decode_kernel<{flags}>"
     vname = {"kda": "", "scalar": " [scalar gate]", "nodelta": " [no delta rule]",
              "scalar-nodelta": " [scalar gate, no delta rule]"}[args.variant]
@@ -211,12 +237,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
                 "g=-softplus(N(-3,1)))",
-        "config": {"workload": "kda_chunk_fwd B8 H32 T8192 d128 bf16 (S0=0) + "
-                               "kda_recurrent_step 256x32 d128 x64 tokens" + vname,
+        "config": {"workload": ((f"kda_chunk_fwd_varlen {n_states // pcfg.H} packed sequences "
+                                 f"(geometric lengths, mean 1024) = 65536 tokens H32 d128 bf16 (S0=0) + ")
+                                if args.packed else "kda_chunk_fwd B8 H32 T8192 d128 bf16 (S0=0) + ")
+                               + "kda_recurrent_step 256x32 d128 x64 tokens" + vname,
                    "prefill_ms": pre_avg, "decode_ms_per_token_step": dec_step_ms},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic(pk),
-                     "kernel": pk + " (bf16, d_k = d_v = 128)",
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": None if args.packed else traffic(pkn),
+                     "kernel": pkn + " (bf16, d_k = d_v = 128)",
                      "mfma_frac_algorithmic": (pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
                                                if flags == 0 else None)},
         "decode": {"value": dcfg.N * dcfg.steps / (dec_avg * 1e-3), "unit": "tokens/s",

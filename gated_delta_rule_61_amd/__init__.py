@@ -46,7 +46,8 @@ _SIGS = {
     "kda_chunk_fwd_ex": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
-    "kda_chunk_fwd_varlen": ([_vp] * 9 + [_i] * 7 + [_vp], _i),
+    "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
+    "kda_varlen_schedule": ([_vp, _i, _i, _vp, _vp], _i),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -167,12 +168,24 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
     return o, S_T
 
 
-def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, o=None, S_T=None, stream=None,
+def varlen_schedule(cu_seqlens, T_total, *, out=None, stream=None):
+    """Longest-first processing order of the packed sequences (int32 [N] on
+    the device), for chunk_fwd_varlen(seq_order=...)."""
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    if out is None:
+        out = torch.empty(max(N, 0), dtype=torch.int32, device=cu_seqlens.device)
+    _check(lib().kda_varlen_schedule(_ptr(cu_seqlens), N, int(T_total), _ptr(out), _stream(stream)))
+    return out
+
+
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o=None, S_T=None, stream=None,
                      want_state=True, scalar_gate=False, delta=True):
     """Prefill of N packed sequences: q, k, g [T_total, H, d_k] (g [T_total, H]
     with scalar_gate), v [T_total, H, d_v], beta [T_total, H], cu_seqlens
     int32 [N + 1] on the device (sequence i = tokens cu[i] .. cu[i+1] - 1),
-    S0 [N, H, d_k, d_v] fp32 or None.  Returns (o [T_total, H, d_v], S_T)."""
+    S0 [N, H, d_k, d_v] fp32 or None; seq_order: int32 [N] start order (see
+    varlen_schedule) or None.  Returns (o [T_total, H, d_v], S_T)."""
     flags = _flags(scalar_gate, delta)
     Tt, H, dk = q.shape
     dv = v.shape[-1]
@@ -189,14 +202,16 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, o=None, S_T=None,
         _need(beta, (Tt, H), dt, "beta")
     if S0 is not None:
         _need(S0, (N, H, dk, dv), torch.float32, "S0")
+    if seq_order is not None:
+        _need(seq_order, (N,), torch.int32, "seq_order")
     dev = q.device
     if o is None:
         o = torch.zeros((Tt, H, dv), dtype=dt, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
-                                      _ptr(S_T), _ptr(cu_seqlens), N, Tt, H, dk, dv, _dtype(q), flags,
-                                      _stream(stream)))
+                                      _ptr(S_T), _ptr(cu_seqlens), _ptr(seq_order), N, Tt, H, dk, dv,
+                                      _dtype(q), flags, _stream(stream)))
     return o, S_T
 
 

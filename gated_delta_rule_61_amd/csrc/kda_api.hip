@@ -192,15 +192,27 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 
+int kda_varlen_schedule(const int32_t* cu_seqlens, int N, int T_total, int32_t* seq_order, void* stream) {
+  KDA_REQUIRE(N >= 0 && T_total >= 0, KDA_ERR_SHAPE);
+  KDA_REQUIRE(N <= kda::kMaxScheduleSeqs, KDA_ERR_SHAPE);
+  if (N == 0) return KDA_OK;
+  KDA_REQUIRE(cu_seqlens && seq_order, KDA_ERR_NULL);
+  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0 && (reinterpret_cast<uintptr_t>(seq_order) & 3u) == 0,
+              KDA_ERR_ALIGN);
+  return hip_status(kda::launch_varlen_schedule(cu_seqlens, N, T_total, seq_order, (hipStream_t)stream));
+}
+
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                         const float* S0, void* o, float* S_T, const int32_t* cu_seqlens, int N, int T_total,
-                         int H, int d_k, int d_v, int dtype, int flags, void* stream) {
+                         const float* S0, void* o, float* S_T, const int32_t* cu_seqlens,
+                         const int32_t* seq_order, int N, int T_total, int H, int d_k, int d_v, int dtype,
+                         int flags, void* stream) {
   int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
   if (st) return st;
   KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
   if ((int64_t)N * H == 0) return KDA_OK;
   KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
-  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0, KDA_ERR_ALIGN);
+  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0 && (reinterpret_cast<uintptr_t>(seq_order) & 3u) == 0,
+              KDA_ERR_ALIGN);
   if (T_total > 0) {
     st = check_tokens(q, k, v, g, beta, o, dtype, flags);
     if (st) return st;
@@ -209,6 +221,7 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, N, T_total, H, d_k, d_v, 1, 0, 1};
   a.variant = flags;
   a.cu_seqlens = cu_seqlens;
+  a.seq_order = seq_order;
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 

@@ -26,6 +26,7 @@ struct PrefillArgs {
   // Packed sequences (pipelined kernel, one pass): B sequences, sequence b is
   // tokens [cu_seqlens[b], cu_seqlens[b+1]) of [T, H, d] tensors; NULL: [B, T, H, d].
   const int* cu_seqlens;
+  const int* seq_order;   // packed sequences: processing order (a permutation of 0..B-1), or NULL
 };
 
 struct StageArgs {
@@ -43,6 +44,10 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Order of packed sequences by decreasing chunk count (ties by index) into
+// order[0..N-1]; N <= kMaxScheduleSeqs.
+constexpr int kMaxScheduleSeqs = 16384;
+hipError_t launch_varlen_schedule(const int* cu_seqlens, int N, int T, int* order, hipStream_t s);
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_stage_cumsum(const StageArgs& a, hipStream_t s);
 hipError_t launch_stage_ut(const StageArgs& a, hipStream_t s);

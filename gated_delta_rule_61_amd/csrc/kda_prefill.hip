@@ -2080,6 +2080,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     int split;
     block_to_head<1>(blockIdx.x, head, split);
     if (head >= a.B * a.H) return;
+    if (a.cu_seqlens && a.seq_order) {
+      // packed sequences in the given order (longest first balances the
+      // tail); entries clamped into range
+      const int sq = min(max(a.seq_order[head / a.H], 0), a.B - 1);
+      head = sq * a.H + head % a.H;
+    }
     if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
     if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
   } else {
@@ -2485,6 +2491,60 @@ int prefill_segment_len(int T, int nseg) {
 
 size_t prefill_segment_workspace(int BH, int nseg) {
   return nseg >= 3 ? (size_t)BH * nseg * 3 * 128 * 128 * sizeof(float) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Processing order of packed sequences: indices sorted by decreasing chunk
+// count (ties by index), so the longest sequences start first and the short
+// ones fill in behind them.  One workgroup; a bitonic sort of 64-bit keys
+// (inverted chunk count, index) in LDS.  Lengths are clamped exactly as the
+// prefill kernel clamps them.
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int* cu, int N, int T, int P,
+                                                                        int* order) {
+  extern __shared__ unsigned long long keys[];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < P; i += kSchedThreads) {
+    unsigned long long key = ~0ull;
+    if (i < N) {
+      const int e0 = min(max(cu[i], 0), T);
+      const int e1 = min(max(cu[i + 1], e0), T);
+      const unsigned nch = (unsigned)((e1 - e0 + C - 1) / C);
+      key = ((unsigned long long)(0xFFFFFFFFu - nch) << 32) | (unsigned)i;
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kSchedThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = keys[i], y = keys[ixj];
+          if ((x > y) == ((i & k) == 0)) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < N; i += kSchedThreads) order[i] = (int)(keys[i] & 0xFFFFFFFFu);
+}
+
+hipError_t launch_varlen_schedule(const int* cu_seqlens, int N, int T, int* order, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (N > kMaxScheduleSeqs) return hipErrorInvalidValue;
+  int P = 1;
+  while (P < N) P <<= 1;
+  const int bytes = P * 8;
+  hipError_t e = set_smem(varlen_schedule_kernel, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), bytes, s, cu_seqlens, N, T, P, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused(const PrefillArgs& a, hipStream_t s) {

@@ -158,6 +158,12 @@ size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, in
  *             the kernel clamps each range into [0, T_total], so bad
  *             values give wrong results but no out-of-bounds access.
  *             Tokens outside every range are neither read nor written.
+ *   seq_order DEVICE int32 [N] or NULL: the order in which sequences are
+ *             started, a permutation of 0..N-1 (entries are clamped into
+ *             range; a repeated entry runs that sequence twice and leaves
+ *             another one unwritten).  Longest first balances the work
+ *             across compute units; kda_varlen_schedule writes that order.
+ *             NULL: index order.
  *   S0, S_T   [N,H,d_k,d_v] fp32 (NULL / aliasing as in kda_chunk_fwd);
  *             an empty sequence copies its S0 to S_T.
  *   flags     kda_variant flags as in kda_chunk_fwd_ex.
@@ -167,8 +173,20 @@ size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, in
  */
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* S0, void* o, float* S_T,
-                         const int32_t* cu_seqlens, int N, int T_total, int H,
-                         int d_k, int d_v, int dtype, int flags, void* stream);
+                         const int32_t* cu_seqlens, const int32_t* seq_order,
+                         int N, int T_total, int H, int d_k, int d_v, int dtype,
+                         int flags, void* stream);
+
+/*
+ * kda_varlen_schedule -- seq_order for kda_chunk_fwd_varlen: the sequences
+ * of cu_seqlens (device int32 [N+1], clamped as kda_chunk_fwd_varlen clamps
+ * them) sorted by decreasing number of 64-token chunks, ties by index,
+ * written to seq_order (device int32 [N]).  One small kernel on `stream`;
+ * the order depends only on cu_seqlens, so one call serves every layer of a
+ * batch.  N <= 16384 (else KDA_ERR_SHAPE; pass seq_order = NULL instead).
+ */
+int kda_varlen_schedule(const int32_t* cu_seqlens, int N, int T_total, int32_t* seq_order,
+                        void* stream);
 
 /*
  * kda_recurrent_step_ex -- kda_recurrent_step for the variants above (every

@@ -131,11 +131,20 @@ def test_variant_validation(L):
 def test_varlen_validation(L):
     p = ctypes.c_void_p(16)
     cu = ctypes.c_void_p(64)
-    f = L.kda_chunk_fwd_varlen
+    f = lambda *a: L.kda_chunk_fwd_varlen(*a[:9], None, *a[9:])
     assert f(p, p, p, p, p, None, p, None, None, 3, 100, 2, 128, 128, 1, 0, None) == -1   # no cu_seqlens
     assert f(p, p, p, p, p, None, p, None, ctypes.c_void_p(66), 3, 100, 2, 128, 128, 1, 0, None) == -4
+    assert L.kda_chunk_fwd_varlen(p, p, p, p, p, None, p, None, cu, ctypes.c_void_p(66), 3, 100, 2, 128, 128,
+                                  1, 0, None) == -4                                       # misaligned order
     assert f(p, p, p, p, p, None, p, None, cu, 3, 100, 2, 64, 64, 1, 0, None) == -7        # bf16 d128 only
     assert f(p, p, p, p, p, None, p, None, cu, 3, 100, 2, 128, 128, 1, 8, None) == -7      # unknown flag
     assert f(p, p, p, p, None, None, p, None, cu, 3, 100, 2, 128, 128, 1, 0, None) == -1   # beta needed
     assert f(p, p, p, p, p, None, p, None, cu, -1, 100, 2, 128, 128, 1, 0, None) == -2
     assert f(p, p, p, p, p, None, p, None, None, 0, 100, 2, 128, 128, 1, 0, None) == 0     # nothing to do
+    s = L.kda_varlen_schedule
+    assert s(cu, 0, 100, None, None) == 0
+    assert s(None, 3, 100, p, None) == -1
+    assert s(cu, 3, 100, None, None) == -1
+    assert s(cu, 3, 100, ctypes.c_void_p(18), None) == -4
+    assert s(cu, 16385, 100, p, None) == -2
+    assert s(cu, -1, 100, p, None) == -2

@@ -176,3 +176,42 @@ def test_out_of_range_offsets_are_clamped(kda):
     assert torch.equal(S[1], S0[1])
     o_ref, S_ref = ref(30, 100, 2)
     check_prefill(to64(o[50:])[None], to64(S[2])[None], o_ref[:, 20:], S_ref, torch.bfloat16, "decreasing seq 2")
+
+
+def _expected_order(cu, T):
+    cu = np.asarray(cu, dtype=np.int64)
+    N = len(cu) - 1
+    e0 = np.clip(cu[:-1], 0, T)
+    e1 = np.minimum(np.maximum(cu[1:], e0), T)
+    nch = (e1 - e0 + 63) // 64
+    return sorted(range(N), key=lambda i: (-nch[i], i))
+
+
+@pytest.mark.parametrize("N", [1, 8, 96, 1000, 16384])
+def test_schedule_is_longest_first(kda, N):
+    """kda_varlen_schedule sorts by decreasing chunk count, ties by index
+    (also for clamped offsets), up to its 16384-sequence limit."""
+    rng = np.random.default_rng(N)
+    lengths = rng.integers(0, 400 if N <= 1000 else 40, size=N)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    if N == 96:
+        cu[10] = -5
+        cu[40] = T + 1000
+    order = kda.varlen_schedule(torch.tensor(cu, device="cuda"), T)
+    torch.cuda.synchronize()
+    assert order.cpu().tolist() == _expected_order(cu, T)
+
+
+def test_order_does_not_change_results(kda):
+    """Longest-first order and index order give bit-identical results."""
+    x, cu = _packed(MIX, 3, 55)
+    o1, S1 = _run(kda, x)
+    order = kda.varlen_schedule(x["cu"], int(cu[-1]))
+    assert order.cpu().tolist() == _expected_order(cu, int(cu[-1]))
+    o2, S2 = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], x["S0"], seq_order=order)
+    rev = torch.arange(len(MIX) - 1, -1, -1, dtype=torch.int32, device="cuda")
+    o3, S3 = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], x["S0"], seq_order=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, S3)

@@ -17,6 +17,7 @@ variant without the delta rule draws beta as usual and does not use it.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import torch
@@ -115,3 +116,22 @@ def decode_tokens(cfg: Decode, device="cpu", seed: int | None = None, N: int | N
     q, k, v, g, beta = _tokens((steps, N, cfg.H), cfg.dk, cfg.dv, cfg.dtype, cfg.gate_mu, device, gen,
                                scalar_gate)
     return dict(q=q, k=k, v=v, g=g, beta=beta)
+
+
+def packed_lengths(total: int, mean: float, seed: int, max_len: int | None = None):
+    """Sequence lengths for a packed batch: geometric with the given mean
+    (a serving mix of many short and a few long requests), capped at max_len,
+    drawn until they cover `total` tokens (the last one cut to fit)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    p = 1.0 / mean
+    out, acc = [], 0
+    while acc < total:
+        u = float(torch.rand((), generator=gen))
+        n = 1 + int(math.floor(math.log1p(-u) / math.log1p(-p))) if p < 1 else 1
+        if max_len is not None:
+            n = min(n, max_len)
+        n = min(n, total - acc)
+        out.append(n)
+        acc += n
+    return out
