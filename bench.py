@@ -69,16 +69,24 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# Sources each measured kernel is compiled from (its counter record is valid
+# only while they are unchanged).
+KERNEL_SOURCES = {
+    "prefill": ["kda_prefill.hip", "kda_device.hpp", "kda_launch.hpp"],
+    "decode": ["kda_decode.hip", "kda_device.hpp", "kda_launch.hpp"],
+}
+
+
+def source_digest(family: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_61_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, digest: str):
+def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -87,7 +95,8 @@ def measured_traffic(kernel: str, digest: str):
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != digest:
+    family = "decode" if kernel.startswith("decode") else "prefill"
+    if not rec or rec.get("source_digest") != source_digest(family):
         return None
     return rec.get("bytes_per_launch")
 
@@ -210,7 +219,6 @@ def main():
     pre_bytes = BTH * tok_bytes(scalar_gate, delta) + n_states * STATE_BYTES   # + S_T write
     pre_flops = BTH * PREFILL_FLOPS_PER_TOKHEAD
     pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
-    digest = source_digest()
     step_heads = dcfg.N * dcfg.H
     dec_step_ms = dec_avg / dcfg.steps
     dec_gbs = step_heads * (2 * STATE_BYTES + tok_bytes(scalar_gate, delta)) / (dec_step_ms * 1e-3) / 1e9
@@ -220,7 +228,7 @@ def main():
              "scalar-nodelta": " [scalar gate, no delta rule]"}[args.variant]
 
     def traffic(kernel):
-        t = measured_traffic(kernel, digest)
+        t = measured_traffic(kernel)
         return None if t is None else float(t)
 
     line = {
@@ -243,7 +251,7 @@ def main():
                                + "kda_recurrent_step 256x32 d128 x64 tokens" + vname,
                    "prefill_ms": pre_avg, "decode_ms_per_token_step": dec_step_ms},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": None if args.packed else traffic(pkn),
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": traffic(pkn + ("[packed]" if args.packed else "")),
                      "kernel": pkn + " (bf16, d_k = d_v = 128)",
                      "mfma_frac_algorithmic": (pre_flops / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
                                                if flags == 0 else None)},
