@@ -13,12 +13,18 @@ Two independent fp64 implementations live here:
   Inference More Efficient" §3.3 (KDA equation) with the read-after-write
   output of "Demystifying Hybrid LLM Architectures: Linear Attention,
   Residuals, and Latent MoE" §2.3.
+* ``recurrent_bwd`` -- the derivative of that definition by reverse-mode
+  differentiation of its token loop (C, fp64), with the per-chunk state
+  adjoints on request.  The pages give no backward formulas: the gradient is
+  fixed by the forward definition alone.
 * ``oracle.chunked`` -- the chunkwise-parallel form of the same pages' §IV /
   §2.4, in NumPy fp64, which exposes the per-chunk intermediates (cumulative
   log-gates, W, U, the residual U - W S, the chunk-entry states).
 
-Pins (tests that tie both to something other than themselves) are in
-``tests/test_oracle_pins.py`` and ``tests/test_chunked_model.py``.
+Pins (tests that tie them to something other than themselves) are in
+``tests/test_oracle_pins.py``, ``tests/test_chunked_model.py`` and
+``tests/test_oracle_bwd_pins.py`` (finite differences, torch.autograd of an
+independent recurrence, adjoint composition).
 """
 from __future__ import annotations
 
@@ -67,6 +73,8 @@ def _load():
             lib.kda_oracle_step_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                                i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
             lib.kda_oracle_step_ex.restype = ctypes.c_int
+            lib.kda_oracle_bwd_ex.argtypes = [dp] * 15 + [i64] * 6 + [ctypes.c_int, ctypes.c_int]
+            lib.kda_oracle_bwd_ex.restype = ctypes.c_int
             lib.kda_oracle_max_threads.argtypes = []
             lib.kda_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -143,3 +151,36 @@ def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0, scalar_gate: bool = F
     if rc != 0:
         raise RuntimeError(f"kda_oracle_step failed ({rc})")
     return o, Sn
+
+
+def recurrent_bwd(q, k, v, g, beta, S0, dO, dST=None, nthreads: int = 0, scalar_gate: bool = False,
+                  delta: bool = True, chunk: int = 64, chunk_adjoints: bool = False):
+    """Reverse-mode derivative of ``recurrent_fwd`` (fp64, token by token).
+
+    dO [B,T,H,dv] is the adjoint of o, dST [B,H,dk,dv] that of S_T (None:
+    zero).  Returns a dict with dq, dk, dv [B,T,H,*], dg (same shape as g),
+    dbeta [B,T,H] (zeros without the delta rule), dS0 [B,H,dk,dv] and, with
+    chunk_adjoints, dS_chunks [B,H,ceil(T/chunk),dk,dv] (adjoint of the state
+    at the start of each chunk of ``chunk`` tokens)."""
+    q, k, v, g, dO = (_f64(a) for a in (q, k, v, g, dO))
+    beta = None if beta is None else _f64(beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, T, H, dk) and g.shape == ((B, T, H) if scalar_gate else (B, T, H, dk))
+    assert v.shape == (B, T, H, dv) and dO.shape == (B, T, H, dv)
+    assert (beta is None and not delta) or beta.shape == (B, T, H)
+    S0a = None if S0 is None else _f64(S0)
+    dSTa = None if dST is None else _f64(dST)
+    out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)), dv=np.zeros((B, T, H, dv)),
+               dg=np.zeros(g.shape), dbeta=np.zeros((B, T, H)), dS0=np.zeros((B, H, dk, dv)))
+    nblk = (T + chunk - 1) // chunk
+    dSc = np.zeros((B, H, nblk, dk, dv)) if chunk_adjoints else None
+    rc = _load().kda_oracle_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0a), _ptr(dO),
+                                   _ptr(dSTa), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                   _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(dSc),
+                                   B, T, H, dk, dv, chunk, _flags(scalar_gate, delta), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd failed ({rc})")
+    if chunk_adjoints:
+        out["dS_chunks"] = dSc
+    return out

@@ -141,6 +141,59 @@ def _pins_fail(lib):
     return fails
 
 
+# Slips in the backward (reverse-mode) code, each caught by the
+# finite-difference pin below.
+BWD_MUTANTS = [
+    ("bwd_dr_sign", "dr[j] = -bt * ddelta[j];", "dr[j] = bt * ddelta[j];"),
+    ("bwd_no_retrieve_adjoint", "dS[c * dv + j] += kt[c] * dr[j];", "(void)0;"),
+    ("bwd_decay_not_propagated", "dS[c * dv + j] *= a;", "dS[c * dv + j] *= 1.0;"),
+    ("bwd_dq_from_decayed_state", "acc += S[c * dv + j] * dot[j];", "acc += Sd[c * dv + j] * dot[j];"),
+    ("bwd_dg_against_new_state", "acc += dS[c * dv + j] * Sd[c * dv + j];", "acc += dS[c * dv + j] * S[c * dv + j];"),
+    ("bwd_dbeta_drops_retrieval", "db += ddelta[j] * (vt[j] - r[j]);", "db += ddelta[j] * vt[j];"),
+]
+
+
+def _bwd_pin_fails(lib):
+    """Finite differences of the (same build's) forward against its backward."""
+    rng = np.random.default_rng(3)
+    B, T, H, dk, dv = 1, 7, 1, 4, 3
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.kda_oracle_bwd_ex.argtypes = [dp] * 15 + [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int]
+    x = dict(q=rng.standard_normal((B, T, H, dk)), k=rng.standard_normal((B, T, H, dk)) * 0.5,
+             v=rng.standard_normal((B, T, H, dv)), g=-np.abs(rng.standard_normal((B, T, H, dk))) * 0.4,
+             beta=rng.uniform(0.1, 1, (B, T, H)), S0=rng.standard_normal((B, H, dk, dv)))
+    dO = rng.standard_normal((B, T, H, dv))
+    p = lambda a: None if a is None else a.ctypes.data_as(dp)
+    out = {n: np.zeros_like(x[n]) for n in x}
+    rc = lib.kda_oracle_bwd_ex(*(p(x[n]) for n in ("q", "k", "v", "g", "beta", "S0")), p(dO), None,
+                               p(out["q"]), p(out["k"]), p(out["v"]), p(out["g"]), p(out["beta"]), p(out["S0"]),
+                               None, B, T, H, dk, dv, 3, 0, 1)
+    assert rc == 0
+    f = lambda xx: float((_fwd(lib, *(xx[n] for n in ("q", "k", "v", "g", "beta", "S0")))[0] * dO).sum())
+    for n in x:
+        u = rng.standard_normal(x[n].shape)
+        xp = dict(x); xp[n] = x[n] + 1e-6 * u
+        xm = dict(x); xm[n] = x[n] - 1e-6 * u
+        fd = (f(xp) - f(xm)) / 2e-6
+        if abs(fd - float((out[n] * u).sum())) > 1e-6 * max(1.0, abs(fd)):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_planted_backward_mistake_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    lib = _build(tmp_path, src.replace(old, new), name)
+    assert _pins_fail(lib) == []          # the forward is untouched
+    assert _bwd_pin_fails(lib), f"backward mutant {name} passed the finite-difference pin"
+
+
+def test_unmodified_backward_passes(tmp_path):
+    lib = _build(tmp_path, open(SRC).read(), "ok_bwd")
+    assert not _bwd_pin_fails(lib)
+
+
 def test_unmodified_source_passes(tmp_path):
     lib = _build(tmp_path, open(SRC).read(), "ok")
     assert _pins_fail(lib) == []
