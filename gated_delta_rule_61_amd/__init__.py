@@ -48,6 +48,8 @@ _SIGS = {
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
     "kda_varlen_schedule": ([_vp, _i, _i, _vp, _vp], _i),
+    "kda_chunk_bwd": ([_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp], _i),
+    "kda_chunk_bwd_workspace_size": ([_i] * 6, _sz),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -213,6 +215,32 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
                                       _ptr(S_T), _ptr(cu_seqlens), _ptr(seq_order), N, Tt, H, dk, dv,
                                       _dtype(q), flags, _stream(stream)))
     return o, S_T
+
+
+def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None):
+    """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
+    adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16,
+    d_k = d_v = 128."""
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta)
+    _need(dO, (B, T, H, dv), dt, "dO")
+    if S0 is not None:
+        _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    if dS_T is not None:
+        _need(dS_T, (B, H, dk, dv), torch.float32, "dS_T")
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+               dbeta=torch.empty_like(beta),
+               dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
+    L = lib()
+    code = _dtype(q)
+    wsz = L.kda_chunk_bwd_workspace_size(B, T, H, dk, dv, code)
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                           _ptr(out["dS0"]), B, T, H, dk, dv, code, _ptr(workspace) if wsz else None, wsz,
+                           _stream(stream)))
+    return out
 
 
 def recurrent_step(q, k, v, g, beta, S, *, o=None, stream=None, scalar_gate=False, delta=True):

@@ -225,6 +225,36 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
+  if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
+  return kda::backward_workspace(B * H, T);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta, const float* S0,
+                  const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+                  float* dS0, int B, int T, int H, int d_k, int d_v, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE(variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, dO, dtype);
+    if (st) return st;
+    KDA_REQUIRE(dq && dk && dv && dg && dbeta, KDA_ERR_NULL);
+    KDA_REQUIRE(aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
+                (reinterpret_cast<uintptr_t>(dbeta) & 1u) == 0, KDA_ERR_ALIGN);
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(dS_T) && aligned16(dS0), KDA_ERR_ALIGN);
+  const size_t need = kda::backward_workspace(B * H, T);
+  KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+  kda::BackwardArgs a{q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H,
+                      static_cast<float*>(workspace),
+                      static_cast<float*>(workspace) + need / (2 * sizeof(float))};
+  return hip_status(kda::launch_backward(a, (hipStream_t)stream));
+}
+
 size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype)) return 0;
   return staged_layout(B, T, H, d_k, d_v).total;

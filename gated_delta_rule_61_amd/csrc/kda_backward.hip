@@ -1,0 +1,853 @@
+// kda_backward.hip -- backward of the chunked KDA forward (bf16, d_k = d_v = 128).
+//
+// The gradient of the forward with respect to q, k, v, g, beta and S0, given
+// the adjoints of o and S_T.  The pages give the forward only ("Hybrid Linear
+// Attention Architecture: Making LLM Training and Inference More Efficient"
+// §3.3 for the rule, §IV for the chunked form and its training purpose); the
+// backward here is the reverse-mode derivative of that chunked form, chunk by
+// chunk.  Per chunk, with the forward's notation (b the in-chunk cumulative
+// log-gate, Kg = e^b k, Kd = e^-b k, Qg = e^b q, gamma = e^{b_C}, L =
+// StrictTril(Diag(beta) Kg Kd^T), A = (I + L)^-1, A' = A Diag(beta), entry
+// state S, chunk-end adjoint dS):
+//
+//   Delta  = A' (V - Kg S)                        (= U - W S)
+//   dDelta = P^T dO + Kd (gamma . dS)             (P = Tril(Qg Kd^T), exact diagonal q.k)
+//   dS_prev = gamma . dS + Qg^T dO - Kg^T (A'^T dDelta)
+//   M = Tril(dO Delta^T)        dQg = dO S^T + M Kd      dKd = M^T Qg + dG^T Kg
+//   dKb~ = Delta (gamma . dS)^T (= gamma . dKb)      dW = -dDelta S^T
+//   dV = A'^T dDelta            dKg = Diag(beta) (A^T dW + dL Kd)
+//   dA = (dDelta V^T + dW Kg^T) Diag(beta)     dL = -StrictTril(A^T dA A^T)   dG = Diag(beta) dL
+//   dbeta = rowsum((A^T dDelta) . V) + rowsum((A^T dW) . Kg) + rowsum(Kg . (dL Kd))
+//   db = Kg.dKg - Kd.(dKd + dKb~) + Qg.dQg, plus at the chunk end
+//        sum_t Kd.dKb~ + gamma . rowsum(dS . S);   dg = reverse in-chunk cumsum of db
+//   dq = e^b dQg + M_tt k_t,   dk = e^b dKg + e^-b (dKd + dKb~) + M_tt q_t
+// (M's diagonal and P's diagonal carry no gate factors and are kept exact).
+//
+// Three launches:
+//   1. the pipelined forward kernel in state mode: chunk-entry states S_[n];
+//   2. bwd_chain_kernel: per (sequence, head, half of the value columns) the
+//      adjoint recursion over the chunks in reverse, storing each chunk-end
+//      adjoint (the value columns are independent in it);
+//   3. bwd_grad_kernel: per (chunk, sequence, head), all gradients of the
+//      chunk from its entry state and chunk-end adjoint.
+// Matrix products: v_mfma_f32_16x16x16_bf16 on bf16 operands in LDS (fp32
+// accumulation); the unit-triangular inverse in fp32.
+#include <stdint.h>
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace bwd {
+
+constexpr int C = 64, D = 128, NT = 512;
+constexpr int P128 = 136;   // bf16 rows of 128 (8-byte fragment reads conflict-free)
+constexpr int P64 = 72;     // bf16 rows of 64
+constexpr int PF = 68;      // fp32 rows of 64
+constexpr int PB = 132;     // fp32 rows of 128
+typedef Mma<bf16> MB;
+typedef Mma<float> MF;
+
+// ---------------------------------------------------------------- fragments
+// Operand fragment of a 16-index slab (lane group g: indices k..k+3 with
+// k = slab + 4g; lane i: row `row`), read either from a row-major array whose
+// rows are the fragment rows (indices contiguous) or gathered from one whose
+// rows are the indices.
+__device__ __forceinline__ bf16x4 fr_row(const bf16* p, int ld, int row, int k) {
+  return *reinterpret_cast<const bf16x4*>(p + row * ld + k);
+}
+__device__ __forceinline__ bf16x4 fr_col(const bf16* p, int ld, int row, int k) {
+  bf16x4 v;
+  v[0] = p[k * ld + row];
+  v[1] = p[(k + 1) * ld + row];
+  v[2] = p[(k + 2) * ld + row];
+  v[3] = p[(k + 3) * ld + row];
+  return v;
+}
+
+// Out tile (m0.., n0..) += sum_{k < K} X[m][k] Z[n][k]; XR / ZR: X / Z stored
+// with k contiguous (else stored transposed, k = row).  C layout result:
+// lane (g, i) holds Out[m0 + 4g + r][n0 + i].
+template <bool XR, bool ZR>
+__device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int ldz, int m0, int n0, int K,
+                                      floatx4 acc, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  for (int k = 0; k < K; k += 16) {
+    const bf16x4 a = XR ? fr_row(X, ldx, m0 + i, k + 4 * g) : fr_col(X, ldx, m0 + i, k + 4 * g);
+    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_col(Z, ldz, n0 + i, k + 4 * g);
+    acc = MB::mma16(a, b, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// C-layout tile -> row-major dst[m][n] (2-byte stores)
+__device__ __forceinline__ void st_rm(bf16* dst, int ld, int m0, int n0, floatx4 v, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(m0 + 4 * g + r) * ld + n0 + i] = (bf16)v[r];
+}
+// C-layout tile -> transposed row-major dst[n][m] (8-byte stores)
+__device__ __forceinline__ void st_tr(bf16* dst, int ld, int m0, int n0, floatx4 v, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  bf16x4 x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (bf16)v[r];
+  *reinterpret_cast<bf16x4*>(dst + (n0 + i) * ld + m0 + 4 * g) = x;
+}
+
+// Sum over the 16 lanes of the caller's 16-lane row (lanes i = 0..15, same g).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// ---------------------------------------------------------------- chunk basics
+struct Chunk {
+  int64_t row0;   // token index (b*T + t0)*H + h of the chunk's first token
+  int nv;         // valid rows
+  int rstride;    // elements between rows of a [.., H, 128] tensor (= H*128)
+};
+
+// Shared LDS of the chunk basics (offsets in bytes from the kernel's base).
+struct Basics {
+  bf16 *Kg, *Kd, *Qg;   // [64][P128]
+  bf16 *A;              // [64][P64] (I + L)^-1, unscaled; upper part zero
+  bf16 *PT;             // [64][P64] P^T (P = Tril(Qg Kd^T), diagonal q.k)
+  float *beta, *gam, *qk;   // [64], [128], [64]
+};
+
+// In-chunk cumulative log-gates b (fp32 [64][PB] in `bs`), the gated operands
+// Kg Kd Qg, gamma, beta and q.k.  Rows past nv are zero (g = 0 there, so b is
+// constant and the chunk end gate is that of the last valid row).
+__device__ void chunk_gates(const Basics& L, float* bs, const bf16* q, const bf16* k, const bf16* g,
+                            const bf16* beta, const Chunk& ch, int H, int tid) {
+  // g -> bs (fp32); thread: row t = e / 16, channels 8 (e % 16) .. + 8
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, c0 = 8 * (e & 15);
+    Vec16 x = {{0u, 0u, 0u, 0u}};
+    if (t < ch.nv) x = ldg16(g + (ch.row0 + (int64_t)t * H) * D + c0);
+    float f[8];
+    vec_to_f32<bf16>(x, f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bs[t * PB + c0 + u] = f[u];
+  }
+  if (tid < C) L.beta[tid] = tid < ch.nv ? (float)beta[ch.row0 + (int64_t)tid * H] : 0.f;
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int t = 0; t < C; ++t) {
+      s += bs[t * PB + tid];
+      bs[t * PB + tid] = s;
+    }
+    L.gam[tid] = __expf(s);
+  }
+  __syncthreads();
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, c0 = 8 * (e & 15);
+    Vec16 xq = {{0u, 0u, 0u, 0u}}, xk = {{0u, 0u, 0u, 0u}};
+    if (t < ch.nv) {
+      xq = ldg16(q + (ch.row0 + (int64_t)t * H) * D + c0);
+      xk = ldg16(k + (ch.row0 + (int64_t)t * H) * D + c0);
+    }
+    float fq[8], fk[8];
+    vec_to_f32<bf16>(xq, fq);
+    vec_to_f32<bf16>(xk, fk);
+    bf16x8 kg, kd, qg;
+    float qk = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float b = bs[t * PB + c0 + u];
+      const float ep = __expf(b), em = __expf(-b);
+      kg[u] = (bf16)(fk[u] * ep);
+      kd[u] = (bf16)(fk[u] * em);
+      qg[u] = (bf16)(fq[u] * ep);
+      qk += fq[u] * fk[u];
+    }
+    *reinterpret_cast<bf16x8*>(L.Kg + t * P128 + c0) = kg;
+    *reinterpret_cast<bf16x8*>(L.Kd + t * P128 + c0) = kd;
+    *reinterpret_cast<bf16x8*>(L.Qg + t * P128 + c0) = qg;
+    // the 16 threads of row t are 16 consecutive lanes
+    qk = sum16(qk);
+    if ((e & 15) == 0) L.qk[t] = qk;
+  }
+  __syncthreads();
+}
+
+// L = StrictTril(Diag(beta) Kg Kd^T) into Ls (fp32 [64][PF], zero elsewhere)
+// and P^T into L.PT (bf16, zero where P is zero).
+__device__ void chunk_gram(const Basics& L, float* Ls, int tid) {
+  const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  for (int e = tid; e < C * PF; e += NT) Ls[e] = 0.f;
+  for (int e = tid; e < C * P64; e += NT) L.PT[e] = (bf16)0.f;
+  __syncthreads();
+  // 10 lower tiles of each of G and P
+  for (int q = wave; q < 20; q += NT / 64) {
+    const int tq = q % 10;
+    int I = 0, J = 0;
+    {
+      int c = 0;
+      for (int a = 0; a < 4; ++a)
+        for (int b2 = 0; b2 <= a; ++b2) {
+          if (c == tq) { I = a; J = b2; }
+          ++c;
+        }
+    }
+    if (q < 10) {
+      const floatx4 acc = mm<true, true>(L.Kg, P128, L.Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        Ls[t * PF + s] = t > s ? acc[r] * L.beta[t] : 0.f;
+      }
+    } else {
+      floatx4 acc = mm<true, true>(L.Qg, P128, L.Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        acc[r] = t > s ? acc[r] : (t == s ? L.qk[t] : 0.f);
+      }
+      st_tr(L.PT, P64, 16 * I, 16 * J, acc, lane);
+    }
+  }
+  __syncthreads();
+}
+
+// Off-diagonal blocks of block column J (fp32 MFMA; the column's blocks in
+// C layout serve as B operands).
+template <int J>
+__device__ __forceinline__ void solve_col(const float* Ls, float* As, int lane) {
+  const int g4 = lane >> 4, i = lane & 15;
+  floatx4 col[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) col[J][r] = As[(16 * J + 4 * g4 + r) * PF + 16 * J + i];
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    floatx4 t = zero4();
+#pragma unroll
+    for (int K = J; K < I; ++K) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(Ls + (16 * I + i) * PF + 16 * K + 4 * g4);
+      t = MF::mma16(a, col[K], t);
+    }
+    const floatx4 d = *reinterpret_cast<const floatx4*>(As + (16 * I + i) * PF + 16 * I + 4 * g4);
+    floatx4 y = MF::mma16(d, t, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      y[r] = -y[r];
+      As[(16 * I + 4 * g4 + r) * PF + 16 * J + i] = y[r];
+    }
+    col[I] = y;
+  }
+}
+
+// A = (I + L)^-1 (fp32, in As [64][PF]) from Ls; then bf16 into L.A.
+// Diagonal 16x16 blocks by forward substitution (one wavefront each, lane =
+// column); off-diagonal blocks of block column J top to bottom,
+// A_IJ = -D_I sum_{J<=K<I} L_IK A_KJ, with fp32 MFMA and the column's blocks
+// kept in registers (waves 0-2, one column each).
+__device__ void chunk_solve(const Basics& L, const float* Ls, float* As, int tid) {
+  const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  if (wave < 4) {
+    const int I = wave, c = i;
+    const float* Lb = Ls + 16 * I * PF + 16 * I;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int m = 0; m < r; ++m) x[r] -= Lb[r * PF + m] * x[m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (rr == 4 * g4 + r) v = x[rr];
+      As[(16 * I + 4 * g4 + r) * PF + 16 * I + c] = v;
+    }
+  }
+  // zero the strictly upper blocks
+  for (int e = tid; e < C * C; e += NT) {
+    const int t = e >> 6, s = e & 63;
+    if ((s >> 4) > (t >> 4)) As[t * PF + s] = 0.f;
+  }
+  __syncthreads();
+  if (wave == 0) solve_col<0>(Ls, As, lane);
+  else if (wave == 1) solve_col<1>(Ls, As, lane);
+  else if (wave == 2) solve_col<2>(Ls, As, lane);
+  __syncthreads();
+  for (int e = tid; e < C * C; e += NT) {
+    const int t = e >> 6, s = e & 63;
+    L.A[t * P64 + s] = (bf16)(s <= t ? As[t * PF + s] : 0.f);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- the chain
+// LDS of bwd_chain_kernel (bytes).
+namespace ch {
+constexpr int O_KG = 0;
+constexpr int O_KD = O_KG + C * P128 * 2;
+constexpr int O_QG = O_KD + C * P128 * 2;
+constexpr int O_A = O_QG + C * P128 * 2;
+constexpr int O_PT = O_A + C * P64 * 2;
+constexpr int O_DO = O_PT + C * P64 * 2;          // dO[:, J] row-major [64][P64]
+constexpr int O_DSG = O_DO + C * P64 * 2;         // (gamma . dS)^T [64 j][P128]
+constexpr int O_DDT = O_DSG + 64 * P128 * 2;      // dDelta^T [64 j][P64]
+constexpr int O_ET = O_DDT + 64 * P64 * 2;        // (A'^T dDelta)^T [64 j][P64]
+constexpr int O_BS = O_ET + 64 * P64 * 2;         // fp32 b [64][PB]; later Ls, As [64][PF] each
+constexpr int SZ_BS = (C * PB > 2 * C * PF ? C * PB : 2 * C * PF) * 4;
+constexpr int O_BETA = O_BS + SZ_BS;
+constexpr int O_GAM = O_BETA + C * 4;
+constexpr int O_QK = O_GAM + D * 4;
+constexpr int BYTES = O_QK + C * 4;
+static_assert(BYTES <= 160 * 1024, "LDS");
+}  // namespace ch
+
+__device__ __forceinline__ Basics basics(unsigned char* sm, int kg, int kd, int qg, int a, int pt, int be, int ga,
+                                         int qk) {
+  Basics L;
+  L.Kg = reinterpret_cast<bf16*>(sm + kg);
+  L.Kd = reinterpret_cast<bf16*>(sm + kd);
+  L.Qg = reinterpret_cast<bf16*>(sm + qg);
+  L.A = reinterpret_cast<bf16*>(sm + a);
+  L.PT = reinterpret_cast<bf16*>(sm + pt);
+  L.beta = reinterpret_cast<float*>(sm + be);
+  L.gam = reinterpret_cast<float*>(sm + ga);
+  L.qk = reinterpret_cast<float*>(sm + qk);
+  return L;
+}
+
+// One workgroup per (sequence, head, value-column half jh): dS[:, J] in
+// registers (wave w: c tiles 4(w/4) .. +3, j tile w % 4), chunks in reverse.
+__global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x >> 1, jh = blockIdx.x & 1;
+  if (bh >= a.B * a.H) return;
+  const int b = bh / a.H, h = bh % a.H;
+  const int N = (a.T + C - 1) / C;
+  const int J0 = 64 * jh;
+  const Basics L = basics(sm, ch::O_KG, ch::O_KD, ch::O_QG, ch::O_A, ch::O_PT, ch::O_BETA, ch::O_GAM, ch::O_QK);
+  bf16* sDO = reinterpret_cast<bf16*>(sm + ch::O_DO);
+  bf16* sDSG = reinterpret_cast<bf16*>(sm + ch::O_DSG);
+  bf16* sDDT = reinterpret_cast<bf16*>(sm + ch::O_DDT);
+  bf16* sET = reinterpret_cast<bf16*>(sm + ch::O_ET);
+  float* bs = reinterpret_cast<float*>(sm + ch::O_BS);
+  float* Ls = bs;
+  float* As = bs + C * PF;
+  const bf16* q = reinterpret_cast<const bf16*>(a.q);
+  const bf16* k = reinterpret_cast<const bf16*>(a.k);
+  const bf16* g = reinterpret_cast<const bf16*>(a.g);
+  const bf16* be = reinterpret_cast<const bf16*>(a.beta);
+  const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
+
+  const int ct0 = 4 * (wave >> 2), jt = wave & 3;   // my dS tiles: (ct0 + u, jt)
+  floatx4 dS[4];
+  const float* dST = a.dS_T ? a.dS_T + (int64_t)bh * D * D : nullptr;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dS[u][r] = dST ? dST[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] : 0.f;
+
+  for (int n = N - 1; n >= 0; --n) {
+    Chunk c;
+    c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
+    c.nv = min(C, a.T - n * C);
+    c.rstride = a.H * D;
+    // chunk-end adjoint of this chunk
+    float* adj = a.adjoints + ((int64_t)bh * N + n) * D * D;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) adj[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] = dS[u][r];
+    chunk_gates(L, bs, q, k, g, be, c, a.H, tid);
+    chunk_gram(L, Ls, tid);
+    chunk_solve(L, Ls, As, tid);
+    // dO[:, J] (rows past nv zero) and (gamma . dS)^T
+    for (int e = tid; e < C * 8; e += NT) {
+      const int t = e >> 3, c0 = 8 * (e & 7);
+      Vec16 x = {{0u, 0u, 0u, 0u}};
+      if (t < c.nv) x = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + J0 + c0);
+      *reinterpret_cast<Vec16*>(sDO + t * P64 + c0) = x;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      floatx4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * (ct0 + u) + 4 * g4 + r];
+      st_tr(sDSG, P128, 16 * (ct0 + u), 16 * jt, v, lane);
+    }
+    __syncthreads();
+    // dDelta[:, J] = P^T dO + Kd (gamma . dS), stored transposed
+    for (int tile = wave; tile < 16; tile += NT / 64) {
+      const int tt = tile >> 2, jj = tile & 3;
+      floatx4 acc = mm<true, false>(L.PT, P64, sDO, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+      acc = mm<true, true>(L.Kd, P128, sDSG, P128, 16 * tt, 16 * jj, D, acc, lane);
+      st_tr(sDDT, P64, 16 * tt, 16 * jj, acc, lane);
+    }
+    __syncthreads();
+    // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed
+    for (int tile = wave; tile < 16; tile += NT / 64) {
+      const int tt = tile >> 2, jj = tile & 3;
+      floatx4 acc = mm<false, true>(L.A, P64, sDDT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= L.beta[16 * tt + 4 * g4 + r];
+      st_tr(sET, P64, 16 * tt, 16 * jj, acc, lane);
+    }
+    __syncthreads();
+    // dS <- gamma . dS + Qg^T dO - Kg^T E
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ct = ct0 + u;
+      floatx4 p = mm<false, false>(L.Qg, P128, sDO, P64, 16 * ct, 16 * jt, C, zero4(), lane);
+      floatx4 m = mm<false, true>(L.Kg, P128, sET, P64, 16 * ct, 16 * jt, C, zero4(), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * ct + 4 * g4 + r] * dS[u][r] + p[r] - m[r];
+    }
+    __syncthreads();
+  }
+  if (a.dS0) {
+    float* out = a.dS0 + (int64_t)bh * D * D;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] = dS[u][r];
+  }
+}
+
+// ---------------------------------------------------------------- gradients
+namespace gr {
+constexpr int O_KG = 0;
+constexpr int O_KD = O_KG + C * P128 * 2;
+constexpr int O_QG = O_KD + C * P128 * 2;
+constexpr int O_A = O_QG + C * P128 * 2;
+constexpr int O_PT = O_A + C * P64 * 2;
+constexpr int O_BETA = O_PT + C * P64 * 2;
+constexpr int O_GAM = O_BETA + C * 4;
+constexpr int O_QK = O_GAM + D * 4;
+constexpr int O_DGAM = O_QK + C * 4;          // rowsum(dS . S), [128]
+constexpr int O_MD = O_DGAM + D * 4;          // diagonal of M, [64]
+constexpr int O_DB = O_MD + C * 4;            // dbeta partial sums [8 waves][64]
+constexpr int O_WORK = O_DB + 8 * C * 4;      // phase-dependent area
+// half-loop layout inside the work area
+constexpr int H_S = 0;                         // S[:, J]        [128][P64] bf16
+constexpr int H_DSG = H_S + D * P64 * 2;       // gamma.dS[:, J] [128][P64]
+constexpr int H_V = H_DSG + D * P64 * 2;       // V[:, J]        [64][P64]
+constexpr int H_DO = H_V + C * P64 * 2;        // dO[:, J]
+constexpr int H_D = H_DO + C * P64 * 2;        // Delta[:, J]
+constexpr int H_DD = H_D + C * P64 * 2;        // dDelta[:, J]
+constexpr int H_XT = H_DD + C * P64 * 2;       // (beta . (V - Kg S))^T [64 j][P64]
+constexpr int H_END = H_XT + C * P64 * 2;
+// after the halves
+constexpr int Q_DW = 0;                        // dW row-major [64][P128]
+constexpr int Q_M = Q_DW + C * P128 * 2;       // M (zero diagonal) [64][P64]
+constexpr int Q_DA = Q_M + C * P64 * 2;        // dA (strictly lower) [64][P64]
+constexpr int Q_Z1T = Q_DA + C * P64 * 2;      // (dA A^T)^T [64][P64]
+constexpr int Q_DL = Q_Z1T + C * P64 * 2;      // dL [64][P64]
+constexpr int Q_DG = Q_DL + C * P64 * 2;       // Diag(beta) dL [64][P64]
+constexpr int Q_END = Q_DG + C * P64 * 2;
+constexpr int Z_DB = 0;                        // db fp32 [64][PB] (assembly)
+constexpr int BYTES = O_WORK + (H_END > Q_END ? H_END : Q_END);
+static_assert(C * PB * 4 <= H_END, "gate scratch inside the work area");
+static_assert(2 * C * PF * 4 <= H_END, "solver scratch inside the work area");
+static_assert(Q_END <= H_END, "after-halves buffers inside the work area");
+static_assert(BYTES <= 160 * 1024, "LDS");
+}  // namespace gr
+
+// One workgroup per (chunk, sequence, head).  [t][c] results: wave w owns
+// channels 16w .. 16w+15 (4 tiles of each); [t][j] results of a half and the
+// lower [t][t'] tiles are spread over the waves.
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = (a.T + C - 1) / C;
+  const int bh = blockIdx.x / N, n = blockIdx.x % N;
+  if (bh >= a.B * a.H) return;
+  const int b = bh / a.H, h = bh % a.H;
+  const Basics L = basics(sm, gr::O_KG, gr::O_KD, gr::O_QG, gr::O_A, gr::O_PT, gr::O_BETA, gr::O_GAM, gr::O_QK);
+  float* dgam = reinterpret_cast<float*>(sm + gr::O_DGAM);
+  float* md = reinterpret_cast<float*>(sm + gr::O_MD);
+  float* dbp = reinterpret_cast<float*>(sm + gr::O_DB);
+  unsigned char* work = sm + gr::O_WORK;
+  const bf16* q = reinterpret_cast<const bf16*>(a.q);
+  const bf16* k = reinterpret_cast<const bf16*>(a.k);
+  const bf16* g = reinterpret_cast<const bf16*>(a.g);
+  const bf16* be = reinterpret_cast<const bf16*>(a.beta);
+  const bf16* v = reinterpret_cast<const bf16*>(a.v);
+  const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
+  Chunk c;
+  c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
+  c.nv = min(C, a.T - n * C);
+  c.rstride = a.H * D;
+  const float* Sn = a.states + ((int64_t)bh * N + n) * D * D;
+  const float* dSn = a.adjoints + ((int64_t)bh * N + n) * D * D;
+
+  {
+    float* bs = reinterpret_cast<float*>(work);
+    chunk_gates(L, bs, q, k, g, be, c, a.H, tid);
+    float* Ls = reinterpret_cast<float*>(work);
+    chunk_gram(L, Ls, tid);
+    chunk_solve(L, Ls, Ls + C * PF, tid);
+  }
+  for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
+  if (tid < D) dgam[tid] = 0.f;
+
+  // persistent accumulators
+  const int c0 = 16 * wave;     // my channel block
+  floatx4 aQg[4], aKd[4], aKb[4], aW[4], aKg[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) aQg[u] = aKd[u] = aKb[u] = aW[u] = aKg[u] = zero4();
+  // lower [t][t'] tiles: tile index q = wave, wave + 8 (< 10)
+  floatx4 aM[2] = {zero4(), zero4()}, aA[2] = {zero4(), zero4()};
+  auto lower_tile = [](int tq, int& I, int& J) {
+    int cc = 0;
+    I = J = 0;
+    for (int x = 0; x < 4; ++x)
+      for (int y = 0; y <= x; ++y) {
+        if (cc == tq) { I = x; J = y; }
+        ++cc;
+      }
+  };
+
+  bf16* hS = reinterpret_cast<bf16*>(work + gr::H_S);
+  bf16* hDSG = reinterpret_cast<bf16*>(work + gr::H_DSG);
+  bf16* hV = reinterpret_cast<bf16*>(work + gr::H_V);
+  bf16* hDO = reinterpret_cast<bf16*>(work + gr::H_DO);
+  bf16* hD = reinterpret_cast<bf16*>(work + gr::H_D);
+  bf16* hDD = reinterpret_cast<bf16*>(work + gr::H_DD);
+  bf16* hXT = reinterpret_cast<bf16*>(work + gr::H_XT);
+  float dgp = 0.f;   // rowsum(dS . S) partial of row tid / 4 (tid < 512: rows 0..127)
+
+  for (int jh = 0; jh < 2; ++jh) {
+    const int J0 = 64 * jh;
+    __syncthreads();
+    // S[:, J], gamma . dS[:, J]: thread -> row c = tid / 4, 16 columns
+    {
+      const int cr = tid >> 2, cc = 16 * (tid & 3);
+      const float gm = L.gam[cr];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const floatx4 s = *reinterpret_cast<const floatx4*>(Sn + cr * D + J0 + cc + 4 * u);
+        const floatx4 d = *reinterpret_cast<const floatx4*>(dSn + cr * D + J0 + cc + 4 * u);
+        bf16x4 sb, db;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dgp += s[r] * d[r];
+          sb[r] = (bf16)s[r];
+          db[r] = (bf16)(gm * d[r]);
+        }
+        *reinterpret_cast<bf16x4*>(hS + cr * P64 + cc + 4 * u) = sb;
+        *reinterpret_cast<bf16x4*>(hDSG + cr * P64 + cc + 4 * u) = db;
+      }
+    }
+    // V[:, J], dO[:, J]
+    for (int e = tid; e < C * 8; e += NT) {
+      const int t = e >> 3, x0 = 8 * (e & 7);
+      Vec16 xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
+      if (t < c.nv) {
+        xv = ldg16(v + (c.row0 + (int64_t)t * a.H) * D + J0 + x0);
+        xo = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + J0 + x0);
+      }
+      *reinterpret_cast<Vec16*>(hV + t * P64 + x0) = xv;
+      *reinterpret_cast<Vec16*>(hDO + t * P64 + x0) = xo;
+    }
+    __syncthreads();
+    // X = beta . (V - Kg S), stored transposed
+    for (int tile = wave; tile < 16; tile += NT / 64) {
+      const int tt = tile >> 2, jj = tile & 3;
+      floatx4 ks = mm<true, false>(L.Kg, P128, hS, P64, 16 * tt, 16 * jj, D, zero4(), lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        ks[r] = L.beta[t] * ((float)hV[t * P64 + 16 * jj + i] - ks[r]);
+      }
+      st_tr(hXT, P64, 16 * tt, 16 * jj, ks, lane);
+    }
+    __syncthreads();
+    // Delta = A X; dDelta = P^T dO + Kd (gamma . dS); both row-major
+    for (int tile = wave; tile < 16; tile += NT / 64) {
+      const int tt = tile >> 2, jj = tile & 3;
+      const floatx4 dl = mm<true, true>(L.A, P64, hXT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+      st_rm(hD, P64, 16 * tt, 16 * jj, dl, lane);
+      floatx4 dd = mm<true, false>(L.PT, P64, hDO, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+      dd = mm<true, false>(L.Kd, P128, hDSG, P64, 16 * tt, 16 * jj, D, dd, lane);
+      st_rm(hDD, P64, 16 * tt, 16 * jj, dd, lane);
+    }
+    __syncthreads();
+    // [t][c] products over this half's value columns
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      aQg[u] = mm<true, true>(hDO, P64, hS, P64, 16 * u, c0, 64, aQg[u], lane);    // dO S^T
+      aKb[u] = mm<true, true>(hD, P64, hDSG, P64, 16 * u, c0, 64, aKb[u], lane);   // Delta (g.dS)^T
+      aW[u] = mm<true, true>(hDD, P64, hS, P64, 16 * u, c0, 64, aW[u], lane);      // dDelta S^T
+    }
+    // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int tq = wave + 8 * x;
+      if (tq < 10) {
+        int I, J;
+        lower_tile(tq, I, J);
+        aM[x] = mm<true, true>(hDO, P64, hD, P64, 16 * I, 16 * J, 64, aM[x], lane);
+        aA[x] = mm<true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
+      }
+    }
+    // dV[:, J] = Diag(beta) A^T dDelta -> output; dbeta += rowsum((A^T dDelta) . V)
+    for (int tile = wave; tile < 16; tile += NT / 64) {
+      const int tt = tile >> 2, jj = tile & 3;
+      const floatx4 x = mm<false, false>(L.A, P64, hDD, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+      bf16* dv = reinterpret_cast<bf16*>(a.dv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        if (t < c.nv) dv[(c.row0 + (int64_t)t * a.H) * D + J0 + 16 * jj + i] = (bf16)(L.beta[t] * x[r]);
+        const float p = sum16(x[r] * (float)hV[t * P64 + 16 * jj + i]);
+        if (i == 0) dbp[wave * C + t] += p;
+      }
+    }
+  }
+  // rowsum(dS . S): 4 threads per row
+  dgp += __shfl_xor(dgp, 1);
+  dgp += __shfl_xor(dgp, 2);
+  if ((tid & 3) == 0) dgam[tid >> 2] = dgp;
+  __syncthreads();   // the half-loop buffers are dead from here
+
+  bf16* qDW = reinterpret_cast<bf16*>(work + gr::Q_DW);
+  bf16* qM = reinterpret_cast<bf16*>(work + gr::Q_M);
+  bf16* qDA = reinterpret_cast<bf16*>(work + gr::Q_DA);
+  bf16* qZ1T = reinterpret_cast<bf16*>(work + gr::Q_Z1T);
+  bf16* qDL = reinterpret_cast<bf16*>(work + gr::Q_DL);
+  bf16* qDG = reinterpret_cast<bf16*>(work + gr::Q_DG);
+  // dW = -dDelta S^T (row-major); M with its diagonal moved out; zero fills
+  for (int e = tid; e < C * P64; e += NT) {
+    qM[e] = (bf16)0.f;
+    qDA[e] = (bf16)0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    floatx4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = -aW[u][r];
+    aW[u] = w;
+    st_rm(qDW, P128, 16 * u, c0, w, lane);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int tq = wave + 8 * x;
+    if (tq < 10) {
+      int I, J;
+      lower_tile(tq, I, J);
+      floatx4 m = aM[x];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        if (t == s) md[t] = m[r];
+        m[r] = t > s ? m[r] : 0.f;
+      }
+      st_rm(qM, P64, 16 * I, 16 * J, m, lane);
+      // dA = (dDelta V^T + dW Kg^T) Diag(beta), strictly lower
+      floatx4 da = mm<true, true>(qDW, P128, L.Kg, P128, 16 * I, 16 * J, D, aA[x], lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        da[r] = t > s ? da[r] * L.beta[s] : 0.f;
+      }
+      st_rm(qDA, P64, 16 * I, 16 * J, da, lane);
+    }
+  }
+  __syncthreads();
+  // Z1^T = A dA^T ( = (dA A^T)^T ), all 16 tiles
+  for (int tile = wave; tile < 16; tile += NT / 64) {
+    const int I = tile >> 2, J = tile & 3;
+    const floatx4 z = mm<true, true>(L.A, P64, qDA, P64, 16 * I, 16 * J, C, zero4(), lane);
+    st_rm(qZ1T, P64, 16 * I, 16 * J, z, lane);
+  }
+  // [t][c]: M Kd, M^T Qg, A^T dW
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    aQg[u] = mm<true, false>(qM, P64, L.Kd, P128, 16 * u, c0, C, aQg[u], lane);
+    aKd[u] = mm<false, false>(qM, P64, L.Qg, P128, 16 * u, c0, C, aKd[u], lane);
+  }
+  {
+    // Y = A^T dW with dW from registers (B operand of the 16-index slabs)
+    bf16x4 wf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wf[u] = MB::frag16(aW[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      floatx4 y = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) y = MB::mma16(fr_col(L.A, P64, 16 * u + i, 16 * ks + 4 * g4), wf[ks], y);
+      // dKg += Diag(beta) Y; dbeta += rowsum(Y . Kg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * u + 4 * g4 + r;
+        aKg[u][r] += L.beta[t] * y[r];
+        const float p = sum16(y[r] * (float)L.Kg[t * P128 + c0 + i]);
+        if (i == 0) dbp[wave * C + t] += p;
+      }
+    }
+  }
+  __syncthreads();
+  // dL = -StrictTril(A^T Z1); dG = Diag(beta) dL
+  for (int e = tid; e < C * P64; e += NT) {
+    qDL[e] = (bf16)0.f;
+    qDG[e] = (bf16)0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int tq = wave + 8 * x;
+    if (tq < 10) {
+      int I, J;
+      lower_tile(tq, I, J);
+      floatx4 l = mm<false, true>(L.A, P64, qZ1T, P64, 16 * I, 16 * J, C, zero4(), lane);
+      floatx4 gg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        l[r] = t > s ? -l[r] : 0.f;
+        gg[r] = l[r] * L.beta[t];
+      }
+      st_rm(qDL, P64, 16 * I, 16 * J, l, lane);
+      st_rm(qDG, P64, 16 * I, 16 * J, gg, lane);
+    }
+  }
+  __syncthreads();
+  // dKg += Diag(beta) dL Kd (dbeta += rowsum(Kg . dL Kd)); dKd += dG^T Kg
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const floatx4 lk = mm<true, false>(qDL, P64, L.Kd, P128, 16 * u, c0, C, zero4(), lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * u + 4 * g4 + r;
+      aKg[u][r] += L.beta[t] * lk[r];
+      const float p = sum16(lk[r] * (float)L.Kg[t * P128 + c0 + i]);
+      if (i == 0) dbp[wave * C + t] += p;
+    }
+    aKd[u] = mm<false, false>(qDG, P64, L.Kg, P128, 16 * u, c0, C, aKd[u], lane);
+  }
+  __syncthreads();   // the work area becomes the db array
+
+  // assembly: gate factors from b (recomputed), raw q, k
+  float* bs = reinterpret_cast<float*>(work + gr::Z_DB);
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, x0 = 8 * (e & 15);
+    Vec16 x = {{0u, 0u, 0u, 0u}};
+    if (t < c.nv) x = ldg16(g + (c.row0 + (int64_t)t * a.H) * D + x0);
+    float f[8];
+    vec_to_f32<bf16>(x, f);
+#pragma unroll
+    for (int uu = 0; uu < 8; ++uu) bs[t * PB + x0 + uu] = f[uu];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int t = 0; t < C; ++t) {
+      s += bs[t * PB + tid];
+      bs[t * PB + tid] = s;
+    }
+  }
+  __syncthreads();
+  // per element: dq, dk and db (db overwrites b in place, each element read
+  // before it is written by the same lane)
+  float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // sum_t Kd . dKb~ for column c0 + i (per lane, 4 row groups)
+  bf16* dq = reinterpret_cast<bf16*>(a.dq);
+  bf16* dk = reinterpret_cast<bf16*>(a.dk);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * u + 4 * g4 + r, cc = c0 + i;
+      const float bb = bs[t * PB + cc];
+      const float ep = __expf(bb), em = __expf(-bb);
+      float qv = 0.f, kv = 0.f;
+      if (t < c.nv) {
+        qv = (float)q[(c.row0 + (int64_t)t * a.H) * D + cc];
+        kv = (float)k[(c.row0 + (int64_t)t * a.H) * D + cc];
+      }
+      const float kg = kv * ep, kd = kv * em, qg = qv * ep;
+      const float dkd = aKd[u][r] + aKb[u][r];
+      const float dqv = ep * aQg[u][r] + md[t] * kv;
+      const float dkv = ep * aKg[u][r] + em * dkd + md[t] * qv;
+      if (t < c.nv) {
+        dq[(c.row0 + (int64_t)t * a.H) * D + cc] = (bf16)dqv;
+        dk[(c.row0 + (int64_t)t * a.H) * D + cc] = (bf16)dkv;
+      }
+      colsum[0] += kd * aKb[u][r];
+      bs[t * PB + cc] = kg * aKg[u][r] - kd * dkd + qg * aQg[u][r];
+    }
+  }
+  // chunk-end terms at row 63: sum over t of Kd . dKb~ (across the 4 row groups) + gamma . dgam
+  {
+    float s = colsum[0];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (g4 == 0) {
+      const int cc = c0 + i;
+      bs[(C - 1) * PB + cc] += s + L.gam[cc] * dgam[cc];
+    }
+  }
+  __syncthreads();
+  // dg = reverse cumulative sum of db over the chunk's rows
+  bf16* dgo = reinterpret_cast<bf16*>(a.dg);
+  if (tid < D) {
+    float s = 0.f;
+    for (int t = C - 1; t >= 0; --t) {
+      s += bs[t * PB + tid];
+      if (t < c.nv) dgo[(c.row0 + (int64_t)t * a.H) * D + tid] = (bf16)s;
+    }
+  }
+  if (tid < C && tid < c.nv) {
+    float s = 0.f;
+    for (int w = 0; w < NT / 64; ++w) s += dbp[w * C + tid];
+    reinterpret_cast<bf16*>(a.dbeta)[c.row0 + (int64_t)tid * a.H] = (bf16)s;
+  }
+}
+
+}  // namespace bwd
+
+size_t backward_workspace(int BH, int T) {
+  const size_t N = ((size_t)T + bwd::C - 1) / bwd::C;
+  return 2 * (size_t)BH * N * bwd::D * bwd::D * sizeof(float);
+}
+
+template <typename K>
+static hipError_t set_lds(K kern, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  if (BH == 0) return hipSuccess;
+  const int N = (a.T + bwd::C - 1) / bwd::C;
+  hipError_t e;
+  if (N > 0) {
+    // 1. chunk-entry states: the forward kernel in state mode
+    PrefillArgs f{};
+    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
+    f.S0 = a.S0; f.B = a.B; f.T = a.T; f.H = a.H; f.dk = 128; f.dv = 128; f.bf16 = 1; f.pipeline = 1;
+    f.states = a.states;
+    if ((e = launch_fused(f, s)) != hipSuccess) return e;
+  }
+  // 2. adjoint recursion (also writes dS0; with T = 0 it copies dS_T)
+  if ((e = set_lds(bwd::bwd_chain_kernel, bwd::ch::BYTES)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd::bwd_chain_kernel, dim3(2 * BH), dim3(bwd::NT), bwd::ch::BYTES, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (N == 0) return hipSuccess;
+  // 3. per-chunk gradients
+  if ((e = set_lds(bwd::bwd_grad_kernel, bwd::gr::BYTES)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd::bwd_grad_kernel, dim3(BH * N), dim3(bwd::NT), bwd::gr::BYTES, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -27,6 +27,9 @@ struct PrefillArgs {
   // tokens [cu_seqlens[b], cu_seqlens[b+1]) of [T, H, d] tensors; NULL: [B, T, H, d].
   const int* cu_seqlens;
   const int* seq_order;   // packed sequences: processing order (a permutation of 0..B-1), or NULL
+  // Chunk-entry states (one pass, no outputs): state at the start of every
+  // chunk, fp32 [B*H][ceil(T/64)][dk][dv]; NULL: normal forward.
+  float* states;
 };
 
 struct StageArgs {
@@ -44,6 +47,18 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Backward of the chunked forward (bf16, d_k = d_v = 128).
+struct BackwardArgs {
+  const void* q; const void* k; const void* v; const void* g; const void* beta;
+  const float* S0; const void* dO; const float* dS_T;
+  void* dq; void* dk; void* dv; void* dg; void* dbeta; float* dS0;
+  int B, T, H;
+  float* states;    // [B*H][N][128][128] chunk-entry states
+  float* adjoints;  // [B*H][N][128][128] adjoints of the chunk-end states
+};
+size_t backward_workspace(int BH, int T);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 // Order of packed sequences by decreasing chunk count (ties by index) into
 // order[0..N-1]; N <= kMaxScheduleSeqs.
 constexpr int kMaxScheduleSeqs = 16384;

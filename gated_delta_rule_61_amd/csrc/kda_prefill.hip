@@ -2088,6 +2088,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     }
     if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
     if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
+    if (a.states) outp = false;   // chunk-entry states only
   } else {
     const int njobs = a.pass == 1 ? 2 * a.nseg - 3 : a.nseg - 1;
     head = blockIdx.x / njobs;
@@ -2183,6 +2184,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
               make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
           owner_store(O, ro, a.H * DV, col0, lane);
         }
+        if (a.states) store_state_v(S, a.states + ((int64_t)head * ((a.T + C - 1) / C) + c0 + n) * DK * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
       // V^T of chunk n+1 (U is formed in phase 3)

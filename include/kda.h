@@ -198,6 +198,31 @@ int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const voi
                           int N, int H, int d_k, int d_v, int dtype, int flags, void* stream);
 
 /*
+ * kda_chunk_bwd -- gradient of kda_chunk_fwd: given the adjoints of its
+ * outputs, the adjoints of its inputs (the reverse-mode derivative of the
+ * chunked form of "...Making LLM Training and Inference More Efficient" §IV,
+ * whose stated purpose is training).
+ *   q,k,v,g,beta,S0  the forward's inputs (as kda_chunk_fwd; S0 NULL = zeros)
+ *   dO          adjoint of o [B,T,H,d_v], dtype `dtype`
+ *   dS_T        adjoint of S_T [B,H,d_k,d_v] fp32, or NULL for zero
+ *   dq,dk,dg    [B,T,H,d_k], dv [B,T,H,d_v], dbeta [B,T,H]: outputs, dtype `dtype`
+ *   dS0         [B,H,d_k,d_v] fp32 output, or NULL to skip it
+ *   workspace   kda_chunk_bwd_workspace_size() bytes (required), 16-byte aligned
+ * The forward is recomputed inside (its chunk-entry states go to the
+ * workspace); no forward state needs to be kept between the calls.
+ * Supported: dtype KDA_BF16 with d_k = d_v = 128 (else KDA_ERR_ARG);
+ * outputs must not alias inputs.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S0, const void* dO, const float* dS_T,
+                  void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS0,
+                  int B, int T, int H, int d_k, int d_v, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_chunk_bwd (2 * B*H*ceil(T/64) * d_k*d_v * 4). */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
+
+/*
  * Staged schedule: the same forward as kda_chunk_fwd, run as four separate
  * kernels with intermediates in a caller-provided workspace (the chunked
  * method's steps one by one).  Slower than kda_chunk_fwd; it exists so each

@@ -1,0 +1,175 @@
+"""GPU parity of the chunked backward (kda_chunk_bwd) against the fp64
+reverse-mode oracle, through the C ABI.  Needs an MI355X.
+
+Tolerances (bf16 inputs, gradients in bf16): per-head relative L2 of every
+gradient <= 1e-2 (dS0: fp32 output, same bound), and max |err| beyond the
+output's own bf16 rounding <= 0.1 * RMS(reference).  Each gradient is a
+sum of products with two to four chained bf16-rounded operands (unit
+roundoff 2^-9 each) where a forward output has one or two, and the forward's
+bound is 5e-3 per head; the backward bound allows twice that.  Measured:
+3.5-3.8e-3 for dq, dk, dv, dbeta, about 6e-3 for dg (a reverse sum over the
+chunk of terms that partly cancel), 1.8e-3 for dS0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import BF16_U, rms, to64
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAX_OVER = 0.1
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_61_amd as kda
+    kda.lib()
+    return kda
+
+
+def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K):
+    inp = W.prefill_inputs(cfg, device="cuda", seed=seed, B=B, T=T, H=H)
+    if not s0:
+        inp["S0"] = None
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 17)
+    inp["dO"] = torch.randn(B, T, H, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    inp["dST"] = (torch.randn(B, H, 128, 128, device="cuda", generator=gen) * 0.1) if dst else None
+    return inp
+
+
+def _oracle(inp, heads=None, chunk_adjoints=False):
+    names = ("q", "k", "v", "g", "beta")
+    if heads is None:
+        x = [to64(inp[n]) for n in names]
+        S0, dO, dST = to64(inp["S0"]), to64(inp["dO"]), to64(inp["dST"])
+    else:
+        x = [np.stack([to64(inp[n][b, :, h]) for b, h in heads])[:, :, None] for n in names]
+        S0 = None if inp["S0"] is None else np.stack([to64(inp["S0"][b, h]) for b, h in heads])[:, None]
+        dO = np.stack([to64(inp["dO"][b, :, h]) for b, h in heads])[:, :, None]
+        dST = None if inp["dST"] is None else np.stack([to64(inp["dST"][b, h]) for b, h in heads])[:, None]
+    return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints)
+
+
+def _pick(gr, heads):
+    out = {}
+    for n in NAMES:
+        t = gr[n]
+        if n == "dS0":
+            out[n] = np.stack([to64(t[b, h]) for b, h in heads])[:, None]
+        else:
+            out[n] = np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
+    return out
+
+
+def _check(got, ref, what):
+    """got/ref: dicts of numpy arrays shaped [B, T, H, ...] ([B, H, ...] for dS0)."""
+    worst = {}
+    for n in NAMES:
+        g, r = got[n], ref[n]
+        if r.size == 0:
+            continue
+        if n == "dS0":
+            heads = [(b, h) for b in range(r.shape[0]) for h in range(r.shape[1])]
+            sl = lambda x, b, h: x[b, h]
+        else:
+            heads = [(b, h) for b in range(r.shape[0]) for h in range(r.shape[2])]
+            sl = lambda x, b, h: x[b, :, h]
+        rel = 0.0
+        for b, h in heads:
+            den = np.linalg.norm(sl(r, b, h))
+            if den > 0:
+                rel = max(rel, float(np.linalg.norm(sl(g, b, h) - sl(r, b, h)) / den))
+        allow = 0.0 if n == "dS0" else BF16_U
+        over = float(np.max(np.abs(g - r) - allow * np.abs(r))) / max(rms(r), 1e-30)
+        worst[n] = (rel, over)
+    print(f"[bwd parity] {what}: " + " ".join(f"{n}=({a:.2e},{b:.2e})" for n, (a, b) in worst.items()), flush=True)
+    for n, (a, b) in worst.items():
+        assert a <= REL_L2, f"{what}: {n} per-head rel L2 {a:.3e} > {REL_L2}"
+        assert b <= MAX_OVER, f"{what}: {n} max err beyond rounding {b:.3e} > {MAX_OVER} RMS"
+
+
+def _run(kda, inp, workspace=None):
+    gr = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], inp["dO"], inp["dST"],
+                       workspace=workspace)
+    torch.cuda.synchronize()
+    return gr
+
+
+SHAPES = [(1, 1, 2, True, True), (1, 63, 2, True, False), (1, 64, 1, False, True), (2, 130, 3, True, True),
+          (1, 517, 2, True, True), (3, 192, 1, False, False)]
+
+
+@pytest.mark.parametrize("B,T,H,s0,dst", SHAPES,
+                         ids=[f"B{b}T{t}H{h}{'-S0' if s else ''}{'-dST' if d else ''}" for b, t, h, s, d in SHAPES])
+def test_small_shapes(kda, B, T, H, s0, dst):
+    inp = _inputs(B, T, H, 1000 + T + H, s0, dst)
+    print(f"case bwd B{B} T{T} H{H} s0={s0} dST={dst}", flush=True)
+    gr = _run(kda, inp)
+    ref = _oracle(inp)
+    got = {n: to64(gr[n]) for n in NAMES}
+    _check(got, ref, f"B{B}T{T}H{H}")
+
+
+def test_chunk_states_and_adjoints(kda):
+    """The workspace's chunk-entry states and chunk-end adjoints against the
+    oracle's forward states and per-chunk adjoints (fp32, same bounds)."""
+    B, T, H = 1, 200, 2
+    inp = _inputs(B, T, H, 77)
+    N = (T + 63) // 64
+    ws = torch.zeros(kda.lib().kda_chunk_bwd_workspace_size(B, T, H, 128, 128, 1) // 4, dtype=torch.float32,
+                     device="cuda")
+    _run(kda, inp, workspace=ws)
+    half = ws.numel() // 2
+    states = ws[:half].view(B * H, N, 128, 128)
+    adj = ws[half:].view(B * H, N, 128, 128)
+    ref = _oracle(inp, chunk_adjoints=True)["dS_chunks"]          # [B,H,N,dk,dv], adjoint at chunk start
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        for n in range(N):
+            want = ref[b, h, n + 1] if n + 1 < N else to64(inp["dST"][b, h])
+            got = to64(adj[bh, n])
+            rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+            assert rel < 1e-2, (bh, n, rel)
+        S = to64(inp["S0"][b, h])
+        for n in range(N):
+            got = to64(states[bh, n])
+            rel = np.linalg.norm(got - S) / max(np.linalg.norm(S), 1e-30)
+            assert rel < 5e-3, ("state", bh, n, rel)
+            t0, t1 = 64 * n, min(T, 64 * n + 64)
+            _, S = oracle.recurrent_fwd(*(to64(inp[x][b:b + 1, t0:t1, h:h + 1]) for x in ("q", "k", "v", "g", "beta")),
+                                        S[None, None])
+            S = S[0, 0]
+
+
+def test_B8_H32_T8192_sampled(kda):
+    """The benchmark's prefill workload: full-size backward, sampled heads."""
+    cfg = W.PREFILL_BF16_B8_H32_T8K
+    inp = _inputs(cfg.B, cfg.T, cfg.H, 2, s0=False, dst=False, cfg=cfg)
+    print("case bwd B8 H32 T8192", flush=True)
+    gr = _run(kda, inp)
+    heads = [(0, 0), (5, 20), (7, 31)]
+    ref = _oracle(inp, heads)
+    _check(_pick(gr, heads), ref, "B8 H32 T8192")
+    for n in NAMES[:-1]:
+        assert torch.isfinite(gr[n].float()).all(), n
+
+
+def test_zero_length(kda):
+    inp = _inputs(2, 0, 3, 5)
+    gr = _run(kda, inp)
+    assert torch.equal(gr["dS0"], inp["dST"])
+
+
+def test_deterministic(kda):
+    inp = _inputs(1, 300, 2, 9)
+    g1, g2 = _run(kda, inp), _run(kda, inp)
+    for n in NAMES:
+        assert torch.equal(g1[n], g2[n]), n
