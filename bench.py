@@ -42,6 +42,11 @@ PREFILL_FLOPS_PER_TOKHEAD = 6 * D * D + (C + 1) * 4 * D + (C - 1) * D + C * C / 
 STATE_BYTES = D * D * 4
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKHEAD   # state read + write + token I/O
 
+# Backward: reads q, k, v, g (4 x 256), beta 2, dO 256; writes dq, dk, dv, dg
+# (4 x 256), dbeta 2 -- the chunk states and adjoints it keeps in a workspace
+# are not part of the algorithmic bytes.
+BWD_BYTES_PER_TOKHEAD = 4 * D * 2 + 2 + D * 2 + 4 * D * 2 + 2
+
 # Variants: (scalar_gate, delta).  A scalar gate reads one bf16 per token and
 # head instead of d_k; without the delta rule beta is not read.
 VARIANTS = {"kda": (False, True), "scalar": (True, True), "nodelta": (False, False),
@@ -62,6 +67,8 @@ def parse():
                     help="skip the CPU oracle leg (used for profiler runs)")
     ap.add_argument("--variant", choices=sorted(VARIANTS), default="kda",
                     help="recurrence variant (default: KDA)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward (kda_chunk_bwd) measurement")
     ap.add_argument("--packed", action="store_true",
                     help="prefill over variable-length packed sequences of the same tokens")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -117,6 +124,40 @@ def cpu_baseline(W, oracle, torch, scalar_gate=False, delta=True):
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole prefill workload (B={cfg.B}, H={cfg.H}, T={cfg.T}, d=128) once, "
                       f"fp64 token recurrence, {dt:.1f} s wall"}
+
+
+def measure_backward(kda, W, torch, pcfg, inp, args, stream):
+    """kda_chunk_bwd on the prefill workload (adjoints dO ~ N(0,1) bf16,
+    dS_T = 0), timed alone with events on the launch stream."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12345)
+    dO = torch.randn(pcfg.B, pcfg.T, pcfg.H, D, device="cuda", generator=gen).to(torch.bfloat16)
+    ws = torch.empty(kda.lib().kda_chunk_bwd_workspace_size(pcfg.B, pcfg.T, pcfg.H, D, D, 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], dO, None, want_dS0=False,
+                      workspace=ws)
+
+    for _ in range(max(args.warmup, 1)):
+        bwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    BTH = pcfg.B * pcfg.T * pcfg.H
+    alg = BTH * BWD_BYTES_PER_TOKHEAD
+    gbs = alg / (ms * 1e-3) / 1e9
+    del ws, dO
+    return {"value": pcfg.B * pcfg.T / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
+            "workload": "kda_chunk_bwd B8 H32 T8192 d128 bf16 (S0=0, dS_T=0)",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "forward state pass + bwd_chain_kernel + bwd_grad_kernel"}}
 
 
 def main():
@@ -260,6 +301,8 @@ def main():
                                 "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic(dk_name),
                                 "kernel": dk_name + " (bf16, 128 x 128)"}},
     }
+    if not args.no_backward and flags == 0 and not args.packed:
+        line["backward"] = measure_backward(kda, W, torch, pcfg, inp, args, stream)
     del inp, o, S, tok, steps_tok
     if not args.no_cpu_baseline:
         import oracle

@@ -121,6 +121,32 @@ struct Basics {
   float *beta, *gam, *qk;   // [64], [128], [64]
 };
 
+// Inclusive prefix sums down the 64 rows of the 128 columns of bs (fp32
+// [64][PB]), in place: thread (column c, row group of 16) sums its rows in
+// registers, the four group totals meet in `tot` (4 x 128 floats of scratch
+// after the array).  gam (if not NULL) receives exp of each column's total.
+// REV: suffix sums (from the last row up) instead.
+template <bool REV>
+__device__ void scan_cols(float* bs, float* gam, int tid) {
+  float* tot = bs + C * PB;
+  const int c = tid & 127, rg = tid >> 7;
+  // row of step r of my group
+  auto row = [&](int r) { return REV ? C - 1 - (16 * rg + r) : 16 * rg + r; };
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = bs[row(r) * PB + c];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) x[r] += x[r - 1];
+  tot[rg * D + c] = x[15];
+  __syncthreads();
+  float off = 0.f;
+  for (int u = 0; u < rg; ++u) off += tot[u * D + c];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bs[row(r) * PB + c] = x[r] + off;
+  if (gam && rg == 3) gam[c] = __expf(x[15] + off);
+  __syncthreads();
+}
+
 // In-chunk cumulative log-gates b (fp32 [64][PB] in `bs`), the gated operands
 // Kg Kd Qg, gamma, beta and q.k.  Rows past nv are zero (g = 0 there, so b is
 // constant and the chunk end gate is that of the last valid row).
@@ -138,15 +164,7 @@ __device__ void chunk_gates(const Basics& L, float* bs, const bf16* q, const bf1
   }
   if (tid < C) L.beta[tid] = tid < ch.nv ? (float)beta[ch.row0 + (int64_t)tid * H] : 0.f;
   __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-    for (int t = 0; t < C; ++t) {
-      s += bs[t * PB + tid];
-      bs[t * PB + tid] = s;
-    }
-    L.gam[tid] = __expf(s);
-  }
-  __syncthreads();
+  scan_cols<false>(bs, L.gam, tid);
   for (int e = tid; e < C * 16; e += NT) {
     const int t = e >> 4, c0 = 8 * (e & 15);
     Vec16 xq = {{0u, 0u, 0u, 0u}}, xk = {{0u, 0u, 0u, 0u}};
@@ -178,45 +196,6 @@ __device__ void chunk_gates(const Basics& L, float* bs, const bf16* q, const bf1
   __syncthreads();
 }
 
-// L = StrictTril(Diag(beta) Kg Kd^T) into Ls (fp32 [64][PF], zero elsewhere)
-// and P^T into L.PT (bf16, zero where P is zero).
-__device__ void chunk_gram(const Basics& L, float* Ls, int tid) {
-  const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
-  for (int e = tid; e < C * PF; e += NT) Ls[e] = 0.f;
-  for (int e = tid; e < C * P64; e += NT) L.PT[e] = (bf16)0.f;
-  __syncthreads();
-  // 10 lower tiles of each of G and P
-  for (int q = wave; q < 20; q += NT / 64) {
-    const int tq = q % 10;
-    int I = 0, J = 0;
-    {
-      int c = 0;
-      for (int a = 0; a < 4; ++a)
-        for (int b2 = 0; b2 <= a; ++b2) {
-          if (c == tq) { I = a; J = b2; }
-          ++c;
-        }
-    }
-    if (q < 10) {
-      const floatx4 acc = mm<true, true>(L.Kg, P128, L.Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
-        Ls[t * PF + s] = t > s ? acc[r] * L.beta[t] : 0.f;
-      }
-    } else {
-      floatx4 acc = mm<true, true>(L.Qg, P128, L.Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
-        acc[r] = t > s ? acc[r] : (t == s ? L.qk[t] : 0.f);
-      }
-      st_tr(L.PT, P64, 16 * I, 16 * J, acc, lane);
-    }
-  }
-  __syncthreads();
-}
-
 // Off-diagonal blocks of block column J (fp32 MFMA; the column's blocks in
 // C layout serve as B operands).
 template <int J>
@@ -244,12 +223,12 @@ __device__ __forceinline__ void solve_col(const float* Ls, float* As, int lane) 
   }
 }
 
-// A = (I + L)^-1 (fp32, in As [64][PF]) from Ls; then bf16 into L.A.
+// A = (I + L)^-1 (fp32, in As [64][PF]) from Ls.
 // Diagonal 16x16 blocks by forward substitution (one wavefront each, lane =
 // column); off-diagonal blocks of block column J top to bottom,
 // A_IJ = -D_I sum_{J<=K<I} L_IK A_KJ, with fp32 MFMA and the column's blocks
 // kept in registers (waves 0-2, one column each).
-__device__ void chunk_solve(const Basics& L, const float* Ls, float* As, int tid) {
+__device__ void solve_fp32(const float* Ls, float* As, int tid) {
   const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   if (wave < 4) {
     const int I = wave, c = i;
@@ -280,11 +259,164 @@ __device__ void chunk_solve(const Basics& L, const float* Ls, float* As, int tid
   else if (wave == 1) solve_col<1>(Ls, As, lane);
   else if (wave == 2) solve_col<2>(Ls, As, lane);
   __syncthreads();
-  for (int e = tid; e < C * C; e += NT) {
-    const int t = e >> 6, s = e & 63;
-    L.A[t * P64 + s] = (bf16)(s <= t ? As[t * PF + s] : 0.f);
+}
+
+// ---------------------------------------------------------------- per-chunk matrices
+// A = (I + L)^-1 and P^T of every chunk (bf16 [64][64] each, row-major), for
+// the chain and the gradient kernels: one workgroup per (chunk, sequence,
+// head), in an order that lets Qg and Kg share one buffer (P first, then G).
+namespace pr {
+constexpr int O_X = 0;                           // Qg, then Kg [64][P128]
+constexpr int O_KD = O_X + C * P128 * 2;         // Kd
+constexpr int O_BS = O_KD + C * P128 * 2;        // fp32 b (+ scan scratch); later Ls, As
+constexpr int SZ_BS = (C * PB + 4 * D > 2 * C * PF ? C * PB + 4 * D : 2 * C * PF) * 4;
+constexpr int O_BETA = O_BS + SZ_BS;
+constexpr int O_QK = O_BETA + C * 4;
+constexpr int BYTES = O_QK + C * 4;
+static_assert(BYTES <= 80 * 1024, "two workgroups per compute unit");
+}  // namespace pr
+
+__device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t bh, int N, int n) {
+  return reinterpret_cast<bf16*>(a.mats) + ((bh * N + n) * 2) * (int64_t)(C * C);
+}
+
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = (a.T + C - 1) / C;
+  const int bh = blockIdx.x / N, n = blockIdx.x % N;
+  if (bh >= a.B * a.H) return;
+  const int b = bh / a.H, h = bh % a.H;
+  bf16* X = reinterpret_cast<bf16*>(sm + pr::O_X);
+  bf16* Kd = reinterpret_cast<bf16*>(sm + pr::O_KD);
+  float* bs = reinterpret_cast<float*>(sm + pr::O_BS);
+  float* beta = reinterpret_cast<float*>(sm + pr::O_BETA);
+  float* qkd = reinterpret_cast<float*>(sm + pr::O_QK);
+  const bf16* q = reinterpret_cast<const bf16*>(a.q);
+  const bf16* k = reinterpret_cast<const bf16*>(a.k);
+  const bf16* g = reinterpret_cast<const bf16*>(a.g);
+  const int64_t row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
+  const int nv = min(C, a.T - n * C);
+  bf16* Am = chunk_mats(a, bh, N, n);
+  bf16* PTm = Am + C * C;
+
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, x0 = 8 * (e & 15);
+    Vec16 x = {{0u, 0u, 0u, 0u}};
+    if (t < nv) x = ldg16(g + (row0 + (int64_t)t * a.H) * D + x0);
+    float f[8];
+    vec_to_f32<bf16>(x, f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bs[t * PB + x0 + u] = f[u];
+  }
+  if (tid < C) beta[tid] = tid < nv ? (float)reinterpret_cast<const bf16*>(a.beta)[row0 + (int64_t)tid * a.H] : 0.f;
+  __syncthreads();
+  scan_cols<false>(bs, nullptr, tid);
+  // Qg (into X), Kd, exact q.k
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, x0 = 8 * (e & 15);
+    Vec16 xq = {{0u, 0u, 0u, 0u}}, xk = xq;
+    if (t < nv) {
+      xq = ldg16(q + (row0 + (int64_t)t * a.H) * D + x0);
+      xk = ldg16(k + (row0 + (int64_t)t * a.H) * D + x0);
+    }
+    float fq[8], fk[8];
+    vec_to_f32<bf16>(xq, fq);
+    vec_to_f32<bf16>(xk, fk);
+    bf16x8 qg, kd;
+    float qk = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float bb = bs[t * PB + x0 + u];
+      qg[u] = (bf16)(fq[u] * __expf(bb));
+      kd[u] = (bf16)(fk[u] * __expf(-bb));
+      qk += fq[u] * fk[u];
+    }
+    *reinterpret_cast<bf16x8*>(X + t * P128 + x0) = qg;
+    *reinterpret_cast<bf16x8*>(Kd + t * P128 + x0) = kd;
+    qk = sum16(qk);
+    if ((e & 15) == 0) qkd[t] = qk;
   }
   __syncthreads();
+  // P^T to memory (zero tiles where P is zero); lower tiles from Qg Kd^T
+  for (int e = tid; e < C * C / 4; e += NT) {
+    const int r = e >> 4, c4 = 4 * (e & 15);    // PT row r = t', columns t = c4..c4+3
+    if ((r >> 4) <= (c4 >> 4)) continue;         // written below (P tile (c4/16, r/16) is lower)
+    *reinterpret_cast<bf16x4*>(PTm + r * C + c4) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  }
+  for (int q10 = wave; q10 < 10; q10 += NT / 64) {
+    int I = 0, J = 0;
+    {
+      int cc = 0;
+      for (int x = 0; x < 4; ++x)
+        for (int y = 0; y <= x; ++y) {
+          if (cc == q10) { I = x; J = y; }
+          ++cc;
+        }
+    }
+    floatx4 acc = mm<true, true>(X, P128, Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * I + 4 * g4 + r, s2 = 16 * J + i;
+      acc[r] = t > s2 ? acc[r] : (t == s2 ? qkd[t] : 0.f);
+    }
+    st_tr(PTm, C, 16 * I, 16 * J, acc, lane);
+  }
+  __syncthreads();
+  // Kg (into X)
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, x0 = 8 * (e & 15);
+    Vec16 xk = {{0u, 0u, 0u, 0u}};
+    if (t < nv) xk = ldg16(k + (row0 + (int64_t)t * a.H) * D + x0);
+    float fk[8];
+    vec_to_f32<bf16>(xk, fk);
+    bf16x8 kg;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kg[u] = (bf16)(fk[u] * __expf(bs[t * PB + x0 + u]));
+    *reinterpret_cast<bf16x8*>(X + t * P128 + x0) = kg;
+  }
+  __syncthreads();
+  // L = StrictTril(Diag(beta) Kg Kd^T) (over b: b is dead), then A
+  float* Ls = bs;
+  float* As = bs + C * PF;
+  for (int e = tid; e < C * PF; e += NT) Ls[e] = 0.f;
+  __syncthreads();
+  for (int q10 = wave; q10 < 10; q10 += NT / 64) {
+    int I = 0, J = 0;
+    {
+      int cc = 0;
+      for (int x = 0; x < 4; ++x)
+        for (int y = 0; y <= x; ++y) {
+          if (cc == q10) { I = x; J = y; }
+          ++cc;
+        }
+    }
+    const floatx4 acc = mm<true, true>(X, P128, Kd, P128, 16 * I, 16 * J, D, zero4(), lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * I + 4 * g4 + r, s2 = 16 * J + i;
+      Ls[t * PF + s2] = t > s2 ? acc[r] * beta[t] : 0.f;
+    }
+  }
+  __syncthreads();
+  solve_fp32(Ls, As, tid);
+  for (int e = tid; e < C * C / 4; e += NT) {
+    const int t = e >> 4, s4 = 4 * (e & 15);
+    bf16x4 x;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = (bf16)(s4 + u <= t ? As[t * PF + s4 + u] : 0.f);
+    *reinterpret_cast<bf16x4*>(Am + t * C + s4) = x;
+  }
+}
+
+// A and P^T of a chunk from memory into LDS rows of pitch P64.
+__device__ __forceinline__ void load_mats(const Basics& L, const bf16* Am, int tid) {
+  for (int e = tid; e < 2 * C * 8; e += NT) {
+    const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
+    const Vec16 x = ldg16(Am + m * C * C + r * C + c8);
+    *reinterpret_cast<Vec16*>((m ? L.PT : L.A) + r * P64 + c8) = x;
+  }
 }
 
 // ---------------------------------------------------------------- the chain
@@ -295,16 +427,15 @@ constexpr int O_KD = O_KG + C * P128 * 2;
 constexpr int O_QG = O_KD + C * P128 * 2;
 constexpr int O_A = O_QG + C * P128 * 2;
 constexpr int O_PT = O_A + C * P64 * 2;
-constexpr int O_DO = O_PT + C * P64 * 2;          // dO[:, J] row-major [64][P64]
-constexpr int O_DSG = O_DO + C * P64 * 2;         // (gamma . dS)^T [64 j][P128]
-constexpr int O_DDT = O_DSG + 64 * P128 * 2;      // dDelta^T [64 j][P64]
-constexpr int O_ET = O_DDT + 64 * P64 * 2;        // (A'^T dDelta)^T [64 j][P64]
-constexpr int O_BS = O_ET + 64 * P64 * 2;         // fp32 b [64][PB]; later Ls, As [64][PF] each
-constexpr int SZ_BS = (C * PB > 2 * C * PF ? C * PB : 2 * C * PF) * 4;
+constexpr int O_DO = O_PT + C * P64 * 2;          // dO row-major [64][P128]
+constexpr int O_DSG = O_DO + C * P128 * 2;        // (gamma . dS)^T [128 j][P128]; later E^T [128 j][P64]
+constexpr int O_BS = O_DSG + D * P128 * 2;        // gate scratch; later dDelta^T [128 j][P64]
+constexpr int SZ_BS = (C * PB + 4 * D) * 4;
 constexpr int O_BETA = O_BS + SZ_BS;
 constexpr int O_GAM = O_BETA + C * 4;
 constexpr int O_QK = O_GAM + D * 4;
 constexpr int BYTES = O_QK + C * 4;
+static_assert(D * P64 * 2 <= SZ_BS, "dDelta^T inside the gate scratch");
 static_assert(BYTES <= 160 * 1024, "LDS");
 }  // namespace ch
 
@@ -322,80 +453,78 @@ __device__ __forceinline__ Basics basics(unsigned char* sm, int kg, int kd, int 
   return L;
 }
 
-// One workgroup per (sequence, head, value-column half jh): dS[:, J] in
-// registers (wave w: c tiles 4(w/4) .. +3, j tile w % 4), chunks in reverse.
+// One workgroup per (sequence, head): dS in registers (wave w: value-column
+// tile w, all eight channel tiles), chunks in reverse.
 __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x >> 1, jh = blockIdx.x & 1;
+  const int bh = blockIdx.x;
   if (bh >= a.B * a.H) return;
   const int b = bh / a.H, h = bh % a.H;
   const int N = (a.T + C - 1) / C;
-  const int J0 = 64 * jh;
   const Basics L = basics(sm, ch::O_KG, ch::O_KD, ch::O_QG, ch::O_A, ch::O_PT, ch::O_BETA, ch::O_GAM, ch::O_QK);
   bf16* sDO = reinterpret_cast<bf16*>(sm + ch::O_DO);
   bf16* sDSG = reinterpret_cast<bf16*>(sm + ch::O_DSG);
-  bf16* sDDT = reinterpret_cast<bf16*>(sm + ch::O_DDT);
-  bf16* sET = reinterpret_cast<bf16*>(sm + ch::O_ET);
+  bf16* sET = sDSG;
   float* bs = reinterpret_cast<float*>(sm + ch::O_BS);
-  float* Ls = bs;
-  float* As = bs + C * PF;
+  bf16* sDDT = reinterpret_cast<bf16*>(sm + ch::O_BS);
   const bf16* q = reinterpret_cast<const bf16*>(a.q);
   const bf16* k = reinterpret_cast<const bf16*>(a.k);
   const bf16* g = reinterpret_cast<const bf16*>(a.g);
   const bf16* be = reinterpret_cast<const bf16*>(a.beta);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
 
-  const int ct0 = 4 * (wave >> 2), jt = wave & 3;   // my dS tiles: (ct0 + u, jt)
-  floatx4 dS[4];
+  const int jt = wave;   // my dS tiles: (ct, jt), ct = 0..7
+  floatx4 dS[8];
   const float* dST = a.dS_T ? a.dS_T + (int64_t)bh * D * D : nullptr;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      dS[u][r] = dST ? dST[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] : 0.f;
+    for (int r = 0; r < 4; ++r) dS[u][r] = dST ? dST[(16 * u + 4 * g4 + r) * D + 16 * jt + i] : 0.f;
 
   for (int n = N - 1; n >= 0; --n) {
     Chunk c;
     c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
     c.nv = min(C, a.T - n * C);
     c.rstride = a.H * D;
-    // chunk-end adjoint of this chunk
-    float* adj = a.adjoints + ((int64_t)bh * N + n) * D * D;
+    // chunk-end adjoint of this chunk (bf16, transposed: [j][c])
+    bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u) {
+      bf16x4 x;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) adj[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] = dS[u][r];
+      for (int r = 0; r < 4; ++r) x[r] = (bf16)dS[u][r];
+      *reinterpret_cast<bf16x4*>(adj + (16 * jt + i) * D + 16 * u + 4 * g4) = x;
+    }
+    load_mats(L, chunk_mats(a, bh, N, n), tid);
     chunk_gates(L, bs, q, k, g, be, c, a.H, tid);
-    chunk_gram(L, Ls, tid);
-    chunk_solve(L, Ls, As, tid);
-    // dO[:, J] (rows past nv zero) and (gamma . dS)^T
-    for (int e = tid; e < C * 8; e += NT) {
-      const int t = e >> 3, c0 = 8 * (e & 7);
+    // dO (rows past nv zero) and (gamma . dS)^T
+    for (int e = tid; e < C * 16; e += NT) {
+      const int t = e >> 4, c0 = 8 * (e & 15);
       Vec16 x = {{0u, 0u, 0u, 0u}};
-      if (t < c.nv) x = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + J0 + c0);
-      *reinterpret_cast<Vec16*>(sDO + t * P64 + c0) = x;
+      if (t < c.nv) x = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + c0);
+      *reinterpret_cast<Vec16*>(sDO + t * P128 + c0) = x;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       floatx4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * (ct0 + u) + 4 * g4 + r];
-      st_tr(sDSG, P128, 16 * (ct0 + u), 16 * jt, v, lane);
+      for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * u + 4 * g4 + r];
+      st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
     }
     __syncthreads();
-    // dDelta[:, J] = P^T dO + Kd (gamma . dS), stored transposed
-    for (int tile = wave; tile < 16; tile += NT / 64) {
-      const int tt = tile >> 2, jj = tile & 3;
-      floatx4 acc = mm<true, false>(L.PT, P64, sDO, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+    // dDelta = P^T dO + Kd (gamma . dS), stored transposed (over the gate scratch)
+    for (int tile = wave; tile < 32; tile += NT / 64) {
+      const int tt = tile >> 3, jj = tile & 7;
+      floatx4 acc = mm<true, false>(L.PT, P64, sDO, P128, 16 * tt, 16 * jj, C, zero4(), lane);
       acc = mm<true, true>(L.Kd, P128, sDSG, P128, 16 * tt, 16 * jj, D, acc, lane);
       st_tr(sDDT, P64, 16 * tt, 16 * jj, acc, lane);
     }
     __syncthreads();
-    // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed
-    for (int tile = wave; tile < 16; tile += NT / 64) {
-      const int tt = tile >> 2, jj = tile & 3;
+    // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed (over (gamma . dS)^T)
+    for (int tile = wave; tile < 32; tile += NT / 64) {
+      const int tt = tile >> 3, jj = tile & 7;
       floatx4 acc = mm<false, true>(L.A, P64, sDDT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= L.beta[16 * tt + 4 * g4 + r];
@@ -404,21 +533,20 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     __syncthreads();
     // dS <- gamma . dS + Qg^T dO - Kg^T E
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ct = ct0 + u;
-      floatx4 p = mm<false, false>(L.Qg, P128, sDO, P64, 16 * ct, 16 * jt, C, zero4(), lane);
-      floatx4 m = mm<false, true>(L.Kg, P128, sET, P64, 16 * ct, 16 * jt, C, zero4(), lane);
+    for (int u = 0; u < 8; ++u) {
+      floatx4 p = mm<false, false>(L.Qg, P128, sDO, P128, 16 * u, 16 * jt, C, zero4(), lane);
+      floatx4 m = mm<false, true>(L.Kg, P128, sET, P64, 16 * u, 16 * jt, C, zero4(), lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * ct + 4 * g4 + r] * dS[u][r] + p[r] - m[r];
+      for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * u + 4 * g4 + r] * dS[u][r] + p[r] - m[r];
     }
     __syncthreads();
   }
   if (a.dS0) {
     float* out = a.dS0 + (int64_t)bh * D * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(16 * (ct0 + u) + 4 * g4 + r) * D + J0 + 16 * jt + i] = dS[u][r];
+      for (int r = 0; r < 4; ++r) out[(16 * u + 4 * g4 + r) * D + 16 * jt + i] = dS[u][r];
   }
 }
 
@@ -432,7 +560,7 @@ constexpr int O_PT = O_A + C * P64 * 2;
 constexpr int O_BETA = O_PT + C * P64 * 2;
 constexpr int O_GAM = O_BETA + C * 4;
 constexpr int O_QK = O_GAM + D * 4;
-constexpr int O_DGAM = O_QK + C * 4;          // rowsum(dS . S), [128]
+constexpr int O_DGAM = O_QK + C * 4;          // gamma . rowsum(dS . S), [128]
 constexpr int O_MD = O_DGAM + D * 4;          // diagonal of M, [64]
 constexpr int O_DB = O_MD + C * 4;            // dbeta partial sums [8 waves][64]
 constexpr int O_WORK = O_DB + 8 * C * 4;      // phase-dependent area
@@ -453,11 +581,14 @@ constexpr int Q_Z1T = Q_DA + C * P64 * 2;      // (dA A^T)^T [64][P64]
 constexpr int Q_DL = Q_Z1T + C * P64 * 2;      // dL [64][P64]
 constexpr int Q_DG = Q_DL + C * P64 * 2;       // Diag(beta) dL [64][P64]
 constexpr int Q_END = Q_DG + C * P64 * 2;
-constexpr int Z_DB = 0;                        // db fp32 [64][PB] (assembly)
+constexpr int Z_DB = 0;                        // db fp32 [64][PB] + scan scratch (assembly)
+constexpr int Z_Q = (C * PB + 4 * D) * 4;      // q, then dq, bf16 [64][P128]
+constexpr int Z_K = Z_Q + C * P128 * 2;        // k, then dk
+constexpr int Z_END = Z_K + C * P128 * 2;
 constexpr int BYTES = O_WORK + (H_END > Q_END ? H_END : Q_END);
-static_assert(C * PB * 4 <= H_END, "gate scratch inside the work area");
-static_assert(2 * C * PF * 4 <= H_END, "solver scratch inside the work area");
+static_assert((C * PB + 4 * D) * 4 <= H_END, "gate scratch inside the work area");
 static_assert(Q_END <= H_END, "after-halves buffers inside the work area");
+static_assert(Z_END <= H_END, "assembly buffers inside the work area");
 static_assert(BYTES <= 160 * 1024, "LDS");
 }  // namespace gr
 
@@ -487,16 +618,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
   c.nv = min(C, a.T - n * C);
   c.rstride = a.H * D;
-  const float* Sn = a.states + ((int64_t)bh * N + n) * D * D;
-  const float* dSn = a.adjoints + ((int64_t)bh * N + n) * D * D;
+  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // [j][c]
+  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // [j][c]
 
-  {
-    float* bs = reinterpret_cast<float*>(work);
-    chunk_gates(L, bs, q, k, g, be, c, a.H, tid);
-    float* Ls = reinterpret_cast<float*>(work);
-    chunk_gram(L, Ls, tid);
-    chunk_solve(L, Ls, Ls + C * PF, tid);
-  }
+  load_mats(L, chunk_mats(a, bh, N, n), tid);
+  chunk_gates(L, reinterpret_cast<float*>(work), q, k, g, be, c, a.H, tid);
   for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
   if (tid < D) dgam[tid] = 0.f;
 
@@ -524,28 +650,28 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* hD = reinterpret_cast<bf16*>(work + gr::H_D);
   bf16* hDD = reinterpret_cast<bf16*>(work + gr::H_DD);
   bf16* hXT = reinterpret_cast<bf16*>(work + gr::H_XT);
-  float dgp = 0.f;   // rowsum(dS . S) partial of row tid / 4 (tid < 512: rows 0..127)
+  float dgp = 0.f;   // gamma . rowsum(dS . S) partial of column tid (tid < 128)
 
   for (int jh = 0; jh < 2; ++jh) {
     const int J0 = 64 * jh;
     __syncthreads();
-    // S[:, J], gamma . dS[:, J]: thread -> row c = tid / 4, 16 columns
+    // S[:, J] and gamma . dS[:, J] into [c][j] from the transposed [j][c]
+    // copies: thread -> value column j = tid / 8, channels 16 (tid % 8) .. + 16
     {
-      const int cr = tid >> 2, cc = 16 * (tid & 3);
-      const float gm = L.gam[cr];
+      const int jr = tid >> 3, cc = 16 * (tid & 7);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const floatx4 s = *reinterpret_cast<const floatx4*>(Sn + cr * D + J0 + cc + 4 * u);
-        const floatx4 d = *reinterpret_cast<const floatx4*>(dSn + cr * D + J0 + cc + 4 * u);
-        bf16x4 sb, db;
+      for (int u = 0; u < 2; ++u) {
+        const Vec16 xs = ldg16(Sn + (J0 + jr) * D + cc + 8 * u);
+        const Vec16 xd = ldg16(dSn + (J0 + jr) * D + cc + 8 * u);
+        float fs[8], fd[8];
+        vec_to_f32<bf16>(xs, fs);
+        vec_to_f32<bf16>(xd, fd);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dgp += s[r] * d[r];
-          sb[r] = (bf16)s[r];
-          db[r] = (bf16)(gm * d[r]);
+        for (int e = 0; e < 8; ++e) {
+          const int cr = cc + 8 * u + e;
+          hS[cr * P64 + jr] = (bf16)fs[e];
+          hDSG[cr * P64 + jr] = (bf16)(L.gam[cr] * fd[e]);
         }
-        *reinterpret_cast<bf16x4*>(hS + cr * P64 + cc + 4 * u) = sb;
-        *reinterpret_cast<bf16x4*>(hDSG + cr * P64 + cc + 4 * u) = db;
       }
     }
     // V[:, J], dO[:, J]
@@ -560,6 +686,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       *reinterpret_cast<Vec16*>(hDO + t * P64 + x0) = xo;
     }
     __syncthreads();
+    // gamma . rowsum(dS . S) over this half (from the rounded copies)
+    if (tid < D) {
+#pragma unroll 4
+      for (int j = 0; j < 64; j += 4) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hS + tid * P64 + j);
+        const bf16x4 y = *reinterpret_cast<const bf16x4*>(hDSG + tid * P64 + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dgp += (float)x[e] * (float)y[e];
+      }
+    }
     // X = beta . (V - Kg S), stored transposed
     for (int tile = wave; tile < 16; tile += NT / 64) {
       const int tt = tile >> 2, jj = tile & 3;
@@ -588,6 +724,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       aQg[u] = mm<true, true>(hDO, P64, hS, P64, 16 * u, c0, 64, aQg[u], lane);    // dO S^T
       aKb[u] = mm<true, true>(hD, P64, hDSG, P64, 16 * u, c0, 64, aKb[u], lane);   // Delta (g.dS)^T
       aW[u] = mm<true, true>(hDD, P64, hS, P64, 16 * u, c0, 64, aW[u], lane);      // dDelta S^T
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands in flight at a time
     }
     // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
 #pragma unroll
@@ -600,24 +737,38 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
         aA[x] = mm<true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
       }
     }
-    // dV[:, J] = Diag(beta) A^T dDelta -> output; dbeta += rowsum((A^T dDelta) . V)
+    // dV[:, J] = Diag(beta) A^T dDelta, staged row-major where X^T was (dead
+    // since Delta); dbeta += rowsum((A^T dDelta) . V)
     for (int tile = wave; tile < 16; tile += NT / 64) {
       const int tt = tile >> 2, jj = tile & 3;
-      const floatx4 x = mm<false, false>(L.A, P64, hDD, P64, 16 * tt, 16 * jj, C, zero4(), lane);
-      bf16* dv = reinterpret_cast<bf16*>(a.dv);
+      floatx4 x = mm<false, false>(L.A, P64, hDD, P64, 16 * tt, 16 * jj, C, zero4(), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * g4 + r;
-        if (t < c.nv) dv[(c.row0 + (int64_t)t * a.H) * D + J0 + 16 * jj + i] = (bf16)(L.beta[t] * x[r]);
         const float p = sum16(x[r] * (float)hV[t * P64 + 16 * jj + i]);
         if (i == 0) dbp[wave * C + t] += p;
+        x[r] *= L.beta[t];
       }
+      st_rm(hXT, P64, 16 * tt, 16 * jj, x, lane);
+    }
+    __syncthreads();
+    {
+      const int t = tid >> 3, x0 = 8 * (tid & 7);
+      if (t < c.nv)
+        *reinterpret_cast<Vec16*>(reinterpret_cast<bf16*>(a.dv) + (c.row0 + (int64_t)t * a.H) * D + J0 + x0) =
+            *reinterpret_cast<const Vec16*>(hXT + t * P64 + x0);
     }
   }
-  // rowsum(dS . S): 4 threads per row
-  dgp += __shfl_xor(dgp, 1);
-  dgp += __shfl_xor(dgp, 2);
-  if ((tid & 3) == 0) dgam[tid >> 2] = dgp;
+  if (tid < D) dgam[tid] = dgp;
+  // fold dKb~ into dKd, keeping its column sums against Kd (chunk-end terms)
+  float colsum = 0.f;   // sum over my rows of Kd . dKb~ for column c0 + i
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      colsum += (float)L.Kd[(16 * u + 4 * g4 + r) * P128 + c0 + i] * aKb[u][r];
+      aKd[u][r] += aKb[u][r];
+    }
   __syncthreads();   // the half-loop buffers are dead from here
 
   bf16* qDW = reinterpret_cast<bf16*>(work + gr::Q_DW);
@@ -738,31 +889,31 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   }
   __syncthreads();   // the work area becomes the db array
 
-  // assembly: gate factors from b (recomputed), raw q, k
+  // assembly: gate factors from b (recomputed), raw q and k staged in LDS;
+  // dq and dk replace q and k there (each element read, then written, by the
+  // same lane) and leave with row-wide stores
   float* bs = reinterpret_cast<float*>(work + gr::Z_DB);
+  bf16* zq = reinterpret_cast<bf16*>(work + gr::Z_Q);
+  bf16* zk = reinterpret_cast<bf16*>(work + gr::Z_K);
   for (int e = tid; e < C * 16; e += NT) {
     const int t = e >> 4, x0 = 8 * (e & 15);
-    Vec16 x = {{0u, 0u, 0u, 0u}};
-    if (t < c.nv) x = ldg16(g + (c.row0 + (int64_t)t * a.H) * D + x0);
+    Vec16 x = {{0u, 0u, 0u, 0u}}, xq = x, xk = x;
+    if (t < c.nv) {
+      const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
+      x = ldg16(g + off);
+      xq = ldg16(q + off);
+      xk = ldg16(k + off);
+    }
     float f[8];
     vec_to_f32<bf16>(x, f);
 #pragma unroll
     for (int uu = 0; uu < 8; ++uu) bs[t * PB + x0 + uu] = f[uu];
+    *reinterpret_cast<Vec16*>(zq + t * P128 + x0) = xq;
+    *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = xk;
   }
   __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-    for (int t = 0; t < C; ++t) {
-      s += bs[t * PB + tid];
-      bs[t * PB + tid] = s;
-    }
-  }
-  __syncthreads();
-  // per element: dq, dk and db (db overwrites b in place, each element read
-  // before it is written by the same lane)
-  float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // sum_t Kd . dKb~ for column c0 + i (per lane, 4 row groups)
-  bf16* dq = reinterpret_cast<bf16*>(a.dq);
-  bf16* dk = reinterpret_cast<bf16*>(a.dk);
+  scan_cols<false>(bs, nullptr, tid);
+  // per element: dq, dk and db (db overwrites b in place)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -770,41 +921,35 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       const int t = 16 * u + 4 * g4 + r, cc = c0 + i;
       const float bb = bs[t * PB + cc];
       const float ep = __expf(bb), em = __expf(-bb);
-      float qv = 0.f, kv = 0.f;
-      if (t < c.nv) {
-        qv = (float)q[(c.row0 + (int64_t)t * a.H) * D + cc];
-        kv = (float)k[(c.row0 + (int64_t)t * a.H) * D + cc];
-      }
+      const float qv = (float)zq[t * P128 + cc], kv = (float)zk[t * P128 + cc];
       const float kg = kv * ep, kd = kv * em, qg = qv * ep;
-      const float dkd = aKd[u][r] + aKb[u][r];
-      const float dqv = ep * aQg[u][r] + md[t] * kv;
-      const float dkv = ep * aKg[u][r] + em * dkd + md[t] * qv;
-      if (t < c.nv) {
-        dq[(c.row0 + (int64_t)t * a.H) * D + cc] = (bf16)dqv;
-        dk[(c.row0 + (int64_t)t * a.H) * D + cc] = (bf16)dkv;
-      }
-      colsum[0] += kd * aKb[u][r];
+      const float dkd = aKd[u][r];
+      zq[t * P128 + cc] = (bf16)(ep * aQg[u][r] + md[t] * kv);
+      zk[t * P128 + cc] = (bf16)(ep * aKg[u][r] + em * dkd + md[t] * qv);
       bs[t * PB + cc] = kg * aKg[u][r] - kd * dkd + qg * aQg[u][r];
     }
   }
-  // chunk-end terms at row 63: sum over t of Kd . dKb~ (across the 4 row groups) + gamma . dgam
-  {
-    float s = colsum[0];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (g4 == 0) {
-      const int cc = c0 + i;
-      bs[(C - 1) * PB + cc] += s + L.gam[cc] * dgam[cc];
-    }
-  }
+  // chunk-end terms at row 63: sum over t of Kd . dKb~ (across the 4 row
+  // groups) + gamma . rowsum(dS . S)
+  colsum += __shfl_xor(colsum, 16);
+  colsum += __shfl_xor(colsum, 32);
+  if (g4 == 0) bs[(C - 1) * PB + c0 + i] += colsum + dgam[c0 + i];
   __syncthreads();
   // dg = reverse cumulative sum of db over the chunk's rows
+  scan_cols<true>(bs, nullptr, tid);
+  bf16* dq = reinterpret_cast<bf16*>(a.dq);
+  bf16* dk = reinterpret_cast<bf16*>(a.dk);
   bf16* dgo = reinterpret_cast<bf16*>(a.dg);
-  if (tid < D) {
-    float s = 0.f;
-    for (int t = C - 1; t >= 0; --t) {
-      s += bs[t * PB + tid];
-      if (t < c.nv) dgo[(c.row0 + (int64_t)t * a.H) * D + tid] = (bf16)s;
+  for (int e = tid; e < C * 16; e += NT) {
+    const int t = e >> 4, x0 = 8 * (e & 15);
+    if (t < c.nv) {
+      const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
+      *reinterpret_cast<Vec16*>(dq + off) = *reinterpret_cast<const Vec16*>(zq + t * P128 + x0);
+      *reinterpret_cast<Vec16*>(dk + off) = *reinterpret_cast<const Vec16*>(zk + t * P128 + x0);
+      bf16x8 y;
+#pragma unroll
+      for (int uu = 0; uu < 8; ++uu) y[uu] = (bf16)bs[t * PB + x0 + uu];
+      *reinterpret_cast<bf16x8*>(dgo + off) = y;
     }
   }
   if (tid < C && tid < c.nv) {
@@ -818,7 +963,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 
 size_t backward_workspace(int BH, int T) {
   const size_t N = ((size_t)T + bwd::C - 1) / bwd::C;
-  return 2 * (size_t)BH * N * bwd::D * bwd::D * sizeof(float);
+  return (size_t)BH * N * (2 * bwd::D * bwd::D + 2 * bwd::C * bwd::C) * sizeof(bf16);
 }
 
 template <typename K>
@@ -839,12 +984,18 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     f.states = a.states;
     if ((e = launch_fused(f, s)) != hipSuccess) return e;
   }
-  // 2. adjoint recursion (also writes dS0; with T = 0 it copies dS_T)
+  // 2. per-chunk A and P^T
+  if (N > 0) {
+    if ((e = set_lds(bwd::bwd_prep_kernel, bwd::pr::BYTES)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd::bwd_prep_kernel, dim3(BH * N), dim3(bwd::NT), bwd::pr::BYTES, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 3. adjoint recursion (also writes dS0; with T = 0 it copies dS_T)
   if ((e = set_lds(bwd::bwd_chain_kernel, bwd::ch::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd::bwd_chain_kernel, dim3(2 * BH), dim3(bwd::NT), bwd::ch::BYTES, s, a);
+  hipLaunchKernelGGL(bwd::bwd_chain_kernel, dim3(BH), dim3(bwd::NT), bwd::ch::BYTES, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (N == 0) return hipSuccess;
-  // 3. per-chunk gradients
+  // 4. per-chunk gradients
   if ((e = set_lds(bwd::bwd_grad_kernel, bwd::gr::BYTES)) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd::bwd_grad_kernel, dim3(BH * N), dim3(bwd::NT), bwd::gr::BYTES, s, a);
   return hipGetLastError();

@@ -28,8 +28,8 @@ struct PrefillArgs {
   const int* cu_seqlens;
   const int* seq_order;   // packed sequences: processing order (a permutation of 0..B-1), or NULL
   // Chunk-entry states (one pass, no outputs): state at the start of every
-  // chunk, fp32 [B*H][ceil(T/64)][dk][dv]; NULL: normal forward.
-  float* states;
+  // chunk, bf16 and transposed, [B*H][ceil(T/64)][dv][dk]; NULL: normal forward.
+  void* states;
 };
 
 struct StageArgs {
@@ -54,8 +54,9 @@ struct BackwardArgs {
   const float* S0; const void* dO; const float* dS_T;
   void* dq; void* dk; void* dv; void* dg; void* dbeta; float* dS0;
   int B, T, H;
-  float* states;    // [B*H][N][128][128] chunk-entry states
-  float* adjoints;  // [B*H][N][128][128] adjoints of the chunk-end states
+  void* states;     // bf16 [B*H][N][d_v][d_k] chunk-entry states, transposed
+  void* adjoints;   // bf16 [B*H][N][d_v][d_k] adjoints of the chunk-end states, transposed
+  void* mats;       // bf16 [B*H][N][2][64][64]: A = (I + L)^-1 and P^T of each chunk
 };
 size_t backward_workspace(int BH, int T);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);

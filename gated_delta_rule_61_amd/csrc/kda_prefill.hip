@@ -1421,6 +1421,21 @@ __device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], fl
       for (int j = 0; j < 4; ++j) out[(16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
 }
 
+// The same tiles as bf16 into a transposed [d_v][d_k] matrix: a lane's four
+// rows of one column are contiguous there (one 8-byte store each).
+__device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], bf16* out, int col0, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt) {
+      bf16x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = (bf16)S[nt][rt][j];
+      *reinterpret_cast<bf16x4*>(out + (col0 + vcol(nt, l16)) * DK + 16 * rt + 4 * g4) = x;
+    }
+}
+
 // Workspace matrix (fp32 [d_k][d_v]) of the segmented schedule: for sequence /
 // head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N.
 __device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int s, int kind) {
@@ -2184,7 +2199,9 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
               make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
           owner_store(O, ro, a.H * DV, col0, lane);
         }
-        if (a.states) store_state_v(S, a.states + ((int64_t)head * ((a.T + C - 1) / C) + c0 + n) * DK * DV, col0, lane);
+        if (a.states)
+          store_state_t(S, reinterpret_cast<bf16*>(a.states) + ((int64_t)head * ((a.T + C - 1) / C) + c0 + n) * DK * DV,
+                        col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
       // V^T of chunk n+1 (U is formed in phase 3)

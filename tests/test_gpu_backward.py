@@ -119,17 +119,17 @@ def test_small_shapes(kda, B, T, H, s0, dst):
 
 
 def test_chunk_states_and_adjoints(kda):
-    """The workspace's chunk-entry states and chunk-end adjoints against the
-    oracle's forward states and per-chunk adjoints (fp32, same bounds)."""
+    """The workspace's chunk-entry states and chunk-end adjoints (bf16, stored
+    transposed) against the oracle's forward states and per-chunk adjoints."""
     B, T, H = 1, 200, 2
     inp = _inputs(B, T, H, 77)
     N = (T + 63) // 64
-    ws = torch.zeros(kda.lib().kda_chunk_bwd_workspace_size(B, T, H, 128, 128, 1) // 4, dtype=torch.float32,
+    ws = torch.zeros(kda.lib().kda_chunk_bwd_workspace_size(B, T, H, 128, 128, 1) // 2, dtype=torch.bfloat16,
                      device="cuda")
     _run(kda, inp, workspace=ws)
-    half = ws.numel() // 2
-    states = ws[:half].view(B * H, N, 128, 128)
-    adj = ws[half:].view(B * H, N, 128, 128)
+    nst = B * H * N * 128 * 128          # states, then adjoints, then per-chunk 64 x 64 matrices
+    states = ws[:nst].view(B * H, N, 128, 128).transpose(-1, -2)
+    adj = ws[nst:2 * nst].view(B * H, N, 128, 128).transpose(-1, -2)
     ref = _oracle(inp, chunk_adjoints=True)["dS_chunks"]          # [B,H,N,dk,dv], adjoint at chunk start
     for bh in range(B * H):
         b, h = divmod(bh, H)
