@@ -1797,67 +1797,78 @@ __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[N
 }
 
 // Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32.
-// Lane c = l16 computes column c of D_I by forward substitution (the four
-// 16-lane groups repeat the same work); lane group g then holds entries
-// 4g..4g+3 of that column, i.e. D_I in MFMA accumulator layout.  The rows of
-// D_I come from a product with the identity (an MFMA whose A operand is read
-// from an accumulator tile multiplies by that tile's transpose), taken on a
-// two-term fp16 split so the transposed values keep fp32 accuracy.  Writes
-// D_I, D_I^T and block (I, I) of A' = D_I Diag(beta), 8 bytes per lane.
+// With N = -L_II (strictly lower, N^16 = 0), D_I = (I + N)(I + N^2)(I + N^4)
+// (I + N^8): three squarings and three products on fp32 MFMA instead of a
+// 15-step substitution.  Every factor is kept in accumulator layout together
+// with its transpose: the accumulator tile of X^T is exactly the A-operand
+// fragment of X (lane (g, i): X[i][4g..4g+3]), and the tile of X is the
+// B-operand fragment, so X Y needs tiles of X^T and Y, and (X Y)^T = Y^T X^T
+// tiles of Y and X^T.  D_I and D_I^T come out in accumulator layout: D_I^T's
+// tile is D_I by rows.  Writes D_I, D_I^T and block (I, I) of A' = D_I Diag(beta),
+// 8 bytes per lane.
 __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
+  typedef Mma<float> MF;
+  floatx4 n, nt;   // N and N^T tiles
   {
-    const bool kq[1] = {false};
-    const int II[1] = {I};
-    floatx4 acc[1];
-    kh_tiles<1, false>(p, kq, II, II, acc, lane);
+    const int fl = frag_lane(lane);
+    MB::F32 af[DK / 32], bf[DK / 32];
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      af[ks] = ldc_b(p.Kt + fl + frag_off(I, ks));
+      bf[ks] = ldc_b(p.Kh + fl + frag_off(I, ks));
+    }
+    KDA_READS_FIRST();
+    floatx4 x = {0.f, 0.f, 0.f, 0.f}, xt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      x = MB::mma32(af[ks], bf[ks], x);     // lane: (Kt Kh^T)[4g + jj][l16]
+      xt = MB::mma32(bf[ks], af[ks], xt);   // lane: (Kt Kh^T)[l16][4g + jj]
+    }
     const floatx4 bt = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4 * g4);
+    const float bl = p.beta[16 * I + l16];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[0][jj] = (4 * g4 + jj > l16) ? acc[0][jj] * bt[jj] : 0.f;
-    // L_II^T row l16 = column l16 of L_II (same wavefront reads it back: LDS order suffices)
-    *reinterpret_cast<floatx4*>(p.LdT + (I * 16 + l16) * LDL + 4 * g4) = acc[0];
-  }
-  const int c = l16;
-  const float* Lt = p.LdT + I * 16 * LDL;
-  // x = column c of D_I: forward substitution, column by column of L
-  // (row mm of L^T holds column mm of L; entries 4q4..4q4+3, q4 >= (mm+1)/4)
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-  for (int mm = 0; mm < 15; ++mm) {
-#pragma unroll
-    for (int q4 = (mm + 1) / 4; q4 < 4; ++q4) {
-      const floatx4 col = *reinterpret_cast<const floatx4*>(Lt + mm * LDL + 4 * q4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (4 * q4 + u > mm) x[4 * q4 + u] -= col[u] * x[mm];
+    for (int jj = 0; jj < 4; ++jj) {
+      n[jj] = (4 * g4 + jj > l16) ? -x[jj] * bt[jj] : 0.f;
+      nt[jj] = (l16 > 4 * g4 + jj) ? -xt[jj] * bl : 0.f;
     }
   }
-  // entries 4g..4g+3 of the column: D_I in accumulator layout
-  floatx4 dc;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    dc[jj] = g4 == 0 ? x[jj] : g4 == 1 ? x[4 + jj] : g4 == 2 ? x[8 + jj] : x[12 + jj];
-  MH::F16 dh, dl, eye;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    dh[jj] = (f16)dc[jj];
-    dl[jj] = (f16)(dc[jj] - (float)dh[jj]);
-    eye[jj] = (f16)(4 * g4 + jj == l16 ? 1.f : 0.f);
-  }
-  // D_I^T row c = column c of D_I, entries 4g..4g+3
-  *reinterpret_cast<f16x4*>(p.Dt + (I * 16 + c) * LDB + 4 * g4) = dh;
-  // lane (g, c): D_I[c][4g..4g+3]
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  const floatx4 dr = MH::mma16(dh, eye, MH::mma16(dl, eye, z));
+  floatx4 eye;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) eye[jj] = (4 * g4 + jj == l16) ? 1.f : 0.f;
+  // powers
+  const floatx4 n2 = MF::mma16(nt, n, z), n2t = MF::mma16(n, nt, z);
+  const floatx4 n4 = MF::mma16(n2t, n2, z), n4t = MF::mma16(n2, n2t, z);
+  const floatx4 n8 = MF::mma16(n4t, n4, z), n8t = MF::mma16(n4, n4t, z);
+  // D = D1 (I + N^2)(I + N^4)(I + N^8), D1 = I + N; D_k+1 = D_k + D_k M, D_k+1^T = D_k^T + M^T D_k^T
+  floatx4 d = eye + n, dt = eye + nt;
+  {
+    const floatx4 e = MF::mma16(dt, n2, d), et = MF::mma16(n2, dt, dt);
+    d = e;
+    dt = et;
+  }
+  {
+    const floatx4 e = MF::mma16(dt, n4, d), et = MF::mma16(n4, dt, dt);
+    d = e;
+    dt = et;
+  }
+  {
+    const floatx4 e = MF::mma16(dt, n8, d), et = MF::mma16(n8, dt, dt);
+    d = e;
+    dt = et;
+  }
+  // d: lane (g, c) = D[4g + jj][c] -> D^T row c; dt: lane (g, c) = D[c][4g + jj] -> D row c
+  const int c = l16;
   const floatx4 bt = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4 * g4);
-  f16x4 drow, arow;
+  f16x4 dcol, drow, arow;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    drow[jj] = (f16)dr[jj];
-    arow[jj] = (f16)(dr[jj] * bt[jj]);
+    dcol[jj] = (f16)d[jj];
+    drow[jj] = (f16)dt[jj];
+    arow[jj] = (f16)(dt[jj] * bt[jj]);
   }
+  *reinterpret_cast<f16x4*>(p.Dt + (I * 16 + c) * LDB + 4 * g4) = dcol;
   *reinterpret_cast<f16x4*>(p.D + (I * 16 + c) * LDB + 4 * g4) = drow;
   // row 16I + c of A', columns 16I + 4g .. 16I + 4g + 3
   *reinterpret_cast<f16x4*>(p.A + (16 * I + c) * LDT + 16 * I + 4 * g4) = arow;
