@@ -2220,6 +2220,13 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
       if (!ND && nxt) solver_block(p, o, lane);
+      // with outputs the workers form the P blocks and two of the L blocks;
+      // each owner forms one of the other four (L(1,0), L(3,2), L(3,1), L(3,0))
+      if (!ND && nxt && outp) {
+        const bool q[1] = {false};
+        const int I1[1] = {o == 0 ? 1 : 3}, J1[1] = {o == 0 ? 0 : o == 1 ? 2 : o == 2 ? 1 : 0};
+        lp_block_tiles<1>(p, q, I1, J1, lane);
+      }
       // values of chunk n+2: unconditional (zeros past the end), and after the
       // role switch -- loads issued just before such a switch were seen to
       // leave one wavefront's copy of the loaded registers wrong
@@ -2274,9 +2281,9 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 2a: Kt^T, Kb^T; P blocks and the off-diagonal blocks of L, four
-      // each (state-only runs: the L blocks alone; no delta rule: the P blocks
-      // alone)
+      // phase 2a: Kt^T, Kb^T; the ten P blocks and two off-diagonal blocks of
+      // L, three each (the owners form the other four L blocks; state-only
+      // runs: the six L blocks alone; no delta rule: the P blocks alone)
       if (ND && nxt && outp) {
         worker_kbt<V>(p, kb, kt_t, w, lane);
         switch (w) {
@@ -2306,14 +2313,14 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       } else if (nxt) {
         worker_kbt<V>(p, kb, kt_t, w, lane);
         switch (w) {
-          case 0: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {0, 3, 3, 1}, J[4] = {0, 0, 3, 0};
-                    lp_block_tiles<4>(p, q, I, J, lane); break; }
-          case 1: { const bool q[4] = {1, 1, 1, 0}; const int I[4] = {1, 1, 3, 3}, J[4] = {0, 1, 1, 2};
-                    lp_block_tiles<4>(p, q, I, J, lane); break; }
-          case 2: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 2, 2, 3}, J[4] = {0, 1, 0, 1};
-                    lp_block_tiles<4>(p, q, I, J, lane); break; }
-          default: { const bool q[4] = {1, 1, 0, 0}; const int I[4] = {2, 3, 2, 3}, J[4] = {2, 2, 1, 0};
-                     lp_block_tiles<4>(p, q, I, J, lane); break; }
+          case 0: { const bool q[3] = {1, 1, 1}; const int I[3] = {0, 3, 3}, J[3] = {0, 0, 3};
+                    lp_block_tiles<3>(p, q, I, J, lane); break; }
+          case 1: { const bool q[3] = {1, 1, 1}; const int I[3] = {1, 1, 3}, J[3] = {0, 1, 1};
+                    lp_block_tiles<3>(p, q, I, J, lane); break; }
+          case 2: { const bool q[3] = {1, 1, 0}; const int I[3] = {2, 2, 2}, J[3] = {0, 1, 0};
+                    lp_block_tiles<3>(p, q, I, J, lane); break; }
+          default: { const bool q[3] = {1, 1, 0}; const int I[3] = {2, 3, 2}, J[3] = {2, 2, 1};
+                     lp_block_tiles<3>(p, q, I, J, lane); break; }
         }
       }
       p.sync(smem_raw);
