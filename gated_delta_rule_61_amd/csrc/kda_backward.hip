@@ -276,8 +276,15 @@ constexpr int BYTES = O_QK + C * 4;
 static_assert(BYTES <= 80 * 1024, "two workgroups per compute unit");
 }  // namespace pr
 
+// Per-chunk block of the workspace (bf16 element offsets): A, P^T (64 x 64),
+// the gated operands Kg, Kd, Qg (64 x 128, row-major) and gamma (fp32 [128]).
+constexpr int M_A = 0, M_PT = C * C, M_KG = 2 * C * C, M_KD = M_KG + C * D, M_QG = M_KD + C * D;
+constexpr int M_GAM = M_QG + C * D;
+constexpr int MATS = M_GAM + 2 * D;
+static_assert((MATS * 2) % 16 == 0, "16-byte aligned blocks");
+
 __device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t bh, int N, int n) {
-  return reinterpret_cast<bf16*>(a.mats) + ((bh * N + n) * 2) * (int64_t)(C * C);
+  return reinterpret_cast<bf16*>(a.mats) + (bh * N + n) * (int64_t)MATS;
 }
 
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   const int64_t row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
   const int nv = min(C, a.T - n * C);
   bf16* Am = chunk_mats(a, bh, N, n);
-  bf16* PTm = Am + C * C;
+  bf16* PTm = Am + M_PT;
 
   for (int e = tid; e < C * 16; e += NT) {
     const int t = e >> 4, x0 = 8 * (e & 15);
@@ -335,9 +342,12 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
     }
     *reinterpret_cast<bf16x8*>(X + t * P128 + x0) = qg;
     *reinterpret_cast<bf16x8*>(Kd + t * P128 + x0) = kd;
+    *reinterpret_cast<bf16x8*>(Am + M_QG + t * D + x0) = qg;
+    *reinterpret_cast<bf16x8*>(Am + M_KD + t * D + x0) = kd;
     qk = sum16(qk);
     if ((e & 15) == 0) qkd[t] = qk;
   }
+  if (tid < D) reinterpret_cast<float*>(Am + M_GAM)[tid] = __expf(bs[(C - 1) * PB + tid]);
   __syncthreads();
   // P^T to memory (zero tiles where P is zero); lower tiles from Qg Kd^T
   for (int e = tid; e < C * C / 4; e += NT) {
@@ -375,6 +385,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) kg[u] = (bf16)(fk[u] * __expf(bs[t * PB + x0 + u]));
     *reinterpret_cast<bf16x8*>(X + t * P128 + x0) = kg;
+    *reinterpret_cast<bf16x8*>(Am + M_KG + t * D + x0) = kg;
   }
   __syncthreads();
   // L = StrictTril(Diag(beta) Kg Kd^T) (over b: b is dead), then A
@@ -410,13 +421,23 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   }
 }
 
-// A and P^T of a chunk from memory into LDS rows of pitch P64.
-__device__ __forceinline__ void load_mats(const Basics& L, const bf16* Am, int tid) {
+// A chunk's block from the workspace into LDS (A and P^T in rows of P64,
+// Kg Kd Qg in rows of P128, gamma) and its beta from the input (zero past nv).
+__device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, const bf16* beta, const Chunk& c,
+                                           int H, int tid) {
   for (int e = tid; e < 2 * C * 8; e += NT) {
     const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
     const Vec16 x = ldg16(Am + m * C * C + r * C + c8);
     *reinterpret_cast<Vec16*>((m ? L.PT : L.A) + r * P64 + c8) = x;
   }
+  for (int e = tid; e < 3 * C * 16; e += NT) {
+    const int m = e >> 10, r = (e >> 4) & 63, c8 = 8 * (e & 15);
+    const Vec16 x = ldg16(Am + M_KG + m * C * D + r * D + c8);
+    *reinterpret_cast<Vec16*>((m == 0 ? L.Kg : m == 1 ? L.Kd : L.Qg) + r * P128 + c8) = x;
+  }
+  if (tid < D) L.gam[tid] = reinterpret_cast<const float*>(Am + M_GAM)[tid];
+  if (tid < C) L.beta[tid] = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- the chain
@@ -497,8 +518,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int r = 0; r < 4; ++r) x[r] = (bf16)dS[u][r];
       *reinterpret_cast<bf16x4*>(adj + (16 * jt + i) * D + 16 * u + 4 * g4) = x;
     }
-    load_mats(L, chunk_mats(a, bh, N, n), tid);
-    chunk_gates(L, bs, q, k, g, be, c, a.H, tid);
+    load_chunk(L, chunk_mats(a, bh, N, n), be, c, a.H, tid);
     // dO (rows past nv zero) and (gamma . dS)^T
     for (int e = tid; e < C * 16; e += NT) {
       const int t = e >> 4, c0 = 8 * (e & 15);
@@ -621,8 +641,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // [j][c]
   const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // [j][c]
 
-  load_mats(L, chunk_mats(a, bh, N, n), tid);
-  chunk_gates(L, reinterpret_cast<float*>(work), q, k, g, be, c, a.H, tid);
+  load_chunk(L, chunk_mats(a, bh, N, n), be, c, a.H, tid);
   for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
   if (tid < D) dgam[tid] = 0.f;
 
@@ -963,7 +982,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 
 size_t backward_workspace(int BH, int T) {
   const size_t N = ((size_t)T + bwd::C - 1) / bwd::C;
-  return (size_t)BH * N * (2 * bwd::D * bwd::D + 2 * bwd::C * bwd::C) * sizeof(bf16);
+  return (size_t)BH * N * (2 * bwd::D * bwd::D + bwd::MATS) * sizeof(bf16);
 }
 
 template <typename K>
