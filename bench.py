@@ -81,6 +81,7 @@ def parse():
 KERNEL_SOURCES = {
     "prefill": ["kda_prefill.hip", "kda_device.hpp", "kda_launch.hpp"],
     "decode": ["kda_decode.hip", "kda_device.hpp", "kda_launch.hpp"],
+    "backward": ["kda_backward.hip", "kda_prefill.hip", "kda_device.hpp", "kda_launch.hpp"],
 }
 
 
