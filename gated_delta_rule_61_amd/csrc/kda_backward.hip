@@ -50,19 +50,23 @@ typedef Mma<float> MF;
 
 // ---------------------------------------------------------------- fragments
 // Operand fragment of a 16-index slab (lane group g: indices k..k+3 with
-// k = slab + 4g; lane i: row `row`), read either from a row-major array whose
-// rows are the fragment rows (indices contiguous) or gathered from one whose
-// rows are the indices.
+// k = slab + 4g; lane i: row m0 + i), read either from a row-major array whose
+// rows are the fragment rows (indices contiguous, one 8-byte read) or from one
+// whose rows are the indices, with one LDS transpose read
+// (ds_read_b64_tr_b16).  That instruction works on each 16-lane group alone:
+// lane i receives, for r = 0..3, element i % 4 of the four 16-bit elements at
+// the address of lane 4r + i / 4.  So lane j addresses row k + j / 4, columns
+// m0 + 4 (j % 4) .. + 3, and lane i receives p[k + r][m0 + i] (m0 a multiple
+// of 4 and ld a multiple of 4: 8-byte aligned addresses).
 __device__ __forceinline__ bf16x4 fr_row(const bf16* p, int ld, int row, int k) {
   return *reinterpret_cast<const bf16x4*>(p + row * ld + k);
 }
-__device__ __forceinline__ bf16x4 fr_col(const bf16* p, int ld, int row, int k) {
-  bf16x4 v;
-  v[0] = p[k * ld + row];
-  v[1] = p[(k + 1) * ld + row];
-  v[2] = p[(k + 2) * ld + row];
-  v[3] = p[(k + 3) * ld + row];
-  return v;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 fr_tr(const bf16* p, int ld, int m0, int k, int lane) {
+  const int j = lane & 15;
+  const bf16* a = p + (k + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+  return __builtin_bit_cast(bf16x4, x);
 }
 
 // Out tile (m0.., n0..) += sum_{k < K} X[m][k] Z[n][k]; XR / ZR: X / Z stored
@@ -73,8 +77,8 @@ __device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int
                                       floatx4 acc, int lane) {
   const int g = lane >> 4, i = lane & 15;
   for (int k = 0; k < K; k += 16) {
-    const bf16x4 a = XR ? fr_row(X, ldx, m0 + i, k + 4 * g) : fr_col(X, ldx, m0 + i, k + 4 * g);
-    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_col(Z, ldz, n0 + i, k + 4 * g);
+    const bf16x4 a = XR ? fr_row(X, ldx, m0 + i, k + 4 * g) : fr_tr(X, ldx, m0, k + 4 * g, lane);
+    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_tr(Z, ldz, n0, k + 4 * g, lane);
     acc = MB::mma16(a, b, acc);
   }
   return acc;
@@ -425,15 +429,16 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
 // Kg Kd Qg in rows of P128, gamma) and its beta from the input (zero past nv).
 __device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, const bf16* beta, const Chunk& c,
                                            int H, int tid) {
+  // (A, P^T and Kg, Kd, Qg are adjacent in LDS, in that order)
   for (int e = tid; e < 2 * C * 8; e += NT) {
     const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
     const Vec16 x = ldg16(Am + m * C * C + r * C + c8);
-    *reinterpret_cast<Vec16*>((m ? L.PT : L.A) + r * P64 + c8) = x;
+    *reinterpret_cast<Vec16*>(L.A + m * C * P64 + r * P64 + c8) = x;
   }
   for (int e = tid; e < 3 * C * 16; e += NT) {
     const int m = e >> 10, r = (e >> 4) & 63, c8 = 8 * (e & 15);
     const Vec16 x = ldg16(Am + M_KG + m * C * D + r * D + c8);
-    *reinterpret_cast<Vec16*>((m == 0 ? L.Kg : m == 1 ? L.Kd : L.Qg) + r * P128 + c8) = x;
+    *reinterpret_cast<Vec16*>(L.Kg + m * C * P128 + r * P128 + c8) = x;
   }
   if (tid < D) L.gam[tid] = reinterpret_cast<const float*>(Am + M_GAM)[tid];
   if (tid < C) L.beta[tid] = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
@@ -457,6 +462,8 @@ constexpr int O_GAM = O_BETA + C * 4;
 constexpr int O_QK = O_GAM + D * 4;
 constexpr int BYTES = O_QK + C * 4;
 static_assert(D * P64 * 2 <= SZ_BS, "dDelta^T inside the gate scratch");
+static_assert(O_KD == O_KG + C * P128 * 2 && O_QG == O_KD + C * P128 * 2 && O_PT == O_A + C * P64 * 2,
+              "load_chunk layout");
 static_assert(BYTES <= 160 * 1024, "LDS");
 }  // namespace ch
 
@@ -610,6 +617,8 @@ static_assert((C * PB + 4 * D) * 4 <= H_END, "gate scratch inside the work area"
 static_assert(Q_END <= H_END, "after-halves buffers inside the work area");
 static_assert(Z_END <= H_END, "assembly buffers inside the work area");
 static_assert(BYTES <= 160 * 1024, "LDS");
+static_assert(O_KD == O_KG + C * P128 * 2 && O_QG == O_KD + C * P128 * 2 && O_PT == O_A + C * P64 * 2,
+              "load_chunk layout");
 }  // namespace gr
 
 // One workgroup per (chunk, sequence, head).  [t][c] results: wave w owns
@@ -856,7 +865,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     for (int u = 0; u < 4; ++u) {
       floatx4 y = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) y = MB::mma16(fr_col(L.A, P64, 16 * u + i, 16 * ks + 4 * g4), wf[ks], y);
+      for (int ks = 0; ks < 4; ++ks) y = MB::mma16(fr_tr(L.A, P64, 16 * u, 16 * ks + 4 * g4, lane), wf[ks], y);
       // dKg += Diag(beta) Y; dbeta += rowsum(Y . Kg)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
