@@ -445,6 +445,62 @@ __device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, cons
   __syncthreads();
 }
 
+// The chain's operands of one chunk held in registers between their loads and
+// their stores to LDS, so that the next chunk's loads overlap this chunk's
+// products: A, P^T (two 16-byte pieces per thread), Kg, Kd, Qg (six), dO (two),
+// gamma (threads < 128) and beta (threads < 64).  The split of the pieces
+// assumes 512 threads.
+struct ChainOps {
+  Vec16 m[8], o[2];
+  float gam, beta;
+};
+static_assert(NT == 512, "ChainOps piece split");
+
+__device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const bf16* dO, const bf16* beta,
+                                            const Chunk& c, int H, int tid) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * NT;
+    if (u < 2) {
+      const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
+      x.m[u] = ldg16(Am + m * C * C + r * C + c8);
+    } else {
+      const int f = e - 2 * C * 8, m = f >> 10, r = (f >> 4) & 63, c8 = 8 * (f & 15);
+      x.m[u] = ldg16(Am + M_KG + m * C * D + r * D + c8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
+    x.o[u] = Vec16{{0u, 0u, 0u, 0u}};
+    if (t < c.nv) x.o[u] = ldg16(dO + (c.row0 + (int64_t)t * H) * D + c0);
+  }
+  x.gam = tid < D ? reinterpret_cast<const float*>(Am + M_GAM)[tid] : 0.f;
+  x.beta = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
+}
+
+// (A, P^T and Kg, Kd, Qg adjacent in LDS, in that order)
+__device__ __forceinline__ void chain_commit(const ChainOps& x, const Basics& L, bf16* sDO, int tid) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * NT;
+    if (u < 2) {
+      const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
+      *reinterpret_cast<Vec16*>(L.A + m * C * P64 + r * P64 + c8) = x.m[u];
+    } else {
+      const int f = e - 2 * C * 8, m = f >> 10, r = (f >> 4) & 63, c8 = 8 * (f & 15);
+      *reinterpret_cast<Vec16*>(L.Kg + m * C * P128 + r * P128 + c8) = x.m[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
+    *reinterpret_cast<Vec16*>(sDO + t * P128 + c0) = x.o[u];
+  }
+  if (tid < D) L.gam[tid] = x.gam;
+  if (tid < C) L.beta[tid] = x.beta;
+}
+
 // ---------------------------------------------------------------- the chain
 // LDS of bwd_chain_kernel (bytes).
 namespace ch {
@@ -511,11 +567,20 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) dS[u][r] = dST ? dST[(16 * u + 4 * g4 + r) * D + 16 * jt + i] : 0.f;
 
-  for (int n = N - 1; n >= 0; --n) {
+  auto chunk_of = [&](int n) {
     Chunk c;
     c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
     c.nv = min(C, a.T - n * C);
     c.rstride = a.H * D;
+    return c;
+  };
+  ChainOps ops;
+  if (N > 0) {
+    chain_issue(ops, chunk_mats(a, bh, N, N - 1), dO, be, chunk_of(N - 1), a.H, tid);
+    chain_commit(ops, L, sDO, tid);
+    __syncthreads();
+  }
+  for (int n = N - 1; n >= 0; --n) {
     // chunk-end adjoint of this chunk (bf16, transposed: [j][c])
     bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;
 #pragma unroll
@@ -525,14 +590,9 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int r = 0; r < 4; ++r) x[r] = (bf16)dS[u][r];
       *reinterpret_cast<bf16x4*>(adj + (16 * jt + i) * D + 16 * u + 4 * g4) = x;
     }
-    load_chunk(L, chunk_mats(a, bh, N, n), be, c, a.H, tid);
-    // dO (rows past nv zero) and (gamma . dS)^T
-    for (int e = tid; e < C * 16; e += NT) {
-      const int t = e >> 4, c0 = 8 * (e & 15);
-      Vec16 x = {{0u, 0u, 0u, 0u}};
-      if (t < c.nv) x = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + c0);
-      *reinterpret_cast<Vec16*>(sDO + t * P128 + c0) = x;
-    }
+    // the next chunk's operands, in flight during this chunk's products
+    if (n > 0) chain_issue(ops, chunk_mats(a, bh, N, n - 1), dO, be, chunk_of(n - 1), a.H, tid);
+    // (gamma . dS)^T (this chunk's operands are in LDS)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       floatx4 v;
@@ -567,6 +627,10 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * u + 4 * g4 + r] * dS[u][r] + p[r] - m[r];
     }
     __syncthreads();
+    if (n > 0) {
+      chain_commit(ops, L, sDO, tid);
+      __syncthreads();
+    }
   }
   if (a.dS0) {
     float* out = a.dS0 + (int64_t)bh * D * D;
