@@ -425,39 +425,20 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   }
 }
 
-// A chunk's block from the workspace into LDS (A and P^T in rows of P64,
-// Kg Kd Qg in rows of P128, gamma) and its beta from the input (zero past nv).
-__device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, const bf16* beta, const Chunk& c,
-                                           int H, int tid) {
-  // (A, P^T and Kg, Kd, Qg are adjacent in LDS, in that order)
-  for (int e = tid; e < 2 * C * 8; e += NT) {
-    const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
-    const Vec16 x = ldg16(Am + m * C * C + r * C + c8);
-    *reinterpret_cast<Vec16*>(L.A + m * C * P64 + r * P64 + c8) = x;
-  }
-  for (int e = tid; e < 3 * C * 16; e += NT) {
-    const int m = e >> 10, r = (e >> 4) & 63, c8 = 8 * (e & 15);
-    const Vec16 x = ldg16(Am + M_KG + m * C * D + r * D + c8);
-    *reinterpret_cast<Vec16*>(L.Kg + m * C * P128 + r * P128 + c8) = x;
-  }
-  if (tid < D) L.gam[tid] = reinterpret_cast<const float*>(Am + M_GAM)[tid];
-  if (tid < C) L.beta[tid] = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
-  __syncthreads();
-}
-
-// The chain's operands of one chunk held in registers between their loads and
-// their stores to LDS, so that the next chunk's loads overlap this chunk's
-// products: A, P^T (two 16-byte pieces per thread), Kg, Kd, Qg (six), dO (two),
-// gamma (threads < 128) and beta (threads < 64).  The split of the pieces
-// assumes 512 threads.
-struct ChainOps {
-  Vec16 m[8], o[2];
+// A chunk's block of the workspace (A, P^T, Kg, Kd, Qg, gamma) and its beta
+// (zero past nv), held in registers between their loads and their stores to
+// LDS: every load of a thread is issued before the first store, so the loads
+// overlap each other (and, in the chain, the previous chunk's products).  A,
+// P^T take two 16-byte pieces per thread, Kg, Kd, Qg six; gamma threads < 128,
+// beta threads < 64.  The split of the pieces assumes 512 threads.
+struct ChunkOps {
+  Vec16 m[8];
   float gam, beta;
 };
-static_assert(NT == 512, "ChainOps piece split");
+static_assert(NT == 512, "ChunkOps piece split (and the gradient kernel's staging: 64 x 64 halves, one piece per thread)");
 
-__device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const bf16* dO, const bf16* beta,
-                                            const Chunk& c, int H, int tid) {
+__device__ __forceinline__ void ops_issue(ChunkOps& x, const bf16* Am, const bf16* beta, const Chunk& c, int H,
+                                          int tid) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int e = tid + u * NT;
@@ -469,18 +450,12 @@ __device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const b
       x.m[u] = ldg16(Am + M_KG + m * C * D + r * D + c8);
     }
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
-    x.o[u] = Vec16{{0u, 0u, 0u, 0u}};
-    if (t < c.nv) x.o[u] = ldg16(dO + (c.row0 + (int64_t)t * H) * D + c0);
-  }
   x.gam = tid < D ? reinterpret_cast<const float*>(Am + M_GAM)[tid] : 0.f;
   x.beta = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
 }
 
 // (A, P^T and Kg, Kd, Qg adjacent in LDS, in that order)
-__device__ __forceinline__ void chain_commit(const ChainOps& x, const Basics& L, bf16* sDO, int tid) {
+__device__ __forceinline__ void ops_commit(const ChunkOps& x, const Basics& L, int tid) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int e = tid + u * NT;
@@ -492,13 +467,43 @@ __device__ __forceinline__ void chain_commit(const ChainOps& x, const Basics& L,
       *reinterpret_cast<Vec16*>(L.Kg + m * C * P128 + r * P128 + c8) = x.m[u];
     }
   }
+  if (tid < D) L.gam[tid] = x.gam;
+  if (tid < C) L.beta[tid] = x.beta;
+}
+
+__device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, const bf16* beta, const Chunk& c,
+                                           int H, int tid) {
+  ChunkOps x;
+  ops_issue(x, Am, beta, c, H, tid);
+  ops_commit(x, L, tid);
+  __syncthreads();
+}
+
+// The chain's operands of one chunk in registers: the chunk block and dO
+// (two 16-byte pieces per thread, rows past nv zero).
+struct ChainOps {
+  ChunkOps k;
+  Vec16 o[2];
+};
+
+__device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const bf16* dO, const bf16* beta,
+                                            const Chunk& c, int H, int tid) {
+  ops_issue(x.k, Am, beta, c, H, tid);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
+    x.o[u] = Vec16{{0u, 0u, 0u, 0u}};
+    if (t < c.nv) x.o[u] = ldg16(dO + (c.row0 + (int64_t)t * H) * D + c0);
+  }
+}
+
+__device__ __forceinline__ void chain_commit(const ChainOps& x, const Basics& L, bf16* sDO, int tid) {
+  ops_commit(x.k, L, tid);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
     *reinterpret_cast<Vec16*>(sDO + t * P128 + c0) = x.o[u];
   }
-  if (tid < D) L.gam[tid] = x.gam;
-  if (tid < C) L.beta[tid] = x.beta;
 }
 
 // ---------------------------------------------------------------- the chain
@@ -656,9 +661,9 @@ constexpr int O_MD = O_DGAM + D * 4;          // diagonal of M, [64]
 constexpr int O_DB = O_MD + C * 4;            // dbeta partial sums [8 waves][64]
 constexpr int O_WORK = O_DB + 8 * C * 4;      // phase-dependent area
 // half-loop layout inside the work area
-constexpr int H_S = 0;                         // S[:, J]        [128][P64] bf16
-constexpr int H_DSG = H_S + D * P64 * 2;       // gamma.dS[:, J] [128][P64]
-constexpr int H_V = H_DSG + D * P64 * 2;       // V[:, J]        [64][P64]
+constexpr int H_S = 0;                         // S[:, J] as [j][c]        [64][P128] bf16
+constexpr int H_DSG = H_S + C * P128 * 2;      // (gamma . dS)[:, J], [j][c] [64][P128]
+constexpr int H_V = H_DSG + C * P128 * 2;      // V[:, J]        [64][P64]
 constexpr int H_DO = H_V + C * P64 * 2;        // dO[:, J]
 constexpr int H_D = H_DO + C * P64 * 2;        // Delta[:, J]
 constexpr int H_DD = H_D + C * P64 * 2;        // dDelta[:, J]
@@ -742,56 +747,47 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* hD = reinterpret_cast<bf16*>(work + gr::H_D);
   bf16* hDD = reinterpret_cast<bf16*>(work + gr::H_DD);
   bf16* hXT = reinterpret_cast<bf16*>(work + gr::H_XT);
-  float dgp = 0.f;   // gamma . rowsum(dS . S) partial of column tid (tid < 128)
+  // gamma . rowsum(S . dS), the chunk-end term of each channel: the diagonal
+  // of S (gamma . dS)^T, wave w forming its diagonal tile (channels 16w..)
+  floatx4 aSD = zero4();
 
   for (int jh = 0; jh < 2; ++jh) {
     const int J0 = 64 * jh;
     __syncthreads();
-    // S[:, J] and gamma . dS[:, J] into [c][j] from the transposed [j][c]
-    // copies: thread -> value column j = tid / 8, channels 16 (tid % 8) .. + 16
+    // S[:, J] and gamma . dS[:, J] in their stored order [j][c] (thread: value
+    // column j = tid / 8, channels 16 (tid % 8) .. + 16), V[:, J] and dO[:, J]
+    // (rows past nv zero); every load issued before the first store.
     {
       const int jr = tid >> 3, cc = 16 * (tid & 7);
+      const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
+      Vec16 xs[2], xd[2], xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const Vec16 xs = ldg16(Sn + (J0 + jr) * D + cc + 8 * u);
-        const Vec16 xd = ldg16(dSn + (J0 + jr) * D + cc + 8 * u);
-        float fs[8], fd[8];
-        vec_to_f32<bf16>(xs, fs);
-        vec_to_f32<bf16>(xd, fd);
+        xs[u] = ldg16(Sn + (J0 + jr) * D + cc + 8 * u);
+        xd[u] = ldg16(dSn + (J0 + jr) * D + cc + 8 * u);
+      }
+      if (tv < c.nv) {
+        xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);
+        xo = ldg16(dO + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cr = cc + 8 * u + e;
-          hS[cr * P64 + jr] = (bf16)fs[e];
-          hDSG[cr * P64 + jr] = (bf16)(L.gam[cr] * fd[e]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        float fd[8];
+        vec_to_f32<bf16>(xd[u], fd);
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)(L.gam[cc + 8 * u + e] * fd[e]);
+        *reinterpret_cast<Vec16*>(hS + jr * P128 + cc + 8 * u) = xs[u];
+        *reinterpret_cast<bf16x8*>(hDSG + jr * P128 + cc + 8 * u) = y;
       }
-    }
-    // V[:, J], dO[:, J]
-    for (int e = tid; e < C * 8; e += NT) {
-      const int t = e >> 3, x0 = 8 * (e & 7);
-      Vec16 xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
-      if (t < c.nv) {
-        xv = ldg16(v + (c.row0 + (int64_t)t * a.H) * D + J0 + x0);
-        xo = ldg16(dO + (c.row0 + (int64_t)t * a.H) * D + J0 + x0);
-      }
-      *reinterpret_cast<Vec16*>(hV + t * P64 + x0) = xv;
-      *reinterpret_cast<Vec16*>(hDO + t * P64 + x0) = xo;
+      *reinterpret_cast<Vec16*>(hV + tv * P64 + xv0) = xv;
+      *reinterpret_cast<Vec16*>(hDO + tv * P64 + xv0) = xo;
     }
     __syncthreads();
-    // gamma . rowsum(dS . S) over this half (from the rounded copies)
-    if (tid < D) {
-#pragma unroll 4
-      for (int j = 0; j < 64; j += 4) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hS + tid * P64 + j);
-        const bf16x4 y = *reinterpret_cast<const bf16x4*>(hDSG + tid * P64 + j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dgp += (float)x[e] * (float)y[e];
-      }
-    }
     // X = beta . (V - Kg S), stored transposed
     for (int tile = wave; tile < 16; tile += NT / 64) {
       const int tt = tile >> 2, jj = tile & 3;
-      floatx4 ks = mm<true, false>(L.Kg, P128, hS, P64, 16 * tt, 16 * jj, D, zero4(), lane);
+      floatx4 ks = mm<true, true>(L.Kg, P128, hS, P128, 16 * tt, 16 * jj, D, zero4(), lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * g4 + r;
@@ -806,18 +802,19 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       const floatx4 dl = mm<true, true>(L.A, P64, hXT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
       st_rm(hD, P64, 16 * tt, 16 * jj, dl, lane);
       floatx4 dd = mm<true, false>(L.PT, P64, hDO, P64, 16 * tt, 16 * jj, C, zero4(), lane);
-      dd = mm<true, false>(L.Kd, P128, hDSG, P64, 16 * tt, 16 * jj, D, dd, lane);
+      dd = mm<true, true>(L.Kd, P128, hDSG, P128, 16 * tt, 16 * jj, D, dd, lane);
       st_rm(hDD, P64, 16 * tt, 16 * jj, dd, lane);
     }
     __syncthreads();
     // [t][c] products over this half's value columns
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      aQg[u] = mm<true, true>(hDO, P64, hS, P64, 16 * u, c0, 64, aQg[u], lane);    // dO S^T
-      aKb[u] = mm<true, true>(hD, P64, hDSG, P64, 16 * u, c0, 64, aKb[u], lane);   // Delta (g.dS)^T
-      aW[u] = mm<true, true>(hDD, P64, hS, P64, 16 * u, c0, 64, aW[u], lane);      // dDelta S^T
+      aQg[u] = mm<true, false>(hDO, P64, hS, P128, 16 * u, c0, 64, aQg[u], lane);    // dO S^T
+      aKb[u] = mm<true, false>(hD, P64, hDSG, P128, 16 * u, c0, 64, aKb[u], lane);   // Delta (g.dS)^T
+      aW[u] = mm<true, false>(hDD, P64, hS, P128, 16 * u, c0, 64, aW[u], lane);      // dDelta S^T
       __builtin_amdgcn_sched_barrier(0);   // one tile's operands in flight at a time
     }
+    aSD = mm<false, false>(hS, P128, hDSG, P128, c0, c0, 64, aSD, lane);
     // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -851,7 +848,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
             *reinterpret_cast<const Vec16*>(hXT + t * P64 + x0);
     }
   }
-  if (tid < D) dgam[tid] = dgp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (4 * g4 + r == i) dgam[c0 + i] = aSD[r];
   // fold dKb~ into dKd, keeping its column sums against Kd (chunk-end terms)
   float colsum = 0.f;   // sum over my rows of Kd . dKb~ for column c0 + i
 #pragma unroll
@@ -987,21 +986,29 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   float* bs = reinterpret_cast<float*>(work + gr::Z_DB);
   bf16* zq = reinterpret_cast<bf16*>(work + gr::Z_Q);
   bf16* zk = reinterpret_cast<bf16*>(work + gr::Z_K);
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, x0 = 8 * (e & 15);
-    Vec16 x = {{0u, 0u, 0u, 0u}}, xq = x, xk = x;
-    if (t < c.nv) {
-      const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
-      x = ldg16(g + off);
-      xq = ldg16(q + off);
-      xk = ldg16(k + off);
-    }
-    float f[8];
-    vec_to_f32<bf16>(x, f);
+  {
+    Vec16 xg[2], xq[2], xk[2];
 #pragma unroll
-    for (int uu = 0; uu < 8; ++uu) bs[t * PB + x0 + uu] = f[uu];
-    *reinterpret_cast<Vec16*>(zq + t * P128 + x0) = xq;
-    *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = xk;
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+      xg[u] = xq[u] = xk[u] = Vec16{{0u, 0u, 0u, 0u}};
+      if (t < c.nv) {
+        const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
+        xg[u] = ldg16(g + off);
+        xq[u] = ldg16(q + off);
+        xk[u] = ldg16(k + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+      float f[8];
+      vec_to_f32<bf16>(xg[u], f);
+#pragma unroll
+      for (int uu = 0; uu < 8; ++uu) bs[t * PB + x0 + uu] = f[uu];
+      *reinterpret_cast<Vec16*>(zq + t * P128 + x0) = xq[u];
+      *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = xk[u];
+    }
   }
   __syncthreads();
   scan_cols<false>(bs, nullptr, tid);
