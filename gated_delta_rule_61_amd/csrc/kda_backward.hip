@@ -86,6 +86,22 @@ __device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// NTL tiles (m0[t].., n0..) of the same product shape sharing their Z
+// columns: each Z fragment is read once per 16-index step for all of them.
+template <bool XR, bool ZR, int NTL>
+__device__ __forceinline__ void mm_zs(const bf16* X, int ldx, const int (&m0)[NTL], const bf16* Z, int ldz, int n0,
+                                      int K, floatx4 (&acc)[NTL], int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  for (int k = 0; k < K; k += 16) {
+    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_tr(Z, ldz, n0, k + 4 * g, lane);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const bf16x4 a = XR ? fr_row(X, ldx, m0[t] + i, k + 4 * g) : fr_tr(X, ldx, m0[t], k + 4 * g, lane);
+      acc[t] = MB::mma16(a, b, acc[t]);
+    }
+  }
+}
+
 // C-layout tile -> row-major dst[m][n] (2-byte stores)
 __device__ __forceinline__ void st_rm(bf16* dst, int ld, int m0, int n0, floatx4 v, int lane) {
   const int g = lane >> 4, i = lane & 15;
@@ -785,36 +801,49 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
     __syncthreads();
     // X = beta . (V - Kg S), stored transposed
-    for (int tile = wave; tile < 16; tile += NT / 64) {
-      const int tt = tile >> 2, jj = tile & 3;
-      floatx4 ks = mm<true, true>(L.Kg, P128, hS, P128, 16 * tt, 16 * jj, D, zero4(), lane);
+    // (tiles (tt, jj) and (tt + 2, jj) per wave: tiles wave and wave + 8 of 16)
+    const int jj = wave & 3, tA = wave >> 2;
+    const int mT[2] = {16 * tA, 16 * (tA + 2)};
+    {
+      floatx4 ks[2] = {zero4(), zero4()};
+      mm_zs<true, true, 2>(L.Kg, P128, mT, hS, P128, 16 * jj, D, ks, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * g4 + r;
-        ks[r] = L.beta[t] * ((float)hV[t * P64 + 16 * jj + i] - ks[r]);
+      for (int x = 0; x < 2; ++x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = mT[x] + 4 * g4 + r;
+          ks[x][r] = L.beta[t] * ((float)hV[t * P64 + 16 * jj + i] - ks[x][r]);
+        }
+        st_tr(hXT, P64, mT[x], 16 * jj, ks[x], lane);
       }
-      st_tr(hXT, P64, 16 * tt, 16 * jj, ks, lane);
     }
     __syncthreads();
     // Delta = A X; dDelta = P^T dO + Kd (gamma . dS); both row-major
-    for (int tile = wave; tile < 16; tile += NT / 64) {
-      const int tt = tile >> 2, jj = tile & 3;
-      const floatx4 dl = mm<true, true>(L.A, P64, hXT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
-      st_rm(hD, P64, 16 * tt, 16 * jj, dl, lane);
-      floatx4 dd = mm<true, false>(L.PT, P64, hDO, P64, 16 * tt, 16 * jj, C, zero4(), lane);
-      dd = mm<true, true>(L.Kd, P128, hDSG, P128, 16 * tt, 16 * jj, D, dd, lane);
-      st_rm(hDD, P64, 16 * tt, 16 * jj, dd, lane);
+    {
+      floatx4 dl[2] = {zero4(), zero4()}, dd[2] = {zero4(), zero4()};
+      mm_zs<true, true, 2>(L.A, P64, mT, hXT, P64, 16 * jj, C, dl, lane);
+      mm_zs<true, false, 2>(L.PT, P64, mT, hDO, P64, 16 * jj, C, dd, lane);
+      mm_zs<true, true, 2>(L.Kd, P128, mT, hDSG, P128, 16 * jj, D, dd, lane);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        st_rm(hD, P64, mT[x], 16 * jj, dl[x], lane);
+        st_rm(hDD, P64, mT[x], 16 * jj, dd[x], lane);
+      }
     }
     __syncthreads();
     // [t][c] products over this half's value columns
+    // (dO S^T, Delta (g.dS)^T, dDelta S^T: the S and g.dS fragments of a step
+    // serve all four row tiles; the diagonal tile of S (g.dS)^T alongside)
+    for (int k = 0; k < 64; k += 16) {
+      const bf16x4 fs = fr_tr(hS, P128, c0, k + 4 * g4, lane), fd = fr_tr(hDSG, P128, c0, k + 4 * g4, lane);
+      aSD = MB::mma16(fs, fd, aSD);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      aQg[u] = mm<true, false>(hDO, P64, hS, P128, 16 * u, c0, 64, aQg[u], lane);    // dO S^T
-      aKb[u] = mm<true, false>(hD, P64, hDSG, P128, 16 * u, c0, 64, aKb[u], lane);   // Delta (g.dS)^T
-      aW[u] = mm<true, false>(hDD, P64, hS, P128, 16 * u, c0, 64, aW[u], lane);      // dDelta S^T
-      __builtin_amdgcn_sched_barrier(0);   // one tile's operands in flight at a time
+      for (int u = 0; u < 4; ++u) {
+        aQg[u] = MB::mma16(fr_row(hDO, P64, 16 * u + i, k + 4 * g4), fs, aQg[u]);
+        aKb[u] = MB::mma16(fr_row(hD, P64, 16 * u + i, k + 4 * g4), fd, aKb[u]);
+        aW[u] = MB::mma16(fr_row(hDD, P64, 16 * u + i, k + 4 * g4), fs, aW[u]);
+      }
     }
-    aSD = mm<false, false>(hS, P128, hDSG, P128, c0, c0, 64, aSD, lane);
     // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -828,17 +857,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
     // dV[:, J] = Diag(beta) A^T dDelta, staged row-major where X^T was (dead
     // since Delta); dbeta += rowsum((A^T dDelta) . V)
-    for (int tile = wave; tile < 16; tile += NT / 64) {
-      const int tt = tile >> 2, jj = tile & 3;
-      floatx4 x = mm<false, false>(L.A, P64, hDD, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+    {
+      floatx4 xv[2] = {zero4(), zero4()};
+      mm_zs<false, false, 2>(L.A, P64, mT, hDD, P64, 16 * jj, C, xv, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * g4 + r;
-        const float p = sum16(x[r] * (float)hV[t * P64 + 16 * jj + i]);
-        if (i == 0) dbp[wave * C + t] += p;
-        x[r] *= L.beta[t];
+      for (int x = 0; x < 2; ++x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = mT[x] + 4 * g4 + r;
+          const float p = sum16(xv[x][r] * (float)hV[t * P64 + 16 * jj + i]);
+          if (i == 0) dbp[wave * C + t] += p;
+          xv[x][r] *= L.beta[t];
+        }
+        st_rm(hXT, P64, mT[x], 16 * jj, xv[x], lane);
       }
-      st_rm(hXT, P64, 16 * tt, 16 * jj, x, lane);
     }
     __syncthreads();
     {
@@ -908,17 +940,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   }
   __syncthreads();
   // Z1^T = A dA^T ( = (dA A^T)^T ), all 16 tiles
-  for (int tile = wave; tile < 16; tile += NT / 64) {
-    const int I = tile >> 2, J = tile & 3;
-    const floatx4 z = mm<true, true>(L.A, P64, qDA, P64, 16 * I, 16 * J, C, zero4(), lane);
-    st_rm(qZ1T, P64, 16 * I, 16 * J, z, lane);
+  // (tiles (I, J) and (I + 2, J) per wave: tiles wave and wave + 8 of 16)
+  const int mT[2] = {16 * (wave >> 2), 16 * ((wave >> 2) + 2)};
+  {
+    floatx4 z[2] = {zero4(), zero4()};
+    mm_zs<true, true, 2>(L.A, P64, mT, qDA, P64, 16 * (wave & 3), C, z, lane);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) st_rm(qZ1T, P64, mT[x], 16 * (wave & 3), z[x], lane);
   }
   // [t][c]: M Kd, M^T Qg, A^T dW
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    aQg[u] = mm<true, false>(qM, P64, L.Kd, P128, 16 * u, c0, C, aQg[u], lane);
-    aKd[u] = mm<false, false>(qM, P64, L.Qg, P128, 16 * u, c0, C, aKd[u], lane);
-  }
+  const int mU[4] = {0, 16, 32, 48};
+  mm_zs<true, false, 4>(qM, P64, mU, L.Kd, P128, c0, C, aQg, lane);
+  mm_zs<false, false, 4>(qM, P64, mU, L.Qg, P128, c0, C, aKd, lane);
   {
     // Y = A^T dW with dW from registers (B operand of the 16-index slabs)
     bf16x4 wf[4];
@@ -966,18 +999,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   }
   __syncthreads();
   // dKg += Diag(beta) dL Kd (dbeta += rowsum(Kg . dL Kd)); dKd += dG^T Kg
+  {
+    floatx4 lk[4] = {zero4(), zero4(), zero4(), zero4()};
+    mm_zs<true, false, 4>(qDL, P64, mU, L.Kd, P128, c0, C, lk, lane);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const floatx4 lk = mm<true, false>(qDL, P64, L.Kd, P128, 16 * u, c0, C, zero4(), lane);
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * u + 4 * g4 + r;
-      aKg[u][r] += L.beta[t] * lk[r];
-      const float p = sum16(lk[r] * (float)L.Kg[t * P128 + c0 + i]);
-      if (i == 0) dbp[wave * C + t] += p;
-    }
-    aKd[u] = mm<false, false>(qDG, P64, L.Kg, P128, 16 * u, c0, C, aKd[u], lane);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * u + 4 * g4 + r;
+        aKg[u][r] += L.beta[t] * lk[u][r];
+        const float p = sum16(lk[u][r] * (float)L.Kg[t * P128 + c0 + i]);
+        if (i == 0) dbp[wave * C + t] += p;
+      }
   }
+  mm_zs<false, false, 4>(qDG, P64, mU, L.Kg, P128, c0, C, aKd, lane);
   __syncthreads();   // the work area becomes the db array
 
   // assembly: gate factors from b (recomputed), raw q and k staged in LDS;
