@@ -622,30 +622,43 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
     }
     __syncthreads();
-    // dDelta = P^T dO + Kd (gamma . dS), stored transposed (over the gate scratch)
-    for (int tile = wave; tile < 32; tile += NT / 64) {
-      const int tt = tile >> 3, jj = tile & 7;
-      floatx4 acc = mm<true, false>(L.PT, P64, sDO, P128, 16 * tt, 16 * jj, C, zero4(), lane);
-      acc = mm<true, true>(L.Kd, P128, sDSG, P128, 16 * tt, 16 * jj, D, acc, lane);
-      st_tr(sDDT, P64, 16 * tt, 16 * jj, acc, lane);
+    // dDelta = P^T dO + Kd (gamma . dS), stored transposed (over the gate
+    // scratch); wave w: the four token tiles of value-column tile w, which
+    // share their column operands
+    const int mT[4] = {0, 16, 32, 48};
+    {
+      floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+      mm_zs<true, false, 4>(L.PT, P64, mT, sDO, P128, 16 * jt, C, acc, lane);
+      mm_zs<true, true, 4>(L.Kd, P128, mT, sDSG, P128, 16 * jt, D, acc, lane);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) st_tr(sDDT, P64, mT[x], 16 * jt, acc[x], lane);
     }
     __syncthreads();
     // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed (over (gamma . dS)^T)
-    for (int tile = wave; tile < 32; tile += NT / 64) {
-      const int tt = tile >> 3, jj = tile & 7;
-      floatx4 acc = mm<false, true>(L.A, P64, sDDT, P64, 16 * tt, 16 * jj, C, zero4(), lane);
+    {
+      floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+      mm_zs<false, true, 4>(L.A, P64, mT, sDDT, P64, 16 * jt, C, acc, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= L.beta[16 * tt + 4 * g4 + r];
-      st_tr(sET, P64, 16 * tt, 16 * jj, acc, lane);
+      for (int x = 0; x < 4; ++x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[x][r] *= L.beta[mT[x] + 4 * g4 + r];
+        st_tr(sET, P64, mT[x], 16 * jt, acc[x], lane);
+      }
     }
     __syncthreads();
-    // dS <- gamma . dS + Qg^T dO - Kg^T E
+    // dS <- gamma . dS + Qg^T dO - Kg^T E, in two groups of four channel tiles
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      floatx4 p = mm<false, false>(L.Qg, P128, sDO, P128, 16 * u, 16 * jt, C, zero4(), lane);
-      floatx4 m = mm<false, true>(L.Kg, P128, sET, P64, 16 * u, 16 * jt, C, zero4(), lane);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int mC[4] = {64 * hf, 64 * hf + 16, 64 * hf + 32, 64 * hf + 48};
+      floatx4 p[4] = {zero4(), zero4(), zero4(), zero4()}, m[4] = {zero4(), zero4(), zero4(), zero4()};
+      mm_zs<false, false, 4>(L.Qg, P128, mC, sDO, P128, 16 * jt, C, p, lane);
+      mm_zs<false, true, 4>(L.Kg, P128, mC, sET, P64, 16 * jt, C, m, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * u + 4 * g4 + r] * dS[u][r] + p[r] - m[r];
+      for (int x = 0; x < 4; ++x) {
+        const int u = 4 * hf + x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * u + 4 * g4 + r] * dS[u][r] + p[x][r] - m[x][r];
+      }
     }
     __syncthreads();
     if (n > 0) {
