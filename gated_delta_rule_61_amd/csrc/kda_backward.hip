@@ -117,13 +117,18 @@ __device__ __forceinline__ void st_tr(bf16* dst, int ld, int m0, int n0, floatx4
   *reinterpret_cast<bf16x4*>(dst + (n0 + i) * ld + m0 + 4 * g) = x;
 }
 
-// Sum over the 16 lanes of the caller's 16-lane row (lanes i = 0..15, same g).
+// Sum over the 16 lanes of the caller's 16-lane row (lanes i = 0..15, same g),
+// in every lane of the row: a butterfly of DPP row rotations (row_ror by 8,
+// 4, 2, 1), VALU only.
+template <int K>
+__device__ __forceinline__ float add_row_ror(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + K, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
+  x = add_row_ror<8>(x);
+  x = add_row_ror<4>(x);
+  x = add_row_ror<2>(x);
+  return add_row_ror<1>(x);
 }
 
 // ---------------------------------------------------------------- chunk basics
