@@ -172,55 +172,6 @@ __device__ void scan_cols(float* bs, float* gam, int tid) {
   __syncthreads();
 }
 
-// In-chunk cumulative log-gates b (fp32 [64][PB] in `bs`), the gated operands
-// Kg Kd Qg, gamma, beta and q.k.  Rows past nv are zero (g = 0 there, so b is
-// constant and the chunk end gate is that of the last valid row).
-__device__ void chunk_gates(const Basics& L, float* bs, const bf16* q, const bf16* k, const bf16* g,
-                            const bf16* beta, const Chunk& ch, int H, int tid) {
-  // g -> bs (fp32); thread: row t = e / 16, channels 8 (e % 16) .. + 8
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, c0 = 8 * (e & 15);
-    Vec16 x = {{0u, 0u, 0u, 0u}};
-    if (t < ch.nv) x = ldg16(g + (ch.row0 + (int64_t)t * H) * D + c0);
-    float f[8];
-    vec_to_f32<bf16>(x, f);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) bs[t * PB + c0 + u] = f[u];
-  }
-  if (tid < C) L.beta[tid] = tid < ch.nv ? (float)beta[ch.row0 + (int64_t)tid * H] : 0.f;
-  __syncthreads();
-  scan_cols<false>(bs, L.gam, tid);
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, c0 = 8 * (e & 15);
-    Vec16 xq = {{0u, 0u, 0u, 0u}}, xk = {{0u, 0u, 0u, 0u}};
-    if (t < ch.nv) {
-      xq = ldg16(q + (ch.row0 + (int64_t)t * H) * D + c0);
-      xk = ldg16(k + (ch.row0 + (int64_t)t * H) * D + c0);
-    }
-    float fq[8], fk[8];
-    vec_to_f32<bf16>(xq, fq);
-    vec_to_f32<bf16>(xk, fk);
-    bf16x8 kg, kd, qg;
-    float qk = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float b = bs[t * PB + c0 + u];
-      const float ep = __expf(b), em = __expf(-b);
-      kg[u] = (bf16)(fk[u] * ep);
-      kd[u] = (bf16)(fk[u] * em);
-      qg[u] = (bf16)(fq[u] * ep);
-      qk += fq[u] * fk[u];
-    }
-    *reinterpret_cast<bf16x8*>(L.Kg + t * P128 + c0) = kg;
-    *reinterpret_cast<bf16x8*>(L.Kd + t * P128 + c0) = kd;
-    *reinterpret_cast<bf16x8*>(L.Qg + t * P128 + c0) = qg;
-    // the 16 threads of row t are 16 consecutive lanes
-    qk = sum16(qk);
-    if ((e & 15) == 0) L.qk[t] = qk;
-  }
-  __syncthreads();
-}
-
 // Off-diagonal blocks of block column J (fp32 MFMA; the column's blocks in
 // C layout serve as B operands).
 template <int J>
@@ -333,29 +284,38 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   bf16* Am = chunk_mats(a, bh, N, n);
   bf16* PTm = Am + M_PT;
 
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, x0 = 8 * (e & 15);
-    Vec16 x = {{0u, 0u, 0u, 0u}};
-    if (t < nv) x = ldg16(g + (row0 + (int64_t)t * a.H) * D + x0);
-    float f[8];
-    vec_to_f32<bf16>(x, f);
+  // g, q, k of the chunk (thread: rows t = e / 16 of e = tid, tid + 512,
+  // channels 8 (e % 16) .. + 8; rows past nv zero), every load issued first
+  Vec16 xg[2], xq[2], xk[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) bs[t * PB + x0 + u] = f[u];
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+    xg[u] = xq[u] = xk[u] = Vec16{{0u, 0u, 0u, 0u}};
+    if (t < nv) {
+      const int64_t off = (row0 + (int64_t)t * a.H) * D + x0;
+      xg[u] = ldg16(g + off);
+      xq[u] = ldg16(q + off);
+      xk[u] = ldg16(k + off);
+    }
   }
   if (tid < C) beta[tid] = tid < nv ? (float)reinterpret_cast<const bf16*>(a.beta)[row0 + (int64_t)tid * a.H] : 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+    float f[8];
+    vec_to_f32<bf16>(xg[u], f);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) bs[t * PB + x0 + v] = f[v];
+  }
   __syncthreads();
   scan_cols<false>(bs, nullptr, tid);
   // Qg (into X), Kd, exact q.k
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, x0 = 8 * (e & 15);
-    Vec16 xq = {{0u, 0u, 0u, 0u}}, xk = xq;
-    if (t < nv) {
-      xq = ldg16(q + (row0 + (int64_t)t * a.H) * D + x0);
-      xk = ldg16(k + (row0 + (int64_t)t * a.H) * D + x0);
-    }
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+    const int e = tid + uu * NT, t = e >> 4, x0 = 8 * (e & 15);
     float fq[8], fk[8];
-    vec_to_f32<bf16>(xq, fq);
-    vec_to_f32<bf16>(xk, fk);
+    vec_to_f32<bf16>(xq[uu], fq);
+    vec_to_f32<bf16>(xk[uu], fk);
     bf16x8 qg, kd;
     float qk = 0.f;
 #pragma unroll
@@ -400,12 +360,11 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   }
   __syncthreads();
   // Kg (into X)
-  for (int e = tid; e < C * 16; e += NT) {
-    const int t = e >> 4, x0 = 8 * (e & 15);
-    Vec16 xk = {{0u, 0u, 0u, 0u}};
-    if (t < nv) xk = ldg16(k + (row0 + (int64_t)t * a.H) * D + x0);
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+    const int e = tid + uu * NT, t = e >> 4, x0 = 8 * (e & 15);
     float fk[8];
-    vec_to_f32<bf16>(xk, fk);
+    vec_to_f32<bf16>(xk[uu], fk);
     bf16x8 kg;
 #pragma unroll
     for (int u = 0; u < 8; ++u) kg[u] = (bf16)(fk[u] * __expf(bs[t * PB + x0 + u]));
