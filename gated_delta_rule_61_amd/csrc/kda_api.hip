@@ -249,7 +249,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
   const size_t need = kda::backward_workspace(B * H, T);
   KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
   KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
-  // workspace: chunk states, chunk-end adjoints (bf16 d_v x d_k each), A and P^T (bf16 64 x 64 each)
+  // workspace: chunk states, chunk-end adjoints (bf16 d_k x d_v each), then per-chunk operand blocks
   const size_t nst = (size_t)B * H * (size_t)((T + 63) / 64) * d_k * d_v * 2;
   kda::BackwardArgs a{q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H, workspace,
                       static_cast<char*>(workspace) + nst, static_cast<char*>(workspace) + 2 * nst};

@@ -253,10 +253,11 @@ static_assert(BYTES <= 80 * 1024, "two workgroups per compute unit");
 }  // namespace pr
 
 // Per-chunk block of the workspace (bf16 element offsets): A, P^T (64 x 64),
-// the gated operands Kg, Kd, Qg (64 x 128, row-major) and gamma (fp32 [128]).
+// the gated operands Kg, Kd, Qg (64 x 128, row-major), then fp32 gamma [128]
+// and beta [64] (zero past the chunk's valid rows).
 constexpr int M_A = 0, M_PT = C * C, M_KG = 2 * C * C, M_KD = M_KG + C * D, M_QG = M_KD + C * D;
 constexpr int M_GAM = M_QG + C * D;
-constexpr int MATS = M_GAM + 2 * D;
+constexpr int MATS = M_GAM + 2 * (D + C);
 static_assert((MATS * 2) % 16 == 0, "16-byte aligned blocks");
 
 __device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t bh, int N, int n) {
@@ -333,6 +334,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
     if ((e & 15) == 0) qkd[t] = qk;
   }
   if (tid < D) reinterpret_cast<float*>(Am + M_GAM)[tid] = __expf(bs[(C - 1) * PB + tid]);
+  if (tid < C) reinterpret_cast<float*>(Am + M_GAM)[D + tid] = beta[tid];
   __syncthreads();
   // P^T to memory (zero tiles where P is zero); lower tiles from Qg Kd^T
   for (int e = tid; e < C * C / 4; e += NT) {
@@ -405,22 +407,25 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   }
 }
 
-// A chunk's block of the workspace (A, P^T, Kg, Kd, Qg, gamma) and its beta
-// (zero past nv), held in registers between their loads and their stores to
-// LDS: every load of a thread is issued before the first store, so the loads
-// overlap each other (and, in the chain, the previous chunk's products).  A,
-// P^T take two 16-byte pieces per thread, Kg, Kd, Qg six; gamma threads < 128,
-// beta threads < 64.  The split of the pieces assumes 512 threads.
+// A chunk's block of the workspace (A, P^T, Kg, Kd, Qg, gamma, beta), held in
+// registers between their loads and their stores to LDS: every load of a
+// thread is issued before the first store, so the loads overlap each other
+// (and, in the chain, the previous chunk's products).  A, P^T take two
+// 16-byte pieces per thread, Kg, Kd, Qg six, and the 192 floats of gamma and
+// beta one float each (threads < 192, every thread loading one in range: a
+// load under a branch, or a narrow load converted where it lands, made the
+// compiler wait there for every load issued before it).  The split of the
+// pieces assumes 512 threads.
 struct ChunkOps {
   Vec16 m[8];
-  float gam, beta;
+  float gb;
 };
 static_assert(NT == 512, "ChunkOps piece split (and the gradient kernel's staging: 64 x 64 halves, one piece per thread)");
 
-__device__ __forceinline__ void ops_issue(ChunkOps& x, const bf16* Am, const bf16* beta, const Chunk& c, int H,
-                                          int tid) {
+template <int U0 = 0, int U1 = 8>
+__device__ __forceinline__ void ops_issue(ChunkOps& x, const bf16* Am, int tid) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = U0; u < U1; ++u) {
     const int e = tid + u * NT;
     if (u < 2) {
       const int m = e >> 9, r = (e >> 3) & 63, c8 = 8 * (e & 7);
@@ -430,8 +435,7 @@ __device__ __forceinline__ void ops_issue(ChunkOps& x, const bf16* Am, const bf1
       x.m[u] = ldg16(Am + M_KG + m * C * D + r * D + c8);
     }
   }
-  x.gam = tid < D ? reinterpret_cast<const float*>(Am + M_GAM)[tid] : 0.f;
-  x.beta = tid < c.nv ? (float)beta[c.row0 + (int64_t)tid * H] : 0.f;
+  if (U0 == 0) x.gb = reinterpret_cast<const float*>(Am + M_GAM)[min(tid, D + C - 1)];
 }
 
 // (A, P^T and Kg, Kd, Qg adjacent in LDS, in that order)
@@ -447,14 +451,15 @@ __device__ __forceinline__ void ops_commit(const ChunkOps& x, const Basics& L, i
       *reinterpret_cast<Vec16*>(L.Kg + m * C * P128 + r * P128 + c8) = x.m[u];
     }
   }
-  if (tid < D) L.gam[tid] = x.gam;
-  if (tid < C) L.beta[tid] = x.beta;
+  if (tid < D)
+    L.gam[tid] = x.gb;
+  else if (tid < D + C)
+    L.beta[tid - D] = x.gb;
 }
 
-__device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, const bf16* beta, const Chunk& c,
-                                           int H, int tid) {
+__device__ __forceinline__ void load_chunk(const Basics& L, const bf16* Am, int tid) {
   ChunkOps x;
-  ops_issue(x, Am, beta, c, H, tid);
+  ops_issue(x, Am, tid);
   ops_commit(x, L, tid);
   __syncthreads();
 }
@@ -466,14 +471,22 @@ struct ChainOps {
   Vec16 o[2];
 };
 
-__device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const bf16* dO, const bf16* beta,
-                                            const Chunk& c, int H, int tid) {
-  ops_issue(x.k, Am, beta, c, H, tid);
+// In three parts, one at the start of each product phase of the chain, so
+// that no phase stalls on issuing all eleven loads at once: A, P^T, gamma and
+// beta; Kg, half of Kd; the rest of Kd, Qg, dO.
+template <int PART>
+__device__ __forceinline__ void chain_issue(ChainOps& x, const bf16* Am, const bf16* dO, const Chunk& c, int H,
+                                            int tid) {
+  if (PART == 0) ops_issue<0, 2>(x.k, Am, tid);
+  if (PART == 1) ops_issue<2, 5>(x.k, Am, tid);
+  if (PART == 2) {
+    ops_issue<5, 8>(x.k, Am, tid);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
-    x.o[u] = Vec16{{0u, 0u, 0u, 0u}};
-    if (t < c.nv) x.o[u] = ldg16(dO + (c.row0 + (int64_t)t * H) * D + c0);
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + u * NT, t = e >> 4, c0 = 8 * (e & 15);
+      x.o[u] = Vec16{{0u, 0u, 0u, 0u}};
+      if (t < c.nv) x.o[u] = ldg16(dO + (c.row0 + (int64_t)t * H) * D + c0);
+    }
   }
 }
 
@@ -541,7 +554,6 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   const bf16* q = reinterpret_cast<const bf16*>(a.q);
   const bf16* k = reinterpret_cast<const bf16*>(a.k);
   const bf16* g = reinterpret_cast<const bf16*>(a.g);
-  const bf16* be = reinterpret_cast<const bf16*>(a.beta);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
 
   const int jt = wave;   // my dS tiles: (ct, jt), ct = 0..7
@@ -561,22 +573,28 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   };
   ChainOps ops;
   if (N > 0) {
-    chain_issue(ops, chunk_mats(a, bh, N, N - 1), dO, be, chunk_of(N - 1), a.H, tid);
+    chain_issue<0>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<1>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<2>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
     chain_commit(ops, L, sDO, tid);
     __syncthreads();
   }
   for (int n = N - 1; n >= 0; --n) {
-    // chunk-end adjoint of this chunk (bf16, transposed: [j][c])
+    // chunk-end adjoint of this chunk (bf16, in 16 x 16 tiles: tile (j/16, c/16)
+    // at position 8 (j/16) + c/16, [j%16][c%16] inside): one wave store
+    // writes one whole tile, 512 contiguous bytes
     bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       bf16x4 x;
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = (bf16)dS[u][r];
-      *reinterpret_cast<bf16x4*>(adj + (16 * jt + i) * D + 16 * u + 4 * g4) = x;
+      *reinterpret_cast<bf16x4*>(adj + (8 * jt + u) * 256 + 16 * i + 4 * g4) = x;
     }
     // the next chunk's operands, in flight during this chunk's products
-    if (n > 0) chain_issue(ops, chunk_mats(a, bh, N, n - 1), dO, be, chunk_of(n - 1), a.H, tid);
+    const Chunk cn = chunk_of(n > 0 ? n - 1 : 0);
+    const bf16* Amn = chunk_mats(a, bh, N, n > 0 ? n - 1 : 0);
+    if (n > 0) chain_issue<0>(ops, Amn, dO, cn, a.H, tid);
     // (gamma . dS)^T (this chunk's operands are in LDS)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -586,6 +604,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
     }
     __syncthreads();
+    if (n > 0) chain_issue<1>(ops, Amn, dO, cn, a.H, tid);
     // dDelta = P^T dO + Kd (gamma . dS), stored transposed (over the gate
     // scratch); wave w: the four token tiles of value-column tile w, which
     // share their column operands
@@ -598,6 +617,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int x = 0; x < 4; ++x) st_tr(sDDT, P64, mT[x], 16 * jt, acc[x], lane);
     }
     __syncthreads();
+    if (n > 0) chain_issue<2>(ops, Amn, dO, cn, a.H, tid);
     // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed (over (gamma . dS)^T)
     {
       floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -702,7 +722,6 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const bf16* q = reinterpret_cast<const bf16*>(a.q);
   const bf16* k = reinterpret_cast<const bf16*>(a.k);
   const bf16* g = reinterpret_cast<const bf16*>(a.g);
-  const bf16* be = reinterpret_cast<const bf16*>(a.beta);
   const bf16* v = reinterpret_cast<const bf16*>(a.v);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
   Chunk c;
@@ -710,9 +729,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   c.nv = min(C, a.T - n * C);
   c.rstride = a.H * D;
   const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // [j][c]
-  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // [j][c]
+  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // 16 x 16 tiles
 
-  load_chunk(L, chunk_mats(a, bh, N, n), be, c, a.H, tid);
+  load_chunk(L, chunk_mats(a, bh, N, n), tid);
   for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
   if (tid < D) dgam[tid] = 0.f;
 
@@ -757,7 +776,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         xs[u] = ldg16(Sn + (J0 + jr) * D + cc + 8 * u);
-        xd[u] = ldg16(dSn + (J0 + jr) * D + cc + 8 * u);
+        xd[u] = ldg16(dSn + (8 * ((J0 + jr) >> 4) + (cc >> 4)) * 256 + 16 * ((J0 + jr) & 15) + 8 * u);
       }
       if (tv < c.nv) {
         xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);

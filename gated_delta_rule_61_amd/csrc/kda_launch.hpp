@@ -55,7 +55,7 @@ struct BackwardArgs {
   void* dq; void* dk; void* dv; void* dg; void* dbeta; float* dS0;
   int B, T, H;
   void* states;     // bf16 [B*H][N][d_v][d_k] chunk-entry states, transposed
-  void* adjoints;   // bf16 [B*H][N][d_v][d_k] adjoints of the chunk-end states, transposed
+  void* adjoints;   // bf16 [B*H][N] adjoints of the chunk-end states, 16 x 16 tiles ([j][c] inside)
   void* mats;       // bf16 [B*H][N][2][64][64]: A = (I + L)^-1 and P^T of each chunk
 };
 size_t backward_workspace(int BH, int T);

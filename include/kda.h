@@ -219,9 +219,10 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   int B, int T, int H, int d_k, int d_v, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of kda_chunk_bwd: B*H*ceil(T/64) * 131584 for d = 128
+/* Workspace bytes of kda_chunk_bwd: B*H*ceil(T/64) * 131840 for d = 128
  * (per chunk, bf16: the chunk-entry state and chunk-end adjoint, two 64 x 64
- * matrices, three gated 64 x 128 key/query blocks, and 128 fp32 decays). */
+ * matrices, three gated 64 x 128 key/query blocks; then 128 fp32 decays and
+ * 64 fp32 betas). */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
 
 /*

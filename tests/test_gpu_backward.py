@@ -127,9 +127,11 @@ def test_chunk_states_and_adjoints(kda):
     ws = torch.zeros(kda.lib().kda_chunk_bwd_workspace_size(B, T, H, 128, 128, 1) // 2, dtype=torch.bfloat16,
                      device="cuda")
     _run(kda, inp, workspace=ws)
-    nst = B * H * N * 128 * 128          # states, then adjoints, then per-chunk 64 x 64 matrices
-    states = ws[:nst].view(B * H, N, 128, 128).transpose(-1, -2)
-    adj = ws[nst:2 * nst].view(B * H, N, 128, 128).transpose(-1, -2)
+    nst = B * H * N * 128 * 128          # states, then adjoints, then per-chunk operand blocks
+    states = ws[:nst].view(B * H, N, 128, 128).transpose(-1, -2)          # stored [j][c]
+    # adjoints in 16 x 16 tiles: tile (j/16, c/16) at 8 (j/16) + c/16, [j%16][c%16] inside
+    adj = (ws[nst:2 * nst].view(B * H, N, 8, 8, 16, 16).permute(0, 1, 2, 4, 3, 5)
+           .reshape(B * H, N, 128, 128).transpose(-1, -2))
     ref = _oracle(inp, chunk_adjoints=True)["dS_chunks"]          # [B,H,N,dk,dv], adjoint at chunk start
     for bh in range(B * H):
         b, h = divmod(bh, H)
