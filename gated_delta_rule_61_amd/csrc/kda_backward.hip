@@ -659,6 +659,16 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   }
 }
 
+// Element offset, in a chunk state stored by the forward's state mode (the
+// owners' fragment order: 16 x 16 blocks 8 (2 o + nt) + rt, o = j / 32), of
+// key rows 16 ct .. 16 ct + 15 of value column j (16 contiguous elements).
+// The owners' two column tiles interleave in groups of four: column j' = j % 32
+// is lane 4 (j' / 8) + j' % 4 of tile (j' / 4) % 2.
+__device__ __forceinline__ int state_off(int j, int ct) {
+  const int jp = j & 31, nt = (jp >> 2) & 1, l16 = 4 * (jp >> 3) + (jp & 3);
+  return (8 * (2 * (j >> 5) + nt) + ct) * 256 + 16 * l16;
+}
+
 // ---------------------------------------------------------------- gradients
 namespace gr {
 constexpr int O_KG = 0;
@@ -728,7 +738,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
   c.nv = min(C, a.T - n * C);
   c.rstride = a.H * D;
-  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // [j][c]
+  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // fragment order
   const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // 16 x 16 tiles
 
   load_chunk(L, chunk_mats(a, bh, N, n), tid);
@@ -775,7 +785,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       Vec16 xs[2], xd[2], xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        xs[u] = ldg16(Sn + (J0 + jr) * D + cc + 8 * u);
+        xs[u] = ldg16(Sn + state_off(J0 + jr, cc >> 4) + 8 * u);
         xd[u] = ldg16(dSn + (8 * ((J0 + jr) >> 4) + (cc >> 4)) * 256 + 16 * ((J0 + jr) & 15) + 8 * u);
       }
       if (tv < c.nv) {

@@ -54,7 +54,7 @@ struct BackwardArgs {
   const float* S0; const void* dO; const float* dS_T;
   void* dq; void* dk; void* dv; void* dg; void* dbeta; float* dS0;
   int B, T, H;
-  void* states;     // bf16 [B*H][N][d_v][d_k] chunk-entry states, transposed
+  void* states;     // bf16 [B*H][N] chunk-entry states, in the forward owners' fragment order
   void* adjoints;   // bf16 [B*H][N] adjoints of the chunk-end states, 16 x 16 tiles ([j][c] inside)
   void* mats;       // bf16 [B*H][N][2][64][64]: A = (I + L)^-1 and P^T of each chunk
 };

@@ -1286,6 +1286,11 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
 // runs in registers (DPP row shifts across the 16 token groups), and the
 // transposed operands are written 4 tokens at a time.
 // ---------------------------------------------------------------------------
+// Internal template flag of fused_pipe_kernel, beside the variant bits: the
+// state-mode instantiation (chunk-entry states out, no outputs), so that the
+// forward proper carries none of its code.
+constexpr int kPipeStates = 4;
+
 namespace pipe {
 
 constexpr int DK = 128, DV = 128;
@@ -1421,10 +1426,15 @@ __device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], fl
       for (int j = 0; j < 4; ++j) out[(16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
 }
 
-// The same tiles as bf16 into a transposed [d_v][d_k] matrix: a lane's four
-// rows of one column are contiguous there (one 8-byte store each).
+// The same tiles as bf16 in the owners' fragment order: owner o = col0 / 32,
+// tile (nt, rt) is the 256-element block 8 (2 o + nt) + rt, inside which
+// lane (g, i) holds elements 16 i + 4 g .. + 3, i.e. rows 16 rt + 4 g .. + 3
+// of value column col0 + vcol(nt, i).  Each wave store writes one whole
+// block (512 contiguous bytes), and the 16 key rows 16 rt .. + 15 of one
+// value column are 32 contiguous bytes.
 __device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], bf16* out, int col0, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
+  const int o = col0 >> 5;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -1432,7 +1442,7 @@ __device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], bf
       bf16x4 x;
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = (bf16)S[nt][rt][j];
-      *reinterpret_cast<bf16x4*>(out + (col0 + vcol(nt, l16)) * DK + 16 * rt + 4 * g4) = x;
+      *reinterpret_cast<bf16x4*>(out + (8 * (2 * o + nt) + rt) * 256 + 16 * l16 + 4 * g4) = x;
     }
 }
 
@@ -2085,6 +2095,7 @@ template <int V>
 __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   using namespace pipe;
   constexpr bool ND = (V & kVarNoDelta) != 0;
+  constexpr bool ST = (V & kPipeStates) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2114,7 +2125,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     }
     if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
     if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
-    if (a.states) outp = false;   // chunk-entry states only
+    if (ST) outp = false;   // chunk-entry states only
   } else {
     const int njobs = a.pass == 1 ? 2 * a.nseg - 3 : a.nseg - 1;
     head = blockIdx.x / njobs;
@@ -2210,7 +2221,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
               make_rsrc(reinterpret_cast<bf16*>(a.o) + tok0 * DV, chunk_bytes(nv, a.H * DV, DV, 2));
           owner_store(O, ro, a.H * DV, col0, lane);
         }
-        if (a.states)
+        if constexpr (ST)
           store_state_t(S, reinterpret_cast<bf16*>(a.states) + ((int64_t)head * ((a.T + C - 1) / C) + c0 + n) * DK * DV,
                         col0, lane);
         owner_state(p, Df, S, n & 1, lane);
@@ -2489,6 +2500,8 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
 }
 
 static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
+  // chunk-entry states (for the backward): KDA only, one pass
+  if (a.states) return a.variant == 0 && a.nseg < 3 ? launch_pipe_v<kPipeStates>(a, s) : hipErrorInvalidValue;
   switch (a.variant) {
     case 0: return launch_pipe_v<0>(a, s);
     case kVarScalarGate: return launch_pipe_v<kVarScalarGate>(a, s);

@@ -128,7 +128,13 @@ def test_chunk_states_and_adjoints(kda):
                      device="cuda")
     _run(kda, inp, workspace=ws)
     nst = B * H * N * 128 * 128          # states, then adjoints, then per-chunk operand blocks
-    states = ws[:nst].view(B * H, N, 128, 128).transpose(-1, -2)          # stored [j][c]
+    # states in the forward owners' fragment order: block 8 (2 o + nt) + rt,
+    # [i][c % 16] inside, value column 32 o + 8 (i / 4) + 4 nt + i % 4
+    blk = ws[:nst].view(B * H, N, 4, 2, 8, 16, 16)                     # o, nt, rt, i, c%16
+    jcol = torch.tensor([[32 * o + 8 * (i // 4) + 4 * nt + i % 4 for i in range(16)] for o in range(4)
+                         for nt in range(2)], device=ws.device).view(-1)   # (o, nt, i) -> j
+    states = torch.empty(B * H, N, 128, 128, dtype=ws.dtype, device=ws.device)   # [c][j]
+    states[:, :, :, jcol] = blk.permute(0, 1, 4, 6, 2, 3, 5).reshape(B * H, N, 128, 128)
     # adjoints in 16 x 16 tiles: tile (j/16, c/16) at 8 (j/16) + c/16, [j%16][c%16] inside
     adj = (ws[nst:2 * nst].view(B * H, N, 8, 8, 16, 16).permute(0, 1, 2, 4, 3, 5)
            .reshape(B * H, N, 128, 128).transpose(-1, -2))
