@@ -659,16 +659,6 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   }
 }
 
-// Element offset, in a chunk state stored by the forward's state mode (the
-// owners' fragment order: 16 x 16 blocks 8 (2 o + nt) + rt, o = j / 32), of
-// key rows 16 ct .. 16 ct + 15 of value column j (16 contiguous elements).
-// The owners' two column tiles interleave in groups of four: column j' = j % 32
-// is lane 4 (j' / 8) + j' % 4 of tile (j' / 4) % 2.
-__device__ __forceinline__ int state_off(int j, int ct) {
-  const int jp = j & 31, nt = (jp >> 2) & 1, l16 = 4 * (jp >> 3) + (jp & 3);
-  return (8 * (2 * (j >> 5) + nt) + ct) * 256 + 16 * l16;
-}
-
 // ---------------------------------------------------------------- gradients
 namespace gr {
 constexpr int O_KG = 0;
@@ -776,17 +766,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   for (int jh = 0; jh < 2; ++jh) {
     const int J0 = 64 * jh;
     __syncthreads();
-    // S[:, J] and gamma . dS[:, J] in their stored order [j][c] (thread: value
-    // column j = tid / 8, channels 16 (tid % 8) .. + 16), V[:, J] and dO[:, J]
-    // (rows past nv zero); every load issued before the first store.
+    // S[:, J] and gamma . dS[:, J] as [j][c] rows, V[:, J] and dO[:, J] (rows
+    // past nv zero); every load issued before the first store.  The half's S
+    // (blocks 32 jh .. 32 jh + 31 of the owners' fragment order) and dS
+    // (tiles 32 jh .. of 16 x 16) are each 16 KB contiguous: piece p = tid,
+    // tid + 512 is the 16 bytes at 8 p of it, channels 8 (p % 2) .. + 8 of
+    // row p / 2 % 16 of block p / 32.
     {
-      const int jr = tid >> 3, cc = 16 * (tid & 7);
       const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
       Vec16 xs[2], xd[2], xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        xs[u] = ldg16(Sn + state_off(J0 + jr, cc >> 4) + 8 * u);
-        xd[u] = ldg16(dSn + (8 * ((J0 + jr) >> 4) + (cc >> 4)) * 256 + 16 * ((J0 + jr) & 15) + 8 * u);
+        const int pc = tid + u * NT;
+        xs[u] = ldg16(Sn + 32 * 256 * jh + 8 * pc);
+        xd[u] = ldg16(dSn + 32 * 256 * jh + 8 * pc);
       }
       if (tv < c.nv) {
         xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);
@@ -794,13 +787,19 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        const int pc = tid + u * NT, blk = pc >> 5, row = (pc >> 1) & 15, ch = 8 * (pc & 1);
+        // S: block 32 jh + blk = 8 (2 o + nt) + rt, row = lane i of tile nt
+        const int bs_ = 32 * jh + blk, ot = bs_ >> 3, rt = bs_ & 7;
+        const int js = 32 * (ot >> 1) + 8 * (row >> 2) + 4 * (ot & 1) + (row & 3) - J0;
+        *reinterpret_cast<Vec16*>(hS + js * P128 + 16 * rt + ch) = xs[u];
+        // dS: tile 32 jh + blk = 8 (j / 16) + c / 16, row = j % 16
+        const int bd = 32 * jh + blk, jd = 16 * (bd >> 3) + row - J0, cd = 16 * (bd & 7) + ch;
         float fd[8];
         vec_to_f32<bf16>(xd[u], fd);
         bf16x8 y;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (bf16)(L.gam[cc + 8 * u + e] * fd[e]);
-        *reinterpret_cast<Vec16*>(hS + jr * P128 + cc + 8 * u) = xs[u];
-        *reinterpret_cast<bf16x8*>(hDSG + jr * P128 + cc + 8 * u) = y;
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)(L.gam[cd + e] * fd[e]);
+        *reinterpret_cast<bf16x8*>(hDSG + jd * P128 + cd) = y;
       }
       *reinterpret_cast<Vec16*>(hV + tv * P64 + xv0) = xv;
       *reinterpret_cast<Vec16*>(hDO + tv * P64 + xv0) = xo;
