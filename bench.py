@@ -164,8 +164,8 @@ def measure_backward(kda, W, torch, pcfg, inp, args, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels here are "
+              "one GPU's share of a head-sharded job and have no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.calibrate_copy:

@@ -90,7 +90,7 @@ def _fwd(lib, q, k, v, g, beta, S0, flags=0):
 
 
 def _pins_fail(lib):
-    """Return the names of the pins this build fails."""
+    """Return the names of the pins that the oracle library `lib` fails."""
     rng = np.random.default_rng(7)
     fails = []
     # P5 hand-worked example
