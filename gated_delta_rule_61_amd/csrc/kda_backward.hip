@@ -72,14 +72,14 @@ __device__ __forceinline__ bf16x4 fr_tr(const bf16* p, int ld, int m0, int k, in
 // Out tile (m0.., n0..) += sum_{k < K} X[m][k] Z[n][k]; XR / ZR: X / Z stored
 // with k contiguous (else stored transposed, k = row).  C layout result:
 // lane (g, i) holds Out[m0 + 4g + r][n0 + i].
-template <bool XR, bool ZR>
+template <bool XR, bool ZR, bool SWAP = false>
 __device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int ldz, int m0, int n0, int K,
                                       floatx4 acc, int lane) {
   const int g = lane >> 4, i = lane & 15;
   for (int k = 0; k < K; k += 16) {
     const bf16x4 a = XR ? fr_row(X, ldx, m0 + i, k + 4 * g) : fr_tr(X, ldx, m0, k + 4 * g, lane);
     const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_tr(Z, ldz, n0, k + 4 * g, lane);
-    acc = MB::mma16(a, b, acc);
+    acc = SWAP ? MB::mma16(b, a, acc) : MB::mma16(a, b, acc);
   }
   return acc;
 }
@@ -88,7 +88,9 @@ __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f};
 
 // NTL tiles (m0[t].., n0..) of the same product shape sharing their Z
 // columns: each Z fragment is read once per 16-index step for all of them.
-template <bool XR, bool ZR, int NTL>
+// SWAP: the tiles are formed transposed (operands swapped), so lane (g, i)
+// holds Out[m0 + i][n0 + 4g + r]: four adjacent columns of one row.
+template <bool XR, bool ZR, int NTL, bool SWAP = false>
 __device__ __forceinline__ void mm_zs(const bf16* X, int ldx, const int (&m0)[NTL], const bf16* Z, int ldz, int n0,
                                       int K, floatx4 (&acc)[NTL], int lane) {
   const int g = lane >> 4, i = lane & 15;
@@ -97,7 +99,7 @@ __device__ __forceinline__ void mm_zs(const bf16* X, int ldx, const int (&m0)[NT
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
       const bf16x4 a = XR ? fr_row(X, ldx, m0[t] + i, k + 4 * g) : fr_tr(X, ldx, m0[t], k + 4 * g, lane);
-      acc[t] = MB::mma16(a, b, acc[t]);
+      acc[t] = SWAP ? MB::mma16(b, a, acc[t]) : MB::mma16(a, b, acc[t]);
     }
   }
 }
@@ -107,6 +109,15 @@ __device__ __forceinline__ void st_rm(bf16* dst, int ld, int m0, int n0, floatx4
   const int g = lane >> 4, i = lane & 15;
 #pragma unroll
   for (int r = 0; r < 4; ++r) dst[(m0 + 4 * g + r) * ld + n0 + i] = (bf16)v[r];
+}
+// Transposed-layout tile (lane: row m0 + i, columns n0 + 4g ..) -> row-major
+// dst[m][n] (8-byte stores)
+__device__ __forceinline__ void st_rm8(bf16* dst, int ld, int m0, int n0, floatx4 v, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  bf16x4 x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (bf16)v[r];
+  *reinterpret_cast<bf16x4*>(dst + (m0 + i) * ld + n0 + 4 * g) = x;
 }
 // C-layout tile -> transposed row-major dst[n][m] (8-byte stores)
 __device__ __forceinline__ void st_tr(bf16* dst, int ld, int m0, int n0, floatx4 v, int lane) {
@@ -680,7 +691,7 @@ constexpr int H_V = H_DSG + C * P128 * 2;      // V[:, J]        [64][P64]
 constexpr int H_DO = H_V + C * P64 * 2;        // dO[:, J]
 constexpr int H_D = H_DO + C * P64 * 2;        // Delta[:, J]
 constexpr int H_DD = H_D + C * P64 * 2;        // dDelta[:, J]
-constexpr int H_XT = H_DD + C * P64 * 2;       // (beta . (V - Kg S))^T [64 j][P64]
+constexpr int H_XT = H_DD + C * P64 * 2;       // X = beta . (V - Kg S) [64 t][P64]; then dV[:, J]
 constexpr int H_END = H_XT + C * P64 * 2;
 // after the halves
 constexpr int Q_DW = 0;                        // dW row-major [64][P128]
@@ -810,29 +821,29 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     const int jj = wave & 3, tA = wave >> 2;
     const int mT[2] = {16 * tA, 16 * (tA + 2)};
     {
+      // (lane: token mT + i, value columns 16 jj + 4 g4 ..)
       floatx4 ks[2] = {zero4(), zero4()};
-      mm_zs<true, true, 2>(L.Kg, P128, mT, hS, P128, 16 * jj, D, ks, lane);
+      mm_zs<true, true, 2, true>(L.Kg, P128, mT, hS, P128, 16 * jj, D, ks, lane);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
+        const int t = mT[x] + i;
+        const bf16x4 vv = *reinterpret_cast<const bf16x4*>(hV + t * P64 + 16 * jj + 4 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = mT[x] + 4 * g4 + r;
-          ks[x][r] = L.beta[t] * ((float)hV[t * P64 + 16 * jj + i] - ks[x][r]);
-        }
-        st_tr(hXT, P64, mT[x], 16 * jj, ks[x], lane);
+        for (int r = 0; r < 4; ++r) ks[x][r] = L.beta[t] * ((float)vv[r] - ks[x][r]);
+        st_rm8(hXT, P64, mT[x], 16 * jj, ks[x], lane);
       }
     }
     __syncthreads();
     // Delta = A X; dDelta = P^T dO + Kd (gamma . dS); both row-major
     {
       floatx4 dl[2] = {zero4(), zero4()}, dd[2] = {zero4(), zero4()};
-      mm_zs<true, true, 2>(L.A, P64, mT, hXT, P64, 16 * jj, C, dl, lane);
-      mm_zs<true, false, 2>(L.PT, P64, mT, hDO, P64, 16 * jj, C, dd, lane);
-      mm_zs<true, true, 2>(L.Kd, P128, mT, hDSG, P128, 16 * jj, D, dd, lane);
+      mm_zs<true, false, 2, true>(L.A, P64, mT, hXT, P64, 16 * jj, C, dl, lane);
+      mm_zs<true, false, 2, true>(L.PT, P64, mT, hDO, P64, 16 * jj, C, dd, lane);
+      mm_zs<true, true, 2, true>(L.Kd, P128, mT, hDSG, P128, 16 * jj, D, dd, lane);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        st_rm(hD, P64, mT[x], 16 * jj, dl[x], lane);
-        st_rm(hDD, P64, mT[x], 16 * jj, dd[x], lane);
+        st_rm8(hD, P64, mT[x], 16 * jj, dl[x], lane);
+        st_rm8(hDD, P64, mT[x], 16 * jj, dd[x], lane);
       }
     }
     __syncthreads();
@@ -856,8 +867,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       if (tq < 10) {
         int I, J;
         lower_tile(tq, I, J);
-        aM[x] = mm<true, true>(hDO, P64, hD, P64, 16 * I, 16 * J, 64, aM[x], lane);
-        aA[x] = mm<true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
+        // (transposed tiles: lane holds row 16 I + i, columns 16 J + 4 g4 ..)
+        aM[x] = mm<true, true, true>(hDO, P64, hD, P64, 16 * I, 16 * J, 64, aM[x], lane);
+        aA[x] = mm<true, true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
       }
     }
     // dV[:, J] = Diag(beta) A^T dDelta, staged row-major where X^T was (dead
@@ -926,21 +938,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       int I, J;
       lower_tile(tq, I, J);
       floatx4 m = aM[x];
+      const int t = 16 * I + i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
+        const int s = 16 * J + 4 * g4 + r;
         if (t == s) md[t] = m[r];
         m[r] = t > s ? m[r] : 0.f;
       }
-      st_rm(qM, P64, 16 * I, 16 * J, m, lane);
+      st_rm8(qM, P64, 16 * I, 16 * J, m, lane);
       // dA = (dDelta V^T + dW Kg^T) Diag(beta), strictly lower
-      floatx4 da = mm<true, true>(qDW, P128, L.Kg, P128, 16 * I, 16 * J, D, aA[x], lane);
+      floatx4 da = mm<true, true, true>(qDW, P128, L.Kg, P128, 16 * I, 16 * J, D, aA[x], lane);
+      const floatx4 bs4 = *reinterpret_cast<const floatx4*>(L.beta + 16 * J + 4 * g4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
-        da[r] = t > s ? da[r] * L.beta[s] : 0.f;
-      }
-      st_rm(qDA, P64, 16 * I, 16 * J, da, lane);
+      for (int r = 0; r < 4; ++r) da[r] = t > 16 * J + 4 * g4 + r ? da[r] * bs4[r] : 0.f;
+      st_rm8(qDA, P64, 16 * I, 16 * J, da, lane);
     }
   }
   __syncthreads();
@@ -949,9 +960,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const int mT[2] = {16 * (wave >> 2), 16 * ((wave >> 2) + 2)};
   {
     floatx4 z[2] = {zero4(), zero4()};
-    mm_zs<true, true, 2>(L.A, P64, mT, qDA, P64, 16 * (wave & 3), C, z, lane);
+    mm_zs<true, true, 2, true>(L.A, P64, mT, qDA, P64, 16 * (wave & 3), C, z, lane);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) st_rm(qZ1T, P64, mT[x], 16 * (wave & 3), z[x], lane);
+    for (int x = 0; x < 2; ++x) st_rm8(qZ1T, P64, mT[x], 16 * (wave & 3), z[x], lane);
   }
   // [t][c]: M Kd, M^T Qg, A^T dW
   const int mU[4] = {0, 16, 32, 48};
@@ -990,16 +1001,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     if (tq < 10) {
       int I, J;
       lower_tile(tq, I, J);
-      floatx4 l = mm<false, true>(L.A, P64, qZ1T, P64, 16 * I, 16 * J, C, zero4(), lane);
+      // (transposed tile: lane holds row t = 16 I + i, columns 16 J + 4 g4 ..)
+      floatx4 l = mm<false, true, true>(L.A, P64, qZ1T, P64, 16 * I, 16 * J, C, zero4(), lane);
       floatx4 gg;
+      const int t = 16 * I + i;
+      const float bt = L.beta[t];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * g4 + r, s = 16 * J + i;
-        l[r] = t > s ? -l[r] : 0.f;
-        gg[r] = l[r] * L.beta[t];
+        l[r] = t > 16 * J + 4 * g4 + r ? -l[r] : 0.f;
+        gg[r] = l[r] * bt;
       }
-      st_rm(qDL, P64, 16 * I, 16 * J, l, lane);
-      st_rm(qDG, P64, 16 * I, 16 * J, gg, lane);
+      st_rm8(qDL, P64, 16 * I, 16 * J, l, lane);
+      st_rm8(qDG, P64, 16 * I, 16 * J, gg, lane);
     }
   }
   __syncthreads();
