@@ -742,9 +742,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // fragment order
   const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // 16 x 16 tiles
 
-  load_chunk(L, chunk_mats(a, bh, N, n), tid);
-  for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
-  if (tid < D) dgam[tid] = 0.f;
+  ChunkOps ops;
+  ops_issue(ops, chunk_mats(a, bh, N, n), tid);
 
   // persistent accumulators
   const int c0 = 16 * wave;     // my channel block
@@ -774,28 +773,39 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   // of S (gamma . dS)^T, wave w forming its diagonal tile (channels 16w..)
   floatx4 aSD = zero4();
 
+  // Staging of a value half: S[:, J] and gamma . dS[:, J] as [j][c] rows,
+  // V[:, J] and dO[:, J] (rows past nv zero).  The half's S (blocks
+  // 32 jh .. 32 jh + 31 of the owners' fragment order) and dS (tiles 32 jh ..
+  // of 16 x 16) are each 16 KB contiguous: piece p = tid, tid + 512 is the
+  // 16 bytes at 8 p of it, channels 8 (p % 2) .. + 8 of row p / 2 % 16 of
+  // block p / 32.  The loads of half 0 are issued with the chunk's operand
+  // block, those of half 1 during half 0's products.
+  const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
+  Vec16 xs[2], xd[2], xv, xo;
+  auto half_issue = [&](int jh) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = tid + u * NT;
+      xs[u] = ldg16(Sn + 32 * 256 * jh + 8 * pc);
+      xd[u] = ldg16(dSn + 32 * 256 * jh + 8 * pc);
+    }
+    xv = xo = Vec16{{0u, 0u, 0u, 0u}};
+    if (tv < c.nv) {
+      xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + 64 * jh + xv0);
+      xo = ldg16(dO + (c.row0 + (int64_t)tv * a.H) * D + 64 * jh + xv0);
+    }
+  };
+  half_issue(0);
+  ops_commit(ops, L, tid);
+  for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
+  if (tid < D) dgam[tid] = 0.f;
+  __syncthreads();
+
+#pragma unroll
   for (int jh = 0; jh < 2; ++jh) {
     const int J0 = 64 * jh;
-    __syncthreads();
-    // S[:, J] and gamma . dS[:, J] as [j][c] rows, V[:, J] and dO[:, J] (rows
-    // past nv zero); every load issued before the first store.  The half's S
-    // (blocks 32 jh .. 32 jh + 31 of the owners' fragment order) and dS
-    // (tiles 32 jh .. of 16 x 16) are each 16 KB contiguous: piece p = tid,
-    // tid + 512 is the 16 bytes at 8 p of it, channels 8 (p % 2) .. + 8 of
-    // row p / 2 % 16 of block p / 32.
+    if (jh > 0) __syncthreads();
     {
-      const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
-      Vec16 xs[2], xd[2], xv = {{0u, 0u, 0u, 0u}}, xo = {{0u, 0u, 0u, 0u}};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pc = tid + u * NT;
-        xs[u] = ldg16(Sn + 32 * 256 * jh + 8 * pc);
-        xd[u] = ldg16(dSn + 32 * 256 * jh + 8 * pc);
-      }
-      if (tv < c.nv) {
-        xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);
-        xo = ldg16(dO + (c.row0 + (int64_t)tv * a.H) * D + J0 + xv0);
-      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int pc = tid + u * NT, blk = pc >> 5, row = (pc >> 1) & 15, ch = 8 * (pc & 1);
@@ -848,6 +858,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
     __syncthreads();
     // [t][c] products over this half's value columns
+    if (jh == 0) half_issue(1);
     // (dO S^T, Delta (g.dS)^T, dDelta S^T: the S and g.dS fragments of a step
     // serve all four row tiles; the diagonal tile of S (g.dS)^T alongside)
     for (int k = 0; k < 64; k += 16) {
@@ -900,6 +911,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (4 * g4 + r == i) dgam[c0 + i] = aSD[r];
+  // the assembly's inputs g, q, k (rows past nv zero), in flight during the
+  // 64 x 64 products
+  Vec16 xg[2], xq[2], xk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+    xg[u] = xq[u] = xk[u] = Vec16{{0u, 0u, 0u, 0u}};
+    if (t < c.nv) {
+      const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
+      xg[u] = ldg16(g + off);
+      xq[u] = ldg16(q + off);
+      xk[u] = ldg16(k + off);
+    }
+  }
   // fold dKb~ into dKd, keeping its column sums against Kd (chunk-end terms)
   float colsum = 0.f;   // sum over my rows of Kd . dKb~ for column c0 + i
 #pragma unroll
@@ -1040,18 +1065,6 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* zq = reinterpret_cast<bf16*>(work + gr::Z_Q);
   bf16* zk = reinterpret_cast<bf16*>(work + gr::Z_K);
   {
-    Vec16 xg[2], xq[2], xk[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
-      xg[u] = xq[u] = xk[u] = Vec16{{0u, 0u, 0u, 0u}};
-      if (t < c.nv) {
-        const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
-        xg[u] = ldg16(g + off);
-        xq[u] = ldg16(q + off);
-        xk[u] = ldg16(k + off);
-      }
-    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
