@@ -68,6 +68,16 @@ __device__ __forceinline__ bf16x4 fr_tr(const bf16* p, int ld, int m0, int k, in
   const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
   return __builtin_bit_cast(bf16x4, x);
 }
+// The same for a 32-index slab and v_mfma_f32_16x16x32_bf16 (lane group g:
+// indices k..k+7 with k = slab + 8g): one 16-byte read, or two transpose
+// reads (indices k..k+3, k+4..k+7).
+__device__ __forceinline__ bf16x8 fr_row8(const bf16* p, int ld, int row, int k) {
+  return *reinterpret_cast<const bf16x8*>(p + row * ld + k);
+}
+__device__ __forceinline__ bf16x8 fr_tr8(const bf16* p, int ld, int m0, int k, int lane) {
+  const bf16x4 lo = fr_tr(p, ld, m0, k, lane), hi = fr_tr(p, ld, m0, k + 4, lane);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Out tile (m0.., n0..) += sum_{k < K} X[m][k] Z[n][k]; XR / ZR: X / Z stored
 // with k contiguous (else stored transposed, k = row).  C layout result:
@@ -76,10 +86,10 @@ template <bool XR, bool ZR, bool SWAP = false>
 __device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int ldz, int m0, int n0, int K,
                                       floatx4 acc, int lane) {
   const int g = lane >> 4, i = lane & 15;
-  for (int k = 0; k < K; k += 16) {
-    const bf16x4 a = XR ? fr_row(X, ldx, m0 + i, k + 4 * g) : fr_tr(X, ldx, m0, k + 4 * g, lane);
-    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_tr(Z, ldz, n0, k + 4 * g, lane);
-    acc = SWAP ? MB::mma16(b, a, acc) : MB::mma16(a, b, acc);
+  for (int k = 0; k < K; k += 32) {
+    const bf16x8 a = XR ? fr_row8(X, ldx, m0 + i, k + 8 * g) : fr_tr8(X, ldx, m0, k + 8 * g, lane);
+    const bf16x8 b = ZR ? fr_row8(Z, ldz, n0 + i, k + 8 * g) : fr_tr8(Z, ldz, n0, k + 8 * g, lane);
+    acc = SWAP ? MB::mma32(b, a, acc) : MB::mma32(a, b, acc);
   }
   return acc;
 }
@@ -94,12 +104,12 @@ template <bool XR, bool ZR, int NTL, bool SWAP = false>
 __device__ __forceinline__ void mm_zs(const bf16* X, int ldx, const int (&m0)[NTL], const bf16* Z, int ldz, int n0,
                                       int K, floatx4 (&acc)[NTL], int lane) {
   const int g = lane >> 4, i = lane & 15;
-  for (int k = 0; k < K; k += 16) {
-    const bf16x4 b = ZR ? fr_row(Z, ldz, n0 + i, k + 4 * g) : fr_tr(Z, ldz, n0, k + 4 * g, lane);
+  for (int k = 0; k < K; k += 32) {
+    const bf16x8 b = ZR ? fr_row8(Z, ldz, n0 + i, k + 8 * g) : fr_tr8(Z, ldz, n0, k + 8 * g, lane);
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
-      const bf16x4 a = XR ? fr_row(X, ldx, m0[t] + i, k + 4 * g) : fr_tr(X, ldx, m0[t], k + 4 * g, lane);
-      acc[t] = SWAP ? MB::mma16(b, a, acc[t]) : MB::mma16(a, b, acc[t]);
+      const bf16x8 a = XR ? fr_row8(X, ldx, m0[t] + i, k + 8 * g) : fr_tr8(X, ldx, m0[t], k + 8 * g, lane);
+      acc[t] = SWAP ? MB::mma32(b, a, acc[t]) : MB::mma32(a, b, acc[t]);
     }
   }
 }
@@ -861,14 +871,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     if (jh == 0) half_issue(1);
     // (dO S^T, Delta (g.dS)^T, dDelta S^T: the S and g.dS fragments of a step
     // serve all four row tiles; the diagonal tile of S (g.dS)^T alongside)
-    for (int k = 0; k < 64; k += 16) {
-      const bf16x4 fs = fr_tr(hS, P128, c0, k + 4 * g4, lane), fd = fr_tr(hDSG, P128, c0, k + 4 * g4, lane);
-      aSD = MB::mma16(fs, fd, aSD);
+    for (int k = 0; k < 64; k += 32) {
+      const bf16x8 fs = fr_tr8(hS, P128, c0, k + 8 * g4, lane), fd = fr_tr8(hDSG, P128, c0, k + 8 * g4, lane);
+      aSD = MB::mma32(fs, fd, aSD);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        aQg[u] = MB::mma16(fr_row(hDO, P64, 16 * u + i, k + 4 * g4), fs, aQg[u]);
-        aKb[u] = MB::mma16(fr_row(hD, P64, 16 * u + i, k + 4 * g4), fd, aKb[u]);
-        aW[u] = MB::mma16(fr_row(hDD, P64, 16 * u + i, k + 4 * g4), fs, aW[u]);
+        aQg[u] = MB::mma32(fr_row8(hDO, P64, 16 * u + i, k + 8 * g4), fs, aQg[u]);
+        aKb[u] = MB::mma32(fr_row8(hD, P64, 16 * u + i, k + 8 * g4), fd, aKb[u]);
+        aW[u] = MB::mma32(fr_row8(hDD, P64, 16 * u + i, k + 8 * g4), fs, aW[u]);
       }
     }
     // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
