@@ -1766,44 +1766,86 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
 
 __device__ __forceinline__ int ln_block(int I, int J) { return I * (I - 1) / 2 + J; }
 
+// One tile (I, J) of P = Tril(Qt Kh^T) (isP) or of L = Diag(beta) Kt Kh^T,
+// stored as -L, both fp16, from its transposed accumulator (lane: row l16,
+// columns 4g..4g+3).
+__device__ __forceinline__ void lp_store(const Ptr& p, bool isP, int I, int J, floatx4 acc, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  f16x4 v;
+  if (isP) {
+    float dg = 0.f;
+    if (I == J) {
+      const int row = 16 * I + l16;
+      float sp[NQK];
+#pragma unroll
+      for (int u = 0; u < NQK; ++u) sp[u] = p.qk[u * C + row];
+#pragma unroll
+      for (int st = 1; st < NQK; st *= 2)
+#pragma unroll
+        for (int u = 0; u + st < NQK; u += 2 * st) sp[u] += sp[u + st];
+      dg = sp[0];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float x = (I > J || l16 >= 4 * g4 + jj) ? acc[jj] : 0.f;
+      if (I == J && l16 == 4 * g4 + jj) x = dg;
+      v[jj] = (f16)x;
+    }
+    *reinterpret_cast<f16x4*>(p.P + (16 * I + l16) * LDT + slot32(16 * J + 4 * g4)) = v;
+  } else {
+    const float bt = -p.beta[16 * I + l16];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(acc[jj] * bt);
+    *reinterpret_cast<f16x4*>(p.Ln + ln_block(I, J) * 16 * LDB + l16 * LDB + 4 * g4) = v;
+  }
+}
+
 // Workers in phase 2a: blocks (I_t, J_t) of P = Tril(Qt Kh^T) (isP[t]) and
 // off-diagonal blocks of L = Diag(beta) Kt Kh^T, stored as -L, all fp16.
 template <int NTL>
 __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[NTL], const int (&I)[NTL],
                                             const int (&J)[NTL], int lane) {
-  const int g4 = lane >> 4, l16 = lane & 15;
   floatx4 acc[NTL];
   kh_tiles<NTL, true>(p, isP, I, J, acc, lane);     // lane: row l16, columns 4g..4g+3
 #pragma unroll
-  for (int t = 0; t < NTL; ++t) {
-    f16x4 v;
-    if (isP[t]) {
-      float dg = 0.f;
-      if (I[t] == J[t]) {
-        const int row = 16 * I[t] + l16;
-        float sp[NQK];
+  for (int t = 0; t < NTL; ++t) lp_store(p, isP[t], I[t], J[t], acc[t], lane);
+}
+
+// The tiles of P (isP) or L in row blocks I0, I0 + 1 and column blocks J0,
+// J0 + 1 that are needed (all four below the diagonal; with I0 == J0 the
+// three of the lower triangle), from one read of those two row blocks of Qt
+// (or Kt) and of Kh: 16 fragments for three or four tiles instead of eight
+// per tile.
+template <bool DIAG>
+__device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J0, int lane) {
+  const int fl = frag_lane(lane);
+  const bf16* A = isP ? p.Qt : p.Kt;
+  MB::F32 af[2][DK / 32], bf[2][DK / 32];
 #pragma unroll
-        for (int u = 0; u < NQK; ++u) sp[u] = p.qk[u * C + row];
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int st = 1; st < NQK; st *= 2)
-#pragma unroll
-          for (int u = 0; u + st < NQK; u += 2 * st) sp[u] += sp[u + st];
-        dg = sp[0];
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float x = (I[t] > J[t] || l16 >= 4 * g4 + jj) ? acc[t][jj] : 0.f;
-        if (I[t] == J[t] && l16 == 4 * g4 + jj) x = dg;
-        v[jj] = (f16)x;
-      }
-      *reinterpret_cast<f16x4*>(p.P + (16 * I[t] + l16) * LDT + slot32(16 * J[t] + 4 * g4)) = v;
-    } else {
-      const float bt = -p.beta[16 * I[t] + l16];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] = (f16)(acc[t][jj] * bt);
-      *reinterpret_cast<f16x4*>(p.Ln + ln_block(I[t], J[t]) * 16 * LDB + l16 * LDB + 4 * g4) = v;
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      af[x][ks] = ldc_b(A + fl + frag_off(I0 + x, ks));
+      bf[x][ks] = ldc_b(p.Kh + fl + frag_off(J0 + x, ks));
     }
-  }
+  KDA_READS_FIRST();
+  floatx4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (!DIAG || y <= x) acc[x][y] = MB::mma32(bf[y][ks], af[x][ks], acc[x][y]);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      if (!DIAG || y <= x) lp_store(p, isP, I0 + x, J0 + y, acc[x][y], lane);
 }
 
 // Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32.
@@ -2231,11 +2273,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
       if (!ND && nxt) solver_block(p, o, lane);
-      // with outputs the workers form the P blocks and two of the L blocks;
-      // each owner forms one of the other four (L(1,0), L(3,2), L(3,1), L(3,0))
-      if (!ND && nxt && outp) {
+      // with outputs the workers form the P blocks and the L blocks (2-3) x
+      // (0-1); owners 0 and 1 form L(1,0) and L(3,2)
+      if (!ND && nxt && outp && o < 2) {
         const bool q[1] = {false};
-        const int I1[1] = {o == 0 ? 1 : 3}, J1[1] = {o == 0 ? 0 : o == 1 ? 2 : o == 2 ? 1 : 0};
+        const int I1[1] = {o == 0 ? 1 : 3}, J1[1] = {o == 0 ? 0 : 2};
         lp_block_tiles<1>(p, q, I1, J1, lane);
       }
       // values of chunk n+2: unconditional (zeros past the end), and after the
@@ -2322,16 +2364,15 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
                      lp_block_tiles<1>(p, q, I, J, lane); break; }
         }
       } else if (nxt) {
+        // P in three groups sharing operand rows (blocks 2-3 x 0-1; the
+        // lower triangles of 0-1 x 0-1 and of 2-3 x 2-3), and the L blocks
+        // (2-3) x (0-1); the owners form L(1,0), L(3,2) and the diagonal blocks
         worker_kbt<V>(p, kb, kt_t, w, lane);
         switch (w) {
-          case 0: { const bool q[3] = {1, 1, 1}; const int I[3] = {0, 3, 3}, J[3] = {0, 0, 3};
-                    lp_block_tiles<3>(p, q, I, J, lane); break; }
-          case 1: { const bool q[3] = {1, 1, 1}; const int I[3] = {1, 1, 3}, J[3] = {0, 1, 1};
-                    lp_block_tiles<3>(p, q, I, J, lane); break; }
-          case 2: { const bool q[3] = {1, 1, 0}; const int I[3] = {2, 2, 2}, J[3] = {0, 1, 0};
-                    lp_block_tiles<3>(p, q, I, J, lane); break; }
-          default: { const bool q[3] = {1, 1, 0}; const int I[3] = {2, 3, 2}, J[3] = {2, 2, 1};
-                     lp_block_tiles<3>(p, q, I, J, lane); break; }
+          case 0: lp_block22<false>(p, true, 2, 0, lane); break;
+          case 1: lp_block22<true>(p, true, 0, 0, lane); break;
+          case 2: lp_block22<true>(p, true, 2, 2, lane); break;
+          default: lp_block22<false>(p, false, 2, 0, lane); break;
         }
       }
       p.sync(smem_raw);
