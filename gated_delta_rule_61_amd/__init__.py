@@ -50,6 +50,8 @@ _SIGS = {
     "kda_varlen_schedule": ([_vp, _i, _i, _vp, _vp], _i),
     "kda_chunk_bwd": ([_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp], _i),
     "kda_chunk_bwd_workspace_size": ([_i] * 6, _sz),
+    "kda_chunk_bwd_ex": ([_vp] * 14 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_bwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -217,11 +219,13 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
     return o, S_T
 
 
-def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None):
+def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None,
+              scalar_gate=False):
     """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
     adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16,
-    d_k = d_v = 128."""
-    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta)
+    d_k = d_v = 128.  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet)."""
+    flags = _flags(scalar_gate, True)
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate=scalar_gate)
     _need(dO, (B, T, H, dv), dt, "dO")
     if S0 is not None:
         _need(S0, (B, H, dk, dv), torch.float32, "S0")
@@ -233,13 +237,13 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=N
                dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
     L = lib()
     code = _dtype(q)
-    wsz = L.kda_chunk_bwd_workspace_size(B, T, H, dk, dv, code)
+    wsz = L.kda_chunk_bwd_ex_workspace_size(B, T, H, dk, dv, code, flags)
     if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
         workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    _check(L.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
-                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
-                           _ptr(out["dS0"]), B, T, H, dk, dv, code, _ptr(workspace) if wsz else None, wsz,
-                           _stream(stream)))
+    _check(L.kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                              _ptr(out["dbeta"]), _ptr(out["dS0"]), B, T, H, dk, dv, code, flags,
+                              _ptr(workspace) if wsz else None, wsz, _stream(stream)))
     return out
 
 

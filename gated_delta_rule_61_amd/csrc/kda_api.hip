@@ -225,35 +225,65 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 
-size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
+size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
+  if ((flags & ~KDA_GATE_SCALAR) != 0) return 0;
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
-  return kda::backward_workspace(B * H, T);
+  size_t n = kda::backward_workspace(B * H, T);
+  // scalar gate: the broadcast gate (bf16) and the per-channel dg (fp32), [B,T,H,d_k] each
+  if (flags & KDA_GATE_SCALAR) n += (size_t)B * T * H * d_k * (2 + 4);
+  return n;
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
+  return kda_chunk_bwd_ex_workspace_size(B, T, H, d_k, d_v, dtype, 0);
+}
+
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, const float* S0,
+                     const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+                     float* dS0, int B, int T, int H, int d_k, int d_v, int dtype, int flags, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE((flags & ~KDA_GATE_SCALAR) == 0 && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  const bool sg = (flags & KDA_GATE_SCALAR) != 0;
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, dO, dtype, flags);
+    if (st) return st;
+    KDA_REQUIRE(dq && dk && dv && dg && dbeta, KDA_ERR_NULL);
+    KDA_REQUIRE(aligned16(dq) && aligned16(dk) && aligned16(dv) && (sg || aligned16(dg)) &&
+                (reinterpret_cast<uintptr_t>(dg) & 1u) == 0 && (reinterpret_cast<uintptr_t>(dbeta) & 1u) == 0,
+                KDA_ERR_ALIGN);
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(dS_T) && aligned16(dS0), KDA_ERR_ALIGN);
+  const size_t need = kda_chunk_bwd_ex_workspace_size(B, T, H, d_k, d_v, dtype, flags);
+  KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+  // workspace: chunk states, chunk-end adjoints (bf16 d_k x d_v each), the
+  // per-chunk operand blocks; then (scalar gate) the broadcast gate and the
+  // per-channel dg
+  char* ws = static_cast<char*>(workspace);
+  const size_t nst = (size_t)B * H * (size_t)((T + 63) / 64) * d_k * d_v * 2;
+  const size_t base = kda::backward_workspace(B * H, T);
+  const int64_t rows = (int64_t)B * T * H;
+  void* gfull = ws + base;
+  float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
+  kda::BackwardArgs a{q, k, v, sg ? gfull : g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H,
+                      workspace, ws + nst, ws + 2 * nst, sg ? dg32 : nullptr};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (sg && T > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);
+  if ((e = kda::launch_backward(a, s)) != hipSuccess) return hip_status(e);
+  if (sg && T > 0) return hip_status(kda::launch_gate_reduce(dg32, dg, rows, s));
+  return KDA_OK;
 }
 
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta, const float* S0,
                   const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                   float* dS0, int B, int T, int H, int d_k, int d_v, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
-  if (st) return st;
-  KDA_REQUIRE(variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
-  if ((int64_t)B * H == 0) return KDA_OK;
-  if (T > 0) {
-    st = check_tokens(q, k, v, g, beta, dO, dtype);
-    if (st) return st;
-    KDA_REQUIRE(dq && dk && dv && dg && dbeta, KDA_ERR_NULL);
-    KDA_REQUIRE(aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
-                (reinterpret_cast<uintptr_t>(dbeta) & 1u) == 0, KDA_ERR_ALIGN);
-  }
-  KDA_REQUIRE(aligned16(S0) && aligned16(dS_T) && aligned16(dS0), KDA_ERR_ALIGN);
-  const size_t need = kda::backward_workspace(B * H, T);
-  KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
-  KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
-  // workspace: chunk states, chunk-end adjoints (bf16 d_k x d_v each), then per-chunk operand blocks
-  const size_t nst = (size_t)B * H * (size_t)((T + 63) / 64) * d_k * d_v * 2;
-  kda::BackwardArgs a{q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H, workspace,
-                      static_cast<char*>(workspace) + nst, static_cast<char*>(workspace) + 2 * nst};
-  return hip_status(kda::launch_backward(a, (hipStream_t)stream));
+  return kda_chunk_bwd_ex(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H, d_k, d_v, dtype, 0,
+                          workspace, workspace_bytes, stream);
 }
 
 size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {

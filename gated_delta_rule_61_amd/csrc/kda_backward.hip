@@ -1121,10 +1121,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
       *reinterpret_cast<Vec16*>(dq + off) = *reinterpret_cast<const Vec16*>(zq + t * P128 + x0);
       *reinterpret_cast<Vec16*>(dk + off) = *reinterpret_cast<const Vec16*>(zk + t * P128 + x0);
-      bf16x8 y;
+      if (a.dg32) {
+        // fp32 per-channel dg (the scalar-gate path sums it over the channels)
+        *reinterpret_cast<floatx4*>(a.dg32 + off) = *reinterpret_cast<const floatx4*>(bs + t * PB + x0);
+        *reinterpret_cast<floatx4*>(a.dg32 + off + 4) = *reinterpret_cast<const floatx4*>(bs + t * PB + x0 + 4);
+      } else {
+        bf16x8 y;
 #pragma unroll
-      for (int uu = 0; uu < 8; ++uu) y[uu] = (bf16)bs[t * PB + x0 + uu];
-      *reinterpret_cast<bf16x8*>(dgo + off) = y;
+        for (int uu = 0; uu < 8; ++uu) y[uu] = (bf16)bs[t * PB + x0 + uu];
+        *reinterpret_cast<bf16x8*>(dgo + off) = y;
+      }
     }
   }
   if (tid < C && tid < c.nv) {
@@ -1134,7 +1140,50 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- scalar gate
+// A scalar gate g [rows] (one per token and head) is the per-channel gate with
+// every channel equal, so its gradient is the channel sum of the per-channel
+// gradient of the broadcast gate.  gate_expand: gfull[r][c] = g[r] (bf16,
+// 16-byte stores); gate_reduce: dg[r] = sum_c dg32[r][c] (fp32 sums, one
+// 16-lane row per token and head).
+__global__ __launch_bounds__(256) void gate_expand_kernel(const bf16* g, bf16* gfull, int64_t rows) {
+  const int64_t pieces = rows * (D / 8);
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * 256) {
+    const bf16 x = g[p / (D / 8)];
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x;
+    *reinterpret_cast<bf16x8*>(gfull + 8 * p) = y;
+  }
+}
+
+__global__ __launch_bounds__(256) void gate_reduce_kernel(const float* dg32, bf16* dg, int64_t rows) {
+  const int lane16 = threadIdx.x & 15;
+  for (int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; r < rows; r += (int64_t)gridDim.x * 16) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(dg32 + r * D + 8 * lane16);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(dg32 + r * D + 8 * lane16 + 4);
+    const float x = sum16(a[0] + a[1] + a[2] + a[3] + b[0] + b[1] + b[2] + b[3]);
+    if (lane16 == 0) dg[r] = (bf16)x;
+  }
+}
+
 }  // namespace bwd
+
+hipError_t launch_gate_expand(const void* g, void* gfull, int64_t rows, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows * (bwd::D / 8) + 255) / 256;
+  hipLaunchKernelGGL(bwd::gate_expand_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                     reinterpret_cast<const bf16*>(g), reinterpret_cast<bf16*>(gfull), rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_reduce(const float* dg32, void* dg, int64_t rows, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows * 16 + 255) / 256;
+  hipLaunchKernelGGL(bwd::gate_reduce_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                     dg32, reinterpret_cast<bf16*>(dg), rows);
+  return hipGetLastError();
+}
 
 size_t backward_workspace(int BH, int T) {
   const size_t N = ((size_t)T + bwd::C - 1) / bwd::C;

@@ -56,10 +56,14 @@ struct BackwardArgs {
   int B, T, H;
   void* states;     // bf16 [B*H][N] chunk-entry states, in the forward owners' fragment order
   void* adjoints;   // bf16 [B*H][N] adjoints of the chunk-end states, 16 x 16 tiles ([j][c] inside)
-  void* mats;       // bf16 [B*H][N][2][64][64]: A = (I + L)^-1 and P^T of each chunk
+  void* mats;       // bf16 [B*H][N] per-chunk operand blocks (A, P^T, Kg, Kd, Qg, gamma, beta)
+  float* dg32;      // if set: dg as fp32 [B,T,H,d_k] here instead of bf16 into dg
 };
 size_t backward_workspace(int BH, int T);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+// scalar gate: g [rows] broadcast to bf16 [rows][128]; dg [rows] = channel sums of fp32 [rows][128]
+hipError_t launch_gate_expand(const void* g, void* gfull, int64_t rows, hipStream_t s);
+hipError_t launch_gate_reduce(const float* dg32, void* dg, int64_t rows, hipStream_t s);
 // Order of packed sequences by decreasing chunk count (ties by index) into
 // order[0..N-1]; N <= kMaxScheduleSeqs.
 constexpr int kMaxScheduleSeqs = 16384;

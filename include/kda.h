@@ -226,6 +226,29 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
 
 /*
+ * kda_chunk_bwd_ex -- kda_chunk_bwd for the scalar-gate variant (Gated
+ * DeltaNet, "...Making LLM Training and Inference More Efficient" §3.2):
+ * flags = KDA_GATE_SCALAR takes g [B,T,H] and returns dg [B,T,H] (both
+ * dtype `dtype`, aligned to the element size); flags = 0 is exactly
+ * kda_chunk_bwd.  The scalar gate is the per-channel gate with all channels
+ * equal, so its gradient is the sum over the channels of the per-channel
+ * one: the gate is broadcast into the workspace, the per-channel backward
+ * runs with its dg in fp32, and the channel sums are taken on the device.
+ * KDA_NO_DELTA and unknown bits return KDA_ERR_ARG.  Other arguments,
+ * layouts, support and aliasing as for kda_chunk_bwd.
+ */
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* S0, const void* dO, const float* dS_T,
+                     void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS0,
+                     int B, int T, int H, int d_k, int d_v, int dtype, int flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_chunk_bwd_ex: kda_chunk_bwd_workspace_size() plus,
+ * with KDA_GATE_SCALAR, B*T*H*d_k*6 (the broadcast gate in bf16 and the
+ * per-channel dg in fp32); 0 for unsupported flags or sizes. */
+size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
+
+/*
  * Staged schedule: the same forward as kda_chunk_fwd, run as four separate
  * kernels with intermediates in a caller-provided workspace (the chunked
  * method's steps one by one).  Slower than kda_chunk_fwd; it exists so each

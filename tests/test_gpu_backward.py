@@ -34,8 +34,8 @@ def kda():
     return kda
 
 
-def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K):
-    inp = W.prefill_inputs(cfg, device="cuda", seed=seed, B=B, T=T, H=H)
+def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K, scalar_gate=False):
+    inp = W.prefill_inputs(cfg, device="cuda", seed=seed, B=B, T=T, H=H, scalar_gate=scalar_gate)
     if not s0:
         inp["S0"] = None
     gen = torch.Generator(device="cuda")
@@ -45,7 +45,7 @@ def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K):
     return inp
 
 
-def _oracle(inp, heads=None, chunk_adjoints=False):
+def _oracle(inp, heads=None, chunk_adjoints=False, scalar_gate=False):
     names = ("q", "k", "v", "g", "beta")
     if heads is None:
         x = [to64(inp[n]) for n in names]
@@ -55,7 +55,7 @@ def _oracle(inp, heads=None, chunk_adjoints=False):
         S0 = None if inp["S0"] is None else np.stack([to64(inp["S0"][b, h]) for b, h in heads])[:, None]
         dO = np.stack([to64(inp["dO"][b, :, h]) for b, h in heads])[:, :, None]
         dST = None if inp["dST"] is None else np.stack([to64(inp["dST"][b, h]) for b, h in heads])[:, None]
-    return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints)
+    return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints, scalar_gate=scalar_gate)
 
 
 def _pick(gr, heads):
@@ -69,8 +69,10 @@ def _pick(gr, heads):
     return out
 
 
-def _check(got, ref, what):
-    """got/ref: dicts of numpy arrays shaped [B, T, H, ...] ([B, H, ...] for dS0)."""
+def _check(got, ref, what, dg_scale=None):
+    """got/ref: dicts of numpy arrays shaped [B, T, H, ...] ([B, H, ...] for dS0).
+    dg_scale (scalar gate): per-token magnitude sum_c |dg_c| of the per-channel
+    gradient whose channel sum dg is; dg is measured against it."""
     worst = {}
     for n in NAMES:
         g, r = got[n], ref[n]
@@ -83,12 +85,13 @@ def _check(got, ref, what):
             heads = [(b, h) for b in range(r.shape[0]) for h in range(r.shape[2])]
             sl = lambda x, b, h: x[b, :, h]
         rel = 0.0
+        scale = dg_scale if (n == "dg" and dg_scale is not None) else r
         for b, h in heads:
-            den = np.linalg.norm(sl(r, b, h))
+            den = np.linalg.norm(sl(scale, b, h))
             if den > 0:
                 rel = max(rel, float(np.linalg.norm(sl(g, b, h) - sl(r, b, h)) / den))
         allow = 0.0 if n == "dS0" else BF16_U
-        over = float(np.max(np.abs(g - r) - allow * np.abs(r))) / max(rms(r), 1e-30)
+        over = float(np.max(np.abs(g - r) - allow * np.abs(r))) / max(rms(scale), 1e-30)
         worst[n] = (rel, over)
     print(f"[bwd parity] {what}: " + " ".join(f"{n}=({a:.2e},{b:.2e})" for n, (a, b) in worst.items()), flush=True)
     for n, (a, b) in worst.items():
@@ -96,9 +99,9 @@ def _check(got, ref, what):
         assert b <= MAX_OVER, f"{what}: {n} max err beyond rounding {b:.3e} > {MAX_OVER} RMS"
 
 
-def _run(kda, inp, workspace=None):
+def _run(kda, inp, workspace=None, scalar_gate=False):
     gr = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], inp["dO"], inp["dST"],
-                       workspace=workspace)
+                       workspace=workspace, scalar_gate=scalar_gate)
     torch.cuda.synchronize()
     return gr
 
@@ -181,3 +184,42 @@ def test_deterministic(kda):
     g1, g2 = _run(kda, inp), _run(kda, inp)
     for n in NAMES:
         assert torch.equal(g1[n], g2[n]), n
+
+
+# ---------------------------------------------------------------- scalar gate
+# g [B,T,H] (Gated DeltaNet): the backward of the per-channel kernels on the
+# broadcast gate, dg summed over the channels on the device.  Same bounds,
+# except that dg -- a sum over 128 channels of terms of both signs, in these
+# workloads 4-12 % of the sum of their magnitudes -- is measured against that
+# magnitude sum sum_c |dg_c| (the per-channel bound carried through the sum),
+# taken from the oracle's per-channel gradient on the broadcast gate.
+
+
+def _dg_scale(inp, heads=None):
+    full = dict(inp)
+    full["g"] = inp["g"][..., None].expand(*inp["g"].shape, 128).contiguous()
+    per = _oracle(full, heads)["dg"]
+    return np.abs(per).sum(-1)
+SG_SHAPES = [(1, 1, 2, True, True), (2, 130, 3, True, True), (1, 517, 2, False, True), (3, 192, 1, True, False)]
+
+
+@pytest.mark.parametrize("B,T,H,s0,dst", SG_SHAPES,
+                         ids=[f"B{b}T{t}H{h}{'-S0' if s else ''}{'-dST' if d else ''}" for b, t, h, s, d in SG_SHAPES])
+def test_scalar_gate_small_shapes(kda, B, T, H, s0, dst):
+    inp = _inputs(B, T, H, 2000 + T + H, s0, dst, scalar_gate=True)
+    print(f"case bwd scalar gate B{B} T{T} H{H} s0={s0} dST={dst}", flush=True)
+    gr = _run(kda, inp, scalar_gate=True)
+    assert gr["dg"].shape == (B, T, H)
+    ref = _oracle(inp, scalar_gate=True)
+    got = {n: to64(gr[n]) for n in NAMES}
+    _check(got, ref, f"scalar gate B{B}T{T}H{H}", dg_scale=_dg_scale(inp))
+
+
+def test_scalar_gate_B8_H32_T8192_sampled(kda):
+    cfg = W.PREFILL_BF16_B8_H32_T8K
+    inp = _inputs(cfg.B, cfg.T, cfg.H, 4, s0=False, dst=False, cfg=cfg, scalar_gate=True)
+    print("case bwd scalar gate B8 H32 T8192", flush=True)
+    gr = _run(kda, inp, scalar_gate=True)
+    heads = [(1, 3), (6, 30)]
+    ref = _oracle(inp, heads, scalar_gate=True)
+    _check(_pick(gr, heads), ref, "scalar gate B8 H32 T8192", dg_scale=_dg_scale(inp, heads))

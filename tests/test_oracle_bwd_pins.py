@@ -144,3 +144,17 @@ def test_output_adjoint_only_reaches_earlier_tokens():
     gr = oracle.recurrent_bwd(*(inp[n] for n in ("q", "k", "v", "g", "beta", "S0")), dO, None)
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         assert np.all(gr[key][:, 6:] == 0.0), key
+
+
+def test_scalar_gate_gradient_is_the_channel_sum():
+    """A scalar gate is the per-channel gate with all channels equal; by the
+    chain rule through that broadcast, its gradient is the channel sum of the
+    per-channel gradient (the GPU path computes it that way)."""
+    rng = np.random.default_rng(31)
+    inp, dO, dST = _case(rng, B=2, T=9, H=2, dk=5, dv=3, scalar_gate=True)
+    sc = oracle.recurrent_bwd(*(inp[n] for n in ("q", "k", "v", "g", "beta", "S0")), dO, dST, scalar_gate=True)
+    gfull = np.repeat(inp["g"][..., None], 5, axis=-1)
+    per = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], gfull, inp["beta"], inp["S0"], dO, dST)
+    assert np.max(np.abs(per["dg"].sum(-1) - sc["dg"])) <= 1e-12 * max(1.0, np.abs(sc["dg"]).max())
+    for key in ("dq", "dk", "dv", "dbeta", "dS0"):
+        assert np.max(np.abs(per[key] - sc[key])) <= 1e-12 * max(1.0, np.abs(sc[key]).max()), key
