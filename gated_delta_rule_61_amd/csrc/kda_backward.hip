@@ -95,6 +95,13 @@ __device__ __forceinline__ floatx4 mm(const bf16* X, int ldx, const bf16* Z, int
 }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+// x if keep, else zeros (word by word)
+__device__ __forceinline__ Vec16 keep_or_zero(const Vec16& x, bool keep) {
+  Vec16 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r.w[w] = keep ? x.w[w] : 0u;
+  return r;
+}
 
 // NTL tiles (m0[t].., n0..) of the same product shape sharing their Z
 // columns: each Z fragment is read once per 16-index step for all of them.
@@ -799,11 +806,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       xs[u] = ldg16(Sn + 32 * 256 * jh + 8 * pc);
       xd[u] = ldg16(dSn + 32 * 256 * jh + 8 * pc);
     }
-    xv = xo = Vec16{{0u, 0u, 0u, 0u}};
-    if (tv < c.nv) {
-      xv = ldg16(v + (c.row0 + (int64_t)tv * a.H) * D + 64 * jh + xv0);
-      xo = ldg16(dO + (c.row0 + (int64_t)tv * a.H) * D + 64 * jh + xv0);
-    }
+    // (every thread loads a row in range, rows past nv are zeroed when
+    // stored: a load under a branch made the compiler wait for it at the join)
+    const int tr = min(tv, c.nv - 1);
+    xv = ldg16(v + (c.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
+    xo = ldg16(dO + (c.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
   };
   half_issue(0);
   ops_commit(ops, L, tid);
@@ -832,8 +839,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
         for (int e = 0; e < 8; ++e) y[e] = (bf16)(L.gam[cd + e] * fd[e]);
         *reinterpret_cast<bf16x8*>(hDSG + jd * P128 + cd) = y;
       }
-      *reinterpret_cast<Vec16*>(hV + tv * P64 + xv0) = xv;
-      *reinterpret_cast<Vec16*>(hDO + tv * P64 + xv0) = xo;
+      *reinterpret_cast<Vec16*>(hV + tv * P64 + xv0) = keep_or_zero(xv, tv < c.nv);
+      *reinterpret_cast<Vec16*>(hDO + tv * P64 + xv0) = keep_or_zero(xo, tv < c.nv);
     }
     __syncthreads();
     // X = beta . (V - Kg S), stored transposed
@@ -923,17 +930,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     if (4 * g4 + r == i) dgam[c0 + i] = aSD[r];
   // the assembly's inputs g, q, k (rows past nv zero), in flight during the
   // 64 x 64 products
+  // (rows in range for every thread, zeroed past nv when stored)
   Vec16 xg[2], xq[2], xk[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
-    xg[u] = xq[u] = xk[u] = Vec16{{0u, 0u, 0u, 0u}};
-    if (t < c.nv) {
-      const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
-      xg[u] = ldg16(g + off);
-      xq[u] = ldg16(q + off);
-      xk[u] = ldg16(k + off);
-    }
+    const int e = tid + u * NT, t = min(e >> 4, c.nv - 1), x0 = 8 * (e & 15);
+    const int64_t off = (c.row0 + (int64_t)t * a.H) * D + x0;
+    xg[u] = ldg16(g + off);
+    xq[u] = ldg16(q + off);
+    xk[u] = ldg16(k + off);
   }
   // fold dKb~ into dKd, keeping its column sums against Kd (chunk-end terms)
   float colsum = 0.f;   // sum over my rows of Kd . dKb~ for column c0 + i
@@ -1078,12 +1083,13 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
+      const bool in = t < c.nv;
       float f[8];
-      vec_to_f32<bf16>(xg[u], f);
+      vec_to_f32<bf16>(keep_or_zero(xg[u], in), f);
 #pragma unroll
       for (int uu = 0; uu < 8; ++uu) bs[t * PB + x0 + uu] = f[uu];
-      *reinterpret_cast<Vec16*>(zq + t * P128 + x0) = xq[u];
-      *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = xk[u];
+      *reinterpret_cast<Vec16*>(zq + t * P128 + x0) = keep_or_zero(xq[u], in);
+      *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = keep_or_zero(xk[u], in);
     }
   }
   __syncthreads();
