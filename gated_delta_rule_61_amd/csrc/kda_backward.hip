@@ -1094,19 +1094,25 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   }
   __syncthreads();
   scan_cols<false>(bs, nullptr, tid);
-  // per element: dq, dk and db (db overwrites b in place)
+  // per element: dq, dk and db (db overwrites b in place).  The lane's four
+  // q and k of rows 16u + 4 g4 .. + 3, column c0 + i, are one transpose read
+  // each (the whole wavefront reads a row block before writing into it; other
+  // wavefronts own other columns).
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    const bf16x4 q4 = fr_tr(zq, P128, c0, 16 * u + 4 * g4, lane);
+    const bf16x4 k4 = fr_tr(zk, P128, c0, 16 * u + 4 * g4, lane);
+    const floatx4 md4 = *reinterpret_cast<const floatx4*>(md + 16 * u + 4 * g4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * u + 4 * g4 + r, cc = c0 + i;
       const float bb = bs[t * PB + cc];
       const float ep = __expf(bb), em = __expf(-bb);
-      const float qv = (float)zq[t * P128 + cc], kv = (float)zk[t * P128 + cc];
+      const float qv = (float)q4[r], kv = (float)k4[r];
       const float kg = kv * ep, kd = kv * em, qg = qv * ep;
       const float dkd = aKd[u][r];
-      zq[t * P128 + cc] = (bf16)(ep * aQg[u][r] + md[t] * kv);
-      zk[t * P128 + cc] = (bf16)(ep * aKg[u][r] + em * dkd + md[t] * qv);
+      zq[t * P128 + cc] = (bf16)(ep * aQg[u][r] + md4[r] * kv);
+      zk[t * P128 + cc] = (bf16)(ep * aKg[u][r] + em * dkd + md4[r] * qv);
       bs[t * PB + cc] = kg * aKg[u][r] - kd * dkd + qg * aQg[u][r];
     }
   }
