@@ -158,7 +158,7 @@ def measure_backward(kda, W, torch, pcfg, inp, args, stream):
             "workload": "kda_chunk_bwd B8 H32 T8192 d128 bf16 (S0=0, dS_T=0)",
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "forward state pass + bwd_chain_kernel + bwd_grad_kernel"}}
+                         "kernel": "the whole backward: state pass (fused_pipe_kernel<4>) + bwd_prep_kernel + bwd_chain_kernel + bwd_grad_kernel"}}
 
 
 def main():
