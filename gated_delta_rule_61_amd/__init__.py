@@ -220,12 +220,13 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
 
 
 def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None,
-              scalar_gate=False):
+              scalar_gate=False, delta=True):
     """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
     adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16,
-    d_k = d_v = 128.  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet)."""
-    flags = _flags(scalar_gate, True)
-    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate=scalar_gate)
+    d_k = d_v = 128.  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet);
+    delta=False: no delta rule (beta may be None, dbeta is None)."""
+    flags = _flags(scalar_gate, delta)
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate=scalar_gate, delta=delta)
     _need(dO, (B, T, H, dv), dt, "dO")
     if S0 is not None:
         _need(S0, (B, H, dk, dv), torch.float32, "S0")
@@ -233,7 +234,7 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=N
         _need(dS_T, (B, H, dk, dv), torch.float32, "dS_T")
     dev = q.device
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
-               dbeta=torch.empty_like(beta),
+               dbeta=torch.empty((B, T, H), dtype=dt, device=dev) if delta else None,
                dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
     L = lib()
     code = _dtype(q)

@@ -226,7 +226,7 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
 }
 
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
-  if ((flags & ~KDA_GATE_SCALAR) != 0) return 0;
+  if (!valid_flags(flags)) return 0;
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
   size_t n = kda::backward_workspace(B * H, T);
   // scalar gate: the broadcast gate (bf16) and the per-channel dg (fp32), [B,T,H,d_k] each
@@ -244,13 +244,13 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE((flags & ~KDA_GATE_SCALAR) == 0 && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
-  const bool sg = (flags & KDA_GATE_SCALAR) != 0;
+  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  const bool sg = (flags & KDA_GATE_SCALAR) != 0, nd = (flags & KDA_NO_DELTA) != 0;
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
     st = check_tokens(q, k, v, g, beta, dO, dtype, flags);
     if (st) return st;
-    KDA_REQUIRE(dq && dk && dv && dg && dbeta, KDA_ERR_NULL);
+    KDA_REQUIRE(dq && dk && dv && dg && (dbeta || nd), KDA_ERR_NULL);
     KDA_REQUIRE(aligned16(dq) && aligned16(dk) && aligned16(dv) && (sg || aligned16(dg)) &&
                 (reinterpret_cast<uintptr_t>(dg) & 1u) == 0 && (reinterpret_cast<uintptr_t>(dbeta) & 1u) == 0,
                 KDA_ERR_ALIGN);
@@ -268,8 +268,9 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   const int64_t rows = (int64_t)B * T * H;
   void* gfull = ws + base;
   float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
-  kda::BackwardArgs a{q, k, v, sg ? gfull : g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, B, T, H,
-                      workspace, ws + nst, ws + 2 * nst, sg ? dg32 : nullptr};
+  kda::BackwardArgs a{q, k, v, sg ? gfull : g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg,
+                      nd ? nullptr : dbeta, dS0, B, T, H, workspace, ws + nst, ws + 2 * nst,
+                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (sg && T > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);

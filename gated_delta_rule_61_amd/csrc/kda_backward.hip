@@ -292,7 +292,11 @@ __device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t bh, i
   return reinterpret_cast<bf16*>(a.mats) + (bh * N + n) * (int64_t)MATS;
 }
 
+// V: variant flags (kVarNoDelta: no beta, no L or A; the A block is left
+// unwritten and never read).
+template <int V>
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
+  constexpr bool ND = (V & kVarNoDelta) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
       xk[u] = ldg16(k + off);
     }
   }
-  if (tid < C) beta[tid] = tid < nv ? (float)reinterpret_cast<const bf16*>(a.beta)[row0 + (int64_t)tid * a.H] : 0.f;
+  if (tid < C) beta[tid] = !ND && tid < nv ? (float)reinterpret_cast<const bf16*>(a.beta)[row0 + (int64_t)tid * a.H] : 0.f;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int e = tid + u * NT, t = e >> 4, x0 = 8 * (e & 15);
@@ -402,6 +406,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
     *reinterpret_cast<bf16x8*>(Am + M_KG + t * D + x0) = kg;
   }
   __syncthreads();
+  if constexpr (!ND) {
   // L = StrictTril(Diag(beta) Kg Kd^T) (over b: b is dead), then A
   float* Ls = bs;
   float* As = bs + C * PF;
@@ -432,6 +437,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) x[u] = (bf16)(s4 + u <= t ? As[t * PF + s4 + u] : 0.f);
     *reinterpret_cast<bf16x4*>(Am + t * C + s4) = x;
+  }
   }
 }
 
@@ -565,7 +571,10 @@ __device__ __forceinline__ Basics basics(unsigned char* sm, int kg, int kd, int 
 
 // One workgroup per (sequence, head): dS in registers (wave w: value-column
 // tile w, all eight channel tiles), chunks in reverse.
+// V: variant flags (kVarNoDelta: dS <- gamma . dS + Qg^T dO, no E term).
+template <int V>
 __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
+  constexpr bool ND = (V & kVarNoDelta) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -624,12 +633,14 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     const bf16* Amn = chunk_mats(a, bh, N, n > 0 ? n - 1 : 0);
     if (n > 0) chain_issue<0>(ops, Amn, dO, cn, a.H, tid);
     // (gamma . dS)^T (this chunk's operands are in LDS)
+    if constexpr (!ND) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      floatx4 v;
+      for (int u = 0; u < 8; ++u) {
+        floatx4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * u + 4 * g4 + r];
-      st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
+        for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * u + 4 * g4 + r];
+        st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
+      }
     }
     __syncthreads();
     if (n > 0) chain_issue<1>(ops, Amn, dO, cn, a.H, tid);
@@ -637,7 +648,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     // scratch); wave w: the four token tiles of value-column tile w, which
     // share their column operands
     const int mT[4] = {0, 16, 32, 48};
-    {
+    if constexpr (!ND) {
       floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
       mm_zs<true, false, 4>(L.PT, P64, mT, sDO, P128, 16 * jt, C, acc, lane);
       mm_zs<true, true, 4>(L.Kd, P128, mT, sDSG, P128, 16 * jt, D, acc, lane);
@@ -647,7 +658,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     __syncthreads();
     if (n > 0) chain_issue<2>(ops, Amn, dO, cn, a.H, tid);
     // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed (over (gamma . dS)^T)
-    {
+    if constexpr (!ND) {
       floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
       mm_zs<false, true, 4>(L.A, P64, mT, sDDT, P64, 16 * jt, C, acc, lane);
 #pragma unroll
@@ -664,7 +675,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       const int mC[4] = {64 * hf, 64 * hf + 16, 64 * hf + 32, 64 * hf + 48};
       floatx4 p[4] = {zero4(), zero4(), zero4(), zero4()}, m[4] = {zero4(), zero4(), zero4(), zero4()};
       mm_zs<false, false, 4>(L.Qg, P128, mC, sDO, P128, 16 * jt, C, p, lane);
-      mm_zs<false, true, 4>(L.Kg, P128, mC, sET, P64, 16 * jt, C, m, lane);
+      if constexpr (!ND) mm_zs<false, true, 4>(L.Kg, P128, mC, sET, P64, 16 * jt, C, m, lane);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int u = 4 * hf + x;
@@ -734,7 +745,10 @@ static_assert(O_KD == O_KG + C * P128 * 2 && O_QG == O_KD + C * P128 * 2 && O_PT
 // One workgroup per (chunk, sequence, head).  [t][c] results: wave w owns
 // channels 16w .. 16w+15 (4 tiles of each); [t][j] results of a half and the
 // lower [t][t'] tiles are spread over the waves.
+// V: variant flags (kVarNoDelta: Delta = V, A = I, no W / L terms, no dbeta).
+template <int V>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
+  constexpr bool ND = (V & kVarNoDelta) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -783,7 +797,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* hDSG = reinterpret_cast<bf16*>(work + gr::H_DSG);
   bf16* hV = reinterpret_cast<bf16*>(work + gr::H_V);
   bf16* hDO = reinterpret_cast<bf16*>(work + gr::H_DO);
-  bf16* hD = reinterpret_cast<bf16*>(work + gr::H_D);
+  bf16* hD = ND ? hV : reinterpret_cast<bf16*>(work + gr::H_D);   // Delta (= V without the delta rule)
   bf16* hDD = reinterpret_cast<bf16*>(work + gr::H_DD);
   bf16* hXT = reinterpret_cast<bf16*>(work + gr::H_XT);
   // gamma . rowsum(S . dS), the chunk-end term of each channel: the diagonal
@@ -847,7 +861,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     // (tiles (tt, jj) and (tt + 2, jj) per wave: tiles wave and wave + 8 of 16)
     const int jj = wave & 3, tA = wave >> 2;
     const int mT[2] = {16 * tA, 16 * (tA + 2)};
-    {
+    if constexpr (!ND) {
       // (lane: token mT + i, value columns 16 jj + 4 g4 ..)
       floatx4 ks[2] = {zero4(), zero4()};
       mm_zs<true, true, 2, true>(L.Kg, P128, mT, hS, P128, 16 * jj, D, ks, lane);
@@ -859,17 +873,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
         for (int r = 0; r < 4; ++r) ks[x][r] = L.beta[t] * ((float)vv[r] - ks[x][r]);
         st_rm8(hXT, P64, mT[x], 16 * jj, ks[x], lane);
       }
+      __syncthreads();
     }
-    __syncthreads();
     // Delta = A X; dDelta = P^T dO + Kd (gamma . dS); both row-major
     {
       floatx4 dl[2] = {zero4(), zero4()}, dd[2] = {zero4(), zero4()};
-      mm_zs<true, false, 2, true>(L.A, P64, mT, hXT, P64, 16 * jj, C, dl, lane);
+      if constexpr (!ND) mm_zs<true, false, 2, true>(L.A, P64, mT, hXT, P64, 16 * jj, C, dl, lane);
       mm_zs<true, false, 2, true>(L.PT, P64, mT, hDO, P64, 16 * jj, C, dd, lane);
       mm_zs<true, true, 2, true>(L.Kd, P128, mT, hDSG, P128, 16 * jj, D, dd, lane);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        st_rm8(hD, P64, mT[x], 16 * jj, dl[x], lane);
+        if constexpr (!ND) st_rm8(hD, P64, mT[x], 16 * jj, dl[x], lane);
         st_rm8(hDD, P64, mT[x], 16 * jj, dd[x], lane);
       }
     }
@@ -885,7 +899,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       for (int u = 0; u < 4; ++u) {
         aQg[u] = MB::mma32(fr_row8(hDO, P64, 16 * u + i, k + 8 * g4), fs, aQg[u]);
         aKb[u] = MB::mma32(fr_row8(hD, P64, 16 * u + i, k + 8 * g4), fd, aKb[u]);
-        aW[u] = MB::mma32(fr_row8(hDD, P64, 16 * u + i, k + 8 * g4), fs, aW[u]);
+        if constexpr (!ND) aW[u] = MB::mma32(fr_row8(hDD, P64, 16 * u + i, k + 8 * g4), fs, aW[u]);
       }
     }
     // lower [t][t'] tiles: M += dO Delta^T, dA1 += dDelta V^T
@@ -897,12 +911,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
         lower_tile(tq, I, J);
         // (transposed tiles: lane holds row 16 I + i, columns 16 J + 4 g4 ..)
         aM[x] = mm<true, true, true>(hDO, P64, hD, P64, 16 * I, 16 * J, 64, aM[x], lane);
-        aA[x] = mm<true, true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
+        if constexpr (!ND) aA[x] = mm<true, true, true>(hDD, P64, hV, P64, 16 * I, 16 * J, 64, aA[x], lane);
       }
     }
     // dV[:, J] = Diag(beta) A^T dDelta, staged row-major where X^T was (dead
     // since Delta); dbeta += rowsum((A^T dDelta) . V)
-    {
+    if constexpr (!ND) {
       floatx4 xv[2] = {zero4(), zero4()};
       mm_zs<false, false, 2>(L.A, P64, mT, hDD, P64, 16 * jj, C, xv, lane);
 #pragma unroll
@@ -922,7 +936,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       const int t = tid >> 3, x0 = 8 * (tid & 7);
       if (t < c.nv)
         *reinterpret_cast<Vec16*>(reinterpret_cast<bf16*>(a.dv) + (c.row0 + (int64_t)t * a.H) * D + J0 + x0) =
-            *reinterpret_cast<const Vec16*>(hXT + t * P64 + x0);
+            *reinterpret_cast<const Vec16*>((ND ? hDD : hXT) + t * P64 + x0);   // dV (= dDelta without the delta rule)
     }
   }
 #pragma unroll
@@ -960,15 +974,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   // dW = -dDelta S^T (row-major); M with its diagonal moved out; zero fills
   for (int e = tid; e < C * P64; e += NT) {
     qM[e] = (bf16)0.f;
-    qDA[e] = (bf16)0.f;
+    if constexpr (!ND) qDA[e] = (bf16)0.f;
   }
+  if constexpr (!ND) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    floatx4 w;
+    for (int u = 0; u < 4; ++u) {
+      floatx4 w;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = -aW[u][r];
-    aW[u] = w;
-    st_rm(qDW, P128, 16 * u, c0, w, lane);
+      for (int r = 0; r < 4; ++r) w[r] = -aW[u][r];
+      aW[u] = w;
+      st_rm(qDW, P128, 16 * u, c0, w, lane);
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -986,19 +1002,21 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
         m[r] = t > s ? m[r] : 0.f;
       }
       st_rm8(qM, P64, 16 * I, 16 * J, m, lane);
-      // dA = (dDelta V^T + dW Kg^T) Diag(beta), strictly lower
-      floatx4 da = mm<true, true, true>(qDW, P128, L.Kg, P128, 16 * I, 16 * J, D, aA[x], lane);
-      const floatx4 bs4 = *reinterpret_cast<const floatx4*>(L.beta + 16 * J + 4 * g4);
+      if constexpr (!ND) {
+        // dA = (dDelta V^T + dW Kg^T) Diag(beta), strictly lower
+        floatx4 da = mm<true, true, true>(qDW, P128, L.Kg, P128, 16 * I, 16 * J, D, aA[x], lane);
+        const floatx4 bs4 = *reinterpret_cast<const floatx4*>(L.beta + 16 * J + 4 * g4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) da[r] = t > 16 * J + 4 * g4 + r ? da[r] * bs4[r] : 0.f;
-      st_rm8(qDA, P64, 16 * I, 16 * J, da, lane);
+        for (int r = 0; r < 4; ++r) da[r] = t > 16 * J + 4 * g4 + r ? da[r] * bs4[r] : 0.f;
+        st_rm8(qDA, P64, 16 * I, 16 * J, da, lane);
+      }
     }
   }
   __syncthreads();
   // Z1^T = A dA^T ( = (dA A^T)^T ), all 16 tiles
   // (tiles (I, J) and (I + 2, J) per wave: tiles wave and wave + 8 of 16)
   const int mT[2] = {16 * (wave >> 2), 16 * ((wave >> 2) + 2)};
-  {
+  if constexpr (!ND) {
     floatx4 z[2] = {zero4(), zero4()};
     mm_zs<true, true, 2, true>(L.A, P64, mT, qDA, P64, 16 * (wave & 3), C, z, lane);
 #pragma unroll
@@ -1008,7 +1026,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const int mU[4] = {0, 16, 32, 48};
   mm_zs<true, false, 4>(qM, P64, mU, L.Kd, P128, c0, C, aQg, lane);
   mm_zs<false, false, 4>(qM, P64, mU, L.Qg, P128, c0, C, aKd, lane);
-  {
+  if constexpr (!ND) {
     // Y = A^T dW with dW from registers (B operand of the 16-index slabs)
     bf16x4 wf[4];
 #pragma unroll
@@ -1028,6 +1046,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
     }
   }
+  if constexpr (!ND) {
   __syncthreads();
   // dL = -StrictTril(A^T Z1); dG = Diag(beta) dL
   for (int e = tid; e < C * P64; e += NT) {
@@ -1071,6 +1090,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
   }
   mm_zs<false, false, 4>(qDG, P64, mU, L.Kg, P128, c0, C, aKd, lane);
+  }
   __syncthreads();   // the work area becomes the db array
 
   // assembly: gate factors from b (recomputed), raw q and k staged in LDS;
@@ -1145,7 +1165,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
     }
   }
-  if (tid < C && tid < c.nv) {
+  if (!ND && tid < C && tid < c.nv) {
     float s = 0.f;
     for (int w = 0; w < NT / 64; ++w) s += dbp[w * C + tid];
     reinterpret_cast<bf16*>(a.dbeta)[c.row0 + (int64_t)tid * a.H] = (bf16)s;
@@ -1218,22 +1238,26 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
     f.S0 = a.S0; f.B = a.B; f.T = a.T; f.H = a.H; f.dk = 128; f.dv = 128; f.bf16 = 1; f.pipeline = 1;
     f.states = a.states;
+    f.variant = a.variant;
     if ((e = launch_fused(f, s)) != hipSuccess) return e;
   }
   // 2. per-chunk A and P^T
   if (N > 0) {
-    if ((e = set_lds(bwd::bwd_prep_kernel, bwd::pr::BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::bwd_prep_kernel, dim3(BH * N), dim3(bwd::NT), bwd::pr::BYTES, s, a);
+    auto prep = a.variant ? bwd::bwd_prep_kernel<kVarNoDelta> : bwd::bwd_prep_kernel<0>;
+    if ((e = set_lds(prep, bwd::pr::BYTES)) != hipSuccess) return e;
+    hipLaunchKernelGGL(prep, dim3(BH * N), dim3(bwd::NT), bwd::pr::BYTES, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. adjoint recursion (also writes dS0; with T = 0 it copies dS_T)
-  if ((e = set_lds(bwd::bwd_chain_kernel, bwd::ch::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd::bwd_chain_kernel, dim3(BH), dim3(bwd::NT), bwd::ch::BYTES, s, a);
+  auto chain = a.variant ? bwd::bwd_chain_kernel<kVarNoDelta> : bwd::bwd_chain_kernel<0>;
+  if ((e = set_lds(chain, bwd::ch::BYTES)) != hipSuccess) return e;
+  hipLaunchKernelGGL(chain, dim3(BH), dim3(bwd::NT), bwd::ch::BYTES, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (N == 0) return hipSuccess;
   // 4. per-chunk gradients
-  if ((e = set_lds(bwd::bwd_grad_kernel, bwd::gr::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd::bwd_grad_kernel, dim3(BH * N), dim3(bwd::NT), bwd::gr::BYTES, s, a);
+  auto grad = a.variant ? bwd::bwd_grad_kernel<kVarNoDelta> : bwd::bwd_grad_kernel<0>;
+  if ((e = set_lds(grad, bwd::gr::BYTES)) != hipSuccess) return e;
+  hipLaunchKernelGGL(grad, dim3(BH * N), dim3(bwd::NT), bwd::gr::BYTES, s, a);
   return hipGetLastError();
 }
 

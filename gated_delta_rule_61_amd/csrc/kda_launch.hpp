@@ -58,6 +58,7 @@ struct BackwardArgs {
   void* adjoints;   // bf16 [B*H][N] adjoints of the chunk-end states, 16 x 16 tiles ([j][c] inside)
   void* mats;       // bf16 [B*H][N] per-chunk operand blocks (A, P^T, Kg, Kd, Qg, gamma, beta)
   float* dg32;      // if set: dg as fp32 [B,T,H,d_k] here instead of bf16 into dg
+  int variant;      // 0 (KDA) or kVarNoDelta (beta and dbeta unused)
 };
 size_t backward_workspace(int BH, int T);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);

@@ -2541,8 +2541,13 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
 }
 
 static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
-  // chunk-entry states (for the backward): KDA only, one pass
-  if (a.states) return a.variant == 0 && a.nseg < 3 ? launch_pipe_v<kPipeStates>(a, s) : hipErrorInvalidValue;
+  // chunk-entry states (for the backward): KDA or no delta rule, one pass
+  if (a.states) {
+    if (a.nseg >= 3) return hipErrorInvalidValue;
+    if (a.variant == 0) return launch_pipe_v<kPipeStates>(a, s);
+    if (a.variant == kVarNoDelta) return launch_pipe_v<kPipeStates | kVarNoDelta>(a, s);
+    return hipErrorInvalidValue;
+  }
   switch (a.variant) {
     case 0: return launch_pipe_v<0>(a, s);
     case kVarScalarGate: return launch_pipe_v<kVarScalarGate>(a, s);

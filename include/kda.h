@@ -226,15 +226,19 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
 
 /*
- * kda_chunk_bwd_ex -- kda_chunk_bwd for the scalar-gate variant (Gated
- * DeltaNet, "...Making LLM Training and Inference More Efficient" §3.2):
- * flags = KDA_GATE_SCALAR takes g [B,T,H] and returns dg [B,T,H] (both
- * dtype `dtype`, aligned to the element size); flags = 0 is exactly
- * kda_chunk_bwd.  The scalar gate is the per-channel gate with all channels
- * equal, so its gradient is the sum over the channels of the per-channel
- * one: the gate is broadcast into the workspace, the per-channel backward
- * runs with its dg in fp32, and the channel sums are taken on the device.
- * KDA_NO_DELTA and unknown bits return KDA_ERR_ARG.  Other arguments,
+ * kda_chunk_bwd_ex -- kda_chunk_bwd for the variants of kda_chunk_fwd_ex
+ * ("...Making LLM Training and Inference More Efficient" §3.2, §3.3); flags
+ * = 0 is exactly kda_chunk_bwd.
+ *   KDA_GATE_SCALAR  g [B,T,H] in, dg [B,T,H] out (both dtype `dtype`,
+ *                    aligned to the element size).  The scalar gate is the
+ *                    per-channel gate with all channels equal, so its
+ *                    gradient is the sum over the channels of the
+ *                    per-channel one: the gate is broadcast into the
+ *                    workspace, the per-channel backward runs with its dg in
+ *                    fp32, and the channel sums are taken on the device.
+ *   KDA_NO_DELTA     no delta rule: beta is not read and dbeta not written
+ *                    (both may be NULL).
+ * Both may be combined; unknown bits return KDA_ERR_ARG.  Other arguments,
  * layouts, support and aliasing as for kda_chunk_bwd.
  */
 int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,

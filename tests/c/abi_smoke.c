@@ -38,8 +38,10 @@ int main(void) {
         KDA_ERR_WORKSPACE);
   if (kda_chunk_bwd_workspace_size(1, 64, 1, 128, 128, KDA_BF16) != (size_t)131840)
     return 1;
+  CHECK(kda_chunk_bwd_ex(p, p, p, p, NULL, NULL, p, NULL, p, p, p, p, NULL, NULL, 1, 64, 1, 128, 128, KDA_BF16,
+                         KDA_NO_DELTA, NULL, 0, NULL), KDA_ERR_WORKSPACE);
   CHECK(kda_chunk_bwd_ex(p, p, p, p, p, NULL, p, NULL, p, p, p, p, p, NULL, 1, 64, 1, 128, 128, KDA_BF16,
-                         KDA_NO_DELTA, NULL, 0, NULL), KDA_ERR_ARG);
+                         4, NULL, 0, NULL), KDA_ERR_ARG);
   CHECK(kda_chunk_bwd_ex(p, p, p, odd, p, NULL, p, NULL, p, p, p, odd, p, NULL, 1, 64, 1, 128, 128, KDA_BF16,
                          KDA_GATE_SCALAR, NULL, 0, NULL), KDA_ERR_WORKSPACE);
   if (kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, KDA_BF16, KDA_GATE_SCALAR) !=

@@ -150,18 +150,21 @@ def test_varlen_validation(L):
     assert s(cu, -1, 100, p, None) == -2
 
 
-def _bwd_ex(L, flags, g=16, dg=16, ws=None, wsz=0, T=64, dk=128):
+def _bwd_ex(L, flags, g=16, dg=16, ws=None, wsz=0, T=64, dk=128, beta=16, dbeta=16):
     p = lambda x: None if x is None else ctypes.c_void_p(x)
-    return L.kda_chunk_bwd_ex(p(16), p(16), p(16), p(g), p(16), None, p(16), None, p(16), p(16), p(16), p(dg),
-                              p(16), None, 1, T, 1, dk, dk, 1, flags, p(ws), wsz, None)
+    return L.kda_chunk_bwd_ex(p(16), p(16), p(16), p(g), p(beta), None, p(16), None, p(16), p(16), p(16), p(dg),
+                              p(dbeta), None, 1, T, 1, dk, dk, 1, flags, p(ws), wsz, None)
 
 
 def test_backward_variant_validation(L):
-    """kda_chunk_bwd_ex: the scalar gate is accepted (g, dg aligned to the
-    element size), the no-delta variant and unknown bits are not; the scalar
-    path needs the broadcast gate and the fp32 per-channel dg in its
-    workspace."""
-    assert _bwd_ex(L, 2) == -7                       # KDA_NO_DELTA
+    """kda_chunk_bwd_ex: the scalar gate (g, dg aligned to the element size)
+    and the no-delta variant (beta and dbeta may be NULL) are accepted,
+    unknown bits are not; the scalar path needs the broadcast gate and the
+    fp32 per-channel dg in its workspace."""
+    assert _bwd_ex(L, 2, beta=None, dbeta=None) == -5    # KDA_NO_DELTA: checks pass, workspace missing
+    assert _bwd_ex(L, 3, g=18, dg=18, beta=None, dbeta=None) == -5
+    assert _bwd_ex(L, 0, dbeta=None) == -1           # KDA needs dbeta
+    assert _bwd_ex(L, 0, beta=None) == -1            # ... and beta
     assert _bwd_ex(L, 4) == -7                       # unknown bit
     assert _bwd_ex(L, 1, dk=64) == -7                # bf16, d = 128 only
     assert _bwd_ex(L, 1, g=17) == -4                 # g not 2-byte aligned
@@ -170,5 +173,7 @@ def test_backward_variant_validation(L):
     base = L.kda_chunk_bwd_workspace_size(1, 64, 1, 128, 128, 1)
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 0) == base
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 1) == base + 64 * 128 * 6
-    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 2) == 0
+    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 2) == base
+    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 3) == base + 64 * 128 * 6
+    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 4) == 0
     assert _bwd_ex(L, 1, ws=1024, wsz=base) == -5    # too small for the scalar path

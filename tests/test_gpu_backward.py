@@ -45,7 +45,7 @@ def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K, scalar
     return inp
 
 
-def _oracle(inp, heads=None, chunk_adjoints=False, scalar_gate=False):
+def _oracle(inp, heads=None, chunk_adjoints=False, scalar_gate=False, delta=True):
     names = ("q", "k", "v", "g", "beta")
     if heads is None:
         x = [to64(inp[n]) for n in names]
@@ -55,13 +55,18 @@ def _oracle(inp, heads=None, chunk_adjoints=False, scalar_gate=False):
         S0 = None if inp["S0"] is None else np.stack([to64(inp["S0"][b, h]) for b, h in heads])[:, None]
         dO = np.stack([to64(inp["dO"][b, :, h]) for b, h in heads])[:, :, None]
         dST = None if inp["dST"] is None else np.stack([to64(inp["dST"][b, h]) for b, h in heads])[:, None]
-    return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints, scalar_gate=scalar_gate)
+    if not delta:
+        x[4] = None
+    return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints, scalar_gate=scalar_gate,
+                                delta=delta)
 
 
 def _pick(gr, heads):
     out = {}
     for n in NAMES:
         t = gr[n]
+        if t is None:
+            continue
         if n == "dS0":
             out[n] = np.stack([to64(t[b, h]) for b, h in heads])[:, None]
         else:
@@ -75,6 +80,8 @@ def _check(got, ref, what, dg_scale=None):
     gradient whose channel sum dg is; dg is measured against it."""
     worst = {}
     for n in NAMES:
+        if n not in got:
+            continue
         g, r = got[n], ref[n]
         if r.size == 0:
             continue
@@ -99,9 +106,9 @@ def _check(got, ref, what, dg_scale=None):
         assert b <= MAX_OVER, f"{what}: {n} max err beyond rounding {b:.3e} > {MAX_OVER} RMS"
 
 
-def _run(kda, inp, workspace=None, scalar_gate=False):
-    gr = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], inp["dO"], inp["dST"],
-                       workspace=workspace, scalar_gate=scalar_gate)
+def _run(kda, inp, workspace=None, scalar_gate=False, delta=True):
+    gr = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"] if delta else None, inp["S0"], inp["dO"],
+                       inp["dST"], workspace=workspace, scalar_gate=scalar_gate, delta=delta)
     torch.cuda.synchronize()
     return gr
 
@@ -200,6 +207,8 @@ def _dg_scale(inp, heads=None):
     full["g"] = inp["g"][..., None].expand(*inp["g"].shape, 128).contiguous()
     per = _oracle(full, heads)["dg"]
     return np.abs(per).sum(-1)
+
+
 SG_SHAPES = [(1, 1, 2, True, True), (2, 130, 3, True, True), (1, 517, 2, False, True), (3, 192, 1, True, False)]
 
 
@@ -223,3 +232,45 @@ def test_scalar_gate_B8_H32_T8192_sampled(kda):
     heads = [(1, 3), (6, 30)]
     ref = _oracle(inp, heads, scalar_gate=True)
     _check(_pick(gr, heads), ref, "scalar gate B8 H32 T8192", dg_scale=_dg_scale(inp, heads))
+
+
+# ---------------------------------------------------------------- no delta rule
+# S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T (GLA-style decay): the same kernels
+# with Delta = V and no A, L or beta terms; dbeta is not produced.  Same bounds.
+ND_SHAPES = [(1, 1, 2, True, True), (1, 63, 2, True, False), (2, 130, 3, True, True), (1, 517, 2, False, True),
+             (3, 192, 1, True, False)]
+
+
+@pytest.mark.parametrize("B,T,H,s0,dst", ND_SHAPES,
+                         ids=[f"B{b}T{t}H{h}{'-S0' if s else ''}{'-dST' if d else ''}" for b, t, h, s, d in ND_SHAPES])
+def test_no_delta_small_shapes(kda, B, T, H, s0, dst):
+    inp = _inputs(B, T, H, 3000 + T + H, s0, dst)
+    print(f"case bwd no delta B{B} T{T} H{H} s0={s0} dST={dst}", flush=True)
+    gr = _run(kda, inp, delta=False)
+    assert gr["dbeta"] is None
+    ref = _oracle(inp, delta=False)
+    got = {n: to64(gr[n]) for n in NAMES if gr[n] is not None}
+    _check(got, ref, f"no delta B{B}T{T}H{H}")
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 70, 2), (2, 192, 1)], ids=["B1T70H2", "B2T192H1"])
+def test_no_delta_scalar_gate(kda, B, T, H):
+    inp = _inputs(B, T, H, 4000 + T + H, scalar_gate=True)
+    print(f"case bwd no delta, scalar gate B{B} T{T} H{H}", flush=True)
+    gr = _run(kda, inp, scalar_gate=True, delta=False)
+    ref = _oracle(inp, scalar_gate=True, delta=False)
+    full = dict(inp)
+    full["g"] = inp["g"][..., None].expand(*inp["g"].shape, 128).contiguous()
+    scale = np.abs(_oracle(full, delta=False)["dg"]).sum(-1)
+    got = {n: to64(gr[n]) for n in NAMES if gr[n] is not None}
+    _check(got, ref, f"no delta, scalar gate B{B}T{T}H{H}", dg_scale=scale)
+
+
+def test_no_delta_B8_H32_T8192_sampled(kda):
+    cfg = W.PREFILL_BF16_B8_H32_T8K
+    inp = _inputs(cfg.B, cfg.T, cfg.H, 6, s0=False, dst=False, cfg=cfg)
+    print("case bwd no delta B8 H32 T8192", flush=True)
+    gr = _run(kda, inp, delta=False)
+    heads = [(2, 7), (7, 31)]
+    ref = _oracle(inp, heads, delta=False)
+    _check(_pick(gr, heads), ref, "no delta B8 H32 T8192")
