@@ -52,6 +52,8 @@ _SIGS = {
     "kda_chunk_bwd_workspace_size": ([_i] * 6, _sz),
     "kda_chunk_bwd_ex": ([_vp] * 14 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_chunk_bwd_ex_workspace_size": ([_i] * 7, _sz),
+    "kda_chunk_bwd_varlen": ([_vp] * 15 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_bwd_varlen_workspace_size": ([_i] * 7, _sz),
     "kda_chunk_fwd_staged_workspace_size": ([_i] * 6, _sz),
     "kda_recurrent_step": ([_vp] * 7 + [_i] * 5 + [_vp], _i),
     "kda_stage_cumsum": ([_vp, _vp] + [_i] * 5 + [_vp], _i),
@@ -248,6 +250,46 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=N
     return out
 
 
+def chunk_bwd_varlen(q, k, v, g, beta, cu_seqlens, S0, dO, dS_T=None, *, want_dS0=True, workspace=None,
+                     stream=None, scalar_gate=False, delta=True):
+    """Gradient of chunk_fwd_varlen for N packed sequences: q, k, g, v, beta,
+    dO packed as there ([T_total, H, ...]), S0 and dS_T [N, H, d_k, d_v] fp32
+    or None.  Returns dict(dq, dk, dv, dg, dbeta, dS0) (dbeta None without the
+    delta rule, dS0 [N, H, d_k, d_v])."""
+    flags = _flags(scalar_gate, delta)
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise KDAError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _need(q, (Tt, H, dk), dt, "q")
+    _need(k, (Tt, H, dk), dt, "k")
+    _need(g, (Tt, H) if scalar_gate else (Tt, H, dk), dt, "g")
+    _need(v, (Tt, H, dv), dt, "v")
+    _need(dO, (Tt, H, dv), dt, "dO")
+    if delta or beta is not None:
+        _need(beta, (Tt, H), dt, "beta")
+    for name, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None:
+            _need(x, (N, H, dk, dv), torch.float32, name)
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+               dbeta=torch.empty((Tt, H), dtype=dt, device=dev) if delta else None,
+               dS0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
+    L = lib()
+    code = _dtype(q)
+    wsz = L.kda_chunk_bwd_varlen_workspace_size(N, Tt, H, dk, dv, code, flags)
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                  _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                  _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, Tt, H, dk, dv, code,
+                                  flags, _ptr(workspace) if wsz else None, wsz, _stream(stream)))
+    return out
+
+
 def recurrent_step(q, k, v, g, beta, S, *, o=None, stream=None, scalar_gate=False, delta=True):
     """One decode token for N sequences; S [N,H,d_k,d_v] fp32 is updated in
     place.  Returns o [N,H,d_v].  Variants as for chunk_fwd (g [N,H] with
@@ -314,5 +356,5 @@ def stage_output(q, k, b, Delta, S_chunks, *, stream=None):
     return o
 
 
-__all__ = ["chunk_fwd", "recurrent_step", "stage_cumsum", "stage_ut", "stage_state",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_varlen", "recurrent_step", "stage_cumsum", "stage_ut", "stage_state",
            "stage_output", "lib", "KDAError", "LIB_PATH", "HEADER"]

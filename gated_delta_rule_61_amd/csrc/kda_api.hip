@@ -270,12 +270,64 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
   kda::BackwardArgs a{q, k, v, sg ? gfull : g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg,
                       nd ? nullptr : dbeta, dS0, B, T, H, workspace, ws + nst, ws + 2 * nst,
-                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0};
+                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, nullptr, 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (sg && T > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);
   if ((e = kda::launch_backward(a, s)) != hipSuccess) return hip_status(e);
   if (sg && T > 0) return hip_status(kda::launch_gate_reduce(dg32, dg, rows, s));
+  return KDA_OK;
+}
+
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v, int dtype, int flags) {
+  if (!valid_flags(flags)) return 0;
+  if (check_chunk_dims(N, T_total, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
+  if ((int64_t)N * H == 0 || T_total == 0) return 0;
+  size_t n = kda::backward_varlen_workspace(N, T_total, H);
+  if (flags & KDA_GATE_SCALAR) n += (size_t)T_total * H * d_k * (2 + 4);
+  return n;
+}
+
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dg,
+                         void* dbeta, float* dS0, const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                         int d_v, int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  const bool sg = (flags & KDA_GATE_SCALAR) != 0, nd = (flags & KDA_NO_DELTA) != 0;
+  if ((int64_t)N * H == 0) return KDA_OK;
+  KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
+  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0, KDA_ERR_ALIGN);
+  if (T_total > 0) {
+    st = check_tokens(q, k, v, g, beta, dO, dtype, flags);
+    if (st) return st;
+    KDA_REQUIRE(dq && dk && dv && dg && (dbeta || nd), KDA_ERR_NULL);
+    KDA_REQUIRE(aligned16(dq) && aligned16(dk) && aligned16(dv) && (sg || aligned16(dg)) &&
+                (reinterpret_cast<uintptr_t>(dg) & 1u) == 0 && (reinterpret_cast<uintptr_t>(dbeta) & 1u) == 0,
+                KDA_ERR_ALIGN);
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(dS_T) && aligned16(dS0), KDA_ERR_ALIGN);
+  const size_t need = kda_chunk_bwd_varlen_workspace_size(N, T_total, H, d_k, d_v, dtype, flags);
+  KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+  // workspace: chunk states, chunk-end adjoints, operand blocks (nslots x H
+  // blocks each); then (scalar gate) the broadcast gate and the per-channel dg
+  char* ws = static_cast<char*>(workspace);
+  const int nslots = kda::backward_varlen_slots(N, T_total);
+  const size_t nst = (size_t)nslots * H * d_k * d_v * 2;
+  const size_t base = kda::backward_varlen_workspace(N, T_total, H);
+  const int64_t rows = (int64_t)T_total * H;
+  void* gfull = ws + base;
+  float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
+  kda::BackwardArgs a{q, k, v, sg ? gfull : g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg,
+                      nd ? nullptr : dbeta, dS0, N, T_total, H, workspace, ws + nst, ws + 2 * nst,
+                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, cu_seqlens, nslots};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (sg && T_total > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);
+  if ((e = kda::launch_backward(a, s)) != hipSuccess) return hip_status(e);
+  if (sg && T_total > 0) return hip_status(kda::launch_gate_reduce(dg32, dg, rows, s));
   return KDA_OK;
 }
 

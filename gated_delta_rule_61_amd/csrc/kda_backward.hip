@@ -288,8 +288,64 @@ constexpr int M_GAM = M_QG + C * D;
 constexpr int MATS = M_GAM + 2 * (D + C);
 static_assert((MATS * 2) % 16 == 0, "16-byte aligned blocks");
 
-__device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t bh, int N, int n) {
-  return reinterpret_cast<bf16*>(a.mats) + (bh * N + n) * (int64_t)MATS;
+__device__ __forceinline__ bf16* chunk_mats(const BackwardArgs& a, int64_t idx) {
+  return reinterpret_cast<bf16*>(a.mats) + idx * (int64_t)MATS;
+}
+
+// Sequence b, head h: its first row (token-major rows of H), its length, its
+// chunk count, and where its chunks sit in the per-chunk arrays (states,
+// adjoints, operand blocks): chunk n is block idx0 + n * istride.  A batch
+// stores each (sequence, head) contiguously; packed sequences (cu_seqlens,
+// entries clamped to [0, T]) put chunk n of sequence b in slot
+// floor(cu[b] / C) + b + n, head-minor: the slot ranges of consecutive
+// sequences are disjoint and every slot is below floor(T / C) + B.
+struct SeqView {
+  int64_t row0, idx0;
+  int len, nch, istride;
+};
+__device__ __forceinline__ SeqView seq_view(const BackwardArgs& a, int b, int h) {
+  SeqView v;
+  if (a.cu_seqlens) {
+    const int e0 = min(max(a.cu_seqlens[b], 0), a.T), e1 = min(max(a.cu_seqlens[b + 1], e0), a.T);
+    v.row0 = (int64_t)e0 * a.H + h;
+    v.len = e1 - e0;
+    v.idx0 = (int64_t)(e0 / C + b) * a.H + h;
+    v.istride = a.H;
+  } else {
+    v.row0 = (int64_t)b * a.T * a.H + h;
+    v.len = a.T;
+    v.idx0 = (int64_t)(b * a.H + h) * ((a.T + C - 1) / C);
+    v.istride = 1;
+  }
+  v.nch = (v.len + C - 1) / C;
+  return v;
+}
+
+// Workgroup -> (sequence, head, chunk) of the per-chunk kernels; false for a
+// slot no chunk uses (packed sequences: grid nslots * H, the sequence found by
+// binary search over the slot starts floor(cu[b] / C) + b).
+__device__ __forceinline__ bool chunk_of_block(const BackwardArgs& a, int& b, int& h, int& n) {
+  const int blk = blockIdx.x;
+  if (!a.cu_seqlens) {
+    const int N = (a.T + C - 1) / C;
+    const int bh = blk / N;
+    n = blk % N;
+    b = bh / a.H;
+    h = bh % a.H;
+    return bh < a.B * a.H;
+  }
+  const int slot = blk / a.H;
+  h = blk % a.H;
+  auto start = [&](int x) { return min(max(a.cu_seqlens[x], 0), a.T) / C + x; };
+  int lo = 0, hi = a.B - 1;   // largest b with start(b) <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start(mid) <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  b = lo;
+  n = slot - start(b);
+  return n >= 0 && slot < a.nslots && n < seq_view(a, b, h).nch;
 }
 
 // V: variant flags (kVarNoDelta: no beta, no L or A; the A block is left
@@ -300,10 +356,9 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = (a.T + C - 1) / C;
-  const int bh = blockIdx.x / N, n = blockIdx.x % N;
-  if (bh >= a.B * a.H) return;
-  const int b = bh / a.H, h = bh % a.H;
+  int b, h, n;
+  if (!chunk_of_block(a, b, h, n)) return;
+  const SeqView sv = seq_view(a, b, h);
   bf16* X = reinterpret_cast<bf16*>(sm + pr::O_X);
   bf16* Kd = reinterpret_cast<bf16*>(sm + pr::O_KD);
   float* bs = reinterpret_cast<float*>(sm + pr::O_BS);
@@ -312,9 +367,9 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   const bf16* q = reinterpret_cast<const bf16*>(a.q);
   const bf16* k = reinterpret_cast<const bf16*>(a.k);
   const bf16* g = reinterpret_cast<const bf16*>(a.g);
-  const int64_t row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
-  const int nv = min(C, a.T - n * C);
-  bf16* Am = chunk_mats(a, bh, N, n);
+  const int64_t row0 = sv.row0 + (int64_t)n * C * a.H;
+  const int nv = min(C, sv.len - n * C);
+  bf16* Am = chunk_mats(a, sv.idx0 + (int64_t)n * sv.istride);
   bf16* PTm = Am + M_PT;
 
   // g, q, k of the chunk (thread: rows t = e / 16 of e = tid, tid + 512,
@@ -581,7 +636,8 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   const int bh = blockIdx.x;
   if (bh >= a.B * a.H) return;
   const int b = bh / a.H, h = bh % a.H;
-  const int N = (a.T + C - 1) / C;
+  const SeqView sv = seq_view(a, b, h);
+  const int N = sv.nch;
   const Basics L = basics(sm, ch::O_KG, ch::O_KD, ch::O_QG, ch::O_A, ch::O_PT, ch::O_BETA, ch::O_GAM, ch::O_QK);
   bf16* sDO = reinterpret_cast<bf16*>(sm + ch::O_DO);
   bf16* sDSG = reinterpret_cast<bf16*>(sm + ch::O_DSG);
@@ -603,16 +659,17 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
 
   auto chunk_of = [&](int n) {
     Chunk c;
-    c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
-    c.nv = min(C, a.T - n * C);
+    c.row0 = sv.row0 + (int64_t)n * C * a.H;
+    c.nv = min(C, sv.len - n * C);
     c.rstride = a.H * D;
     return c;
   };
+  auto blk = [&](int n) { return sv.idx0 + (int64_t)n * sv.istride; };
   ChainOps ops;
   if (N > 0) {
-    chain_issue<0>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
-    chain_issue<1>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
-    chain_issue<2>(ops, chunk_mats(a, bh, N, N - 1), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<0>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<1>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<2>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
     chain_commit(ops, L, sDO, tid);
     __syncthreads();
   }
@@ -620,7 +677,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     // chunk-end adjoint of this chunk (bf16, in 16 x 16 tiles: tile (j/16, c/16)
     // at position 8 (j/16) + c/16, [j%16][c%16] inside): one wave store
     // writes one whole tile, 512 contiguous bytes
-    bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;
+    bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + blk(n) * D * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       bf16x4 x;
@@ -630,7 +687,7 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     }
     // the next chunk's operands, in flight during this chunk's products
     const Chunk cn = chunk_of(n > 0 ? n - 1 : 0);
-    const bf16* Amn = chunk_mats(a, bh, N, n > 0 ? n - 1 : 0);
+    const bf16* Amn = chunk_mats(a, blk(n > 0 ? n - 1 : 0));
     if (n > 0) chain_issue<0>(ops, Amn, dO, cn, a.H, tid);
     // (gamma . dS)^T (this chunk's operands are in LDS)
     if constexpr (!ND) {
@@ -752,10 +809,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = (a.T + C - 1) / C;
-  const int bh = blockIdx.x / N, n = blockIdx.x % N;
-  if (bh >= a.B * a.H) return;
-  const int b = bh / a.H, h = bh % a.H;
+  int b, h, n;
+  if (!chunk_of_block(a, b, h, n)) return;
+  const SeqView sv = seq_view(a, b, h);
+  const int64_t bi = sv.idx0 + (int64_t)n * sv.istride;   // this chunk's block
   const Basics L = basics(sm, gr::O_KG, gr::O_KD, gr::O_QG, gr::O_A, gr::O_PT, gr::O_BETA, gr::O_GAM, gr::O_QK);
   float* dgam = reinterpret_cast<float*>(sm + gr::O_DGAM);
   float* md = reinterpret_cast<float*>(sm + gr::O_MD);
@@ -767,14 +824,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const bf16* v = reinterpret_cast<const bf16*>(a.v);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
   Chunk c;
-  c.row0 = ((int64_t)b * a.T + (int64_t)n * C) * a.H + h;
-  c.nv = min(C, a.T - n * C);
+  c.row0 = sv.row0 + (int64_t)n * C * a.H;
+  c.nv = min(C, sv.len - n * C);
   c.rstride = a.H * D;
-  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + ((int64_t)bh * N + n) * D * D;      // fragment order
-  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + ((int64_t)bh * N + n) * D * D;   // 16 x 16 tiles
+  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + bi * D * D;      // fragment order
+  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + bi * D * D;   // 16 x 16 tiles
 
   ChunkOps ops;
-  ops_issue(ops, chunk_mats(a, bh, N, n), tid);
+  ops_issue(ops, chunk_mats(a, bi), tid);
 
   // persistent accumulators
   const int c0 = 16 * wave;     // my channel block
@@ -1222,6 +1279,12 @@ size_t backward_workspace(int BH, int T) {
   return (size_t)BH * N * (2 * bwd::D * bwd::D + bwd::MATS) * sizeof(bf16);
 }
 
+int backward_varlen_slots(int nseq, int T) { return T / bwd::C + nseq; }
+
+size_t backward_varlen_workspace(int nseq, int T, int H) {
+  return (size_t)backward_varlen_slots(nseq, T) * H * (2 * bwd::D * bwd::D + bwd::MATS) * sizeof(bf16);
+}
+
 template <typename K>
 static hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -1231,6 +1294,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
   const int N = (a.T + bwd::C - 1) / bwd::C;
+  // per-chunk workgroups: chunks x sequences x heads, or (packed sequences)
+  // slots x heads with the unused slots returning at once
+  const int nblk = a.cu_seqlens ? a.nslots * a.H : BH * N;
   hipError_t e;
   if (N > 0) {
     // 1. chunk-entry states: the forward kernel in state mode
@@ -1239,13 +1305,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     f.S0 = a.S0; f.B = a.B; f.T = a.T; f.H = a.H; f.dk = 128; f.dv = 128; f.bf16 = 1; f.pipeline = 1;
     f.states = a.states;
     f.variant = a.variant;
+    f.cu_seqlens = a.cu_seqlens;
     if ((e = launch_fused(f, s)) != hipSuccess) return e;
   }
   // 2. per-chunk A and P^T
   if (N > 0) {
     auto prep = a.variant ? bwd::bwd_prep_kernel<kVarNoDelta> : bwd::bwd_prep_kernel<0>;
     if ((e = set_lds(prep, bwd::pr::BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(prep, dim3(BH * N), dim3(bwd::NT), bwd::pr::BYTES, s, a);
+    hipLaunchKernelGGL(prep, dim3(nblk), dim3(bwd::NT), bwd::pr::BYTES, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. adjoint recursion (also writes dS0; with T = 0 it copies dS_T)
@@ -1257,7 +1324,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   // 4. per-chunk gradients
   auto grad = a.variant ? bwd::bwd_grad_kernel<kVarNoDelta> : bwd::bwd_grad_kernel<0>;
   if ((e = set_lds(grad, bwd::gr::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(grad, dim3(BH * N), dim3(bwd::NT), bwd::gr::BYTES, s, a);
+  hipLaunchKernelGGL(grad, dim3(nblk), dim3(bwd::NT), bwd::gr::BYTES, s, a);
   return hipGetLastError();
 }
 

@@ -59,8 +59,15 @@ struct BackwardArgs {
   void* mats;       // bf16 [B*H][N] per-chunk operand blocks (A, P^T, Kg, Kd, Qg, gamma, beta)
   float* dg32;      // if set: dg as fp32 [B,T,H,d_k] here instead of bf16 into dg
   int variant;      // 0 (KDA) or kVarNoDelta (beta and dbeta unused)
+  // Packed sequences: B sequences, sequence b is tokens [cu_seqlens[b],
+  // cu_seqlens[b+1]) of [T, H, d] tensors; the per-chunk arrays hold nslots x H
+  // blocks (backward_varlen_slots).  NULL: [B, T, H, d].
+  const int* cu_seqlens;
+  int nslots;
 };
 size_t backward_workspace(int BH, int T);
+int backward_varlen_slots(int nseq, int T);
+size_t backward_varlen_workspace(int nseq, int T, int H);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 // scalar gate: g [rows] broadcast to bf16 [rows][128]; dg [rows] = channel sums of fp32 [rows][128]
 hipError_t launch_gate_expand(const void* g, void* gfull, int64_t rows, hipStream_t s);

@@ -2199,6 +2199,9 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   }
   int bb = head / a.H;
   const int h = head % a.H;
+  // chunk-entry states: chunk n of this sequence is block st0 + n * stn
+  // (packed sequences: slot floor(cu[b] / C) + b + n, head-minor)
+  int64_t st0 = (int64_t)head * ((a.T + C - 1) / C), stn = 1;
   if (a.cu_seqlens) {
     // packed sequences (one pass): sequence bb is tokens [cu[bb], cu[bb+1]) of
     // the [T, H, d] tensors, clamped to them; from here on it is addressed as a
@@ -2206,6 +2209,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int e0 = min(max(a.cu_seqlens[bb], 0), a.T);
     const int e1 = min(max(a.cu_seqlens[bb + 1], e0), a.T);
     const int64_t r0 = (int64_t)e0 * a.H;   // first row of the sequence
+    st0 = (int64_t)(e0 / C + bb) * a.H + h;
+    stn = a.H;
     a.q = reinterpret_cast<const bf16*>(a.q) + r0 * DK;
     a.k = reinterpret_cast<const bf16*>(a.k) + r0 * DK;
     a.g = reinterpret_cast<const bf16*>(a.g) + r0 * ((V & kVarScalarGate) ? 1 : DK);
@@ -2264,8 +2269,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           owner_store(O, ro, a.H * DV, col0, lane);
         }
         if constexpr (ST)
-          store_state_t(S, reinterpret_cast<bf16*>(a.states) + ((int64_t)head * ((a.T + C - 1) / C) + c0 + n) * DK * DV,
-                        col0, lane);
+          store_state_t(S, reinterpret_cast<bf16*>(a.states) + (st0 + (int64_t)(c0 + n) * stn) * DK * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
       // V^T of chunk n+1 (U is formed in phase 3)

@@ -253,6 +253,40 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
 
 /*
+ * kda_chunk_bwd_varlen -- kda_chunk_bwd_ex for N packed variable-length
+ * sequences, the gradient of kda_chunk_fwd_varlen (the reverse-mode
+ * derivative of the chunked form of "...Making LLM Training and Inference
+ * More Efficient" §IV over the packed layout of "Linear Attention
+ * Architecture Deep Dive: From State Updates to Efficient Chunked
+ * Computation" §5): each sequence runs the backward from its own entry state S0[i]
+ * and chunk-end adjoint dS_T[i], and gets its own dS0[i].
+ *   q,k,g,dq,dk,dg [T_total,H,d_k]  v,dO,dv [T_total,H,d_v]
+ *   beta,dbeta [T_total,H] (NULL with KDA_NO_DELTA); g, dg [T_total,H] with
+ *   KDA_GATE_SCALAR; S0, dS_T, dS0 fp32 [N,H,d_k,d_v] (S0, dS_T NULL: zero;
+ *   dS0 NULL: not written)
+ *   cu_seqlens DEVICE int32 [N+1], nondecreasing, cu_seqlens[0] = 0 and
+ *   cu_seqlens[N] = T_total: sequence i is tokens [cu_seqlens[i],
+ *   cu_seqlens[i+1]); entries are clamped to [0, T_total] on the device.
+ *   Zero-length sequences are allowed (dS0[i] = dS_T[i]).
+ * Supported as kda_chunk_bwd_ex (bf16, d_k = d_v = 128, flags as there).
+ * Workspace: kda_chunk_bwd_varlen_workspace_size bytes, 16-byte aligned
+ * (chunk states, adjoints and operand blocks in floor(T_total/64) + N slots
+ * per head).  Enqueued on `stream`; the caller keeps every buffer alive until
+ * it completes.
+ */
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* S0, const void* dO,
+                         const float* dS_T, void* dq, void* dk, void* dv, void* dg,
+                         void* dbeta, float* dS0, const int32_t* cu_seqlens, int N,
+                         int T_total, int H, int d_k, int d_v, int dtype, int flags,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kda_chunk_bwd_varlen needs (0 for unsupported arguments or
+ * nothing to do). */
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
+                                           int dtype, int flags);
+
+/*
  * Staged schedule: the same forward as kda_chunk_fwd, run as four separate
  * kernels with intermediates in a caller-provided workspace (the chunked
  * method's steps one by one).  Slower than kda_chunk_fwd; it exists so each

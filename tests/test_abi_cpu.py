@@ -177,3 +177,24 @@ def test_backward_variant_validation(L):
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 3) == base + 64 * 128 * 6
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 4) == 0
     assert _bwd_ex(L, 1, ws=1024, wsz=base) == -5    # too small for the scalar path
+
+
+def test_backward_varlen_validation(L):
+    """kda_chunk_bwd_varlen: argument checks before any launch; the workspace
+    holds floor(T_total / 64) + N chunk slots per head (each slot a chunk
+    state, a chunk-end adjoint and an operand block: 131840 bytes)."""
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(cu=16, N=2, T=100, flags=0, ws=None, wsz=0, dk=128):
+        return L.kda_chunk_bwd_varlen(p(16), p(16), p(16), p(16), p(16), None, p(16), None, p(16), p(16), p(16),
+                                      p(16), p(16), None, p(cu), N, T, 1, dk, dk, 1, flags, p(ws), wsz, None)
+    assert call(cu=None) == -1                        # cu_seqlens required
+    assert call(cu=18) == -4                          # int32-aligned
+    assert call(flags=4) == -7
+    assert call(dk=64) == -7
+    assert call() == -5                               # workspace missing
+    assert call(N=0) == 0                             # nothing to do
+    assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 0) == 3 * 131840
+    assert L.kda_chunk_bwd_varlen_workspace_size(5, 64 * 7, 3, 128, 128, 1, 0) == (7 + 5) * 3 * 131840
+    assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 1) == 3 * 131840 + 100 * 128 * 6
+    assert L.kda_chunk_bwd_varlen_workspace_size(2, 0, 1, 128, 128, 1, 0) == 0
