@@ -47,6 +47,12 @@ int main(void) {
   if (kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, KDA_BF16, KDA_GATE_SCALAR) !=
       (size_t)131840 + (size_t)64 * 128 * 6)
     return 1;
+  CHECK(kda_chunk_bwd_varlen(p, p, p, p, p, NULL, p, NULL, p, p, p, p, p, NULL, NULL, 2, 100, 1, 128, 128,
+                             KDA_BF16, 0, NULL, 0, NULL), KDA_ERR_NULL);
+  CHECK(kda_chunk_bwd_varlen(p, p, p, p, NULL, NULL, p, NULL, p, p, p, p, NULL, NULL, p, 2, 100, 1, 128, 128,
+                             KDA_BF16, KDA_NO_DELTA, NULL, 0, NULL), KDA_ERR_WORKSPACE);
+  if (kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, KDA_BF16, 0) != (size_t)3 * 131840)
+    return 1;
   printf("kda C ABI ok (version %d)\n", kda_version());
   return 0;
 }
