@@ -1314,7 +1314,14 @@ constexpr int O_BETA = O_A + SZ_CC;
 constexpr int O_GAM = O_BETA + C * 4;    // two chunk parities
 constexpr int O_QK = O_GAM + 2 * DK * 4;  // q_t . k_t partial sums, per worker
 constexpr int NQK = 16;                   // q.k partial sums per token (worker lane groups)
-constexpr int BYTES = O_QK + NQK * C * 4;
+// Operand reference of each chunk (two chunk parities): the integer log2
+// exponent rho_c per key channel that the gated operands are taken relative
+// to, the largest of them per worker, and per worker whether its channels'
+// referenced operands fit fp16 (1) or the chunk keeps bf16 operands (0).
+constexpr int O_RHO = O_QK + NQK * C * 4;  // int [2][DK]
+constexpr int O_RMX = O_RHO + 2 * DK * 4;  // int [2][4]
+constexpr int O_FLG = O_RMX + 2 * 4 * 4;   // int [2][4]
+constexpr int BYTES = O_FLG + 2 * 4 * 4;
 // solver scratch inside the -W region
 constexpr int S_LDT = 0;                           // fp32 [4][16][LDL]: L_II^T
 constexpr int S_LN = S_LDT + 4 * 16 * LDL * 4;     // fp16 [6][16][LDB]: -L_IJ, I > J
@@ -1328,6 +1335,7 @@ struct Ptr {
   bf16 *Kt, *Kh, *Qt, *Wn;
   f16 *KtT, *KbT, *VT, *P, *A;
   float *beta, *gam, *qk;
+  int *rho, *rmx, *flg;
   float* LdT; f16 *Ln, *D, *Dt;
   __device__ __forceinline__ void set(unsigned char* b) {
     Kt = reinterpret_cast<bf16*>(b + O_KT);
@@ -1342,6 +1350,9 @@ struct Ptr {
     beta = reinterpret_cast<float*>(b + O_BETA);
     gam = reinterpret_cast<float*>(b + O_GAM);
     qk = reinterpret_cast<float*>(b + O_QK);
+    rho = reinterpret_cast<int*>(b + O_RHO);
+    rmx = reinterpret_cast<int*>(b + O_RMX);
+    flg = reinterpret_cast<int*>(b + O_FLG);
     LdT = reinterpret_cast<float*>(b + O_WN + S_LDT);
     Ln = reinterpret_cast<f16*>(b + O_WN + S_LN);
     D = reinterpret_cast<f16*>(b + O_WN + S_D);
@@ -1568,7 +1579,94 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
 struct Gates {
   float b[4][8];
   float gm[8];
+  int rho[8];   // reference exponent of each of the lane's channels
 };
+
+// lane 7 of the caller's 16-lane row (ds_swizzle bit mode: and 0x10, or 0x07)
+__device__ __forceinline__ float row_lane7(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x0F0));
+}
+
+// Operand precision of a chunk.  The products Qg Kd^T (P), Kg Kd^T (L) and
+// Qg S only need the gate ratios 2^(b_t - b_j) (and, for Qg S, a row scaling
+// of S), so they may use Qg' = q 2^(b - rho), Kg' = k 2^(b - rho),
+// Kd' = k 2^(rho - b) and S' = Diag(2^rho) S for any per-channel reference
+// rho.  With rho the (rounded) log2 cumulative gate at the middle of the
+// chunk the referenced operands stay within 2^+-12 of the inputs' scale for
+// half-chunk decays of up to 12 bits (8.3 nats), where fp16 carries them with
+// 3 more mantissa bits than bf16 at the same MFMA rate; the rounding of these
+// gated operands is what dominates the output error with bf16 operands.  A
+// chunk whose referenced operands could leave that range keeps bf16 operands
+// and rho = 0 (the factorisation needs only the bf16 exponent range).
+//
+// Reference of the lane's channels (the cumulative gate of token 31) and
+// whether this worker's referenced operands of the chunk in r / gt fit fp16:
+// every |x| 2^(b - rho) and |k| 2^(rho - b) below 2^15 and the referenced
+// exponents within 12 bits.  |q|, |k| are bounded through the OR of their
+// bf16 bit patterns (the exponent field of the OR is at least every
+// element's).  Wave-uniform.
+__device__ __forceinline__ bool worker_range(const WRegs& r, Gates& gt) {
+  float u = -1e30f, dn = -1e30f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float rf = __builtin_rintf(row_lane7(gt.b[3][e]));
+    gt.rho[e] = (int)rf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = gt.b[i][e] - rf;
+      u = fmaxf(u, x);
+      dn = fmaxf(dn, -x);
+    }
+  }
+  uint32_t orb = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) orb |= r.q[i].w[k] | r.k[i].w[k];
+  const int eo = (int)max((orb >> 23) & 0xffu, (orb >> 7) & 0xffu);   // exponent fields of both halves
+  const float ext = fmaxf(u, dn);
+  const bool ok = ext <= 12.f && (float)(eo - 126) + ext <= 15.f;
+  return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
+// Commits the operand reference of the scanned chunk once every worker's
+// range check is in (fp16: the reference of the range check, else 0): the
+// gates become b - rho, gm becomes 2^(b_C - rho) (so that Kb = k 2^(b_C - b)
+// = Kd' gm), and the un-referenced chunk decay 2^b_C, the reference and the
+// worker's largest reference go to LDS for the owners (parity par).
+__device__ __forceinline__ void ref_commit(const Ptr& p, Gates& gt, bool f16m, int w, int lane, int par) {
+  const int j = lane >> 4, m = lane & 15;
+  const int c0 = 32 * w + 8 * j;
+  int rmax = -(1 << 20);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int rr = f16m ? gt.rho[e] : 0;
+    gt.rho[e] = rr;
+    rmax = max(rmax, rr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gt.b[i][e] -= (float)rr;
+  }
+  if (m == 0) {
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
+    typedef int intx4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<intx4*>(p.rho + par * DK + c0) = intx4{gt.rho[0], gt.rho[1], gt.rho[2], gt.rho[3]};
+    *reinterpret_cast<intx4*>(p.rho + par * DK + c0 + 4) = intx4{gt.rho[4], gt.rho[5], gt.rho[6], gt.rho[7]};
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gt.gm[e] = __builtin_amdgcn_ldexpf(gt.gm[e], -gt.rho[e]);
+  // largest reference of the worker's channels (wave maximum)
+#pragma unroll
+  for (int st = 1; st < 64; st *= 2) rmax = max(rmax, __shfl_xor(rmax, st));
+  if (lane == 0) p.rmx[par * 4 + w] = rmax;
+}
+
+// Combined fp16 decision of the four workers for the chunk of parity par.
+__device__ __forceinline__ bool chunk_f16(const Ptr& p, int par) {
+  typedef int intx4 __attribute__((ext_vector_type(4)));
+  const intx4 f = *reinterpret_cast<const intx4*>(p.flg + par * 4);
+  return __builtin_amdgcn_readfirstlane(f[0] & f[1] & f[2] & f[3]) != 0;
+}
 
 // Prefix sums of the gates in r.g; r.g is then reloaded with the gates of the
 // chunk that nx addresses (the next scan's input).  With a scalar gate the
@@ -1621,29 +1719,28 @@ __device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc<V>
   }
 }
 
-// Phase 1 of a worker: from the prefix sums, Kt = 2^b k, Kh = 2^-b k,
-// Qt = 2^b q (row-major bf16), the chunk decay gam of its channels and the
-// q.k partial sums; Kt and Kb = gam 2^-b k stay in registers as fp16
-// (kt_t[e], kb[e] = tokens 4m..4m+3 of channel e) and are stored transposed
-// in phase 2a.
+// Phase 1 of a worker: from the referenced prefix sums b' = b - rho,
+// Kt = 2^b' k, Kh = 2^-b' k, Qt = 2^b' q (row-major; fp16 or bf16 as the
+// chunk's operand choice f16m says) and the q.k partial sums; Kt^T and
+// Kb = gm' 2^-b' k = 2^(b_C - b) k stay in registers as fp16 (kt_t[e], kb[e]
+// = tokens 4m..4m+3 of channel e) and are stored transposed in phase 2a.
+// (Kt^T is referenced too: W = A' Kt picks up the factor 2^rho per channel
+// when it is stored.)
 //
 // The next-but-one chunk's k and q are loaded into the same registers row by
 // row as each row is consumed, so the loads spread over this phase's
 // arithmetic instead of arriving as one burst; each row's loads are pinned in
-// place by scheduling fences.
+// place by scheduling fences.  Only the stores depend on f16m, so no load is
+// under that branch.
 //
 // Without the delta rule Kt (row-major and transposed) has no reader and is
 // not formed.
 template <int V>
-__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
+__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, bool f16m,
                                              f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc<V>& nx) {
   constexpr bool ND = (V & kVarNoDelta) != 0;
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
-  if (m == 0) {
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
-  }
   // rows 4m + i: rmo(4m + i, e) = 4m LDK + i LDK + (e ^ ((m & 7) << 3)) for i < 4
   const int wb0 = 4 * m * LDK + (slot32(c0) ^ ((m & 7) << 3));
   const int wb1 = 4 * m * LDK + (slot32(c0 + 4) ^ ((m & 7) << 3));
@@ -1660,30 +1757,43 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
     qk[i] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qk[i] += qf[e] * kf[e];
-    bf16x8 kt, kh, qt;
+    float kt[8], kh[8], qt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // (a scalar gate: the same factors for every channel)
       const int es = (V & kVarScalarGate) ? 0 : e;
       const float ep = exp2_hw(gt.b[i][es]);
       const float em = exp2_hw(-gt.b[i][es]);
-      const float a = kf[e] * ep, d = kf[e] * em;
-      kt[e] = (bf16)a;
-      kh[e] = (bf16)d;
-      qt[e] = (bf16)(qf[e] * ep);
-      if constexpr (!ND) kt_t[e][i] = (f16)a;
-      kb[e][i] = (f16)(d * gt.gm[es]);
+      kt[e] = kf[e] * ep;
+      kh[e] = kf[e] * em;
+      qt[e] = qf[e] * ep;
+      if constexpr (!ND) kt_t[e][i] = (f16)kt[e];
+      kb[e][i] = (f16)(kh[e] * gt.gm[es]);
     }
     // channels c0..c0+3 and c0+4..c0+7 sit apart in the slab order
     const int r0 = wb0 + i * LDK, r1 = wb1 + i * LDK;
-    if constexpr (!ND) {
-      *reinterpret_cast<bf16x4*>(p.Kt + r0) = __builtin_shufflevector(kt, kt, 0, 1, 2, 3);
-      *reinterpret_cast<bf16x4*>(p.Kt + r1) = __builtin_shufflevector(kt, kt, 4, 5, 6, 7);
+    if (f16m) {
+      f16* Kt = reinterpret_cast<f16*>(p.Kt);
+      f16* Kh = reinterpret_cast<f16*>(p.Kh);
+      f16* Qt = reinterpret_cast<f16*>(p.Qt);
+      if constexpr (!ND) {
+        *reinterpret_cast<f16x4*>(Kt + r0) = f16x4{(f16)kt[0], (f16)kt[1], (f16)kt[2], (f16)kt[3]};
+        *reinterpret_cast<f16x4*>(Kt + r1) = f16x4{(f16)kt[4], (f16)kt[5], (f16)kt[6], (f16)kt[7]};
+      }
+      *reinterpret_cast<f16x4*>(Kh + r0) = f16x4{(f16)kh[0], (f16)kh[1], (f16)kh[2], (f16)kh[3]};
+      *reinterpret_cast<f16x4*>(Kh + r1) = f16x4{(f16)kh[4], (f16)kh[5], (f16)kh[6], (f16)kh[7]};
+      *reinterpret_cast<f16x4*>(Qt + r0) = f16x4{(f16)qt[0], (f16)qt[1], (f16)qt[2], (f16)qt[3]};
+      *reinterpret_cast<f16x4*>(Qt + r1) = f16x4{(f16)qt[4], (f16)qt[5], (f16)qt[6], (f16)qt[7]};
+    } else {
+      if constexpr (!ND) {
+        *reinterpret_cast<bf16x4*>(p.Kt + r0) = bf16x4{(bf16)kt[0], (bf16)kt[1], (bf16)kt[2], (bf16)kt[3]};
+        *reinterpret_cast<bf16x4*>(p.Kt + r1) = bf16x4{(bf16)kt[4], (bf16)kt[5], (bf16)kt[6], (bf16)kt[7]};
+      }
+      *reinterpret_cast<bf16x4*>(p.Kh + r0) = bf16x4{(bf16)kh[0], (bf16)kh[1], (bf16)kh[2], (bf16)kh[3]};
+      *reinterpret_cast<bf16x4*>(p.Kh + r1) = bf16x4{(bf16)kh[4], (bf16)kh[5], (bf16)kh[6], (bf16)kh[7]};
+      *reinterpret_cast<bf16x4*>(p.Qt + r0) = bf16x4{(bf16)qt[0], (bf16)qt[1], (bf16)qt[2], (bf16)qt[3]};
+      *reinterpret_cast<bf16x4*>(p.Qt + r1) = bf16x4{(bf16)qt[4], (bf16)qt[5], (bf16)qt[6], (bf16)qt[7]};
     }
-    *reinterpret_cast<bf16x4*>(p.Kh + r0) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
-    *reinterpret_cast<bf16x4*>(p.Kh + r1) = __builtin_shufflevector(kh, kh, 4, 5, 6, 7);
-    *reinterpret_cast<bf16x4*>(p.Qt + r0) = __builtin_shufflevector(qt, qt, 0, 1, 2, 3);
-    *reinterpret_cast<bf16x4*>(p.Qt + r1) = __builtin_shufflevector(qt, qt, 4, 5, 6, 7);
   }
   // the diagonal of P is q_t . k_t (the gates cancel): summed in fp32 from
   // the inputs instead of from the separately rounded gated operands; each
@@ -1737,22 +1847,29 @@ __device__ __forceinline__ void owner_vt(const Ptr& p, const Vec16 (&v)[4], int 
 __device__ __forceinline__ MB::F32 ldc_b(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ MH::F32 ldc_h(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 
+// A 16-byte operand fragment of the row-major gated arrays (Kt, Kh, Qt),
+// which hold fp16 or bf16 values as the chunk's operand choice says.
+template <typename TT>
+__device__ __forceinline__ typename Mma<TT>::F32 ldc_g(const bf16* p) {
+  return *reinterpret_cast<const typename Mma<TT>::F32*>(p);
+}
+
 // NTL 16x16 tiles X_t = A[rows 16 I_t ..] Kh[rows 16 J_t ..]^T of row-major
-// bf16 [C][DK] arrays (C layout).
+// [C][DK] arrays of TT (C layout).
 // (A_t = Qt where useQ[t], else Kt)
-template <int NTL, bool SWAP>
+template <typename TT, int NTL, bool SWAP>
 __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], const int (&I)[NTL],
                                          const int (&J)[NTL], floatx4 (&acc)[NTL], int lane) {
-  const int g4 = lane >> 4, l16 = lane & 15;
+  typedef Mma<TT> MT;
   const bf16* Kh = p.Kh;
   const int fl = frag_lane(lane);
-  MB::F32 af[NTL][DK / 32], bf[NTL][DK / 32];
+  typename MT::F32 af[NTL][DK / 32], bf[NTL][DK / 32];
 #pragma unroll
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[t][ks] = ldc_b((useQ[t] ? p.Qt : p.Kt) + fl + frag_off(I[t], ks));
-      bf[t][ks] = ldc_b(Kh + fl + frag_off(J[t], ks));
+      af[t][ks] = ldc_g<TT>((useQ[t] ? p.Qt : p.Kt) + fl + frag_off(I[t], ks));
+      bf[t][ks] = ldc_g<TT>(Kh + fl + frag_off(J[t], ks));
     }
   KDA_READS_FIRST();
 #pragma unroll
@@ -1761,7 +1878,7 @@ __device__ __forceinline__ void kh_tiles(const Ptr& p, const bool (&useQ)[NTL], 
   for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
     for (int t = 0; t < NTL; ++t)
-      acc[t] = SWAP ? MB::mma32(bf[t][ks], af[t][ks], acc[t]) : MB::mma32(af[t][ks], bf[t][ks], acc[t]);
+      acc[t] = SWAP ? MT::mma32(bf[t][ks], af[t][ks], acc[t]) : MT::mma32(af[t][ks], bf[t][ks], acc[t]);
 }
 
 __device__ __forceinline__ int ln_block(int I, int J) { return I * (I - 1) / 2 + J; }
@@ -1802,11 +1919,11 @@ __device__ __forceinline__ void lp_store(const Ptr& p, bool isP, int I, int J, f
 
 // Workers in phase 2a: blocks (I_t, J_t) of P = Tril(Qt Kh^T) (isP[t]) and
 // off-diagonal blocks of L = Diag(beta) Kt Kh^T, stored as -L, all fp16.
-template <int NTL>
+template <typename TT, int NTL>
 __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[NTL], const int (&I)[NTL],
                                             const int (&J)[NTL], int lane) {
   floatx4 acc[NTL];
-  kh_tiles<NTL, true>(p, isP, I, J, acc, lane);     // lane: row l16, columns 4g..4g+3
+  kh_tiles<TT, NTL, true>(p, isP, I, J, acc, lane);     // lane: row l16, columns 4g..4g+3
 #pragma unroll
   for (int t = 0; t < NTL; ++t) lp_store(p, isP[t], I[t], J[t], acc[t], lane);
 }
@@ -1816,17 +1933,18 @@ __device__ __forceinline__ void lp_block_tiles(const Ptr& p, const bool (&isP)[N
 // three of the lower triangle), from one read of those two row blocks of Qt
 // (or Kt) and of Kh: 16 fragments for three or four tiles instead of eight
 // per tile.
-template <bool DIAG>
+template <typename TT, bool DIAG>
 __device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J0, int lane) {
+  typedef Mma<TT> MT;
   const int fl = frag_lane(lane);
   const bf16* A = isP ? p.Qt : p.Kt;
-  MB::F32 af[2][DK / 32], bf[2][DK / 32];
+  typename MT::F32 af[2][DK / 32], bf[2][DK / 32];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[x][ks] = ldc_b(A + fl + frag_off(I0 + x, ks));
-      bf[x][ks] = ldc_b(p.Kh + fl + frag_off(J0 + x, ks));
+      af[x][ks] = ldc_g<TT>(A + fl + frag_off(I0 + x, ks));
+      bf[x][ks] = ldc_g<TT>(p.Kh + fl + frag_off(J0 + x, ks));
     }
   KDA_READS_FIRST();
   floatx4 acc[2][2];
@@ -1840,7 +1958,7 @@ __device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int y = 0; y < 2; ++y)
-        if (!DIAG || y <= x) acc[x][y] = MB::mma32(bf[y][ks], af[x][ks], acc[x][y]);
+        if (!DIAG || y <= x) acc[x][y] = MT::mma32(bf[y][ks], af[x][ks], acc[x][y]);
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -1858,24 +1976,26 @@ __device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J
 // tiles of Y and X^T.  D_I and D_I^T come out in accumulator layout: D_I^T's
 // tile is D_I by rows.  Writes D_I, D_I^T and block (I, I) of A' = D_I Diag(beta),
 // 8 bytes per lane.
+template <typename TT>
 __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   typedef Mma<float> MF;
+  typedef Mma<TT> MT;
   floatx4 n, nt;   // N and N^T tiles
   {
     const int fl = frag_lane(lane);
-    MB::F32 af[DK / 32], bf[DK / 32];
+    typename MT::F32 af[DK / 32], bf[DK / 32];
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      af[ks] = ldc_b(p.Kt + fl + frag_off(I, ks));
-      bf[ks] = ldc_b(p.Kh + fl + frag_off(I, ks));
+      af[ks] = ldc_g<TT>(p.Kt + fl + frag_off(I, ks));
+      bf[ks] = ldc_g<TT>(p.Kh + fl + frag_off(I, ks));
     }
     KDA_READS_FIRST();
     floatx4 x = {0.f, 0.f, 0.f, 0.f}, xt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      x = MB::mma32(af[ks], bf[ks], x);     // lane: (Kt Kh^T)[4g + jj][l16]
-      xt = MB::mma32(bf[ks], af[ks], xt);   // lane: (Kt Kh^T)[l16][4g + jj]
+      x = MT::mma32(af[ks], bf[ks], x);     // lane: (Kt Kh^T)[4g + jj][l16]
+      xt = MT::mma32(bf[ks], af[ks], xt);   // lane: (Kt Kh^T)[l16][4g + jj]
     }
     const floatx4 bt = *reinterpret_cast<const floatx4*>(p.beta + 16 * I + 4 * g4);
     const float bl = p.beta[16 * I + l16];
@@ -1967,9 +2087,15 @@ __device__ __forceinline__ void solver_offdiag_col(const Ptr& p, int lane) {
 // Phase 3, workers: W^T tile rows 32w.. of W = A' Kt (fp16 products from Kt^T
 // and A'), stored as -W into the row-major bf16 array.  A' is lower
 // triangular, so token blocks 0 and 1 need only the first 32-token slab.
-__device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
+// Kt^T holds the referenced k 2^(b - rho), so each channel row of W^T takes
+// the exact factor 2^rho (rho: the chunk's reference exponents).
+__device__ __forceinline__ void worker_w(const Ptr& p, const int* rho, int w, int lane) {
+  typedef int intx4 __attribute__((ext_vector_type(4)));
   const int g4 = lane >> 4, l16 = lane & 15;
   const int fl = frag_lane(lane);
+  intx4 rc[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) rc[ct] = *reinterpret_cast<const intx4*>(rho + 32 * w + 16 * ct + 4 * g4);
   MH::F32 ka[2][2], ab[4][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -1988,7 +2114,7 @@ __device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
       if (tb >= 2) acc = MH::mma32(ka[ct][1], ab[tb][1], acc);
       bf16x4 o;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
+      for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-__builtin_amdgcn_ldexpf(acc[jj], rc[ct][jj]));
       // = rmo(16 tb + l16, slot32(32 w + 16 ct + 4 g4))
       *reinterpret_cast<bf16x4*>(p.Wn + fl + 16 * tb * LDK + 32 * (w ^ (tb & 1)) + 4 * ct) = o;
     }
@@ -2063,6 +2189,67 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
   }
 }
 
+// Phase 2b, owners, for a chunk with fp16 operands: Dx[nt][I] = Qt'[rows
+// 16I..] @ S', the tiles held transposed as rows_times_state_b<true> holds
+// them, with Qt' = 2^(b - rho) q (fp16, LDS) and S' = 2^-kx Diag(2^rho) S
+// formed from the registers as fp16 fragments (rho: the chunk's reference
+// exponent of each key row; kx >= 0 keeps S' in the fp16 range and is put
+// back on Dx by the caller).
+__device__ __forceinline__ void qt_times_state_h(const bf16* Qt, const int* rho, int kx,
+                                                 const floatx4 (&S)[2][DK / 16], floatx4 (&Dx)[2][4], int lane) {
+  typedef int intx4 __attribute__((ext_vector_type(4)));
+  const int fl = frag_lane(lane);
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    MH::F32 af[2][4];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) af[k2][I] = ldc_g<f16>(Qt + fl + frag_off(I, 2 * hf + k2));
+    intx4 rr[2][2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        rr[k2][u] = *reinterpret_cast<const intx4*>(rho + 32 * (2 * hf + k2) + 16 * u + 4 * g4) - kx;
+    KDA_READS_FIRST();
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ks = 2 * hf + k2;
+      MH::F32 sf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          sf[nt][jj] = (f16)__builtin_amdgcn_ldexpf(S[nt][2 * ks][jj], rr[k2][0][jj]);
+          sf[nt][4 + jj] = (f16)__builtin_amdgcn_ldexpf(S[nt][2 * ks + 1][jj], rr[k2][1][jj]);
+        }
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) Dx[nt][I] = MH::mma32(sf[nt], af[k2][I], Dx[nt][I]);
+    }
+  }
+}
+
+// Scale exponent kx >= 0 that keeps an owner's S' = Diag(2^rho) S within
+// 2^15 (rmx: the chunk's largest reference exponent).  Wave-uniform.
+__device__ __forceinline__ int state_f16_shift(const floatx4 (&S)[2][DK / 16], int rmx) {
+  float mx = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, fabsf(S[nt][rt][jj]));
+#pragma unroll
+  for (int st = 1; st < 64; st *= 2) mx = fmaxf(mx, __shfl_xor(mx, st));
+  // mx < 2^ex; S' < 2^(ex + rmx - kx) <= 2^15
+  const int ex = __builtin_amdgcn_frexp_expf(mx);
+  return __builtin_amdgcn_readfirstlane(max(0, ex + rmx - 15));
+}
+
 // Phase 1, owners: O += P Delta, S <- Diag(gam) S + Kb^T Delta.
 template <int NTL>
 __device__ __forceinline__ void owner_intra(const Ptr& p, const MH::F32 (&Df)[NTL][2], floatx4 (&O)[NTL][4], int lane) {
@@ -2128,6 +2315,50 @@ __device__ __forceinline__ void owner_store(const floatx4 (&O)[2][4], __amdgpu_b
   }
 }
 
+}  // namespace pipe
+
+namespace pipe {
+// Phase 2a tile schedules of the workers, per operand type.
+// No delta rule: the ten P blocks, three / three / two / two per worker.
+template <typename TT>
+__device__ __forceinline__ void nd_p_tiles(const Ptr& p, int w, int lane) {
+  switch (w) {
+    case 0: { const bool q[3] = {1, 1, 1}; const int I[3] = {0, 3, 3}, J[3] = {0, 0, 3};
+              lp_block_tiles<TT, 3>(p, q, I, J, lane); break; }
+    case 1: { const bool q[3] = {1, 1, 1}; const int I[3] = {1, 1, 3}, J[3] = {0, 1, 1};
+              lp_block_tiles<TT, 3>(p, q, I, J, lane); break; }
+    case 2: { const bool q[2] = {1, 1}; const int I[2] = {2, 2}, J[2] = {0, 1};
+              lp_block_tiles<TT, 2>(p, q, I, J, lane); break; }
+    default: { const bool q[2] = {1, 1}; const int I[2] = {2, 3}, J[2] = {2, 2};
+               lp_block_tiles<TT, 2>(p, q, I, J, lane); break; }
+  }
+}
+// State only: the six off-diagonal L blocks.
+template <typename TT>
+__device__ __forceinline__ void state_l_tiles(const Ptr& p, int w, int lane) {
+  switch (w) {
+    case 0: { const bool q[2] = {0, 0}; const int I[2] = {1, 2}, J[2] = {0, 1};
+              lp_block_tiles<TT, 2>(p, q, I, J, lane); break; }
+    case 1: { const bool q[2] = {0, 0}; const int I[2] = {2, 3}, J[2] = {0, 2};
+              lp_block_tiles<TT, 2>(p, q, I, J, lane); break; }
+    case 2: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {0};
+              lp_block_tiles<TT, 1>(p, q, I, J, lane); break; }
+    default: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {1};
+               lp_block_tiles<TT, 1>(p, q, I, J, lane); break; }
+  }
+}
+// With outputs: P in three groups sharing operand rows (blocks 2-3 x 0-1;
+// the lower triangles of 0-1 x 0-1 and of 2-3 x 2-3), and the L blocks
+// (2-3) x (0-1); the owners form L(1,0), L(3,2) and the diagonal blocks.
+template <typename TT>
+__device__ __forceinline__ void pl_tiles(const Ptr& p, int w, int lane) {
+  switch (w) {
+    case 0: lp_block22<TT, false>(p, true, 2, 0, lane); break;
+    case 1: lp_block22<TT, true>(p, true, 0, 0, lane); break;
+    case 2: lp_block22<TT, true>(p, true, 2, 2, lane); break;
+    default: lp_block22<TT, false>(p, false, 2, 0, lane); break;
+  }
+}
 }  // namespace pipe
 
 // V: variant flags (kVarScalarGate, kVarNoDelta).  Without the delta rule
@@ -2246,6 +2477,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
+    __syncthreads();   // the workers' range checks of the first chunk
     // (the owners keep their per-lane addresses in registers for the whole
     // loop; the workers, short of registers, recompute them in each phase)
     for (int n = -1; n < nchunks; ++n) {
@@ -2276,13 +2508,22 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       if (nxt && !vzero) owner_vt(p, vr, o, lane);
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
-      if (!ND && nxt) solver_block(p, o, lane);
+      const bool f16m = chunk_f16(p, (n + 1) & 1);
+      if (!ND && nxt) {
+        if (f16m)
+          solver_block<f16>(p, o, lane);
+        else
+          solver_block<bf16>(p, o, lane);
+      }
       // with outputs the workers form the P blocks and the L blocks (2-3) x
       // (0-1); owners 0 and 1 form L(1,0) and L(3,2)
       if (!ND && nxt && outp && o < 2) {
         const bool q[1] = {false};
         const int I1[1] = {o == 0 ? 1 : 3}, J1[1] = {o == 0 ? 0 : 2};
-        lp_block_tiles<1>(p, q, I1, J1, lane);
+        if (f16m)
+          lp_block_tiles<f16, 1>(p, q, I1, J1, lane);
+        else
+          lp_block_tiles<bf16, 1>(p, q, I1, J1, lane);
       }
       // values of chunk n+2: unconditional (zeros past the end), and after the
       // role switch -- loads issued just before such a switch were seen to
@@ -2296,7 +2537,25 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (nxt && outp) rows_times_state_b<true>(p.Qt, S, O, lane);
+      if (nxt && outp) {
+        const int par = (n + 1) & 1;
+        if (chunk_f16(p, par)) {
+          typedef int intx4 __attribute__((ext_vector_type(4)));
+          const intx4 rm = *reinterpret_cast<const intx4*>(p.rmx + par * 4);
+          const int kx = state_f16_shift(S, max(max(rm[0], rm[1]), max(rm[2], rm[3])));
+          qt_times_state_h(p.Qt, p.rho + par * DK, kx, S, O, lane);
+          if (kx != 0) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) O[nt][I][jj] = __builtin_amdgcn_ldexpf(O[nt][I][jj], kx);
+          }
+        } else {
+          rows_times_state_b<true>(p.Qt, S, O, lane);
+        }
+      }
       p.sync(smem_raw);
       // phase 3: U of chunk n+1
 #pragma unroll
@@ -2318,6 +2577,14 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     Gates gt;
     fetch_qkg<V>(r, a, bb, h, c0, w, lane);   // zeros when the sequence is empty
     worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + 1, w, lane));
+    {
+      const bool ok = worker_range(r, gt);
+      if (lane == 0) p.flg[w] = ok;
+    }
+    __syncthreads();
+    // operand choice of the chunk being prepared (f16m) and of the next
+    bool f16m = chunk_f16(p, 0);
+    ref_commit(p, gt, f16m, w, lane, 0);
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
@@ -2334,7 +2601,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
           r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
         }
-        worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, kb, kt_t, nx);
+        worker_apply<V>(p, r, gt, w, lane, f16m, kb, kt_t, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
@@ -2343,41 +2610,27 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // runs: the six L blocks alone; no delta rule: the P blocks alone)
       if (ND && nxt && outp) {
         worker_kbt<V>(p, kb, kt_t, w, lane);
-        switch (w) {
-          case 0: { const bool q[3] = {1, 1, 1}; const int I[3] = {0, 3, 3}, J[3] = {0, 0, 3};
-                    lp_block_tiles<3>(p, q, I, J, lane); break; }
-          case 1: { const bool q[3] = {1, 1, 1}; const int I[3] = {1, 1, 3}, J[3] = {0, 1, 1};
-                    lp_block_tiles<3>(p, q, I, J, lane); break; }
-          case 2: { const bool q[2] = {1, 1}; const int I[2] = {2, 2}, J[2] = {0, 1};
-                    lp_block_tiles<2>(p, q, I, J, lane); break; }
-          default: { const bool q[2] = {1, 1}; const int I[2] = {2, 3}, J[2] = {2, 2};
-                     lp_block_tiles<2>(p, q, I, J, lane); break; }
-        }
+        if (f16m)
+          nd_p_tiles<f16>(p, w, lane);
+        else
+          nd_p_tiles<bf16>(p, w, lane);
       } else if (ND && nxt) {
         worker_kbt<V>(p, kb, kt_t, w, lane);
       } else if (nxt && !outp) {
         worker_kbt<V>(p, kb, kt_t, w, lane);
-        switch (w) {
-          case 0: { const bool q[2] = {0, 0}; const int I[2] = {1, 2}, J[2] = {0, 1};
-                    lp_block_tiles<2>(p, q, I, J, lane); break; }
-          case 1: { const bool q[2] = {0, 0}; const int I[2] = {2, 3}, J[2] = {0, 2};
-                    lp_block_tiles<2>(p, q, I, J, lane); break; }
-          case 2: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {0};
-                    lp_block_tiles<1>(p, q, I, J, lane); break; }
-          default: { const bool q[1] = {0}; const int I[1] = {3}, J[1] = {1};
-                     lp_block_tiles<1>(p, q, I, J, lane); break; }
-        }
+        if (f16m)
+          state_l_tiles<f16>(p, w, lane);
+        else
+          state_l_tiles<bf16>(p, w, lane);
       } else if (nxt) {
         // P in three groups sharing operand rows (blocks 2-3 x 0-1; the
         // lower triangles of 0-1 x 0-1 and of 2-3 x 2-3), and the L blocks
         // (2-3) x (0-1); the owners form L(1,0), L(3,2) and the diagonal blocks
         worker_kbt<V>(p, kb, kt_t, w, lane);
-        switch (w) {
-          case 0: lp_block22<false>(p, true, 2, 0, lane); break;
-          case 1: lp_block22<true>(p, true, 0, 0, lane); break;
-          case 2: lp_block22<true>(p, true, 2, 2, lane); break;
-          default: lp_block22<false>(p, false, 2, 0, lane); break;
-        }
+        if (f16m)
+          pl_tiles<f16>(p, w, lane);
+        else
+          pl_tiles<bf16>(p, w, lane);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
@@ -2393,10 +2646,16 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           solver_offdiag_col<2>(p, lane);
       }
       worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
+      {
+        const bool ok = worker_range(r, gt);
+        if (lane == 0) p.flg[(n & 1) * 4 + w] = ok;
+      }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 3: W
-      if (!ND && nxt) worker_w(p, w, lane);
+      // phase 3: W; the operand choice of chunk n+2 is in
+      if (!ND && nxt) worker_w(p, p.rho + ((n + 1) & 1) * DK, w, lane);
+      f16m = chunk_f16(p, n & 1);
+      ref_commit(p, gt, f16m, w, lane, n & 1);
     }
   }
 }

@@ -36,9 +36,15 @@
  *     operand tiles for 128 do not fit in one CU's LDS).
  *   - Numerical domain of the chunked path: every channel's log-gate summed
  *     over any 64 consecutive tokens of a chunk must stay above -80 (decay
- *     over one chunk >= e^-80); beyond it results may be Inf/NaN.  The decode
- *     step has no such limit.  NaN/Inf inputs propagate; nothing is checked
- *     on the device.
+ *     over one chunk >= e^-80); beyond it results may be Inf/NaN.  With
+ *     KDA_BF16 inputs some matrix operands are fp16: v, the residual
+ *     U - W S of each chunk and the terms it is formed from must stay below
+ *     65504 in magnitude (q, k of unit scale and |v| up to a few thousand
+ *     are far inside).  The gated q / k operands are fp16 relative to a
+ *     per-channel reference exponent only where they fit (else bf16, chosen
+ *     per chunk), and the state enters its product scaled into range, so
+ *     neither limits the domain.  The decode step has no such limits.
+ *     NaN/Inf inputs propagate; nothing is checked on the device.
  *
  * Return values: KDA_OK (0) or a negative kda_status.  No C++ exception
  * crosses this interface.  On KDA_ERR_HIP the HIP error of the failing call
@@ -116,10 +122,10 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
  * Variants of the recurrence, the two relatives of KDA on "...Making LLM
  * Training and Inference More Efficient", as bit flags:
  *   KDA_GATE_SCALAR  one forget gate per token and head (Gated DeltaNet,
- *                    §3.2): g is [B,T,H] ([N,H] for a decode step) and
+ *                    §3.3, its first formula): g is [B,T,H] ([N,H] for a decode step) and
  *                    Diag(exp g_t) becomes exp(g_t) I.
  *   KDA_NO_DELTA     no delta rule (the per-channel decay of GLA / RWKV-6,
- *                    §3.3): S_t = Diag(exp g_t) S_{t-1} + k_t v_t^T,
+ *                    §3.3, the element-wise gate): S_t = Diag(exp g_t) S_{t-1} + k_t v_t^T,
  *                    o_t = S_t^T q_t; beta is not read and may be NULL.
  * Both may be combined (a scalar-gated linear attention).
  */
@@ -227,7 +233,7 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int d
 
 /*
  * kda_chunk_bwd_ex -- kda_chunk_bwd for the variants of kda_chunk_fwd_ex
- * ("...Making LLM Training and Inference More Efficient" §3.2, §3.3); flags
+ * ("...Making LLM Training and Inference More Efficient" §3.3); flags
  * = 0 is exactly kda_chunk_bwd.
  *   KDA_GATE_SCALAR  g [B,T,H] in, dg [B,T,H] out (both dtype `dtype`,
  *                    aligned to the element size).  The scalar gate is the
