@@ -134,15 +134,21 @@ def recurrent_fwd(q, k, v, g, beta, S0=None, nthreads: int = 0, scalar_gate: boo
     return o, ST
 
 
-def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0, scalar_gate: bool = False, delta: bool = True):
+def recurrent_step(q, k, v, g, beta, S, nthreads: int = 0, scalar_gate: bool = False, delta: bool = True,
+                   inplace: bool = False):
     """One decode token for N sequences (g [N,H,dk], or [N,H] with
-    scalar_gate).  S [N,H,dk,dv] fp64 is returned updated (a new array; the
-    input is not modified).  Returns (o, S_new)."""
+    scalar_gate).  S [N,H,dk,dv] fp64 is returned updated (a new array and the
+    input untouched; with inplace=True a C-contiguous fp64 S is updated in
+    place and returned).  Returns (o, S_new)."""
     q, k, v, g = (_f64(a) for a in (q, k, v, g))
     beta = None if beta is None else _f64(beta)
     N, H, dk = q.shape
     dv = v.shape[-1]
-    Sn = _f64(S).copy()
+    if inplace:
+        assert isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+        Sn = S
+    else:
+        Sn = _f64(S).copy()
     assert Sn.shape == (N, H, dk, dv)
     o = np.zeros((N, H, dv), dtype=np.float64)
     rc = _load().kda_oracle_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),

@@ -5,11 +5,15 @@ Tolerances (stated as numbers, applied per call):
   bf16 inputs : per-head relative L2 <= 5e-3 on o and on S_T, and
                 max |err| <= 3e-2 * RMS(o_ref) on o and on S_T.
 For the bf16 output o the max-|err| bound is applied to the error beyond the
-output's own rounding: |o - o_ref| - 2^-8 |o_ref| (2^-8 = bf16 unit
-roundoff).  Rounding the exact result to bf16 alone already reaches
-2^-8 |o| per element, i.e. more than 3e-2 * RMS for outputs beyond
-~7.7 RMS, which occur in every large workload; the literal figure is
-reported alongside.  S_T is fp32 and gets no allowance.
+rounding that the bf16 format forces on each element of the exact result,
+    excess = max_i ( |o_i - o_ref_i| - |bf16(o_ref_i) - o_ref_i| ),
+so that the correctly rounded result has excess 0.  (Rounding alone already
+brings the literal max |bf16(o_ref) - o_ref| to 1.5-2.7 % of RMS on the
+H16 T4K workload, depending on the seed, and to ~3 % on the 256-head
+B8 T8K workload.)  A result within e of o_ref before its own rounding has
+excess <= 2e.  The literal max |o - o_ref| and that rounding floor are
+reported beside it, and a caller may assert the literal bound too
+(literal=True).  S_T is fp32 and gets no allowance.
 The oracle always receives exact fp64 copies of the values the GPU received.
 """
 from __future__ import annotations
@@ -22,7 +26,6 @@ import oracle
 FP32_MAX = 1e-4
 BF16_REL_L2 = 5e-3
 BF16_MAX = 3e-2
-BF16_U = 2.0 ** -8   # unit roundoff of the bf16 output format
 
 
 def to64(t):
@@ -35,7 +38,37 @@ def rms(x):
     return float(np.sqrt(np.mean(np.square(x)))) if x.size else 0.0
 
 
-def check_prefill(o_gpu, S_gpu, o_ref, S_ref, dtype, what=""):
+def bf16_round(x):
+    """x (fp64) rounded to the nearest bf16 value (ties to even), as fp64."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).double().numpy()
+
+
+def rounding_floor(o_ref):
+    """|bf16(o_ref) - o_ref| per element: the error the output format forces."""
+    return np.abs(bf16_round(o_ref) - o_ref)
+
+
+def head_rel_l2(x, ref, head_axes):
+    """Largest relative L2 error over heads; head_axes are the axes that index
+    a head (the others are reduced)."""
+    red = tuple(i for i in range(ref.ndim) if i not in head_axes)
+    num = np.sqrt(np.sum(np.square(x - ref), axis=red))
+    den = np.sqrt(np.sum(np.square(ref), axis=red))
+    ok = den > 0
+    return float(np.max(num[ok] / den[ok])) if np.any(ok) else 0.0
+
+
+def bf16_output_stats(o_gpu, o_ref):
+    """(literal max |err|, rounding floor max, excess beyond rounding) of a
+    bf16 output, each over all elements (absolute)."""
+    if not o_ref.size:
+        return 0.0, 0.0, 0.0
+    err = np.abs(o_gpu - o_ref)
+    fl = rounding_floor(o_ref)
+    return float(np.max(err)), float(np.max(fl)), float(np.max(err - fl))
+
+
+def check_prefill(o_gpu, S_gpu, o_ref, S_ref, dtype, what="", literal=False):
     """o_*: [B,T,H,dv]; S_*: [B,H,dk,dv] (numpy fp64)."""
     stats = {}
     if dtype == torch.float32:
@@ -47,34 +80,36 @@ def check_prefill(o_gpu, S_gpu, o_ref, S_ref, dtype, what=""):
         assert e_o <= FP32_MAX * scale + 1e-30, f"{what}: o max err {e_o:.3e} > 1e-4*RMS {scale:.3e}"
         assert e_s <= FP32_MAX * max(scale, 1e-30), f"{what}: S_T max err {e_s:.3e} > 1e-4*RMS(o) {scale:.3e}"
         return stats
-    B, T, H, dv = o_ref.shape
-    worst_o = 0.0
-    for b in range(B):
-        for h in range(H):
-            ref = o_ref[b, :, h]
-            n = np.linalg.norm(ref)
-            if n > 0:
-                worst_o = max(worst_o, float(np.linalg.norm(o_gpu[b, :, h] - ref) / n))
-    worst_s = 0.0
-    for b in range(B):
-        for h in range(H):
-            ref = S_ref[b, h]
-            n = np.linalg.norm(ref)
-            if n > 0:
-                worst_s = max(worst_s, float(np.linalg.norm(S_gpu[b, h] - ref) / n))
-    e_o = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
-    x_o = float(np.max(np.abs(o_gpu - o_ref) - BF16_U * np.abs(o_ref))) if o_ref.size else 0.0
+    worst_o = head_rel_l2(o_gpu, o_ref, (0, 2))
+    worst_s = head_rel_l2(S_gpu, S_ref, (0, 1))
+    e_o, fl_o, x_o = bf16_output_stats(o_gpu, o_ref)
     e_s = float(np.max(np.abs(S_gpu - S_ref))) if S_ref.size else 0.0
-    r_o = rms(o_ref)
-    stats.update(rel_l2_o=worst_o, rel_l2_S=worst_s, max_err_o_over_rms=e_o / max(r_o, 1e-30),
-                 excess_err_o_over_rms=x_o / max(r_o, 1e-30), max_err_S_over_rms_o=e_s / max(r_o, 1e-30),
-                 max_err_S_over_rms_S=e_s / max(rms(S_ref), 1e-30))
+    r_o = max(rms(o_ref), 1e-30)
+    stats.update(rel_l2_o=worst_o, rel_l2_S=worst_s, max_err_o_over_rms=e_o / r_o,
+                 rounding_floor_o_over_rms=fl_o / r_o, excess_err_o_over_rms=x_o / r_o,
+                 max_err_S_over_rms_o=e_s / r_o, max_err_S_over_rms_S=e_s / max(rms(S_ref), 1e-30))
     print(f"[parity] {what}: " + " ".join(f"{k}={v:.3e}" for k, v in stats.items()), flush=True)
     assert worst_o <= BF16_REL_L2, f"{what}: per-head rel L2 of o {worst_o:.3e} > 5e-3"
     assert worst_s <= BF16_REL_L2, f"{what}: per-head rel L2 of S_T {worst_s:.3e} > 5e-3"
     assert x_o <= BF16_MAX * r_o, f"{what}: o error beyond rounding {x_o:.3e} > 3e-2*RMS {r_o:.3e}"
     assert e_s <= BF16_MAX * r_o, f"{what}: S_T max err {e_s:.3e} > 3e-2*RMS(o) {r_o:.3e}"
+    if literal:
+        assert e_o <= BF16_MAX * r_o, f"{what}: o max err {e_o:.3e} > 3e-2*RMS {r_o:.3e}"
     return stats
+
+
+def check_step(o_gpu, o_ref, dtype, what=""):
+    """One decode step's output o [N,H,dv] (numpy fp64) at the same bounds."""
+    if dtype == torch.float32:
+        assert np.max(np.abs(o_gpu - o_ref)) <= FP32_MAX * rms(o_ref), what
+        return {}
+    worst = head_rel_l2(o_gpu, o_ref, (0, 1))
+    e_o, fl_o, x_o = bf16_output_stats(o_gpu, o_ref)
+    r_o = max(rms(o_ref), 1e-30)
+    assert worst <= BF16_REL_L2, f"{what}: per-head rel L2 {worst:.3e} > 5e-3"
+    assert x_o <= BF16_MAX * r_o, f"{what}: error beyond rounding {x_o:.3e} > 3e-2*RMS {r_o:.3e}"
+    return dict(rel_l2=worst, max_err_over_rms=e_o / r_o, rounding_floor_over_rms=fl_o / r_o,
+                excess_err_over_rms=x_o / r_o)
 
 
 def oracle_prefill(inp, heads=None, nthreads=0, scalar_gate=False, delta=True):

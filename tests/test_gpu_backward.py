@@ -3,12 +3,16 @@ reverse-mode oracle, through the C ABI.  Needs an MI355X.
 
 Tolerances (bf16 inputs, gradients in bf16): per-head relative L2 of every
 gradient <= 1e-2 (dS0: fp32 output, same bound), and max |err| beyond the
-output's own bf16 rounding <= 0.1 * RMS(reference).  Each gradient is a
-sum of products with two to four chained bf16-rounded operands (unit
-roundoff 2^-9 each) where a forward output has one or two, and the forward's
-bound is 5e-3 per head; the backward bound allows twice that.  Measured:
-3.5-3.8e-3 for dq, dk, dv, dbeta, about 6e-3 for dg (a reverse sum over the
-chunk of terms that partly cancel), 1.8e-3 for dS0.
+rounding that the bf16 output format forces on each element of the exact
+gradient (|bf16(r) - r|, none for the fp32 dS0) <= 0.1 * RMS(reference).
+The pages state no tolerance for gradients.  Each gradient is a sum of
+products with two to four chained operands rounded to 16-bit formats (unit
+roundoff 2^-8 for bf16, 2^-11 for fp16) where a forward output has one or
+two, and the forward's bound is 5e-3 per head; the backward bound allows
+twice that.  Every case prints the measured figures; on the full B8 H32
+T8192 workload they are about 3.5-3.8e-3 for dq, dk, dv, dbeta, 6e-3 for dg
+(a reverse sum over the chunk of terms that partly cancel) and 1.8e-3 for
+dS0.
 """
 import numpy as np
 import pytest
@@ -16,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import BF16_U, rms, to64
+from tests.parity import rms, rounding_floor, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -45,62 +49,46 @@ def _inputs(B, T, H, seed, s0=True, dst=True, cfg=W.PREFILL_BF16_H16_T4K, scalar
     return inp
 
 
-def _oracle(inp, heads=None, chunk_adjoints=False, scalar_gate=False, delta=True):
-    names = ("q", "k", "v", "g", "beta")
-    if heads is None:
-        x = [to64(inp[n]) for n in names]
-        S0, dO, dST = to64(inp["S0"]), to64(inp["dO"]), to64(inp["dST"])
-    else:
-        x = [np.stack([to64(inp[n][b, :, h]) for b, h in heads])[:, :, None] for n in names]
-        S0 = None if inp["S0"] is None else np.stack([to64(inp["S0"][b, h]) for b, h in heads])[:, None]
-        dO = np.stack([to64(inp["dO"][b, :, h]) for b, h in heads])[:, :, None]
-        dST = None if inp["dST"] is None else np.stack([to64(inp["dST"][b, h]) for b, h in heads])[:, None]
+def _oracle(inp, chunk_adjoints=False, scalar_gate=False, delta=True):
+    x = [to64(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    S0, dO, dST = to64(inp["S0"]), to64(inp["dO"]), to64(inp["dST"])
     if not delta:
         x[4] = None
     return oracle.recurrent_bwd(*x, S0, dO, dST, chunk_adjoints=chunk_adjoints, scalar_gate=scalar_gate,
                                 delta=delta)
 
 
-def _pick(gr, heads):
-    out = {}
-    for n in NAMES:
-        t = gr[n]
-        if t is None:
-            continue
-        if n == "dS0":
-            out[n] = np.stack([to64(t[b, h]) for b, h in heads])[:, None]
-        else:
-            out[n] = np.stack([to64(t[b, :, h]) for b, h in heads])[:, :, None]
-    return out
+def _head_rel(g, r, scale, head_axes):
+    red = tuple(i for i in range(r.ndim) if i not in head_axes)
+    num = np.sqrt(np.sum(np.square(g - r), axis=red))
+    den = np.sqrt(np.sum(np.square(scale), axis=red))
+    ok = den > 0
+    return float(np.max(num[ok] / den[ok])) if np.any(ok) else 0.0
 
 
 def _check(got, ref, what, dg_scale=None):
     """got/ref: dicts of numpy arrays shaped [B, T, H, ...] ([B, H, ...] for dS0).
     dg_scale (scalar gate): per-token magnitude sum_c |dg_c| of the per-channel
-    gradient whose channel sum dg is; dg is measured against it."""
+    gradient whose channel sum dg is; dg is bounded against it (and its error
+    against its own norm is printed beside)."""
     worst = {}
+    own = None
     for n in NAMES:
         if n not in got:
             continue
         g, r = got[n], ref[n]
         if r.size == 0:
             continue
-        if n == "dS0":
-            heads = [(b, h) for b in range(r.shape[0]) for h in range(r.shape[1])]
-            sl = lambda x, b, h: x[b, h]
-        else:
-            heads = [(b, h) for b in range(r.shape[0]) for h in range(r.shape[2])]
-            sl = lambda x, b, h: x[b, :, h]
-        rel = 0.0
+        axes = (0, 1) if n == "dS0" else (0, 2)
         scale = dg_scale if (n == "dg" and dg_scale is not None) else r
-        for b, h in heads:
-            den = np.linalg.norm(sl(scale, b, h))
-            if den > 0:
-                rel = max(rel, float(np.linalg.norm(sl(g, b, h) - sl(r, b, h)) / den))
-        allow = 0.0 if n == "dS0" else BF16_U
-        over = float(np.max(np.abs(g - r) - allow * np.abs(r))) / max(rms(scale), 1e-30)
+        rel = _head_rel(g, r, scale, axes)
+        if n == "dg" and dg_scale is not None:
+            own = _head_rel(g, r, r, axes)
+        allow = 0.0 if n == "dS0" else rounding_floor(r)
+        over = float(np.max(np.abs(g - r) - allow)) / max(rms(scale), 1e-30)
         worst[n] = (rel, over)
-    print(f"[bwd parity] {what}: " + " ".join(f"{n}=({a:.2e},{b:.2e})" for n, (a, b) in worst.items()), flush=True)
+    print(f"[bwd parity] {what}: " + " ".join(f"{n}=({a:.2e},{b:.2e})" for n, (a, b) in worst.items())
+          + ("" if own is None else f" dg vs its own norm: per-head rel L2 {own:.2e}"), flush=True)
     for n, (a, b) in worst.items():
         assert a <= REL_L2, f"{what}: {n} per-head rel L2 {a:.3e} > {REL_L2}"
         assert b <= MAX_OVER, f"{what}: {n} max err beyond rounding {b:.3e} > {MAX_OVER} RMS"
@@ -167,17 +155,18 @@ def test_chunk_states_and_adjoints(kda):
             S = S[0, 0]
 
 
-def test_B8_H32_T8192_sampled(kda):
-    """The benchmark's prefill workload: full-size backward, sampled heads."""
+def test_B8_H32_T8192(kda):
+    """The benchmark's prefill workload: full-size backward, all 256 heads."""
     cfg = W.PREFILL_BF16_B8_H32_T8K
     inp = _inputs(cfg.B, cfg.T, cfg.H, 2, s0=False, dst=False, cfg=cfg)
     print("case bwd B8 H32 T8192", flush=True)
     gr = _run(kda, inp)
-    heads = [(0, 0), (5, 20), (7, 31)]
-    ref = _oracle(inp, heads)
-    _check(_pick(gr, heads), ref, "B8 H32 T8192")
     for n in NAMES[:-1]:
         assert torch.isfinite(gr[n].float()).all(), n
+    ref = _oracle(inp)
+    got = {n: to64(gr[n]) for n in NAMES}
+    del gr, inp
+    _check(got, ref, "B8 H32 T8192")
 
 
 def test_zero_length(kda):
@@ -202,10 +191,10 @@ def test_deterministic(kda):
 # taken from the oracle's per-channel gradient on the broadcast gate.
 
 
-def _dg_scale(inp, heads=None):
+def _dg_scale(inp):
     full = dict(inp)
     full["g"] = inp["g"][..., None].expand(*inp["g"].shape, 128).contiguous()
-    per = _oracle(full, heads)["dg"]
+    per = _oracle(full)["dg"]
     return np.abs(per).sum(-1)
 
 
@@ -224,14 +213,19 @@ def test_scalar_gate_small_shapes(kda, B, T, H, s0, dst):
     _check(got, ref, f"scalar gate B{B}T{T}H{H}", dg_scale=_dg_scale(inp))
 
 
-def test_scalar_gate_B8_H32_T8192_sampled(kda):
+def test_scalar_gate_B8_H32_T8192(kda):
+    """Full-size scalar-gate backward, every head; the per-channel oracle
+    gradient that bounds dg runs on a quarter of the heads at a time."""
     cfg = W.PREFILL_BF16_B8_H32_T8K
     inp = _inputs(cfg.B, cfg.T, cfg.H, 4, s0=False, dst=False, cfg=cfg, scalar_gate=True)
     print("case bwd scalar gate B8 H32 T8192", flush=True)
     gr = _run(kda, inp, scalar_gate=True)
-    heads = [(1, 3), (6, 30)]
-    ref = _oracle(inp, heads, scalar_gate=True)
-    _check(_pick(gr, heads), ref, "scalar gate B8 H32 T8192", dg_scale=_dg_scale(inp, heads))
+    ref = _oracle(inp, scalar_gate=True)
+    scale = np.concatenate([_dg_scale({k: (v[b0:b0 + 2] if v is not None else None) for k, v in inp.items()})
+                            for b0 in range(0, cfg.B, 2)])
+    got = {n: to64(gr[n]) for n in NAMES}
+    del gr, inp
+    _check(got, ref, "scalar gate B8 H32 T8192", dg_scale=scale)
 
 
 # ---------------------------------------------------------------- no delta rule
@@ -266,11 +260,13 @@ def test_no_delta_scalar_gate(kda, B, T, H):
     _check(got, ref, f"no delta, scalar gate B{B}T{T}H{H}", dg_scale=scale)
 
 
-def test_no_delta_B8_H32_T8192_sampled(kda):
+def test_no_delta_B8_H32_T8192(kda):
+    """Full-size backward without the delta rule, all 256 heads."""
     cfg = W.PREFILL_BF16_B8_H32_T8K
     inp = _inputs(cfg.B, cfg.T, cfg.H, 6, s0=False, dst=False, cfg=cfg)
     print("case bwd no delta B8 H32 T8192", flush=True)
     gr = _run(kda, inp, delta=False)
-    heads = [(2, 7), (7, 31)]
-    ref = _oracle(inp, heads, delta=False)
-    _check(_pick(gr, heads), ref, "no delta B8 H32 T8192")
+    ref = _oracle(inp, delta=False)
+    got = {n: to64(gr[n]) for n in NAMES if gr[n] is not None}
+    del gr, inp
+    _check(got, ref, "no delta B8 H32 T8192")

@@ -106,14 +106,14 @@ def test_matches_batched_backward(kda):
         assert torch.equal(got, ref[n]), n
 
 
-def test_many_sequences_sampled(kda):
-    """A serving mix: 64 sequences of 1 .. 2048 tokens, 8 heads; sampled
-    sequences against the oracle, all outputs finite."""
+def test_many_sequences(kda):
+    """A serving mix: sequences of 1 .. 2048 tokens, 8 heads; every sequence
+    against the oracle, all outputs finite."""
     lengths = W.packed_lengths(24000, 300.0, 9, max_len=2048)
     x, cu = _packed(lengths, 8, 91, dst=False)
     print(f"case bwd varlen {len(lengths)} sequences, T_total={cu[-1]}", flush=True)
     gr = _run(kda, x)
-    for i in (0, len(lengths) // 2, int(np.argmax(lengths)), len(lengths) - 1):
+    for i in range(len(lengths)):
         _check_seq(x, gr, i, int(cu[i]), int(cu[i + 1]), False, True, "varlen many")
     for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
         assert torch.isfinite(gr[n].float()).all(), n

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import BF16_MAX, BF16_REL_L2, BF16_U, FP32_MAX, rms, to64
+from tests.parity import BF16_REL_L2, check_step, head_rel_l2, rms, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -21,17 +21,7 @@ def kda():
 
 
 def _check_step(o_g, o_r, dtype, what):
-    if dtype == torch.float32:
-        assert np.max(np.abs(o_g - o_r)) <= FP32_MAX * rms(o_r), what
-        return
-    N, H, _ = o_r.shape
-    for n in range(N):
-        for h in range(H):
-            den = np.linalg.norm(o_r[n, h])
-            if den > 0:
-                assert np.linalg.norm(o_g[n, h] - o_r[n, h]) / den <= BF16_REL_L2, what
-    # error beyond the bf16 output's own rounding (see tests/parity.py)
-    assert np.max(np.abs(o_g - o_r) - BF16_U * np.abs(o_r)) <= BF16_MAX * rms(o_r), what
+    return check_step(o_g, o_r, dtype, what)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -51,25 +41,27 @@ def test_steps_small(kda, dtype, d):
     assert err <= 1e-5 * rms(S_ref), err
 
 
-def test_decode_workload_256x32_sampled(kda):
-    """The decode workload at full size (256 sequences x 32 heads, 64 steps);
-    every step's o and the final state of sampled heads against the oracle."""
+def test_decode_workload_256x32(kda):
+    """The decode workload at full size (256 sequences x 32 heads, 64 steps):
+    every head's o at every step and every head's final state against the
+    oracle, which runs the same 64 steps on its own fp64 copy of the state."""
     cfg = W.DECODE_256x32
     S = W.decode_state(cfg, device="cuda")
     tok = W.decode_tokens(cfg, device="cuda")
-    picks = [(0, 0), (17, 5), (255, 31), (128, 16), (77, 3), (200, 30)]
-    S_ref = np.stack([to64(S[n, h]) for n, h in picks])[:, None]
+    S_ref = to64(S)
+    worst = {}
     for t in range(cfg.steps):
         args = [tok[n][t] for n in ("q", "k", "v", "g", "beta")]
         o = kda.recurrent_step(*args, S)
-        sel = [np.stack([to64(a[n, h]) for n, h in picks])[:, None] for a in args]
-        o_r, S_ref = oracle.recurrent_step(*sel, S_ref)
+        o_r, S_ref = oracle.recurrent_step(*[to64(a) for a in args], S_ref, inplace=True)
         torch.cuda.synchronize()
-        o_g = np.stack([to64(o[n, h]) for n, h in picks])[:, None]
-        _check_step(o_g, o_r, torch.bfloat16, f"step {t}")
-    S_g = np.stack([to64(S[n, h]) for n, h in picks])[:, None]
-    for i in range(len(picks)):
-        assert np.linalg.norm(S_g[i] - S_ref[i]) / np.linalg.norm(S_ref[i]) <= BF16_REL_L2
+        st = _check_step(to64(o), o_r, torch.bfloat16, f"step {t}")
+        for key, val in st.items():
+            worst[key] = max(worst.get(key, 0.0), val)
+    rel_s = head_rel_l2(to64(S), S_ref, (0, 1))
+    print(f"[parity] decode 256x32 x64: worst over steps " + " ".join(f"{k}={v:.3e}" for k, v in worst.items())
+          + f"; final state per-head rel L2 {rel_s:.3e}", flush=True)
+    assert rel_s <= BF16_REL_L2
     assert torch.isfinite(S).all()
 
 

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import check_prefill, oracle_prefill, pick, to64
+from tests.parity import check_prefill, oracle_prefill, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -142,37 +142,85 @@ def test_workload_fp32_B1_H2_T256(kda):
 
 
 def test_workload_bf16_B1_H16_T4096(kda):
-    """The H16 T4096 bf16 workload at full size, every head against the oracle."""
+    """The H16 T4096 bf16 workload at full size, every head against the
+    oracle; here the literal max-error bound holds as well (the correctly
+    rounded result meets it with room on this workload)."""
     inp = W.prefill_inputs(W.PREFILL_BF16_H16_T4K, device="cuda")
     o, S = _run(kda, inp)
     o_ref, S_ref = oracle_prefill(inp)
-    st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "bf16 B1 H16 T4096")
+    st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "bf16 B1 H16 T4096", literal=True)
     print(st)
 
 
-def test_workload_bf16_B8_H32_T8192_sampled(kda):
-    """Full size (the benchmark's launch), sampled heads against the oracle."""
+def test_workload_bf16_B8_H32_T8192(kda):
+    """Full size (the benchmark's launch), all 256 heads against the oracle."""
     cfg = W.PREFILL_BF16_B8_H32_T8K
     inp = W.prefill_inputs(cfg, device="cuda")
     o, S = _run(kda, inp)
-    heads = [(0, 0), (3, 17), (7, 31), (5, 8)]
-    o_ref, S_ref = oracle_prefill(inp, heads)
-    o_s, S_s = pick(o, S, heads)
-    st = check_prefill(o_s, S_s, o_ref, S_ref, torch.bfloat16, "bf16 B8 H32 T8192")
-    print(st)
     assert torch.isfinite(o.float()).all()
+    o_ref, S_ref = oracle_prefill(inp)
+    del inp
+    st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "bf16 B8 H32 T8192")
+    print(st)
 
 
-def test_workload_bf16_long_T131072_sampled(kda):
-    """Long-context slow-gate workload at full size: two heads vs the oracle."""
+def test_workload_bf16_long_T131072(kda):
+    """Long-context slow-gate workload at full size (the segmented schedule),
+    all 32 heads against the oracle."""
     cfg = W.PREFILL_BF16_LONG_T128K
     inp = W.prefill_inputs(cfg, device="cuda")
     o, S = _run(kda, inp)
-    heads = [(0, 5), (0, 30)]
-    o_ref, S_ref = oracle_prefill(inp, heads)
-    o_s, S_s = pick(o, S, heads)
-    st = check_prefill(o_s, S_s, o_ref, S_ref, torch.bfloat16, "bf16 T131072")
+    o_ref, S_ref = oracle_prefill(inp)
+    del inp
+    st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "bf16 T131072")
     print(st)
+
+
+@pytest.mark.parametrize("pipeline", ["1"], ids=["pipelined"])
+def test_short_sequences_seed_sweep(kda, pipeline, monkeypatch):
+    """T = 2 .. 8 with bf16 inputs over 32 seeds x 4 heads each: one output
+    vector is then carried by few tokens, so a rounding of the gated operands
+    is not averaged away."""
+    monkeypatch.setenv("KDA_FUSED_NSPLIT", "1")
+    monkeypatch.setenv("KDA_FUSED_PIPELINE", pipeline)
+    worst = {}
+    for T in range(2, 9):
+        for seed in range(32):
+            inp = _case(W.PREFILL_BF16_H16_T4K, 1, T, 4, seed=6000 + 100 * T + seed, s0=True)
+            o, S = _run(kda, inp)
+            o_ref, S_ref = oracle_prefill(inp)
+            st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"T{T} seed {seed} pipeline={pipeline}")
+            worst[T] = max(worst.get(T, 0.0), st["rel_l2_o"])
+    print("worst per-head rel L2 of o by T:", {t: f"{v:.2e}" for t, v in worst.items()})
+
+
+def _strong_decay_inputs(B, T, H, seed, burst=None):
+    """The H16 T4K recipe, then a quarter of the channels forget fast (log-gate
+    -1.2 .. -0.8 per step, 51 - 77 nats per 64-token chunk), everywhere or in
+    the token range `burst` only: such chunks leave the fp16 range of the
+    referenced gated operands and keep bf16 operands."""
+    inp = _case(W.PREFILL_BF16_H16_T4K, B, T, H, seed=seed, s0=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 17)
+    g = inp["g"].float()
+    fast = -(0.8 + 0.4 * torch.rand(g.shape, device="cuda", generator=gen))
+    sel = torch.zeros(g.shape, dtype=torch.bool, device="cuda")
+    t0, t1 = burst if burst is not None else (0, T)
+    sel[:, t0:t1, :, ::4] = True
+    inp["g"] = torch.where(sel, fast, g).to(torch.bfloat16).contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("burst", [None, (200, 330)], ids=["all", "burst"])
+def test_bf16_operand_fallback(kda, burst):
+    """Chunks whose gated operands would leave the fp16 range run with bf16
+    operands (every chunk, or only those overlapping a burst of fast
+    forgetting in the middle of the sequence); both kinds of chunk in one
+    sequence hand the state over correctly."""
+    inp = _strong_decay_inputs(2, 517, 3, 77, burst)
+    o, S = _run(kda, inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"strong decay {burst}")
 
 
 def test_empty_sequence_copies_state(kda):
@@ -246,3 +294,82 @@ def test_pins_on_gpu_fp32(kda):
     o_ref, S_ref = oracle.recurrent_fwd(Qf[None, :, None], Kf[None, :, None], Vf[None, :, None],
                                         np.zeros((1, T2, 1, d)), np.ones((1, T2, 1)), None)
     assert np.max(np.abs(to64(S)[0, 0] - S_ref[0, 0])) <= 1e-4 * scale
+
+
+def _f32(x):
+    return torch.tensor(np.asarray(x), dtype=torch.float32, device="cuda").contiguous()
+
+
+def test_pin_orthonormal_recall_and_flush_fp32(kda):
+    """beta = 1, g = 0 and orthonormal keys: the final state recalls every
+    written value, S_T^T k_i = v_i, and equals (I - K^T K) S0 + K^T V; after
+    d_k such keys S0 is erased completely, S_T = K^T V ("Hybrid Linear
+    Attention Architecture: Making LLM Training and Inference More Efficient"
+    §3.2: beta -> 1 overwrites, d steps flush)."""
+    d = 64
+    rng = np.random.default_rng(41)
+    S0 = rng.standard_normal((1, 1, d, d))
+    for T in (40, d):
+        Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        K = Qm[:, :T].T                                  # T orthonormal rows
+        V = rng.standard_normal((T, d))
+        Qr = rng.standard_normal((T, d))
+        k_, v_, q_, s0_ = _f32(K[None, :, None]), _f32(V[None, :, None]), _f32(Qr[None, :, None]), _f32(S0)
+        o, S = kda.chunk_fwd(q_, k_, v_, _f32(np.zeros((1, T, 1, d))), _f32(np.ones((1, T, 1))), s0_)
+        torch.cuda.synchronize()
+        Kf, Vf, S0f = to64(k_)[0, :, 0], to64(v_)[0, :, 0], to64(s0_)[0, 0]
+        St = to64(S)[0, 0]
+        scale = np.sqrt(np.mean(Vf ** 2))
+        # recall of every written value
+        assert np.max(np.abs(Kf @ St - Vf)) <= 1e-4 * scale, T
+        expect = (np.eye(d) - Kf.T @ Kf) @ S0f + Kf.T @ Vf
+        assert np.max(np.abs(St - expect)) <= 1e-4 * scale, T
+        if T == d:
+            assert np.max(np.abs(St - Kf.T @ Vf)) <= 1e-4 * scale
+
+
+def test_pin_decay_first_worked_example_fp32(kda):
+    """The worked one-token example of tests/golden (2 x 1 state, decay by
+    channel before the erase) embedded in d = 64 with zeros: o = 1/4 and
+    S_1 = (1/4, -1/4) ("Hybrid Linear Attention Architecture: Making LLM
+    Training and Inference More Efficient" §3.3)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "decay_first_example.json")) as f:
+        ex = json.load(f)
+    d = 64
+    pad = lambda x: np.concatenate([np.asarray(x, dtype=np.float64), np.zeros(d - len(x))])
+    inp = ex["inputs"]
+    S0 = np.zeros((1, 1, d, d))
+    S0[0, 0, :2, 0] = np.asarray(inp["S0"])[:, 0]
+    args = [_f32(pad(inp[n])[None, None, None]) for n in ("q", "k", "v", "g")]
+    o, S = kda.chunk_fwd(*args, _f32(np.full((1, 1, 1), inp["beta"])), _f32(S0))
+    torch.cuda.synchronize()
+    o_exp = pad(ex["expected"]["o"])
+    S_exp = np.zeros((d, d))
+    S_exp[:2, 0] = np.asarray(ex["expected"]["S1"])[:, 0]
+    S_exp[:, 1:] = 0.0
+    assert np.max(np.abs(to64(o)[0, 0, 0] - o_exp)) <= 1e-6
+    assert np.max(np.abs(to64(S)[0, 0] - S_exp)) <= 1e-6
+
+
+def test_pin_full_overwrite_fp32(kda):
+    """beta = 1, g = 0 and one unit key written again and again: each write
+    replaces the value stored under it, so with q = k every output is the
+    token's own value, o_t = S_t^T k = v_t, across chunk boundaries (same
+    page, §3.2: beta -> 1 is a complete overwrite)."""
+    d, T = 64, 150
+    rng = np.random.default_rng(43)
+    kv = rng.standard_normal(d)
+    kv /= np.linalg.norm(kv)
+    K = np.tile(kv, (T, 1))
+    V = rng.standard_normal((T, d))
+    S0 = rng.standard_normal((1, 1, d, d)) * 0.1
+    k_ = _f32(K[None, :, None])
+    o, S = kda.chunk_fwd(k_, k_, _f32(V[None, :, None]), _f32(np.zeros((1, T, 1, d))),
+                         _f32(np.ones((1, T, 1))), _f32(S0))
+    torch.cuda.synchronize()
+    Vf = to64(_f32(V))
+    scale = np.sqrt(np.mean(Vf ** 2))
+    assert np.max(np.abs(to64(o)[0, :, 0] - Vf)) <= 1e-4 * scale
+    assert np.max(np.abs(to64(k_)[0, -1, 0] @ to64(S)[0, 0] - Vf[-1])) <= 1e-4 * scale

@@ -103,15 +103,15 @@ def test_no_initial_state_and_no_final_state(kda):
     assert S2 is None and torch.equal(o, o2)
 
 
-def test_many_sequences_sampled(kda):
-    """96 sequences of 1 .. 2048 tokens (a serving batch mix), 8 heads;
-    sampled sequences against the oracle."""
+def test_many_sequences(kda):
+    """96 sequences of 1 .. 2048 tokens (a serving batch mix), 8 heads; every
+    sequence against the oracle."""
     rng = np.random.default_rng(5)
     lengths = np.minimum(rng.geometric(1 / 300.0, size=96), 2048).tolist()
     x, cu = _packed(lengths, 8, 47)
     print(f"case varlen 96 sequences, T_total={cu[-1]}", flush=True)
     o, S = _run(kda, x)
-    for i in (0, 17, 50, int(np.argmax(lengths)), 95):
+    for i in range(len(lengths)):
         a, b = int(cu[i]), int(cu[i + 1])
         o_ref, S_ref = _oracle_seq(x, a, b, i, False, True)
         check_prefill(to64(o[a:b])[None], to64(S[i])[None], o_ref, S_ref, torch.bfloat16, f"seq {i} T={b - a}")
