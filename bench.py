@@ -15,6 +15,11 @@ no delta rule, or both) on the same shapes; the default is KDA itself.
 --packed runs the prefill on the same 65 536 tokens x 32 heads cut into
 variable-length sequences (geometric lengths, mean 1024, seeded) through
 kda_varlen_schedule + kda_chunk_fwd_varlen.
+After the step loop (KDA only) the line also carries the backward on the
+B8 H32 T8192 workload, the two other bf16 prefill workloads timed alone
+(B1 H16 T4096 with S0, the cache evicted before each call; B1 H32 T131072
+with slow forgetting, segmented schedule) and a device-to-device copy as
+the achievable-bandwidth reference.
 """
 from __future__ import annotations
 
@@ -71,6 +76,10 @@ def parse():
                     help="skip the backward (kda_chunk_bwd) measurement")
     ap.add_argument("--packed", action="store_true",
                     help="prefill over variable-length packed sequences of the same tokens")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the H16 T4K and H32 T128K prefill workloads after the step loop")
+    ap.add_argument("--only", choices=["t4k", "t128k"], default=None,
+                    help="time only that prefill workload (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -122,9 +131,81 @@ def cpu_baseline(W, oracle, torch, scalar_gate=False, delta=True):
     oracle.recurrent_fwd(*args, nthreads=threads, scalar_gate=scalar_gate, delta=delta)
     dt = time.perf_counter() - t0
     tokens = cfg.B * cfg.T
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpus_usable": affinity, "omp_threads": threads,
             "sample": f"the whole prefill workload (B={cfg.B}, H={cfg.H}, T={cfg.T}, d=128) once, "
                       f"fp64 token recurrence, {dt:.1f} s wall"}
+
+
+def time_prefill_workload(kda, torch, cfg, iters, evict=None):
+    """kda_chunk_fwd on one of the prefill workloads at full size, with the
+    workspace its fastest schedule asks for: the median of `iters` calls, each
+    timed alone with events on the launch stream.  evict: a device buffer
+    written before every call (not timed), so that the inputs do not sit in
+    the 256 MB last-level cache from the previous call."""
+    import workloads as W
+    inp = W.prefill_inputs(cfg, device="cuda")
+    o = torch.empty_like(inp["v"])
+    S_T = torch.empty(cfg.B, cfg.H, D, D, dtype=torch.float32, device="cuda")
+    ws_bytes = kda.lib().kda_chunk_fwd_workspace_size(cfg.B, cfg.T, cfg.H, D, D, 1)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(2):
+        run()
+    ms = []
+    for _ in range(iters):
+        if evict is not None:
+            evict.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    BTH = cfg.B * cfg.T * cfg.H
+    nbytes = BTH * PREFILL_BYTES_PER_TOKHEAD + cfg.B * cfg.H * STATE_BYTES * (2 if cfg.s0_std is not None else 1)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    nseg = kda.lib().kda_chunk_fwd_workspace_size(cfg.B, cfg.T, cfg.H, D, D, 1) // max(cfg.B * cfg.H * 3 * STATE_BYTES, 1)
+    del inp, o, S_T, ws
+    return {"workload": f"kda_chunk_fwd B{cfg.B} H{cfg.H} T{cfg.T} d128 bf16"
+                        + (" (S0 ~ N(0, 0.02))" if cfg.s0_std is not None else " (S0=0)")
+                        + (f", log-gate mean mu={cfg.gate_mu:g}" if cfg.gate_mu != -3.0 else ""),
+            "schedule": f"segmented, {nseg} segments" if nseg >= 3 else "one pass",
+            "cache": "evicted before each call (1 GiB written)" if evict is not None else "warm",
+            "ms": med, "ms_all": ms, "value": cfg.B * cfg.T / (med * 1e-3), "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                         "mfma_frac_algorithmic": BTH * PREFILL_FLOPS_PER_TOKHEAD / (med * 1e-3) / 1e12
+                                                  / BF16_PEAK_TFLOPS}}
+
+
+def copy_reference(torch, stream, nbytes=1 << 30, iters=5):
+    """Bandwidth of a plain device-to-device copy (read + write bytes / time),
+    the achievable-bandwidth reference beside the 8 TB/s peak."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        y.copy_(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del x, y
+    return {"bytes_moved": 2 * nbytes, "ms": ms, "achieved_gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
 def measure_backward(kda, W, torch, pcfg, inp, args, stream):
@@ -185,6 +266,10 @@ def main():
         __graft_entry__.build()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.only is not None:
+        cfg = W.PREFILL_BF16_H16_T4K if args.only == "t4k" else W.PREFILL_BF16_LONG_T128K
+        print(json.dumps(time_prefill_workload(kda, torch, cfg, args.steps)), flush=True)
+        return
 
     scalar_gate, delta = VARIANTS[args.variant]
     flags = (1 if scalar_gate else 0) | (0 if delta else 2)
@@ -229,12 +314,15 @@ def main():
             kda.chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu, None, seq_order=order,
                                  o=o_flat, S_T=S_T, **vkw)
 
+    S_saved = S.clone()
+
     def decode():
         for t in range(dcfg.steps):
             kda.recurrent_step(*steps_tok[t], S, o=od, **vkw)
 
     for _ in range(args.warmup):
         prefill()
+        S.copy_(S_saved)
         decode()
     torch.cuda.synchronize()
 
@@ -246,6 +334,9 @@ def main():
     for e0, e1, e2 in ev:
         e0.record(stream)
         prefill()
+        # every timed decode run starts from the same state (the restore is
+        # inside the step's wall time but outside the decode events)
+        S.copy_(S_saved)
         e1.record(stream)
         decode()
         e2.record(stream)
@@ -302,9 +393,17 @@ def main():
                                 "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic(dk_name),
                                 "kernel": dk_name + " (bf16, 128 x 128)"}},
     }
+    line["decode"]["state_restored_before_each_timed_run"] = True
     if not args.no_backward and flags == 0 and not args.packed:
         line["backward"] = measure_backward(kda, W, torch, pcfg, inp, args, stream)
-    del inp, o, S, tok, steps_tok
+    del inp, o, S, S_saved, tok, steps_tok
+    if flags == 0 and not args.packed and not args.no_other_configs:
+        # the other two prefill workloads, each timed alone after the step loop
+        evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        line["prefill_B1_H16_T4096"] = time_prefill_workload(kda, torch, W.PREFILL_BF16_H16_T4K, 20, evict)
+        del evict
+        line["prefill_B1_H32_T131072"] = time_prefill_workload(kda, torch, W.PREFILL_BF16_LONG_T128K, 5)
+        line["copy_reference"] = copy_reference(torch, stream)
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline(W, oracle, torch, scalar_gate, delta)

@@ -62,5 +62,33 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer
+    on the host code only (the device code is built as usual), into
+    out_dir/libkda.so, for CPU checks of the host-side argument handling."""
+    cc = hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        flags = [f if f != "-O3" else "-O1" for f in _flags()]
+        r = subprocess.run([cc, *flags, "-g", *san, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized) failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    lib = os.path.join(out_dir, "libkda.so")
+    r = subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                        "-Xarch_host", "-fsanitize=undefined", *objs, "-o", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stdout}{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -23,15 +23,23 @@
 //   dq = e^b dQg + M_tt k_t,   dk = e^b dKg + e^-b (dKd + dKb~) + M_tt q_t
 // (M's diagonal and P's diagonal carry no gate factors and are kept exact).
 //
-// Three launches:
-//   1. the pipelined forward kernel in state mode: chunk-entry states S_[n];
-//   2. bwd_chain_kernel: per (sequence, head, half of the value columns) the
-//      adjoint recursion over the chunks in reverse, storing each chunk-end
-//      adjoint (the value columns are independent in it);
-//   3. bwd_grad_kernel: per (chunk, sequence, head), all gradients of the
-//      chunk from its entry state and chunk-end adjoint.
-// Matrix products: v_mfma_f32_16x16x16_bf16 on bf16 operands in LDS (fp32
-// accumulation); the unit-triangular inverse in fp32.
+// Four launches:
+//   1. the pipelined forward kernel in state mode (its own instantiation):
+//      the entry state S_[n] of every chunk, bf16, in the forward owners'
+//      fragment order;
+//   2. bwd_prep_kernel, per (chunk, sequence, head): A = (I + L)^-1 and P^T
+//      (bf16 64 x 64 each), the gated operands Kg, Kd, Qg (bf16 64 x 128),
+//      gamma and beta, into a per-chunk operand block;
+//   3. bwd_chain_kernel, per (sequence, head): the adjoint recursion over the
+//      chunks in reverse (dS fp32 in registers, eight value-column tiles per
+//      wave), storing each chunk-end adjoint (bf16, 16 x 16 tiles) and dS0;
+//   4. bwd_grad_kernel, per (chunk, sequence, head): all gradients of the
+//      chunk from its entry state, its chunk-end adjoint and its operand block.
+// Packed sequences use the same launches: chunk n of sequence b sits in slot
+// floor(cu[b] / 64) + b + n of the per-chunk arrays (head-minor).
+// Matrix products: v_mfma_f32_16x16x32_bf16 on bf16 operands from LDS (16-byte
+// fragments, or pairs of transpose reads), fp32 accumulation; the
+// unit-triangular inverse in fp32.
 #include <stdint.h>
 
 #include "kda_device.hpp"

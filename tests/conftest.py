@@ -13,11 +13,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running (full-size workloads)")
 
 
-def pytest_collection_modifyitems(config, items):
-    # Order GPU tests: cheap kernels first, full-size cases last.
-    pass
-
-
 @pytest.fixture(scope="session")
 def rng():
     import numpy as np
