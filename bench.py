@@ -326,25 +326,25 @@ def main():
         decode()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for e0, e1, e2 in ev:
+    for e0, e1, e2, e3 in ev:
         e0.record(stream)
         prefill()
-        # every timed decode run starts from the same state (the restore is
-        # inside the step's wall time but outside the decode events)
-        S.copy_(S_saved)
         e1.record(stream)
-        decode()
+        # every timed decode run starts from the same state (the restore is
+        # inside the step's wall time but outside both kernels' events)
+        S.copy_(S_saved)
         e2.record(stream)
+        decode()
+        e3.record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    pre_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
-    dec_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    pre_ms = [e0.elapsed_time(e1) for e0, e1, _, _ in ev]
+    dec_ms = [e2.elapsed_time(e3) for _, _, e2, e3 in ev]
     pre_avg = sum(pre_ms) / len(pre_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
 

@@ -1314,13 +1314,12 @@ constexpr int O_BETA = O_A + SZ_CC;
 constexpr int O_GAM = O_BETA + C * 4;    // two chunk parities
 constexpr int O_QK = O_GAM + 2 * DK * 4;  // q_t . k_t partial sums, per worker
 constexpr int NQK = 16;                   // q.k partial sums per token (worker lane groups)
-// Operand reference of each chunk (two chunk parities): the integer log2
-// exponent rho_c per key channel that the gated operands are taken relative
-// to, the largest of them per worker, and per worker whether its channels'
-// referenced operands fit fp16 (1) or the chunk keeps bf16 operands (0).
-constexpr int O_RHO = O_QK + NQK * C * 4;  // int [2][DK]
-constexpr int O_RMX = O_RHO + 2 * DK * 4;  // int [2][4]
-constexpr int O_FLG = O_RMX + 2 * 4 * 4;   // int [2][4]
+// Operand reference of each chunk: the integer log2 exponent rho_c per key
+// channel that the gated operands are taken relative to (three buffers, by
+// chunk index mod 3), and per worker two flag bits (two chunk parities):
+// bit 0 its channels' referenced operands fit fp16, bit 1 a reference moved.
+constexpr int O_RHO = O_QK + NQK * C * 4;  // int [3][DK]
+constexpr int O_FLG = O_RHO + 3 * DK * 4;  // int [2][4]
 constexpr int BYTES = O_FLG + 2 * 4 * 4;
 // solver scratch inside the -W region
 constexpr int S_LDT = 0;                           // fp32 [4][16][LDL]: L_II^T
@@ -1335,7 +1334,8 @@ struct Ptr {
   bf16 *Kt, *Kh, *Qt, *Wn;
   f16 *KtT, *KbT, *VT, *P, *A;
   float *beta, *gam, *qk;
-  int *rho, *rmx, *flg;
+  float* rho;
+  int* flg;
   float* LdT; f16 *Ln, *D, *Dt;
   __device__ __forceinline__ void set(unsigned char* b) {
     Kt = reinterpret_cast<bf16*>(b + O_KT);
@@ -1350,8 +1350,7 @@ struct Ptr {
     beta = reinterpret_cast<float*>(b + O_BETA);
     gam = reinterpret_cast<float*>(b + O_GAM);
     qk = reinterpret_cast<float*>(b + O_QK);
-    rho = reinterpret_cast<int*>(b + O_RHO);
-    rmx = reinterpret_cast<int*>(b + O_RMX);
+    rho = reinterpret_cast<float*>(b + O_RHO);
     flg = reinterpret_cast<int*>(b + O_FLG);
     LdT = reinterpret_cast<float*>(b + O_WN + S_LDT);
     Ln = reinterpret_cast<f16*>(b + O_WN + S_LN);
@@ -1443,16 +1442,19 @@ __device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], fl
 // of value column col0 + vcol(nt, i).  Each wave store writes one whole
 // block (512 contiguous bytes), and the 16 key rows 16 rt .. + 15 of one
 // value column are 32 contiguous bytes.
-__device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], bf16* out, int col0, int lane) {
+// (S is referenced, Diag(2^rho) S: each row is divided by 2^rho first.)
+__device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], const float* rho, bf16* out, int col0,
+                                              int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const int o = col0 >> 5;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt) {
+      const floatx4 e = *reinterpret_cast<const floatx4*>(rho + 16 * rt + 4 * g4);
       bf16x4 x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = (bf16)S[nt][rt][j];
+      for (int j = 0; j < 4; ++j) x[j] = (bf16)__builtin_amdgcn_ldexpf(S[nt][rt][j], -(int)e[j]);
       *reinterpret_cast<bf16x4*>(out + (8 * (2 * o + nt) + rt) * 256 + 16 * l16 + 4 * g4) = x;
     }
 }
@@ -1579,153 +1581,176 @@ __device__ __forceinline__ void fetch_v(Vec16 (&v)[4], const PrefillArgs& a, int
 struct Gates {
   float b[4][8];
   float gm[8];
-  int rho[8];   // reference exponent of each of the lane's channels
+  float bc[8];   // b_C of each channel (unreferenced)
+  float dev;     // largest distance of a referenced range from 0 (lane's channels)
 };
 
-// lane 7 of the caller's 16-lane row (ds_swizzle bit mode: and 0x10, or 0x07)
-__device__ __forceinline__ float row_lane7(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x0F0));
+// lane 0 of the caller's 16-lane row (ds_swizzle bit mode: and 0x10)
+__device__ __forceinline__ float row_first(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x010));
 }
 
 // Operand precision of a chunk.  The products Qg Kd^T (P), Kg Kd^T (L) and
-// Qg S only need the gate ratios 2^(b_t - b_j) (and, for Qg S, a row scaling
-// of S), so they may use Qg' = q 2^(b - rho), Kg' = k 2^(b - rho),
-// Kd' = k 2^(rho - b) and S' = Diag(2^rho) S for any per-channel reference
-// rho.  With rho the (rounded) log2 cumulative gate at the middle of the
-// chunk the referenced operands stay within 2^+-12 of the inputs' scale for
-// half-chunk decays of up to 12 bits (8.3 nats), where fp16 carries them with
-// 3 more mantissa bits than bf16 at the same MFMA rate; the rounding of these
-// gated operands is what dominates the output error with bf16 operands.  A
-// chunk whose referenced operands could leave that range keeps bf16 operands
-// and rho = 0 (the factorisation needs only the bf16 exponent range).
-//
-// Reference of the lane's channels (the cumulative gate of token 31) and
-// whether this worker's referenced operands of the chunk in r / gt fit fp16:
-// every |x| 2^(b - rho) and |k| 2^(rho - b) below 2^15 and the referenced
-// exponents within 12 bits.  |q|, |k| are bounded through the OR of their
-// bf16 bit patterns (the exponent field of the OR is at least every
-// element's).  Wave-uniform.
-__device__ __forceinline__ bool worker_range(const WRegs& r, Gates& gt) {
-  float u = -1e30f, dn = -1e30f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float rf = __builtin_rintf(row_lane7(gt.b[3][e]));
-    gt.rho[e] = (int)rf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = gt.b[i][e] - rf;
-      u = fmaxf(u, x);
-      dn = fmaxf(dn, -x);
-    }
-  }
-  uint32_t orb = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) orb |= r.q[i].w[k] | r.k[i].w[k];
-  const int eo = (int)max((orb >> 23) & 0xffu, (orb >> 7) & 0xffu);   // exponent fields of both halves
-  const float ext = fmaxf(u, dn);
-  const bool ok = ext <= 12.f && (float)(eo - 126) + ext <= 15.f;
-  return __builtin_amdgcn_ballot_w64(!ok) == 0;
-}
+// Qg S only need the gate ratios 2^(b_t - b_j) (and, for Qg S, the state
+// scaled by rows), so they use Qg' = q 2^(b - rho), Kg' = k 2^(b - rho),
+// Kd' = k 2^(rho - b) and S' = Diag(2^rho) S for a per-channel reference
+// exponent rho.  While every referenced exponent b - rho of a chunk lies
+// within +-kRefBits, fp16 carries these operands with 3 more mantissa bits
+// than bf16 at the same MFMA rate (the rounding of these gated operands is
+// what dominates the output error with bf16 operands); a chunk beyond that
+// (a channel decaying by more than 2 kRefBits bits inside one chunk, or a
+// positive log-gate) keeps bf16 operands, for which any reference fits.
+// The reference of a channel is sticky: it moves (to the middle of the
+// chunk's range) only when a chunk leaves +-kRefBits around it, so the
+// owners, which hold S' = Diag(2^rho) S instead of S, rarely rescale.
+constexpr float kRefBits = 8.f;
 
-// Commits the operand reference of the scanned chunk once every worker's
-// range check is in (fp16: the reference of the range check, else 0): the
-// gates become b - rho, gm becomes 2^(b_C - rho) (so that Kb = k 2^(b_C - b)
-// = Kd' gm), and the un-referenced chunk decay 2^b_C, the reference and the
-// worker's largest reference go to LDS for the owners (parity par).
-__device__ __forceinline__ void ref_commit(const Ptr& p, Gates& gt, bool f16m, int w, int lane, int par) {
-  const int j = lane >> 4, m = lane & 15;
-  const int c0 = 32 * w + 8 * j;
-  int rmax = -(1 << 20);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int rr = f16m ? gt.rho[e] : 0;
-    gt.rho[e] = rr;
-    rmax = max(rmax, rr);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gt.b[i][e] -= (float)rr;
-  }
-  if (m == 0) {
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
-    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
-    typedef int intx4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<intx4*>(p.rho + par * DK + c0) = intx4{gt.rho[0], gt.rho[1], gt.rho[2], gt.rho[3]};
-    *reinterpret_cast<intx4*>(p.rho + par * DK + c0 + 4) = intx4{gt.rho[4], gt.rho[5], gt.rho[6], gt.rho[7]};
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gt.gm[e] = __builtin_amdgcn_ldexpf(gt.gm[e], -gt.rho[e]);
-  // largest reference of the worker's channels (wave maximum)
-#pragma unroll
-  for (int st = 1; st < 64; st *= 2) rmax = max(rmax, __shfl_xor(rmax, st));
-  if (lane == 0) p.rmx[par * 4 + w] = rmax;
-}
-
-// Combined fp16 decision of the four workers for the chunk of parity par.
-__device__ __forceinline__ bool chunk_f16(const Ptr& p, int par) {
+// Combined flags of the four workers for the chunk of parity par: bit 0 all
+// of them fit fp16, bit 1 a reference moved.  Wave-uniform.
+__device__ __forceinline__ int chunk_flags(const Ptr& p, int par) {
   typedef int intx4 __attribute__((ext_vector_type(4)));
   const intx4 f = *reinterpret_cast<const intx4*>(p.flg + par * 4);
-  return __builtin_amdgcn_readfirstlane(f[0] & f[1] & f[2] & f[3]) != 0;
+  const int all = f[0] & f[1] & f[2] & f[3], any = f[0] | f[1] | f[2] | f[3];
+  return __builtin_amdgcn_readfirstlane((all & 1) | (any & 2));
 }
 
-// Prefix sums of the gates in r.g; r.g is then reloaded with the gates of the
-// chunk that nx addresses (the next scan's input).  With a scalar gate the
-// one sum per token is formed once and copied to all eight channels.
+// Largest value of a non-negative x over the wavefront (DPP row maxima, then
+// the four row results), wave-uniform.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true)));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Prefix sums of the gates in r.g, log2-scaled and taken relative to the
+// reference rho of each of the lane's channels; r.g is then reloaded with the
+// gates of the chunk that nx addresses (the next scan's input).  With g <= 0
+// the sums fall from b_1 <= 0 to b_C, so the referenced ones lie in
+// [b_C - rho, -rho]; gt.bc keeps b_C and gt.dev the largest distance of that
+// range from 0 over the lane's channels (ref_commit acts on it).  With a
+// scalar gate the one sum per token is formed once and copied to all eight
+// channels (whose references then stay equal).
 template <int V>
-__device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc<V>& nx) {
-  if constexpr ((V & kVarScalarGate) != 0) {
-    float x[4];
+__device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const float (&rho)[8], const QkgSrc<V>& nx) {
+  constexpr int NE = (V & kVarScalarGate) != 0 ? 1 : 8;   // distinct channels
+  float x[4][NE];
+  if constexpr (NE == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = bf_lo(r.gs[i]) * kLog2e;
-    nx.load_g(r);
+    for (int i = 0; i < 4; ++i) x[i][0] = bf_lo(r.gs[i]) * kLog2e;
+  } else {
 #pragma unroll
-    for (int i = 1; i < 4; ++i) x[i] += x[i - 1];
-    const float tot = x[3];
-    float s = add_row_shr<1>(tot);
-    s = add_row_shr<2>(s);
-    s = add_row_shr<4>(s);
-    s = add_row_shr<8>(s);
-    const float ex = s - tot, gm = exp2_hw(row_last(s));
+    for (int i = 0; i < 4; ++i) {
+      unpack8(r.g[i], x[i]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gt.b[i][e] = x[i] + ex;
-      gt.gm[e] = gm;
+      for (int e = 0; e < 8; ++e) x[i][e] *= kLog2e;
     }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    unpack8(r.g[i], gt.b[i]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gt.b[i][e] *= kLog2e;
   }
   nx.load_g(r);
 #pragma unroll
   for (int i = 1; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gt.b[i][e] += gt.b[i - 1][e];
+    for (int e = 0; e < NE; ++e) x[i][e] += x[i - 1][e];
+  float dev = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float tot = gt.b[3][e];
+  for (int e = 0; e < NE; ++e) {
+    const float tot = x[3][e];
     float s = add_row_shr<1>(tot);
     s = add_row_shr<2>(s);
     s = add_row_shr<4>(s);
     s = add_row_shr<8>(s);
-    const float ex = s - tot;
+    const float off = s - tot - rho[e];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gt.b[i][e] += ex;
-    gt.gm[e] = exp2_hw(row_last(s));
+    for (int i = 0; i < 4; ++i) gt.b[i][e] = x[i][e] + off;
+    const float bC = row_last(s);
+    gt.gm[e] = exp2_hw(bC);
+    gt.bc[e] = bC;
+    dev = fmaxf(dev, fmaxf(-rho[e], rho[e] - bC));
+  }
+  gt.dev = dev;
+  if constexpr (NE == 1) {
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt.b[i][e] = gt.b[i][0];
+      gt.gm[e] = gt.gm[0];
+      gt.bc[e] = gt.bc[0];
+    }
+  }
+}
+
+// Commits the reference of the chunk scanned into gt (once per chunk, off the
+// scan's critical path): (rarely) a channel whose referenced range leaves
+// +-kRefBits moves its reference to rint(b_C / 2), the middle of the chunk's
+// range, shifting rho and the sums in place; then the worker's flag bits for
+// the chunk (parity par: bit 0 its channels fit fp16, bit 1 a reference
+// moved) and its references (buffer buf) go to LDS.  Wave-uniform branches.
+__device__ __forceinline__ void ref_commit(const Ptr& p, Gates& gt, float (&rho)[8], int w, int lane, int par,
+                                           int buf) {
+  int flags = 1;
+  if (__builtin_amdgcn_ballot_w64(gt.dev > kRefBits) != 0) {
+    bool moved = false, over = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dv = fmaxf(-rho[e], rho[e] - gt.bc[e]);
+      const float d = dv > kRefBits ? __builtin_rintf(0.5f * gt.bc[e]) - rho[e] : 0.f;
+      rho[e] += d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt.b[i][e] -= d;
+      moved |= d != 0.f;
+      over |= fmaxf(-rho[e], rho[e] - gt.bc[e]) > kRefBits;
+    }
+    flags = (__builtin_amdgcn_ballot_w64(over) == 0 ? 1 : 0) | (__builtin_amdgcn_ballot_w64(moved) != 0 ? 2 : 0);
+  }
+  if (lane == 0) p.flg[par * 4 + w] = flags;
+  if ((lane & 15) == 0) {
+    const int c0 = 32 * w + 8 * (lane >> 4);
+    *reinterpret_cast<floatx4*>(p.rho + buf * DK + c0) = floatx4{rho[0], rho[1], rho[2], rho[3]};
+    *reinterpret_cast<floatx4*>(p.rho + buf * DK + c0 + 4) = floatx4{rho[4], rho[5], rho[6], rho[7]};
+  }
+}
+
+// A chunk that keeps bf16 operands drops its reference (rho = 0: the plain
+// gated operands, as every bf16 product and the fp16 Kg^T, Kb^T of such a
+// chunk need): the sums go back to b, and if a reference of this worker was
+// nonzero its flag word for the chunk (parity par) gets the "moved" bit, so
+// that the owners move their state back.  Called once the four workers'
+// operand choice for the chunk is known.
+__device__ __forceinline__ void worker_unref(const Ptr& p, Gates& gt, float (&rho)[8], int w, int lane, int par) {
+  bool nz = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    nz |= rho[e] != 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gt.b[i][e] += rho[e];
+    rho[e] = 0.f;
+  }
+  if (__builtin_amdgcn_ballot_w64(nz) != 0 && lane == 0) p.flg[par * 4 + w] |= 2;
+}
+
+// The lane's channel references to LDS (buffer buf) for the owners.
+__device__ __forceinline__ void worker_rho(const Ptr& p, const float (&rho)[8], int w, int lane, int buf) {
+  if ((lane & 15) == 0) {
+    const int c0 = 32 * w + 8 * (lane >> 4);
+    *reinterpret_cast<floatx4*>(p.rho + buf * DK + c0) = floatx4{rho[0], rho[1], rho[2], rho[3]};
+    *reinterpret_cast<floatx4*>(p.rho + buf * DK + c0 + 4) = floatx4{rho[4], rho[5], rho[6], rho[7]};
   }
 }
 
 // Phase 1 of a worker: from the referenced prefix sums b' = b - rho,
 // Kt = 2^b' k, Kh = 2^-b' k, Qt = 2^b' q (row-major; fp16 or bf16 as the
-// chunk's operand choice f16m says) and the q.k partial sums; Kt^T and
-// Kb = gm' 2^-b' k = 2^(b_C - b) k stay in registers as fp16 (kt_t[e], kb[e]
-// = tokens 4m..4m+3 of channel e) and are stored transposed in phase 2a.
-// (Kt^T is referenced too: W = A' Kt picks up the factor 2^rho per channel
-// when it is stored.)
+// chunk's operand choice f16m says), the chunk decay gam = 2^b_C of its
+// channels and the q.k partial sums; Kt^T and Kb' = gam Kh = 2^rho Kb stay in
+// registers as fp16 (kt_t[e], kb[e] = tokens 4m..4m+3 of channel e) and are
+// stored transposed in phase 2a.  (Against the owners' referenced state
+// S' = Diag(2^rho) S these referenced operands give the same products as the
+// plain ones: W' S' = W S with W' = A' Kt, and Kb'^T Delta = Diag(2^rho)
+// Kb^T Delta.)
 //
 // The next-but-one chunk's k and q are loaded into the same registers row by
 // row as each row is consumed, so the loads spread over this phase's
@@ -1736,11 +1761,15 @@ __device__ __forceinline__ void worker_scan(WRegs& r, Gates& gt, const QkgSrc<V>
 // Without the delta rule Kt (row-major and transposed) has no reader and is
 // not formed.
 template <int V>
-__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, bool f16m,
-                                             f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc<V>& nx) {
+__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
+                                             bool f16m, f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc<V>& nx) {
   constexpr bool ND = (V & kVarNoDelta) != 0;
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
+  if (m == 0) {
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0) = floatx4{gt.gm[0], gt.gm[1], gt.gm[2], gt.gm[3]};
+    *reinterpret_cast<floatx4*>(p.gam + par * DK + c0 + 4) = floatx4{gt.gm[4], gt.gm[5], gt.gm[6], gt.gm[7]};
+  }
   // rows 4m + i: rmo(4m + i, e) = 4m LDK + i LDK + (e ^ ((m & 7) << 3)) for i < 4
   const int wb0 = 4 * m * LDK + (slot32(c0) ^ ((m & 7) << 3));
   const int wb1 = 4 * m * LDK + (slot32(c0 + 4) ^ ((m & 7) << 3));
@@ -2087,15 +2116,11 @@ __device__ __forceinline__ void solver_offdiag_col(const Ptr& p, int lane) {
 // Phase 3, workers: W^T tile rows 32w.. of W = A' Kt (fp16 products from Kt^T
 // and A'), stored as -W into the row-major bf16 array.  A' is lower
 // triangular, so token blocks 0 and 1 need only the first 32-token slab.
-// Kt^T holds the referenced k 2^(b - rho), so each channel row of W^T takes
-// the exact factor 2^rho (rho: the chunk's reference exponents).
-__device__ __forceinline__ void worker_w(const Ptr& p, const int* rho, int w, int lane) {
-  typedef int intx4 __attribute__((ext_vector_type(4)));
+// (Kt^T holds the referenced k 2^(b - rho): this is W' = W Diag(2^-rho), the
+// matrix the owners' referenced state needs.)
+__device__ __forceinline__ void worker_w(const Ptr& p, int w, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const int fl = frag_lane(lane);
-  intx4 rc[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) rc[ct] = *reinterpret_cast<const intx4*>(rho + 32 * w + 16 * ct + 4 * g4);
   MH::F32 ka[2][2], ab[4][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -2114,7 +2139,7 @@ __device__ __forceinline__ void worker_w(const Ptr& p, const int* rho, int w, in
       if (tb >= 2) acc = MH::mma32(ka[ct][1], ab[tb][1], acc);
       bf16x4 o;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-__builtin_amdgcn_ldexpf(acc[jj], rc[ct][jj]));
+      for (int jj = 0; jj < 4; ++jj) o[jj] = (bf16)(-acc[jj]);
       // = rmo(16 tb + l16, slot32(32 w + 16 ct + 4 g4))
       *reinterpret_cast<bf16x4*>(p.Wn + fl + 16 * tb * LDK + 32 * (w ^ (tb & 1)) + 4 * ct) = o;
     }
@@ -2191,15 +2216,12 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
 
 // Phase 2b, owners, for a chunk with fp16 operands: Dx[nt][I] = Qt'[rows
 // 16I..] @ S', the tiles held transposed as rows_times_state_b<true> holds
-// them, with Qt' = 2^(b - rho) q (fp16, LDS) and S' = 2^-kx Diag(2^rho) S
-// formed from the registers as fp16 fragments (rho: the chunk's reference
-// exponent of each key row; kx >= 0 keeps S' in the fp16 range and is put
-// back on Dx by the caller).
-__device__ __forceinline__ void qt_times_state_h(const bf16* Qt, const int* rho, int kx,
-                                                 const floatx4 (&S)[2][DK / 16], floatx4 (&Dx)[2][4], int lane) {
-  typedef int intx4 __attribute__((ext_vector_type(4)));
+// them, with Qt' (fp16, LDS) and the owner's referenced state S' as fp16
+// fragments, scaled by 2^-kx (kx >= 0 keeps them in the fp16 range; the
+// caller puts 2^kx back on Dx).
+__device__ __forceinline__ void qt_times_state_h(const bf16* Qt, int kx, const floatx4 (&S)[2][DK / 16],
+                                                 floatx4 (&Dx)[2][4], int lane) {
   const int fl = frag_lane(lane);
-  const int g4 = lane >> 4;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     MH::F32 af[2][4];
@@ -2207,24 +2229,25 @@ __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, const int* rho,
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int I = 0; I < 4; ++I) af[k2][I] = ldc_g<f16>(Qt + fl + frag_off(I, 2 * hf + k2));
-    intx4 rr[2][2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        rr[k2][u] = *reinterpret_cast<const intx4*>(rho + 32 * (2 * hf + k2) + 16 * u + 4 * g4) - kx;
     KDA_READS_FIRST();
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int ks = 2 * hf + k2;
       MH::F32 sf[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        if (kx == 0) {
+          sf[nt] = MH::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+        } else {
+          floatx4 lo, hi;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          sf[nt][jj] = (f16)__builtin_amdgcn_ldexpf(S[nt][2 * ks][jj], rr[k2][0][jj]);
-          sf[nt][4 + jj] = (f16)__builtin_amdgcn_ldexpf(S[nt][2 * ks + 1][jj], rr[k2][1][jj]);
+          for (int jj = 0; jj < 4; ++jj) {
+            lo[jj] = __builtin_amdgcn_ldexpf(S[nt][2 * ks][jj], -kx);
+            hi[jj] = __builtin_amdgcn_ldexpf(S[nt][2 * ks + 1][jj], -kx);
+          }
+          sf[nt] = MH::frag32(lo, hi);
         }
+      }
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -2233,21 +2256,42 @@ __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, const int* rho,
   }
 }
 
-// Scale exponent kx >= 0 that keeps an owner's S' = Diag(2^rho) S within
-// 2^15 (rmx: the chunk's largest reference exponent).  Wave-uniform.
-__device__ __forceinline__ int state_f16_shift(const floatx4 (&S)[2][DK / 16], int rmx) {
-  float mx = 0.f;
+// Scale exponent kx >= 0 that keeps an owner's referenced state below 2^15
+// in magnitude.  Wave-uniform.
+__device__ __forceinline__ int state_f16_shift(const floatx4 (&S)[2][DK / 16]) {
+  // a tree of three-input maxima over the lane's 64 values
+  float m[16];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-    for (int rt = 0; rt < DK / 16; ++rt)
+    for (int h = 0; h < 2; ++h)
+      m[2 * rt + h] = fmaxf(fmaxf(fabsf(S[0][rt][2 * h]), fabsf(S[0][rt][2 * h + 1])),
+                            fmaxf(fabsf(S[1][rt][2 * h]), fabsf(S[1][rt][2 * h + 1])));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, fabsf(S[nt][rt][jj]));
+  for (int st = 8; st > 0; st >>= 1)
 #pragma unroll
-  for (int st = 1; st < 64; st *= 2) mx = fmaxf(mx, __shfl_xor(mx, st));
-  // mx < 2^ex; S' < 2^(ex + rmx - kx) <= 2^15
-  const int ex = __builtin_amdgcn_frexp_expf(mx);
-  return __builtin_amdgcn_readfirstlane(max(0, ex + rmx - 15));
+    for (int i = 0; i < st; ++i) m[i] = fmaxf(m[i], m[i + st]);
+  // |S'| < 2^ex; S' 2^-kx < 2^15
+  const int ex = __builtin_amdgcn_frexp_expf(wave_max_nonneg(m[0]));
+  return max(0, ex - 15);
+}
+
+// Rows of an owner's state tiles times 2^e_row, e_row = rho_a[row] -
+// rho_b[row] (moving the state's reference; sign -1 with rho_b NULL divides
+// by 2^rho_a, i.e. back to the plain state).
+__device__ __forceinline__ void state_rescale(floatx4 (&S)[2][DK / 16], const float* rho_a, const float* rho_b,
+                                              int lane) {
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < DK / 16; ++rt) {
+    floatx4 e = *reinterpret_cast<const floatx4*>(rho_a + 16 * rt + 4 * g4);
+    if (rho_b) e -= *reinterpret_cast<const floatx4*>(rho_b + 16 * rt + 4 * g4);
+    else e = -e;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) S[nt][rt][jj] = __builtin_amdgcn_ldexpf(S[nt][rt][jj], (int)e[jj]);
+  }
 }
 
 // Phase 1, owners: O += P Delta, S <- Diag(gam) S + Kb^T Delta.
@@ -2467,6 +2511,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int blk = idx >> 10, r = (idx >> 6) & 15, c = idx & 63;
     p.P[(32 * blk + r) * LDT + c] = (f16)0.f;
   }
+  // the reference before the first chunk (buffer of chunk -1) is 0
+  if (tid < DK) p.rho[2 * DK + tid] = 0.f;
 
   if (wave < 4) {
     // ---------------------------------------------------------------- owners
@@ -2477,7 +2523,10 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
-    __syncthreads();   // the workers' range checks of the first chunk
+    int kx = ST ? 0 : state_f16_shift(S);   // fp16 scale exponent of the state's read-out
+    __syncthreads();   // the workers' operand choice of the first chunk
+    // S holds the state referenced to the current chunk, Diag(2^rho) S; the
+    // reference before the first chunk is 0
     // (the owners keep their per-lane addresses in registers for the whole
     // loop; the workers, short of registers, recompute them in each phase)
     for (int n = -1; n < nchunks; ++n) {
@@ -2501,14 +2550,18 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           owner_store(O, ro, a.H * DV, col0, lane);
         }
         if constexpr (ST)
-          store_state_t(S, reinterpret_cast<bf16*>(a.states) + (st0 + (int64_t)(c0 + n) * stn) * DK * DV, col0, lane);
+          store_state_t(S, p.rho + ((n + 3) % 3) * DK,
+                        reinterpret_cast<bf16*>(a.states) + (st0 + (int64_t)(c0 + n) * stn) * DK * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
+      // range of the state for the fp16 read-out of chunk n+1 (phase 2b),
+      // taken here where the owners are not on the critical path
+      if (!ST && outp) kx = state_f16_shift(S);
       // V^T of chunk n+1 (U is formed in phase 3)
       if (nxt && !vzero) owner_vt(p, vr, o, lane);
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
-      const bool f16m = chunk_f16(p, (n + 1) & 1);
+      const bool f16m = (chunk_flags(p, (n + 1) & 1) & 1) != 0;
       if (!ND && nxt) {
         if (f16m)
           solver_block<f16>(p, o, lane);
@@ -2537,13 +2590,15 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int fl = nxt ? chunk_flags(p, (n + 1) & 1) : 0;
+      // the state moves to the reference of chunk n+1 where it changed
+      if (fl & 2) {
+        state_rescale(S, p.rho + ((n + 1) % 3) * DK, p.rho + ((n + 3) % 3) * DK, lane);
+        if (!ST && outp) kx = state_f16_shift(S);
+      }
       if (nxt && outp) {
-        const int par = (n + 1) & 1;
-        if (chunk_f16(p, par)) {
-          typedef int intx4 __attribute__((ext_vector_type(4)));
-          const intx4 rm = *reinterpret_cast<const intx4*>(p.rmx + par * 4);
-          const int kx = state_f16_shift(S, max(max(rm[0], rm[1]), max(rm[2], rm[3])));
-          qt_times_state_h(p.Qt, p.rho + par * DK, kx, S, O, lane);
+        if (fl & 1) {
+          qt_times_state_h(p.Qt, kx, S, O, lane);
           if (kx != 0) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
@@ -2569,27 +2624,43 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           owner_u(p, col0, U, lane);
       }
     }
-    if (sTp) store_state_v(S, sTp, col0, lane);
+    if (sTp) {
+      // back from the last chunk's reference
+      state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
+      store_state_v(S, sTp, col0, lane);
+    }
   } else {
     // --------------------------------------------------------------- workers
     const int w = wave - 4;
     WRegs r;
     Gates gt;
+    float rho[8];   // reference exponents of the lane's channels
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rho[e] = 0.f;
     fetch_qkg<V>(r, a, bb, h, c0, w, lane);   // zeros when the sequence is empty
-    worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + 1, w, lane));
-    {
-      const bool ok = worker_range(r, gt);
-      if (lane == 0) p.flg[w] = ok;
-    }
+    worker_scan<V>(r, gt, rho, QkgSrc<V>(a, bb, h, c0 + 1, w, lane));
+    ref_commit(p, gt, rho, w, lane, 0, 0);
     __syncthreads();
-    // operand choice of the chunk being prepared (f16m) and of the next
-    bool f16m = chunk_f16(p, 0);
-    ref_commit(p, gt, f16m, w, lane, 0);
+    // operand choice of the chunk being prepared
+    bool f16m = (chunk_flags(p, 0) & 1) != 0;
+    if (!f16m) {
+      worker_unref(p, gt, rho, w, lane, 0);
+      worker_rho(p, rho, w, lane, 0);
+    }
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
       p.sync(smem_raw);
       KDA_FRESH_LANE();
+      if (n >= 0) {
+        // the operand choice of chunk n+1 (its flags were committed in the
+        // previous slot's phase 3); a bf16 chunk drops its reference
+        f16m = (chunk_flags(p, (n + 1) & 1) & 1) != 0;
+        if (!f16m) {
+          worker_unref(p, gt, rho, w, lane, (n + 1) & 1);
+          worker_rho(p, rho, w, lane, (n + 1) % 3);
+        }
+      }
       // phase 1: gated operands of chunk n+1 with the k / q loads of chunk
       // n+2 interleaved.  Runs on every slot (past the last chunk on zeros,
       // into arrays nobody reads again), so the loads are never under a
@@ -2601,7 +2672,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
           r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
         }
-        worker_apply<V>(p, r, gt, w, lane, f16m, kb, kt_t, nx);
+        worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, f16m, kb, kt_t, nx);
       }
       p.sync(smem_raw);
       KDA_FRESH_LANE();
@@ -2645,17 +2716,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         else if (w == 3)
           solver_offdiag_col<2>(p, lane);
       }
-      worker_scan<V>(r, gt, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
-      {
-        const bool ok = worker_range(r, gt);
-        if (lane == 0) p.flg[(n & 1) * 4 + w] = ok;
-      }
+      worker_scan<V>(r, gt, rho, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
       p.sync(smem_raw);
       KDA_FRESH_LANE();
-      // phase 3: W; the operand choice of chunk n+2 is in
-      if (!ND && nxt) worker_w(p, p.rho + ((n + 1) & 1) * DK, w, lane);
-      f16m = chunk_f16(p, n & 1);
-      ref_commit(p, gt, f16m, w, lane, n & 1);
+      // phase 3: W; the references and operand flags of chunk n+2
+      if (!ND && nxt) worker_w(p, w, lane);
+      ref_commit(p, gt, rho, w, lane, n & 1, (n + 2) % 3);
     }
   }
 }
