@@ -44,6 +44,7 @@ _SIGS = {
     "kda_chunk_fwd_staged": ([_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_workspace_size": ([_i] * 6, _sz),
     "kda_chunk_fwd_ex": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_noalloc": ([_vp] * 8 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
@@ -171,6 +172,21 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
         _check(L.kda_chunk_fwd_ex(*args, flags, *tail))
     else:
         _check((L.kda_chunk_fwd_staged if staged else L.kda_chunk_fwd)(*args, *tail))
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, S0=None, *, o, S_T=None, stream=None):
+    """Prefill through kda_chunk_fwd_noalloc: the library's own device scratch
+    holds the workspace, so nothing is allocated (o, and S_T if wanted, must
+    be passed in).  Returns (o, S_T)."""
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta)
+    _need(o, (B, T, H, dv), dt, "o")
+    if S0 is not None:
+        _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    if S_T is not None:
+        _need(S_T, (B, H, dk, dv), torch.float32, "S_T")
+    _check(lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                       _ptr(S_T), B, T, H, dk, dv, _dtype(q), _stream(stream)))
     return o, S_T
 
 

@@ -4,8 +4,16 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_launch.hpp"
+
+// Device scratch of kda_chunk_fwd_noalloc: the segmented schedule's workspace
+// in a file-scope array instead of caller memory.  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` only
+// names the symbol; its device address is taken per device below.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -121,6 +129,37 @@ int check_tokens(const void* q, const void* k, const void* v, const void* g, con
 
 bool valid_flags(int flags) { return (flags & ~(KDA_GATE_SCALAR | KDA_NO_DELTA)) == 0; }
 
+// Per-device address of `scratch`, looked up once per device with that device
+// current (hipGetSymbolAddress; no allocation).  nullptr and the HIP error on
+// failure.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // sizes and dtype for which the prefill variants exist (the pipelined kernel)
 bool variant_dims(int dk, int dv, int dt) { return dt == KDA_BF16 && dk == 128 && dv == 128; }
 
@@ -140,6 +179,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_HIP: return hipGetErrorString((hipError_t)g_last_hip);
     case KDA_ERR_ARG: return "invalid argument";
+    case KDA_ERR_SCRATCH: return "these sizes need more device scratch than kda_chunk_fwd_noalloc holds "
+                                 "(KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -190,6 +231,27 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
     a.ws = static_cast<float*>(workspace);
   }
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
+}
+
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
+                          void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  const size_t need = kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, dtype);
+  KDA_REQUIRE(need <= (size_t)KDA_NOALLOC_SCRATCH_BYTES, KDA_ERR_SCRATCH);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return kda_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype, ws, need, stream);
 }
 
 int kda_varlen_schedule(const int32_t* cu_seqlens, int N, int T_total, int32_t* seq_order, void* stream) {

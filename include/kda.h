@@ -41,9 +41,11 @@
  *     U - W S of each chunk and the terms it is formed from must stay below
  *     65504 in magnitude (q, k of unit scale and |v| up to a few thousand
  *     are far inside).  The gated q / k operands are fp16 relative to a
- *     per-channel reference exponent only where they fit (else bf16, chosen
- *     per chunk), and the state enters its product scaled into range, so
- *     neither limits the domain.  The decode step has no such limits.
+ *     per-channel reference exponent where every channel decays by at most
+ *     16 bits (11 nats) inside the chunk, else bf16 (chosen per chunk), and
+ *     the state enters its product scaled into range; for that choice g
+ *     must be <= 0 and |q|, |k| entries below 256 (unit-norm vectors are
+ *     far inside).  The decode step has no such limits.
  *     NaN/Inf inputs propagate; nothing is checked on the device.
  *
  * Return values: KDA_OK (0) or a negative kda_status.  No C++ exception
@@ -70,7 +72,9 @@ typedef enum {
   KDA_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned               */
   KDA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required        */
   KDA_ERR_HIP = -6,        /* a HIP launch / runtime call failed             */
-  KDA_ERR_ARG = -7         /* any other invalid argument (e.g. bad option)   */
+  KDA_ERR_ARG = -7,        /* any other invalid argument (e.g. bad option)   */
+  KDA_ERR_SCRATCH = -8     /* kda_chunk_fwd_noalloc: sizes need more scratch
+                              than KDA_NOALLOC_SCRATCH_BYTES                  */
 } kda_status;
 
 /*
@@ -105,6 +109,31 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
  * the current device (0 = none needed).  Environment: KDA_SEGMENTS = 0 turns
  * the segmented schedule off, n >= 3 asks for about n segments. */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same computation and schedule choice, with
+ * the segmented schedule's workspace taken from a device array inside the
+ * library instead of a caller buffer.  Arguments as kda_chunk_fwd without
+ * the workspace pair; inputs and outputs are still the caller's.
+ *   - The array holds KDA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the
+ *     library runs on, from that GPU's first call until the process ends.
+ *     Sizes whose schedule needs more (kda_chunk_fwd_workspace_size above
+ *     it, e.g. 128 heads of 131 072 tokens) return KDA_ERR_SCRATCH and
+ *     launch nothing.  The first call on a GPU looks the array up there
+ *     (hipGetSymbolAddress); no call allocates or frees memory.
+ *   - All calls on one GPU share the array, which keeps the last call's
+ *     contents; every call writes all of the scratch it reads, so nothing
+ *     needs clearing.  Calls that overlap in time on one GPU (different
+ *     streams or host threads) race on it and give undefined results:
+ *     serialise them (one stream, or events).
+ * Returns as kda_chunk_fwd, plus KDA_ERR_SCRATCH.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* S0, void* o, float* S_T,
+                          int B, int T, int H, int d_k, int d_v, int dtype, void* stream);
 
 /*
  * kda_recurrent_step -- one decode token for N independent sequences

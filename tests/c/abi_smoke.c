@@ -27,6 +27,8 @@ int main(void) {
                          NULL), KDA_ERR_NULL);
   CHECK(kda_chunk_fwd_ex(p, p, p, p, p, NULL, p, NULL, 1, 64, 1, 64, 64, KDA_BF16, KDA_NO_DELTA, NULL, 0, NULL),
         KDA_ERR_ARG);
+  CHECK(kda_chunk_fwd_noalloc(p, p, p, NULL, p, NULL, p, NULL, 1, 64, 1, 128, 128, KDA_BF16, NULL), KDA_ERR_NULL);
+  CHECK(kda_chunk_fwd_noalloc(p, p, p, p, p, NULL, p, NULL, 0, 64, 1, 128, 128, KDA_BF16, NULL), KDA_OK);
   CHECK(kda_recurrent_step(p, p, p, p, p, NULL, p, 4, 2, 128, 128, KDA_BF16, NULL), KDA_ERR_NULL);
   CHECK(kda_recurrent_step_ex(p, p, p, p, p, p, p, 4, 2, 128, 128, KDA_BF16, 8, NULL), KDA_ERR_ARG);
   CHECK(kda_chunk_fwd_varlen(p, p, p, p, p, NULL, p, NULL, NULL, NULL, 3, 100, 2, 128, 128, KDA_BF16, 0, NULL),

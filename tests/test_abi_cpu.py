@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert L.kda_version() == 10000
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert L.kda_status_string(code)
     assert L.kda_status_string(0) == b"ok"
 
@@ -68,6 +68,23 @@ def test_prefill_validation(L):
     assert _fwd(L, B=0) == 0                            # nothing to do: no launch
     assert _fwd(L, H=0) == 0
     assert L.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 1) == 0
+
+
+def test_noalloc_validation(L):
+    """kda_chunk_fwd_noalloc checks its arguments like kda_chunk_fwd before it
+    looks up its scratch or launches anything."""
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(q=16, B=1, dk=128, dv=128, dt=1, S0=None):
+        return L.kda_chunk_fwd_noalloc(p(q), p(16), p(16), p(16), p(16), p(S0), p(16), None, B, 64, 1, dk, dv, dt,
+                                       None)
+    assert call(q=None) == -1
+    assert call(dk=96, dv=96) == -2
+    assert call(dt=7) == -3
+    assert call(q=18) == -4
+    assert call(S0=20) == -4
+    assert call(B=0) == 0
+    assert b"scratch" in L.kda_status_string(-8)
 
 
 def test_staged_workspace(L):
