@@ -103,19 +103,22 @@ def source_digest(family: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def measured_traffic(kernel: str, family: str = None):
+    """HBM bytes per launch (or per call, for a record that sums several
+    launches) from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    family = "decode" if kernel.startswith("decode") else "prefill"
+    if family is None:
+        family = "decode" if kernel.startswith("decode") else "prefill"
     if not rec or rec.get("source_digest") != source_digest(family):
         return None
-    return rec.get("bytes_per_launch")
+    t = rec.get("bytes_per_launch", rec.get("bytes_per_call"))
+    return None if t is None else float(t)
 
 
 def cpu_baseline(W, oracle, torch, scalar_gate=False, delta=True):
@@ -185,6 +188,8 @@ def time_prefill_workload(kda, torch, cfg, iters, evict=None):
             "ms": med, "ms_all": ms, "value": cfg.B * cfg.T / (med * 1e-3), "unit": "tokens/s",
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                         "traffic": (measured_traffic(f"prefill_segmented[B{cfg.B} H{cfg.H} T{cfg.T}]")
+                                     if nseg >= 3 else None),
                          "mfma_frac_algorithmic": BTH * PREFILL_FLOPS_PER_TOKHEAD / (med * 1e-3) / 1e12
                                                   / BF16_PEAK_TFLOPS}}
 
@@ -238,7 +243,7 @@ def measure_backward(kda, W, torch, pcfg, inp, args, stream):
     return {"value": pcfg.B * pcfg.T / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
             "workload": "kda_chunk_bwd B8 H32 T8192 d128 bf16 (S0=0, dS_T=0)",
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("backward", "backward"),
                          "kernel": "the whole backward: state pass (fused_pipe_kernel<4>) + bwd_prep_kernel + bwd_chain_kernel + bwd_grad_kernel"}}
 
 
