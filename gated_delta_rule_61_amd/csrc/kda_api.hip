@@ -34,10 +34,21 @@ int check_chunk_dims(int B, int T, int H, int dk, int dv, int dt) {
   if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
   if (dt == KDA_BF16 && !((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return KDA_ERR_SHAPE;
-  if (dt == KDA_F32 && !(dk == 64 && dv == 64)) return KDA_ERR_SHAPE;
+  if (dt == KDA_F32 && !((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return KDA_ERR_SHAPE;
   // 32-bit byte offsets inside one chunk of one tensor, 64-bit elsewhere
   if ((int64_t)H * dk * 64 * 4 > INT32_MAX || (int64_t)H * dv * 64 * 4 > INT32_MAX) return KDA_ERR_SHAPE;
   return KDA_OK;
+}
+
+// fp32 at d = 128: the two-launch path (a workspace is required)
+bool f32_wide(int dk, int dt) { return dt == KDA_F32 && dk == 128; }
+
+// The staged schedule and its single steps: as check_chunk_dims, except fp32
+// at d = 128, whose operand tiles the staged kernels cannot hold.
+int check_staged_dims(int B, int T, int H, int dk, int dv, int dt) {
+  const int st = check_chunk_dims(B, T, H, dk, dv, dt);
+  if (st) return st;
+  return f32_wide(dk, dt) ? KDA_ERR_SHAPE : KDA_OK;
 }
 
 int check_step_dims(int N, int H, int dk, int dv, int dt) {
@@ -173,7 +184,7 @@ const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
-    case KDA_ERR_SHAPE: return "unsupported or negative size (supported: d_k = d_v in {64,128} for bf16, 64 for fp32)";
+    case KDA_ERR_SHAPE: return "unsupported or negative size (supported: d_k = d_v in {64,128}; the staged schedule: 64 for fp32)";
     case KDA_ERR_DTYPE: return "unsupported dtype";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -189,6 +200,7 @@ int kda_last_hip_error(void) { return g_last_hip; }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
+  if (f32_wide(d_k, dtype)) return (int64_t)B * H * T == 0 ? 0 : kda::prefill_f32_workspace(B * H, T);
   return kda::prefill_segment_workspace(B * H, segment_count(B, T, H, d_k, d_v, dtype));
 }
 
@@ -218,6 +230,16 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
     if (st) return st;
   }
   KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  if (f32_wide(d_k, dtype)) {
+    // fp32 at d = 128: chunk quantities through the workspace, then the state pass
+    kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 0, 0, 0};
+    if (T > 0) {
+      KDA_REQUIRE(workspace && workspace_bytes >= kda::prefill_f32_workspace(B * H, T), KDA_ERR_WORKSPACE);
+      KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+      a.ws = static_cast<float*>(workspace);
+    }
+    return hip_status(kda::launch_prefill_f32(a, (hipStream_t)stream));
+  }
   // (the variants run on the pipelined kernel whatever the schedule overrides say)
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16,
                      flags ? 0 : env_nsplit(), flags ? 1 : env_pipeline()};
@@ -402,14 +424,14 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
 }
 
 size_t kda_chunk_fwd_staged_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
-  if (check_chunk_dims(B, T, H, d_k, d_v, dtype)) return 0;
+  if (check_staged_dims(B, T, H, d_k, d_v, dtype)) return 0;
   return staged_layout(B, T, H, d_k, d_v).total;
 }
 
 int kda_chunk_fwd_staged(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
                          int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  int st = check_staged_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
@@ -434,7 +456,7 @@ int kda_chunk_fwd_staged(const void* q, const void* k, const void* v, const void
 }
 
 int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k, int dtype, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_k, dtype);
+  int st = check_staged_dims(B, T, H, d_k, d_k, dtype);
   if (st) return st;
   if ((int64_t)B * H * T == 0) return KDA_OK;
   KDA_REQUIRE(g && b, KDA_ERR_NULL);
@@ -446,7 +468,7 @@ int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k, int 
 
 int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b, float* W, float* U, int B,
                  int T, int H, int d_k, int d_v, int dtype, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  int st = check_staged_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
   if ((int64_t)B * H * T == 0) return KDA_OK;
   KDA_REQUIRE(k && v && beta && b && W && U, KDA_ERR_NULL);
@@ -459,7 +481,7 @@ int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b,
 
 int kda_stage_state(const void* k, const float* b, const float* W, const float* U, const float* S0, float* Delta,
                     float* S_chunks, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  int st = check_staged_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
@@ -477,7 +499,7 @@ int kda_stage_state(const void* k, const float* b, const float* W, const float* 
 
 int kda_stage_output(const void* q, const void* k, const float* b, const float* Delta, const float* S_chunks,
                      void* o, int B, int T, int H, int d_k, int d_v, int dtype, void* stream) {
-  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  int st = check_staged_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
   if ((int64_t)B * H * T == 0) return KDA_OK;
   KDA_REQUIRE(q && k && b && Delta && S_chunks && o, KDA_ERR_NULL);

@@ -2527,8 +2527,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     __syncthreads();   // the workers' operand choice of the first chunk
     // S holds the state referenced to the current chunk, Diag(2^rho) S; the
     // reference before the first chunk is 0
-    // (the owners keep their per-lane addresses in registers for the whole
-    // loop; the workers, short of registers, recompute them in each phase)
     for (int n = -1; n < nchunks; ++n) {
       const bool nxt = n + 1 < nchunks;
       p.sync(smem_raw);
@@ -2559,6 +2557,9 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       if (!ST && outp) kx = state_f16_shift(S);
       // V^T of chunk n+1 (U is formed in phase 3)
       if (nxt && !vzero) owner_vt(p, vr, o, lane);
+      // values of chunk n+2 into the registers just consumed: unconditional
+      // (zeros past the end), so that no branch merges them with old values
+      fetch_v(vr, a, bb, h, c0 + n + 2, o, lane);
       p.sync(smem_raw);
       // phase 2a: diagonal block o of L and its inverse (chunk n+1)
       const bool f16m = (chunk_flags(p, (n + 1) & 1) & 1) != 0;
@@ -2578,10 +2579,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         else
           lp_block_tiles<bf16, 1>(p, q, I1, J1, lane);
       }
-      // values of chunk n+2: unconditional (zeros past the end), and after the
-      // role switch -- loads issued just before such a switch were seen to
-      // leave one wavefront's copy of the loaded registers wrong
-      fetch_v(vr, a, bb, h, c0 + n + 2, o, lane);
       p.sync(smem_raw);
       // phase 2b: entry-state readout of chunk n+1
       // O and U are (re)defined on every path, so their previous values are
@@ -2651,7 +2648,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       const bool nxt = n + 1 < nchunks;
       f16x4 kb[8], kt_t[8];
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       if (n >= 0) {
         // the operand choice of chunk n+1 (its flags were committed in the
         // previous slot's phase 3); a bf16 chunk drops its reference
@@ -2675,7 +2671,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, f16m, kb, kt_t, nx);
       }
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 2a: Kt^T, Kb^T; the ten P blocks and two off-diagonal blocks of
       // L, three each (the owners form the other four L blocks; state-only
       // runs: the six L blocks alone; no delta rule: the P blocks alone)
@@ -2704,7 +2699,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           pl_tiles<bf16>(p, w, lane);
       }
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 2b: workers 1-3: the off-diagonal blocks of A' in block columns
       // 0-2; all: gate prefix sums of chunk n+2 and the gate loads of chunk
       // n+3 (on every slot)
@@ -2718,7 +2712,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       }
       worker_scan<V>(r, gt, rho, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
       p.sync(smem_raw);
-      KDA_FRESH_LANE();
       // phase 3: W; the references and operand flags of chunk n+2
       if (!ND && nxt) worker_w(p, w, lane);
       ref_commit(p, gt, rho, w, lane, n & 1, (n + 2) % 3);

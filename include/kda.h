@@ -31,9 +31,10 @@
  *     element size).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
  *     calls return after enqueueing, without synchronising.
- *   - Supported head sizes: d_k = d_v in {64, 128}, except the chunked
- *     path with KDA_F32 inputs, which supports d_k = d_v = 64 (its fp32
- *     operand tiles for 128 do not fit in one CU's LDS).
+ *   - Supported head sizes: d_k = d_v in {64, 128}.  The chunked path with
+ *     KDA_F32 inputs at d = 128 needs a workspace (its fp32 operand tiles
+ *     do not fit in one CU's LDS, so the chunk quantities go through device
+ *     memory); the staged schedule has no KDA_F32 d = 128 form.
  *   - Numerical domain of the chunked path: every channel's log-gate summed
  *     over any 64 consecutive tokens of a chunk must stay above -80 (decay
  *     over one chunk >= e^-80); beyond it results may be Inf/NaN.  With
@@ -90,8 +91,12 @@ typedef enum {
  *   B, T, H       batch, tokens per sequence (any T >= 0; a partial last
  *                 chunk is handled; T = 0 copies S0 to S_T), heads
  *   workspace     device scratch of kda_chunk_fwd_workspace_size() bytes
- *                 (16-byte aligned), or NULL.  A nonzero size means that for
- *                 these sizes a segmented schedule is faster: each sequence
+ *                 (16-byte aligned), or NULL.  KDA_F32 with d = 128: required
+ *                 (one 36992-float block per chunk of 64 tokens and sequence x
+ *                 head, holding the chunk's Qg, W, Kb, U, P and decays;
+ *                 KDA_ERR_WORKSPACE without it).  KDA_BF16 with d = 128: a
+ *                 nonzero size means that for these sizes a segmented
+ *                 schedule is faster: each sequence
  *                 is cut into segments whose state maps S_end = M S_start + N
  *                 are formed in parallel and chained (the state recursion
  *                 between chunks is linear in the state, "...More Efficient"
@@ -114,13 +119,15 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int d
  * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation): the same computation and schedule choice, with
- * the segmented schedule's workspace taken from a device array inside the
- * library instead of a caller buffer.  Arguments as kda_chunk_fwd without
+ * the workspace (the segmented schedule's, or the chunk blocks of KDA_F32 at
+ * d = 128) taken from a device array inside the library instead of a caller
+ * buffer.  Arguments as kda_chunk_fwd without
  * the workspace pair; inputs and outputs are still the caller's.
  *   - The array holds KDA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the
  *     library runs on, from that GPU's first call until the process ends.
  *     Sizes whose schedule needs more (kda_chunk_fwd_workspace_size above
- *     it, e.g. 128 heads of 131 072 tokens) return KDA_ERR_SCRATCH and
+ *     it, e.g. 128 heads of 131 072 tokens, or KDA_F32 at d = 128 past 453
+ *     chunk x head blocks) return KDA_ERR_SCRATCH and
  *     launch nothing.  The first call on a GPU looks the array up there
  *     (hipGetSymbolAddress); no call allocates or frees memory.
  *   - All calls on one GPU share the array, which keeps the last call's

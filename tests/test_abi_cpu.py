@@ -60,7 +60,8 @@ def test_prefill_validation(L):
     assert _fwd(L, q=None) == -1
     assert _fwd(L, dk=96, dv=96) == -2
     assert _fwd(L, dk=128, dv=64) == -2
-    assert _fwd(L, dt=0, dk=128, dv=128) == -2           # fp32 supports d=64 only
+    assert _fwd(L, dt=0, dk=128, dv=128) == -5           # fp32 at d=128 needs its workspace
+    assert _fwd(L, dt=0, dk=128, dv=64) == -2
     assert _fwd(L, dt=7) == -3
     assert _fwd(L, B=-1) == -2
     assert _fwd(L, q=18) == -4                          # misaligned
@@ -68,6 +69,31 @@ def test_prefill_validation(L):
     assert _fwd(L, B=0) == 0                            # nothing to do: no launch
     assert _fwd(L, H=0) == 0
     assert L.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 1) == 0
+    # fp32 at d=128: one 36992-float block of chunk quantities per chunk and head
+    assert L.kda_chunk_fwd_workspace_size(2, 65, 3, 128, 128, 0) == 2 * 3 * 2 * 36992 * 4
+    assert L.kda_chunk_fwd_workspace_size(2, 0, 3, 128, 128, 0) == 0
+    assert L.kda_chunk_fwd_workspace_size(2, 65, 3, 64, 64, 0) == 0
+
+
+def test_fp32_d128_workspace_checks(L):
+    """The fp32 d=128 prefill refuses a missing, short or misaligned workspace,
+    and the staged schedule (which has no fp32 d=128 kernels) refuses the size."""
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    need = L.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 0)
+    f = lambda ws, n: L.kda_chunk_fwd(p(16), p(16), p(16), p(16), p(16), None, p(16), None, 1, 64, 1, 128, 128, 0,
+                                      p(ws), n, None)
+    assert f(None, 0) == -5
+    assert f(4096, need - 1) == -5
+    assert f(4100, need) == -4
+    assert L.kda_chunk_fwd_staged_workspace_size(1, 64, 1, 128, 128, 0) == 0
+    assert L.kda_chunk_fwd_staged(p(16), p(16), p(16), p(16), p(16), None, p(16), None, 1, 64, 1, 128, 128, 0,
+                                  p(4096), 1 << 30, None) == -2
+    assert L.kda_stage_cumsum(p(16), p(16), 1, 64, 1, 128, 0, None) == -2
+    # more than the allocation-free entry point's scratch holds: refused before any device call
+    T = 64 * 454
+    assert L.kda_chunk_fwd_workspace_size(1, T, 1, 128, 128, 0) > (64 << 20)
+    assert L.kda_chunk_fwd_noalloc(p(16), p(16), p(16), p(16), p(16), None, p(16), None, 1, T, 1, 128, 128, 0,
+                                   None) == -8
 
 
 def test_noalloc_validation(L):

@@ -132,6 +132,65 @@ def test_single_token_seeds(kda, pipeline, monkeypatch):
         check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"T1 seed {4000 + seed} pipeline={pipeline}")
 
 
+FP32_D128 = W.Prefill("kda_fwd_fp32_d128", 1, 256, 2, 128, 128, torch.float32, 0.05)
+F32W_SHAPES = [
+    # (B, T, H, s0, gate_mu)
+    (1, 256, 2, False, -3.0),     # the fp32 workload's shape at d = 128
+    (2, 65, 3, True, -3.0),       # one full chunk and a one-token tail
+    (1, 1, 1, True, -3.0),
+    (1, 64, 1, True, -3.0),
+    (1, 200, 2, True, -3.0),
+    (3, 517, 2, True, -3.0),
+    (1, 320, 2, True, 0.0),       # strong forgetting: about e^-50 per chunk and channel
+]
+
+
+@pytest.mark.parametrize("B,T,H,s0,mu", F32W_SHAPES, ids=[f"B{b}T{t}H{h}{'-S0' if z else ''}-mu{m:g}" for b, t, h, z, m in F32W_SHAPES])
+def test_fp32_d128(kda, B, T, H, s0, mu):
+    """fp32 at d_k = d_v = 128 (chunk quantities through the workspace, then
+    the state pass) against the oracle at the fp32 bound, on single-chunk,
+    exact, ragged and multi-chunk lengths, and with strong forgetting."""
+    cfg = W.Prefill("kda_fwd_fp32_d128", B, T, H, 128, 128, torch.float32, 0.05 if s0 else None, mu)
+    inp = W.prefill_inputs(cfg, device="cuda", seed=700 + T + H)
+    assert kda.lib().kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 0) == B * H * ((T + 63) // 64) * 36992 * 4
+    print(f"case fp32 d128 B{B} T{T} H{H} s0={s0} mu={mu}", flush=True)
+    o, S = _run(kda, inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.float32, f"fp32 d128 B{B}T{T}H{H}")
+
+
+def test_fp32_d128_streaming(kda):
+    """fp32 d = 128 in three calls whose S_T aliases S0 (T = 100, 64, 37)
+    equals one call over the whole sequence, and the oracle."""
+    cfg = W.Prefill("kda_fwd_fp32_d128", 1, 201, 2, 128, 128, torch.float32, 0.05)
+    inp = W.prefill_inputs(cfg, device="cuda", seed=77)
+    S = inp["S0"].clone()
+    outs = []
+    for a_, b_ in ((0, 100), (100, 164), (164, 201)):
+        part = [inp[n][:, a_:b_].contiguous() for n in ("q", "k", "v", "g", "beta")]
+        o, _ = kda.chunk_fwd(*part, S, S_T=S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o = torch.cat(outs, 1)
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.float32, "fp32 d128 streaming")
+
+
+def test_fp32_d128_needs_workspace(kda):
+    """Without its workspace the fp32 d = 128 prefill refuses (KDA_ERR_WORKSPACE)
+    and writes nothing."""
+    inp = W.prefill_inputs(FP32_D128, device="cuda", seed=3)
+    o = torch.full_like(inp["v"], 7.0)
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    L = kda.lib()
+    st = L.kda_chunk_fwd(p(inp["q"]), p(inp["k"]), p(inp["v"]), p(inp["g"]), p(inp["beta"]), p(inp["S0"]), p(o),
+                         None, 1, 256, 2, 128, 128, 0, None, 0, None)
+    assert st == -5
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all())
+
+
 def test_workload_fp32_B1_H2_T256(kda):
     """The fp32 workload at its full size (S0 = 0)."""
     inp = W.prefill_inputs(W.PREFILL_FP32_SMALL, device="cuda")

@@ -23,8 +23,9 @@ def kda():
 
 
 def _both(kda, inp):
-    B, T, H, _ = inp["q"].shape
-    need = kda.lib().kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 1)
+    B, T, H, d = inp["q"].shape
+    dt = 1 if inp["q"].dtype == torch.bfloat16 else 0
+    need = kda.lib().kda_chunk_fwd_workspace_size(B, T, H, d, d, dt)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     o1, S1 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], workspace=ws)
     o2 = torch.full_like(o1, float("nan"))
@@ -47,6 +48,20 @@ def test_noalloc_matches_workspace_entry_point(kda):
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
         o_ref, S_ref = oracle_prefill(inp)
         check_prefill(to64(o2), to64(S2), o_ref, S_ref, torch.bfloat16, f"noalloc B{B}T{T}H{H}")
+
+
+def test_noalloc_fp32_d128(kda):
+    """fp32 at d = 128 takes its chunk blocks from the scratch: two calls in a
+    row, the second smaller, each equal to the workspace entry point's."""
+    for B, T, H, seed in ((2, 300, 3, 61), (1, 70, 2, 62)):
+        cfg = W.Prefill("kda_fwd_fp32_d128", B, T, H, 128, 128, torch.float32, 0.05)
+        inp = W.prefill_inputs(cfg, device="cuda", seed=seed)
+        print(f"case noalloc fp32 d128 B{B} T{T} H{H}", flush=True)
+        need, (o1, S1), (o2, S2) = _both(kda, inp)
+        assert 0 < need <= 64 << 20
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+        o_ref, S_ref = oracle_prefill(inp)
+        check_prefill(to64(o2), to64(S2), o_ref, S_ref, torch.float32, f"noalloc fp32 d128 B{B}T{T}H{H}")
 
 
 def test_noalloc_one_pass_needs_no_scratch(kda):
