@@ -2722,14 +2722,20 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // Segmented schedule, between the two passes: the entry state of each
 // segment, S_{s+1} = M_s S_s + N_s for s = 1 .. nseg-2 (S_1 is segment 0's
-// final state), one 1024-thread workgroup per sequence and head, fp32 MFMA
-// (v_mfma_f32_16x16x4_f32) with S_s and M_s staged in LDS.
+// final state).  The columns of the state never mix, so each sequence and
+// head is split into NSC workgroups of 16 columns; each holds its 128 x 16
+// slice of S_s in LDS and M_s in one of two LDS buffers, loading M_{s+1}
+// into registers while it multiplies (fp32 MFMA, v_mfma_f32_16x16x4_f32).
+// Wavefront w forms rows 32w .. 32w+31 of the slice.
 // ---------------------------------------------------------------------------
 namespace segc {
-constexpr int NTC = 1024;
-constexpr int LDS_S = 144;   // fp32 rows of S: B-operand reads (rows 4kb + g, 16 columns) hit 64 banks
-constexpr int LDS_M = 132;   // fp32 rows of M: A-operand reads (16 rows, 4 columns) hit 64 banks
-constexpr int BYTES = (128 * LDS_S + 128 * LDS_M) * 4;
+constexpr int NTC = 256;
+constexpr int NSC = 8;               // column slices per sequence and head
+constexpr int CW = 128 / NSC;        // columns per slice
+constexpr int LDS_S = CW + 4;        // fp32 rows of the S slice
+constexpr int LDS_M = 132;           // fp32 rows of M: A-operand reads (16 rows, 4 columns) spread over the banks
+constexpr int MV = 128 * 128 / 4 / NTC;   // 16-byte vectors of M per thread
+constexpr int BYTES = (128 * LDS_S + 2 * 128 * LDS_M) * 4;
 }  // namespace segc
 
 __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
@@ -2737,59 +2743,68 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   constexpr int D = 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float* Sl = reinterpret_cast<float*>(smem_raw);
-  float* Ml = Sl + D * LDS_S;
-  const int head = blockIdx.x;
+  float* Mb = Sl + D * LDS_S;          // two buffers of D x LDS_M
+  const int head = blockIdx.x / NSC, col0 = (blockIdx.x % NSC) * CW;
   if (head >= a.B * a.H) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   auto mat = [&](int s, int kind) { return a.ws + ((int64_t(head) * a.nseg + s) * 3 + kind) * (D * D); };
+  floatx4 mr[MV];
+  auto load_m = [&](int s) {
+    const floatx4* src = reinterpret_cast<const floatx4*>(mat(s, 1));
+#pragma unroll
+    for (int u = 0; u < MV; ++u) mr[u] = src[tid + u * NTC];
+  };
+  auto store_m = [&](float* dst) {
+#pragma unroll
+    for (int u = 0; u < MV; ++u) {
+      const int i = tid + u * NTC, r = i / (D / 4), c4 = i % (D / 4);
+      *reinterpret_cast<floatx4*>(dst + r * LDS_M + 4 * c4) = mr[u];
+    }
+  };
   {
-    const floatx4* src = reinterpret_cast<const floatx4*>(mat(1, 0));
-    for (int i = tid; i < D * D / 4; i += NTC) {
-      const int r = i / (D / 4), c4 = i % (D / 4);
-      *reinterpret_cast<floatx4*>(Sl + r * LDS_S + 4 * c4) = src[i];
+    const float* src = mat(1, 0);
+    for (int i = tid; i < D * CW / 4; i += NTC) {
+      const int r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
+      *reinterpret_cast<floatx4*>(Sl + r * LDS_S + c4) = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
     }
   }
+  if (a.nseg > 2) {
+    load_m(1);
+    store_m(Mb);
+  }
+  __syncthreads();
   for (int sg = 1; sg + 1 < a.nseg; ++sg) {
-    {
-      const floatx4* src = reinterpret_cast<const floatx4*>(mat(sg, 1));
-      for (int i = tid; i < D * D / 4; i += NTC) {
-        const int r = i / (D / 4), c4 = i % (D / 4);
-        *reinterpret_cast<floatx4*>(Ml + r * LDS_M + 4 * c4) = src[i];
-      }
-    }
-    __syncthreads();
-    // wave w: output tiles 4w .. 4w+3 of the 8 x 8 tile grid (16 x 16 each)
+    const float* Ml = Mb + ((sg - 1) & 1) * D * LDS_M;
+    const bool more = sg + 2 < a.nseg;
+    if (more) load_m(sg + 1);
     const float* Nm = mat(sg, 2);
-    floatx4 acc[4];
+    floatx4 acc[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[u][jj] = Nm[(16 * ti + 4 * g4 + jj) * D + 16 * tj + l16];
-    }
-#pragma unroll 4
+      for (int jj = 0; jj < 4; ++jj) acc[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
+#pragma unroll 8
     for (int kb = 0; kb < D / 4; ++kb) {
+      const float bv = Sl[(4 * kb + g4) * LDS_S + l16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
-        const float av = Ml[(16 * ti + l16) * LDS_M + 4 * kb + g4];
-        const float bv = Sl[(4 * kb + g4) * LDS_S + 16 * tj + l16];
+      for (int u = 0; u < 2; ++u) {
+        const float av = Ml[(32 * wave + 16 * u + l16) * LDS_M + 4 * kb + g4];
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[u], 0, 0, 0);
       }
     }
-    __syncthreads();   // every read of S_s and M_s is done
+    __syncthreads();   // every read of S_s (and of the buffer M_{s+1} goes to) is done
     float* dst = mat(sg + 1, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * wave + u, ti = t >> 3, tj = t & 7;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * ti + 4 * g4 + jj, c = 16 * tj + l16;
-        Sl[r * LDS_S + c] = acc[u][jj];
-        dst[r * D + c] = acc[u][jj];
+        const int r = 32 * wave + 16 * u + 4 * g4 + jj;
+        Sl[r * LDS_S + l16] = acc[u][jj];
+        dst[r * D + col0 + l16] = acc[u][jj];
       }
-    }
+    if (more) store_m(Mb + (sg & 1) * D * LDS_M);
+    __syncthreads();
   }
 }
 
@@ -2856,7 +2871,7 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (2 * a.nseg - 3)), dim3(NT), bytes, s, a1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_combine_kernel, dim3(BH), dim3(segc::NTC), segc::BYTES, s, a);
+  hipLaunchKernelGGL(seg_combine_kernel, dim3(BH * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
   return hipGetLastError();
