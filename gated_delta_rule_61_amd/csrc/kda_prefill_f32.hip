@@ -220,7 +220,7 @@ __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// State pass: grid = B*H*NSPLIT (split-minor), NT threads.  Wavefront w forms
+// State pass: grid = ceil(B*H / 8) * 8 * NSPLIT, NT threads.  Wavefront w forms
 // token rows 16w .. 16w+15 of Delta and O, and updates state rows 32w .. 32w+31.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
@@ -233,7 +233,12 @@ __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
   float* Uv = reinterpret_cast<float*>(smem + S_U);
   float* gm = reinterpret_cast<float*>(smem + S_GM);
 
-  const int head = blockIdx.x / NSPLIT, col0 = (blockIdx.x % NSPLIT) * DVW;
+  // the NSPLIT slices of a head have block ids 8 apart: consecutive ids go to
+  // different XCDs, so the slices of a head share one XCD's L2 for the chunk
+  // blocks they all read
+  const int blk = blockIdx.x;
+  const int head = (blk / (8 * NSPLIT)) * 8 + blk % 8, col0 = ((blk / 8) % NSPLIT) * DVW;
+  if (head >= a.B * a.H) return;
   const int bb = head / a.H, h = head % a.H;
   const int nch = (a.T + C - 1) / C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -359,7 +364,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   const int64_t BH = (int64_t)a.B * a.H;
   const int64_t nch = (a.T + f32c::C - 1) / f32c::C;
   if (BH == 0) return hipSuccess;
-  if (BH * nch > INT32_MAX || BH * f32c::NSPLIT > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t nstate = (BH + 7) / 8 * 8 * f32c::NSPLIT;
+  if (BH * nch > INT32_MAX || nstate > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e;
   if (nch > 0) {
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(f32c::f32_prep_kernel),
@@ -371,7 +377,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(f32c::f32_state_kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, f32c::STATE_BYTES)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(f32c::f32_state_kernel, dim3((unsigned)(BH * f32c::NSPLIT)), dim3(f32c::NT),
+  hipLaunchKernelGGL(f32c::f32_state_kernel, dim3((unsigned)nstate), dim3(f32c::NT),
                      f32c::STATE_BYTES, s, a);
   return hipGetLastError();
 }
