@@ -1779,13 +1779,17 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
     float kf[8], qf[8];
     unpack8(r.k[i], kf);
     unpack8(r.q[i], qf);
+    // q_t . k_t over the lane's 8 channels, straight from the bf16 pairs
+    float d = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, r.q[i].w[u]), __builtin_bit_cast(bf16x2, r.k[i].w[u]),
+                                          d, false);
+    qk[i] = d;
     __builtin_amdgcn_sched_barrier(0);
     r.k[i] = ld16(nx.k, nx.vo, i * nx.rs);
     r.q[i] = ld16(nx.q, nx.vo, i * nx.rs);
     __builtin_amdgcn_sched_barrier(0);
-    qk[i] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qk[i] += qf[e] * kf[e];
     float kt[8], kh[8], qt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1995,10 +1999,32 @@ __device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J
       if (!DIAG || y <= x) lp_store(p, isP, I0 + x, J0 + y, acc[x][y], lane);
 }
 
+// fp32 16 x 16 x 16 products on the fp16 matrix cores: each operand split as
+// hi + lo with hi = fp16(x), lo = fp16(x - hi), and the product formed from
+// the three terms above 2^-22 relative (lo lo dropped).  Three fp16 MFMAs cost
+// about a fifth of the four fp32 ones they replace; operands must lie inside
+// the fp16 range.
+struct Split16 { f16x4 hi, lo; };
+__device__ __forceinline__ Split16 split16(const floatx4& x) {
+  Split16 r;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    r.hi[jj] = (f16)x[jj];
+    r.lo[jj] = (f16)(x[jj] - (float)r.hi[jj]);
+  }
+  return r;
+}
+__device__ __forceinline__ floatx4 mma16_split(const Split16& a, const Split16& b, floatx4 c) {
+  c = MH::mma16(a.lo, b.hi, c);
+  c = MH::mma16(a.hi, b.lo, c);
+  return MH::mma16(a.hi, b.hi, c);
+}
+
 // Owner I in phase 2a: diagonal block I of L and D_I = (I + L_II)^-1 in fp32.
 // With N = -L_II (strictly lower, N^16 = 0), D_I = (I + N)(I + N^2)(I + N^4)
-// (I + N^8): three squarings and three products on fp32 MFMA instead of a
-// 15-step substitution.  Every factor is kept in accumulator layout together
+// (I + N^8): three squarings and three products (split fp16 products, fp32
+// accumulation) instead of a 15-step substitution.  For unit keys |N| <= 1
+// and every factor lies far inside the fp16 range, where D_I is stored.  Every factor is kept in accumulator layout together
 // with its transpose: the accumulator tile of X^T is exactly the A-operand
 // fragment of X (lane (g, i): X[i][4g..4g+3]), and the tile of X is the
 // B-operand fragment, so X Y needs tiles of X^T and Y, and (X Y)^T = Y^T X^T
@@ -2008,7 +2034,6 @@ __device__ __forceinline__ void lp_block22(const Ptr& p, bool isP, int I0, int J
 template <typename TT>
 __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  typedef Mma<float> MF;
   typedef Mma<TT> MT;
   floatx4 n, nt;   // N and N^T tiles
   {
@@ -2039,23 +2064,27 @@ __device__ __forceinline__ void solver_block(const Ptr& p, int I, int lane) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) eye[jj] = (4 * g4 + jj == l16) ? 1.f : 0.f;
   // powers
-  const floatx4 n2 = MF::mma16(nt, n, z), n2t = MF::mma16(n, nt, z);
-  const floatx4 n4 = MF::mma16(n2t, n2, z), n4t = MF::mma16(n2, n2t, z);
-  const floatx4 n8 = MF::mma16(n4t, n4, z), n8t = MF::mma16(n4, n4t, z);
+  const Split16 sn = split16(n), snt = split16(nt);
+  const Split16 sn2 = split16(mma16_split(snt, sn, z)), sn2t = split16(mma16_split(sn, snt, z));
+  const Split16 sn4 = split16(mma16_split(sn2t, sn2, z)), sn4t = split16(mma16_split(sn2, sn2t, z));
+  const Split16 sn8 = split16(mma16_split(sn4t, sn4, z));
   // D = D1 (I + N^2)(I + N^4)(I + N^8), D1 = I + N; D_k+1 = D_k + D_k M, D_k+1^T = D_k^T + M^T D_k^T
   floatx4 d = eye + n, dt = eye + nt;
   {
-    const floatx4 e = MF::mma16(dt, n2, d), et = MF::mma16(n2, dt, dt);
+    const Split16 sdt = split16(dt);
+    const floatx4 e = mma16_split(sdt, sn2, d), et = mma16_split(sn2, sdt, dt);
     d = e;
     dt = et;
   }
   {
-    const floatx4 e = MF::mma16(dt, n4, d), et = MF::mma16(n4, dt, dt);
+    const Split16 sdt = split16(dt);
+    const floatx4 e = mma16_split(sdt, sn4, d), et = mma16_split(sn4, sdt, dt);
     d = e;
     dt = et;
   }
   {
-    const floatx4 e = MF::mma16(dt, n8, d), et = MF::mma16(n8, dt, dt);
+    const Split16 sdt = split16(dt);
+    const floatx4 e = mma16_split(sdt, sn8, d), et = mma16_split(sn8, sdt, dt);
     d = e;
     dt = et;
   }
@@ -2214,11 +2243,12 @@ __device__ __forceinline__ void rows_times_state_b(const bf16* A, const floatx4 
   }
 }
 
-// Phase 2b, owners, for a chunk with fp16 operands: Dx[nt][I] = Qt'[rows
+// Phase 2b, owners, for a chunk with fp16 operands: Dx[nt][I] += Qt'[rows
 // 16I..] @ S', the tiles held transposed as rows_times_state_b<true> holds
 // them, with Qt' (fp16, LDS) and the owner's referenced state S' as fp16
-// fragments, scaled by 2^-kx (kx >= 0 keeps them in the fp16 range; the
-// caller puts 2^kx back on Dx).
+// fragments; with SCALE, S' enters as S' 2^-kx (the caller puts 2^kx back on
+// Dx), for a state beyond the fp16 range.
+template <bool SCALE>
 __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, int kx, const floatx4 (&S)[2][DK / 16],
                                                  floatx4 (&Dx)[2][4], int lane) {
   const int fl = frag_lane(lane);
@@ -2236,9 +2266,7 @@ __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, int kx, const f
       MH::F32 sf[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        if (kx == 0) {
-          sf[nt] = MH::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
-        } else {
+        if constexpr (SCALE) {
           floatx4 lo, hi;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -2246,6 +2274,8 @@ __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, int kx, const f
             hi[jj] = __builtin_amdgcn_ldexpf(S[nt][2 * ks + 1][jj], -kx);
           }
           sf[nt] = MH::frag32(lo, hi);
+        } else {
+          sf[nt] = MH::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
         }
       }
 #pragma unroll
@@ -2254,6 +2284,18 @@ __device__ __forceinline__ void qt_times_state_h(const bf16* Qt, int kx, const f
         for (int nt = 0; nt < 2; ++nt) Dx[nt][I] = MH::mma32(sf[nt], af[k2][I], Dx[nt][I]);
     }
   }
+}
+
+// Whether every lane's 32 values of Dx are finite (wave-uniform).  A sum is
+// enough: an Inf or NaN among them makes it non-finite, and the rare finite
+// values whose sum overflows only send the caller down its exact path.
+__device__ __forceinline__ bool tiles_finite(const floatx4 (&Dx)[2][4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) s += (Dx[nt][I][0] + Dx[nt][I][1]) + (Dx[nt][I][2] + Dx[nt][I][3]);
+  return __builtin_amdgcn_ballot_w64(!__builtin_isfinite(s)) == 0;
 }
 
 // Scale exponent kx >= 0 that keeps an owner's referenced state below 2^15
@@ -2523,7 +2565,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
-    int kx = ST ? 0 : state_f16_shift(S);   // fp16 scale exponent of the state's read-out
     __syncthreads();   // the workers' operand choice of the first chunk
     // S holds the state referenced to the current chunk, Diag(2^rho) S; the
     // reference before the first chunk is 0
@@ -2552,9 +2593,6 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
                         reinterpret_cast<bf16*>(a.states) + (st0 + (int64_t)(c0 + n) * stn) * DK * DV, col0, lane);
         owner_state(p, Df, S, n & 1, lane);
       }
-      // range of the state for the fp16 read-out of chunk n+1 (phase 2b),
-      // taken here where the owners are not on the critical path
-      if (!ST && outp) kx = state_f16_shift(S);
       // V^T of chunk n+1 (U is formed in phase 3)
       if (nxt && !vzero) owner_vt(p, vr, o, lane);
       // values of chunk n+2 into the registers just consumed: unconditional
@@ -2591,12 +2629,20 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       // the state moves to the reference of chunk n+1 where it changed
       if (fl & 2) {
         state_rescale(S, p.rho + ((n + 1) % 3) * DK, p.rho + ((n + 3) % 3) * DK, lane);
-        if (!ST && outp) kx = state_f16_shift(S);
       }
       if (nxt && outp) {
         if (fl & 1) {
-          qt_times_state_h(p.Qt, kx, S, O, lane);
-          if (kx != 0) {
+          // the state as fp16 as it is; an entry beyond the fp16 range turns
+          // into Inf there and makes the product non-finite: then (rarely)
+          // again with the state scaled into range
+          qt_times_state_h<false>(p.Qt, 0, S, O, lane);
+          if (!tiles_finite(O)) {
+            const int kx = state_f16_shift(S);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int I = 0; I < 4; ++I) O[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+            qt_times_state_h<true>(p.Qt, kx, S, O, lane);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll

@@ -282,6 +282,28 @@ def test_bf16_operand_fallback(kda, burst):
     check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"strong decay {burst}")
 
 
+def test_state_beyond_fp16_range(kda):
+    """The fp16 read-out Qg S of a state with entries beyond the fp16 range
+    (here 16 key channels carry entries of order 1e5 that no key touches:
+    k = 0 and g = 0 there, q small) takes the rescaled path and matches the
+    oracle; the other channels are ordinary."""
+    inp = _case(W.PREFILL_BF16_H16_T4K, 1, 300, 2, seed=91)
+    big = slice(0, 16)
+    gen = torch.Generator(device="cuda").manual_seed(92)
+    S0 = inp["S0"].clone()
+    S0[:, :, big, :] = torch.randn(S0[:, :, big, :].shape, generator=gen, device="cuda") * 2e5
+    inp["S0"] = S0
+    for n, f in (("k", 0.0), ("g", 0.0), ("q", 1e-3)):
+        t = inp[n].float()
+        t[..., big] *= f
+        inp[n] = t.to(inp[n].dtype).contiguous()
+    assert float(S0.abs().max()) > 65504
+    o, S = _run(kda, inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "state beyond fp16")
+
+
 def test_empty_sequence_copies_state(kda):
     inp = _case(W.PREFILL_BF16_H16_T4K, 2, 0, 3, seed=1)
     o, S = _run(kda, inp)
