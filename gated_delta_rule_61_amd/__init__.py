@@ -48,6 +48,8 @@ _SIGS = {
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
+    "kda_chunk_fwd_varlen_ws": ([_vp] * 10 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_varlen_workspace_size": ([_i] * 7, _sz),
     "kda_varlen_schedule": ([_vp, _i, _i, _vp, _vp], _i),
     "kda_chunk_bwd": ([_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp], _i),
     "kda_chunk_bwd_workspace_size": ([_i] * 6, _sz),
@@ -202,12 +204,14 @@ def varlen_schedule(cu_seqlens, T_total, *, out=None, stream=None):
 
 
 def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o=None, S_T=None, stream=None,
-                     want_state=True, scalar_gate=False, delta=True):
+                     want_state=True, scalar_gate=False, delta=True, workspace=None, segmented=True):
     """Prefill of N packed sequences: q, k, g [T_total, H, d_k] (g [T_total, H]
     with scalar_gate), v [T_total, H, d_v], beta [T_total, H], cu_seqlens
     int32 [N + 1] on the device (sequence i = tokens cu[i] .. cu[i+1] - 1),
     S0 [N, H, d_k, d_v] fp32 or None; seq_order: int32 [N] start order (see
-    varlen_schedule) or None.  Returns (o [T_total, H, d_v], S_T)."""
+    varlen_schedule) or None.  segmented: pass (or allocate) the workspace of
+    kda_chunk_fwd_varlen_ws, whose segmented schedule splits long sequences.
+    Returns (o [T_total, H, d_v], S_T)."""
     flags = _flags(scalar_gate, delta)
     Tt, H, dk = q.shape
     dv = v.shape[-1]
@@ -231,9 +235,13 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
         o = torch.zeros((Tt, H, dv), dtype=dt, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    _check(lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
-                                      _ptr(S_T), _ptr(cu_seqlens), _ptr(seq_order), N, Tt, H, dk, dv,
-                                      _dtype(q), flags, _stream(stream)))
+    L = lib()
+    wsz = L.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, _dtype(q), flags) if segmented else 0
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_fwd_varlen_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                     _ptr(S_T), _ptr(cu_seqlens), _ptr(seq_order), N, Tt, H, dk, dv,
+                                     _dtype(q), flags, _ptr(workspace) if wsz else None, wsz, _stream(stream)))
     return o, S_T
 
 

@@ -290,6 +290,21 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
                          const float* S0, void* o, float* S_T, const int32_t* cu_seqlens,
                          const int32_t* seq_order, int N, int T_total, int H, int d_k, int d_v, int dtype,
                          int flags, void* stream) {
+  return kda_chunk_fwd_varlen_ws(q, k, v, g, beta, S0, o, S_T, cu_seqlens, seq_order, N, T_total, H, d_k, d_v,
+                                 dtype, flags, nullptr, 0, stream);
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v, int dtype, int flags) {
+  if (check_chunk_dims(N, T_total, H, d_k, d_v, dtype) || !valid_flags(flags) || !variant_dims(d_k, d_v, dtype))
+    return 0;
+  if ((int64_t)N * H == 0) return 0;
+  return kda::varlen_segments(N, T_total, H, device_cus()).bytes;
+}
+
+int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                            const float* S0, void* o, float* S_T, const int32_t* cu_seqlens,
+                            const int32_t* seq_order, int N, int T_total, int H, int d_k, int d_v, int dtype,
+                            int flags, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
   if (st) return st;
   KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
@@ -306,6 +321,16 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   a.variant = flags;
   a.cu_seqlens = cu_seqlens;
   a.seq_order = seq_order;
+  // segmented schedule when the caller passes the workspace it needs
+  const kda::VarlenSeg vs = kda::varlen_segments(N, T_total, H, device_cus());
+  if (vs.L > 0 && workspace && aligned16(workspace) && workspace_bytes >= vs.bytes) {
+    a.plan = static_cast<int*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + vs.plan_bytes);
+    a.seg_len = vs.L;
+    a.plan_j1 = vs.j1;
+    a.plan_j3 = vs.j3;
+    a.plan_ns = vs.ns;
+  }
   return hip_status(kda::launch_fused(a, (hipStream_t)stream));
 }
 

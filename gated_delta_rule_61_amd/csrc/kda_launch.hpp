@@ -30,7 +30,26 @@ struct PrefillArgs {
   // Chunk-entry states (one pass, no outputs): state at the start of every
   // chunk, bf16 and transposed, [B*H][ceil(T/64)][dv][dk]; NULL: normal forward.
   void* states;
+  // Packed sequences, segmented: the device plan (varlen_plan_kernel) with
+  // job tables of plan_j1 / plan_j3 entries, segments of seg_len chunks, the
+  // segment maps in ws; NULL: no segmented schedule for packed sequences.
+  int* plan;
+  int plan_j1, plan_j3, plan_ns;
 };
+
+// Offset (in ints) of the job tables inside a plan for N sequences.
+__host__ __device__ inline int varlen_plan_table_offset(int N) { return (4 + 3 * N + 1) & ~1; }
+
+// Segmented schedule for packed sequences: segment length in chunks (0: one
+// pass), the bounds of its job tables and map slots, and its workspace.
+struct VarlenSeg {
+  int L;          // chunks per segment (0: no segmented schedule)
+  int j1, j3;     // job-table bounds of pass 1 and pass 3
+  int ns;         // bound on the segmented sequences
+  int slots;      // bound on the map slots (each H x 3 maps of d x d fp32)
+  size_t plan_bytes, bytes;
+};
+VarlenSeg varlen_segments(int N, int T_total, int H, int cus);
 
 struct StageArgs {
   const void* q; const void* k; const void* v; const void* g; const void* beta;

@@ -28,6 +28,9 @@
 // 16x16 blocks: the four diagonal blocks are inverted by scalar forward
 // substitution (one wavefront, one lane per column), the off-diagonal
 // coupling runs on MFMA, column tile by column tile, in registers.
+#include <algorithm>
+#include <cstdlib>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -2447,6 +2450,27 @@ __device__ __forceinline__ void pl_tiles(const Ptr& p, int w, int lane) {
 }
 }  // namespace pipe
 
+// Device plan of the segmented schedule for packed sequences (written by
+// varlen_plan_kernel; N sequences, tables of j1 / j3 entries):
+//   count[0], count[1]  jobs of pass 1 and pass 3; count[2] segmented sequences
+//   nsegs[N]   segments of each sequence (P < 3: run whole in pass 1)
+//   mapbase[N] first map slot of a segmented sequence (slots of H x 3 maps)
+//   segseq[N]  the segmented sequences, in order
+//   table1[j1], table3[j3]  jobs (sequence, index inside the sequence)
+struct VarlenPlan {
+  const int* count; const int* nsegs; const int* mapbase; const int* segseq;
+  const int2* table1; const int2* table3;
+  __device__ VarlenPlan(const int* p, int N, int j1, int j3) {
+    count = p;
+    nsegs = p + 4;
+    mapbase = nsegs + N;
+    segseq = mapbase + N;
+    table1 = reinterpret_cast<const int2*>(p + varlen_plan_table_offset(N));
+    table3 = table1 + j1;
+    (void)j3;
+  }
+};
+
 // V: variant flags (kVarScalarGate, kVarNoDelta).  Without the delta rule
 // A' = I and W = 0: the pseudo-values are the values, so the L blocks, the
 // solver, W and the W S product drop out and only P, Kh, Qt, Kb remain.
@@ -2472,6 +2496,9 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   const float* s0p = nullptr;
   float* sTp = nullptr;
   bool ident = false, outp = true, vzero = false;
+  // packed sequences, segmented: this workgroup's segment (-1: the whole
+  // sequence) and the sequence's first map slot
+  int vsg = -1, vmap0 = 0;
   if (a.pass == 0) {
     int split;
     block_to_head<1>(blockIdx.x, head, split);
@@ -2485,6 +2512,45 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
     if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
     if (ST) outp = false;   // chunk-entry states only
+  } else if (a.plan) {
+    // packed sequences, segmented (the plan kernel's job tables): pass 1 runs
+    // whole short sequences and, for the long ones, segment 0, the offsets
+    // N_s and the transitions M_s; pass 3 runs segments 1 .. P-1
+    const VarlenPlan vp(a.plan, a.B, a.plan_j1, a.plan_j3);
+    const int job = blockIdx.x / a.H, hh = blockIdx.x % a.H;
+    if (job >= (a.pass == 1 ? vp.count[0] : vp.count[1])) return;
+    const int2 jb = (a.pass == 1 ? vp.table1 : vp.table3)[job];
+    const int sq = jb.x, k = jb.y, P = vp.nsegs[sq];
+    head = sq * a.H + hh;
+    vmap0 = vp.mapbase[sq];
+    const float* S0h = a.S0 ? a.S0 + (int64_t)head * DK * DV : nullptr;
+    float* STh = a.S_T ? a.S_T + (int64_t)head * DK * DV : nullptr;
+    auto vmap = [&](int sgi, int kind) {
+      return a.ws + (((int64_t)(vmap0 + sgi) * a.H + hh) * 3 + kind) * (int64_t)(DK * DV);
+    };
+    if (a.pass == 1) {
+      if (P < 3) {
+        s0p = S0h;
+        sTp = STh;
+      } else if (k == 0) {
+        vsg = 0;
+        s0p = S0h;
+        sTp = vmap(1, 0);
+      } else if (k <= P - 2) {
+        vsg = k;
+        outp = false;
+        sTp = vmap(k, 2);
+      } else {
+        vsg = k - (P - 2);
+        outp = false;
+        ident = vzero = true;
+        sTp = vmap(vsg, 1);
+      }
+    } else {
+      vsg = k + 1;
+      s0p = vmap(vsg, 0);
+      if (vsg == P - 1) sTp = STh;
+    }
   } else {
     const int njobs = a.pass == 1 ? 2 * a.nseg - 3 : a.nseg - 1;
     head = blockIdx.x / njobs;
@@ -2520,8 +2586,8 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   // (packed sequences: slot floor(cu[b] / C) + b + n, head-minor)
   int64_t st0 = (int64_t)head * ((a.T + C - 1) / C), stn = 1;
   if (a.cu_seqlens) {
-    // packed sequences (one pass): sequence bb is tokens [cu[bb], cu[bb+1]) of
-    // the [T, H, d] tensors, clamped to them; from here on it is addressed as a
+    // packed sequences: sequence bb is tokens [cu[bb], cu[bb+1]) of the
+    // [T, H, d] tensors, clamped to them; from here on it is addressed as a
     // batch of one sequence
     const int e0 = min(max(a.cu_seqlens[bb], 0), a.T);
     const int e1 = min(max(a.cu_seqlens[bb + 1], e0), a.T);
@@ -2537,6 +2603,10 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     a.T = e1 - e0;
     bb = 0;
     nchunks = (a.T + C - 1) / C;
+    if (vsg >= 0) {
+      c0 = vsg * a.seg_len;
+      nchunks = min(a.seg_len, nchunks - c0);
+    }
   }
   Ptr p;
   p.set(smem_raw);
@@ -2790,11 +2860,28 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float* Sl = reinterpret_cast<float*>(smem_raw);
   float* Mb = Sl + D * LDS_S;          // two buffers of D x LDS_M
-  const int head = blockIdx.x / NSC, col0 = (blockIdx.x % NSC) * CW;
-  if (head >= a.B * a.H) return;
+  const int col0 = (blockIdx.x % NSC) * CW;
+  int nseg = a.nseg;
+  // maps of segment s of this sequence and head: batched sequences keep them
+  // per head (nseg x 3); packed ones from their plan's first slot (H x 3 per slot)
+  int64_t mbase, mslot;
+  if (a.plan) {
+    const VarlenPlan vp(a.plan, a.B, a.plan_j1, a.plan_j3);
+    const int i = blockIdx.x / (NSC * a.H), hh = (blockIdx.x / NSC) % a.H;
+    if (i >= vp.count[2]) return;
+    const int sq = vp.segseq[i];
+    nseg = vp.nsegs[sq];
+    mbase = (int64_t)vp.mapbase[sq] * a.H + hh;
+    mslot = a.H;
+  } else {
+    const int head = blockIdx.x / NSC;
+    if (head >= a.B * a.H) return;
+    mbase = (int64_t)head * a.nseg;
+    mslot = 1;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  auto mat = [&](int s, int kind) { return a.ws + ((int64_t(head) * a.nseg + s) * 3 + kind) * (D * D); };
+  auto mat = [&](int s, int kind) { return a.ws + ((mbase + s * mslot) * 3 + kind) * (D * D); };
   floatx4 mr[MV];
   auto load_m = [&](int s) {
     const floatx4* src = reinterpret_cast<const floatx4*>(mat(s, 1));
@@ -2815,14 +2902,14 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
       *reinterpret_cast<floatx4*>(Sl + r * LDS_S + c4) = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
     }
   }
-  if (a.nseg > 2) {
+  if (nseg > 2) {
     load_m(1);
     store_m(Mb);
   }
   __syncthreads();
-  for (int sg = 1; sg + 1 < a.nseg; ++sg) {
+  for (int sg = 1; sg + 1 < nseg; ++sg) {
     const float* Ml = Mb + ((sg - 1) & 1) * D * LDS_M;
-    const bool more = sg + 2 < a.nseg;
+    const bool more = sg + 2 < nseg;
     if (more) load_m(sg + 1);
     const float* Nm = mat(sg, 2);
     floatx4 acc[2];
@@ -2852,6 +2939,117 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
     if (more) store_m(Mb + (sg & 1) * D * LDS_M);
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Plan of the segmented schedule for packed sequences (one workgroup, one
+// thread per sequence or start position, N <= kPlanThreads).  Sequence b
+// (clamped as the prefill clamps it) has nc_b chunks and P_b = ceil(nc_b / L)
+// segments; it is segmented if P_b >= 3.  Pass 1 runs the unsegmented
+// sequences whole (in the start order `order`, longest first if it is the
+// order kda_varlen_schedule writes) and then, per segmented sequence,
+// segment 0 and its 2 (P_b - 2) state maps; pass 3 runs segments 1 .. P_b-1.
+// Layout as VarlenPlan reads it.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int block_excl_scan(int x, int* buf, int& total) {
+  const int tid = threadIdx.x;
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int y = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += y;
+    __syncthreads();
+  }
+  total = buf[kPlanThreads - 1];
+  const int r = buf[tid] - x;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int* cu, const int* order, int N, int T,
+                                                                   int L, int* plan, int j1max, int j3max) {
+  __shared__ int buf[kPlanThreads];
+  __shared__ int nsg[kPlanThreads];
+  const int tid = threadIdx.x;
+  int* nsegs = plan + 4;
+  int* mapbase = nsegs + N;
+  int* segseq = mapbase + N;
+  int2* table1 = reinterpret_cast<int2*>(plan + varlen_plan_table_offset(N));
+  int2* table3 = table1 + j1max;
+  // segments of sequence tid
+  int P = 0;
+  if (tid < N) {
+    const int e0 = min(max(cu[tid], 0), T);
+    const int e1 = min(max(cu[tid + 1], e0), T);
+    const int nc = (e1 - e0 + C - 1) / C;
+    P = (nc + L - 1) / L;
+    nsegs[tid] = P;
+  }
+  nsg[tid] = P;
+  __syncthreads();
+  const bool seg = P >= 3;
+  // unsegmented sequences by start position
+  const int b_i = tid < N ? (order ? min(max(order[tid], 0), N - 1) : tid) : 0;
+  const bool whole_i = tid < N && nsg[b_i] < 3;
+  int U, S1, S3, SL, NS;
+  const int u_off = block_excl_scan(whole_i ? 1 : 0, buf, U);
+  const int s1_off = block_excl_scan(seg ? 2 * P - 3 : 0, buf, S1);
+  const int s3_off = block_excl_scan(seg ? P - 1 : 0, buf, S3);
+  const int sl_off = block_excl_scan(seg ? P : 0, buf, SL);
+  const int ns_off = block_excl_scan(seg ? 1 : 0, buf, NS);
+  if (whole_i && u_off < j1max) table1[u_off] = make_int2(b_i, 0);
+  if (tid < N) {
+    mapbase[tid] = seg ? sl_off : -1;
+    if (seg) {
+      segseq[ns_off] = tid;
+      for (int k = 0; k < 2 * P - 3; ++k)
+        if (U + s1_off + k < j1max) table1[U + s1_off + k] = make_int2(tid, k);
+      for (int k = 0; k < P - 1; ++k)
+        if (s3_off + k < j3max) table3[s3_off + k] = make_int2(tid, k);
+    }
+  }
+  if (tid == 0) {
+    plan[0] = min(U + S1, j1max);
+    plan[1] = min(S3, j3max);
+    plan[2] = NS;
+    plan[3] = SL;
+  }
+}
+
+VarlenSeg varlen_segments(int N, int T_total, int H, int cus) {
+  VarlenSeg v{};
+  if (N <= 0 || N > kPlanThreads || H <= 0 || T_total <= 0) return v;
+  const int64_t nct = ((int64_t)T_total + C - 1) / C;   // chunks of the longest possible sequence
+  const int64_t ncs = nct + N;                           // bound on the chunks of all sequences
+  int64_t L;
+  const char* e = getenv("KDA_SEGMENTS");
+  if (e) {
+    // about n segments for a sequence holding all the tokens (tests)
+    const int want = atoi(e);
+    if (want < 3) return v;
+    L = (nct + want - 1) / want;
+  } else {
+    // segments of about one CU's share of the work; worth it only when one
+    // sequence can be three of them
+    if (cus <= 0) return v;
+    L = std::max<int64_t>(16, (ncs * H + cus - 1) / cus);
+  }
+  if (L < 1 || nct < 2 * L + 1) return v;
+  const int64_t ns = std::min<int64_t>(N, nct / (2 * L + 1));   // segmented sequences have > 2L chunks
+  const int64_t slots = ncs / L + ns;                              // sum of their segment counts
+  const int64_t j1 = N + 2 * slots, j3 = slots;
+  if (j1 * H > INT32_MAX || ns * H * segc::NSC > INT32_MAX) return v;
+  v.L = (int)L;
+  v.j1 = (int)j1;
+  v.j3 = (int)j3;
+  v.ns = (int)ns;
+  v.slots = (int)slots;
+  v.plan_bytes = ((size_t)(varlen_plan_table_offset(N) + 2 * (j1 + j3)) * sizeof(int) + 255) / 256 * 256;
+  v.bytes = v.plan_bytes + (size_t)slots * H * 3 * 128 * 128 * sizeof(float);
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -2903,6 +3101,26 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
   hipError_t e = set_smem(fused_pipe_kernel, bytes);
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H;
+  if (a.plan) {
+    // packed sequences, segmented: the plan, whole short sequences with
+    // segment 0 and the maps of the long ones, entry states, then segments
+    // 1 .. P-1 (grids at the plan's bounds; surplus workgroups exit)
+    hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a.cu_seqlens, a.seq_order, a.B, a.T,
+                       a.seg_len, a.plan, a.plan_j1, a.plan_j3);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    PrefillArgs a1 = a, a3 = a;
+    a1.pass = 1;
+    a3.pass = 3;
+    hipLaunchKernelGGL(fused_pipe_kernel, dim3(a.plan_j1 * a.H), dim3(NT), bytes, s, a1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.plan_ns > 0 && a.plan_j3 > 0) {
+      if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(seg_combine_kernel, dim3(a.plan_ns * a.H * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(fused_pipe_kernel, dim3(a.plan_j3 * a.H), dim3(NT), bytes, s, a3);
+    }
+    return hipGetLastError();
+  }
   if (a.nseg < 3) {
     PrefillArgs a0 = a;
     a0.pass = 0;

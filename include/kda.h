@@ -210,14 +210,38 @@ size_t kda_chunk_fwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, in
  *             an empty sequence copies its S0 to S_T.
  *   flags     kda_variant flags as in kda_chunk_fwd_ex.
  * Supported: dtype KDA_BF16, d_k = d_v = 128 (else KDA_ERR_ARG).  Each
- * sequence runs as one chained pass per head (no segmented schedule), so a
- * single long sequence is better served by kda_chunk_fwd with a workspace.
+ * sequence runs as one chained pass per head; kda_chunk_fwd_varlen_ws with
+ * a workspace splits long sequences into segments.
  */
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* S0, void* o, float* S_T,
                          const int32_t* cu_seqlens, const int32_t* seq_order,
                          int N, int T_total, int H, int d_k, int d_v, int dtype,
                          int flags, void* stream);
+
+/*
+ * kda_chunk_fwd_varlen_ws -- kda_chunk_fwd_varlen with a workspace of
+ * kda_chunk_fwd_varlen_workspace_size() bytes (16-byte aligned): sequences
+ * longer than about three CUs' share of the work (segments of
+ * L = max(16, ceil((T_total/64 + N) H / CUs)) chunks) run segmented, as
+ * kda_chunk_fwd does with its workspace: the state maps S_end = M S_start + N
+ * of their middle segments are formed in parallel and chained, then each
+ * segment runs from its entry state ("...More Efficient" §IV: the recursion
+ * between chunks is linear in the state).  A device plan made from
+ * cu_seqlens on the stream decides which sequences; the others run whole.
+ * With NULL or a smaller workspace, or sizes where no sequence can be
+ * segmented (size 0), this is kda_chunk_fwd_varlen.  The results agree with
+ * it up to rounding.  Arguments otherwise as kda_chunk_fwd_varlen; N <= 1024
+ * for the segmented schedule (size 0 above).  Environment: KDA_SEGMENTS = n
+ * >= 3 asks for segments of ceil(T_total / 64 / n) chunks.
+ */
+int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* S0, void* o, float* S_T,
+                            const int32_t* cu_seqlens, const int32_t* seq_order,
+                            int N, int T_total, int H, int d_k, int d_v, int dtype,
+                            int flags, void* workspace, size_t workspace_bytes, void* stream);
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
+                                           int dtype, int flags);
 
 /*
  * kda_varlen_schedule -- seq_order for kda_chunk_fwd_varlen: the sequences

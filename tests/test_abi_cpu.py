@@ -241,3 +241,24 @@ def test_backward_varlen_validation(L):
     assert L.kda_chunk_bwd_varlen_workspace_size(5, 64 * 7, 3, 128, 128, 1, 0) == (7 + 5) * 3 * 131840
     assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 1) == 3 * 131840 + 100 * 128 * 6
     assert L.kda_chunk_bwd_varlen_workspace_size(2, 0, 1, 128, 128, 1, 0) == 0
+
+
+def test_varlen_segmented_workspace(L, monkeypatch):
+    """Workspace of kda_chunk_fwd_varlen_ws: 0 without a device and without
+    an override; with KDA_SEGMENTS = 6 on 6 sequences, 7597 tokens, H = 2:
+    segments of ceil(119 / 6) = 20 chunks, at most 2 segmented sequences
+    (> 40 chunks each) and 125 // 20 + 2 = 8 map slots: a plan rounded to
+    512 bytes plus 8 slots x 2 heads x 3 maps of 64 KiB."""
+    monkeypatch.delenv("KDA_SEGMENTS", raising=False)
+    assert L.kda_chunk_fwd_varlen_workspace_size(6, 7597, 2, 128, 128, 1, 0) == 0
+    monkeypatch.setenv("KDA_SEGMENTS", "6")
+    assert L.kda_chunk_fwd_varlen_workspace_size(6, 7597, 2, 128, 128, 1, 0) == 512 + 8 * 2 * 3 * 65536
+    assert L.kda_chunk_fwd_varlen_workspace_size(6, 7597, 2, 64, 64, 1, 0) == 0        # pipelined sizes only
+    assert L.kda_chunk_fwd_varlen_workspace_size(1025, 7597, 2, 128, 128, 1, 0) == 0   # plan holds 1024
+    p = ctypes.c_void_p(16)
+    cu = ctypes.c_void_p(64)
+    # argument checks before any launch
+    f = L.kda_chunk_fwd_varlen_ws
+    assert f(p, p, p, p, p, None, p, None, None, None, 6, 7597, 2, 128, 128, 1, 0, None, 0, None) == -1
+    assert f(p, p, p, p, p, None, p, None, cu, None, 6, 7597, 2, 96, 96, 1, 0, None, 0, None) == -2
+    assert f(p, p, p, p, p, None, p, None, cu, None, 0, 7597, 2, 128, 128, 1, 0, None, 0, None) == 0

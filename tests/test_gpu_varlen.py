@@ -215,3 +215,45 @@ def test_order_does_not_change_results(kda):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     assert torch.equal(o1, o3) and torch.equal(S1, S3)
+
+
+SEG_MIX = [64 * 60 + 5, 70, 0, 1, 64 * 12, 64 * 45 + 33]
+
+
+@pytest.mark.parametrize("order", [False, True], ids=["index-order", "longest-first"])
+@pytest.mark.parametrize("scalar_gate,delta", [VARIANTS[0], VARIANTS[3]], ids=[VIDS[0], VIDS[3]])
+def test_segmented_packed(kda, scalar_gate, delta, order, monkeypatch):
+    """The segmented schedule for packed sequences (kda_chunk_fwd_varlen_ws):
+    with segments of ceil(T_total / 64 / 6) = 20 chunks the two longest
+    sequences (61 and 46 chunks) run segmented and the others whole; every
+    sequence against the oracle alone, and against the one-pass schedule."""
+    monkeypatch.setenv("KDA_SEGMENTS", "6")
+    x, cu = _packed(SEG_MIX, 2, 57, scalar_gate)
+    N, Tt, H = len(SEG_MIX), int(cu[-1]), 2
+    flags = (1 if scalar_gate else 0) | (0 if delta else 2)
+    assert kda.lib().kda_chunk_fwd_varlen_workspace_size(N, Tt, H, 128, 128, 1, flags) > 0
+    so = kda.varlen_schedule(x["cu"], Tt) if order else None
+    print(f"case segmented varlen lengths={SEG_MIX} H2 scalar_gate={scalar_gate} delta={delta} order={order}", flush=True)
+    o, S = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"] if delta else None, x["cu"], x["S0"],
+                                seq_order=so, scalar_gate=scalar_gate, delta=delta)
+    torch.cuda.synchronize()
+    _check_all(x, cu, o, S, scalar_gate, delta, "segmented varlen")
+    o1, S1 = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"] if delta else None, x["cu"], x["S0"],
+                                  scalar_gate=scalar_gate, delta=delta, segmented=False)
+    torch.cuda.synchronize()
+    rel = (o.float() - o1.float()).norm() / o1.float().norm()
+    assert rel < 5e-3, rel
+    assert ((S - S1).norm() / S1.norm()) < 1e-3
+
+
+def test_segmented_packed_default_heuristic(kda):
+    """Without an override, 32 heads with one 25 600-token sequence beside a
+    short one: segments of max(16, ceil((T/64 + N) H / CUs)) chunks split the
+    long one; both sequences against the oracle, every head."""
+    lengths = [64 * 400, 100]
+    x, cu = _packed(lengths, 32, 58)
+    N, Tt = len(lengths), int(cu[-1])
+    assert kda.lib().kda_chunk_fwd_varlen_workspace_size(N, Tt, 32, 128, 128, 1, 0) > 0
+    print(f"case segmented varlen default lengths={lengths} H32", flush=True)
+    o, S = _run(kda, x)
+    _check_all(x, cu, o, S, False, True, "segmented varlen default")
