@@ -248,8 +248,9 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
 def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None,
               scalar_gate=False, delta=True):
     """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
-    adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16,
-    d_k = d_v = 128.  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet);
+    adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16 at
+    d = 128 (chunked), fp32 at d = 64 / 128 and bf16 at d = 64 (token
+    recurrence).  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet);
     delta=False: no delta rule (beta may be None, dbeta is None)."""
     flags = _flags(scalar_gate, delta)
     B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate=scalar_gate, delta=delta)

@@ -336,7 +336,8 @@ int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const v
 
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
   if (!valid_flags(flags)) return 0;
-  if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
+  if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
+  if (!variant_dims(d_k, d_v, dtype)) return kda::backward_tok_workspace(B, T, H, d_k);
   size_t n = kda::backward_workspace(B * H, T);
   // scalar gate: the broadcast gate (bf16) and the per-channel dg (fp32), [B,T,H,d_k] each
   if (flags & KDA_GATE_SCALAR) n += (size_t)B * T * H * d_k * (2 + 4);
@@ -353,7 +354,7 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  KDA_REQUIRE(valid_flags(flags), KDA_ERR_ARG);
   const bool sg = (flags & KDA_GATE_SCALAR) != 0, nd = (flags & KDA_NO_DELTA) != 0;
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
@@ -368,6 +369,12 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   const size_t need = kda_chunk_bwd_ex_workspace_size(B, T, H, d_k, d_v, dtype, flags);
   KDA_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), KDA_ERR_WORKSPACE);
   KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
+  if (!variant_dims(d_k, d_v, dtype)) {
+    // fp32, or d = 64: the token recurrence's reverse mode
+    kda::BackwardArgs a{q, k, v, g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg, nd ? nullptr : dbeta, dS0,
+                        B, T, H, nullptr, nullptr, nullptr, nullptr, flags, nullptr, 0};
+    return hip_status(kda::launch_backward_tok(a, d_k, dtype == KDA_BF16, workspace, (hipStream_t)stream));
+  }
   // workspace: chunk states, chunk-end adjoints (bf16 d_k x d_v each), the
   // per-chunk operand blocks; then (scalar gate) the broadcast gate and the
   // per-channel dg

@@ -77,7 +77,7 @@ struct BackwardArgs {
   void* adjoints;   // bf16 [B*H][N] adjoints of the chunk-end states, 16 x 16 tiles ([j][c] inside)
   void* mats;       // bf16 [B*H][N] per-chunk operand blocks (A, P^T, Kg, Kd, Qg, gamma, beta)
   float* dg32;      // if set: dg as fp32 [B,T,H,d_k] here instead of bf16 into dg
-  int variant;      // 0 (KDA) or kVarNoDelta (beta and dbeta unused)
+  int variant;      // kVar* flags: 0 or kVarNoDelta for the chunked backward, any for the token path
   // Packed sequences: B sequences, sequence b is tokens [cu_seqlens[b],
   // cu_seqlens[b+1]) of [T, H, d] tensors; the per-chunk arrays hold nslots x H
   // blocks (backward_varlen_slots).  NULL: [B, T, H, d].
@@ -85,6 +85,11 @@ struct BackwardArgs {
   int nslots;
 };
 size_t backward_workspace(int BH, int T);
+// Backward for the other sizes (fp32 at d = 64 or 128, bf16 at d = 64; every
+// variant): the token recurrence's reverse mode with chunk checkpoints
+// (kda_backward_tok.hip).  ws holds backward_tok_workspace(B, T, H, d) bytes.
+size_t backward_tok_workspace(int B, int T, int H, int d);
+hipError_t launch_backward_tok(const BackwardArgs& a, int d, bool bf16in, void* ws, hipStream_t s);
 int backward_varlen_slots(int nseq, int T);
 size_t backward_varlen_workspace(int nseq, int T, int H);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);

@@ -276,8 +276,12 @@ int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const voi
  *   workspace   kda_chunk_bwd_workspace_size() bytes (required), 16-byte aligned
  * The forward is recomputed inside (its chunk-entry states go to the
  * workspace); no forward state needs to be kept between the calls.
- * Supported: dtype KDA_BF16 with d_k = d_v = 128 (else KDA_ERR_ARG);
- * outputs must not alias inputs.
+ * Sizes: KDA_BF16 with d_k = d_v = 128 runs the chunked backward.  KDA_F32
+ * with d = 64 or 128 and KDA_BF16 with d = 64 run the reverse mode of the
+ * token recurrence (the same function: "...More Efficient" §IV), with the
+ * state checkpointed every 64 tokens and each chunk's token states
+ * recomputed, in fp32 vector arithmetic: a checking-grade path, much slower
+ * than the chunked one.  Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   const void* beta, const float* S0, const void* dO, const float* dS_T,
@@ -285,10 +289,12 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   int B, int T, int H, int d_k, int d_v, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of kda_chunk_bwd: B*H*ceil(T/64) * 131840 for d = 128
- * (per chunk, bf16: the chunk-entry state and chunk-end adjoint, two 64 x 64
- * matrices, three gated 64 x 128 key/query blocks; then 128 fp32 decays and
- * 64 fp32 betas). */
+/* Workspace bytes of kda_chunk_bwd: B*H*ceil(T/64) * 131840 for bf16 at
+ * d = 128 (per chunk, bf16: the chunk-entry state and chunk-end adjoint, two
+ * 64 x 64 matrices, three gated 64 x 128 key/query blocks; then 128 fp32
+ * decays and 64 fp32 betas).  Token path (fp32, or d = 64), in floats:
+ * B*H*ceil(T/64)*d*d state checkpoints, B*H*(d/16)*64*256*(d/16) token-state
+ * scratch, (d/16)*B*T*H*(3d+1) partial sums over the value-column slices. */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype);
 
 /*
@@ -334,7 +340,7 @@ size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, in
  *   cu_seqlens[N] = T_total: sequence i is tokens [cu_seqlens[i],
  *   cu_seqlens[i+1]); entries are clamped to [0, T_total] on the device.
  *   Zero-length sequences are allowed (dS0[i] = dS_T[i]).
- * Supported as kda_chunk_bwd_ex (bf16, d_k = d_v = 128, flags as there).
+ * Supported: dtype KDA_BF16, d_k = d_v = 128 (flags as kda_chunk_bwd_ex).
  * Workspace: kda_chunk_bwd_varlen_workspace_size bytes, 16-byte aligned
  * (chunk states, adjoints and operand blocks in floor(T_total/64) + N slots
  * per head).  Enqueued on `stream`; the caller keeps every buffer alive until

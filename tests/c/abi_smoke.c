@@ -35,7 +35,7 @@ int main(void) {
         KDA_ERR_NULL);
   CHECK(kda_varlen_schedule(p, 16385, 100, p, NULL), KDA_ERR_SHAPE);
   CHECK(kda_chunk_bwd(p, p, p, p, p, NULL, p, NULL, p, p, p, p, p, NULL, 1, 64, 1, 64, 64, KDA_BF16, NULL, 0, NULL),
-        KDA_ERR_ARG);
+        KDA_ERR_WORKSPACE);   /* d = 64: the token-recurrence backward, workspace missing */
   CHECK(kda_chunk_bwd(p, p, p, p, p, NULL, p, NULL, p, p, p, p, p, NULL, 1, 64, 1, 128, 128, KDA_BF16, NULL, 0, NULL),
         KDA_ERR_WORKSPACE);
   if (kda_chunk_bwd_workspace_size(1, 64, 1, 128, 128, KDA_BF16) != (size_t)131840)

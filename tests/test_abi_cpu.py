@@ -209,7 +209,7 @@ def test_backward_variant_validation(L):
     assert _bwd_ex(L, 0, dbeta=None) == -1           # KDA needs dbeta
     assert _bwd_ex(L, 0, beta=None) == -1            # ... and beta
     assert _bwd_ex(L, 4) == -7                       # unknown bit
-    assert _bwd_ex(L, 1, dk=64) == -7                # bf16, d = 128 only
+    assert _bwd_ex(L, 1, dk=64) == -5                # bf16 d = 64: token path, workspace missing
     assert _bwd_ex(L, 1, g=17) == -4                 # g not 2-byte aligned
     assert _bwd_ex(L, 1, g=18, dg=18) == -5          # scalar g / dg 2-byte aligned: workspace missing
     assert _bwd_ex(L, 0, dg=18) == -4                # per-channel dg must be 16-byte aligned
@@ -262,3 +262,19 @@ def test_varlen_segmented_workspace(L, monkeypatch):
     assert f(p, p, p, p, p, None, p, None, None, None, 6, 7597, 2, 128, 128, 1, 0, None, 0, None) == -1
     assert f(p, p, p, p, p, None, p, None, cu, None, 6, 7597, 2, 96, 96, 1, 0, None, 0, None) == -2
     assert f(p, p, p, p, p, None, p, None, cu, None, 0, 7597, 2, 128, 128, 1, 0, None, 0, None) == 0
+
+
+def test_bwd_token_path_workspace(L):
+    """The token-recurrence backward (fp32 at d = 64 / 128, bf16 at d = 64):
+    its workspace size, and the missing-workspace refusal before any launch."""
+    for dt, d in ((0, 64), (0, 128), (1, 64)):
+        B, T, H = 2, 130, 3
+        nch, ns, r = (T + 63) // 64, d // 16, d // 16
+        floats = B * H * nch * d * d + B * H * ns * 64 * 256 * r + ns * B * T * H * (3 * d + 1)
+        assert L.kda_chunk_bwd_ex_workspace_size(B, T, H, d, d, dt, 0) == floats * 4
+        assert L.kda_chunk_bwd_workspace_size(B, T, H, d, d, dt) == floats * 4
+    p = ctypes.c_void_p(16)
+    assert L.kda_chunk_bwd(p, p, p, p, p, None, p, None, p, p, p, p, p, None, 1, 64, 1, 64, 64, 0, None, 0,
+                           None) == -5
+    assert L.kda_chunk_bwd(p, p, p, p, p, None, p, None, p, p, p, p, p, None, 1, 64, 1, 96, 96, 0, None, 0,
+                           None) == -2
