@@ -1755,17 +1755,16 @@ __device__ __forceinline__ void worker_rho(const Ptr& p, const float (&rho)[8], 
 // plain ones: W' S' = W S with W' = A' Kt, and Kb'^T Delta = Diag(2^rho)
 // Kb^T Delta.)
 //
-// The next-but-one chunk's k and q are loaded into the same registers row by
-// row as each row is consumed, so the loads spread over this phase's
-// arithmetic instead of arriving as one burst; each row's loads are pinned in
-// place by scheduling fences.  Only the stores depend on f16m, so no load is
-// under that branch.
+// Phase 1 is the workers' critical phase: the next-but-one chunk's k and q
+// are loaded elsewhere (k at the end of phase 2a, q in phase 2b), into the
+// registers this phase has consumed.  Issued here, row by row, the same loads
+// made the kernel 7 % slower.
 //
 // Without the delta rule Kt (row-major and transposed) has no reader and is
 // not formed.
 template <int V>
-__device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates& gt, int w, int lane, int par,
-                                             bool f16m, f16x4 (&kb)[8], f16x4 (&kt_t)[8], const QkgSrc<V>& nx) {
+__device__ __forceinline__ void worker_apply(const Ptr& p, const WRegs& r, const Gates& gt, int w, int lane, int par,
+                                             bool f16m, f16x4 (&kb)[8], f16x4 (&kt_t)[8]) {
   constexpr bool ND = (V & kVarNoDelta) != 0;
   const int j = lane >> 4, m = lane & 15;
   const int c0 = 32 * w + 8 * j;
@@ -1789,10 +1788,6 @@ __device__ __forceinline__ void worker_apply(const Ptr& p, WRegs& r, const Gates
       d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, r.q[i].w[u]), __builtin_bit_cast(bf16x2, r.k[i].w[u]),
                                           d, false);
     qk[i] = d;
-    __builtin_amdgcn_sched_barrier(0);
-    r.k[i] = ld16(nx.k, nx.vo, i * nx.rs);
-    r.q[i] = ld16(nx.q, nx.vo, i * nx.rs);
-    __builtin_amdgcn_sched_barrier(0);
     float kt[8], kh[8], qt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -2773,18 +2768,17 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           worker_rho(p, rho, w, lane, (n + 1) % 3);
         }
       }
-      // phase 1: gated operands of chunk n+1 with the k / q loads of chunk
-      // n+2 interleaved.  Runs on every slot (past the last chunk on zeros,
-      // into arrays nobody reads again), so the loads are never under a
-      // branch: loaded registers merging with old ones at a join would make
-      // the merge wait for them.
+      // phase 1: gated operands of chunk n+1.  Runs on every slot (past the
+      // last chunk on zeros, into arrays nobody reads again), so the loads of
+      // the other phases are never under a branch: loaded registers merging
+      // with old ones at a join would make the merge wait for them.
       {
         const QkgSrc<V> nx(a, bb, h, c0 + n + 2, w, lane);
         if constexpr (!ND) {
           if (w == 0) p.beta[lane] = __uint_as_float(r.beta_bits << 16);
           r.beta_bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(nx.b, nx.boff, 0, 0);
         }
-        worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, f16m, kb, kt_t, nx);
+        worker_apply<V>(p, r, gt, w, lane, (n + 1) & 1, f16m, kb, kt_t);
       }
       p.sync(smem_raw);
       // phase 2a: Kt^T, Kb^T; the ten P blocks and two off-diagonal blocks of
@@ -2814,6 +2808,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         else
           pl_tiles<bf16>(p, w, lane);
       }
+      // k of chunk n+2 into the registers phase 1 consumed
+      {
+        const QkgSrc<V> nk(a, bb, h, c0 + n + 2, w, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.k[i] = ld16(nk.k, nk.vo, i * nk.rs);
+      }
       p.sync(smem_raw);
       // phase 2b: workers 1-3: the off-diagonal blocks of A' in block columns
       // 0-2; all: gate prefix sums of chunk n+2 and the gate loads of chunk
@@ -2827,6 +2827,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
           solver_offdiag_col<2>(p, lane);
       }
       worker_scan<V>(r, gt, rho, QkgSrc<V>(a, bb, h, c0 + n + 3, w, lane));
+      // q of chunk n+2
+      {
+        const QkgSrc<V> nk(a, bb, h, c0 + n + 2, w, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.q[i] = ld16(nk.q, nk.vo, i * nk.rs);
+      }
       p.sync(smem_raw);
       // phase 3: W; the references and operand flags of chunk n+2
       if (!ND && nxt) worker_w(p, w, lane);
