@@ -40,8 +40,11 @@ int check_chunk_dims(int B, int T, int H, int dk, int dv, int dt) {
   return KDA_OK;
 }
 
-// fp32 at d = 128: the two-launch path (a workspace is required)
+// fp32 at d = 128: the two-launch fp32-operand path (a workspace is required)
 bool f32_wide(int dk, int dt) { return dt == KDA_F32 && dk == 128; }
+// bf16 at d = 64: the same path when the caller passes its workspace (the
+// one-launch kernel's bf16 operands otherwise)
+bool f32_ops_d64(int dk, int dt, int flags) { return dt == KDA_BF16 && dk == 64 && flags == 0; }
 
 // The staged schedule and its single steps: as check_chunk_dims, except fp32
 // at d = 128, whose operand tiles the staged kernels cannot hold.
@@ -200,7 +203,8 @@ int kda_last_hip_error(void) { return g_last_hip; }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype) {
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
-  if (f32_wide(d_k, dtype)) return (int64_t)B * H * T == 0 ? 0 : kda::prefill_f32_workspace(B * H, T);
+  if (f32_wide(d_k, dtype) || f32_ops_d64(d_k, dtype, 0))
+    return (int64_t)B * H * T == 0 ? 0 : kda::prefill_f32_workspace(B * H, T, d_k);
   return kda::prefill_segment_workspace(B * H, segment_count(B, T, H, d_k, d_v, dtype));
 }
 
@@ -234,10 +238,17 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
     // fp32 at d = 128: chunk quantities through the workspace, then the state pass
     kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 0, 0, 0};
     if (T > 0) {
-      KDA_REQUIRE(workspace && workspace_bytes >= kda::prefill_f32_workspace(B * H, T), KDA_ERR_WORKSPACE);
+      KDA_REQUIRE(workspace && workspace_bytes >= kda::prefill_f32_workspace(B * H, T, d_k), KDA_ERR_WORKSPACE);
       KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
       a.ws = static_cast<float*>(workspace);
     }
+    return hip_status(kda::launch_prefill_f32(a, (hipStream_t)stream));
+  }
+  if (f32_ops_d64(d_k, dtype, flags) && T > 0 && workspace && aligned16(workspace) &&
+      workspace_bytes >= kda::prefill_f32_workspace(B * H, T, d_k)) {
+    // bf16 at d = 64 with its workspace: fp32 operands
+    kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 1, 0, 0};
+    a.ws = static_cast<float*>(workspace);
     return hip_status(kda::launch_prefill_f32(a, (hipStream_t)stream));
   }
   // (the variants run on the pipelined kernel whatever the schedule overrides say)

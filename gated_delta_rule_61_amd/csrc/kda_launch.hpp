@@ -106,9 +106,10 @@ hipError_t launch_stage_ut(const StageArgs& a, hipStream_t s);
 hipError_t launch_stage_state(const StageArgs& a, hipStream_t s);
 hipError_t launch_stage_output(const StageArgs& a, hipStream_t s);
 
-// Chunked prefill for fp32 inputs with d_k = d_v = 128 (two launches, see
-// kda_prefill_f32.hip): a.ws must hold prefill_f32_workspace(B*H, T) bytes.
-size_t prefill_f32_workspace(int BH, int T);
+// Chunked prefill with fp32 matrix operands, for fp32 inputs at d = 128 and
+// bf16 inputs at d = 64 (two launches, see kda_prefill_f32.hip): a.ws must
+// hold prefill_f32_workspace(B*H, T, d) bytes.
+size_t prefill_f32_workspace(int BH, int T, int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 
 // Default column split of the fused prefill for B*H heads on this device.

@@ -1,5 +1,7 @@
-// kda_prefill_f32.hip -- chunked KDA forward for fp32 inputs with
-// d_k = d_v = 128, on gfx950.
+// kda_prefill_f32.hip -- chunked KDA forward with every matrix operand in
+// fp32, on gfx950: fp32 inputs at d_k = d_v = 128, and bf16 inputs at
+// d_k = d_v = 64 (where fp32 operands keep short sequences inside the bf16
+// tolerance; the one-launch kernel's bf16 operands do not).
 //
 // The one-launch prefill keeps a chunk's gated key and query tiles in LDS; in
 // fp32 at d = 128 those tiles need more than a CU's 160 KB.  This path cuts
@@ -11,7 +13,7 @@
 //                     at once: all quantities of the chunk that do not
 //                     involve the state, into a workspace block;
 //   f32_state_kernel  one workgroup per (sequence x head, 32 value columns):
-//                     the chunks in order, with its 128 x 32 slice of the
+//                     the chunks in order, with its d x 32 slice of the
 //                     state in LDS.
 // With b the in-chunk prefix sums of g log2(e) per key channel (tokens past
 // the end of the sequence count as g = 0), b_C their value at the chunk's
@@ -25,7 +27,8 @@
 // The reference r halves the exponent range of the operands that carry
 // inverse decays (Kh), so that a chunk decaying by up to e^-80 per channel
 // stays inside fp32.  Every product is fp32 MFMA (v_mfma_f32_16x16x4_f32)
-// with fp32 accumulation.
+// with fp32 accumulation; inputs are converted to fp32 as they are read and
+// the output rounded to the input type as it is stored.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -33,45 +36,48 @@ namespace kda {
 namespace f32c {
 
 constexpr int C = 64;          // chunk length
-constexpr int D = 128;         // d_k = d_v
 constexpr int NT = 256;        // threads per workgroup (4 wavefronts)
-constexpr int LD = D + 4;      // LDS rows of [C][D] tiles (fp32)
 constexpr int LDC = C + 4;     // LDS rows of [C][C] tiles
 constexpr int DVW = 32;        // value columns per state workgroup
 constexpr int LDS_S = DVW + 4; // LDS rows of the [D][DVW] state slice and [C][DVW] values
-constexpr int NSPLIT = D / DVW;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Workspace block of one (sequence x head, chunk), fp32, offsets in floats.
-constexpr int64_t WS_QG = 0;                    // Qg [C][D]
-constexpr int64_t WS_W = WS_QG + C * D;         // W  [C][D]
-constexpr int64_t WS_KB = WS_W + C * D;         // Kb [C][D]
-constexpr int64_t WS_U = WS_KB + C * D;         // U  [C][D]
-constexpr int64_t WS_P = WS_U + C * D;          // P  [C][C] (zero above the diagonal)
-constexpr int64_t WS_GM = WS_P + C * C;         // gamma [D]
-constexpr int64_t WS_BLOCK = WS_GM + D;
-static_assert(WS_BLOCK % 4 == 0, "16-byte blocks");
-
-// LDS of the prep kernel (bytes): Kt, Kh, Qt tiles (Kh later holds Kg and
-// Qt the values V), L (then A in place), beta, and per channel r and b_C.
-constexpr int SZ_T = C * LD * 4;
-constexpr int P_KT = 0, P_KH = SZ_T, P_QT = 2 * SZ_T, P_L = 3 * SZ_T;
-constexpr int P_BETA = P_L + C * LDC * 4;
-constexpr int P_R = P_BETA + C * 4;
-constexpr int P_BC = P_R + D * 4;
-constexpr int PREP_BYTES = P_BC + D * 4;
-
-// LDS of the state kernel: the state slice, W, Qg, Kb, P, the value slice
-// (U, then Delta in place) and gamma.
-constexpr int S_S = 0;
-constexpr int S_W = S_S + D * LDS_S * 4;
-constexpr int S_QG = S_W + SZ_T;
-constexpr int S_KB = S_QG + SZ_T;
-constexpr int S_P = S_KB + SZ_T;
-constexpr int S_U = S_P + C * LDC * 4;
-constexpr int S_GM = S_U + C * LDS_S * 4;
-constexpr int STATE_BYTES = S_GM + D * 4;
-static_assert(PREP_BYTES <= 160 * 1024 && STATE_BYTES <= 160 * 1024, "LDS");
+template <int D>
+struct Geo {
+  static constexpr int LD = D + 4;          // LDS rows of [C][D] tiles (fp32)
+  static constexpr int NPART = NT / D;      // token parts of the prefix sums (2 or 4)
+  static constexpr int TPP = C / NPART;     // tokens per part
+  static constexpr int NSPLIT = D / DVW;    // state workgroups per head
+  // Workspace block of one (sequence x head, chunk), fp32, offsets in floats.
+  static constexpr int64_t WS_QG = 0;                    // Qg [C][D]
+  static constexpr int64_t WS_W = WS_QG + C * D;         // W  [C][D]
+  static constexpr int64_t WS_KB = WS_W + C * D;         // Kb [C][D]
+  static constexpr int64_t WS_U = WS_KB + C * D;         // U  [C][D]
+  static constexpr int64_t WS_P = WS_U + C * D;          // P  [C][C] (zero above the diagonal)
+  static constexpr int64_t WS_GM = WS_P + C * C;         // gamma [D]
+  static constexpr int64_t WS_BLOCK = WS_GM + D;
+  static_assert(WS_BLOCK % 4 == 0, "16-byte blocks");
+  // LDS of the prep kernel (bytes): Kt, Kh, Qt tiles (Kh later holds Kg and
+  // Qt the values V), L (then A in place), beta, and each part's per-channel
+  // total of the prefix sums.
+  static constexpr int SZ_T = C * LD * 4;
+  static constexpr int P_KT = 0, P_KH = SZ_T, P_QT = 2 * SZ_T, P_L = 3 * SZ_T;
+  static constexpr int P_BETA = P_L + C * LDC * 4;
+  static constexpr int P_TOT = P_BETA + C * 4;
+  static constexpr int PREP_BYTES = P_TOT + NPART * D * 4;
+  // LDS of the state kernel: the state slice, W, Qg, Kb, P, the value slice
+  // (U, then Delta in place) and gamma.
+  static constexpr int S_S = 0;
+  static constexpr int S_W = S_S + D * LDS_S * 4;
+  static constexpr int S_QG = S_W + SZ_T;
+  static constexpr int S_KB = S_QG + SZ_T;
+  static constexpr int S_P = S_KB + SZ_T;
+  static constexpr int S_U = S_P + C * LDC * 4;
+  static constexpr int S_GM = S_U + C * LDS_S * 4;
+  static constexpr int STATE_BYTES = S_GM + D * 4;
+  static_assert(PREP_BYTES <= 160 * 1024 && STATE_BYTES <= 160 * 1024, "LDS");
+  static_assert(NPART * D == NT && NPART * TPP == C && 32 % TPP == 0, "token parts");
+};
 
 typedef Mma<float> MF;
 
@@ -83,71 +89,76 @@ __device__ __forceinline__ int64_t tok_index(int bb, int T, int H, int h, int t,
   return (((int64_t)bb * T + t) * H + h) * width;
 }
 
+template <typename T>
+__device__ __forceinline__ float ldf(const void* p, int64_t i) {
+  return to_f32(static_cast<const T*>(p)[i]);
+}
+
 // ---------------------------------------------------------------------------
-// Prep: grid = B*H*nchunks (chunk-minor), NT threads.  Thread (c, half):
-// channel c = tid % 128, tokens 32 half .. 32 half + 31 of the chunk.
+// Prep: grid = B*H*nchunks (chunk-minor), NT threads.  Thread (c, part):
+// channel c = tid % D, tokens TPP part .. TPP part + TPP - 1 of the chunk.
 // ---------------------------------------------------------------------------
+template <typename T, int D>
 __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
+  typedef Geo<D> G;
+  constexpr int LD = G::LD, TPP = G::TPP, NPART = G::NPART;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* Kt = reinterpret_cast<float*>(smem + P_KT);
-  float* Kh = reinterpret_cast<float*>(smem + P_KH);
-  float* Qt = reinterpret_cast<float*>(smem + P_QT);
-  float* Lm = reinterpret_cast<float*>(smem + P_L);
-  float* beta = reinterpret_cast<float*>(smem + P_BETA);
-  float* rr = reinterpret_cast<float*>(smem + P_R);
-  float* bcs = reinterpret_cast<float*>(smem + P_BC);
+  float* Kt = reinterpret_cast<float*>(smem + G::P_KT);
+  float* Kh = reinterpret_cast<float*>(smem + G::P_KH);
+  float* Qt = reinterpret_cast<float*>(smem + G::P_QT);
+  float* Lm = reinterpret_cast<float*>(smem + G::P_L);
+  float* beta = reinterpret_cast<float*>(smem + G::P_BETA);
+  float* tot = reinterpret_cast<float*>(smem + G::P_TOT);
 
   const int nch = (a.T + C - 1) / C;
   const int head = blockIdx.x / nch, n = blockIdx.x % nch;
   const int bb = head / a.H, h = head % a.H;
   const int t0 = n * C, nv = min(C, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid & (D - 1), half = tid >> 7;
-  const float* q = static_cast<const float*>(a.q);
-  const float* k = static_cast<const float*>(a.k);
-  const float* v = static_cast<const float*>(a.v);
-  const float* g = static_cast<const float*>(a.g);
-  const float* bt = static_cast<const float*>(a.beta);
-  float* blk = a.ws + ((int64_t)head * nch + n) * WS_BLOCK;
+  const int c = tid & (D - 1), part = tid / D;
+  float* blk = a.ws + ((int64_t)head * nch + n) * G::WS_BLOCK;
   const int64_t base = tok_index(bb, a.T, a.H, h, t0, D);   // token t0, channel 0
   const int64_t tstr = (int64_t)a.H * D;                   // token stride
 
-  // in-chunk prefix sums: each half scans its 32 tokens, half 1 then adds
-  // half 0's total (which is r, the value at token 31)
-  float b[32];
+  // in-chunk prefix sums: each part scans its tokens and then adds the
+  // totals of the parts before it; r is the sum through token 31, b_C the
+  // chunk's whole sum
+  float b[TPP];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int t = 32 * half + i;
-    s += (t < nv ? g[base + t * tstr + c] : 0.f) * kLog2e;
+  for (int i = 0; i < TPP; ++i) {
+    const int t = TPP * part + i;
+    s += (t < nv ? ldf<T>(a.g, base + t * tstr + c) : 0.f) * kLog2e;
     b[i] = s;
   }
-  if (half == 0) rr[c] = s;
-  if (tid < C) beta[tid] = tid < nv ? bt[((int64_t)bb * a.T + t0 + tid) * a.H + h] : 0.f;
+  tot[part * D + c] = s;
+  if (tid < C) beta[tid] = tid < nv ? ldf<T>(a.beta, ((int64_t)bb * a.T + t0 + tid) * a.H + h) : 0.f;
   __syncthreads();
-  const float r = rr[c];
-  if (half == 1) {
+  float off = 0.f, r = 0.f, bC = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) b[i] += r;
-    bcs[c] = b[31];
+  for (int pp = 0; pp < NPART; ++pp) {
+    const float x = tot[pp * D + c];
+    if (pp < part) off += x;
+    if (pp < 32 / TPP) r += x;
+    bC += x;
   }
-  __syncthreads();
-  const float bC = bcs[c];
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) b[i] += off;
 
   // the gated operands: Kt, Kh, Qt to LDS; Qg, Kb to the workspace
 #pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    const int t = 32 * half + i;
-    const float kv = t < nv ? k[base + t * tstr + c] : 0.f;
-    const float qv = t < nv ? q[base + t * tstr + c] : 0.f;
+  for (int i = 0; i < TPP; ++i) {
+    const int t = TPP * part + i;
+    const float kv = t < nv ? ldf<T>(a.k, base + t * tstr + c) : 0.f;
+    const float qv = t < nv ? ldf<T>(a.q, base + t * tstr + c) : 0.f;
     const float up = exp2f(b[i] - r), dn = exp2f(r - b[i]);
     Kt[t * LD + c] = kv * up;
     Kh[t * LD + c] = kv * dn;
     Qt[t * LD + c] = qv * up;
-    blk[WS_QG + t * D + c] = qv * exp2f(b[i]);
-    blk[WS_KB + t * D + c] = kv * exp2f(bC - b[i]);
+    blk[G::WS_QG + t * D + c] = qv * exp2f(b[i]);
+    blk[G::WS_KB + t * D + c] = kv * exp2f(bC - b[i]);
   }
-  if (half == 1) blk[WS_GM + c] = exp2f(bC);
+  if (part == 0) blk[G::WS_GM + c] = exp2f(bC);
   __syncthreads();
 
   // L and P, 16 x 16 tiles (I, J): 16 tiles of each, 8 per wavefront; tiles
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
     for (int jj = 0; jj < 4; ++jj) {
       const int i = 16 * I + 4 * g4 + jj;
       if (isP)
-        blk[WS_P + i * C + j] = j <= i ? acc[jj] : 0.f;
+        blk[G::WS_P + i * C + j] = j <= i ? acc[jj] : 0.f;
       else if (J <= I)
         Lm[i * LDC + j] = j < i ? beta[i] * acc[jj] : 0.f;
     }
@@ -177,11 +188,11 @@ __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
 
   // Kg = 2^b K over Kh, V over Qt (both are free now)
 #pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    const int t = 32 * half + i;
-    const float kv = t < nv ? k[base + t * tstr + c] : 0.f;
+  for (int i = 0; i < TPP; ++i) {
+    const int t = TPP * part + i;
+    const float kv = t < nv ? ldf<T>(a.k, base + t * tstr + c) : 0.f;
     Kh[t * LD + c] = kv * exp2f(b[i]);
-    Qt[t * LD + c] = t < nv ? v[tok_index(bb, a.T, a.H, h, t0 + t, D) + c] : 0.f;
+    Qt[t * LD + c] = t < nv ? ldf<T>(a.v, tok_index(bb, a.T, a.H, h, t0 + t, D) + c) : 0.f;
   }
   // A = (I + L)^-1 in place, one row after the other, one lane per column:
   // A_i = e_i - sum_{j<i} L_ij A_j (row i of L is read whole before row i of
@@ -196,11 +207,13 @@ __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-  // W = A Diag(beta) Kg and U = A Diag(beta) V: 32 + 32 tiles, 16 per
-  // wavefront; A is lower triangular, so tile row I sums token slabs 0..I
-  for (int tl = wave; tl < 64; tl += 4) {
-    const bool isU = tl >= 32;
-    const int I = (tl & 31) >> 3, N = tl & 7;
+  // W = A Diag(beta) Kg and U = A Diag(beta) V: 2 (C/16) (D/16) tiles over
+  // the four wavefronts; A is lower triangular, so tile row I sums token
+  // slabs 0..I
+  constexpr int NTW = (C / 16) * (D / 16);
+  for (int tl = wave; tl < 2 * NTW; tl += 4) {
+    const bool isU = tl >= NTW;
+    const int I = (tl % NTW) / (D / 16), N = tl % (D / 16);
     const float* X = isU ? Qt : Kh;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int J = 0; J <= I; ++J) {
@@ -213,25 +226,30 @@ __global__ __launch_bounds__(NT) void f32_prep_kernel(PrefillArgs a) {
       for (int jj = 0; jj < 4; ++jj) bf[jj] = X[(t + jj) * LD + 16 * N + l16];
       acc = MF::mma16(af, bf, acc);
     }
-    float* out = blk + (isU ? WS_U : WS_W);
+    float* out = blk + (isU ? G::WS_U : G::WS_W);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) out[(16 * I + 4 * g4 + jj) * D + 16 * N + l16] = acc[jj];
   }
 }
 
 // ---------------------------------------------------------------------------
-// State pass: grid = ceil(B*H / 8) * 8 * NSPLIT, NT threads.  Wavefront w forms
-// token rows 16w .. 16w+15 of Delta and O, and updates state rows 32w .. 32w+31.
+// State pass: grid = ceil(B*H / 8) * 8 * NSPLIT, NT threads.  Wavefront w
+// forms token rows 16w .. 16w+15 of Delta and O, and updates state rows
+// (D/4) w .. (D/4) (w+1) - 1.
 // ---------------------------------------------------------------------------
+template <typename T, int D>
 __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
+  typedef Geo<D> G;
+  constexpr int LD = G::LD, NSPLIT = G::NSPLIT;
+  constexpr int RW = D / 4;   // state rows per wavefront
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* S = reinterpret_cast<float*>(smem + S_S);
-  float* Wm = reinterpret_cast<float*>(smem + S_W);
-  float* Qg = reinterpret_cast<float*>(smem + S_QG);
-  float* Kb = reinterpret_cast<float*>(smem + S_KB);
-  float* Pm = reinterpret_cast<float*>(smem + S_P);
-  float* Uv = reinterpret_cast<float*>(smem + S_U);
-  float* gm = reinterpret_cast<float*>(smem + S_GM);
+  float* S = reinterpret_cast<float*>(smem + G::S_S);
+  float* Wm = reinterpret_cast<float*>(smem + G::S_W);
+  float* Qg = reinterpret_cast<float*>(smem + G::S_QG);
+  float* Kb = reinterpret_cast<float*>(smem + G::S_KB);
+  float* Pm = reinterpret_cast<float*>(smem + G::S_P);
+  float* Uv = reinterpret_cast<float*>(smem + G::S_U);
+  float* gm = reinterpret_cast<float*>(smem + G::S_GM);
 
   // the NSPLIT slices of a head have block ids 8 apart: consecutive ids go to
   // different XCDs, so the slices of a head share one XCD's L2 for the chunk
@@ -243,9 +261,9 @@ __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
   const int nch = (a.T + C - 1) / C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  float* o = static_cast<float*>(a.o);
+  T* o = static_cast<T*>(a.o);
 
-  // entry state slice: rows 0..127, columns col0 .. col0+31
+  // entry state slice: rows 0..D-1, columns col0 .. col0+31
   for (int e = tid; e < D * DVW / 4; e += NT) {
     const int row = e / (DVW / 4), c4 = 4 * (e % (DVW / 4));
     floatx4 x = {0.f, 0.f, 0.f, 0.f};
@@ -254,24 +272,24 @@ __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
   }
 
   for (int n = 0; n < nch; ++n) {
-    const float* blk = a.ws + ((int64_t)head * nch + n) * WS_BLOCK;
+    const float* blkp = a.ws + ((int64_t)head * nch + n) * G::WS_BLOCK;
     const int t0 = n * C, nv = min(C, a.T - t0);
     // the chunk's operands to LDS
     for (int e = tid; e < C * D / 4; e += NT) {
       const int row = e / (D / 4), c4 = 4 * (e % (D / 4));
-      *reinterpret_cast<floatx4*>(Wm + row * LD + c4) = ld4(blk + WS_W + row * D + c4);
-      *reinterpret_cast<floatx4*>(Qg + row * LD + c4) = ld4(blk + WS_QG + row * D + c4);
-      *reinterpret_cast<floatx4*>(Kb + row * LD + c4) = ld4(blk + WS_KB + row * D + c4);
+      *reinterpret_cast<floatx4*>(Wm + row * LD + c4) = ld4(blkp + G::WS_W + row * D + c4);
+      *reinterpret_cast<floatx4*>(Qg + row * LD + c4) = ld4(blkp + G::WS_QG + row * D + c4);
+      *reinterpret_cast<floatx4*>(Kb + row * LD + c4) = ld4(blkp + G::WS_KB + row * D + c4);
     }
     for (int e = tid; e < C * C / 4; e += NT) {
       const int row = e / (C / 4), c4 = 4 * (e % (C / 4));
-      *reinterpret_cast<floatx4*>(Pm + row * LDC + c4) = ld4(blk + WS_P + row * C + c4);
+      *reinterpret_cast<floatx4*>(Pm + row * LDC + c4) = ld4(blkp + G::WS_P + row * C + c4);
     }
     for (int e = tid; e < C * DVW / 4; e += NT) {
       const int row = e / (DVW / 4), c4 = 4 * (e % (DVW / 4));
-      *reinterpret_cast<floatx4*>(Uv + row * LDS_S + c4) = ld4(blk + WS_U + row * D + col0 + c4);
+      *reinterpret_cast<floatx4*>(Uv + row * LDS_S + c4) = ld4(blkp + G::WS_U + row * D + col0 + c4);
     }
-    if (tid < D / 4) *reinterpret_cast<floatx4*>(gm + 4 * tid) = ld4(blk + WS_GM + 4 * tid);
+    if (tid < D / 4) *reinterpret_cast<floatx4*>(gm + 4 * tid) = ld4(blkp + G::WS_GM + 4 * tid);
     __syncthreads();
 
     // Delta = U - W S (over U) and the inter-chunk read-out Qg S, rows 16w..
@@ -311,13 +329,13 @@ __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int row = 16 * w + 4 * g4 + jj;
-        if (row < nv) o[tok_index(bb, a.T, a.H, h, t0 + row, D) + col0 + 16 * nt + l16] = y[jj];
+        if (row < nv) o[tok_index(bb, a.T, a.H, h, t0 + row, D) + col0 + 16 * nt + l16] = from_f32<T>(y[jj]);
       }
     }
-    // S <- Diag(gamma) S + Kb^T Delta, state rows 32w .. 32w+31
+    // S <- Diag(gamma) S + Kb^T Delta, state rows RW w .. RW (w+1) - 1
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int r0 = 32 * w + 16 * rt;
+    for (int rt = 0; rt < RW / 16; ++rt) {
+      const int r0 = RW * w + 16 * rt;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         floatx4 acc;
@@ -353,33 +371,43 @@ __global__ __launch_bounds__(NT) void f32_state_kernel(PrefillArgs a) {
   }
 }
 
+template <typename T, int D>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+  typedef Geo<D> G;
+  const int64_t BH = (int64_t)a.B * a.H;
+  const int64_t nch = (a.T + C - 1) / C;
+  if (BH == 0) return hipSuccess;
+  const int64_t nstate = (BH + 7) / 8 * 8 * G::NSPLIT;
+  if (BH * nch > INT32_MAX || nstate > INT32_MAX) return hipErrorInvalidValue;
+  hipError_t e;
+  auto prep = f32_prep_kernel<T, D>;
+  auto state = f32_state_kernel<T, D>;
+  if (nch > 0) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 G::PREP_BYTES)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(prep, dim3((unsigned)(BH * nch)), dim3(NT), G::PREP_BYTES, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(state), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               G::STATE_BYTES)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(state, dim3((unsigned)nstate), dim3(NT), G::STATE_BYTES, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace f32c
 
-size_t prefill_f32_workspace(int BH, int T) {
+size_t prefill_f32_workspace(int BH, int T, int d) {
   const int64_t nch = (T + f32c::C - 1) / f32c::C;
-  return (size_t)BH * nch * f32c::WS_BLOCK * sizeof(float);
+  const int64_t block = d == 64 ? f32c::Geo<64>::WS_BLOCK : f32c::Geo<128>::WS_BLOCK;
+  return (size_t)BH * nch * block * sizeof(float);
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
-  const int64_t BH = (int64_t)a.B * a.H;
-  const int64_t nch = (a.T + f32c::C - 1) / f32c::C;
-  if (BH == 0) return hipSuccess;
-  const int64_t nstate = (BH + 7) / 8 * 8 * f32c::NSPLIT;
-  if (BH * nch > INT32_MAX || nstate > INT32_MAX) return hipErrorInvalidValue;
-  hipError_t e;
-  if (nch > 0) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(f32c::f32_prep_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, f32c::PREP_BYTES)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(f32c::f32_prep_kernel, dim3((unsigned)(BH * nch)), dim3(f32c::NT), f32c::PREP_BYTES, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(f32c::f32_state_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, f32c::STATE_BYTES)) != hipSuccess)
-    return e;
-  hipLaunchKernelGGL(f32c::f32_state_kernel, dim3((unsigned)nstate), dim3(f32c::NT),
-                     f32c::STATE_BYTES, s, a);
-  return hipGetLastError();
+  if (!a.bf16 && a.dk == 128 && a.dv == 128) return f32c::launch_t<float, 128>(a, s);
+  if (a.bf16 && a.dk == 64 && a.dv == 64) return f32c::launch_t<bf16, 64>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kda

@@ -94,7 +94,12 @@ typedef enum {
  *                 (16-byte aligned), or NULL.  KDA_F32 with d = 128: required
  *                 (one 36992-float block per chunk of 64 tokens and sequence x
  *                 head, holding the chunk's Qg, W, Kb, U, P and decays;
- *                 KDA_ERR_WORKSPACE without it).  KDA_BF16 with d = 128: a
+ *                 KDA_ERR_WORKSPACE without it).  KDA_BF16 with d = 64: with
+ *                 the workspace (blocks of 20544 floats) the same fp32-operand
+ *                 path runs, whose error stays within the bf16 bounds on
+ *                 short sequences too; without it the one-launch kernel (bf16
+ *                 operands: at T <= 8 a head's rel L2 can reach 8e-3).
+ *                 KDA_BF16 with d = 128: a
  *                 nonzero size means that for these sizes a segmented
  *                 schedule is faster: each sequence
  *                 is cut into segments whose state maps S_end = M S_start + N

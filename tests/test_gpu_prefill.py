@@ -253,6 +253,42 @@ def test_short_sequences_seed_sweep(kda, pipeline, monkeypatch):
     print("worst per-head rel L2 of o by T:", {t: f"{v:.2e}" for t, v in worst.items()})
 
 
+def test_short_sequences_seed_sweep_d64(kda):
+    """bf16 at d = 64, T = 1 .. 8 over 32 seeds x 4 heads: with its workspace
+    (the binding passes it) the prefill takes fp32 matrix operands, which keep
+    these outputs inside the bf16 bounds (the one-launch kernel's bf16
+    operands reach 8e-3 per-head rel L2 at T = 2)."""
+    L = kda.lib()
+    assert L.kda_chunk_fwd_workspace_size(1, 8, 4, 64, 64, 1) == 1 * 4 * 1 * (4 * 64 * 64 + 64 * 64 + 64) * 4
+    worst = {}
+    for T in range(1, 9):
+        for seed in range(32):
+            cfg = W.Prefill("bf16_d64", 1, T, 4, 64, 64, torch.bfloat16, 0.05)
+            inp = W.prefill_inputs(cfg, device="cuda", seed=6000 + 97 * T + seed)
+            o, S = _run(kda, inp)
+            o_ref, S_ref = oracle_prefill(inp)
+            st = check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"d64 T{T} seed {seed}")
+            worst[T] = max(worst.get(T, 0.0), st["rel_l2_o"])
+    print("d64 worst per-head rel L2 of o by T:", {t: f"{v:.2e}" for t, v in worst.items()})
+
+
+def test_bf16_d64_without_workspace(kda):
+    """Without a workspace bf16 d = 64 runs the one-launch kernel (bf16
+    operands): same result within the bf16 bounds on an ordinary length."""
+    import ctypes
+    cfg = W.Prefill("bf16_d64", 2, 300, 3, 64, 64, torch.bfloat16, 0.05)
+    inp = W.prefill_inputs(cfg, device="cuda", seed=11)
+    o = torch.empty_like(inp["v"])
+    S = torch.empty(2, 3, 64, 64, dtype=torch.float32, device="cuda")
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = kda.lib().kda_chunk_fwd(p(inp["q"]), p(inp["k"]), p(inp["v"]), p(inp["g"]), p(inp["beta"]), p(inp["S0"]),
+                                 p(o), p(S), 2, 300, 3, 64, 64, 1, None, 0, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, "bf16 d64 one-launch")
+
+
 def _strong_decay_inputs(B, T, H, seed, burst=None):
     """The H16 T4K recipe, then a quarter of the channels forget fast (log-gate
     -1.2 .. -0.8 per step, 51 - 77 nats per 64-token chunk), everywhere or in

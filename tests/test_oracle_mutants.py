@@ -122,7 +122,11 @@ def _pins_fail(lib):
         fails.append("recall")
     # scalar gate (flag 1): one gate per token, g laid out [B, T, H]; a
     # single token against the matrix form with alpha I
-    gs = -np.abs(rng.standard_normal((1, 2, 1)))
+    # (the gates sit at the start of a longer buffer with defined values after
+    # them, so that a per-channel read past the two gates, as a planted
+    # mistake may do, reads known values rather than whatever memory follows)
+    gbuf = np.concatenate([-np.abs(rng.standard_normal(2)), np.full(2 * dk, -0.7)])
+    gs = gbuf[:2].reshape(1, 2, 1)
     q2 = rng.standard_normal((1, 2, 1, dk)); k2 = rng.standard_normal((1, 2, 1, dk))
     v2 = rng.standard_normal((1, 2, 1, dv)); b2 = np.full((1, 2, 1), 0.4)
     o, ST = _fwd(lib, q2, k2, v2, gs, b2, S0, flags=1)
