@@ -2380,6 +2380,66 @@ __device__ __forceinline__ void owner_state(const Ptr& p, const MH::F32 (&Df)[NT
   }
 }
 
+// The two products above for two states of the same chunk (the offset and
+// the transition of a segment, run together): each operand fragment read
+// from LDS once for both, one 32-index slab at a time (two states leave
+// fewer registers for reads ahead).
+__device__ __forceinline__ void rows_times_state2_b(const bf16* A, const floatx4 (&S)[2][DK / 16],
+                                                    const floatx4 (&S2)[2][DK / 16], floatx4 (&Dx)[2][4],
+                                                    floatx4 (&Dx2)[2][4], int lane) {
+  const int fl = frag_lane(lane);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    MB::F32 af[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) af[I] = ldc_b(A + fl + frag_off(I, ks));
+    KDA_READS_FIRST();
+    MB::F32 sf[2], sf2[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      sf[nt] = MB::frag32(S[nt][2 * ks], S[nt][2 * ks + 1]);
+      sf2[nt] = MB::frag32(S2[nt][2 * ks], S2[nt][2 * ks + 1]);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        Dx[nt][I] = MB::mma32(af[I], sf[nt], Dx[nt][I]);
+        Dx2[nt][I] = MB::mma32(af[I], sf2[nt], Dx2[nt][I]);
+      }
+  }
+}
+
+__device__ __forceinline__ void owner_state2(const Ptr& p, const MH::F32 (&Df)[2][2], const MH::F32 (&Df2)[2][2],
+                                             floatx4 (&S)[2][DK / 16], floatx4 (&S2)[2][DK / 16], int par,
+                                             int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    MH::F32 ka[DK / 32][2];
+#pragma unroll
+    for (int r2 = 0; r2 < DK / 32; ++r2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ka[r2][h] = ldc_h(p.KbT + (16 * (hf * DK / 32 + r2) + l16) * LDT + 32 * h + 8 * g4);
+    KDA_READS_FIRST();
+#pragma unroll
+    for (int r2 = 0; r2 < DK / 32; ++r2) {
+      const int rt = hf * DK / 32 + r2;
+      const floatx4 gm = *reinterpret_cast<const floatx4*>(p.gam + par * DK + 16 * rt + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        S[nt][rt] *= gm;
+        S[nt][rt] = MH::mma32(ka[r2][0], Df[nt][0], S[nt][rt]);
+        S[nt][rt] = MH::mma32(ka[r2][1], Df[nt][1], S[nt][rt]);
+        S2[nt][rt] *= gm;
+        S2[nt][rt] = MH::mma32(ka[r2][0], Df2[nt][0], S2[nt][rt]);
+        S2[nt][rt] = MH::mma32(ka[r2][1], Df2[nt][1], S2[nt][rt]);
+      }
+    }
+  }
+}
+
 // Phase 1, owners: the output tile straight to memory.  O is held transposed
 // (lane: token 16I + l16, tile columns 4g..4g+3 of both tiles), which in the
 // owner's column order are the 8 adjacent value columns col0 + 8g .. + 7.
@@ -2483,14 +2543,20 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   // the state runs: no P, no Qg S), values used unless vzero.
   // One pass: the whole sequence.  Segmented (nseg segments of seg_len
   // chunks): pass 1 runs segment 0 (its final state is segment 1's entry
-  // state) and, state only, for each segment s = 1 .. nseg-2 the offset N_s
-  // (from zero) and the transition M_s (from the identity, values zero) of
-  // S_end = M_s S_start + N_s; pass 3 runs segments 1 .. nseg-1 from their
-  // entry states, which the combine kernel has formed in between.
+  // state) and, state only, for each segment s = 1 .. nseg-2 in one
+  // workgroup the offset N_s (from zero) and the transition M_s (from the
+  // identity, values zero) of S_end = M_s S_start + N_s; pass 3 runs segments
+  // 1 .. nseg-1 from their entry states, which the combine kernel has formed
+  // in between.
   int head, c0 = 0, nchunks = (a.T + C - 1) / C;
   const float* s0p = nullptr;
   float* sTp = nullptr;
   bool ident = false, outp = true, vzero = false;
+  // a middle segment of the segmented schedule: its offset N_s (state from
+  // zero, into sTp) and its transition M_s (state from the identity with the
+  // values zeroed, into smp) in one run, state only
+  bool dual = false;
+  float* smp = nullptr;
   // packed sequences, segmented: this workgroup's segment (-1: the whole
   // sequence) and the sequence's first map slot
   int vsg = -1, vmap0 = 0;
@@ -2531,15 +2597,12 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         vsg = 0;
         s0p = S0h;
         sTp = vmap(1, 0);
-      } else if (k <= P - 2) {
+      } else {
         vsg = k;
         outp = false;
+        dual = true;
         sTp = vmap(k, 2);
-      } else {
-        vsg = k - (P - 2);
-        outp = false;
-        ident = vzero = true;
-        sTp = vmap(vsg, 1);
+        smp = vmap(k, 1);
       }
     } else {
       vsg = k + 1;
@@ -2547,25 +2610,21 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       if (vsg == P - 1) sTp = STh;
     }
   } else {
-    const int njobs = a.pass == 1 ? 2 * a.nseg - 3 : a.nseg - 1;
+    const int njobs = a.nseg - 1;
     head = blockIdx.x / njobs;
     const int job = blockIdx.x % njobs;
     if (head >= a.B * a.H) return;
     int sg;
     if (a.pass == 1) {
+      sg = job;
       if (job == 0) {
-        sg = 0;
         if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
         sTp = seg_mat(a.ws, head, a.nseg, 1, 0);
-      } else if (job <= a.nseg - 2) {
-        sg = job;
-        outp = false;
-        sTp = seg_mat(a.ws, head, a.nseg, sg, 2);
       } else {
-        sg = job - (a.nseg - 2);
         outp = false;
-        ident = vzero = true;
-        sTp = seg_mat(a.ws, head, a.nseg, sg, 1);
+        dual = true;
+        sTp = seg_mat(a.ws, head, a.nseg, sg, 2);
+        smp = seg_mat(a.ws, head, a.nseg, sg, 1);
       }
     } else {
       sg = job + 1;
@@ -2621,7 +2680,80 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   // the reference before the first chunk (buffer of chunk -1) is 0
   if (tid < DK) p.rho[2 * DK + tid] = 0.f;
 
-  if (wave < 4) {
+  if (!ST && dual && wave < 4) {
+    // ---------------------------------------------------- owners, two states
+    // N (from zero, with the values) and M (from the identity, values zero):
+    // the same chunk operands, so the workers' half of the work is shared;
+    // the owners' products read each operand fragment once for both states.
+    // The phases and barriers are those of a state-only run.
+    const int o = wave;
+    const int col0 = 32 * o;
+    floatx4 S[2][DK / 16], SM[2][DK / 16];
+    load_state_v(S, nullptr, false, col0, lane);
+    load_state_v(SM, nullptr, true, col0, lane);
+    floatx4 U[2][4];
+    Vec16 vr[4];
+    if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
+    __syncthreads();   // the workers' operand choice of the first chunk
+    for (int n = -1; n < nchunks; ++n) {
+      const bool nxt = n + 1 < nchunks;
+      p.sync(smem_raw);
+      // phase 1: V^T of chunk n+1 first (its registers are free during the
+      // products), then chunk n for both states (Delta_M = -W S_M)
+      if (nxt) owner_vt(p, vr, o, lane);
+      if (n >= 0) {
+        floatx4 UM[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int I = 0; I < 4; ++I) UM[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!ND) rows_times_state2_b(p.Wn, S, SM, U, UM, lane);
+        MH::F32 Df[2][2], DfM[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          Df[nt][0] = MH::frag32(U[nt][0], U[nt][1]);
+          Df[nt][1] = MH::frag32(U[nt][2], U[nt][3]);
+          DfM[nt][0] = MH::frag32(UM[nt][0], UM[nt][1]);
+          DfM[nt][1] = MH::frag32(UM[nt][2], UM[nt][3]);
+        }
+        owner_state2(p, Df, DfM, S, SM, n & 1, lane);
+      }
+      fetch_v(vr, a, bb, h, c0 + n + 2, o, lane);
+      p.sync(smem_raw);
+      // phase 2a: diagonal block o of L and its inverse (chunk n+1)
+      const bool f16m = (chunk_flags(p, (n + 1) & 1) & 1) != 0;
+      if (!ND && nxt) {
+        if (f16m)
+          solver_block<f16>(p, o, lane);
+        else
+          solver_block<bf16>(p, o, lane);
+      }
+      p.sync(smem_raw);
+      // phase 2b: both states move to the reference of chunk n+1 where it changed
+      const int fl = nxt ? chunk_flags(p, (n + 1) & 1) : 0;
+      if (fl & 2) {
+        state_rescale(S, p.rho + ((n + 1) % 3) * DK, p.rho + ((n + 3) % 3) * DK, lane);
+        state_rescale(SM, p.rho + ((n + 1) % 3) * DK, p.rho + ((n + 3) % 3) * DK, lane);
+      }
+      p.sync(smem_raw);
+      // phase 3: U of chunk n+1
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) U[nt][I] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (nxt) {
+        if constexpr (ND)
+          owner_v_rows(p, col0, U, lane);
+        else
+          owner_u(p, col0, U, lane);
+      }
+    }
+    // back from the last chunk's reference
+    state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
+    store_state_v(S, sTp, col0, lane);
+    state_rescale(SM, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
+    store_state_v(SM, smp, col0, lane);
+  } else if (wave < 4) {
     // ---------------------------------------------------------------- owners
     const int o = wave;
     const int col0 = 32 * o;
@@ -2954,7 +3086,8 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
 // segments; it is segmented if P_b >= 3.  Pass 1 runs the unsegmented
 // sequences whole (in the start order `order`, longest first if it is the
 // order kda_varlen_schedule writes) and then, per segmented sequence,
-// segment 0 and its 2 (P_b - 2) state maps; pass 3 runs segments 1 .. P_b-1.
+// segment 0 and the P_b - 2 runs that form the state maps of its middle
+// segments (two maps each); pass 3 runs segments 1 .. P_b-1.
 // Layout as VarlenPlan reads it.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
@@ -3002,7 +3135,7 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int* cu
   const bool whole_i = tid < N && nsg[b_i] < 3;
   int U, S1, S3, SL, NS;
   const int u_off = block_excl_scan(whole_i ? 1 : 0, buf, U);
-  const int s1_off = block_excl_scan(seg ? 2 * P - 3 : 0, buf, S1);
+  const int s1_off = block_excl_scan(seg ? P - 1 : 0, buf, S1);
   const int s3_off = block_excl_scan(seg ? P - 1 : 0, buf, S3);
   const int sl_off = block_excl_scan(seg ? P : 0, buf, SL);
   const int ns_off = block_excl_scan(seg ? 1 : 0, buf, NS);
@@ -3011,7 +3144,7 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int* cu
     mapbase[tid] = seg ? sl_off : -1;
     if (seg) {
       segseq[ns_off] = tid;
-      for (int k = 0; k < 2 * P - 3; ++k)
+      for (int k = 0; k < P - 1; ++k)
         if (U + s1_off + k < j1max) table1[U + s1_off + k] = make_int2(tid, k);
       for (int k = 0; k < P - 1; ++k)
         if (s3_off + k < j3max) table3[s3_off + k] = make_int2(tid, k);
@@ -3046,7 +3179,7 @@ VarlenSeg varlen_segments(int N, int T_total, int H, int cus) {
   if (L < 1 || nct < 2 * L + 1) return v;
   const int64_t ns = std::min<int64_t>(N, nct / (2 * L + 1));   // segmented sequences have > 2L chunks
   const int64_t slots = ncs / L + ns;                              // sum of their segment counts
-  const int64_t j1 = N + 2 * slots, j3 = slots;
+  const int64_t j1 = N + slots, j3 = slots;
   if (j1 * H > INT32_MAX || ns * H * segc::NSC > INT32_MAX) return v;
   v.L = (int)L;
   v.j1 = (int)j1;
@@ -3138,7 +3271,7 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
   PrefillArgs a1 = a, a3 = a;
   a1.pass = 1;
   a3.pass = 3;
-  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (2 * a.nseg - 3)), dim3(NT), bytes, s, a1);
+  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
   hipLaunchKernelGGL(seg_combine_kernel, dim3(BH * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
@@ -3166,11 +3299,11 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
 
 // Segments per sequence for the segmented schedule, from a cost model in
 // units of one chunk step of one workgroup: one pass takes N steps; nseg
-// segments of L chunks take (1 + 0.7 (rounds of pass 1 - 1) + rounds of
+// segments of L chunks take (1 + 0.9 (rounds of pass 1 - 1) + rounds of
 // pass 3) (L + 2) (pass 1's first round holds the full runs of segment 0,
-// its other rounds only state runs at about 0.7 of a full step; 2: pipeline
-// fill and state traffic per workgroup) plus about half a step per combine,
-// where a round is one workgroup per compute unit.  0 if one pass is
+// its other rounds only two-state runs at about 0.9 of a full step; 2:
+// pipeline fill and state traffic per workgroup) plus about half a step per
+// combine, where a round is one workgroup per compute unit.  0 if one pass is
 // cheaper.
 int prefill_segments(int BH, int T, int cus) {
   const int N = (T + C - 1) / C;
@@ -3180,8 +3313,8 @@ int prefill_segments(int BH, int T, int cus) {
   for (int P = 3; P <= 64; ++P) {
     const int L = (N + P - 1) / P, Pe = (N + L - 1) / L;
     if (Pe != P) continue;   // only counts that split into equal-length segments (bar the last)
-    const int r1 = (BH * (2 * P - 3) + cus - 1) / cus, r3 = (BH * (P - 1) + cus - 1) / cus;
-    const double cost = (1.0 + 0.7 * (r1 - 1) + r3) * (L + 2.0) + 0.5 * (P - 2);
+    const int r1 = (BH * (P - 1) + cus - 1) / cus, r3 = r1;
+    const double cost = (1.0 + 0.9 * (r1 - 1) + r3) * (L + 2.0) + 0.5 * (P - 2);
     if (cost < best) { best = cost; best_p = P; }
   }
   return best_p;
