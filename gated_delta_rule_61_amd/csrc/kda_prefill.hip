@@ -3171,10 +3171,11 @@ VarlenSeg varlen_segments(int N, int T_total, int H, int cus) {
     if (want < 3) return v;
     L = (nct + want - 1) / want;
   } else {
-    // segments of about one CU's share of the work; worth it only when one
-    // sequence can be three of them
+    // segments of about one CU's share of the work, so that a sequence
+    // holding all the tokens runs each pass in one round of workgroups
+    // ((P - 1) H <= CUs); worth it only when one sequence can be three of them
     if (cus <= 0) return v;
-    L = std::max<int64_t>(16, (ncs * H + cus - 1) / cus);
+    L = std::max<int64_t>(16, (ncs * H + cus + H - 1) / (cus + H));
   }
   if (L < 1 || nct < 2 * L + 1) return v;
   const int64_t ns = std::min<int64_t>(N, nct / (2 * L + 1));   // segmented sequences have > 2L chunks

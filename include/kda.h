@@ -228,7 +228,7 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  * kda_chunk_fwd_varlen_ws -- kda_chunk_fwd_varlen with a workspace of
  * kda_chunk_fwd_varlen_workspace_size() bytes (16-byte aligned): sequences
  * longer than about three CUs' share of the work (segments of
- * L = max(16, ceil((T_total/64 + N) H / CUs)) chunks) run segmented, as
+ * L = max(16, ceil((T_total/64 + N) H / (CUs + H))) chunks) run segmented, as
  * kda_chunk_fwd does with its workspace: the state maps S_end = M S_start + N
  * of their middle segments are formed in parallel and chained, then each
  * segment runs from its entry state ("...More Efficient" §IV: the recursion
