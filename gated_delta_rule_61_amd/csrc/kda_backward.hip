@@ -868,6 +868,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   // gamma . rowsum(S . dS), the chunk-end term of each channel: the diagonal
   // of S (gamma . dS)^T, wave w forming its diagonal tile (channels 16w..)
   floatx4 aSD = zero4();
+  // dbeta terms rowsum((A^T dDelta) . V) of the lane's rows mT[x] + 4 g4 + r,
+  // summed per lane over both halves (the 16-lane sums follow the loop)
+  floatx4 dvp[2] = {zero4(), zero4()};
 
   // Staging of a value half: S[:, J] and gamma . dS[:, J] as [j][c] rows,
   // V[:, J] and dO[:, J] (rows past nv zero).  The half's S (blocks
@@ -980,18 +983,19 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
     }
     // dV[:, J] = Diag(beta) A^T dDelta, staged row-major where X^T was (dead
-    // since Delta); dbeta += rowsum((A^T dDelta) . V)
+    // since Delta); dbeta += rowsum((A^T dDelta) . V).  The lane's V and beta
+    // of rows mT[x] + 4 g4 .. + 3 are one transpose read and one 16-byte read.
     if constexpr (!ND) {
       floatx4 xv[2] = {zero4(), zero4()};
       mm_zs<false, false, 2>(L.A, P64, mT, hDD, P64, 16 * jj, C, xv, lane);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
+        const bf16x4 vv = fr_tr(hV, P64, 16 * jj, mT[x] + 4 * g4, lane);
+        const floatx4 bt = *reinterpret_cast<const floatx4*>(L.beta + mT[x] + 4 * g4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = mT[x] + 4 * g4 + r;
-          const float p = sum16(xv[x][r] * (float)hV[t * P64 + 16 * jj + i]);
-          if (i == 0) dbp[wave * C + t] += p;
-          xv[x][r] *= L.beta[t];
+          dvp[x][r] += xv[x][r] * (float)vv[r];
+          xv[x][r] *= bt[r];
         }
         st_rm(hXT, P64, mT[x], 16 * jj, xv[x], lane);
       }
@@ -1007,6 +1011,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (4 * g4 + r == i) dgam[c0 + i] = aSD[r];
+  if constexpr (!ND) {
+    // (rows mT[x] + 4 g4 .. + 3 of this wave's partial-sum row; its other rows
+    // are still zero, and the later terms are added by this wave alone)
+    const int mT0[2] = {16 * (wave >> 2), 16 * ((wave >> 2) + 2)};
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      floatx4 sv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sum16(dvp[x][r]);
+      if (i == 0) *reinterpret_cast<floatx4*>(dbp + wave * C + mT0[x] + 4 * g4) = sv;
+    }
+  }
   // the assembly's inputs g, q, k (rows past nv zero), in flight during the
   // 64 x 64 products
   // (rows in range for every thread, zeroed past nv when stored)
@@ -1022,12 +1038,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   // fold dKb~ into dKd, keeping its column sums against Kd (chunk-end terms)
   float colsum = 0.f;   // sum over my rows of Kd . dKb~ for column c0 + i
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u) {
+    const bf16x4 kd4 = fr_tr(L.Kd, P128, c0, 16 * u + 4 * g4, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      colsum += (float)L.Kd[(16 * u + 4 * g4 + r) * P128 + c0 + i] * aKb[u][r];
+      colsum += (float)kd4[r] * aKb[u][r];
       aKd[u][r] += aKb[u][r];
     }
+  }
   __syncthreads();   // the half-loop buffers are dead from here
 
   bf16* qDW = reinterpret_cast<bf16*>(work + gr::Q_DW);
@@ -1037,9 +1055,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* qDL = reinterpret_cast<bf16*>(work + gr::Q_DL);
   bf16* qDG = reinterpret_cast<bf16*>(work + gr::Q_DG);
   // dW = -dDelta S^T (row-major); M with its diagonal moved out; zero fills
-  for (int e = tid; e < C * P64; e += NT) {
-    qM[e] = (bf16)0.f;
-    if constexpr (!ND) qDA[e] = (bf16)0.f;
+  // of the four 64 x 64 arrays whose upper blocks are never written
+  {
+    const Vec16 z = {{0u, 0u, 0u, 0u}};
+    for (int e = tid; e < C * P64 / 8; e += NT) {
+      *reinterpret_cast<Vec16*>(qM + 8 * e) = z;
+      if constexpr (!ND) {
+        *reinterpret_cast<Vec16*>(qDA + 8 * e) = z;
+        *reinterpret_cast<Vec16*>(qDL + 8 * e) = z;
+        *reinterpret_cast<Vec16*>(qDG + 8 * e) = z;
+      }
+    }
   }
   if constexpr (!ND) {
 #pragma unroll
@@ -1101,24 +1127,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       floatx4 y = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) y = MB::mma16(fr_tr(L.A, P64, 16 * u, 16 * ks + 4 * g4, lane), wf[ks], y);
-      // dKg += Diag(beta) Y; dbeta += rowsum(Y . Kg)
+      // aKg holds Y + dL Kd until both are in (then Diag(beta) and the
+      // dbeta term rowsum((Y + dL Kd) . Kg) follow)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * u + 4 * g4 + r;
-        aKg[u][r] += L.beta[t] * y[r];
-        const float p = sum16(y[r] * (float)L.Kg[t * P128 + c0 + i]);
-        if (i == 0) dbp[wave * C + t] += p;
-      }
+      for (int r = 0; r < 4; ++r) aKg[u][r] += y[r];
     }
   }
   if constexpr (!ND) {
   __syncthreads();
-  // dL = -StrictTril(A^T Z1); dG = Diag(beta) dL
-  for (int e = tid; e < C * P64; e += NT) {
-    qDL[e] = (bf16)0.f;
-    qDG[e] = (bf16)0.f;
-  }
-  __syncthreads();
+  // dL = -StrictTril(A^T Z1); dG = Diag(beta) dL (upper blocks zeroed above)
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int tq = wave + 8 * x;
@@ -1140,19 +1157,21 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
   }
   __syncthreads();
-  // dKg += Diag(beta) dL Kd (dbeta += rowsum(Kg . dL Kd)); dKd += dG^T Kg
-  {
-    floatx4 lk[4] = {zero4(), zero4(), zero4(), zero4()};
-    mm_zs<true, false, 4>(qDL, P64, mU, L.Kd, P128, c0, C, lk, lane);
+  // dKg = Diag(beta) (Y + dL Kd), dbeta += rowsum(Kg . (Y + dL Kd)); dKd += dG^T Kg
+  // (the lane's Kg and beta of rows 16 u + 4 g4 .. + 3: one transpose read and
+  // one 16-byte read; its four partial sums go to LDS in one store)
+  mm_zs<true, false, 4>(qDL, P64, mU, L.Kd, P128, c0, C, aKg, lane);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u) {
+    const bf16x4 kg4 = fr_tr(L.Kg, P128, c0, 16 * u + 4 * g4, lane);
+    const floatx4 bt = *reinterpret_cast<const floatx4*>(L.beta + 16 * u + 4 * g4);
+    floatx4 sv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * u + 4 * g4 + r;
-        aKg[u][r] += L.beta[t] * lk[u][r];
-        const float p = sum16(lk[u][r] * (float)L.Kg[t * P128 + c0 + i]);
-        if (i == 0) dbp[wave * C + t] += p;
-      }
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = sum16(aKg[u][r] * (float)kg4[r]);
+      aKg[u][r] *= bt[r];
+    }
+    if (i == 0) *reinterpret_cast<floatx4*>(dbp + wave * C + 16 * u + 4 * g4) += sv;
   }
   mm_zs<false, false, 4>(qDG, P64, mU, L.Kg, P128, c0, C, aKd, lane);
   }
