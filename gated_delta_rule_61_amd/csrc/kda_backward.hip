@@ -329,11 +329,10 @@ __device__ __forceinline__ SeqView seq_view(const BackwardArgs& a, int b, int h)
   return v;
 }
 
-// Workgroup -> (sequence, head, chunk) of the per-chunk kernels; false for a
-// slot no chunk uses (packed sequences: grid nslots * H, the sequence found by
-// binary search over the slot starts floor(cu[b] / C) + b).
-__device__ __forceinline__ bool chunk_of_block(const BackwardArgs& a, int& b, int& h, int& n) {
-  const int blk = blockIdx.x;
+// Block index -> (sequence, head, chunk) of the per-chunk kernels; false for
+// a slot no chunk uses (packed sequences: nslots * H blocks, the sequence
+// found by binary search over the slot starts floor(cu[b] / C) + b).
+__device__ __forceinline__ bool chunk_of_block(const BackwardArgs& a, int blk, int& b, int& h, int& n) {
   if (!a.cu_seqlens) {
     const int N = (a.T + C - 1) / C;
     const int bh = blk / N;
@@ -365,7 +364,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BackwardArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b, h, n;
-  if (!chunk_of_block(a, b, h, n)) return;
+  if (!chunk_of_block(a, blockIdx.x, b, h, n)) return;
   const SeqView sv = seq_view(a, b, h);
   bf16* X = reinterpret_cast<bf16*>(sm + pr::O_X);
   bf16* Kd = reinterpret_cast<bf16*>(sm + pr::O_KD);
@@ -817,10 +816,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // persistent: the workgroup takes blocks blockIdx.x, + gridDim.x, ... (the
+  // unused slots of packed sequences skipped) and loads the operands of its
+  // next chunk during the current chunk's assembly
+  const int nblk = a.cu_seqlens ? a.nslots * a.H : a.B * a.H * ((a.T + C - 1) / C);
   int b, h, n;
-  if (!chunk_of_block(a, b, h, n)) return;
-  const SeqView sv = seq_view(a, b, h);
-  const int64_t bi = sv.idx0 + (int64_t)n * sv.istride;   // this chunk's block
+  int vb = blockIdx.x;
+  while (vb < nblk && !chunk_of_block(a, vb, b, h, n)) vb += gridDim.x;
+  if (vb >= nblk) return;
   const Basics L = basics(sm, gr::O_KG, gr::O_KD, gr::O_QG, gr::O_A, gr::O_PT, gr::O_BETA, gr::O_GAM, gr::O_QK);
   float* dgam = reinterpret_cast<float*>(sm + gr::O_DGAM);
   float* md = reinterpret_cast<float*>(sm + gr::O_MD);
@@ -831,23 +834,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   const bf16* g = reinterpret_cast<const bf16*>(a.g);
   const bf16* v = reinterpret_cast<const bf16*>(a.v);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
+  // block index and rows of a chunk
+  auto locate = [&](int b_, int h_, int n_, int64_t& bi_, Chunk& c_) {
+    const SeqView sv = seq_view(a, b_, h_);
+    bi_ = sv.idx0 + (int64_t)n_ * sv.istride;
+    c_.row0 = sv.row0 + (int64_t)n_ * C * a.H;
+    c_.nv = min(C, sv.len - n_ * C);
+    c_.rstride = a.H * D;
+  };
+  int64_t bi;
   Chunk c;
-  c.row0 = sv.row0 + (int64_t)n * C * a.H;
-  c.nv = min(C, sv.len - n * C);
-  c.rstride = a.H * D;
-  const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + bi * D * D;      // fragment order
-  const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + bi * D * D;   // 16 x 16 tiles
-
-  ChunkOps ops;
-  ops_issue(ops, chunk_mats(a, bi), tid);
-
-  // persistent accumulators
+  locate(b, h, n, bi, c);
   const int c0 = 16 * wave;     // my channel block
-  floatx4 aQg[4], aKd[4], aKb[4], aW[4], aKg[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) aQg[u] = aKd[u] = aKb[u] = aW[u] = aKg[u] = zero4();
-  // lower [t][t'] tiles: tile index q = wave, wave + 8 (< 10)
-  floatx4 aM[2] = {zero4(), zero4()}, aA[2] = {zero4(), zero4()};
   auto lower_tile = [](int tq, int& I, int& J) {
     int cc = 0;
     I = J = 0;
@@ -858,6 +856,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       }
   };
 
+  // lower [t][t'] tiles: tile index q = wave, wave + 8 (< 10)
   bf16* hS = reinterpret_cast<bf16*>(work + gr::H_S);
   bf16* hDSG = reinterpret_cast<bf16*>(work + gr::H_DSG);
   bf16* hV = reinterpret_cast<bf16*>(work + gr::H_V);
@@ -865,12 +864,6 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   bf16* hD = ND ? hV : reinterpret_cast<bf16*>(work + gr::H_D);   // Delta (= V without the delta rule)
   bf16* hDD = reinterpret_cast<bf16*>(work + gr::H_DD);
   bf16* hXT = reinterpret_cast<bf16*>(work + gr::H_XT);
-  // gamma . rowsum(S . dS), the chunk-end term of each channel: the diagonal
-  // of S (gamma . dS)^T, wave w forming its diagonal tile (channels 16w..)
-  floatx4 aSD = zero4();
-  // dbeta terms rowsum((A^T dDelta) . V) of the lane's rows mT[x] + 4 g4 + r,
-  // summed per lane over both halves (the 16-lane sums follow the loop)
-  floatx4 dvp[2] = {zero4(), zero4()};
 
   // Staging of a value half: S[:, J] and gamma . dS[:, J] as [j][c] rows,
   // V[:, J] and dO[:, J] (rows past nv zero).  The half's S (blocks
@@ -879,9 +872,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
   // 16 bytes at 8 p of it, channels 8 (p % 2) .. + 8 of row p / 2 % 16 of
   // block p / 32.  The loads of half 0 are issued with the chunk's operand
   // block, those of half 1 during half 0's products.
-  const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
   Vec16 xs[2], xd[2], xv, xo;
-  auto half_issue = [&](int jh) {
+  auto half_issue = [&](int64_t bi_, const Chunk& c_, int jh, int tid) {
+    const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
+    const bf16* Sn = reinterpret_cast<const bf16*>(a.states) + bi_ * D * D;      // fragment order
+    const bf16* dSn = reinterpret_cast<const bf16*>(a.adjoints) + bi_ * D * D;   // 16 x 16 tiles
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int pc = tid + u * NT;
@@ -890,11 +885,33 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
     // (every thread loads a row in range, rows past nv are zeroed when
     // stored: a load under a branch made the compiler wait for it at the join)
-    const int tr = min(tv, c.nv - 1);
-    xv = ldg16(v + (c.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
-    xo = ldg16(dO + (c.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
+    const int tr = min(tv, c_.nv - 1);
+    xv = ldg16(v + (c_.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
+    xo = ldg16(dO + (c_.row0 + (int64_t)tr * a.H) * D + 64 * jh + xv0);
   };
-  half_issue(0);
+  ChunkOps ops;
+  ops_issue(ops, chunk_mats(a, bi), tid);
+  half_issue(bi, c, 0, tid);
+
+  for (;;) {
+  // (the lane index is made opaque here so that the per-lane addresses are
+  // formed inside the loop: hoisted out of it, they held enough registers
+  // across the whole loop to force spills)
+  int tid_o = threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  const int tid = tid_o, lane = tid & 63, g4 = lane >> 4, i = lane & 15;
+  const int tv = tid >> 3, xv0 = 8 * (tid & 7);   // V, dO: one piece per thread
+  // per-chunk accumulators
+  floatx4 aQg[4], aKd[4], aKb[4], aW[4], aKg[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) aQg[u] = aKd[u] = aKb[u] = aW[u] = aKg[u] = zero4();
+  floatx4 aM[2] = {zero4(), zero4()}, aA[2] = {zero4(), zero4()};
+  // gamma . rowsum(S . dS), the chunk-end term of each channel: the diagonal
+  // of S (gamma . dS)^T, wave w forming its diagonal tile (channels 16w..)
+  floatx4 aSD = zero4();
+  // dbeta terms rowsum((A^T dDelta) . V) of the lane's rows mT[x] + 4 g4 + r,
+  // summed per lane over both halves (the 16-lane sums follow the loop)
+  floatx4 dvp[2] = {zero4(), zero4()};
   ops_commit(ops, L, tid);
   for (int e = tid; e < 8 * C; e += NT) dbp[e] = 0.f;
   if (tid < D) dgam[tid] = 0.f;
@@ -957,7 +974,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     }
     __syncthreads();
     // [t][c] products over this half's value columns
-    if (jh == 0) half_issue(1);
+    if (jh == 0) half_issue(bi, c, 1, tid);
     // (dO S^T, Delta (g.dS)^T, dDelta S^T: the S and g.dS fragments of a step
     // serve all four row tiles; the diagonal tile of S (g.dS)^T alongside)
     for (int k = 0; k < 64; k += 32) {
@@ -1196,6 +1213,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
       *reinterpret_cast<Vec16*>(zk + t * P128 + x0) = keep_or_zero(xk[u], in);
     }
   }
+  // the next chunk's operand block and first value half, in flight during
+  // the assembly (the last chunk loads its own again: the loads are never
+  // under a branch)
+  int nvb = vb + gridDim.x, nb = b, nh = h, nn = n;
+  while (nvb < nblk && !chunk_of_block(a, nvb, nb, nh, nn)) nvb += gridDim.x;
+  int64_t nbi = bi;
+  Chunk nc = c;
+  if (nvb < nblk) locate(nb, nh, nn, nbi, nc);
+  ops_issue(ops, chunk_mats(a, nbi), tid);
+  half_issue(nbi, nc, 0, tid);
   __syncthreads();
   scan_cols<false>(bs, nullptr, tid);
   // per element: dq, dk and db (db overwrites b in place).  The lane's four
@@ -1253,6 +1280,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BackwardArgs a) {
     float s = 0.f;
     for (int w = 0; w < NT / 64; ++w) s += dbp[w * C + tid];
     reinterpret_cast<bf16*>(a.dbeta)[c.row0 + (int64_t)tid * a.H] = (bf16)s;
+  }
+  if (nvb >= nblk) break;
+  vb = nvb;
+  b = nb;
+  h = nh;
+  n = nn;
+  bi = nbi;
+  c = nc;
+  __syncthreads();   // this chunk's last LDS reads are done before the next commit
   }
 }
 
@@ -1349,9 +1385,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (N == 0) return hipSuccess;
   // 4. per-chunk gradients
+  // (persistent: one workgroup per compute unit, which its LDS allows anyway)
   auto grad = a.variant ? bwd::bwd_grad_kernel<kVarNoDelta> : bwd::bwd_grad_kernel<0>;
   if ((e = set_lds(grad, bwd::gr::BYTES)) != hipSuccess) return e;
-  hipLaunchKernelGGL(grad, dim3(nblk), dim3(bwd::NT), bwd::gr::BYTES, s, a);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    cus = nblk;
+  hipLaunchKernelGGL(grad, dim3(nblk < cus ? nblk : cus), dim3(bwd::NT), bwd::gr::BYTES, s, a);
   return hipGetLastError();
 }
 
