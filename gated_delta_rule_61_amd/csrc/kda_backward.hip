@@ -604,14 +604,14 @@ constexpr int O_QG = O_KD + C * P128 * 2;
 constexpr int O_A = O_QG + C * P128 * 2;
 constexpr int O_PT = O_A + C * P64 * 2;
 constexpr int O_DO = O_PT + C * P64 * 2;          // dO row-major [64][P128]
-constexpr int O_DSG = O_DO + C * P128 * 2;        // (gamma . dS)^T [128 j][P128]; later E^T [128 j][P64]
-constexpr int O_BS = O_DSG + D * P128 * 2;        // gate scratch; later dDelta^T [128 j][P64]
-constexpr int SZ_BS = (C * PB + 4 * D) * 4;
-constexpr int O_BETA = O_BS + SZ_BS;
+constexpr int O_DSG = O_DO + C * P128 * 2;        // (gamma . dS)^T [128 j][P128]
+constexpr int O_DDT = O_DSG + D * P128 * 2;       // dDelta^T [128 j][P64]
+constexpr int O_ET = O_DDT + D * P64 * 2;         // E^T [128 j][P64]
+constexpr int O_BETA = O_ET + D * P64 * 2;
 constexpr int O_GAM = O_BETA + C * 4;
-constexpr int O_QK = O_GAM + D * 4;
+constexpr int O_GAMN = O_GAM + D * 4;             // gamma of the next chunk (read before its commit)
+constexpr int O_QK = O_GAMN + D * 4;
 constexpr int BYTES = O_QK + C * 4;
-static_assert(D * P64 * 2 <= SZ_BS, "dDelta^T inside the gate scratch");
 static_assert(O_KD == O_KG + C * P128 * 2 && O_QG == O_KD + C * P128 * 2 && O_PT == O_A + C * P64 * 2,
               "load_chunk layout");
 static_assert(BYTES <= 160 * 1024, "LDS");
@@ -648,12 +648,9 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
   const Basics L = basics(sm, ch::O_KG, ch::O_KD, ch::O_QG, ch::O_A, ch::O_PT, ch::O_BETA, ch::O_GAM, ch::O_QK);
   bf16* sDO = reinterpret_cast<bf16*>(sm + ch::O_DO);
   bf16* sDSG = reinterpret_cast<bf16*>(sm + ch::O_DSG);
-  bf16* sET = sDSG;
-  float* bs = reinterpret_cast<float*>(sm + ch::O_BS);
-  bf16* sDDT = reinterpret_cast<bf16*>(sm + ch::O_BS);
-  const bf16* q = reinterpret_cast<const bf16*>(a.q);
-  const bf16* k = reinterpret_cast<const bf16*>(a.k);
-  const bf16* g = reinterpret_cast<const bf16*>(a.g);
+  bf16* sDDT = reinterpret_cast<bf16*>(sm + ch::O_DDT);
+  bf16* sET = reinterpret_cast<bf16*>(sm + ch::O_ET);
+  float* gamN = reinterpret_cast<float*>(sm + ch::O_GAMN);
   const bf16* dO = reinterpret_cast<const bf16*>(a.dO);
 
   const int jt = wave;   // my dS tiles: (ct, jt), ct = 0..7
@@ -672,19 +669,11 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
     return c;
   };
   auto blk = [&](int n) { return sv.idx0 + (int64_t)n * sv.istride; };
-  ChainOps ops;
-  if (N > 0) {
-    chain_issue<0>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
-    chain_issue<1>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
-    chain_issue<2>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
-    chain_commit(ops, L, sDO, tid);
-    __syncthreads();
-  }
-  for (int n = N - 1; n >= 0; --n) {
-    // chunk-end adjoint of this chunk (bf16, in 16 x 16 tiles: tile (j/16, c/16)
-    // at position 8 (j/16) + c/16, [j%16][c%16] inside): one wave store
-    // writes one whole tile, 512 contiguous bytes
-    bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + blk(n) * D * D;
+  // chunk-end adjoint of chunk nn (bf16, in 16 x 16 tiles: tile (j/16, c/16)
+  // at position 8 (j/16) + c/16, [j%16][c%16] inside): one wave store writes
+  // one whole tile, 512 contiguous bytes
+  auto store_adj = [&](int nn) {
+    bf16* adj = reinterpret_cast<bf16*>(a.adjoints) + blk(nn) * D * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       bf16x4 x;
@@ -692,25 +681,44 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int r = 0; r < 4; ++r) x[r] = (bf16)dS[u][r];
       *reinterpret_cast<bf16x4*>(adj + (8 * jt + u) * 256 + 16 * i + 4 * g4) = x;
     }
-    // the next chunk's operands, in flight during this chunk's products
-    const Chunk cn = chunk_of(n > 0 ? n - 1 : 0);
-    const bf16* Amn = chunk_mats(a, blk(n > 0 ? n - 1 : 0));
-    if (n > 0) chain_issue<0>(ops, Amn, dO, cn, a.H, tid);
-    // (gamma . dS)^T (this chunk's operands are in LDS)
+  };
+  // (gamma . dS)^T for the chunk whose decay gm holds
+  auto stage_gds = [&](const float* gm) {
     if constexpr (!ND) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
+        const floatx4 g4v = *reinterpret_cast<const floatx4*>(gm + 16 * u + 4 * g4);
         floatx4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * L.gam[16 * u + 4 * g4 + r];
+        for (int r = 0; r < 4; ++r) v[r] = dS[u][r] * g4v[r];
         st_tr(sDSG, P128, 16 * u, 16 * jt, v, lane);
       }
     }
+  };
+  // Four phases per chunk: dDelta; E; the dS update with the next chunk's
+  // adjoint staged; the next chunk's operands from registers to LDS.  The
+  // next chunk's loads are issued in three parts (after the commit, then at
+  // the start of the first two phases) and its decay goes to LDS one phase
+  // before the commit, for the staging.
+  ChainOps ops;
+  if (N > 0) {
+    chain_issue<0>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<1>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
+    chain_issue<2>(ops, chunk_mats(a, blk(N - 1)), dO, chunk_of(N - 1), a.H, tid);
+    chain_commit(ops, L, sDO, tid);
     __syncthreads();
-    if (n > 0) chain_issue<1>(ops, Amn, dO, cn, a.H, tid);
-    // dDelta = P^T dO + Kd (gamma . dS), stored transposed (over the gate
-    // scratch); wave w: the four token tiles of value-column tile w, which
-    // share their column operands
+    store_adj(N - 1);
+    stage_gds(L.gam);
+    if (N > 1) chain_issue<0>(ops, chunk_mats(a, blk(N - 2)), dO, chunk_of(N - 2), a.H, tid);
+    __syncthreads();
+  }
+  for (int n = N - 1; n >= 0; --n) {
+    const bool more = n > 0;
+    const Chunk cn = chunk_of(more ? n - 1 : 0);
+    const bf16* Amn = chunk_mats(a, blk(more ? n - 1 : 0));
+    if (more) chain_issue<1>(ops, Amn, dO, cn, a.H, tid);
+    // dDelta = P^T dO + Kd (gamma . dS), stored transposed; wave w: the four
+    // token tiles of value-column tile w, which share their column operands
     const int mT[4] = {0, 16, 32, 48};
     if constexpr (!ND) {
       floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -720,18 +728,21 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
       for (int x = 0; x < 4; ++x) st_tr(sDDT, P64, mT[x], 16 * jt, acc[x], lane);
     }
     __syncthreads();
-    if (n > 0) chain_issue<2>(ops, Amn, dO, cn, a.H, tid);
-    // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed (over (gamma . dS)^T)
+    if (more) chain_issue<2>(ops, Amn, dO, cn, a.H, tid);
+    // E = A'^T dDelta = Diag(beta) A^T dDelta, stored transposed
     if constexpr (!ND) {
       floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
       mm_zs<false, true, 4>(L.A, P64, mT, sDDT, P64, 16 * jt, C, acc, lane);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
+        const floatx4 bt = *reinterpret_cast<const floatx4*>(L.beta + mT[x] + 4 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[x][r] *= L.beta[mT[x] + 4 * g4 + r];
+        for (int r = 0; r < 4; ++r) acc[x][r] *= bt[r];
         st_tr(sET, P64, mT[x], 16 * jt, acc[x], lane);
       }
     }
+    // the next chunk's decay (its load was issued two phases ago)
+    if (more && tid < D) gamN[tid] = ops.k.gb;
     __syncthreads();
     // dS <- gamma . dS + Qg^T dO - Kg^T E, in two groups of four channel tiles
 #pragma unroll
@@ -743,13 +754,21 @@ __global__ __launch_bounds__(NT) void bwd_chain_kernel(BackwardArgs a) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int u = 4 * hf + x;
+        const floatx4 g4v = *reinterpret_cast<const floatx4*>(L.gam + 16 * u + 4 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dS[u][r] = L.gam[16 * u + 4 * g4 + r] * dS[u][r] + p[x][r] - m[x][r];
+        for (int r = 0; r < 4; ++r) dS[u][r] = g4v[r] * dS[u][r] + p[x][r] - m[x][r];
       }
     }
+    // the previous chunk's end adjoint: to memory and staged with its decay
+    // ((gamma . dS)^T was last read by this chunk's dDelta)
+    if (more) {
+      store_adj(n - 1);
+      stage_gds(gamN);
+    }
     __syncthreads();
-    if (n > 0) {
+    if (more) {
       chain_commit(ops, L, sDO, tid);
+      if (n > 1) chain_issue<0>(ops, chunk_mats(a, blk(n - 2)), dO, chunk_of(n - 2), a.H, tid);
       __syncthreads();
     }
   }
