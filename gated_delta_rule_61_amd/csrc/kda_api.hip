@@ -25,6 +25,21 @@ int hip_status(hipError_t e) {
   return KDA_ERR_HIP;
 }
 
+// KDA_SYNC_DEBUG set and not "0" (read on every call): an entry point waits
+// for its stream after its launches and reports a failure of its kernels
+// there, as KDA_ERR_HIP, instead of leaving it to a later call.
+bool sync_debug() {
+  const char* e = getenv("KDA_SYNC_DEBUG");
+  return e && e[0] && e[0] != '0';
+}
+int finish(hipError_t e, void* stream) {
+  if (e == hipSuccess && sync_debug()) {
+    e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  return hip_status(e);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
@@ -242,14 +257,14 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
       KDA_REQUIRE(aligned16(workspace), KDA_ERR_ALIGN);
       a.ws = static_cast<float*>(workspace);
     }
-    return hip_status(kda::launch_prefill_f32(a, (hipStream_t)stream));
+    return finish(kda::launch_prefill_f32(a, (hipStream_t)stream), stream);
   }
   if (f32_ops_d64(d_k, dtype, flags) && T > 0 && workspace && aligned16(workspace) &&
       workspace_bytes >= kda::prefill_f32_workspace(B * H, T, d_k)) {
     // bf16 at d = 64 with its workspace: fp32 operands
     kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 1, 0, 0};
     a.ws = static_cast<float*>(workspace);
-    return hip_status(kda::launch_prefill_f32(a, (hipStream_t)stream));
+    return finish(kda::launch_prefill_f32(a, (hipStream_t)stream), stream);
   }
   // (the variants run on the pipelined kernel whatever the schedule overrides say)
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, dtype == KDA_BF16,
@@ -263,7 +278,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
     a.seg_len = kda::prefill_segment_len(T, nseg);
     a.ws = static_cast<float*>(workspace);
   }
-  return hip_status(kda::launch_fused(a, (hipStream_t)stream));
+  return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
 }
 
 int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -294,7 +309,7 @@ int kda_varlen_schedule(const int32_t* cu_seqlens, int N, int T_total, int32_t* 
   KDA_REQUIRE(cu_seqlens && seq_order, KDA_ERR_NULL);
   KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0 && (reinterpret_cast<uintptr_t>(seq_order) & 3u) == 0,
               KDA_ERR_ALIGN);
-  return hip_status(kda::launch_varlen_schedule(cu_seqlens, N, T_total, seq_order, (hipStream_t)stream));
+  return finish(kda::launch_varlen_schedule(cu_seqlens, N, T_total, seq_order, (hipStream_t)stream), stream);
 }
 
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -342,7 +357,7 @@ int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const v
     a.plan_j3 = vs.j3;
     a.plan_ns = vs.ns;
   }
-  return hip_status(kda::launch_fused(a, (hipStream_t)stream));
+  return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
 }
 
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
@@ -384,7 +399,7 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
     // fp32, or d = 64: the token recurrence's reverse mode
     kda::BackwardArgs a{q, k, v, g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg, nd ? nullptr : dbeta, dS0,
                         B, T, H, nullptr, nullptr, nullptr, nullptr, flags, nullptr, 0};
-    return hip_status(kda::launch_backward_tok(a, d_k, dtype == KDA_BF16, workspace, (hipStream_t)stream));
+    return finish(kda::launch_backward_tok(a, d_k, dtype == KDA_BF16, workspace, (hipStream_t)stream), stream);
   }
   // workspace: chunk states, chunk-end adjoints (bf16 d_k x d_v each), the
   // per-chunk operand blocks; then (scalar gate) the broadcast gate and the
@@ -402,8 +417,8 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   hipError_t e;
   if (sg && T > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);
   if ((e = kda::launch_backward(a, s)) != hipSuccess) return hip_status(e);
-  if (sg && T > 0) return hip_status(kda::launch_gate_reduce(dg32, dg, rows, s));
-  return KDA_OK;
+  if (sg && T > 0) return finish(kda::launch_gate_reduce(dg32, dg, rows, s), stream);
+  return finish(hipSuccess, stream);
 }
 
 size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v, int dtype, int flags) {
@@ -454,8 +469,8 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
   hipError_t e;
   if (sg && T_total > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);
   if ((e = kda::launch_backward(a, s)) != hipSuccess) return hip_status(e);
-  if (sg && T_total > 0) return hip_status(kda::launch_gate_reduce(dg32, dg, rows, s));
-  return KDA_OK;
+  if (sg && T_total > 0) return finish(kda::launch_gate_reduce(dg32, dg, rows, s), stream);
+  return finish(hipSuccess, stream);
 }
 
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta, const float* S0,
@@ -495,7 +510,7 @@ int kda_chunk_fwd_staged(const void* q, const void* k, const void* v, const void
   if (e == hipSuccess) e = kda::launch_stage_ut(a, s);
   if (e == hipSuccess) e = kda::launch_stage_state(a, s);
   if (e == hipSuccess) e = kda::launch_stage_output(a, s);
-  return hip_status(e);
+  return finish(e, stream);
 }
 
 int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k, int dtype, void* stream) {
@@ -506,7 +521,7 @@ int kda_stage_cumsum(const void* g, float* b, int B, int T, int H, int d_k, int 
   KDA_REQUIRE(aligned16(g) && aligned16(b), KDA_ERR_ALIGN);
   kda::StageArgs a{};
   a.g = g; a.b = b; a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_k; a.bf16 = dtype == KDA_BF16;
-  return hip_status(kda::launch_stage_cumsum(a, (hipStream_t)stream));
+  return finish(kda::launch_stage_cumsum(a, (hipStream_t)stream), stream);
 }
 
 int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b, float* W, float* U, int B,
@@ -519,7 +534,7 @@ int kda_stage_ut(const void* k, const void* v, const void* beta, const float* b,
   kda::StageArgs a{};
   a.k = k; a.v = v; a.beta = beta; a.b = const_cast<float*>(b); a.W = W; a.U = U;
   a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
-  return hip_status(kda::launch_stage_ut(a, (hipStream_t)stream));
+  return finish(kda::launch_stage_ut(a, (hipStream_t)stream), stream);
 }
 
 int kda_stage_state(const void* k, const float* b, const float* W, const float* U, const float* S0, float* Delta,
@@ -537,7 +552,7 @@ int kda_stage_state(const void* k, const float* b, const float* W, const float* 
   a.k = k; a.b = const_cast<float*>(b); a.W = const_cast<float*>(W); a.U = const_cast<float*>(U);
   a.S0 = S0; a.Delta = Delta; a.S_chunks = S_chunks; a.S_T = S_T;
   a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
-  return hip_status(kda::launch_stage_state(a, (hipStream_t)stream));
+  return finish(kda::launch_stage_state(a, (hipStream_t)stream), stream);
 }
 
 int kda_stage_output(const void* q, const void* k, const float* b, const float* Delta, const float* S_chunks,
@@ -552,7 +567,7 @@ int kda_stage_output(const void* q, const void* k, const float* b, const float* 
   a.q = q; a.k = k; a.b = const_cast<float*>(b); a.Delta = const_cast<float*>(Delta);
   a.S_chunks = const_cast<float*>(S_chunks); a.o = o;
   a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
-  return hip_status(kda::launch_stage_output(a, (hipStream_t)stream));
+  return finish(kda::launch_stage_output(a, (hipStream_t)stream), stream);
 }
 
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* S,
@@ -572,7 +587,7 @@ int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const voi
   KDA_REQUIRE(aligned16(S), KDA_ERR_ALIGN);
   kda::DecodeArgs a{q, k, v, g, beta, S, o, N, H, d_k, d_v, dtype == KDA_BF16};
   a.variant = flags;
-  return hip_status(kda::launch_decode(a, (hipStream_t)stream));
+  return finish(kda::launch_decode(a, (hipStream_t)stream), stream);
 }
 
 }  // extern "C"

@@ -51,7 +51,12 @@
  *
  * Return values: KDA_OK (0) or a negative kda_status.  No C++ exception
  * crosses this interface.  On KDA_ERR_HIP the HIP error of the failing call
- * is kept per thread; kda_status_string(KDA_ERR_HIP) names it.
+ * is kept per thread; kda_status_string(KDA_ERR_HIP) names it.  Kernels run
+ * asynchronously, so a fault inside one surfaces at a later synchronisation;
+ * with the environment variable KDA_SYNC_DEBUG set (and not "0", read on
+ * every call) each entry point that launches work waits for its stream
+ * before it returns and reports such a failure itself, as KDA_ERR_HIP
+ * (debugging only: it serialises the caller with the GPU).
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -55,6 +55,16 @@ def _fwd(L, **kw):
                            p(a["ST"]), a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], None, 0, None)
 
 
+def test_sync_debug_leaves_validation_alone(L, monkeypatch):
+    """KDA_SYNC_DEBUG only adds a wait after launches: argument errors are
+    still reported before anything is launched or waited for."""
+    monkeypatch.setenv("KDA_SYNC_DEBUG", "1")
+    assert _fwd(L, q=None) == -1
+    assert _fwd(L, dk=96, dv=96) == -2
+    p = ctypes.c_void_p(16)
+    assert L.kda_recurrent_step(p, p, p, p, p, None, p, 4, 2, 128, 128, 1, None) == -1
+
+
 def test_prefill_validation(L):
     # fake aligned addresses: validation must fail before any launch
     assert _fwd(L, q=None) == -1
