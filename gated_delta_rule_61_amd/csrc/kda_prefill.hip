@@ -3040,21 +3040,32 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
       *reinterpret_cast<floatx4*>(Sl + r * LDS_S + c4) = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
     }
   }
-  if (nseg > 2) {
-    load_m(1);
-    store_m(Mb);
-  }
-  __syncthreads();
-  for (int sg = 1; sg + 1 < nseg; ++sg) {
-    const float* Ml = Mb + ((sg - 1) & 1) * D * LDS_M;
-    const bool more = sg + 2 < nseg;
-    if (more) load_m(sg + 1);
-    const float* Nm = mat(sg, 2);
-    floatx4 acc[2];
+  // N_s of the lane's eight entries (the accumulator's start)
+  floatx4 nr[2];
+  auto load_n = [&](int s) {
+    const float* Nm = mat(s, 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
+      for (int jj = 0; jj < 4; ++jj) nr[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
+  };
+  if (nseg > 2) {
+    load_m(1);
+    store_m(Mb);
+    load_n(1);
+  }
+  __syncthreads();
+  // Step s: S_{s+1} = M_s S_s + N_s.  M_{s+1} and N_{s+1} are loaded during
+  // the products (in that order, after N_s is in the accumulators: loads
+  // complete in order, so a wait for N_s issued after them would also wait
+  // for M_{s+1}); the last step reloads its own maps, so that no load is
+  // under a branch.
+  for (int sg = 1; sg + 1 < nseg; ++sg) {
+    const float* Ml = Mb + ((sg - 1) & 1) * D * LDS_M;
+    const int nx = min(sg + 1, nseg - 2);
+    floatx4 acc[2] = {nr[0], nr[1]};
+    load_m(nx);
+    load_n(nx);
 #pragma unroll 8
     for (int kb = 0; kb < D / 4; ++kb) {
       const float bv = Sl[(4 * kb + g4) * LDS_S + l16];
@@ -3074,7 +3085,7 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
         Sl[r * LDS_S + l16] = acc[u][jj];
         dst[r * D + col0 + l16] = acc[u][jj];
       }
-    if (more) store_m(Mb + (sg & 1) * D * LDS_M);
+    store_m(Mb + (sg & 1) * D * LDS_M);   // (unread after the last step)
     __syncthreads();
   }
 }
