@@ -16,7 +16,9 @@ no delta rule, or both) on the same shapes; the default is KDA itself.
 variable-length sequences (geometric lengths, mean 1024, seeded) through
 kda_varlen_schedule + kda_chunk_fwd_varlen.
 After the step loop (KDA only) the line also carries the backward on the
-B8 H32 T8192 workload, the two other bf16 prefill workloads timed alone
+B8 H32 T8192 workload, a training step on it (the forward that keeps the
+chunk states, then the backward on them), the two other bf16 prefill
+workloads timed alone
 (B1 H16 T4096 with S0, the cache evicted before each call; B1 H32 T131072
 with slow forgetting, segmented schedule) and a device-to-device copy as
 the achievable-bandwidth reference.
@@ -247,6 +249,40 @@ def measure_backward(kda, W, torch, pcfg, inp, args, stream):
                          "kernel": "the whole backward: state pass (fused_pipe_kernel<4>) + bwd_prep_kernel + bwd_chain_kernel + bwd_grad_kernel"}}
 
 
+def measure_train_step(kda, W, torch, pcfg, inp, args, stream):
+    """One training step of the layer on the prefill workload: the forward
+    that keeps the chunk states for its backward (kda_chunk_fwd_save) and the
+    backward on them (KDA_STATES_SAVED), timed together with events."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12345)
+    dO = torch.randn(pcfg.B, pcfg.T, pcfg.H, D, device="cuda", generator=gen).to(torch.bfloat16)
+    ws = torch.empty(kda.lib().kda_chunk_bwd_workspace_size(pcfg.B, pcfg.T, pcfg.H, D, D, 1),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["v"])
+    S_T = torch.empty(pcfg.B, pcfg.H, D, D, dtype=torch.float32, device="cuda")
+
+    def step():
+        kda.chunk_fwd_save(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], o=o, S_T=S_T,
+                           workspace=ws)
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], dO, None, want_dS0=False,
+                      workspace=ws, states_saved=True)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    del ws, dO, o, S_T
+    return {"value": pcfg.B * pcfg.T / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
+            "workload": "kda_chunk_fwd_save + kda_chunk_bwd_ex(KDA_STATES_SAVED) B8 H32 T8192 d128 bf16 "
+                        "(S0=0, dS_T=0)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -401,6 +437,7 @@ def main():
     line["decode"]["state_restored_before_each_timed_run"] = True
     if not args.no_backward and flags == 0 and not args.packed:
         line["backward"] = measure_backward(kda, W, torch, pcfg, inp, args, stream)
+        line["train_step"] = measure_train_step(kda, W, torch, pcfg, inp, args, stream)
     del inp, o, S, S_saved, tok, steps_tok
     if flags == 0 and not args.packed and not args.no_other_configs:
         # the other two prefill workloads, each timed alone after the step loop

@@ -33,6 +33,7 @@ HEADER = os.path.join(ROOT, "include", "kda.h")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_SCALAR, KDA_NO_DELTA = 1, 2
+KDA_STATES_SAVED = 4
 _DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
 _lock = threading.Lock()
@@ -46,6 +47,7 @@ _SIGS = {
     "kda_chunk_fwd_ex": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_chunk_fwd_noalloc": ([_vp] * 8 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
+    "kda_chunk_fwd_save": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
     "kda_chunk_fwd_varlen_ws": ([_vp] * 10 + [_i] * 7 + [_vp, _sz, _vp], _i),
@@ -177,6 +179,31 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
     return o, S_T
 
 
+def chunk_fwd_save(q, k, v, g, beta, S0=None, *, o=None, S_T=None, workspace=None, stream=None, delta=True):
+    """Prefill that also keeps every chunk's entry state for the backward
+    (kda_chunk_fwd_save; bf16, d = 128, KDA or delta=False): returns
+    (o, S_T, workspace).  Pass the same workspace to chunk_bwd(...,
+    workspace=workspace, states_saved=True) on the same inputs, and the
+    backward skips its own pass over the states."""
+    flags = _flags(False, delta)
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, False, delta)
+    dev = q.device
+    if S0 is not None:
+        _need(S0, (B, H, dk, dv), torch.float32, "S0")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    L = lib()
+    code = _dtype(q)
+    wsz = L.kda_chunk_bwd_ex_workspace_size(B, T, H, dk, dv, code, flags)
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+                                B, T, H, dk, dv, code, flags, _ptr(workspace) if wsz else None, wsz, _stream(stream)))
+    return o, S_T, workspace
+
+
 def chunk_fwd_noalloc(q, k, v, g, beta, S0=None, *, o, S_T=None, stream=None):
     """Prefill through kda_chunk_fwd_noalloc: the library's own device scratch
     holds the workspace, so nothing is allocated (o, and S_T if wanted, must
@@ -246,13 +273,17 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
 
 
 def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None,
-              scalar_gate=False, delta=True):
+              scalar_gate=False, delta=True, states_saved=False):
     """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
     adjoints dO [B,T,H,d_v] (and dS_T [B,H,d_k,d_v] fp32 or None).  bf16 at
     d = 128 (chunked), fp32 at d = 64 / 128 and bf16 at d = 64 (token
     recurrence).  scalar_gate: g and dg are [B,T,H] (Gated DeltaNet);
-    delta=False: no delta rule (beta may be None, dbeta is None)."""
-    flags = _flags(scalar_gate, delta)
+    delta=False: no delta rule (beta may be None, dbeta is None).
+    states_saved: workspace comes from chunk_fwd_save on the same inputs and
+    already holds the chunk states (KDA_STATES_SAVED)."""
+    flags = _flags(scalar_gate, delta) | (KDA_STATES_SAVED if states_saved else 0)
+    if states_saved and workspace is None:
+        raise KDAError("states_saved needs the workspace that chunk_fwd_save filled")
     B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate=scalar_gate, delta=delta)
     _need(dO, (B, T, H, dv), dt, "dO")
     if S0 is not None:
@@ -267,6 +298,8 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=N
     code = _dtype(q)
     wsz = L.kda_chunk_bwd_ex_workspace_size(B, T, H, dk, dv, code, flags)
     if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        if states_saved:
+            raise KDAError("the saved-state workspace is smaller than the backward needs")
         workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
     _check(L.kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),

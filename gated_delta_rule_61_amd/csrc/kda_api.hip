@@ -192,6 +192,13 @@ hipError_t scratch_address(hipStream_t stream, void** out) {
 // sizes and dtype for which the prefill variants exist (the pipelined kernel)
 bool variant_dims(int dk, int dv, int dt) { return dt == KDA_BF16 && dk == 128 && dv == 128; }
 
+// The backward's flags: a variant, and KDA_STATES_SAVED on the chunked path
+// of the variants the saving forward serves (KDA, no delta rule).
+bool valid_bwd_flags(int flags, int d_k, int d_v, int dtype) {
+  if (!valid_flags(flags & ~KDA_STATES_SAVED)) return false;
+  return !(flags & KDA_STATES_SAVED) || (variant_dims(d_k, d_v, dtype) && !(flags & KDA_GATE_SCALAR));
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +288,29 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
   return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
 }
 
+int kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
+                       int flags, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
+  int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE((flags == 0 || flags == KDA_NO_DELTA) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  if ((int64_t)B * H == 0) return KDA_OK;
+  if (T > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype, flags);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  const size_t need = kda_chunk_bwd_ex_workspace_size(B, T, H, d_k, d_v, dtype, flags);
+  KDA_REQUIRE(need == 0 || (bwd_workspace && bwd_workspace_bytes >= need), KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(bwd_workspace), KDA_ERR_ALIGN);
+  // the pipelined kernel, one pass, storing each chunk's entry state where
+  // the backward's state pass would (the workspace's first region)
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 1, 0, 1};
+  a.variant = flags ? kda::kVarNoDelta : 0;
+  a.states = T > 0 ? bwd_workspace : nullptr;
+  return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
+}
+
 int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v, int dtype,
                           void* stream) {
@@ -361,7 +391,7 @@ int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const v
 }
 
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
-  if (!valid_flags(flags)) return 0;
+  if (!valid_bwd_flags(flags, d_k, d_v, dtype)) return 0;
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
   if (!variant_dims(d_k, d_v, dtype)) return kda::backward_tok_workspace(B, T, H, d_k);
   size_t n = kda::backward_workspace(B * H, T);
@@ -380,7 +410,7 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE(valid_flags(flags), KDA_ERR_ARG);
+  KDA_REQUIRE(valid_bwd_flags(flags, d_k, d_v, dtype), KDA_ERR_ARG);
   const bool sg = (flags & KDA_GATE_SCALAR) != 0, nd = (flags & KDA_NO_DELTA) != 0;
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
@@ -412,7 +442,8 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
   kda::BackwardArgs a{q, k, v, sg ? gfull : g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg,
                       nd ? nullptr : dbeta, dS0, B, T, H, workspace, ws + nst, ws + 2 * nst,
-                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, nullptr, 0};
+                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, nullptr, 0,
+                      (flags & KDA_STATES_SAVED) ? 1 : 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (sg && T > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);

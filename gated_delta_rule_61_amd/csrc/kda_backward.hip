@@ -1380,8 +1380,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   // slots x heads with the unused slots returning at once
   const int nblk = a.cu_seqlens ? a.nslots * a.H : BH * N;
   hipError_t e;
-  if (N > 0) {
-    // 1. chunk-entry states: the forward kernel in state mode
+  if (N > 0 && !a.states_saved) {
+    // 1. chunk-entry states: the forward kernel in state mode (skipped when
+    // the forward saved them)
     PrefillArgs f{};
     f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
     f.S0 = a.S0; f.B = a.B; f.T = a.T; f.H = a.H; f.dk = 128; f.dv = 128; f.bf16 = 1; f.pipeline = 1;

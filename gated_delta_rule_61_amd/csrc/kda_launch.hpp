@@ -27,8 +27,10 @@ struct PrefillArgs {
   // tokens [cu_seqlens[b], cu_seqlens[b+1]) of [T, H, d] tensors; NULL: [B, T, H, d].
   const int* cu_seqlens;
   const int* seq_order;   // packed sequences: processing order (a permutation of 0..B-1), or NULL
-  // Chunk-entry states (one pass, no outputs): state at the start of every
-  // chunk, bf16 and transposed, [B*H][ceil(T/64)][dv][dk]; NULL: normal forward.
+  // Chunk-entry states (one pass; the outputs too unless o is NULL): the
+  // state at the start of every chunk, bf16 in the pipelined kernel's owner
+  // fragment order, one 32 KB block per chunk and head (the backward's
+  // layout); NULL: normal forward.
   void* states;
   // Packed sequences, segmented: the device plan (varlen_plan_kernel) with
   // job tables of plan_j1 / plan_j3 entries, segments of seg_len chunks, the
@@ -83,6 +85,9 @@ struct BackwardArgs {
   // blocks (backward_varlen_slots).  NULL: [B, T, H, d].
   const int* cu_seqlens;
   int nslots;
+  // 1: `states` already holds every chunk's entry state (written by the
+  // forward with kda_chunk_fwd_save), so the state pass is skipped
+  int states_saved;
 };
 size_t backward_workspace(int BH, int T);
 // Backward for the other sizes (fp32 at d = 64 or 128, bf16 at d = 64; every

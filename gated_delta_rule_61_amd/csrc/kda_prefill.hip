@@ -2572,7 +2572,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     }
     if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
     if (a.S_T) sTp = a.S_T + (int64_t)head * DK * DV;
-    if (ST) outp = false;   // chunk-entry states only
+    if (ST) outp = a.o != nullptr;   // chunk-entry states, with or without the outputs
   } else if (a.plan) {
     // packed sequences, segmented (the plan kernel's job tables): pass 1 runs
     // whole short sequences and, for the long ones, segment 0, the offsets

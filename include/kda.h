@@ -176,6 +176,8 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
  * Both may be combined (a scalar-gated linear attention).
  */
 typedef enum { KDA_GATE_SCALAR = 1, KDA_NO_DELTA = 2 } kda_variant;
+/* Flag of kda_chunk_bwd_ex only (see there). */
+typedef enum { KDA_STATES_SAVED = 4 } kda_bwd_flag;
 
 /*
  * kda_chunk_fwd_ex -- kda_chunk_fwd for the variants above.  `flags` is an
@@ -320,7 +322,13 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int d
  *                    fp32, and the channel sums are taken on the device.
  *   KDA_NO_DELTA     no delta rule: beta is not read and dbeta not written
  *                    (both may be NULL).
- * Both may be combined; unknown bits return KDA_ERR_ARG.  Other arguments,
+ *   KDA_STATES_SAVED the workspace already holds every chunk's entry state,
+ *                    written by kda_chunk_fwd_save on the same q, k, v, g,
+ *                    beta, S0, sizes and variant (and not touched since):
+ *                    the backward skips its own forward pass over the
+ *                    states.  bf16 at d = 128 only, not with
+ *                    KDA_GATE_SCALAR (KDA_ERR_ARG otherwise).
+ * They may be combined; unknown bits return KDA_ERR_ARG.  Other arguments,
  * layouts, support and aliasing as for kda_chunk_bwd.
  */
 int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
@@ -333,6 +341,23 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
  * with KDA_GATE_SCALAR, B*T*H*d_k*6 (the broadcast gate in bf16 and the
  * per-channel dg in fp32); 0 for unsupported flags or sizes. */
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
+
+/*
+ * kda_chunk_fwd_save -- kda_chunk_fwd_ex (flags 0 or KDA_NO_DELTA, bf16,
+ * d_k = d_v = 128, one pass over each sequence) that also stores the state
+ * at the start of every chunk, bf16, into bwd_workspace, where
+ * kda_chunk_bwd_ex keeps it: a later kda_chunk_bwd_ex with the same inputs,
+ * sizes and flags | KDA_STATES_SAVED on that workspace then needs no forward
+ * pass of its own (training: the forward saves what its backward needs).
+ *   bwd_workspace  kda_chunk_bwd_ex_workspace_size(B, T, H, 128, 128, 1,
+ *                  flags) bytes (required when T > 0), 16-byte aligned
+ * Outputs o and S_T as kda_chunk_fwd_ex.  Errors as kda_chunk_fwd_ex, plus
+ * KDA_ERR_ARG for other sizes, dtypes or flags.
+ */
+int kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const float* S0, void* o, float* S_T,
+                       int B, int T, int H, int d_k, int d_v, int dtype, int flags,
+                       void* bwd_workspace, size_t bwd_workspace_bytes, void* stream);
 
 /*
  * kda_chunk_bwd_varlen -- kda_chunk_bwd_ex for N packed variable-length

@@ -218,7 +218,10 @@ def test_backward_variant_validation(L):
     assert _bwd_ex(L, 3, g=18, dg=18, beta=None, dbeta=None) == -5
     assert _bwd_ex(L, 0, dbeta=None) == -1           # KDA needs dbeta
     assert _bwd_ex(L, 0, beta=None) == -1            # ... and beta
-    assert _bwd_ex(L, 4) == -7                       # unknown bit
+    assert _bwd_ex(L, 8) == -7                       # unknown bit
+    assert _bwd_ex(L, 4) == -5                       # KDA_STATES_SAVED: checks pass, workspace missing
+    assert _bwd_ex(L, 5, g=18, dg=18) == -7          # ... not with the scalar gate
+    assert _bwd_ex(L, 4, dk=64) == -7                # ... nor on the token path
     assert _bwd_ex(L, 1, dk=64) == -5                # bf16 d = 64: token path, workspace missing
     assert _bwd_ex(L, 1, g=17) == -4                 # g not 2-byte aligned
     assert _bwd_ex(L, 1, g=18, dg=18) == -5          # scalar g / dg 2-byte aligned: workspace missing
@@ -228,7 +231,8 @@ def test_backward_variant_validation(L):
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 1) == base + 64 * 128 * 6
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 2) == base
     assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 3) == base + 64 * 128 * 6
-    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 4) == 0
+    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 4) == base   # KDA_STATES_SAVED: same workspace
+    assert L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 8) == 0
     assert _bwd_ex(L, 1, ws=1024, wsz=base) == -5    # too small for the scalar path
 
 
@@ -272,6 +276,26 @@ def test_varlen_segmented_workspace(L, monkeypatch):
     assert f(p, p, p, p, p, None, p, None, None, None, 6, 7597, 2, 128, 128, 1, 0, None, 0, None) == -1
     assert f(p, p, p, p, p, None, p, None, cu, None, 6, 7597, 2, 96, 96, 1, 0, None, 0, None) == -2
     assert f(p, p, p, p, p, None, p, None, cu, None, 0, 7597, 2, 128, 128, 1, 0, None, 0, None) == 0
+
+
+def test_fwd_save_validation(L):
+    """kda_chunk_fwd_save: bf16 at d = 128, KDA or no delta rule, and the
+    backward's workspace, all checked before any launch."""
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    def f(flags=0, dk=128, dt=1, ws=None, wsz=0, q=16, B=1, T=64):
+        return L.kda_chunk_fwd_save(p(q), p(16), p(16), p(16), p(16), None, p(16), None, B, T, 1, dk, dk, dt, flags,
+                                    p(ws), wsz, None)
+    assert f() == -5                                  # workspace missing
+    assert f(flags=2) == -5
+    assert f(flags=1) == -7                           # no scalar gate
+    assert f(flags=8) == -7
+    assert f(dk=64) == -7                             # chunked backward sizes only
+    assert f(dt=0) == -7
+    assert f(q=None) == -1
+    need = L.kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, 1, 0)
+    assert f(ws=32, wsz=need - 1) == -5
+    assert f(ws=40, wsz=need) == -4                   # workspace not 16-byte aligned
+    assert f(B=0) == 0
 
 
 def test_bwd_token_path_workspace(L):
