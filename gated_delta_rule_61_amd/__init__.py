@@ -48,6 +48,7 @@ _SIGS = {
     "kda_chunk_fwd_noalloc": ([_vp] * 8 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_ex_workspace_size": ([_i] * 7, _sz),
     "kda_chunk_fwd_save": ([_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp], _i),
+    "kda_chunk_fwd_varlen_save": ([_vp] * 10 + [_i] * 7 + [_vp, _sz, _vp], _i),
     "kda_recurrent_step_ex": ([_vp] * 7 + [_i] * 6 + [_vp], _i),
     "kda_chunk_fwd_varlen": ([_vp] * 10 + [_i] * 7 + [_vp], _i),
     "kda_chunk_fwd_varlen_ws": ([_vp] * 10 + [_i] * 7 + [_vp, _sz, _vp], _i),
@@ -272,6 +273,44 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
     return o, S_T
 
 
+def chunk_fwd_varlen_save(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o=None, S_T=None,
+                          workspace=None, stream=None, delta=True):
+    """chunk_fwd_varlen (one pass, KDA or delta=False) that also keeps every
+    chunk's entry state for chunk_bwd_varlen(..., workspace=workspace,
+    states_saved=True): returns (o, S_T, workspace)."""
+    flags = _flags(False, delta)
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise KDAError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _need(q, (Tt, H, dk), dt, "q")
+    _need(k, (Tt, H, dk), dt, "k")
+    _need(g, (Tt, H, dk), dt, "g")
+    _need(v, (Tt, H, dv), dt, "v")
+    if delta or beta is not None:
+        _need(beta, (Tt, H), dt, "beta")
+    if S0 is not None:
+        _need(S0, (N, H, dk, dv), torch.float32, "S0")
+    if seq_order is not None:
+        _need(seq_order, (N,), torch.int32, "seq_order")
+    dev = q.device
+    if o is None:
+        o = torch.zeros((Tt, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    L = lib()
+    wsz = L.kda_chunk_bwd_varlen_workspace_size(N, Tt, H, dk, dv, _dtype(q), flags)
+    if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_fwd_varlen_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+                                       _ptr(cu_seqlens), _ptr(seq_order), N, Tt, H, dk, dv, _dtype(q), flags,
+                                       _ptr(workspace) if wsz else None, wsz, _stream(stream)))
+    return o, S_T, workspace
+
+
 def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=None, stream=None,
               scalar_gate=False, delta=True, states_saved=False):
     """Gradient of chunk_fwd: returns dict(dq, dk, dv, dg, dbeta, dS0) for the
@@ -309,12 +348,15 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, *, want_dS0=True, workspace=N
 
 
 def chunk_bwd_varlen(q, k, v, g, beta, cu_seqlens, S0, dO, dS_T=None, *, want_dS0=True, workspace=None,
-                     stream=None, scalar_gate=False, delta=True):
+                     stream=None, scalar_gate=False, delta=True, states_saved=False):
     """Gradient of chunk_fwd_varlen for N packed sequences: q, k, g, v, beta,
     dO packed as there ([T_total, H, ...]), S0 and dS_T [N, H, d_k, d_v] fp32
     or None.  Returns dict(dq, dk, dv, dg, dbeta, dS0) (dbeta None without the
-    delta rule, dS0 [N, H, d_k, d_v])."""
-    flags = _flags(scalar_gate, delta)
+    delta rule, dS0 [N, H, d_k, d_v]).  states_saved: workspace comes from
+    chunk_fwd_varlen_save on the same inputs."""
+    flags = _flags(scalar_gate, delta) | (KDA_STATES_SAVED if states_saved else 0)
+    if states_saved and workspace is None:
+        raise KDAError("states_saved needs the workspace that chunk_fwd_varlen_save filled")
     Tt, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -340,6 +382,8 @@ def chunk_bwd_varlen(q, k, v, g, beta, cu_seqlens, S0, dO, dS_T=None, *, want_dS
     code = _dtype(q)
     wsz = L.kda_chunk_bwd_varlen_workspace_size(N, Tt, H, dk, dv, code, flags)
     if wsz and (workspace is None or workspace.numel() * workspace.element_size() < wsz):
+        if states_saved:
+            raise KDAError("the saved-state workspace is smaller than the backward needs")
         workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
     _check(L.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
                                   _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),

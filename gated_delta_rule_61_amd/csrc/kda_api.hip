@@ -390,6 +390,34 @@ int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const v
   return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
 }
 
+int kda_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const float* S0, void* o, float* S_T, const int32_t* cu_seqlens,
+                              const int32_t* seq_order, int N, int T_total, int H, int d_k, int d_v, int dtype,
+                              int flags, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
+  int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
+  if (st) return st;
+  KDA_REQUIRE((flags == 0 || flags == KDA_NO_DELTA) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  if ((int64_t)N * H == 0) return KDA_OK;
+  KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
+  KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0 && (reinterpret_cast<uintptr_t>(seq_order) & 3u) == 0,
+              KDA_ERR_ALIGN);
+  if (T_total > 0) {
+    st = check_tokens(q, k, v, g, beta, o, dtype, flags);
+    if (st) return st;
+  }
+  KDA_REQUIRE(aligned16(S0) && aligned16(S_T), KDA_ERR_ALIGN);
+  const size_t need = kda_chunk_bwd_varlen_workspace_size(N, T_total, H, d_k, d_v, dtype, flags);
+  KDA_REQUIRE(need == 0 || (bwd_workspace && bwd_workspace_bytes >= need), KDA_ERR_WORKSPACE);
+  KDA_REQUIRE(aligned16(bwd_workspace), KDA_ERR_ALIGN);
+  // one pass, each chunk's entry state into the backward's slot layout
+  kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, N, T_total, H, d_k, d_v, 1, 0, 1};
+  a.variant = flags ? kda::kVarNoDelta : 0;
+  a.cu_seqlens = cu_seqlens;
+  a.seq_order = seq_order;
+  a.states = T_total > 0 ? bwd_workspace : nullptr;
+  return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
+}
+
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags) {
   if (!valid_bwd_flags(flags, d_k, d_v, dtype)) return 0;
   if (check_chunk_dims(B, T, H, d_k, d_v, dtype) != KDA_OK) return 0;
@@ -453,7 +481,7 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
 }
 
 size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v, int dtype, int flags) {
-  if (!valid_flags(flags)) return 0;
+  if (!valid_bwd_flags(flags, d_k, d_v, dtype)) return 0;
   if (check_chunk_dims(N, T_total, H, d_k, d_v, dtype) != KDA_OK || !variant_dims(d_k, d_v, dtype)) return 0;
   if ((int64_t)N * H == 0 || T_total == 0) return 0;
   size_t n = kda::backward_varlen_workspace(N, T_total, H);
@@ -467,7 +495,7 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                          int d_v, int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  KDA_REQUIRE(valid_bwd_flags(flags, d_k, d_v, dtype) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
   const bool sg = (flags & KDA_GATE_SCALAR) != 0, nd = (flags & KDA_NO_DELTA) != 0;
   if ((int64_t)N * H == 0) return KDA_OK;
   KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
@@ -495,7 +523,8 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
   float* dg32 = reinterpret_cast<float*>(ws + base + (size_t)rows * d_k * 2);
   kda::BackwardArgs a{q, k, v, sg ? gfull : g, nd ? nullptr : beta, S0, dO, dS_T, dq, dk, dv, dg,
                       nd ? nullptr : dbeta, dS0, N, T_total, H, workspace, ws + nst, ws + 2 * nst,
-                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, cu_seqlens, nslots};
+                      sg ? dg32 : nullptr, nd ? kda::kVarNoDelta : 0, cu_seqlens, nslots,
+                      (flags & KDA_STATES_SAVED) ? 1 : 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (sg && T_total > 0 && (e = kda::launch_gate_expand(g, gfull, rows, s)) != hipSuccess) return hip_status(e);

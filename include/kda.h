@@ -375,7 +375,8 @@ int kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* 
  *   cu_seqlens[N] = T_total: sequence i is tokens [cu_seqlens[i],
  *   cu_seqlens[i+1]); entries are clamped to [0, T_total] on the device.
  *   Zero-length sequences are allowed (dS0[i] = dS_T[i]).
- * Supported: dtype KDA_BF16, d_k = d_v = 128 (flags as kda_chunk_bwd_ex).
+ * Supported: dtype KDA_BF16, d_k = d_v = 128 (flags as kda_chunk_bwd_ex;
+ * KDA_STATES_SAVED after kda_chunk_fwd_varlen_save).
  * Workspace: kda_chunk_bwd_varlen_workspace_size bytes, 16-byte aligned
  * (chunk states, adjoints and operand blocks in floor(T_total/64) + N slots
  * per head).  Enqueued on `stream`; the caller keeps every buffer alive until
@@ -392,6 +393,25 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
  * nothing to do). */
 size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
                                            int dtype, int flags);
+
+/*
+ * kda_chunk_fwd_varlen_save -- kda_chunk_fwd_varlen (flags 0 or
+ * KDA_NO_DELTA, one pass over each sequence) that also stores the state at
+ * the start of every chunk, bf16, into bwd_workspace in kda_chunk_bwd_varlen's
+ * slot layout; a later kda_chunk_bwd_varlen with the same inputs, offsets,
+ * sizes and flags | KDA_STATES_SAVED on that workspace needs no forward pass
+ * of its own.
+ *   bwd_workspace  kda_chunk_bwd_varlen_workspace_size(N, T_total, H, 128,
+ *                  128, 1, flags) bytes (required when T_total > 0), 16-byte
+ *                  aligned
+ * Other arguments, outputs and errors as kda_chunk_fwd_varlen; KDA_ERR_ARG
+ * for other sizes, dtypes or flags.
+ */
+int kda_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, const float* S0, void* o, float* S_T,
+                              const int32_t* cu_seqlens, const int32_t* seq_order, int N,
+                              int T_total, int H, int d_k, int d_v, int dtype, int flags,
+                              void* bwd_workspace, size_t bwd_workspace_bytes, void* stream);
 
 /*
  * Staged schedule: the same forward as kda_chunk_fwd, run as four separate

@@ -247,7 +247,8 @@ def test_backward_varlen_validation(L):
                                       p(16), p(16), None, p(cu), N, T, 1, dk, dk, 1, flags, p(ws), wsz, None)
     assert call(cu=None) == -1                        # cu_seqlens required
     assert call(cu=18) == -4                          # int32-aligned
-    assert call(flags=4) == -7
+    assert call(flags=8) == -7
+    assert call(flags=4) == -5                       # KDA_STATES_SAVED: checks pass, workspace missing
     assert call(dk=64) == -7
     assert call() == -5                               # workspace missing
     assert call(N=0) == 0                             # nothing to do
@@ -296,6 +297,21 @@ def test_fwd_save_validation(L):
     assert f(ws=32, wsz=need - 1) == -5
     assert f(ws=40, wsz=need) == -4                   # workspace not 16-byte aligned
     assert f(B=0) == 0
+
+
+def test_fwd_varlen_save_validation(L):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    def f(flags=0, cu=64, ws=None, wsz=0, dk=128):
+        return L.kda_chunk_fwd_varlen_save(p(16), p(16), p(16), p(16), p(16), None, p(16), None, p(cu), None, 2, 100,
+                                           1, dk, dk, 1, flags, p(ws), wsz, None)
+    assert f() == -5                  # workspace missing
+    assert f(flags=1) == -7           # no scalar gate
+    assert f(dk=64) == -7
+    assert f(cu=None) == -1
+    assert f(cu=66) == -4             # offsets 4-byte aligned
+    need = L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 0)
+    assert need > 0 and L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 4) == need
+    assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 5) == 0
 
 
 def test_bwd_token_path_workspace(L):
