@@ -180,14 +180,15 @@ def chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, staged=False,
     return o, S_T
 
 
-def chunk_fwd_save(q, k, v, g, beta, S0=None, *, o=None, S_T=None, workspace=None, stream=None, delta=True):
+def chunk_fwd_save(q, k, v, g, beta, S0=None, *, o=None, S_T=None, workspace=None, stream=None, scalar_gate=False,
+                   delta=True):
     """Prefill that also keeps every chunk's entry state for the backward
-    (kda_chunk_fwd_save; bf16, d = 128, KDA or delta=False): returns
+    (kda_chunk_fwd_save; bf16, d = 128, any variant): returns
     (o, S_T, workspace).  Pass the same workspace to chunk_bwd(...,
     workspace=workspace, states_saved=True) on the same inputs, and the
     backward skips its own pass over the states."""
-    flags = _flags(False, delta)
-    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, False, delta)
+    flags = _flags(scalar_gate, delta)
+    B, T, H, dk, dv, dt = _prefill_shapes(q, k, v, g, beta, scalar_gate, delta)
     dev = q.device
     if S0 is not None:
         _need(S0, (B, H, dk, dv), torch.float32, "S0")
@@ -274,11 +275,11 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o
 
 
 def chunk_fwd_varlen_save(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=None, o=None, S_T=None,
-                          workspace=None, stream=None, delta=True):
-    """chunk_fwd_varlen (one pass, KDA or delta=False) that also keeps every
+                          workspace=None, stream=None, scalar_gate=False, delta=True):
+    """chunk_fwd_varlen (one pass, any variant) that also keeps every
     chunk's entry state for chunk_bwd_varlen(..., workspace=workspace,
     states_saved=True): returns (o, S_T, workspace)."""
-    flags = _flags(False, delta)
+    flags = _flags(scalar_gate, delta)
     Tt, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -288,7 +289,7 @@ def chunk_fwd_varlen_save(q, k, v, g, beta, cu_seqlens, S0=None, *, seq_order=No
     _need(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
     _need(q, (Tt, H, dk), dt, "q")
     _need(k, (Tt, H, dk), dt, "k")
-    _need(g, (Tt, H, dk), dt, "g")
+    _need(g, (Tt, H) if scalar_gate else (Tt, H, dk), dt, "g")
     _need(v, (Tt, H, dv), dt, "v")
     if delta or beta is not None:
         _need(beta, (Tt, H), dt, "beta")

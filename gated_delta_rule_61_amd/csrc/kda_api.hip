@@ -192,11 +192,10 @@ hipError_t scratch_address(hipStream_t stream, void** out) {
 // sizes and dtype for which the prefill variants exist (the pipelined kernel)
 bool variant_dims(int dk, int dv, int dt) { return dt == KDA_BF16 && dk == 128 && dv == 128; }
 
-// The backward's flags: a variant, and KDA_STATES_SAVED on the chunked path
-// of the variants the saving forward serves (KDA, no delta rule).
+// The backward's flags: a variant, and KDA_STATES_SAVED on the chunked path.
 bool valid_bwd_flags(int flags, int d_k, int d_v, int dtype) {
   if (!valid_flags(flags & ~KDA_STATES_SAVED)) return false;
-  return !(flags & KDA_STATES_SAVED) || (variant_dims(d_k, d_v, dtype) && !(flags & KDA_GATE_SCALAR));
+  return !(flags & KDA_STATES_SAVED) || variant_dims(d_k, d_v, dtype);
 }
 
 }  // namespace
@@ -293,7 +292,7 @@ int kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* 
                        int flags, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
   int st = check_chunk_dims(B, T, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE((flags == 0 || flags == KDA_NO_DELTA) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
   if ((int64_t)B * H == 0) return KDA_OK;
   if (T > 0) {
     st = check_tokens(q, k, v, g, beta, o, dtype, flags);
@@ -306,7 +305,7 @@ int kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* 
   // the pipelined kernel, one pass, storing each chunk's entry state where
   // the backward's state pass would (the workspace's first region)
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, d_k, d_v, 1, 0, 1};
-  a.variant = flags ? kda::kVarNoDelta : 0;
+  a.variant = flags;
   a.states = T > 0 ? bwd_workspace : nullptr;
   return finish(kda::launch_fused(a, (hipStream_t)stream), stream);
 }
@@ -396,7 +395,7 @@ int kda_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const
                               int flags, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
   int st = check_chunk_dims(N, T_total, H, d_k, d_v, dtype);
   if (st) return st;
-  KDA_REQUIRE((flags == 0 || flags == KDA_NO_DELTA) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
+  KDA_REQUIRE(valid_flags(flags) && variant_dims(d_k, d_v, dtype), KDA_ERR_ARG);
   if ((int64_t)N * H == 0) return KDA_OK;
   KDA_REQUIRE(cu_seqlens != nullptr, KDA_ERR_NULL);
   KDA_REQUIRE((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) == 0 && (reinterpret_cast<uintptr_t>(seq_order) & 3u) == 0,
@@ -411,7 +410,7 @@ int kda_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const
   KDA_REQUIRE(aligned16(bwd_workspace), KDA_ERR_ALIGN);
   // one pass, each chunk's entry state into the backward's slot layout
   kda::PrefillArgs a{q, k, v, g, beta, S0, o, S_T, N, T_total, H, d_k, d_v, 1, 0, 1};
-  a.variant = flags ? kda::kVarNoDelta : 0;
+  a.variant = flags;
   a.cu_seqlens = cu_seqlens;
   a.seq_order = seq_order;
   a.states = T_total > 0 ? bwd_workspace : nullptr;

@@ -3296,9 +3296,13 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
   // chunk-entry states (for the backward): KDA or no delta rule, one pass
   if (a.states) {
     if (a.nseg >= 3) return hipErrorInvalidValue;
-    if (a.variant == 0) return launch_pipe_v<kPipeStates>(a, s);
-    if (a.variant == kVarNoDelta) return launch_pipe_v<kPipeStates | kVarNoDelta>(a, s);
-    return hipErrorInvalidValue;
+    switch (a.variant) {
+      case 0: return launch_pipe_v<kPipeStates>(a, s);
+      case kVarNoDelta: return launch_pipe_v<kPipeStates | kVarNoDelta>(a, s);
+      case kVarScalarGate: return launch_pipe_v<kPipeStates | kVarScalarGate>(a, s);
+      case kVarScalarGate | kVarNoDelta: return launch_pipe_v<kPipeStates | kVarScalarGate | kVarNoDelta>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (a.variant) {
     case 0: return launch_pipe_v<0>(a, s);

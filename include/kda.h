@@ -326,8 +326,8 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int d_k, int d_v, int d
  *                    written by kda_chunk_fwd_save on the same q, k, v, g,
  *                    beta, S0, sizes and variant (and not touched since):
  *                    the backward skips its own forward pass over the
- *                    states.  bf16 at d = 128 only, not with
- *                    KDA_GATE_SCALAR (KDA_ERR_ARG otherwise).
+ *                    states.  bf16 at d = 128 only (KDA_ERR_ARG
+ *                    otherwise).
  * They may be combined; unknown bits return KDA_ERR_ARG.  Other arguments,
  * layouts, support and aliasing as for kda_chunk_bwd.
  */
@@ -343,8 +343,8 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
 size_t kda_chunk_bwd_ex_workspace_size(int B, int T, int H, int d_k, int d_v, int dtype, int flags);
 
 /*
- * kda_chunk_fwd_save -- kda_chunk_fwd_ex (flags 0 or KDA_NO_DELTA, bf16,
- * d_k = d_v = 128, one pass over each sequence) that also stores the state
+ * kda_chunk_fwd_save -- kda_chunk_fwd_ex (any flags, bf16, d_k = d_v = 128,
+ * one pass over each sequence) that also stores the state
  * at the start of every chunk, bf16, into bwd_workspace, where
  * kda_chunk_bwd_ex keeps it: a later kda_chunk_bwd_ex with the same inputs,
  * sizes and flags | KDA_STATES_SAVED on that workspace then needs no forward
@@ -395,8 +395,8 @@ size_t kda_chunk_bwd_varlen_workspace_size(int N, int T_total, int H, int d_k, i
                                            int dtype, int flags);
 
 /*
- * kda_chunk_fwd_varlen_save -- kda_chunk_fwd_varlen (flags 0 or
- * KDA_NO_DELTA, one pass over each sequence) that also stores the state at
+ * kda_chunk_fwd_varlen_save -- kda_chunk_fwd_varlen (any flags, one pass
+ * over each sequence) that also stores the state at
  * the start of every chunk, bf16, into bwd_workspace in kda_chunk_bwd_varlen's
  * slot layout; a later kda_chunk_bwd_varlen with the same inputs, offsets,
  * sizes and flags | KDA_STATES_SAVED on that workspace needs no forward pass

@@ -46,8 +46,8 @@ int main(void) {
                          8, NULL, 0, NULL), KDA_ERR_ARG);
   CHECK(kda_chunk_bwd_ex(p, p, p, p, p, NULL, p, NULL, p, p, p, p, p, NULL, 1, 64, 1, 128, 128, KDA_BF16,
                          KDA_STATES_SAVED, NULL, 0, NULL), KDA_ERR_WORKSPACE);
-  CHECK(kda_chunk_fwd_save(p, p, p, p, p, NULL, p, NULL, 1, 64, 1, 128, 128, KDA_BF16, KDA_GATE_SCALAR, NULL, 0,
-                           NULL), KDA_ERR_ARG);
+  CHECK(kda_chunk_fwd_save(p, p, p, p, p, NULL, p, NULL, 1, 64, 1, 64, 64, KDA_BF16, 0, NULL, 0, NULL),
+        KDA_ERR_ARG);
   CHECK(kda_chunk_bwd_ex(p, p, p, odd, p, NULL, p, NULL, p, p, p, odd, p, NULL, 1, 64, 1, 128, 128, KDA_BF16,
                          KDA_GATE_SCALAR, NULL, 0, NULL), KDA_ERR_WORKSPACE);
   if (kda_chunk_bwd_ex_workspace_size(1, 64, 1, 128, 128, KDA_BF16, KDA_GATE_SCALAR) !=

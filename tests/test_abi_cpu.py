@@ -220,7 +220,7 @@ def test_backward_variant_validation(L):
     assert _bwd_ex(L, 0, beta=None) == -1            # ... and beta
     assert _bwd_ex(L, 8) == -7                       # unknown bit
     assert _bwd_ex(L, 4) == -5                       # KDA_STATES_SAVED: checks pass, workspace missing
-    assert _bwd_ex(L, 5, g=18, dg=18) == -7          # ... not with the scalar gate
+    assert _bwd_ex(L, 5, g=18, dg=18) == -5          # ... with the scalar gate too
     assert _bwd_ex(L, 4, dk=64) == -7                # ... nor on the token path
     assert _bwd_ex(L, 1, dk=64) == -5                # bf16 d = 64: token path, workspace missing
     assert _bwd_ex(L, 1, g=17) == -4                 # g not 2-byte aligned
@@ -288,7 +288,7 @@ def test_fwd_save_validation(L):
                                     p(ws), wsz, None)
     assert f() == -5                                  # workspace missing
     assert f(flags=2) == -5
-    assert f(flags=1) == -7                           # no scalar gate
+    assert f(flags=3) == -5                           # every variant
     assert f(flags=8) == -7
     assert f(dk=64) == -7                             # chunked backward sizes only
     assert f(dt=0) == -7
@@ -305,13 +305,14 @@ def test_fwd_varlen_save_validation(L):
         return L.kda_chunk_fwd_varlen_save(p(16), p(16), p(16), p(16), p(16), None, p(16), None, p(cu), None, 2, 100,
                                            1, dk, dk, 1, flags, p(ws), wsz, None)
     assert f() == -5                  # workspace missing
-    assert f(flags=1) == -7           # no scalar gate
+    assert f(flags=8) == -7           # unknown bit
     assert f(dk=64) == -7
     assert f(cu=None) == -1
     assert f(cu=66) == -4             # offsets 4-byte aligned
     need = L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 0)
     assert need > 0 and L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 4) == need
-    assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 5) == 0
+    assert L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 5) == \
+        L.kda_chunk_bwd_varlen_workspace_size(2, 100, 1, 128, 128, 1, 1)
 
 
 def test_bwd_token_path_workspace(L):

@@ -247,29 +247,32 @@ def test_no_delta_small_shapes(kda, B, T, H, s0, dst):
     _check(got, ref, f"no delta B{B}T{T}H{H}")
 
 
-@pytest.mark.parametrize("delta", [True, False], ids=["kda", "nodelta"])
-def test_states_saved_by_forward(kda, delta):
+@pytest.mark.parametrize("scalar_gate,delta", [(False, True), (False, False), (True, True), (True, False)],
+                         ids=["kda", "nodelta", "scalar", "scalar-nodelta"])
+def test_states_saved_by_forward(kda, scalar_gate, delta):
     """The forward that keeps the chunk states (kda_chunk_fwd_save) gives the
     outputs of the one-pass kda_chunk_fwd_ex, and the backward on its
     workspace (KDA_STATES_SAVED) the gradients of the backward that runs its
     own state pass -- bit for bit: the same kernels compute the same states."""
     import ctypes
     L = kda.lib()
-    flags = 0 if delta else 2
+    flags = (1 if scalar_gate else 0) | (0 if delta else 2)
     for B, T, H, seed in ((2, 300, 3, 91), (1, 64 * 5, 2, 92)):
-        inp = _inputs(B, T, H, seed)
+        inp = _inputs(B, T, H, seed, scalar_gate=scalar_gate)
         beta = inp["beta"] if delta else None
-        print(f"case fwd_save + bwd B{B} T{T} H{H} delta={delta}", flush=True)
+        print(f"case fwd_save + bwd B{B} T{T} H{H} scalar_gate={scalar_gate} delta={delta}", flush=True)
         P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
         o1 = torch.empty_like(inp["v"])
         S1 = torch.empty(B, H, 128, 128, dtype=torch.float32, device="cuda")
         assert L.kda_chunk_fwd_ex(P(inp["q"]), P(inp["k"]), P(inp["v"]), P(inp["g"]), P(beta), P(inp["S0"]), P(o1),
                                   P(S1), B, T, H, 128, 128, 1, flags, None, 0, None) == 0
-        o2, S2, ws = kda.chunk_fwd_save(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"], delta=delta)
+        o2, S2, ws = kda.chunk_fwd_save(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"],
+                                        scalar_gate=scalar_gate, delta=delta)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
-        g1 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"], inp["dO"], inp["dST"], delta=delta)
-        g2 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"], inp["dO"], inp["dST"], delta=delta,
+        kw = dict(scalar_gate=scalar_gate, delta=delta)
+        g1 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"], inp["dO"], inp["dST"], **kw)
+        g2 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], beta, inp["S0"], inp["dO"], inp["dST"], **kw,
                            workspace=ws, states_saved=True)
         torch.cuda.synchronize()
         for n in g1:

@@ -106,22 +106,23 @@ def test_matches_batched_backward(kda):
         assert torch.equal(got, ref[n]), n
 
 
-@pytest.mark.parametrize("delta", [True, False], ids=["kda", "nodelta"])
-def test_states_saved_packed(kda, delta):
+@pytest.mark.parametrize("scalar_gate,delta", [(False, True), (False, False), (True, True)],
+                         ids=["kda", "nodelta", "scalar"])
+def test_states_saved_packed(kda, scalar_gate, delta):
     """kda_chunk_fwd_varlen_save gives the outputs of the one-pass packed
     forward, and the packed backward on its workspace (KDA_STATES_SAVED) the
     gradients of the backward with its own state pass, bit for bit."""
     lengths = [130, 1, 64, 200, 7]
-    x, cu = _packed(lengths, 3, 97)
+    x, cu = _packed(lengths, 3, 97, scalar_gate=scalar_gate)
     beta = x["beta"] if delta else None
-    print(f"case varlen fwd_save + bwd delta={delta}", flush=True)
-    o1, S1 = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], delta=delta,
-                                  segmented=False)
-    o2, S2, ws = kda.chunk_fwd_varlen_save(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], delta=delta)
+    print(f"case varlen fwd_save + bwd scalar_gate={scalar_gate} delta={delta}", flush=True)
+    kw = dict(scalar_gate=scalar_gate, delta=delta)
+    o1, S1 = kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], segmented=False, **kw)
+    o2, S2, ws = kda.chunk_fwd_varlen_save(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], **kw)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
-    g1 = kda.chunk_bwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], x["dO"], x["dST"], delta=delta)
-    g2 = kda.chunk_bwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], x["dO"], x["dST"], delta=delta,
+    g1 = kda.chunk_bwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], x["dO"], x["dST"], **kw)
+    g2 = kda.chunk_bwd_varlen(x["q"], x["k"], x["v"], x["g"], beta, x["cu"], x["S0"], x["dO"], x["dST"], **kw,
                               workspace=ws, states_saved=True)
     torch.cuda.synchronize()
     for n in g1:
