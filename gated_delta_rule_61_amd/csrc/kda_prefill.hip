@@ -1462,10 +1462,29 @@ __device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], co
     }
 }
 
-// Workspace matrix (fp32 [d_k][d_v]) of the segmented schedule: for sequence /
-// head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N.
+// Workspace matrix (fp32, d_k x d_v) of the segmented schedule: for sequence /
+// head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N
+// (row-major [d_k][d_v], except M: in the combine's operand order, mfrag_index).
 __device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int s, int kind) {
   return ws + ((head * nseg + s) * 3 + kind) * (int64_t)(DK * DV);
+}
+
+// Transition M of the segmented schedule in the A-operand order of the
+// combine kernel's products (v_mfma_f32_16x16x4_f32 on a 16-row tile):
+// element (r, c) sits in the 256-float block 8 (r / 16) + c / 16, at lane
+// 16 (c % 4) + r % 16, position (c / 4) % 4 of that lane's four, so that a
+// lane of the combine reads four consecutive 4-index steps as one vector.
+__device__ __forceinline__ int mfrag_index(int r, int c) {
+  return ((r >> 4) * 8 + (c >> 4)) * 256 + (16 * (c & 3) + (r & 15)) * 4 + ((c >> 2) & 3);
+}
+__device__ __forceinline__ void store_state_mfrag(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[mfrag_index(16 * rt + 4 * g4 + j, col0 + vcol(nt, l16))] = S[nt][rt][j];
 }
 
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
@@ -2752,7 +2771,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
     store_state_v(S, sTp, col0, lane);
     state_rescale(SM, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
-    store_state_v(SM, smp, col0, lane);
+    store_state_mfrag(SM, smp, col0, lane);
   } else if (wave < 4) {
     // ---------------------------------------------------------------- owners
     const int o = wave;
@@ -2977,27 +2996,27 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
 // Segmented schedule, between the two passes: the entry state of each
 // segment, S_{s+1} = M_s S_s + N_s for s = 1 .. nseg-2 (S_1 is segment 0's
 // final state).  The columns of the state never mix, so each sequence and
-// head is split into NSC workgroups of 16 columns; each holds its 128 x 16
-// slice of S_s in LDS and M_s in one of two LDS buffers, loading M_{s+1}
-// into registers while it multiplies (fp32 MFMA, v_mfma_f32_16x16x4_f32).
-// Wavefront w forms rows 32w .. 32w+31 of the slice.
+// head is split into NSC workgroups of 16 columns (fp32 MFMA,
+// v_mfma_f32_16x16x4_f32); wavefront w forms rows 32w .. 32w+31 of the
+// slice.  M_s comes from the workspace in the A-operand order of those
+// products (mfrag_index), straight into registers, one step ahead; the S
+// slice alternates between two LDS buffers, stored transposed so that a
+// lane's B operands of a step are eight 16-byte reads.
 // ---------------------------------------------------------------------------
 namespace segc {
 constexpr int NTC = 256;
 constexpr int NSC = 8;               // column slices per sequence and head
 constexpr int CW = 128 / NSC;        // columns per slice
-constexpr int LDS_S = CW + 4;        // fp32 rows of the S slice
-constexpr int LDS_M = 132;           // fp32 rows of M: A-operand reads (16 rows, 4 columns) spread over the banks
-constexpr int MV = 128 * 128 / 4 / NTC;   // 16-byte vectors of M per thread
-constexpr int BYTES = (128 * LDS_S + 2 * 128 * LDS_M) * 4;
+constexpr int LDS_T = 132;           // fp32 per slice column: [row % 4][row / 4], padded
+constexpr int BYTES = 2 * CW * LDS_T * 4;
 }  // namespace segc
 
 __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   using namespace segc;
   constexpr int D = 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  float* Sl = reinterpret_cast<float*>(smem_raw);
-  float* Mb = Sl + D * LDS_S;          // two buffers of D x LDS_M
+  float* T0 = reinterpret_cast<float*>(smem_raw);
+  float* T1 = T0 + CW * LDS_T;
   const int col0 = (blockIdx.x % NSC) * CW;
   int nseg = a.nseg;
   // maps of segment s of this sequence and head: batched sequences keep them
@@ -3020,74 +3039,94 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   auto mat = [&](int s, int kind) { return a.ws + ((mbase + s * mslot) * 3 + kind) * (D * D); };
-  floatx4 mr[MV];
-  auto load_m = [&](int s) {
+  // the lane's A operands of M_s: tile u (rows 32 wave + 16 u ..), 16-index
+  // group kq, four consecutive 4-index steps in one vector
+  auto load_m = [&](int s, floatx4 (&m)[2][8]) {
     const floatx4* src = reinterpret_cast<const floatx4*>(mat(s, 1));
 #pragma unroll
-    for (int u = 0; u < MV; ++u) mr[u] = src[tid + u * NTC];
-  };
-  auto store_m = [&](float* dst) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < MV; ++u) {
-      const int i = tid + u * NTC, r = i / (D / 4), c4 = i % (D / 4);
-      *reinterpret_cast<floatx4*>(dst + r * LDS_M + 4 * c4) = mr[u];
-    }
+      for (int kq = 0; kq < 8; ++kq) m[u][kq] = src[((2 * wave + u) * 8 + kq) * 64 + lane];
   };
-  {
-    const float* src = mat(1, 0);
-    for (int i = tid; i < D * CW / 4; i += NTC) {
-      const int r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
-      *reinterpret_cast<floatx4*>(Sl + r * LDS_S + c4) = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
-    }
-  }
   // N_s of the lane's eight entries (the accumulator's start)
-  floatx4 nr[2];
-  auto load_n = [&](int s) {
+  auto load_n = [&](int s, floatx4 (&nr)[2]) {
     const float* Nm = mat(s, 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) nr[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
   };
+  // slice element (row r, column c) of a transposed buffer
+  auto tpos = [](int r, int c) { return c * LDS_T + (r & 3) * 32 + (r >> 2); };
+  // three register sets of the maps: step s uses set (s - 1) % 3 and loads
+  // the maps of step s + 2 into set (s + 1) % 3
+  floatx4 mA[2][8], mB[2][8], mC[2][8], nA[2], nB[2], nC[2];
+  // S_1 (the slice's 128 x 16 entries, two 16-byte pieces per thread) and
+  // the first two steps' maps, all in flight together
+  static_assert(D * CW / 4 == 2 * NTC, "two pieces of the slice per thread");
+  floatx4 sv[2];
+  {
+    const float* src = mat(1, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * NTC, r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
+      sv[u] = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
+    }
+  }
   if (nseg > 2) {
-    load_m(1);
-    store_m(Mb);
-    load_n(1);
+    load_m(1, mA);
+    load_n(1, nA);
+    load_m(min(2, nseg - 2), mB);
+    load_n(min(2, nseg - 2), nB);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * NTC, r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) T0[tpos(r, c4 + j)] = sv[u][j];
   }
   __syncthreads();
-  // Step s: S_{s+1} = M_s S_s + N_s.  M_{s+1} and N_{s+1} are loaded during
-  // the products (in that order, after N_s is in the accumulators: loads
-  // complete in order, so a wait for N_s issued after them would also wait
-  // for M_{s+1}); the last step reloads its own maps, so that no load is
-  // under a branch.
-  for (int sg = 1; sg + 1 < nseg; ++sg) {
-    const float* Ml = Mb + ((sg - 1) & 1) * D * LDS_M;
-    const int nx = min(sg + 1, nseg - 2);
-    floatx4 acc[2] = {nr[0], nr[1]};
-    load_m(nx);
-    load_n(nx);
-#pragma unroll 8
-    for (int kb = 0; kb < D / 4; ++kb) {
-      const float bv = Sl[(4 * kb + g4) * LDS_S + l16];
+  // Step s: S_{s+1} = M_s S_s + N_s, from buffer (s - 1) % 2 into the other.
+  // The maps of step s + 2 are loaded during the products (loads complete in
+  // order; the last steps reload maps already held, so that no load is under
+  // a branch).  One barrier per step: the buffer a step writes was last read
+  // a step earlier.
+  auto step = [&](const floatx4 (&mc)[2][8], const floatx4 (&nc)[2], floatx4 (&mf)[2][8], floatx4 (&nf)[2],
+                  int sg) {
+    const float* Tc = (sg & 1) ? T0 : T1;
+    float* Tn = (sg & 1) ? T1 : T0;
+    const int nx = min(sg + 2, nseg - 2);
+    floatx4 acc[2] = {nc[0], nc[1]};
+    load_m(nx, mf);
+    load_n(nx, nf);
+    // B operands: S_s[4 kb + g4][l16] for kb = 0 .. 31
+    floatx4 bq[8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float av = Ml[(32 * wave + 16 * u + l16) * LDS_M + 4 * kb + g4];
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[u], 0, 0, 0);
-      }
-    }
-    __syncthreads();   // every read of S_s (and of the buffer M_{s+1} goes to) is done
+    for (int q = 0; q < 8; ++q) bq[q] = *reinterpret_cast<const floatx4*>(Tc + l16 * LDS_T + g4 * 32 + 4 * q);
+#pragma unroll
+    for (int kb = 0; kb < D / 4; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[u][kb >> 2][kb & 3], bq[kb >> 2][kb & 3], acc[u], 0, 0, 0);
     float* dst = mat(sg + 1, 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 32 * wave + 16 * u + 4 * g4 + jj;
-        Sl[r * LDS_S + l16] = acc[u][jj];
+        Tn[tpos(r, l16)] = acc[u][jj];
         dst[r * D + col0 + l16] = acc[u][jj];
       }
-    store_m(Mb + (sg & 1) * D * LDS_M);   // (unread after the last step)
     __syncthreads();
+  };
+  int sg = 1;
+  for (; sg + 3 < nseg; sg += 3) {
+    step(mA, nA, mC, nC, sg);
+    step(mB, nB, mA, nA, sg + 1);
+    step(mC, nC, mB, nB, sg + 2);
   }
+  if (sg + 1 < nseg) step(mA, nA, mC, nC, sg);
+  if (sg + 2 < nseg) step(mB, nB, mA, nA, sg + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -3318,8 +3357,8 @@ static hipError_t launch_pipe(const PrefillArgs& a, hipStream_t s) {
 // segments of L chunks take (1 + 0.9 (rounds of pass 1 - 1) + rounds of
 // pass 3) (L + 2) (pass 1's first round holds the full runs of segment 0,
 // its other rounds only two-state runs at about 0.9 of a full step; 2:
-// pipeline fill and state traffic per workgroup) plus about half a step per
-// combine, where a round is one workgroup per compute unit.  0 if one pass is
+// pipeline fill and state traffic per workgroup) plus about a quarter of a
+// step per combine step, where a round is one workgroup per compute unit.  0 if one pass is
 // cheaper.
 int prefill_segments(int BH, int T, int cus) {
   const int N = (T + C - 1) / C;
@@ -3330,7 +3369,7 @@ int prefill_segments(int BH, int T, int cus) {
     const int L = (N + P - 1) / P, Pe = (N + L - 1) / L;
     if (Pe != P) continue;   // only counts that split into equal-length segments (bar the last)
     const int r1 = (BH * (P - 1) + cus - 1) / cus, r3 = r1;
-    const double cost = (1.0 + 0.9 * (r1 - 1) + r3) * (L + 2.0) + 0.5 * (P - 2);
+    const double cost = (1.0 + 0.9 * (r1 - 1) + r3) * (L + 2.0) + 0.25 * (P - 2);
     if (cost < best) { best = cost; best_p = P; }
   }
   return best_p;
