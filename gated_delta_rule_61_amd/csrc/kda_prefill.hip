@@ -1464,27 +1464,36 @@ __device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], co
 
 // Workspace matrix (fp32, d_k x d_v) of the segmented schedule: for sequence /
 // head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N
-// (row-major [d_k][d_v], except M: in the combine's operand order, mfrag_index).
+// (row-major [d_k][d_v], except M: split bf16 parts in the combine's operand
+// order, mfrag_index).
 __device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int s, int kind) {
   return ws + ((head * nseg + s) * 3 + kind) * (int64_t)(DK * DV);
 }
 
-// Transition M of the segmented schedule in the A-operand order of the
-// combine kernel's products (v_mfma_f32_16x16x4_f32 on a 16-row tile):
-// element (r, c) sits in the 256-float block 8 (r / 16) + c / 16, at lane
-// 16 (c % 4) + r % 16, position (c / 4) % 4 of that lane's four, so that a
-// lane of the combine reads four consecutive 4-index steps as one vector.
-__device__ __forceinline__ int mfrag_index(int r, int c) {
-  return ((r >> 4) * 8 + (c >> 4)) * 256 + (16 * (c & 3) + (r & 15)) * 4 + ((c >> 2) & 3);
+// Transition M of the segmented schedule for the combine kernel's products
+// (v_mfma_f32_16x16x32_bf16 on a 16-row tile, M split into a bf16 high part
+// and the bf16 rounding of the rest): element (r, c), part h (0 high, 1
+// low) sits in the A-operand vector (16 bytes) of lane 16 ((c / 8) % 4) +
+// r % 16 for row tile r / 16, 32-index slab c / 32 and part h, at position
+// c % 8; a lane of the combine reads each of its operands as one vector.
+__device__ __forceinline__ int mfrag_index(int r, int c, int h) {
+  return ((((r >> 4) * 4 + (c >> 5)) * 2 + h) * 64 + 16 * ((c >> 3) & 3) + (r & 15)) * 8 + (c & 7);
 }
 __device__ __forceinline__ void store_state_mfrag(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
+  bf16* o16 = reinterpret_cast<bf16*>(out);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[mfrag_index(16 * rt + 4 * g4 + j, col0 + vcol(nt, l16))] = S[nt][rt][j];
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * rt + 4 * g4 + j, c = col0 + vcol(nt, l16);
+        const float x = S[nt][rt][j];
+        const bf16 hi = (bf16)x;
+        o16[mfrag_index(r, c, 0)] = hi;
+        o16[mfrag_index(r, c, 1)] = (bf16)(x - (float)hi);
+      }
 }
 
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
@@ -2996,27 +3005,34 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
 // Segmented schedule, between the two passes: the entry state of each
 // segment, S_{s+1} = M_s S_s + N_s for s = 1 .. nseg-2 (S_1 is segment 0's
 // final state).  The columns of the state never mix, so each sequence and
-// head is split into NSC workgroups of 16 columns (fp32 MFMA,
-// v_mfma_f32_16x16x4_f32); wavefront w forms rows 32w .. 32w+31 of the
-// slice.  M_s comes from the workspace in the A-operand order of those
-// products (mfrag_index), straight into registers, one step ahead; the S
-// slice alternates between two LDS buffers, stored transposed so that a
-// lane's B operands of a step are eight 16-byte reads.
+// head is split into NSC workgroups of 16 columns; wavefront w forms rows
+// 32w .. 32w+31 of the slice.  Each fp32 product runs as three bf16 MFMAs
+// (v_mfma_f32_16x16x32_bf16) on split operands, x = hi + lo with hi the bf16
+// rounding of x and lo that of x - hi: hi hi + hi lo + lo hi, relative error
+// about 2^-16 (the dropped lo lo term and the rounding of lo), against 2^-9
+// for the bf16 operands of the state update the maps stand for.  M_s comes
+// from the workspace already split, in the A-operand order (mfrag_index),
+// straight into registers two steps ahead; the slice of S_s alternates
+// between two LDS buffers, split and stored column by column, so that each
+// B operand of a lane is one 16-byte read.
 // ---------------------------------------------------------------------------
 namespace segc {
 constexpr int NTC = 256;
 constexpr int NSC = 8;               // column slices per sequence and head
 constexpr int CW = 128 / NSC;        // columns per slice
-constexpr int LDS_T = 132;           // fp32 per slice column: [row % 4][row / 4], padded
-constexpr int BYTES = 2 * CW * LDS_T * 4;
+constexpr int LDS_T = 136;           // bf16 per slice column (its 128 rows, padded)
+constexpr int PART = CW * LDS_T;     // bf16 of one part (high or low) of a buffer
+constexpr int BYTES = 2 * 2 * PART * 2;
 }  // namespace segc
 
 __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   using namespace segc;
   constexpr int D = 128;
+  typedef Mma<bf16> CM;
+  typedef CM::F32 Frag;   // bf16x8
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  float* T0 = reinterpret_cast<float*>(smem_raw);
-  float* T1 = T0 + CW * LDS_T;
+  bf16* T0 = reinterpret_cast<bf16*>(smem_raw);   // buffer 0: high part, then low part
+  bf16* T1 = T0 + 2 * PART;
   const int col0 = (blockIdx.x % NSC) * CW;
   int nseg = a.nseg;
   // maps of segment s of this sequence and head: batched sequences keep them
@@ -3039,14 +3055,15 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   auto mat = [&](int s, int kind) { return a.ws + ((mbase + s * mslot) * 3 + kind) * (D * D); };
-  // the lane's A operands of M_s: tile u (rows 32 wave + 16 u ..), 16-index
-  // group kq, four consecutive 4-index steps in one vector
-  auto load_m = [&](int s, floatx4 (&m)[2][8]) {
-    const floatx4* src = reinterpret_cast<const floatx4*>(mat(s, 1));
+  // the lane's A operands of M_s: tile u (rows 32 wave + 16 u ..), slab kk, part h
+  auto load_m = [&](int s, Frag (&m)[2][4][2]) {
+    const Frag* src = reinterpret_cast<const Frag*>(mat(s, 1));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int kq = 0; kq < 8; ++kq) m[u][kq] = src[((2 * wave + u) * 8 + kq) * 64 + lane];
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) m[u][kk][h] = src[(((2 * wave + u) * 4 + kk) * 2 + h) * 64 + lane];
   };
   // N_s of the lane's eight entries (the accumulator's start)
   auto load_n = [&](int s, floatx4 (&nr)[2]) {
@@ -3056,11 +3073,14 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) nr[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
   };
-  // slice element (row r, column c) of a transposed buffer
-  auto tpos = [](int r, int c) { return c * LDS_T + (r & 3) * 32 + (r >> 2); };
+  auto split = [](float x, bf16& hi, bf16& lo) {
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+  };
   // three register sets of the maps: step s uses set (s - 1) % 3 and loads
   // the maps of step s + 2 into set (s + 1) % 3
-  floatx4 mA[2][8], mB[2][8], mC[2][8], nA[2], nB[2], nC[2];
+  Frag mA[2][4][2], mB[2][4][2], mC[2][4][2];
+  floatx4 nA[2], nB[2], nC[2];
   // S_1 (the slice's 128 x 16 entries, two 16-byte pieces per thread) and
   // the first two steps' maps, all in flight together
   static_assert(D * CW / 4 == 2 * NTC, "two pieces of the slice per thread");
@@ -3083,7 +3103,7 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   for (int u = 0; u < 2; ++u) {
     const int i = tid + u * NTC, r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) T0[tpos(r, c4 + j)] = sv[u][j];
+    for (int j = 0; j < 4; ++j) split(sv[u][j], T0[(c4 + j) * LDS_T + r], T0[PART + (c4 + j) * LDS_T + r]);
   }
   __syncthreads();
   // Step s: S_{s+1} = M_s S_s + N_s, from buffer (s - 1) % 2 into the other.
@@ -3091,32 +3111,50 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   // order; the last steps reload maps already held, so that no load is under
   // a branch).  One barrier per step: the buffer a step writes was last read
   // a step earlier.
-  auto step = [&](const floatx4 (&mc)[2][8], const floatx4 (&nc)[2], floatx4 (&mf)[2][8], floatx4 (&nf)[2],
+  auto step = [&](const Frag (&mc)[2][4][2], const floatx4 (&nc)[2], Frag (&mf)[2][4][2], floatx4 (&nf)[2],
                   int sg) {
-    const float* Tc = (sg & 1) ? T0 : T1;
-    float* Tn = (sg & 1) ? T1 : T0;
+    const bf16* Tc = (sg & 1) ? T0 : T1;
+    bf16* Tn = (sg & 1) ? T1 : T0;
     const int nx = min(sg + 2, nseg - 2);
     floatx4 acc[2] = {nc[0], nc[1]};
     load_m(nx, mf);
     load_n(nx, nf);
-    // B operands: S_s[4 kb + g4][l16] for kb = 0 .. 31
-    floatx4 bq[8];
+    // B operands: rows 32 kk + 8 g4 .. + 7 of slice column l16, both parts
+    Frag bh[4], bl[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) bq[q] = *reinterpret_cast<const floatx4*>(Tc + l16 * LDS_T + g4 * 32 + 4 * q);
+    for (int kk = 0; kk < 4; ++kk) {
+      bh[kk] = *reinterpret_cast<const Frag*>(Tc + l16 * LDS_T + 32 * kk + 8 * g4);
+      bl[kk] = *reinterpret_cast<const Frag*>(Tc + PART + l16 * LDS_T + 32 * kk + 8 * g4);
+    }
+    // the small terms first
 #pragma unroll
-    for (int kb = 0; kb < D / 4; ++kb)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[u][kb >> 2][kb & 3], bq[kb >> 2][kb & 3], acc[u], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        acc[u] = CM::mma32(mc[u][kk][1], bh[kk], acc[u]);
+        acc[u] = CM::mma32(mc[u][kk][0], bl[kk], acc[u]);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) acc[u] = CM::mma32(mc[u][kk][0], bh[kk], acc[u]);
     float* dst = mat(sg + 1, 0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      bf16x4 hi, lo;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 32 * wave + 16 * u + 4 * g4 + jj;
-        Tn[tpos(r, l16)] = acc[u][jj];
         dst[r * D + col0 + l16] = acc[u][jj];
+        bf16 h_, l_;
+        split(acc[u][jj], h_, l_);
+        hi[jj] = h_;
+        lo[jj] = l_;
       }
+      const int r0 = 32 * wave + 16 * u + 4 * g4;
+      *reinterpret_cast<bf16x4*>(Tn + l16 * LDS_T + r0) = hi;
+      *reinterpret_cast<bf16x4*>(Tn + PART + l16 * LDS_T + r0) = lo;
+    }
     __syncthreads();
   };
   int sg = 1;
