@@ -1289,10 +1289,13 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
 // runs in registers (DPP row shifts across the 16 token groups), and the
 // transposed operands are written 4 tokens at a time.
 // ---------------------------------------------------------------------------
-// Internal template flag of fused_pipe_kernel, beside the variant bits: the
+// Internal template flags of fused_pipe_kernel, beside the variant bits: the
 // state-mode instantiation (chunk-entry states out, no outputs), so that the
-// forward proper carries none of its code.
+// forward proper carries none of its code; and the instantiation of the
+// segmented schedule's first pass, the only one that holds the two-state
+// owners (whose registers would otherwise size every other launch too).
 constexpr int kPipeStates = 4;
+constexpr int kPipeDual = 8;
 
 namespace pipe {
 
@@ -2562,6 +2565,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   using namespace pipe;
   constexpr bool ND = (V & kVarNoDelta) != 0;
   constexpr bool ST = (V & kPipeStates) != 0;
+  constexpr bool DU = (V & kPipeDual) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2708,7 +2712,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   // the reference before the first chunk (buffer of chunk -1) is 0
   if (tid < DK) p.rho[2 * DK + tid] = 0.f;
 
-  if (!ST && dual && wave < 4) {
+  if (!ST && DU && dual && wave < 4) {
     // ---------------------------------------------------- owners, two states
     // N (from zero, with the values) and M (from the identity, values zero):
     // the same chunk operands, so the workers' half of the work is shared;
@@ -3322,12 +3326,16 @@ static hipError_t launch_fused_d(const PrefillArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// The segmented schedule: pass 1 (segment 0 and the maps of the middle
+// segments, with the two-state owners), the combine, pass 3.
 template <int V>
-static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
+static hipError_t launch_pipe_seg(const PrefillArgs& a, hipStream_t s) {
   const int bytes = pipe::BYTES;
   auto fused_pipe_kernel = ::kda::fused_pipe_kernel<V>;
+  auto fused_pipe_pass1 = ::kda::fused_pipe_kernel<V | kPipeDual>;
   hipError_t e = set_smem(fused_pipe_kernel, bytes);
   if (e != hipSuccess) return e;
+  if ((e = set_smem(fused_pipe_pass1, bytes)) != hipSuccess) return e;
   const int BH = a.B * a.H;
   if (a.plan) {
     // packed sequences, segmented: the plan, whole short sequences with
@@ -3339,7 +3347,7 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
     PrefillArgs a1 = a, a3 = a;
     a1.pass = 1;
     a3.pass = 3;
-    hipLaunchKernelGGL(fused_pipe_kernel, dim3(a.plan_j1 * a.H), dim3(NT), bytes, s, a1);
+    hipLaunchKernelGGL(fused_pipe_pass1, dim3(a.plan_j1 * a.H), dim3(NT), bytes, s, a1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.plan_ns > 0 && a.plan_j3 > 0) {
       if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
@@ -3349,23 +3357,34 @@ static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (a.nseg < 3) {
-    PrefillArgs a0 = a;
-    a0.pass = 0;
-    hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(BH, 1)), dim3(NT), bytes, s, a0);
-    return hipGetLastError();
-  }
-  // segmented: segment 0 and the maps of the middle segments, entry states,
-  // then segments 1 .. nseg-1
+  // segment 0 and the maps of the middle segments, entry states, then
+  // segments 1 .. nseg-1
   PrefillArgs a1 = a, a3 = a;
   a1.pass = 1;
   a3.pass = 3;
-  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a1);
+  hipLaunchKernelGGL(fused_pipe_pass1, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
   hipLaunchKernelGGL(seg_combine_kernel, dim3(BH * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
+  return hipGetLastError();
+}
+
+template <int V>
+static hipError_t launch_pipe_v(const PrefillArgs& a, hipStream_t s) {
+  const int bytes = pipe::BYTES;
+  auto fused_pipe_kernel = ::kda::fused_pipe_kernel<V>;
+  hipError_t e = set_smem(fused_pipe_kernel, bytes);
+  if (e != hipSuccess) return e;
+  const int BH = a.B * a.H;
+  if (a.plan || a.nseg >= 3) {
+    if constexpr ((V & kPipeStates) == 0) return launch_pipe_seg<V>(a, s);
+    return hipErrorInvalidValue;
+  }
+  PrefillArgs a0 = a;
+  a0.pass = 0;
+  hipLaunchKernelGGL(fused_pipe_kernel, dim3(grid_heads(BH, 1)), dim3(NT), bytes, s, a0);
   return hipGetLastError();
 }
 
