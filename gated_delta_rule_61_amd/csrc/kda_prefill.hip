@@ -1482,21 +1482,40 @@ __device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int
 __device__ __forceinline__ int mfrag_index(int r, int c, int h) {
   return ((((r >> 4) * 4 + (c >> 5)) * 2 + h) * 64 + 16 * ((c >> 3) & 3) + (r & 15)) * 8 + (c & 7);
 }
-__device__ __forceinline__ void store_state_mfrag(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane) {
-  const int g4 = lane >> 4, l16 = lane & 15;
-  bf16* o16 = reinterpret_cast<bf16*>(out);
+// Owner o's columns 32o .. 32o+31 of M are exactly slab o of that order, so
+// each owner writes its slab alone: its 128 x 32 block goes row-major into
+// its own LDS area `stage` (128 rows of 36 floats), and each lane reads back
+// the eight columns of one row that form one of its vectors, splits them and
+// stores the high and the low vector (16 bytes each, a whole 1 KB block per
+// wave store).  The area is read only by the wave that wrote it, after its
+// writes (LDS operations of one wavefront complete in order).
+constexpr int kMStageRow = 36;
+__device__ __forceinline__ void store_state_mfrag(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane,
+                                                  float* stage) {
+  const int g4 = lane >> 4, l16 = lane & 15, o = col0 >> 5;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rt + 4 * g4 + j, c = col0 + vcol(nt, l16);
-        const float x = S[nt][rt][j];
-        const bf16 hi = (bf16)x;
-        o16[mfrag_index(r, c, 0)] = hi;
-        o16[mfrag_index(r, c, 1)] = (bf16)(x - (float)hi);
-      }
+      for (int j = 0; j < 4; ++j) stage[(16 * rt + 4 * g4 + j) * kMStageRow + vcol(nt, l16)] = S[nt][rt][j];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  bf16x8* o16 = reinterpret_cast<bf16x8*>(out);
+#pragma unroll
+  for (int rt = 0; rt < DK / 16; ++rt) {
+    const float* src = stage + (16 * rt + l16) * kMStageRow + 8 * g4;
+    const floatx4 x0 = *reinterpret_cast<const floatx4*>(src), x1 = *reinterpret_cast<const floatx4*>(src + 4);
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < 4 ? x0[e] : x1[e - 4];
+      hi[e] = (bf16)x;
+      lo[e] = (bf16)(x - (float)hi[e]);
+    }
+    o16[((rt * 4 + o) * 2 + 0) * 64 + lane] = hi;
+    o16[((rt * 4 + o) * 2 + 1) * 64 + lane] = lo;
+  }
 }
 
 // Keeps a batch of LDS reads ahead of the products that use them (otherwise
@@ -2784,7 +2803,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
     store_state_v(S, sTp, col0, lane);
     state_rescale(SM, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
-    store_state_mfrag(SM, smp, col0, lane);
+    // (after the loop the workers touch only rho and the flags: the four
+    // row-major operand areas are free, one per owner)
+    static_assert(DK * kMStageRow * 4 <= SZ_RM && O_KH == O_KT + SZ_RM && O_QT == O_KH + SZ_RM &&
+                      O_WN == O_QT + SZ_RM && O_WN + SZ_RM <= O_RHO, "map staging areas");
+    store_state_mfrag(SM, smp, col0, lane, reinterpret_cast<float*>(smem_raw + O_KT + o * SZ_RM));
   } else if (wave < 4) {
     // ---------------------------------------------------------------- owners
     const int o = wave;
