@@ -1296,6 +1296,9 @@ __global__ __launch_bounds__(NT) void stage_output_kernel(StageArgs a) {
 // owners (whose registers would otherwise size every other launch too).
 constexpr int kPipeStates = 4;
 constexpr int kPipeDual = 8;
+// and the third pass's instantiation, whose entry states come from the
+// workspace in the owners' fragment order (sfrag_index)
+constexpr int kPipeSegIn = 16;
 
 namespace pipe {
 
@@ -1442,6 +1445,33 @@ __device__ __forceinline__ void store_state_v(const floatx4 (&S)[2][DK / 16], fl
       for (int j = 0; j < 4; ++j) out[(16 * rt + 4 * g4 + j) * DV + col0 + vcol(nt, l16)] = S[nt][rt][j];
 }
 
+// The same tiles in fp32 in the owners' fragment order, for the segmented
+// schedule's workspace (entry states and offsets N): owner o = col0 / 32, tile
+// (nt, rt) is the 256-float block 8 (2 o + nt) + rt, inside which lane (g, i)
+// holds elements 4 (16 g + i) .. + 3 = rows 16 rt + 4 g .. + 3 of value
+// column col0 + vcol(nt, i): one 16-byte access per lane and tile, a whole
+// 1 KB block per wave access.
+__device__ __forceinline__ int sfrag_index(int r, int c) {
+  const int cl = c & 31, nt = (cl >> 2) & 1, i = 4 * (cl >> 3) + (cl & 3);
+  return ((8 * (2 * (c >> 5) + nt) + (r >> 4)) * 64 + 16 * ((r >> 2) & 3) + i) * 4 + (r & 3);
+}
+__device__ __forceinline__ void load_state_f(floatx4 (&S)[2][DK / 16], const float* src, int col0, int lane) {
+  const floatx4* s4 = reinterpret_cast<const floatx4*>(src);
+  const int o = col0 >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt) S[nt][rt] = s4[(8 * (2 * o + nt) + rt) * 64 + lane];
+}
+__device__ __forceinline__ void store_state_f(const floatx4 (&S)[2][DK / 16], float* out, int col0, int lane) {
+  floatx4* o4 = reinterpret_cast<floatx4*>(out);
+  const int o = col0 >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt) o4[(8 * (2 * o + nt) + rt) * 64 + lane] = S[nt][rt];
+}
+
 // The same tiles as bf16 in the owners' fragment order: owner o = col0 / 32,
 // tile (nt, rt) is the 256-element block 8 (2 o + nt) + rt, inside which
 // lane (g, i) holds elements 16 i + 4 g .. + 3, i.e. rows 16 rt + 4 g .. + 3
@@ -1467,8 +1497,8 @@ __device__ __forceinline__ void store_state_t(const floatx4 (&S)[2][DK / 16], co
 
 // Workspace matrix (fp32, d_k x d_v) of the segmented schedule: for sequence /
 // head `head` and segment s, kind 0 = entry state, 1 = transition M, 2 = offset N
-// (row-major [d_k][d_v], except M: split bf16 parts in the combine's operand
-// order, mfrag_index).
+// (entry states and N in the owners' fp32 fragment order, sfrag_index; M as
+// split bf16 parts in the combine's operand order, mfrag_index).
 __device__ __forceinline__ float* seg_mat(float* ws, int64_t head, int nseg, int s, int kind) {
   return ws + ((head * nseg + s) * 3 + kind) * (int64_t)(DK * DV);
 }
@@ -2585,6 +2615,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   constexpr bool ND = (V & kVarNoDelta) != 0;
   constexpr bool ST = (V & kPipeStates) != 0;
   constexpr bool DU = (V & kPipeDual) != 0;
+  constexpr bool SI = (V & kPipeSegIn) != 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2602,6 +2633,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
   int head, c0 = 0, nchunks = (a.T + C - 1) / C;
   const float* s0p = nullptr;
   float* sTp = nullptr;
+  bool sTf = false;   // sTp is a workspace entry state (fragment order)
   bool ident = false, outp = true, vzero = false;
   // a middle segment of the segmented schedule: its offset N_s (state from
   // zero, into sTp) and its transition M_s (state from the identity with the
@@ -2648,6 +2680,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
         vsg = 0;
         s0p = S0h;
         sTp = vmap(1, 0);
+        sTf = true;
       } else {
         vsg = k;
         outp = false;
@@ -2671,6 +2704,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
       if (job == 0) {
         if (a.S0) s0p = a.S0 + (int64_t)head * DK * DV;
         sTp = seg_mat(a.ws, head, a.nseg, 1, 0);
+        sTf = true;
       } else {
         outp = false;
         dual = true;
@@ -2801,7 +2835,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     }
     // back from the last chunk's reference
     state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
-    store_state_v(S, sTp, col0, lane);
+    store_state_f(S, sTp, col0, lane);
     state_rescale(SM, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
     // (after the loop the workers touch only rho and the flags: the four
     // row-major operand areas are free, one per owner)
@@ -2813,7 +2847,11 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     const int o = wave;
     const int col0 = 32 * o;
     floatx4 S[2][DK / 16];
-    load_state_v(S, s0p, ident, col0, lane);
+    // (the third pass's entry states come from the workspace, always)
+    if constexpr (SI)
+      load_state_f(S, s0p, col0, lane);
+    else
+      load_state_v(S, s0p, ident, col0, lane);
     floatx4 O[2][4], U[2][4];
     Vec16 vr[4];
     if (nchunks > 0) fetch_v(vr, a, bb, h, c0, o, lane);
@@ -2922,7 +2960,10 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
     if (sTp) {
       // back from the last chunk's reference
       state_rescale(S, p.rho + ((nchunks + 2) % 3) * DK, nullptr, lane);
-      store_state_v(S, sTp, col0, lane);
+      if (sTf)
+        store_state_f(S, sTp, col0, lane);
+      else
+        store_state_v(S, sTp, col0, lane);
     }
   } else {
     // --------------------------------------------------------------- workers
@@ -3093,12 +3134,13 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
         for (int h = 0; h < 2; ++h) m[u][kk][h] = src[(((2 * wave + u) * 4 + kk) * 2 + h) * 64 + lane];
   };
   // N_s of the lane's eight entries (the accumulator's start)
+  // (entry states and N in the owners' fragment order: the lane's four rows
+  // of a tile, 4 g4 .. + 3, are one vector)
+  auto sfrag = [&](int u) { return pipe::sfrag_index(32 * wave + 16 * u + 4 * g4, col0 + l16); };
   auto load_n = [&](int s, floatx4 (&nr)[2]) {
     const float* Nm = mat(s, 2);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) nr[u][jj] = Nm[(32 * wave + 16 * u + 4 * g4 + jj) * D + col0 + l16];
+    for (int u = 0; u < 2; ++u) nr[u] = *reinterpret_cast<const floatx4*>(Nm + sfrag(u));
   };
   auto split = [](float x, bf16& hi, bf16& lo) {
     hi = (bf16)x;
@@ -3110,14 +3152,15 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   floatx4 nA[2], nB[2], nC[2];
   // S_1 (the slice's 128 x 16 entries, two 16-byte pieces per thread) and
   // the first two steps' maps, all in flight together
+  // (piece v = tid + 256 u: rows 4 (v / 16) .. + 3 of slice column v % 16)
   static_assert(D * CW / 4 == 2 * NTC, "two pieces of the slice per thread");
   floatx4 sv[2];
   {
     const float* src = mat(1, 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int i = tid + u * NTC, r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
-      sv[u] = *reinterpret_cast<const floatx4*>(src + r * D + col0 + c4);
+      const int v = tid + u * NTC;
+      sv[u] = *reinterpret_cast<const floatx4*>(src + pipe::sfrag_index(4 * (v >> 4), col0 + (v & 15)));
     }
   }
   if (nseg > 2) {
@@ -3128,9 +3171,9 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int i = tid + u * NTC, r = i / (CW / 4), c4 = 4 * (i % (CW / 4));
+    const int v = tid + u * NTC, r0 = 4 * (v >> 4), c = v & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split(sv[u][j], T0[(c4 + j) * LDS_T + r], T0[PART + (c4 + j) * LDS_T + r]);
+    for (int j = 0; j < 4; ++j) split(sv[u][j], T0[c * LDS_T + r0 + j], T0[PART + c * LDS_T + r0 + j]);
   }
   __syncthreads();
   // Step s: S_{s+1} = M_s S_s + N_s, from buffer (s - 1) % 2 into the other.
@@ -3168,11 +3211,10 @@ __global__ __launch_bounds__(segc::NTC) void seg_combine_kernel(PrefillArgs a) {
     float* dst = mat(sg + 1, 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<floatx4*>(dst + sfrag(u)) = acc[u];
       bf16x4 hi, lo;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int r = 32 * wave + 16 * u + 4 * g4 + jj;
-        dst[r * D + col0 + l16] = acc[u][jj];
         bf16 h_, l_;
         split(acc[u][jj], h_, l_);
         hi[jj] = h_;
@@ -3354,11 +3396,11 @@ static hipError_t launch_fused_d(const PrefillArgs& a, hipStream_t s) {
 template <int V>
 static hipError_t launch_pipe_seg(const PrefillArgs& a, hipStream_t s) {
   const int bytes = pipe::BYTES;
-  auto fused_pipe_kernel = ::kda::fused_pipe_kernel<V>;
   auto fused_pipe_pass1 = ::kda::fused_pipe_kernel<V | kPipeDual>;
-  hipError_t e = set_smem(fused_pipe_kernel, bytes);
+  auto fused_pipe_pass3 = ::kda::fused_pipe_kernel<V | kPipeSegIn>;
+  hipError_t e = set_smem(fused_pipe_pass1, bytes);
   if (e != hipSuccess) return e;
-  if ((e = set_smem(fused_pipe_pass1, bytes)) != hipSuccess) return e;
+  if ((e = set_smem(fused_pipe_pass3, bytes)) != hipSuccess) return e;
   const int BH = a.B * a.H;
   if (a.plan) {
     // packed sequences, segmented: the plan, whole short sequences with
@@ -3376,7 +3418,7 @@ static hipError_t launch_pipe_seg(const PrefillArgs& a, hipStream_t s) {
       if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
       hipLaunchKernelGGL(seg_combine_kernel, dim3(a.plan_ns * a.H * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL(fused_pipe_kernel, dim3(a.plan_j3 * a.H), dim3(NT), bytes, s, a3);
+      hipLaunchKernelGGL(fused_pipe_pass3, dim3(a.plan_j3 * a.H), dim3(NT), bytes, s, a3);
     }
     return hipGetLastError();
   }
@@ -3390,7 +3432,7 @@ static hipError_t launch_pipe_seg(const PrefillArgs& a, hipStream_t s) {
   if ((e = set_smem(seg_combine_kernel, segc::BYTES)) != hipSuccess) return e;
   hipLaunchKernelGGL(seg_combine_kernel, dim3(BH * segc::NSC), dim3(segc::NTC), segc::BYTES, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(fused_pipe_kernel, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
+  hipLaunchKernelGGL(fused_pipe_pass3, dim3(BH * (a.nseg - 1)), dim3(NT), bytes, s, a3);
   return hipGetLastError();
 }
 
