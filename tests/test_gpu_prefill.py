@@ -93,8 +93,11 @@ def test_bf16_d128_schedules(kda, B, T, H, pipeline, monkeypatch):
     check_prefill(to64(o), to64(S), o_ref, S_ref, torch.bfloat16, f"B{B}T{T}H{H} pipeline={pipeline}")
 
 
+# (segment counts 3 .. 8: the combine chains P - 2 steps, three per loop
+# iteration, and P = 6, 7 leave one and two steps after a whole iteration)
 SEG_SHAPES = [(1, 64 * 12, 2, 3, True), (1, 64 * 13 + 17, 2, 4, True), (2, 64 * 20, 1, 5, False),
-              (1, 64 * 9 + 1, 3, 3, True), (1, 64 * 40, 1, 8, True)]
+              (1, 64 * 9 + 1, 3, 3, True), (1, 64 * 40, 1, 8, True), (1, 64 * 30 + 5, 2, 6, True),
+              (1, 64 * 35, 1, 7, False)]
 
 
 @pytest.mark.parametrize("B,T,H,nseg,s0", SEG_SHAPES, ids=[f"B{b}T{t}H{h}-seg{n}{'-S0' if z else ''}" for b, t, h, n, z in SEG_SHAPES])
