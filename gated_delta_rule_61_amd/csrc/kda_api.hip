@@ -72,6 +72,9 @@ int check_staged_dims(int B, int T, int H, int dk, int dv, int dt) {
 int check_step_dims(int N, int H, int dk, int dv, int dt) {
   if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
   if (N < 0 || H < 0) return KDA_ERR_SHAPE;
+  // one 256-thread workgroup per sequence and head, in one launch dimension
+  // of at most 2^32 - 1 work-items
+  if ((int64_t)N * H > KDA_STEP_MAX_HEADS) return KDA_ERR_SHAPE;
   if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return KDA_ERR_SHAPE;
   return KDA_OK;
 }

@@ -159,7 +159,10 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
  *   q,k,g [N,H,d_k], v [N,H,d_v], beta [N,H]  (dtype `dtype`)
  *   S     [N,H,d_k,d_v] fp32, read and overwritten IN PLACE with S_t
  *   o     [N,H,d_v] output (dtype `dtype`), o = S_t^T q
+ * N * H <= KDA_STEP_MAX_HEADS (else KDA_ERR_SHAPE): one launch holds one
+ * workgroup per sequence and head.
  */
+#define KDA_STEP_MAX_HEADS 16777215
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* S, void* o,
                        int N, int H, int d_k, int d_v, int dtype, void* stream);

@@ -141,6 +141,8 @@ def test_decode_validation(L):
     assert L.kda_recurrent_step(p, p, p, p, p, p, p, 4, 2, 128, 128, 5, None) == -3
     assert L.kda_recurrent_step(p, p, p, p, p, ctypes.c_void_p(20), p, 4, 2, 128, 128, 1, None) == -4
     assert L.kda_recurrent_step(p, p, p, p, p, p, p, 0, 2, 128, 128, 1, None) == 0
+    # more sequence-heads than one launch holds (KDA_STEP_MAX_HEADS = 2^24 - 1)
+    assert L.kda_recurrent_step(p, p, p, p, p, p, p, 1 << 16, 256, 64, 64, 1, None) == -2
 
 
 def test_binding_rejects_cpu_tensors():
