@@ -3077,7 +3077,7 @@ __global__ __launch_bounds__(NT) void fused_pipe_kernel(PrefillArgs a) {
 // 32w .. 32w+31 of the slice.  Each fp32 product runs as three bf16 MFMAs
 // (v_mfma_f32_16x16x32_bf16) on split operands, x = hi + lo with hi the bf16
 // rounding of x and lo that of x - hi: hi hi + hi lo + lo hi, relative error
-// about 2^-16 (the dropped lo lo term and the rounding of lo), against 2^-9
+// about 2^-16 (the dropped lo lo term and the rounding of lo), against 2^-8
 // for the bf16 operands of the state update the maps stand for.  M_s comes
 // from the workspace already split, in the A-operand order (mfrag_index),
 // straight into registers two steps ahead; the slice of S_s alternates
